@@ -1,0 +1,165 @@
+#!/usr/bin/env python3
+"""Benchmark of the Domino head block draft on one MI355X.
+
+One step = one call of domino_head_draft: the whole drafting loop (A_H
+precompute, anchor GRU step, then 16 x (low-rank activation, W2 correction +
+residual + greedy argmax, embedding gather + GRU step)) over one batch of
+seeded synthetic inputs already resident in device memory.
+
+Prints ONE JSON line on stdout.  Diagnostics go to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def logical_bytes(sh, B, store_logits=False):
+    """Algorithmic bytes of one block draft: every operand each step reads once.
+
+    Per position (K of them): W2 [V,r], the L_base slice [B,V] fp32 and the state
+    columns of W1 [r,h].  Per GRU step (K of them: the anchor plus K-1 fed-back
+    tokens): W_ih [3h,d], W_hh [3h,h], the gathered embedding rows [B,d] and both
+    bias vectors.  Once per call: the H columns of W1 [r,d], H [B,K,d] and the
+    tokens [B,K].  Returns (total, w2_and_lbase).
+    """
+    s = 4 if sh.wdtype == "f32" else 2
+    K, V, r, h, d = sh.K, sh.V, sh.r, sh.h, sh.d
+    per_pos = V * r * s + B * V * 4 + r * h * s
+    per_gru = 3 * h * d * s + 3 * h * h * s + B * d * s + 6 * h * s
+    once = r * d * s + B * K * d * s + B * K * 4
+    total = K * per_pos + K * per_gru + once
+    if store_logits:
+        total += B * K * V * 4
+    return total, K * (V * r * s + B * V * 4)
+
+
+def cpu_baseline(w, inp, budget_s):
+    """The fp64 oracle as it stands, on this host's cores, on row 0 of the workload."""
+    import oracle
+
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.draft(w, inp.H[:1], inp.L_base[:1], inp.last_tok[:1], want_logits=False, want_state=False)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return n, el, oracle.max_threads()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3_8b_b1")
+    ap.add_argument("--mode", default="auto", choices=["auto", "persistent", "stepwise"])
+    ap.add_argument("--store-logits", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        eprint("bench.py runs on one GPU only: the Domino head path here is single-device "
+               "(batch rows shard trivially across GPUs with no exchange); --gpus %d is not supported" % args.gpus)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import causal_draft_correction_amd as dca
+    import domino_synth as ds
+
+    torch.cuda.set_device(0)
+    wl = ds.WORKLOADS[args.workload]
+    sh = wl.shape
+    eprint("bench: generating %s (B=%d, d=%d, h=%d, r=%d, V=%d, %s)" % (wl.name, wl.B, sh.d, sh.h, sh.r, sh.V,
+                                                                      sh.wdtype))
+    w, inp = ds.make_workload(wl.name)
+    mode = {"auto": dca.EXEC_AUTO, "persistent": dca.EXEC_PERSISTENT, "stepwise": dca.EXEC_STEPWISE}[args.mode]
+    head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B, exec_mode=mode)
+    H = dca.device_tensor(inp.H)
+    L = dca.device_tensor(inp.L_base)
+    lt = dca.device_tensor(inp.last_tok)
+    out = {"tokens": torch.empty((wl.B, sh.K), dtype=torch.int32, device="cuda")}
+    if args.store_logits:
+        out["L_final"] = torch.empty((wl.B, sh.K, sh.V), dtype=torch.float32, device="cuda")
+    exec_name = args.mode
+    if args.mode == "auto":
+        exec_name = "persistent" if wl.B <= 8 else "stepwise"
+
+    for _ in range(args.warmup):
+        head.draft(H, L, lt, out=out)
+    torch.cuda.synchronize()
+    assert head.check_error() == 0
+    eprint("bench: warmup done, timing %d steps" % args.steps)
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        head.draft(H, L, lt, out=out)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    flags = head.check_error()
+    assert flags == 0, "device flags %d" % flags
+    per_call_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_ms = float(np.mean(per_call_ms))
+    ms_per_step = wall * 1e3 / args.steps
+    blocks_per_s = wl.B * args.steps / wall
+
+    total_bytes, w2l_bytes = logical_bytes(sh, wl.B, args.store_logits)
+    achieved = total_bytes / (avg_ms * 1e-3) / 1e9
+    w2l = w2l_bytes / (avg_ms * 1e-3) / 1e9
+    traffic = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        eprint("bench: timing the fp64 oracle on the host (cpu_baseline)")
+        n, el, threads = cpu_baseline(w, inp, args.cpu_budget)
+        cpu = {"value": n / el, "unit": "blocks/s", "cores": threads, "kind": "oracle",
+               "sample": "%d block draft(s) of row 0 of %s (free running, K=%d, V=%d), fp64 C oracle" % (
+                   n, wl.name, sh.K, sh.V)}
+
+    rec = {
+        "metric": "Domino-head draft blocks/sec (16 tok, V=151936) + achieved HBM GB/s at 1 GPU",
+        "value": blocks_per_s,
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "K": sh.K, "V": sh.V, "d": sh.d, "h": sh.h, "r": sh.r,
+                   "weights": sh.wdtype, "exec": exec_name, "store_logits": bool(args.store_logits),
+                   "kernel_avg_us": avg_ms * 1e3, "w2_lbase_GBps": w2l,
+                   "w2_lbase_frac_of_hbm_peak": w2l / HBM_PEAK_GBPS},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

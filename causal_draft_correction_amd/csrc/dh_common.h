@@ -1,0 +1,223 @@
+// Device-side building blocks of the Domino head kernels (gfx950, wave64).
+//
+// Storage types, 16-byte chunk unpacking, block reductions, the packed argmax
+// key and the grid barrier used by the persistent launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dh {
+
+constexpr int NT = 512;           // threads per block (8 waves)
+constexpr int NWAVE = NT / 64;
+constexpr int NG = 16;            // barrier groups = partial argmax slots per position
+constexpr int MAXK = 16;          // largest block size
+constexpr int BC = 8;             // batch rows sharing one pass over W2
+constexpr int BAR_STRIDE = 64;    // uints between barrier words (256 bytes: own cache line)
+constexpr int BAR_WORDS = (2 * NG + 1) * BAR_STRIDE;
+
+// Storage tag for bfloat16 (raw 16-bit patterns).
+struct bf16s {
+    uint16_t bits;
+};
+
+template <typename WT>
+struct WT16;
+
+template <>
+struct WT16<float> {
+    static constexpr int EPC = 4;  // elements per 16-byte chunk
+    __device__ static inline void unpack(const uint4 &q, float *o)
+    {
+        o[0] = __uint_as_float(q.x);
+        o[1] = __uint_as_float(q.y);
+        o[2] = __uint_as_float(q.z);
+        o[3] = __uint_as_float(q.w);
+    }
+    __device__ static inline float one(const void *base, size_t i) { return static_cast<const float *>(base)[i]; }
+};
+
+template <>
+struct WT16<bf16s> {
+    static constexpr int EPC = 8;
+    __device__ static inline void unpack(const uint4 &q, float *o)
+    {
+        o[0] = __uint_as_float(q.x << 16);
+        o[1] = __uint_as_float(q.x & 0xFFFF0000u);
+        o[2] = __uint_as_float(q.y << 16);
+        o[3] = __uint_as_float(q.y & 0xFFFF0000u);
+        o[4] = __uint_as_float(q.z << 16);
+        o[5] = __uint_as_float(q.z & 0xFFFF0000u);
+        o[6] = __uint_as_float(q.w << 16);
+        o[7] = __uint_as_float(q.w & 0xFFFF0000u);
+    }
+    __device__ static inline float one(const void *base, size_t i)
+    {
+        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(base)[i]) << 16);
+    }
+};
+
+// 16-byte load of the chunk starting at element `elem` of a WT array.
+template <typename WT>
+__device__ inline uint4 ld16(const void *base, size_t elem)
+{
+    return *reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + elem * sizeof(WT));
+}
+
+// acc + sum_e w[e] * x[e] over one chunk, in element order.
+template <typename WT>
+__device__ inline float dot_chunk(const uint4 &q, const float *x, float acc)
+{
+    float w[WT16<WT>::EPC];
+    WT16<WT>::unpack(q, w);
+#pragma unroll
+    for (int e = 0; e < WT16<WT>::EPC; ++e)
+        acc = fmaf(w[e], x[e], acc);
+    return acc;
+}
+
+// fp32 chunk of EPC consecutive floats (EPC = 4 or 8) from global memory.
+template <int EPC>
+__device__ inline void ld_f32(const float *p, float *o)
+{
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    o[0] = a.x;
+    o[1] = a.y;
+    o[2] = a.z;
+    o[3] = a.w;
+    if constexpr (EPC == 8) {
+        const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+        o[4] = b.x;
+        o[5] = b.y;
+        o[6] = b.z;
+        o[7] = b.w;
+    }
+}
+
+__device__ inline float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ inline uint64_t wave_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o);
+        uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o);
+        uint64_t w = (static_cast<uint64_t>(hi) << 32) | lo;
+        v = w > v ? w : v;
+    }
+    return v;
+}
+
+// Sums M per-thread values over the block in a fixed order.  Results land in
+// red[NWAVE*M + m]; the caller syncs before reusing `red`.
+template <int M>
+__device__ inline void block_sum(float (&v)[M], float *red)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        v[m] = wave_sum(v[m]);
+    if (lane == 0) {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            red[wave * M + m] = v[m];
+    }
+    __syncthreads();
+    if (threadIdx.x < M) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w)
+            s += red[w * M + threadIdx.x];
+        red[NWAVE * M + threadIdx.x] = s;
+    }
+    __syncthreads();
+}
+
+__device__ inline float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
+
+// Argmax key: larger key = better candidate.  High word orders the float
+// (NaN above +inf, -0 folded into +0); low word prefers the lower index.
+__device__ inline uint64_t argmax_key(float f, uint32_t idx)
+{
+    uint32_t ord;
+    if (f != f) {
+        ord = 0xFFFFFFFFu;
+    } else {
+        uint32_t bits = (f == 0.f) ? 0u : __float_as_uint(f);
+        ord = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+    }
+    return (static_cast<uint64_t>(ord) << 32) | (0xFFFFFFFFu - idx);
+}
+
+__device__ inline uint32_t key_index(uint64_t key) { return 0xFFFFFFFFu - static_cast<uint32_t>(key); }
+
+__device__ inline uint64_t ld_agent_u64(const uint64_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Grid barrier for a cooperative launch.  Two levels: the blocks of group
+// g = blockIdx % NG count in on their group word; the last of a group counts
+// in on the top word; the last group leader publishes generation+1 into NG
+// per-group release words that the blocks of each group poll.  All counters
+// return to zero inside every barrier, so the words are reusable across
+// launches.  Thread 0 keeps the generation in `gen`.  A spin that exceeds
+// `spin_limit` polls sets DOMINO_FLAG_SYNC_TIMEOUT (bit 1) and returns false
+// in every thread of the block; the caller must then leave the kernel.
+// ---------------------------------------------------------------------------
+__device__ inline unsigned *bar_group(unsigned *bar, int g) { return bar + g * BAR_STRIDE; }
+__device__ inline unsigned *bar_top(unsigned *bar) { return bar + NG * BAR_STRIDE; }
+__device__ inline unsigned *bar_gen(unsigned *bar, int g) { return bar + (NG + 1 + g) * BAR_STRIDE; }
+
+__device__ inline unsigned barrier_gen_init(unsigned *bar)
+{
+    const int ngr = gridDim.x < NG ? static_cast<int>(gridDim.x) : NG;
+    return __hip_atomic_load(bar_gen(bar, blockIdx.x % ngr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline bool grid_sync(unsigned *bar, unsigned &gen, unsigned spin_limit, unsigned *flags)
+{
+    __shared__ int s_ok;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int nblk = static_cast<int>(gridDim.x);
+        const int ngr = nblk < NG ? nblk : NG;
+        const int g = static_cast<int>(blockIdx.x) % ngr;
+        const unsigned members = static_cast<unsigned>((nblk - g + ngr - 1) / ngr);
+        int ok = 1;
+        unsigned a = __hip_atomic_fetch_add(bar_group(bar, g), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (a == members - 1) {
+            __hip_atomic_store(bar_group(bar, g), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            unsigned a2 = __hip_atomic_fetch_add(bar_top(bar), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            if (a2 == static_cast<unsigned>(ngr) - 1) {
+                __hip_atomic_store(bar_top(bar), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int gg = 0; gg < ngr; ++gg)
+                    __hip_atomic_store(bar_gen(bar, gg), gen + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        unsigned spins = 0;
+        while (__hip_atomic_load(bar_gen(bar, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+            if (++spins > spin_limit) {
+                __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        gen += 1;
+        s_ok = ok;
+    }
+    __syncthreads();
+    return s_ok != 0;
+}
+
+}  // namespace dh

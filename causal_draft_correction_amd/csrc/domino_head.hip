@@ -1,0 +1,505 @@
+// Domino head drafting library for MI355X (gfx950): kernels and the C ABI.
+//
+// Two orchestrations of the same phases (dh_phases.h):
+//   * persistent: one cooperative launch of one block per compute unit runs
+//     the whole block draft, phases separated by a two-level grid barrier
+//     (48 barriers for K = 16);
+//   * stepwise: one launch per phase and position on the caller's stream.
+// Both run identical per-element arithmetic, so their outputs are bitwise
+// equal.  The verify-side prefix match is a separate small kernel.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/domino_head.h"
+#include "dh_phases.h"
+
+using namespace dh;
+
+// ============================================================================
+// kernels
+// ============================================================================
+
+__global__ __launch_bounds__(256) void k_clear_state(unsigned *bar, unsigned *flags)
+{
+    for (int i = threadIdx.x; i < BAR_WORDS; i += blockDim.x)
+        bar[i] = 0u;
+    if (threadIdx.x == 0)
+        *flags = 0u;
+}
+
+template <typename WT, int LPR, int NL>
+__global__ __launch_bounds__(NT) void k_persistent(Params p)
+{
+    extern __shared__ float smem[];
+    const int blk = blockIdx.x, nblk = gridDim.x;
+    unsigned gen = 0;
+    if (threadIdx.x == 0)
+        gen = barrier_gen_init(p.bar);
+    if (blk == 0)
+        prologue_bookkeeping(p);
+    phase_ah<WT>(p, blk, nblk, smem);
+    phase_gru<WT>(p, blk, nblk, 0, smem);
+    if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+        return;
+    for (int pos = 0; pos < p.K; ++pos) {
+        phase_u<WT>(p, blk, nblk, pos, smem);
+        if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+            return;
+        phase_w2<WT, LPR, NL>(p, blk, nblk, pos, smem);
+        if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+            return;
+        if (pos + 1 < p.K) {
+            phase_gru<WT>(p, blk, nblk, pos + 1, smem);
+            if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+                return;
+        }
+    }
+    if (blk == 0)
+        write_tokens(p, p.K - 1);
+}
+
+template <typename WT>
+__global__ __launch_bounds__(NT) void k_step_prologue(Params p)
+{
+    extern __shared__ float smem[];
+    if (blockIdx.x == 0)
+        prologue_bookkeeping(p);
+    phase_ah<WT>(p, blockIdx.x, gridDim.x, smem);
+    phase_gru<WT>(p, blockIdx.x, gridDim.x, 0, smem);
+}
+
+template <typename WT>
+__global__ __launch_bounds__(NT) void k_step_u(Params p, int pos)
+{
+    extern __shared__ float smem[];
+    phase_u<WT>(p, blockIdx.x, gridDim.x, pos, smem);
+}
+
+template <typename WT, int LPR, int NL>
+__global__ __launch_bounds__(NT) void k_step_w2(Params p, int pos)
+{
+    extern __shared__ float smem[];
+    phase_w2<WT, LPR, NL>(p, blockIdx.x, gridDim.x, pos, smem);
+}
+
+template <typename WT>
+__global__ __launch_bounds__(NT) void k_step_gru(Params p, int q)
+{
+    extern __shared__ float smem[];
+    phase_gru<WT>(p, blockIdx.x, gridDim.x, q, smem);
+}
+
+__global__ __launch_bounds__(NT) void k_step_final(Params p)
+{
+    write_tokens(p, p.K - 1);
+}
+
+// Verify-side accept length: one thread per row.
+__global__ __launch_bounds__(256) void k_accept_len(int B, int K, const int *__restrict__ draft,
+                                                    const int *__restrict__ target, int *__restrict__ out)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B)
+        return;
+    const int *d = draft + static_cast<size_t>(b) * K;
+    const int *t = target + static_cast<size_t>(b) * K;
+    int j = 0;
+    while (j < K && d[j] == t[j])
+        ++j;
+    out[b] = j;
+}
+
+// ============================================================================
+// host side
+// ============================================================================
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(DOMINO_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(call, what)                 \
+    do {                                    \
+        hipError_t e_ = (call);             \
+        if (e_ != hipSuccess)               \
+            return hip_fail(e_, what);      \
+    } while (0)
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Layout {
+    size_t bar, flags, keys, A_H, S_buf, u_buf, total;
+};
+
+Layout layout_of(const domino_head_config &c)
+{
+    Layout L{};
+    size_t off = 0;
+    L.bar = off;
+    off = align_up(off + sizeof(unsigned) * BAR_WORDS);
+    L.flags = off;
+    off = align_up(off + 64);
+    L.keys = off;
+    off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(c.K) * NG * c.max_batch);
+    L.A_H = off;
+    off = align_up(off + sizeof(float) * static_cast<size_t>(c.max_batch) * c.K * c.r);
+    L.S_buf = off;
+    off = align_up(off + sizeof(float) * 2 * static_cast<size_t>(c.max_batch) * c.h);
+    L.u_buf = off;
+    off = align_up(off + sizeof(float) * static_cast<size_t>(c.max_batch) * c.r);
+    L.total = off;
+    return L;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int validate_config(const domino_head_config *c)
+{
+    if (!c)
+        return fail(DOMINO_EINVAL, "config is NULL");
+    if (c->wdtype != DOMINO_F32 && c->wdtype != DOMINO_BF16)
+        return fail(DOMINO_EUNSUPPORTED, "wdtype %d is neither DOMINO_F32 nor DOMINO_BF16", c->wdtype);
+    if (c->K < 1 || c->K > MAXK)
+        return fail(DOMINO_EINVAL, "K=%d outside [1, %d]", c->K, MAXK);
+    if (c->max_batch < 1 || c->max_batch > 1024)
+        return fail(DOMINO_EINVAL, "max_batch=%d outside [1, 1024]", c->max_batch);
+    if (c->V < 1)
+        return fail(DOMINO_EINVAL, "V=%d < 1", c->V);
+    if (c->d < 8 || c->d % 8 || c->h < 8 || c->h % 8 || c->h > 4096)
+        return fail(DOMINO_EUNSUPPORTED, "d=%d and h=%d must be positive multiples of 8 (h <= 4096)", c->d, c->h);
+    const int epc = c->wdtype == DOMINO_BF16 ? 8 : 4;
+    if (c->r < epc || c->r % epc || !pow2(c->r / epc) || c->r / epc > 128 || c->r > 1024)
+        return fail(DOMINO_EUNSUPPORTED, "r=%d: r/%d must be a power of two <= 128 and r <= 1024", c->r, epc);
+    const void *ptrs[] = {c->W1, c->W2, c->W_ih, c->W_hh, c->E};
+    const char *names[] = {"W1", "W2", "W_ih", "W_hh", "E"};
+    for (int i = 0; i < 5; ++i) {
+        if (!ptrs[i])
+            return fail(DOMINO_EINVAL, "%s is NULL", names[i]);
+        if (!aligned16(ptrs[i]))
+            return fail(DOMINO_EINVAL, "%s is not 16-byte aligned", names[i]);
+    }
+    if (c->flags & ~(DOMINO_EXEC_PERSISTENT | DOMINO_EXEC_STEPWISE))
+        return fail(DOMINO_EINVAL, "unknown flags 0x%x", c->flags);
+    if ((c->flags & DOMINO_EXEC_PERSISTENT) && (c->flags & DOMINO_EXEC_STEPWISE))
+        return fail(DOMINO_EINVAL, "flags ask for both persistent and stepwise execution");
+    return DOMINO_OK;
+}
+
+// ---- kernel table -------------------------------------------------------------
+
+struct Kernels {
+    const void *persistent;
+    const void *w2;
+    const void *prologue, *u, *gru;
+};
+
+template <typename WT, int LPR, int NL>
+Kernels kernels_for()
+{
+    return Kernels{reinterpret_cast<const void *>(&k_persistent<WT, LPR, NL>),
+                   reinterpret_cast<const void *>(&k_step_w2<WT, LPR, NL>),
+                   reinterpret_cast<const void *>(&k_step_prologue<WT>),
+                   reinterpret_cast<const void *>(&k_step_u<WT>), reinterpret_cast<const void *>(&k_step_gru<WT>)};
+}
+
+template <typename WT>
+Kernels pick_lpr(int nchunks)
+{
+    switch (nchunks) {
+    case 1: return kernels_for<WT, 1, 1>();
+    case 2: return kernels_for<WT, 2, 1>();
+    case 4: return kernels_for<WT, 4, 1>();
+    case 8: return kernels_for<WT, 8, 1>();
+    case 16: return kernels_for<WT, 8, 2>();
+    case 32: return kernels_for<WT, 8, 4>();
+    case 64: return kernels_for<WT, 8, 8>();
+    default: return kernels_for<WT, 8, 16>();  // 128
+    }
+}
+
+Kernels pick_kernels(const domino_head_config &c)
+{
+    if (c.wdtype == DOMINO_BF16)
+        return pick_lpr<bf16s>(c.r / 8);
+    return pick_lpr<float>(c.r / 4);
+}
+
+}  // namespace
+
+struct domino_head {
+    domino_head_config cfg;
+    char *ws;
+    size_t ws_bytes;
+    Layout L;
+    Kernels kern;
+    int device;
+    int cus;
+    int persist_grid;      // blocks of the persistent launch (0: not co-resident)
+    size_t persist_smem;
+    bool state_ready;      // barrier words and flags cleared on the device
+    hipStream_t last_stream;
+    unsigned spin_limit;
+};
+
+extern "C" {
+
+const char *domino_last_error(void) { return g_err.c_str(); }
+
+int domino_head_workspace_size(const domino_head_config *cfg, size_t *bytes)
+{
+    int rc = validate_config(cfg);
+    if (rc)
+        return rc;
+    if (!bytes)
+        return fail(DOMINO_EINVAL, "bytes is NULL");
+    *bytes = layout_of(*cfg).total;
+    return DOMINO_OK;
+}
+
+int domino_head_param_count(const domino_head_config *cfg, int64_t *n)
+{
+    if (!cfg || !n)
+        return fail(DOMINO_EINVAL, "NULL argument");
+    const int64_t d = cfg->d, h = cfg->h, r = cfg->r, V = cfg->V;
+    int64_t c = r * (d + h) + V * r + 3 * h * d + 3 * h * h;
+    if (cfg->b_ih)
+        c += 3 * h;
+    if (cfg->b_hh)
+        c += 3 * h;
+    *n = c;
+    return DOMINO_OK;
+}
+
+int domino_head_create(const domino_head_config *cfg, void *workspace, size_t workspace_bytes, domino_head_t *out)
+{
+    int rc = validate_config(cfg);
+    if (rc)
+        return rc;
+    if (!out)
+        return fail(DOMINO_EINVAL, "out is NULL");
+    const Layout L = layout_of(*cfg);
+    if (!workspace)
+        return fail(DOMINO_EWORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % ALIGN)
+        return fail(DOMINO_EWORKSPACE, "workspace is not %zu-byte aligned", ALIGN);
+    if (workspace_bytes < L.total)
+        return fail(DOMINO_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    int cus = 0;
+    HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "hipDeviceGetAttribute");
+    domino_head *hd = new domino_head{};
+    hd->cfg = *cfg;
+    hd->ws = static_cast<char *>(workspace);
+    hd->ws_bytes = workspace_bytes;
+    hd->L = L;
+    hd->kern = pick_kernels(*cfg);
+    hd->device = dev;
+    hd->cus = cus;
+    hd->state_ready = false;
+    hd->last_stream = nullptr;
+    hd->spin_limit = 1u << 22;
+    if (const char *s = std::getenv("DOMINO_BARRIER_SPIN_LIMIT"))
+        hd->spin_limit = static_cast<unsigned>(std::strtoul(s, nullptr, 10));
+    // persistent launch: one block per compute unit, all co-resident
+    const int rows_cap = (cfg->V + cus - 1) / cus;
+    hd->persist_smem = sizeof(float) * smem_floats(cfg->r, rows_cap);
+    int per_cu = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, hd->kern.persistent, NT, hd->persist_smem);
+    hd->persist_grid = (e == hipSuccess && per_cu >= 1) ? cus : 0;
+    *out = hd;
+    return DOMINO_OK;
+}
+
+void domino_head_destroy(domino_head_t hd) { delete hd; }
+
+static Params make_params(domino_head_t hd, int B, const void *H, const float *L_base, const int32_t *last_tok,
+                          const int32_t *teacher, const float *S_init, int32_t *tokens, float *L_final, float *S_out,
+                          float *u_out)
+{
+    const domino_head_config &c = hd->cfg;
+    Params p{};
+    p.d = c.d;
+    p.h = c.h;
+    p.r = c.r;
+    p.V = c.V;
+    p.K = c.K;
+    p.B = B;
+    p.maxB = c.max_batch;
+    p.W1 = c.W1;
+    p.W2 = c.W2;
+    p.W_ih = c.W_ih;
+    p.W_hh = c.W_hh;
+    p.b_ih = c.b_ih;
+    p.b_hh = c.b_hh;
+    p.E = c.E;
+    p.H = H;
+    p.L_base = L_base;
+    p.last_tok = last_tok;
+    p.teacher = teacher;
+    p.S_init = S_init;
+    p.tokens = tokens;
+    p.L_final = L_final;
+    p.S_out = S_out;
+    p.u_out = u_out;
+    p.A_H = reinterpret_cast<float *>(hd->ws + hd->L.A_H);
+    p.S_buf = reinterpret_cast<float *>(hd->ws + hd->L.S_buf);
+    p.u_buf = reinterpret_cast<float *>(hd->ws + hd->L.u_buf);
+    p.keys = reinterpret_cast<uint64_t *>(hd->ws + hd->L.keys);
+    p.bar = reinterpret_cast<unsigned *>(hd->ws + hd->L.bar);
+    p.flags = reinterpret_cast<unsigned *>(hd->ws + hd->L.flags);
+    p.spin_limit = hd->spin_limit;
+    return p;
+}
+
+static int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L_base, const int32_t *last_tok,
+                      const int32_t *teacher, const float *S_init, int32_t *tokens, float *L_final, float *S_out,
+                      float *u_out, void *stream)
+{
+    if (!hd)
+        return fail(DOMINO_EINVAL, "handle is NULL");
+    const domino_head_config &c = hd->cfg;
+    if (B < 1 || B > c.max_batch)
+        return fail(DOMINO_EINVAL, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
+    const void *req[] = {H, L_base, last_tok, tokens};
+    const char *req_names[] = {"H", "L_base", "last_tok", "tokens"};
+    for (int i = 0; i < 4; ++i) {
+        if (!req[i])
+            return fail(DOMINO_EINVAL, "%s is NULL", req_names[i]);
+        if (!aligned16(req[i]))
+            return fail(DOMINO_EINVAL, "%s is not 16-byte aligned", req_names[i]);
+    }
+    const void *opt[] = {teacher, S_init, L_final, S_out, u_out};
+    const char *opt_names[] = {"teacher", "S_init", "L_final", "S_out", "u_out"};
+    for (int i = 0; i < 5; ++i)
+        if (opt[i] && !aligned16(opt[i]))
+            return fail(DOMINO_EINVAL, "%s is not 16-byte aligned", opt_names[i]);
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    if (dev != hd->device)
+        return fail(DOMINO_EINVAL, "current device %d differs from the handle's device %d", dev, hd->device);
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!hd->state_ready) {
+        hipLaunchKernelGGL(k_clear_state, dim3(1), dim3(256), 0, st, reinterpret_cast<unsigned *>(hd->ws + hd->L.bar),
+                           reinterpret_cast<unsigned *>(hd->ws + hd->L.flags));
+        HIP_TRY(hipGetLastError(), "launch k_clear_state");
+        hd->state_ready = true;
+    }
+    Params p = make_params(hd, B, H, L_base, last_tok, teacher, S_init, tokens, L_final, S_out, u_out);
+
+    bool persistent;
+    if (c.flags & DOMINO_EXEC_PERSISTENT)
+        persistent = true;
+    else if (c.flags & DOMINO_EXEC_STEPWISE)
+        persistent = false;
+    else
+        persistent = B <= BC;
+    if (persistent && hd->persist_grid == 0) {
+        if (c.flags & DOMINO_EXEC_PERSISTENT)
+            return fail(DOMINO_EUNSUPPORTED, "persistent launch cannot keep one block per compute unit resident");
+        persistent = false;
+    }
+    hd->last_stream = st;
+    if (persistent) {
+        void *args[] = {&p};
+        HIP_TRY(hipLaunchCooperativeKernel(hd->kern.persistent, dim3(hd->persist_grid), dim3(NT), args,
+                                           static_cast<unsigned>(hd->persist_smem), st),
+                "hipLaunchCooperativeKernel(persistent)");
+        return DOMINO_OK;
+    }
+    // stepwise
+    const int cap = 4 * hd->cus;
+    const int g_pro = clampi(B * c.r > B * ((c.h + 3) / 4) ? B * c.r : B * ((c.h + 3) / 4), 1, cap);
+    const int g_u = clampi(B * ((c.r + 3) / 4), 1, cap);
+    const int g_gru = clampi(B * ((c.h + 3) / 4), 1, cap);
+    const int g_w2 = clampi((c.V + 63) / 64, 1, cap);
+    const size_t sm_small = sizeof(float) * 256;
+    const size_t sm_w2 = sizeof(float) * smem_floats(c.r, (c.V + g_w2 - 1) / g_w2);
+    {
+        void *args[] = {&p};
+        HIP_TRY(hipLaunchKernel(hd->kern.prologue, dim3(g_pro), dim3(NT), args, sm_small, st), "launch prologue");
+    }
+    for (int pos = 0; pos < c.K; ++pos) {
+        void *args[] = {&p, &pos};
+        HIP_TRY(hipLaunchKernel(hd->kern.u, dim3(g_u), dim3(NT), args, sm_small, st), "launch u");
+        HIP_TRY(hipLaunchKernel(hd->kern.w2, dim3(g_w2), dim3(NT), args, sm_w2, st), "launch w2");
+        if (pos + 1 < c.K) {
+            int q = pos + 1;
+            void *gargs[] = {&p, &q};
+            HIP_TRY(hipLaunchKernel(hd->kern.gru, dim3(g_gru), dim3(NT), gargs, sm_small, st), "launch gru");
+        }
+    }
+    {
+        void *args[] = {&p};
+        HIP_TRY(hipLaunchKernel(reinterpret_cast<const void *>(&k_step_final), dim3(1), dim3(NT), args, 0, st),
+                "launch final");
+    }
+    return DOMINO_OK;
+}
+
+int domino_accept_len(int32_t B, int32_t K, const int32_t *draft, const int32_t *target, int32_t *out_len,
+                      void *stream)
+{
+    if (B < 0)
+        return fail(DOMINO_EINVAL, "B=%d < 0", B);
+    if (K < 1 || K > MAXK)
+        return fail(DOMINO_EINVAL, "K=%d outside [1, %d]", K, MAXK);
+    if (B == 0)
+        return DOMINO_OK;
+    if (!draft || !target || !out_len)
+        return fail(DOMINO_EINVAL, "NULL pointer");
+    if (!aligned16(draft) || !aligned16(target) || !aligned16(out_len))
+        return fail(DOMINO_EINVAL, "pointers must be 16-byte aligned");
+    hipLaunchKernelGGL(k_accept_len, dim3((B + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), B, K,
+                       draft, target, out_len);
+    HIP_TRY(hipGetLastError(), "launch k_accept_len");
+    return DOMINO_OK;
+}
+
+int domino_head_check_error(domino_head_t hd, uint32_t *device_flags)
+{
+    if (!hd)
+        return fail(DOMINO_EINVAL, "handle is NULL");
+    uint32_t f = 0;
+    if (hd->state_ready) {
+        HIP_TRY(hipStreamSynchronize(hd->last_stream), "hipStreamSynchronize");
+        HIP_TRY(hipMemcpy(&f, hd->ws + hd->L.flags, sizeof f, hipMemcpyDeviceToHost), "hipMemcpy(flags)");
+        // the next draft clears barrier words and flags before it runs
+        hd->state_ready = false;
+    }
+    if (device_flags)
+        *device_flags = f;
+    if (f)
+        return fail(DOMINO_EDEVICE, "device flags 0x%x (bit0: token id outside [0,V); bit1: grid barrier timeout)", f);
+    return DOMINO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,152 @@
+/*
+ * domino_head.h -- C ABI of the MI355X (gfx950) Domino head drafting library.
+ *
+ * The Domino head (paper.oopus.info review of "Domino: Decoupling Causal
+ * Modeling from Autoregressive Drafting in Speculative Decoding", section 二,
+ * 第二步 Domino Head) turns the output of a parallel draft backbone -- hidden
+ * states H and base logits L_base for a whole block, produced in one forward
+ * pass (same section, 第一步; news.sig.ai article, section "Domino怎么做") --
+ * into a causally consistent greedy draft.  For block positions p = 0..K-1:
+ *
+ *     u_p       = SiLU(W1 [H_p ; S_p])                    (rank r, no bias)
+ *     L_final_p = L_base_p + W2 u_p                        (logit space)
+ *     t_p       = argmax_v L_final_p[v]                    (greedy decoding)
+ *     S_{p+1}   = GRU(E[x_p], S_p),  x_p = t_p or teacher[p]
+ *
+ * with S_0 = GRU(E[last_tok], S_init) (anchor step on the last confirmed
+ * token; S_init = 0 when not given).  GRU is PyTorch's GRUCell: rows of
+ * W_ih/W_hh/b_ih/b_hh in blocks (reset, update, new);
+ *     r = sig(W_ir x + b_ir + W_hr s + b_hr), z = sig(W_iz x + b_iz + W_hz s + b_hz),
+ *     n = tanh(W_in x + b_in + r * (W_hn s + b_hn)),  s' = (1 - z) * n + z * s.
+ * SiLU(a) = a * sig(a).  Ties in the argmax go to the lowest index; a NaN
+ * logit counts as larger than any number (the first NaN wins); -0 equals +0.
+ * The head state S and all accumulation are float32.
+ *
+ * Every entry point returns 0 on success or a negative DOMINO_E* code; the
+ * message of the last failure on the calling thread is domino_last_error().
+ * Device work is asynchronous and ordered on the given HIP stream (NULL =
+ * the null stream); nothing synchronizes except domino_head_check_error.
+ * All tensors are row-major and contiguous, owned by the caller, and every
+ * device pointer must be 16-byte aligned.
+ */
+#ifndef DOMINO_HEAD_H
+#define DOMINO_HEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- error codes ---- */
+#define DOMINO_OK 0
+#define DOMINO_EINVAL (-1)      /* bad argument: NULL, misaligned, B out of range, K > 16 */
+#define DOMINO_EUNSUPPORTED (-2) /* dimensions or dtype the kernels do not handle */
+#define DOMINO_EWORKSPACE (-3)  /* workspace missing or smaller than domino_head_workspace_size */
+#define DOMINO_EHIP (-4)        /* a HIP runtime call failed (message carries the HIP error) */
+#define DOMINO_EDEVICE (-5)     /* domino_head_check_error found device-side flags */
+
+/* ---- weight storage types ---- */
+#define DOMINO_F32 0
+#define DOMINO_BF16 1
+
+/* ---- device-side flags reported by domino_head_check_error ---- */
+#define DOMINO_FLAG_BAD_TOKEN 1u      /* a last_tok or used teacher id was outside [0, V) */
+#define DOMINO_FLAG_SYNC_TIMEOUT 2u   /* a grid barrier spin limit ran out; outputs invalid */
+
+/* ---- config.flags bits (execution strategy; results do not depend on them) ---- */
+#define DOMINO_EXEC_AUTO 0u        /* pick per call from B */
+#define DOMINO_EXEC_PERSISTENT 1u  /* one cooperative launch covering all K positions */
+#define DOMINO_EXEC_STEPWISE 2u    /* one launch per phase and position */
+
+/*
+ * Head configuration.  All weight pointers are DEVICE pointers, borrowed for
+ * the lifetime of the handle (never copied, never written), stored in
+ * `wdtype` (float32, or bfloat16 as raw 16-bit patterns):
+ *   W1   [r, d+h]  columns 0..d-1 multiply H_p, columns d..d+h-1 multiply S_p
+ *   W2   [V, r]
+ *   W_ih [3h, d], W_hh [3h, h]   GRU weights, row blocks (reset, update, new)
+ *   b_ih [3h], b_hh [3h]         GRU biases, NULL means zero
+ *   E    [V, d]                  token embedding table (the GRU input rows)
+ * Limits: 1 <= K <= 16; d, h multiples of 8; r a multiple of 8 for bf16
+ * (4 for float32); r <= 1024; h <= 4096; 1 <= max_batch <= 1024; V >= 1.
+ */
+typedef struct domino_head_config {
+    int32_t d, h, r, V, K, max_batch;
+    int32_t wdtype;
+    uint32_t flags;
+    const void *W1, *W2, *W_ih, *W_hh, *b_ih, *b_hh, *E;
+} domino_head_config;
+
+typedef struct domino_head *domino_head_t;
+
+/* Host only.  Bytes of device workspace a handle with this config needs. */
+int domino_head_workspace_size(const domino_head_config *cfg, size_t *bytes);
+
+/*
+ * Host only (no device work, no allocation).  Validates cfg and binds the
+ * caller-allocated device `workspace` (>= domino_head_workspace_size bytes,
+ * 256-byte aligned, not shared with another handle).  On success *out is a
+ * new handle; release it with domino_head_destroy.
+ */
+int domino_head_create(const domino_head_config *cfg, void *workspace, size_t workspace_bytes,
+                       domino_head_t *out);
+
+/*
+ * Draft one block for B rows (1 <= B <= max_batch).  Device pointers:
+ *   H        [B, K, d]  wdtype     backbone hidden states of the block
+ *   L_base   [B, K, V]  float32    backbone base logits of the block
+ *   last_tok [B]        int32      last confirmed token (anchor GRU input)
+ *   teacher  [B, K]     int32      NULL = free running; else teacher forcing:
+ *                                  teacher[b][p] replaces t_p as GRU input for
+ *                                  p <= K-2 (teacher[b][K-1] is never read)
+ *   S_init   [B, h]     float32    NULL = zero initial state
+ * Outputs (device):
+ *   tokens   [B, K]     int32      greedy draft t_0..t_{K-1}; -1 for every
+ *                                  position of a row whose last_tok or used
+ *                                  teacher id lies outside [0, V)
+ *   L_final  [B, K, V]  float32    NULL = not stored
+ *   S_out    [B, K, h]  float32    NULL = not stored; S_0..S_{K-1}
+ *   u_out    [B, K, r]  float32    NULL = not stored; u_0..u_{K-1}
+ * Outputs may not alias inputs.  One draft may be in flight per handle (the
+ * workspace is reused); calls on one handle must be ordered on one stream.
+ * Bad token ids and barrier timeouts never abort: they set device flags read
+ * by domino_head_check_error.
+ */
+int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L_base, const int32_t *last_tok,
+                      const int32_t *teacher, const float *S_init, int32_t *tokens, float *L_final, float *S_out,
+                      float *u_out, void *stream);
+
+/*
+ * Verify-side accept length (paper.oopus.info review, section 一; the
+ * researchpapers.dev summary, 关键结果: the verifier keeps the longest draft
+ * prefix that equals its own tokens).  Device pointers: draft, target [B, K]
+ * int32; out_len [B] int32 receives the first p with draft[b][p] !=
+ * target[b][p], or K when the whole row matches.  0 <= B, 1 <= K <= 16;
+ * B = 0 is a no-op.  Raw int32 comparison, asynchronous on `stream`.
+ */
+int domino_accept_len(int32_t B, int32_t K, const int32_t *draft, const int32_t *target, int32_t *out_len,
+                      void *stream);
+
+/*
+ * Synchronizes the stream of the handle's last draft, reads and clears the
+ * device flags (DOMINO_FLAG_*) into *device_flags (may be NULL) and resets
+ * the handle's barrier state.  Returns DOMINO_EDEVICE if any flag was set.
+ */
+int domino_head_check_error(domino_head_t hd, uint32_t *device_flags);
+
+/* Host only.  Parameters of the head: r(d+h) + V r + 3h d + 3h h (+ 6h if GRU biases are given). */
+int domino_head_param_count(const domino_head_config *cfg, int64_t *n);
+
+/* Releases the handle (not the workspace or the weights).  NULL is a no-op. */
+void domino_head_destroy(domino_head_t hd);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *domino_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DOMINO_HEAD_H */

@@ -1,0 +1,252 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
+
+Inputs come from the seeded generator; expected values come from the oracle
+on the same inputs.  Protocols and tolerances are in gpu_common.py.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import causal_draft_correction_amd as dca
+import domino_synth as ds
+import oracle
+from gpu_common import (GAP_TOL, compare_free_running, compare_teacher_forced, gpu_draft, log, make_head)
+
+pytestmark = pytest.mark.gpu
+
+MODES = [("persistent", dca.EXEC_PERSISTENT), ("stepwise", dca.EXEC_STEPWISE)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dca.load_library()
+
+
+def run_both_protocols(w, inp, head, S_init=None, lf_tol=2e-2, s_tol=1e-4, u_tol=1e-4, label=""):
+    o = oracle.draft(w, inp.H, inp.L_base, inp.last_tok, S_init=S_init)
+    g, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok, S_init=S_init)
+    assert flags == 0
+    div = compare_free_running(o, g, lf_tol, s_tol, u_tol)
+    # teacher forcing with the oracle's own draft isolates per-step error
+    ot = oracle.draft(w, inp.H, inp.L_base, inp.last_tok, teacher=o["tokens"], S_init=S_init)
+    gt, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok, teacher=o["tokens"], S_init=S_init)
+    assert flags == 0
+    compare_teacher_forced(ot, gt, lf_tol, s_tol, u_tol)
+    log("%s: free-running rows diverged=%d, L_final err fr=%.3g tf=%.3g, S err tf=%.3g" % (
+        label, div, np.abs(o["L_final"][:, :1] - g["L_final"][:, :1]).max(),
+        np.abs(ot["L_final"] - gt["L_final"]).max(), np.abs(ot["S"] - gt["S"]).max()))
+    return o, g
+
+
+@pytest.mark.parametrize("mode_name,mode", MODES)
+def test_tiny_fp32_head(mode_name, mode):
+    w, inp = ds.make_workload("tiny")
+    head = make_head(w, 1, mode)
+    run_both_protocols(w, inp, head, lf_tol=1e-4, label="tiny/" + mode_name)
+    S0 = np.random.default_rng(0).standard_normal((1, w.shape.h)).astype(np.float32)
+    run_both_protocols(w, inp, head, S_init=S0, lf_tol=1e-4, label="tiny+S_init/" + mode_name)
+
+
+@pytest.mark.parametrize("mode_name,mode", MODES)
+@pytest.mark.parametrize("K", [16, 5, 1])
+def test_ragged_bf16_gru_sensitive(mode_name, mode, K):
+    """V, d, h chosen so no tile or block partition divides them; GRU-sensitive
+    weights and no planted peak so that the fed-back tokens change the logits."""
+    sh = ds.HeadShape(d=520, h=136, r=64, V=5003, K=K, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 40), gru_sensitive=True)
+    inp = ds.make_inputs(sh, 3, (9, 41), sigma=0.5, peak="none")
+    head = make_head(w, 4, mode)
+    run_both_protocols(w, inp, head, label="ragged K=%d/%s" % (K, mode_name))
+
+
+def test_random_teacher_and_state_init():
+    sh = ds.HeadShape(d=256, h=128, r=32, V=3001, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 42), gru_sensitive=True)
+    inp = ds.make_inputs(sh, 2, (9, 43), sigma=0.5, peak="none")
+    y = ds.uniform_tokens((9, 44), (2, 16), sh.V)
+    S0 = np.random.default_rng(1).standard_normal((2, sh.h)).astype(np.float32)
+    for mode in (dca.EXEC_PERSISTENT, dca.EXEC_STEPWISE):
+        head = make_head(w, 2, mode)
+        o = oracle.draft(w, inp.H, inp.L_base, inp.last_tok, teacher=y, S_init=S0)
+        g, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok, teacher=y, S_init=S0)
+        assert flags == 0
+        compare_teacher_forced(o, g)
+
+
+def test_persistent_and_stepwise_are_bitwise_equal_and_deterministic():
+    sh = ds.HeadShape(d=520, h=136, r=64, V=5003, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 45), gru_sensitive=True)
+    inp = ds.make_inputs(sh, 4, (9, 46), sigma=0.5, peak="none")
+    a, _ = gpu_draft(make_head(w, 4, dca.EXEC_PERSISTENT), inp.H, inp.L_base, inp.last_tok)
+    hp = make_head(w, 4, dca.EXEC_PERSISTENT)
+    b, _ = gpu_draft(hp, inp.H, inp.L_base, inp.last_tok)
+    b2, _ = gpu_draft(hp, inp.H, inp.L_base, inp.last_tok)
+    c, _ = gpu_draft(make_head(w, 4, dca.EXEC_STEPWISE), inp.H, inp.L_base, inp.last_tok)
+    for k in ("tokens", "L_final", "S", "u"):
+        assert np.array_equal(a[k], b[k]), k
+        assert np.array_equal(b[k], b2[k]), k
+        assert np.array_equal(a[k], c[k]), k
+
+
+@pytest.mark.parametrize("mode", [dca.EXEC_PERSISTENT, dca.EXEC_STEPWISE])
+def test_batch_rows_are_independent(mode):
+    sh = ds.HeadShape(d=256, h=64, r=32, V=2000, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 47), gru_sensitive=True)
+    inp = ds.make_inputs(sh, 5, (9, 48), sigma=0.5, peak="none")
+    head = make_head(w, 5, mode)
+    full, _ = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
+    for b in (0, 3):
+        one, _ = gpu_draft(head, inp.H[b:b + 1], inp.L_base[b:b + 1], inp.last_tok[b:b + 1])
+        for k in ("tokens", "L_final", "S", "u"):
+            assert np.array_equal(one[k][0], full[k][b]), (b, k)
+
+
+@pytest.mark.parametrize("mode", [dca.EXEC_PERSISTENT, dca.EXEC_STEPWISE])
+def test_zero_W2_ties_nan_signed_zero(mode):
+    """W2 = 0: L_final must equal L_base bitwise and tokens follow numpy.argmax
+    (first index among equal maxima, first NaN wins, -0 == +0)."""
+    sh = ds.HeadShape(d=64, h=32, r=16, V=777, K=16, wdtype="f32")
+    w = ds.make_weights(sh, (9, 49))
+    w.W2 = np.zeros_like(w.W2)
+    inp = ds.make_inputs(sh, 3, (9, 50), sigma=2.0, peak="none")
+    L = inp.L_base.copy()
+    L[0, 1, 300] = L[0, 1, 30] = 100.0
+    L[0, 2, :] = -1.0
+    L[0, 2, 500] = -0.0
+    L[0, 2, 400] = 0.0
+    L[1, 3, 600] = np.nan
+    L[1, 3, 700] = np.nan
+    L[1, 3, 2] = np.inf
+    L[2, 0, :] = 5.0
+    L[2, 5, 776] = 50.0  # last index
+    g, flags = gpu_draft(make_head(w, 3, mode), inp.H, L, inp.last_tok)
+    assert flags == 0
+    assert np.array_equal(g["L_final"].view(np.uint32), L.view(np.uint32)) or np.array_equal(
+        np.nan_to_num(g["L_final"], nan=1e30), np.nan_to_num(L, nan=1e30))
+    assert np.array_equal(g["tokens"], np.argmax(L, axis=-1))
+    assert g["tokens"][0, 1] == 30 and g["tokens"][0, 2] == 400 and g["tokens"][1, 3] == 600
+    assert g["tokens"][2, 0] == 0 and g["tokens"][2, 5] == 776
+
+
+@pytest.mark.parametrize("mode", [dca.EXEC_PERSISTENT, dca.EXEC_STEPWISE])
+def test_out_of_range_tokens_flag_rows(mode):
+    sh = ds.HeadShape(d=64, h=32, r=16, V=500, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 51), gru_sensitive=True)
+    inp = ds.make_inputs(sh, 4, (9, 52), sigma=0.5, peak="none")
+    last = inp.last_tok.copy()
+    last[1] = sh.V
+    head = make_head(w, 4, mode)
+    g, flags = gpu_draft(head, inp.H, inp.L_base, last)
+    assert flags & dca.FLAG_BAD_TOKEN
+    assert np.all(g["tokens"][1] == -1)
+    o = oracle.draft(w, inp.H, inp.L_base, last)
+    assert list(o["flags"]) == [0, 1, 0, 0]
+    good = [0, 2, 3]
+    compare_free_running(o, {k: v[good] for k, v in g.items()}, orows=good)
+    # a bad teacher id in a used position; the last teacher entry is never read
+    y = ds.uniform_tokens((9, 53), (4, 16), sh.V)
+    y[2, 4] = -7
+    y[3, 15] = 10 ** 6
+    g, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok, teacher=y)
+    assert flags & dca.FLAG_BAD_TOKEN
+    assert np.all(g["tokens"][2] == -1) and np.all(g["tokens"][3] >= 0)
+    # flags were cleared by the read
+    g, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
+    assert flags == 0
+
+
+def test_barrier_timeout_is_reported_not_hung(monkeypatch):
+    """A spin limit of 0 forces every waiting block out of its first barrier:
+    the launch must end, report DOMINO_FLAG_SYNC_TIMEOUT, and the next head on
+    the same workspace state must work normally."""
+    sh = ds.HeadShape(d=64, h=32, r=16, V=500, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 54))
+    inp = ds.make_inputs(sh, 1, (9, 55))
+    monkeypatch.setenv("DOMINO_BARRIER_SPIN_LIMIT", "0")
+    head = make_head(w, 1, dca.EXEC_PERSISTENT)
+    monkeypatch.delenv("DOMINO_BARRIER_SPIN_LIMIT")
+    _, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
+    assert flags & dca.FLAG_SYNC_TIMEOUT
+    head2 = make_head(w, 1, dca.EXEC_PERSISTENT)
+    o = oracle.draft(w, inp.H, inp.L_base, inp.last_tok)
+    g, flags = gpu_draft(head2, inp.H, inp.L_base, inp.last_tok)
+    assert flags == 0
+    compare_free_running(o, g)
+
+
+def test_host_validation_of_draft_arguments():
+    sh = ds.HeadShape(d=64, h=32, r=16, V=500, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 56))
+    head = make_head(w, 2, dca.EXEC_AUTO)
+    inp = ds.make_inputs(sh, 3, (9, 57))
+    with pytest.raises(dca.DominoError) as e:
+        gpu_draft(head, inp.H, inp.L_base, inp.last_tok)  # B = 3 > max_batch = 2
+    assert e.value.code == -1
+
+
+# ------------------------------------------------------------------ full sizes
+@pytest.fixture(scope="module")
+def w8b():
+    log("generating Qwen3-8B-shaped head weights")
+    return ds.make_weights(ds.QWEN3_8B, ds.WORKLOADS["qwen3_8b_b1"].weight_key)
+
+
+@pytest.mark.slow
+def test_qwen3_4b_b1_full():
+    wl = ds.WORKLOADS["qwen3_4b_b1"]
+    w, inp = ds.make_workload("qwen3_4b_b1")
+    head = make_head(w, 1)
+    run_both_protocols(w, inp, head, label="4B B=1")
+
+
+@pytest.mark.slow
+def test_qwen3_8b_b1_full(w8b):
+    wl = ds.WORKLOADS["qwen3_8b_b1"]
+    inp = ds.make_inputs(wl.shape, 1, wl.row_key, wl.sigma, wl.peak, wl.peak_height, wl.temperature)
+    for mode in (dca.EXEC_AUTO, dca.EXEC_STEPWISE):
+        head = make_head(w8b, 1, mode)
+        run_both_protocols(w8b, inp, head, label="8B B=1 mode=%d" % mode)
+    # a uniform random teacher as well
+    y = ds.uniform_tokens((3, 2), (1, 16), wl.shape.V)
+    o = oracle.draft(w8b, inp.H, inp.L_base, inp.last_tok, teacher=y)
+    g, flags = gpu_draft(make_head(w8b, 1), inp.H, inp.L_base, inp.last_tok, teacher=y)
+    assert flags == 0
+    compare_teacher_forced(o, g)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,rows", [("qwen3_8b_b32", [0, 13, 31]), ("qwen3_8b_b256", [0, 101, 255])])
+def test_qwen3_8b_batched_sampled_rows(w8b, name, rows):
+    """Full batch on the device (the launch the benchmark times); the oracle checks sampled rows."""
+    wl = ds.WORKLOADS[name]
+    inp = ds.make_inputs(wl.shape, wl.B, wl.row_key, wl.sigma, wl.peak, wl.peak_height, wl.temperature)
+    head = make_head(w8b, wl.B)
+    g, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok, rows=rows)
+    assert flags == 0
+    sub = ds.make_inputs(wl.shape, rows, wl.row_key, wl.sigma, wl.peak, wl.peak_height, wl.temperature)
+    o = oracle.draft(w8b, sub.H, sub.L_base, sub.last_tok)
+    div = compare_free_running(o, g)
+    log("%s sampled rows %s: diverged=%d" % (name, rows, div))
+    # accept length on synthetic verifier tokens built from the oracle draft
+    tgt, k = ds.geometric_prefix_targets(o["tokens"], (4, 3), wl.shape.V)
+    got = dca.accept_len(dca.device_tensor(g["tokens"]), dca.device_tensor(tgt)).cpu().numpy()
+    assert np.array_equal(got, oracle.accept_len(g["tokens"], tgt))
+
+
+# ------------------------------------------------------------------ accept length
+@pytest.mark.parametrize("B,K", [(1, 16), (37, 16), (256, 16), (1000, 16), (300, 5), (7, 1)])
+def test_accept_len_bit_exact(B, K):
+    rng = np.random.default_rng(B * 31 + K)
+    draft = rng.integers(0, 151936, size=(B, K)).astype(np.int32)
+    tgt, k = ds.geometric_prefix_targets(draft, (8, B, K), 151936)
+    tgt[0] = draft[0]  # a full match (k = K)
+    if B > 1:
+        tgt[1, 0] = draft[1, 0] + 1  # k = 0
+    got = dca.accept_len(dca.device_tensor(draft), dca.device_tensor(tgt)).cpu().numpy()
+    ref = oracle.accept_len(draft, tgt)
+    assert np.array_equal(got, ref)
+    assert got[0] == K

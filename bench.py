@@ -25,19 +25,21 @@ def eprint(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def logical_bytes(sh, B, store_logits=False):
+def logical_bytes(sh, B, store_logits=False, fold=False):
     """Algorithmic bytes of one block draft: every operand each step reads once.
 
     Per position (K of them): W2 [V,r], the L_base slice [B,V] fp32 and the state
     columns of W1 [r,h].  Per GRU step (K of them: the anchor plus K-1 fed-back
-    tokens): W_ih [3h,d], W_hh [3h,h], the gathered embedding rows [B,d] and both
-    bias vectors.  Once per call: the H columns of W1 [r,d], H [B,K,d] and the
-    tokens [B,K].  Returns (total, w2_and_lbase).
+    tokens): W_hh [3h,h] and both bias vectors, plus the input part: W_ih [3h,d]
+    and the gathered embedding rows [B,d], or with the folded table one gathered
+    row of P [B,3h] fp32.  Once per call: the H columns of W1 [r,d], H [B,K,d] and
+    the tokens [B,K].  Returns (total, w2_and_lbase).
     """
     s = 4 if sh.wdtype == "f32" else 2
     K, V, r, h, d = sh.K, sh.V, sh.r, sh.h, sh.d
     per_pos = V * r * s + B * V * 4 + r * h * s
-    per_gru = 3 * h * d * s + 3 * h * h * s + B * d * s + 6 * h * s
+    gru_in = B * 3 * h * 4 if fold else 3 * h * d * s + B * d * s
+    per_gru = gru_in + 3 * h * h * s + 6 * h * s
     once = r * d * s + B * K * d * s + B * K * 4
     total = K * per_pos + K * per_gru + once
     if store_logits:
@@ -68,6 +70,8 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_b1")
     ap.add_argument("--mode", default="auto", choices=["auto", "persistent", "stepwise"])
     ap.add_argument("--store-logits", action="store_true")
+    ap.add_argument("--no-fold", action="store_true",
+                    help="do not precompute the folded input-gate table (GRU input GEMV every step)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -90,7 +94,12 @@ def main():
                                                                       sh.wdtype))
     w, inp = ds.make_workload(wl.name)
     mode = {"auto": dca.EXEC_AUTO, "persistent": dca.EXEC_PERSISTENT, "stepwise": dca.EXEC_STEPWISE}[args.mode]
-    head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B, exec_mode=mode)
+    fold = not args.no_fold
+    t_create = time.perf_counter()
+    head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B, exec_mode=mode,
+                          fold_embedding=fold)
+    torch.cuda.synchronize()
+    t_create = time.perf_counter() - t_create
     H = dca.device_tensor(inp.H)
     L = dca.device_tensor(inp.L_base)
     lt = dca.device_tensor(inp.last_tok)
@@ -124,7 +133,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     blocks_per_s = wl.B * args.steps / wall
 
-    total_bytes, w2l_bytes = logical_bytes(sh, wl.B, args.store_logits)
+    total_bytes, w2l_bytes = logical_bytes(sh, wl.B, args.store_logits, fold)
     achieved = total_bytes / (avg_ms * 1e-3) / 1e9
     w2l = w2l_bytes / (avg_ms * 1e-3) / 1e9
     traffic = None
@@ -152,6 +161,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "K": sh.K, "V": sh.V, "d": sh.d, "h": sh.h, "r": sh.r,
                    "weights": sh.wdtype, "exec": exec_name, "store_logits": bool(args.store_logits),
+                   "fold_embedding": fold, "create_s": t_create,
                    "kernel_avg_us": avg_ms * 1e3, "w2_lbase_GBps": w2l,
                    "w2_lbase_frac_of_hbm_peak": w2l / HBM_PEAK_GBPS},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -21,6 +21,7 @@ DOMINO_BF16 = 1
 EXEC_AUTO = 0
 EXEC_PERSISTENT = 1
 EXEC_STEPWISE = 2
+FOLD_EMBED = 4
 FLAG_BAD_TOKEN = 1
 FLAG_SYNC_TIMEOUT = 2
 
@@ -93,12 +94,16 @@ def _weight_dtype(wdtype: int):
 class DominoHead:
     """A Domino head bound to borrowed device weights.
 
+    fold_embedding: precompute the folded input-gate table P = E W_ih^T + b_ih ([V, 3h] float32 in the
+    workspace) once, so each GRU step gathers a row of P instead of a W_ih matrix-vector product.
+
     weights: dict with W1 [r,d+h], W2 [V,r], W_ih [3h,d], W_hh [3h,h], b_ih/b_hh [3h] (or None) and
     E [V,d], all contiguous CUDA tensors of one dtype (float32 or bfloat16).  The tensors must stay
     alive and unmodified while the head exists (the object keeps references).
     """
 
-    def __init__(self, weights: dict, K: int = 16, max_batch: int = 1, exec_mode: int = EXEC_AUTO):
+    def __init__(self, weights: dict, K: int = 16, max_batch: int = 1, exec_mode: int = EXEC_AUTO,
+                 fold_embedding: bool = False):
         lib = load_library()
         W1 = weights["W1"]
         wdtype = DOMINO_F32 if W1.dtype == torch.float32 else DOMINO_BF16
@@ -119,7 +124,8 @@ class DominoHead:
         self.max_batch = max_batch
         self.wdtype = wdtype
         self._weights = dict(weights)
-        self.cfg = Config(d, h, r, V, K, max_batch, wdtype, exec_mode, _ptr(W1), _ptr(weights["W2"]),
+        flags = exec_mode | (FOLD_EMBED if fold_embedding else 0)
+        self.cfg = Config(d, h, r, V, K, max_batch, wdtype, flags, _ptr(W1), _ptr(weights["W2"]),
                           _ptr(weights["W_ih"]), _ptr(weights["W_hh"]), _ptr(weights.get("b_ih")),
                           _ptr(weights.get("b_hh")), _ptr(weights["E"]))
         nbytes = ctypes.c_size_t()

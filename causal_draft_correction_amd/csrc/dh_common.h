@@ -15,7 +15,6 @@ constexpr int NG = 16;            // barrier groups = partial argmax slots per p
 constexpr int MAXK = 16;          // largest block size
 constexpr int BC = 8;             // batch rows sharing one pass over W2
 constexpr int BAR_STRIDE = 64;    // uints between barrier words (256 bytes: own cache line)
-constexpr int BAR_WORDS = (2 * NG + 1) * BAR_STRIDE;
 
 // Storage tag for bfloat16 (raw 16-bit patterns).
 struct bf16s {
@@ -164,47 +163,78 @@ __device__ inline uint64_t ld_agent_u64(const uint64_t *p)
 }
 
 // ---------------------------------------------------------------------------
-// Grid barrier for a cooperative launch.  Two levels: the blocks of group
-// g = blockIdx % NG count in on their group word; the last of a group counts
-// in on the top word; the last group leader publishes generation+1 into NG
-// per-group release words that the blocks of each group poll.  All counters
-// return to zero inside every barrier, so the words are reusable across
-// launches.  Thread 0 keeps the generation in `gen`.  A spin that exceeds
-// `spin_limit` polls sets DOMINO_FLAG_SYNC_TIMEOUT (bit 1) and returns false
-// in every thread of the block; the caller must then leave the kernel.
+// Cross-block exchange.  Values handed from one block to another inside a
+// persistent launch (activations, state products, argmax keys) are written
+// and read with agent-scope atomic accesses, which bypass the per-XCD L2
+// caches that are not coherent with each other.  The barrier below then only
+// has to order completed accesses; it needs no L2 write-back or invalidate.
 // ---------------------------------------------------------------------------
-__device__ inline unsigned *bar_group(unsigned *bar, int g) { return bar + g * BAR_STRIDE; }
-__device__ inline unsigned *bar_top(unsigned *bar) { return bar + NG * BAR_STRIDE; }
-__device__ inline unsigned *bar_gen(unsigned *bar, int g) { return bar + (NG + 1 + g) * BAR_STRIDE; }
+__device__ inline void xst(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline float xld(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Grid barrier for a cooperative launch (one block per compute unit).
+// Arrival: every thread waits for its own memory operations to complete, the
+// block syncs, and thread 0 writes the new generation into the block's own
+// arrival slot (no contended counter).  Block 0 polls all slots; when every
+// block has arrived it writes the generation into NG release words (one per
+// group of blocks, on separate cache lines) that the other blocks poll.
+// Layout of `bar` (uints): release word g at g*BAR_STRIDE, arrival slots from
+// BAR_SLOTS.  Generations only grow, so the words carry over between launches
+// and need clearing only once.  Spins are bounded: past `spin_limit` polls the
+// block sets DOMINO_FLAG_SYNC_TIMEOUT (bit 1) and grid_sync returns false in
+// every thread of that block; the caller must then leave the kernel.
+// ---------------------------------------------------------------------------
+constexpr int BAR_SLOTS = NG * BAR_STRIDE;
+constexpr int MAX_GRID = 1024;
+constexpr int BAR_WORDS_ALL = BAR_SLOTS + MAX_GRID;
+
+__device__ inline unsigned *bar_release(unsigned *bar, int g) { return bar + g * BAR_STRIDE; }
 
 __device__ inline unsigned barrier_gen_init(unsigned *bar)
 {
-    const int ngr = gridDim.x < NG ? static_cast<int>(gridDim.x) : NG;
-    return __hip_atomic_load(bar_gen(bar, blockIdx.x % ngr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(bar_release(bar, blockIdx.x % NG), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// `gen` is tracked identically by every thread of the block.
 __device__ inline bool grid_sync(unsigned *bar, unsigned &gen, unsigned spin_limit, unsigned *flags)
 {
     __shared__ int s_ok;
+    const unsigned next = gen + 1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const int nblk = static_cast<int>(gridDim.x);
-        const int ngr = nblk < NG ? nblk : NG;
-        const int g = static_cast<int>(blockIdx.x) % ngr;
-        const unsigned members = static_cast<unsigned>((nblk - g + ngr - 1) / ngr);
-        int ok = 1;
-        unsigned a = __hip_atomic_fetch_add(bar_group(bar, g), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (a == members - 1) {
-            __hip_atomic_store(bar_group(bar, g), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            unsigned a2 = __hip_atomic_fetch_add(bar_top(bar), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-            if (a2 == static_cast<unsigned>(ngr) - 1) {
-                __hip_atomic_store(bar_top(bar), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                for (int gg = 0; gg < ngr; ++gg)
-                    __hip_atomic_store(bar_gen(bar, gg), gen + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned *slots = bar + BAR_SLOTS;
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&slots[blockIdx.x], next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int ok = 1;
+    if (blockIdx.x == 0) {
+        unsigned spins = 0;
+        for (;;) {
+            int mine = 1;
+            for (int i = threadIdx.x; i < static_cast<int>(gridDim.x); i += blockDim.x)
+                if (__hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != next)
+                    mine = 0;
+            if (__syncthreads_and(mine))
+                break;
+            if (++spins > spin_limit) {
+                ok = 0;
+                break;
             }
         }
+        __builtin_amdgcn_s_waitcnt(0);
+        if (threadIdx.x < NG)
+            __hip_atomic_store(bar_release(bar, threadIdx.x), next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!ok && threadIdx.x == 0)
+            __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (threadIdx.x == 0) {
         unsigned spins = 0;
-        while (__hip_atomic_load(bar_gen(bar, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+        const unsigned *rel = bar_release(bar, blockIdx.x % NG);
+        while (__hip_atomic_load(const_cast<unsigned *>(rel), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != next) {
             if (++spins > spin_limit) {
                 __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 ok = 0;
@@ -212,11 +242,11 @@ __device__ inline bool grid_sync(unsigned *bar, unsigned &gen, unsigned spin_lim
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        gen += 1;
         s_ok = ok;
     }
+    gen = next;
     __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     return s_ok != 0;
 }
 

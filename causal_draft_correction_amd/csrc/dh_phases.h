@@ -5,13 +5,22 @@
 //
 // Method (paper.oopus.info review, section 二, 第二步 Domino Head; news.sig.ai
 // article, section "Domino怎么做"), positions p = 0..K-1:
-//   A_H[p]  = W1[:, :d] H_p                      (phase_ah, once per call)
-//   S_0     = GRU(E[last_tok], S_init)           (phase_gru, q = 0)
-//   u_p     = SiLU(A_H[p] + W1[:, d:] S_p)       (phase_u)
-//   L_p     = L_base_p + W2 u_p, t_p = argmax    (phase_w2)
-//   S_{p+1} = GRU(E[x_p], S_p)                   (phase_gru, q = p+1)
-// W1 [H_p; S_p] is split into its H and S column blocks; the H part does not
-// depend on the recurrence, so it is computed for all positions up front.
+//   u_p     = SiLU(W1 [H_p; S_p])
+//   L_p     = L_base_p + W2 u_p,  t_p = argmax L_p   (greedy)
+//   S_{p+1} = GRU(E[x_p], S_p),   x_p = t_p or the teacher token
+// with S_0 = GRU(E[last_tok], S_init).  The work is regrouped as follows; every
+// regrouping is an exact identity:
+//   * W1 [H_p; S_p] = W1_H H_p + W1_S S_p, and A_H[p] = W1_H H_p for all
+//     positions is computed once (phase_ah);
+//   * the GRU cell is split into its two affine parts, the input part
+//     g = W_ih E[x] + b_ih and the state part q = W_hh S + b_hh, plus the
+//     elementwise gate update.  q for the next step and u for the next position
+//     depend only on the new state, so both are dot products over S computed
+//     right after it (phase_state).  g is either a row of the folded table
+//     P = E W_ih^T + b_ih (gathered) or computed after the token is known
+//     (phase_g);
+//   * the elementwise update is cheap, so every block computes the whole new
+//     state for itself: S never has to cross blocks in the persistent launch.
 #pragma once
 
 #include "dh_common.h"
@@ -21,6 +30,7 @@ namespace dh {
 struct Params {
     int d, h, r, V, K, B, maxB;
     const void *W1, *W2, *W_ih, *W_hh, *b_ih, *b_hh, *E;
+    const float *P;  // folded input-gate table [V, 3h] or nullptr
     const void *H;
     const float *L_base;
     const int *last_tok, *teacher;
@@ -29,13 +39,31 @@ struct Params {
     float *L_final, *S_out, *u_out;
     // workspace
     float *A_H;      // [maxB, K, r]
-    float *S_buf;    // [2, maxB, h]
+    float *S_buf;    // [2, maxB, h]  state carried between stepwise launches
     float *u_buf;    // [maxB, r]
+    float *q_buf;    // [2, maxB, 3h] W_hh S + b_hh
+    float *g_buf;    // [maxB, 3h]    W_ih E[x] + b_ih (when not folded)
     uint64_t *keys;  // [K, NG, maxB] partial argmax keys
     unsigned *bar;   // barrier words
     unsigned *flags; // device flags
     unsigned spin_limit;
+    int persistent;  // 1: blocks keep the state in LDS between phases
 };
+
+// ---- shared-memory layout (floats) ----------------------------------------------
+// red [256] | kred [2*NWAVE] | tok [TOK_SLOTS] | u_lds [BC*r] | lbuf [BC*rows_cap] | S_lds [BC*h]
+// Every kernel allocates the prefix it uses: the small phases up to tok, the
+// W2 phase up to lbuf, phase_state up to S_lds with rows_cap = 0 in stepwise
+// launches, the persistent kernel all of it.  TOK_SLOTS covers the batch rows
+// one block touches in phase_update (NT/8 + 2 at h >= 8).
+constexpr int TOK_SLOTS = 128;
+__host__ __device__ inline int smem_off_tok() { return 256 + 2 * NWAVE; }
+__host__ __device__ inline int smem_off_u() { return 256 + 2 * NWAVE + TOK_SLOTS; }
+__host__ __device__ inline int smem_off_lbuf(int r) { return smem_off_u() + BC * r; }
+__host__ __device__ inline int smem_off_S(int r, int rows_cap) { return smem_off_lbuf(r) + BC * rows_cap; }
+__host__ __device__ inline int smem_floats_small() { return smem_off_u(); }
+__host__ __device__ inline int smem_floats_w2(int r, int rows_cap) { return smem_off_S(r, rows_cap); }
+__host__ __device__ inline int smem_floats(int r, int h, int rows_cap) { return smem_off_S(r, rows_cap) + BC * h; }
 
 // ---- token bookkeeping ------------------------------------------------------
 
@@ -84,7 +112,7 @@ __device__ inline int gru_input_token(const Params &p, int q, int b)
     return tok_ok(t, p.V) ? t : 0;
 }
 
-// Block-level side job: publish tokens[:, pos] once position pos is complete.
+// Publish tokens[:, pos] once position pos is complete (one block).
 __device__ inline void write_tokens(const Params &p, int pos)
 {
     for (int b = threadIdx.x; b < p.B; b += NT)
@@ -97,11 +125,34 @@ __device__ inline void prologue_bookkeeping(const Params &p)
     const int n = p.K * NG;
     for (int i = threadIdx.x; i < n * p.B; i += NT) {
         const int slot = i / p.B, b = i % p.B;
-        p.keys[static_cast<size_t>(slot) * p.maxB + b] = 0ull;
+        __hip_atomic_store(p.keys + static_cast<size_t>(slot) * p.maxB + b, 0ull, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
     for (int b = threadIdx.x; b < p.B; b += NT)
         if (row_bad(p, b))
             __hip_atomic_fetch_or(p.flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline float *q_slot(const Params &p, int s) { return p.q_buf + static_cast<size_t>(s & 1) * p.maxB * 3 * p.h; }
+__device__ inline float *S_slot(const Params &p, int s) { return p.S_buf + static_cast<size_t>(s & 1) * p.maxB * p.h; }
+
+// Wave-cooperative dot of one WT row (n elements from `off`) with x given by a
+// chunk loader xf(elem, float*).  Lanes take chunks lane, lane+64, ...; the
+// per-lane partials are combined with a fixed xor tree, so every lane returns
+// the same sum.
+template <typename WT, typename XF>
+__device__ inline float wave_dot(const void *W, size_t off, int n, XF xf)
+{
+    constexpr int EPC = WT16<WT>::EPC;
+    const int lane = threadIdx.x & 63;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int c = lane; c < n / EPC; c += 64) {
+        float x[EPC];
+        xf(c * EPC, x);
+        acc = dot_chunk<WT>(ld16<WT>(W, off + static_cast<size_t>(c) * EPC), x, acc);
+    }
+    return wave_sum(acc);
 }
 
 // ---- phase: A_H = W1[:, :d] H for every position ------------------------------
@@ -134,138 +185,186 @@ __device__ void phase_ah(const Params &p, int blk, int nblk, float *red)
         }
         block_sum<MAXK>(acc, red);
         if (threadIdx.x < p.K)
-            p.A_H[(static_cast<size_t>(b) * p.K + threadIdx.x) * p.r + k] = red[NWAVE * MAXK + threadIdx.x];
+            xst(&p.A_H[(static_cast<size_t>(b) * p.K + threadIdx.x) * p.r + k], red[NWAVE * MAXK + threadIdx.x]);
         __syncthreads();
     }
 }
 
-// ---- phase: GRU step producing S_q ---------------------------------------------
-// Work unit: 4 hidden units of one batch row (12 rows of W_ih, 12 of W_hh).
+// ---- phase: q for the initial state: W_hh S_init + b_hh ----------------------------
 template <typename WT>
-__device__ void phase_gru(const Params &p, int blk, int nblk, int q, float *red)
+__device__ void phase_q_init(const Params &p, int blk, int nblk)
 {
-    constexpr int EPC = WT16<WT>::EPC;
-    constexpr int UPP = 4;
-    __shared__ int s_tok;
-    const int h = p.h, d = p.d;
-    const int ngrp = (h + UPP - 1) / UPP;
-    const int ntask = p.B * ngrp;
-    const float *s_prev_all = (q == 0) ? p.S_init : p.S_buf + static_cast<size_t>((q - 1) & 1) * p.maxB * h;
-    float *s_next_all = p.S_buf + static_cast<size_t>(q & 1) * p.maxB * h;
-    if (q >= 1 && blk == 0)
-        write_tokens(p, q - 1);
-    for (int task = blk; task < ntask; task += nblk) {
-        const int b = task / ngrp, j0 = (task % ngrp) * UPP;
-        if (threadIdx.x == 0)
-            s_tok = gru_input_token(p, q, b);
+    const int h3 = 3 * p.h;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float *qo = q_slot(p, 0);
+    for (int m = blk * NWAVE + wave; m < h3; m += nblk * NWAVE) {
+        const float bias = p.b_hh ? WT16<WT>::one(p.b_hh, m) : 0.f;
+        for (int b = 0; b < p.B; ++b) {
+            float v = bias;
+            if (p.S_init) {
+                const float *s = p.S_init + static_cast<size_t>(b) * p.h;
+                v += wave_dot<WT>(p.W_hh, static_cast<size_t>(m) * p.h, p.h, [&](int e, float *x) {
+                    for (int i = 0; i < WT16<WT>::EPC; ++i)
+                        x[i] = s[e + i];
+                });
+            }
+            if (lane == 0)
+                xst(&qo[static_cast<size_t>(b) * h3 + m], v);
+        }
+    }
+}
+
+// ---- phase: g = W_ih E[x_q] + b_ih for the GRU step producing S_q (not folded) ------
+template <typename WT>
+__device__ void phase_g(const Params &p, int blk, int nblk, int q, float *smem)
+{
+    const int h3 = 3 * p.h;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int *tok = reinterpret_cast<int *>(smem + smem_off_tok());
+    for (int b0 = 0; b0 < p.B; b0 += BC) {
+        const int nb = (p.B - b0) < BC ? (p.B - b0) : BC;
         __syncthreads();
-        const int tok = s_tok;
-        const float *sp = s_prev_all ? s_prev_all + static_cast<size_t>(b) * h : nullptr;
-        float acc[UPP * 6];
-#pragma unroll
-        for (int i = 0; i < UPP * 6; ++i)
-            acc[i] = 0.f;
-        for (int c = threadIdx.x; c < d / EPC; c += NT) {
-            float x[EPC];
-            WT16<WT>::unpack(ld16<WT>(p.E, static_cast<size_t>(tok) * d + static_cast<size_t>(c) * EPC), x);
-#pragma unroll
-            for (int u = 0; u < UPP; ++u) {
-                const int j = j0 + u;
-                if (j < h) {
-#pragma unroll
-                    for (int gt = 0; gt < 3; ++gt)
-                        acc[u * 6 + gt] = dot_chunk<WT>(
-                            ld16<WT>(p.W_ih, static_cast<size_t>(gt * h + j) * d + static_cast<size_t>(c) * EPC), x,
-                            acc[u * 6 + gt]);
-                }
+        if (threadIdx.x < nb)
+            tok[threadIdx.x] = gru_input_token(p, q, b0 + threadIdx.x);
+        __syncthreads();
+        for (int m = blk * NWAVE + wave; m < h3; m += nblk * NWAVE) {
+            const float bias = p.b_ih ? WT16<WT>::one(p.b_ih, m) : 0.f;
+            for (int bb = 0; bb < nb; ++bb) {
+                const size_t eo = static_cast<size_t>(tok[bb]) * p.d;
+                const float v = bias + wave_dot<WT>(p.W_ih, static_cast<size_t>(m) * p.d, p.d, [&](int e, float *x) {
+                    WT16<WT>::unpack(ld16<WT>(p.E, eo + e), x);
+                });
+                if (lane == 0)
+                    xst(&p.g_buf[static_cast<size_t>(b0 + bb) * h3 + m], v);
             }
         }
-        if (sp) {
-            for (int c = threadIdx.x; c < h / EPC; c += NT) {
-                float s[EPC];
-                ld_f32<EPC>(sp + static_cast<size_t>(c) * EPC, s);
-#pragma unroll
-                for (int u = 0; u < UPP; ++u) {
-                    const int j = j0 + u;
-                    if (j < h) {
-#pragma unroll
-                        for (int gt = 0; gt < 3; ++gt)
-                            acc[u * 6 + 3 + gt] = dot_chunk<WT>(
-                                ld16<WT>(p.W_hh, static_cast<size_t>(gt * h + j) * h + static_cast<size_t>(c) * EPC),
-                                s, acc[u * 6 + 3 + gt]);
+    }
+}
+
+// ---- GRU gate update of one state entry ---------------------------------------------
+// S_q[b][j] from g (P row or g_buf), q_{q-1} (W_hh S_{q-1} + b_hh) and S_{q-1}[b][j].
+__device__ inline float gate_update(const Params &p, int q, int b, int j, int tokb, float sprev)
+{
+    const int h = p.h, h3 = 3 * h;
+    float gr, gz, gn;
+    if (p.P) {
+        const float *prow = p.P + static_cast<size_t>(tokb) * h3;
+        gr = prow[j];
+        gz = prow[h + j];
+        gn = prow[2 * h + j];
+    } else {
+        const float *g = p.g_buf + static_cast<size_t>(b) * h3;
+        gr = xld(&g[j]);
+        gz = xld(&g[h + j]);
+        gn = xld(&g[2 * h + j]);
+    }
+    const float *qv = q_slot(p, q) + static_cast<size_t>(b) * h3;
+    const float qr = xld(&qv[j]), qz = xld(&qv[h + j]), qn = xld(&qv[2 * h + j]);
+    const float rg = sigmoidf_(gr + qr);
+    const float zg = sigmoidf_(gz + qz);
+    const float ng = tanhf(gn + rg * qn);
+    return (1.f - zg) * ng + zg * sprev;
+}
+
+__device__ inline float state_prev(const Params &p, int q, int b, int j)
+{
+    if (q == 0)
+        return p.S_init ? p.S_init[static_cast<size_t>(b) * p.h + j] : 0.f;
+    return xld(&S_slot(p, q - 1)[static_cast<size_t>(b) * p.h + j]);
+}
+
+// ---- phase (stepwise launches): distributed gate update producing S_q -------------------
+__device__ void phase_update(const Params &p, int blk, int nblk, int q, float *smem)
+{
+    if (q >= 1 && blk == 0)
+        write_tokens(p, q - 1);
+    const int h = p.h;
+    int *tok = reinterpret_cast<int *>(smem + smem_off_tok());
+    // rows are processed in order, so a block touches few distinct rows
+    for (size_t i = static_cast<size_t>(blk) * NT; i < static_cast<size_t>(p.B) * h; i += static_cast<size_t>(nblk) * NT) {
+        const size_t e = i + threadIdx.x;
+        const int b_first = static_cast<int>(i / h);
+        const int b_last = static_cast<int>((i + NT - 1) / h) < p.B - 1 ? static_cast<int>((i + NT - 1) / h) : p.B - 1;
+        __syncthreads();
+        if (p.P && threadIdx.x <= b_last - b_first)
+            tok[threadIdx.x] = gru_input_token(p, q, b_first + threadIdx.x);
+        __syncthreads();
+        if (e < static_cast<size_t>(p.B) * h) {
+            const int b = static_cast<int>(e / h), j = static_cast<int>(e % h);
+            const float sn = gate_update(p, q, b, j, p.P ? tok[b - b_first] : 0, state_prev(p, q, b, j));
+            xst(&S_slot(p, q)[static_cast<size_t>(b) * h + j], sn);
+            if (p.S_out)
+                p.S_out[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
+        }
+    }
+}
+
+// ---- phase: dot products over S_q: u_q and q for the next step ------------------------
+// Rows m < r are W1_S rows (u_q = SiLU(A_H[q] + W1_S S_q)); rows r.. are W_hh
+// rows (W_hh S_q + b_hh, used by the next gate update).  Rows are spread over
+// the waves of the grid; each wave dots its row with S_q of every batch row.
+// In the persistent launch every block first computes all of S_q itself into
+// LDS from its own copy of S_{q-1} (the gate update is cheap), so the state
+// never crosses blocks; block 0 also publishes S_q and tokens[:, q-1].  In
+// stepwise launches S_q comes from the preceding phase_update.
+template <typename WT>
+__device__ void phase_state(const Params &p, int blk, int nblk, int q, float *smem, float *S_lds)
+{
+    const int h = p.h, h3 = 3 * h, r = p.r;
+    int *tok = reinterpret_cast<int *>(smem + smem_off_tok());
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float *qn_all = q_slot(p, q + 1);
+    if (p.persistent && q >= 1 && blk == 0)
+        write_tokens(p, q - 1);
+    for (int b0 = 0; b0 < p.B; b0 += BC) {
+        const int nb = (p.B - b0) < BC ? (p.B - b0) : BC;
+        __syncthreads();
+        if (p.persistent) {
+            if (p.P && threadIdx.x < nb)
+                tok[threadIdx.x] = gru_input_token(p, q, b0 + threadIdx.x);
+            __syncthreads();
+            for (int i = threadIdx.x; i < nb * h; i += NT) {
+                const int bb = i / h, j = i % h, b = b0 + bb;
+                const float sprev = (q == 0) ? state_prev(p, 0, b, j) : S_lds[bb * h + j];
+                const float sn = gate_update(p, q, b, j, p.P ? tok[bb] : 0, sprev);
+                S_lds[bb * h + j] = sn;  // each thread reads only the entry it writes
+                if (blk == 0) {
+                    xst(&S_slot(p, q)[static_cast<size_t>(b) * h + j], sn);
+                    if (p.S_out)
+                        p.S_out[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
+                }
+            }
+        } else {
+            for (int i = threadIdx.x; i < nb * h; i += NT)
+                S_lds[i] = xld(&S_slot(p, q)[static_cast<size_t>(b0) * h + i]);
+        }
+        __syncthreads();
+        const int R = r + h3;
+        for (int m = blk * NWAVE + wave; m < R; m += nblk * NWAVE) {
+            const bool is_u = m < r;
+            const void *W = is_u ? p.W1 : p.W_hh;
+            const size_t off = is_u ? static_cast<size_t>(m) * (p.d + h) + p.d : static_cast<size_t>(m - r) * h;
+            const float bias = (!is_u && p.b_hh) ? WT16<WT>::one(p.b_hh, m - r) : 0.f;
+            for (int bb = 0; bb < nb; ++bb) {
+                const float *s = S_lds + bb * h;
+                const float dot = wave_dot<WT>(W, off, h, [&](int e, float *x) {
+                    for (int i2 = 0; i2 < WT16<WT>::EPC; ++i2)
+                        x[i2] = s[e + i2];
+                });
+                if (lane == 0) {
+                    const int b = b0 + bb;
+                    if (is_u) {
+                        const float a = xld(&p.A_H[(static_cast<size_t>(b) * p.K + q) * r + m]) + dot;
+                        const float u = a * sigmoidf_(a);
+                        xst(&p.u_buf[static_cast<size_t>(b) * r + m], u);
+                        if (p.u_out)
+                            p.u_out[(static_cast<size_t>(b) * p.K + q) * r + m] = u;
+                    } else {
+                        xst(&qn_all[static_cast<size_t>(b) * h3 + (m - r)], dot + bias);
                     }
                 }
             }
         }
-        block_sum<UPP * 6>(acc, red);
-        if (threadIdx.x < UPP) {
-            const int j = j0 + threadIdx.x;
-            if (j < h) {
-                const float *t = red + NWAVE * UPP * 6 + threadIdx.x * 6;
-                float gr = t[0], gz = t[1], gn = t[2], qr = t[3], qz = t[4], qn = t[5];
-                if (p.b_ih) {
-                    gr += WT16<WT>::one(p.b_ih, j);
-                    gz += WT16<WT>::one(p.b_ih, h + j);
-                    gn += WT16<WT>::one(p.b_ih, 2 * h + j);
-                }
-                if (p.b_hh) {
-                    qr += WT16<WT>::one(p.b_hh, j);
-                    qz += WT16<WT>::one(p.b_hh, h + j);
-                    qn += WT16<WT>::one(p.b_hh, 2 * h + j);
-                }
-                const float rg = sigmoidf_(gr + qr);
-                const float zg = sigmoidf_(gz + qz);
-                const float ng = tanhf(gn + rg * qn);
-                const float sprev = sp ? sp[j] : 0.f;
-                const float sn = (1.f - zg) * ng + zg * sprev;
-                s_next_all[static_cast<size_t>(b) * h + j] = sn;
-                if (p.S_out)
-                    p.S_out[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// ---- phase: u_p = SiLU(A_H[p] + W1[:, d:] S_p) ---------------------------------
-template <typename WT>
-__device__ void phase_u(const Params &p, int blk, int nblk, int pos, float *red)
-{
-    constexpr int EPC = WT16<WT>::EPC;
-    constexpr int KPP = 4;
-    const int ngrp = (p.r + KPP - 1) / KPP;
-    const int ntask = p.B * ngrp;
-    const float *Sb = p.S_buf + static_cast<size_t>(pos & 1) * p.maxB * p.h;
-    for (int task = blk; task < ntask; task += nblk) {
-        const int b = task / ngrp, k0 = (task % ngrp) * KPP;
-        float acc[KPP];
-#pragma unroll
-        for (int i = 0; i < KPP; ++i)
-            acc[i] = 0.f;
-        for (int c = threadIdx.x; c < p.h / EPC; c += NT) {
-            float s[EPC];
-            ld_f32<EPC>(Sb + static_cast<size_t>(b) * p.h + static_cast<size_t>(c) * EPC, s);
-#pragma unroll
-            for (int kk = 0; kk < KPP; ++kk) {
-                const int k = k0 + kk;
-                if (k < p.r)
-                    acc[kk] = dot_chunk<WT>(
-                        ld16<WT>(p.W1, static_cast<size_t>(k) * (p.d + p.h) + p.d + static_cast<size_t>(c) * EPC), s,
-                        acc[kk]);
-            }
-        }
-        block_sum<KPP>(acc, red);
-        if (threadIdx.x < KPP) {
-            const int k = k0 + threadIdx.x;
-            if (k < p.r) {
-                const float a = p.A_H[(static_cast<size_t>(b) * p.K + pos) * p.r + k] + red[NWAVE * KPP + threadIdx.x];
-                const float u = a * sigmoidf_(a);
-                p.u_buf[static_cast<size_t>(b) * p.r + k] = u;
-                if (p.u_out)
-                    p.u_out[(static_cast<size_t>(b) * p.K + pos) * p.r + k] = u;
-            }
-        }
-        __syncthreads();
     }
 }
 
@@ -277,10 +376,6 @@ __device__ void phase_u(const Params &p, int blk, int nblk, int pos, float *red)
 // flight.  The block's dot products for up to BC batch rows go to LDS; the
 // epilogue adds L_base, stores L_final, reduces the block's argmax key and
 // folds it into the partial slot of group blk % NG with an atomic max.
-//
-// Shared memory: red (256 floats) | kred (NWAVE u64) | u_lds [BC][r] | lbuf [BC][rows_cap]
-__host__ __device__ inline int smem_floats(int r, int rows_cap) { return 256 + 2 * NWAVE + BC * (r + rows_cap); }
-
 template <typename WT, int LPR, int NL>
 struct W2Rows {
     static constexpr int RPW = 64 / LPR;  // rows per wave per group
@@ -338,8 +433,8 @@ __device__ void phase_w2(const Params &p, int blk, int nblk, int pos, float *sme
     const int n = static_cast<int>(v1 - v0);
     const int rows_cap = (p.V + nblk - 1) / nblk;
     uint64_t *kred = reinterpret_cast<uint64_t *>(smem + 256);
-    float *u_lds = smem + 256 + 2 * NWAVE;
-    float *lbuf = u_lds + BC * r;
+    float *u_lds = smem + smem_off_u();
+    float *lbuf = smem + smem_off_lbuf(r);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % LPR, rw = lane / LPR;
     const int g = blk % NG;
@@ -351,8 +446,9 @@ __device__ void phase_w2(const Params &p, int blk, int nblk, int pos, float *sme
         uint4 wa[R::UG][NL], wb[R::UG][NL];
         int base = wave * RPW;
         R::load(wa, p.W2, r, v0, n, base, rw, sub, stride);
+        __syncthreads();
         for (int i = threadIdx.x; i < nb * r; i += NT)
-            u_lds[i] = p.u_buf[static_cast<size_t>(b0) * r + i];
+            u_lds[i] = xld(&p.u_buf[static_cast<size_t>(b0) * r + i]);
         __syncthreads();
         while (base < n) {
             const int nbase = base + bstride;

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <string>
 
 #include "../../include/domino_head.h"
@@ -27,35 +28,88 @@ using namespace dh;
 
 __global__ __launch_bounds__(256) void k_clear_state(unsigned *bar, unsigned *flags)
 {
-    for (int i = threadIdx.x; i < BAR_WORDS; i += blockDim.x)
+    for (int i = threadIdx.x; i < BAR_WORDS_ALL; i += blockDim.x)
         bar[i] = 0u;
     if (threadIdx.x == 0)
         *flags = 0u;
 }
 
+// Folded input-gate table P[v][m] = b_ih[m] + sum_k E[v][k] W_ih[m][k]
+// (V x 3h, float32), a 64x64 output tile per block, 4x4 per thread.
+template <typename WT>
+__global__ __launch_bounds__(256) void k_fold(const void *E, const void *W_ih, const void *b_ih, float *P, int V,
+                                              int d, int n3)
+{
+    __shared__ float As[32][68];
+    __shared__ float Bs[32][68];
+    const int v0 = blockIdx.y * 64, m0 = blockIdx.x * 64;
+    const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < d; k0 += 32) {
+        for (int i = threadIdx.x; i < 64 * 32; i += 256) {
+            const int rr = i / 32, kk = i % 32, k = k0 + kk;
+            const int v = v0 + rr, m = m0 + rr;
+            As[kk][rr] = (v < V && k < d) ? WT16<WT>::one(E, static_cast<size_t>(v) * d + k) : 0.f;
+            Bs[kk][rr] = (m < n3 && k < d) ? WT16<WT>::one(W_ih, static_cast<size_t>(m) * d + k) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int kk = 0; kk < 32; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[i] = As[kk][ty * 4 + i];
+                b[i] = Bs[kk][tx * 4 + i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int v = v0 + ty * 4 + i, m = m0 + tx * 4 + j;
+            if (v < V && m < n3)
+                P[static_cast<size_t>(v) * n3 + m] = acc[i][j] + (b_ih ? WT16<WT>::one(b_ih, m) : 0.f);
+        }
+}
+
+// Whole block draft in one cooperative launch.  Barriers per call:
+// 2 + K + (K - 1) with the folded table, 2 + K + 2 (K - 1) without.
 template <typename WT, int LPR, int NL>
 __global__ __launch_bounds__(NT) void k_persistent(Params p)
 {
     extern __shared__ float smem[];
     const int blk = blockIdx.x, nblk = gridDim.x;
-    unsigned gen = 0;
-    if (threadIdx.x == 0)
-        gen = barrier_gen_init(p.bar);
+    float *S_lds = smem + smem_off_S(p.r, (p.V + nblk - 1) / nblk);
+    unsigned gen = barrier_gen_init(p.bar);
     if (blk == 0)
         prologue_bookkeeping(p);
     phase_ah<WT>(p, blk, nblk, smem);
-    phase_gru<WT>(p, blk, nblk, 0, smem);
+    phase_q_init<WT>(p, blk, nblk);
+    if (!p.P)
+        phase_g<WT>(p, blk, nblk, 0, smem);
+    if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+        return;
+    phase_state<WT>(p, blk, nblk, 0, smem, S_lds);
     if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
         return;
     for (int pos = 0; pos < p.K; ++pos) {
-        phase_u<WT>(p, blk, nblk, pos, smem);
-        if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
-            return;
         phase_w2<WT, LPR, NL>(p, blk, nblk, pos, smem);
         if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
             return;
         if (pos + 1 < p.K) {
-            phase_gru<WT>(p, blk, nblk, pos + 1, smem);
+            if (!p.P) {
+                phase_g<WT>(p, blk, nblk, pos + 1, smem);
+                if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+                    return;
+            }
+            phase_state<WT>(p, blk, nblk, pos + 1, smem, S_lds);
             if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
                 return;
         }
@@ -71,14 +125,22 @@ __global__ __launch_bounds__(NT) void k_step_prologue(Params p)
     if (blockIdx.x == 0)
         prologue_bookkeeping(p);
     phase_ah<WT>(p, blockIdx.x, gridDim.x, smem);
-    phase_gru<WT>(p, blockIdx.x, gridDim.x, 0, smem);
+    phase_q_init<WT>(p, blockIdx.x, gridDim.x);
+    if (!p.P)
+        phase_g<WT>(p, blockIdx.x, gridDim.x, 0, smem);
+}
+
+__global__ __launch_bounds__(NT) void k_step_update(Params p, int q)
+{
+    extern __shared__ float smem[];
+    phase_update(p, blockIdx.x, gridDim.x, q, smem);
 }
 
 template <typename WT>
-__global__ __launch_bounds__(NT) void k_step_u(Params p, int pos)
+__global__ __launch_bounds__(NT) void k_step_state(Params p, int q)
 {
     extern __shared__ float smem[];
-    phase_u<WT>(p, blockIdx.x, gridDim.x, pos, smem);
+    phase_state<WT>(p, blockIdx.x, gridDim.x, q, smem, smem + smem_off_S(p.r, 0));
 }
 
 template <typename WT, int LPR, int NL>
@@ -89,10 +151,10 @@ __global__ __launch_bounds__(NT) void k_step_w2(Params p, int pos)
 }
 
 template <typename WT>
-__global__ __launch_bounds__(NT) void k_step_gru(Params p, int q)
+__global__ __launch_bounds__(NT) void k_step_g(Params p, int q)
 {
     extern __shared__ float smem[];
-    phase_gru<WT>(p, blockIdx.x, gridDim.x, q, smem);
+    phase_g<WT>(p, blockIdx.x, gridDim.x, q, smem);
 }
 
 __global__ __launch_bounds__(NT) void k_step_final(Params p)
@@ -148,10 +210,11 @@ int hip_fail(hipError_t e, const char *what)
     } while (0)
 
 constexpr size_t ALIGN = 256;
+constexpr int W2_STEP_ROWS = 128;  // vocabulary rows per block in stepwise W2 launches
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t bar, flags, keys, A_H, S_buf, u_buf, total;
+    size_t bar, flags, keys, A_H, S_buf, u_buf, q_buf, g_buf, P, total;
 };
 
 Layout layout_of(const domino_head_config &c)
@@ -159,7 +222,7 @@ Layout layout_of(const domino_head_config &c)
     Layout L{};
     size_t off = 0;
     L.bar = off;
-    off = align_up(off + sizeof(unsigned) * BAR_WORDS);
+    off = align_up(off + sizeof(unsigned) * BAR_WORDS_ALL);
     L.flags = off;
     off = align_up(off + 64);
     L.keys = off;
@@ -170,6 +233,13 @@ Layout layout_of(const domino_head_config &c)
     off = align_up(off + sizeof(float) * 2 * static_cast<size_t>(c.max_batch) * c.h);
     L.u_buf = off;
     off = align_up(off + sizeof(float) * static_cast<size_t>(c.max_batch) * c.r);
+    L.q_buf = off;
+    off = align_up(off + sizeof(float) * 2 * static_cast<size_t>(c.max_batch) * 3 * c.h);
+    L.g_buf = off;
+    off = align_up(off + sizeof(float) * static_cast<size_t>(c.max_batch) * 3 * c.h);
+    L.P = off;
+    if (c.flags & DOMINO_FOLD_EMBED)
+        off = align_up(off + sizeof(float) * static_cast<size_t>(c.V) * 3 * c.h);
     L.total = off;
     return L;
 }
@@ -190,8 +260,8 @@ int validate_config(const domino_head_config *c)
         return fail(DOMINO_EINVAL, "max_batch=%d outside [1, 1024]", c->max_batch);
     if (c->V < 1)
         return fail(DOMINO_EINVAL, "V=%d < 1", c->V);
-    if (c->d < 8 || c->d % 8 || c->h < 8 || c->h % 8 || c->h > 4096)
-        return fail(DOMINO_EUNSUPPORTED, "d=%d and h=%d must be positive multiples of 8 (h <= 4096)", c->d, c->h);
+    if (c->d < 8 || c->d % 8 || c->h < 8 || c->h % 8 || c->h > 2048)
+        return fail(DOMINO_EUNSUPPORTED, "d=%d and h=%d must be positive multiples of 8 (h <= 2048)", c->d, c->h);
     const int epc = c->wdtype == DOMINO_BF16 ? 8 : 4;
     if (c->r < epc || c->r % epc || !pow2(c->r / epc) || c->r / epc > 128 || c->r > 1024)
         return fail(DOMINO_EUNSUPPORTED, "r=%d: r/%d must be a power of two <= 128 and r <= 1024", c->r, epc);
@@ -203,7 +273,7 @@ int validate_config(const domino_head_config *c)
         if (!aligned16(ptrs[i]))
             return fail(DOMINO_EINVAL, "%s is not 16-byte aligned", names[i]);
     }
-    if (c->flags & ~(DOMINO_EXEC_PERSISTENT | DOMINO_EXEC_STEPWISE))
+    if (c->flags & ~(DOMINO_EXEC_PERSISTENT | DOMINO_EXEC_STEPWISE | DOMINO_FOLD_EMBED))
         return fail(DOMINO_EINVAL, "unknown flags 0x%x", c->flags);
     if ((c->flags & DOMINO_EXEC_PERSISTENT) && (c->flags & DOMINO_EXEC_STEPWISE))
         return fail(DOMINO_EINVAL, "flags ask for both persistent and stepwise execution");
@@ -212,10 +282,23 @@ int validate_config(const domino_head_config *c)
 
 // ---- kernel table -------------------------------------------------------------
 
+typedef hipError_t (*FoldLaunch)(const domino_head_config &c, float *P);
+
+template <typename WT>
+hipError_t launch_fold(const domino_head_config &c, float *P)
+{
+    const int n3 = 3 * c.h;
+    dim3 grid((n3 + 63) / 64, (c.V + 63) / 64);
+    hipLaunchKernelGGL(k_fold<WT>, grid, dim3(256), 0, nullptr, c.E, c.W_ih, c.b_ih, P, c.V, c.d, n3);
+    hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : hipStreamSynchronize(nullptr);
+}
+
 struct Kernels {
     const void *persistent;
     const void *w2;
-    const void *prologue, *u, *gru;
+    const void *prologue, *state, *g;
+    FoldLaunch fold;
 };
 
 template <typename WT, int LPR, int NL>
@@ -224,7 +307,8 @@ Kernels kernels_for()
     return Kernels{reinterpret_cast<const void *>(&k_persistent<WT, LPR, NL>),
                    reinterpret_cast<const void *>(&k_step_w2<WT, LPR, NL>),
                    reinterpret_cast<const void *>(&k_step_prologue<WT>),
-                   reinterpret_cast<const void *>(&k_step_u<WT>), reinterpret_cast<const void *>(&k_step_gru<WT>)};
+                   reinterpret_cast<const void *>(&k_step_state<WT>), reinterpret_cast<const void *>(&k_step_g<WT>),
+                   &launch_fold<WT>};
 }
 
 template <typename WT>
@@ -259,7 +343,7 @@ struct domino_head {
     Kernels kern;
     int device;
     int cus;
-    int persist_grid;      // blocks of the persistent launch (0: not co-resident)
+    int persist_grid;      // blocks of the persistent launch (0: cannot be co-resident)
     size_t persist_smem;
     bool state_ready;      // barrier words and flags cleared on the device
     hipStream_t last_stream;
@@ -313,12 +397,24 @@ int domino_head_create(const domino_head_config *cfg, void *workspace, size_t wo
     HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
     int cus = 0;
     HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "hipDeviceGetAttribute");
+    const Kernels kern = pick_kernels(*cfg);
+    int lds_max = 0;
+    HIP_TRY(hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev), "hipDeviceGetAttribute");
+    // largest stepwise kernel: the W2 phase (rows_cap <= W2_STEP_ROWS) or phase_state (rows_cap = 0)
+    const size_t step_smem = sizeof(float) * std::max(smem_floats_w2(cfg->r, W2_STEP_ROWS), smem_floats(cfg->r, cfg->h, 0));
+    if (step_smem + 1024 > static_cast<size_t>(lds_max))
+        return fail(DOMINO_EUNSUPPORTED, "r=%d, h=%d need %zu bytes of LDS per block, the device has %d", cfg->r,
+                    cfg->h, step_smem, lds_max);
+    if (cfg->flags & DOMINO_FOLD_EMBED) {
+        // one-time table P = E W_ih^T + b_ih on the null stream, waited for here
+        HIP_TRY(kern.fold(*cfg, reinterpret_cast<float *>(static_cast<char *>(workspace) + L.P)), "folded gate table");
+    }
     domino_head *hd = new domino_head{};
     hd->cfg = *cfg;
     hd->ws = static_cast<char *>(workspace);
     hd->ws_bytes = workspace_bytes;
     hd->L = L;
-    hd->kern = pick_kernels(*cfg);
+    hd->kern = kern;
     hd->device = dev;
     hd->cus = cus;
     hd->state_ready = false;
@@ -328,10 +424,13 @@ int domino_head_create(const domino_head_config *cfg, void *workspace, size_t wo
         hd->spin_limit = static_cast<unsigned>(std::strtoul(s, nullptr, 10));
     // persistent launch: one block per compute unit, all co-resident
     const int rows_cap = (cfg->V + cus - 1) / cus;
-    hd->persist_smem = sizeof(float) * smem_floats(cfg->r, rows_cap);
+    hd->persist_smem = sizeof(float) * smem_floats(cfg->r, cfg->h, rows_cap);
     int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, hd->kern.persistent, NT, hd->persist_smem);
-    hd->persist_grid = (e == hipSuccess && per_cu >= 1) ? cus : 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern.persistent, NT, hd->persist_smem);
+    hd->persist_grid =
+        (e == hipSuccess && per_cu >= 1 && cus <= MAX_GRID && hd->persist_smem + 1024 <= static_cast<size_t>(lds_max))
+            ? cus
+            : 0;
     *out = hd;
     return DOMINO_OK;
 }
@@ -340,7 +439,7 @@ void domino_head_destroy(domino_head_t hd) { delete hd; }
 
 static Params make_params(domino_head_t hd, int B, const void *H, const float *L_base, const int32_t *last_tok,
                           const int32_t *teacher, const float *S_init, int32_t *tokens, float *L_final, float *S_out,
-                          float *u_out)
+                          float *u_out, bool persistent)
 {
     const domino_head_config &c = hd->cfg;
     Params p{};
@@ -358,6 +457,7 @@ static Params make_params(domino_head_t hd, int B, const void *H, const float *L
     p.b_ih = c.b_ih;
     p.b_hh = c.b_hh;
     p.E = c.E;
+    p.P = (c.flags & DOMINO_FOLD_EMBED) ? reinterpret_cast<const float *>(hd->ws + hd->L.P) : nullptr;
     p.H = H;
     p.L_base = L_base;
     p.last_tok = last_tok;
@@ -370,14 +470,15 @@ static Params make_params(domino_head_t hd, int B, const void *H, const float *L
     p.A_H = reinterpret_cast<float *>(hd->ws + hd->L.A_H);
     p.S_buf = reinterpret_cast<float *>(hd->ws + hd->L.S_buf);
     p.u_buf = reinterpret_cast<float *>(hd->ws + hd->L.u_buf);
+    p.q_buf = reinterpret_cast<float *>(hd->ws + hd->L.q_buf);
+    p.g_buf = reinterpret_cast<float *>(hd->ws + hd->L.g_buf);
     p.keys = reinterpret_cast<uint64_t *>(hd->ws + hd->L.keys);
     p.bar = reinterpret_cast<unsigned *>(hd->ws + hd->L.bar);
     p.flags = reinterpret_cast<unsigned *>(hd->ws + hd->L.flags);
     p.spin_limit = hd->spin_limit;
+    p.persistent = persistent ? 1 : 0;
     return p;
 }
-
-static int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L_base, const int32_t *last_tok,
                       const int32_t *teacher, const float *S_init, int32_t *tokens, float *L_final, float *S_out,
@@ -406,15 +507,6 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
     if (dev != hd->device)
         return fail(DOMINO_EINVAL, "current device %d differs from the handle's device %d", dev, hd->device);
 
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (!hd->state_ready) {
-        hipLaunchKernelGGL(k_clear_state, dim3(1), dim3(256), 0, st, reinterpret_cast<unsigned *>(hd->ws + hd->L.bar),
-                           reinterpret_cast<unsigned *>(hd->ws + hd->L.flags));
-        HIP_TRY(hipGetLastError(), "launch k_clear_state");
-        hd->state_ready = true;
-    }
-    Params p = make_params(hd, B, H, L_base, last_tok, teacher, S_init, tokens, L_final, S_out, u_out);
-
     bool persistent;
     if (c.flags & DOMINO_EXEC_PERSISTENT)
         persistent = true;
@@ -422,11 +514,20 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
         persistent = false;
     else
         persistent = B <= BC;
-    if (persistent && hd->persist_grid == 0) {
+    if (persistent && (hd->persist_grid == 0 || B > BC)) {
         if (c.flags & DOMINO_EXEC_PERSISTENT)
-            return fail(DOMINO_EUNSUPPORTED, "persistent launch cannot keep one block per compute unit resident");
+            return fail(DOMINO_EUNSUPPORTED, "persistent launch needs B <= %d and one resident block per compute unit",
+                        BC);
         persistent = false;
     }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!hd->state_ready) {
+        hipLaunchKernelGGL(k_clear_state, dim3(1), dim3(256), 0, st, reinterpret_cast<unsigned *>(hd->ws + hd->L.bar),
+                           reinterpret_cast<unsigned *>(hd->ws + hd->L.flags));
+        HIP_TRY(hipGetLastError(), "launch k_clear_state");
+        hd->state_ready = true;
+    }
+    Params p = make_params(hd, B, H, L_base, last_tok, teacher, S_init, tokens, L_final, S_out, u_out, persistent);
     hd->last_stream = st;
     if (persistent) {
         void *args[] = {&p};
@@ -435,26 +536,36 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
                 "hipLaunchCooperativeKernel(persistent)");
         return DOMINO_OK;
     }
-    // stepwise
-    const int cap = 4 * hd->cus;
-    const int g_pro = clampi(B * c.r > B * ((c.h + 3) / 4) ? B * c.r : B * ((c.h + 3) / 4), 1, cap);
-    const int g_u = clampi(B * ((c.r + 3) / 4), 1, cap);
-    const int g_gru = clampi(B * ((c.h + 3) / 4), 1, cap);
-    const int g_w2 = clampi((c.V + 63) / 64, 1, cap);
-    const size_t sm_small = sizeof(float) * 256;
-    const size_t sm_w2 = sizeof(float) * smem_floats(c.r, (c.V + g_w2 - 1) / g_w2);
+    // stepwise: prologue, update(0), state(0), then per position w2 [, g], update, state
+    const int h3 = 3 * c.h;
+    const int g_pro = std::max(B * c.r, (h3 + NWAVE - 1) / NWAVE);
+    const int g_rows = (c.r + h3 + NWAVE - 1) / NWAVE;
+    const int g_g = (h3 + NWAVE - 1) / NWAVE;
+    const int g_w2 = (c.V + W2_STEP_ROWS - 1) / W2_STEP_ROWS;
+    const int g_upd = (B * c.h + NT - 1) / NT;
+    const size_t sm_small = sizeof(float) * smem_floats_small();
+    const size_t sm_w2 = sizeof(float) * smem_floats_w2(c.r, (c.V + g_w2 - 1) / g_w2);
+    const size_t sm_state = sizeof(float) * smem_floats(c.r, c.h, 0);
     {
         void *args[] = {&p};
         HIP_TRY(hipLaunchKernel(hd->kern.prologue, dim3(g_pro), dim3(NT), args, sm_small, st), "launch prologue");
+        int q = 0;
+        void *sargs[] = {&p, &q};
+        HIP_TRY(hipLaunchKernel(reinterpret_cast<const void *>(&k_step_update), dim3(g_upd), dim3(NT), sargs,
+                                sm_small, st), "launch update");
+        HIP_TRY(hipLaunchKernel(hd->kern.state, dim3(g_rows), dim3(NT), sargs, sm_state, st), "launch state");
     }
     for (int pos = 0; pos < c.K; ++pos) {
         void *args[] = {&p, &pos};
-        HIP_TRY(hipLaunchKernel(hd->kern.u, dim3(g_u), dim3(NT), args, sm_small, st), "launch u");
         HIP_TRY(hipLaunchKernel(hd->kern.w2, dim3(g_w2), dim3(NT), args, sm_w2, st), "launch w2");
         if (pos + 1 < c.K) {
             int q = pos + 1;
             void *gargs[] = {&p, &q};
-            HIP_TRY(hipLaunchKernel(hd->kern.gru, dim3(g_gru), dim3(NT), gargs, sm_small, st), "launch gru");
+            if (!p.P)
+                HIP_TRY(hipLaunchKernel(hd->kern.g, dim3(g_g), dim3(NT), gargs, sm_small, st), "launch g");
+            HIP_TRY(hipLaunchKernel(reinterpret_cast<const void *>(&k_step_update), dim3(g_upd), dim3(NT), gargs,
+                                    sm_small, st), "launch update");
+            HIP_TRY(hipLaunchKernel(hd->kern.state, dim3(g_rows), dim3(NT), gargs, sm_state, st), "launch state");
         }
     }
     {

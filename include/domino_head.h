@@ -59,6 +59,9 @@ extern "C" {
 #define DOMINO_EXEC_AUTO 0u        /* pick per call from B */
 #define DOMINO_EXEC_PERSISTENT 1u  /* one cooperative launch covering all K positions */
 #define DOMINO_EXEC_STEPWISE 2u    /* one launch per phase and position */
+#define DOMINO_FOLD_EMBED 4u       /* precompute P = E W_ih^T + b_ih ([V, 3h] float32, in the workspace) at
+                                      create time, so each GRU step gathers one row of P instead of
+                                      multiplying W_ih by the embedding row (same values up to rounding) */
 
 /*
  * Head configuration.  All weight pointers are DEVICE pointers, borrowed for
@@ -69,8 +72,8 @@ extern "C" {
  *   W_ih [3h, d], W_hh [3h, h]   GRU weights, row blocks (reset, update, new)
  *   b_ih [3h], b_hh [3h]         GRU biases, NULL means zero
  *   E    [V, d]                  token embedding table (the GRU input rows)
- * Limits: 1 <= K <= 16; d, h multiples of 8; r a multiple of 8 for bf16
- * (4 for float32); r <= 1024; h <= 4096; 1 <= max_batch <= 1024; V >= 1.
+ * Limits: 1 <= K <= 16; d, h multiples of 8, h <= 2048; r/8 (bf16) or r/4
+ * (float32) a power of two, r <= 1024; 1 <= max_batch <= 1024; V >= 1.
  */
 typedef struct domino_head_config {
     int32_t d, h, r, V, K, max_batch;
@@ -85,10 +88,12 @@ typedef struct domino_head *domino_head_t;
 int domino_head_workspace_size(const domino_head_config *cfg, size_t *bytes);
 
 /*
- * Host only (no device work, no allocation).  Validates cfg and binds the
- * caller-allocated device `workspace` (>= domino_head_workspace_size bytes,
- * 256-byte aligned, not shared with another handle).  On success *out is a
- * new handle; release it with domino_head_destroy.
+ * Validates cfg and binds the caller-allocated device `workspace` (>=
+ * domino_head_workspace_size bytes, 256-byte aligned, not shared with another
+ * handle).  No allocation.  Without DOMINO_FOLD_EMBED no device work either;
+ * with it, one kernel fills the folded table on the null stream and create
+ * waits for it.  On success *out is a new handle; release it with
+ * domino_head_destroy.  The workspace state is cleared by the first draft.
  */
 int domino_head_create(const domino_head_config *cfg, void *workspace, size_t workspace_bytes,
                        domino_head_t *out);

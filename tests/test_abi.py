@@ -74,6 +74,14 @@ def test_config_validation_codes(kw, code):
     assert last_error() != ""
 
 
+def test_fold_flag_adds_the_gate_table_to_the_workspace():
+    rc, plain = ws_size(cfg(V=1000, h=32))
+    rc2, folded = ws_size(cfg(V=1000, h=32, flags=dca.FOLD_EMBED))
+    assert rc == rc2 == 0
+    assert folded - plain >= 1000 * 3 * 32 * 4
+    assert ws_size(cfg(flags=dca.FOLD_EMBED | dca.EXEC_PERSISTENT))[0] == 0
+
+
 def test_param_count_closed_form():
     lib = dca.load_library()
     n = ctypes.c_int64()

@@ -42,62 +42,67 @@ def run_both_protocols(w, inp, head, S_init=None, lf_tol=2e-2, s_tol=1e-4, u_tol
     return o, g
 
 
+@pytest.mark.parametrize("fold", [False, True])
 @pytest.mark.parametrize("mode_name,mode", MODES)
-def test_tiny_fp32_head(mode_name, mode):
+def test_tiny_fp32_head(mode_name, mode, fold):
     w, inp = ds.make_workload("tiny")
-    head = make_head(w, 1, mode)
-    run_both_protocols(w, inp, head, lf_tol=1e-4, label="tiny/" + mode_name)
+    head = make_head(w, 1, mode, fold=fold)
+    run_both_protocols(w, inp, head, lf_tol=1e-4, label="tiny/%s/fold=%d" % (mode_name, fold))
     S0 = np.random.default_rng(0).standard_normal((1, w.shape.h)).astype(np.float32)
-    run_both_protocols(w, inp, head, S_init=S0, lf_tol=1e-4, label="tiny+S_init/" + mode_name)
+    run_both_protocols(w, inp, head, S_init=S0, lf_tol=1e-4, label="tiny+S_init/%s/fold=%d" % (mode_name, fold))
 
 
+@pytest.mark.parametrize("fold", [False, True])
 @pytest.mark.parametrize("mode_name,mode", MODES)
 @pytest.mark.parametrize("K", [16, 5, 1])
-def test_ragged_bf16_gru_sensitive(mode_name, mode, K):
+def test_ragged_bf16_gru_sensitive(mode_name, mode, K, fold):
     """V, d, h chosen so no tile or block partition divides them; GRU-sensitive
     weights and no planted peak so that the fed-back tokens change the logits."""
     sh = ds.HeadShape(d=520, h=136, r=64, V=5003, K=K, wdtype="bf16")
     w = ds.make_weights(sh, (9, 40), gru_sensitive=True)
     inp = ds.make_inputs(sh, 3, (9, 41), sigma=0.5, peak="none")
-    head = make_head(w, 4, mode)
-    run_both_protocols(w, inp, head, label="ragged K=%d/%s" % (K, mode_name))
+    head = make_head(w, 4, mode, fold=fold)
+    run_both_protocols(w, inp, head, label="ragged K=%d/%s/fold=%d" % (K, mode_name, fold))
 
 
-def test_random_teacher_and_state_init():
+@pytest.mark.parametrize("fold", [False, True])
+def test_random_teacher_and_state_init(fold):
     sh = ds.HeadShape(d=256, h=128, r=32, V=3001, K=16, wdtype="bf16")
     w = ds.make_weights(sh, (9, 42), gru_sensitive=True)
     inp = ds.make_inputs(sh, 2, (9, 43), sigma=0.5, peak="none")
     y = ds.uniform_tokens((9, 44), (2, 16), sh.V)
     S0 = np.random.default_rng(1).standard_normal((2, sh.h)).astype(np.float32)
     for mode in (dca.EXEC_PERSISTENT, dca.EXEC_STEPWISE):
-        head = make_head(w, 2, mode)
+        head = make_head(w, 2, mode, fold=fold)
         o = oracle.draft(w, inp.H, inp.L_base, inp.last_tok, teacher=y, S_init=S0)
         g, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok, teacher=y, S_init=S0)
         assert flags == 0
         compare_teacher_forced(o, g)
 
 
-def test_persistent_and_stepwise_are_bitwise_equal_and_deterministic():
+@pytest.mark.parametrize("fold", [False, True])
+def test_persistent_and_stepwise_are_bitwise_equal_and_deterministic(fold):
     sh = ds.HeadShape(d=520, h=136, r=64, V=5003, K=16, wdtype="bf16")
     w = ds.make_weights(sh, (9, 45), gru_sensitive=True)
     inp = ds.make_inputs(sh, 4, (9, 46), sigma=0.5, peak="none")
-    a, _ = gpu_draft(make_head(w, 4, dca.EXEC_PERSISTENT), inp.H, inp.L_base, inp.last_tok)
-    hp = make_head(w, 4, dca.EXEC_PERSISTENT)
+    a, _ = gpu_draft(make_head(w, 4, dca.EXEC_PERSISTENT, fold=fold), inp.H, inp.L_base, inp.last_tok)
+    hp = make_head(w, 4, dca.EXEC_PERSISTENT, fold=fold)
     b, _ = gpu_draft(hp, inp.H, inp.L_base, inp.last_tok)
     b2, _ = gpu_draft(hp, inp.H, inp.L_base, inp.last_tok)
-    c, _ = gpu_draft(make_head(w, 4, dca.EXEC_STEPWISE), inp.H, inp.L_base, inp.last_tok)
+    c, _ = gpu_draft(make_head(w, 4, dca.EXEC_STEPWISE, fold=fold), inp.H, inp.L_base, inp.last_tok)
     for k in ("tokens", "L_final", "S", "u"):
         assert np.array_equal(a[k], b[k]), k
         assert np.array_equal(b[k], b2[k]), k
         assert np.array_equal(a[k], c[k]), k
 
 
+@pytest.mark.parametrize("fold", [False, True])
 @pytest.mark.parametrize("mode", [dca.EXEC_PERSISTENT, dca.EXEC_STEPWISE])
-def test_batch_rows_are_independent(mode):
+def test_batch_rows_are_independent(mode, fold):
     sh = ds.HeadShape(d=256, h=64, r=32, V=2000, K=16, wdtype="bf16")
     w = ds.make_weights(sh, (9, 47), gru_sensitive=True)
     inp = ds.make_inputs(sh, 5, (9, 48), sigma=0.5, peak="none")
-    head = make_head(w, 5, mode)
+    head = make_head(w, 5, mode, fold=fold)
     full, _ = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
     for b in (0, 3):
         one, _ = gpu_draft(head, inp.H[b:b + 1], inp.L_base[b:b + 1], inp.last_tok[b:b + 1])
@@ -132,14 +137,15 @@ def test_zero_W2_ties_nan_signed_zero(mode):
     assert g["tokens"][2, 0] == 0 and g["tokens"][2, 5] == 776
 
 
+@pytest.mark.parametrize("fold", [False, True])
 @pytest.mark.parametrize("mode", [dca.EXEC_PERSISTENT, dca.EXEC_STEPWISE])
-def test_out_of_range_tokens_flag_rows(mode):
+def test_out_of_range_tokens_flag_rows(mode, fold):
     sh = ds.HeadShape(d=64, h=32, r=16, V=500, K=16, wdtype="bf16")
     w = ds.make_weights(sh, (9, 51), gru_sensitive=True)
     inp = ds.make_inputs(sh, 4, (9, 52), sigma=0.5, peak="none")
     last = inp.last_tok.copy()
     last[1] = sh.V
-    head = make_head(w, 4, mode)
+    head = make_head(w, 4, mode, fold=fold)
     g, flags = gpu_draft(head, inp.H, inp.L_base, last)
     assert flags & dca.FLAG_BAD_TOKEN
     assert np.all(g["tokens"][1] == -1)
@@ -196,24 +202,25 @@ def w8b():
 
 
 @pytest.mark.slow
-def test_qwen3_4b_b1_full():
-    wl = ds.WORKLOADS["qwen3_4b_b1"]
+@pytest.mark.parametrize("fold", [False, True])
+def test_qwen3_4b_b1_full(fold):
     w, inp = ds.make_workload("qwen3_4b_b1")
-    head = make_head(w, 1)
-    run_both_protocols(w, inp, head, label="4B B=1")
+    head = make_head(w, 1, fold=fold)
+    run_both_protocols(w, inp, head, label="4B B=1 fold=%d" % fold)
 
 
 @pytest.mark.slow
 def test_qwen3_8b_b1_full(w8b):
     wl = ds.WORKLOADS["qwen3_8b_b1"]
     inp = ds.make_inputs(wl.shape, 1, wl.row_key, wl.sigma, wl.peak, wl.peak_height, wl.temperature)
-    for mode in (dca.EXEC_AUTO, dca.EXEC_STEPWISE):
-        head = make_head(w8b, 1, mode)
-        run_both_protocols(w8b, inp, head, label="8B B=1 mode=%d" % mode)
+    for mode, fold in ((dca.EXEC_AUTO, True), (dca.EXEC_AUTO, False), (dca.EXEC_STEPWISE, False)):
+        head = make_head(w8b, 1, mode, fold=fold)
+        run_both_protocols(w8b, inp, head, label="8B B=1 mode=%d fold=%d" % (mode, fold))
+        del head
     # a uniform random teacher as well
     y = ds.uniform_tokens((3, 2), (1, 16), wl.shape.V)
     o = oracle.draft(w8b, inp.H, inp.L_base, inp.last_tok, teacher=y)
-    g, flags = gpu_draft(make_head(w8b, 1), inp.H, inp.L_base, inp.last_tok, teacher=y)
+    g, flags = gpu_draft(make_head(w8b, 1, fold=True), inp.H, inp.L_base, inp.last_tok, teacher=y)
     assert flags == 0
     compare_teacher_forced(o, g)
 

@@ -250,4 +250,122 @@ __device__ inline bool grid_sync(unsigned *bar, unsigned &gen, unsigned spin_lim
     return s_ok != 0;
 }
 
+// ---------------------------------------------------------------------------
+// Barrier that also reduces the greedy argmax (persistent launch, V <= 2^18).
+// Each block arrives by storing, for each of its nb batch rows, its local
+// argmax key into its own 64-bit arrival word, with the 14 spare high bits of
+// the index field replaced by the generation (an index below 2^18 leaves the
+// top 14 of its 32 bits unused).  Block 0 polls all arrival words; the poll
+// that sees every word at the new generation also holds every partial key, so
+// it reduces them directly and releases the barrier with 64-bit words
+// {generation, token} (one per batch row and group).  Every block leaves with
+// the tokens of this position in tok[0..nb).  Arrival words: aslot[blk*BC + b];
+// release words: arel[g*ASYNC_STRIDE + b].
+// ---------------------------------------------------------------------------
+constexpr int ASYNC_STRIDE = 32;  // u64 per release group (256 bytes)
+constexpr int ASYNC_WORDS = MAX_GRID * BC + NG * ASYNC_STRIDE;
+constexpr uint64_t KEY_ORD_MASK = 0xFFFFFFFF00000000ull;
+constexpr uint64_t KEY_IDX_MASK = 0x3FFFFull;
+
+__device__ inline uint64_t argmax_key18(float f, uint32_t idx)
+{
+    return (argmax_key(f, 0) & KEY_ORD_MASK) | (KEY_IDX_MASK - idx);
+}
+
+__device__ inline bool grid_argmax_sync(uint64_t *asy, unsigned &gen, const uint64_t *local_key, int nb, int *tok,
+                                        unsigned spin_limit, unsigned *flags)
+{
+    __shared__ int s_ok;
+    __shared__ uint64_t s_red[NWAVE * BC];
+    const unsigned next = gen + 1;
+    const uint64_t g14 = static_cast<uint64_t>(next & 0x3FFFu) << 18;
+    uint64_t *aslot = asy;
+    uint64_t *arel = asy + MAX_GRID * BC;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (threadIdx.x < nb) {
+        const uint64_t k = local_key[threadIdx.x];
+        __hip_atomic_store(&aslot[blockIdx.x * BC + threadIdx.x], (k & (KEY_ORD_MASK | KEY_IDX_MASK)) | g14,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    int ok = 1;
+    if (blockIdx.x == 0) {
+        const int total = static_cast<int>(gridDim.x) * nb;
+        uint64_t best[BC];
+        unsigned spins = 0;
+        for (;;) {
+            int mine = 1;
+#pragma unroll
+            for (int b = 0; b < BC; ++b)
+                best[b] = 0;
+            for (int e = threadIdx.x; e < total; e += blockDim.x) {
+                const int blk = e / nb, b = e % nb;
+                const uint64_t w = __hip_atomic_load(&aslot[blk * BC + b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (((w >> 18) & 0x3FFFu) != (next & 0x3FFFu))
+                    mine = 0;
+                const uint64_t k = w & (KEY_ORD_MASK | KEY_IDX_MASK);
+#pragma unroll
+                for (int bb = 0; bb < BC; ++bb)
+                    if (bb == b && k > best[bb])
+                        best[bb] = k;
+            }
+            if (__syncthreads_and(mine))
+                break;
+            if (++spins > spin_limit) {
+                ok = 0;
+                break;
+            }
+        }
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int b = 0; b < BC; ++b) {
+            const uint64_t m = wave_max_u64(best[b]);
+            if (lane == 0)
+                s_red[wave * BC + b] = m;
+        }
+        __syncthreads();
+        if (threadIdx.x < nb) {
+            uint64_t m = 0;
+            for (int w = 0; w < NWAVE; ++w)
+                m = s_red[w * BC + threadIdx.x] > m ? s_red[w * BC + threadIdx.x] : m;
+            const uint32_t t = m ? static_cast<uint32_t>(KEY_IDX_MASK - (m & KEY_IDX_MASK)) : 0u;
+            const uint64_t rel = (static_cast<uint64_t>(next) << 32) | t;
+            for (int g = 0; g < NG; ++g)
+                __hip_atomic_store(&arel[g * ASYNC_STRIDE + threadIdx.x], rel, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (!ok && threadIdx.x == 0)
+            __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (threadIdx.x == 0) {
+        const int g = blockIdx.x % NG;
+        unsigned spins = 0;
+        for (;;) {
+            int done = 1;
+            for (int b = 0; b < nb; ++b) {
+                const uint64_t w =
+                    __hip_atomic_load(&arel[g * ASYNC_STRIDE + b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (static_cast<unsigned>(w >> 32) != next)
+                    done = 0;
+                else
+                    tok[b] = static_cast<int>(static_cast<uint32_t>(w));
+            }
+            if (done)
+                break;
+            if (++spins > spin_limit) {
+                __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        s_ok = ok;
+    }
+    gen = next;
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return s_ok != 0;
+}
+
 }  // namespace dh

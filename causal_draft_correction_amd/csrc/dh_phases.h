@@ -45,6 +45,7 @@ struct Params {
     float *g_buf;    // [maxB, 3h]    W_ih E[x] + b_ih (when not folded)
     uint64_t *keys;  // [K, NG, maxB] partial argmax keys
     unsigned *bar;   // barrier words
+    uint64_t *asy;   // argmax barrier words
     unsigned *flags; // device flags
     unsigned spin_limit;
     int persistent;  // 1: blocks keep the state in LDS between phases
@@ -57,6 +58,7 @@ struct Params {
 // launches, the persistent kernel all of it.  TOK_SLOTS covers the batch rows
 // one block touches in phase_update (NT/8 + 2 at h >= 8).
 constexpr int TOK_SLOTS = 128;
+constexpr int ATOK_OFF = 64;  // persistent launch: barrier-delivered tokens at tok + ATOK_OFF
 __host__ __device__ inline int smem_off_tok() { return 256 + 2 * NWAVE; }
 __host__ __device__ inline int smem_off_u() { return 256 + 2 * NWAVE + TOK_SLOTS; }
 __host__ __device__ inline int smem_off_lbuf(int r) { return smem_off_u() + BC * r; }
@@ -100,7 +102,9 @@ __device__ inline int key_token(const Params &p, int pos, int b)
 
 // GRU input token producing S_q: last_tok for q = 0, else teacher[q-1] or t_{q-1}.
 // Invalid ids gather row 0; the row is reported through the flags instead.
-__device__ inline int gru_input_token(const Params &p, int q, int b)
+// `atok` (persistent launch): greedy tokens of position q-1 delivered by the
+// argmax barrier, indexed by batch row; otherwise they are read from the keys.
+__device__ inline int gru_input_token(const Params &p, int q, int b, const int *atok = nullptr)
 {
     int t;
     if (q == 0)
@@ -108,7 +112,7 @@ __device__ inline int gru_input_token(const Params &p, int q, int b)
     else if (p.teacher)
         t = p.teacher[static_cast<size_t>(b) * p.K + (q - 1)];
     else
-        t = key_token(p, q - 1, b);
+        t = atok ? atok[b] : key_token(p, q - 1, b);
     return tok_ok(t, p.V) ? t : 0;
 }
 
@@ -157,7 +161,7 @@ __device__ inline float wave_dot(const void *W, size_t off, int n, XF xf)
 
 // ---- phase: A_H = W1[:, :d] H for every position ------------------------------
 template <typename WT>
-__device__ void phase_ah(const Params &p, int blk, int nblk, float *red)
+__device__ __forceinline__ void phase_ah(const Params &p, int blk, int nblk, float *red)
 {
     constexpr int EPC = WT16<WT>::EPC;
     const int nch = p.d / EPC;
@@ -192,7 +196,7 @@ __device__ void phase_ah(const Params &p, int blk, int nblk, float *red)
 
 // ---- phase: q for the initial state: W_hh S_init + b_hh ----------------------------
 template <typename WT>
-__device__ void phase_q_init(const Params &p, int blk, int nblk)
+__device__ __forceinline__ void phase_q_init(const Params &p, int blk, int nblk)
 {
     const int h3 = 3 * p.h;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -216,7 +220,7 @@ __device__ void phase_q_init(const Params &p, int blk, int nblk)
 
 // ---- phase: g = W_ih E[x_q] + b_ih for the GRU step producing S_q (not folded) ------
 template <typename WT>
-__device__ void phase_g(const Params &p, int blk, int nblk, int q, float *smem)
+__device__ __forceinline__ void phase_g(const Params &p, int blk, int nblk, int q, float *smem, const int *atok = nullptr)
 {
     const int h3 = 3 * p.h;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -225,7 +229,7 @@ __device__ void phase_g(const Params &p, int blk, int nblk, int q, float *smem)
         const int nb = (p.B - b0) < BC ? (p.B - b0) : BC;
         __syncthreads();
         if (threadIdx.x < nb)
-            tok[threadIdx.x] = gru_input_token(p, q, b0 + threadIdx.x);
+            tok[threadIdx.x] = gru_input_token(p, q, b0 + threadIdx.x, atok ? atok + b0 : nullptr);
         __syncthreads();
         for (int m = blk * NWAVE + wave; m < h3; m += nblk * NWAVE) {
             const float bias = p.b_ih ? WT16<WT>::one(p.b_ih, m) : 0.f;
@@ -274,7 +278,7 @@ __device__ inline float state_prev(const Params &p, int q, int b, int j)
 }
 
 // ---- phase (stepwise launches): distributed gate update producing S_q -------------------
-__device__ void phase_update(const Params &p, int blk, int nblk, int q, float *smem)
+__device__ __forceinline__ void phase_update(const Params &p, int blk, int nblk, int q, float *smem)
 {
     if (q >= 1 && blk == 0)
         write_tokens(p, q - 1);
@@ -307,27 +311,144 @@ __device__ void phase_update(const Params &p, int blk, int nblk, int q, float *s
 // LDS from its own copy of S_{q-1} (the gate update is cheap), so the state
 // never crosses blocks; block 0 also publishes S_q and tokens[:, q-1].  In
 // stepwise launches S_q comes from the preceding phase_update.
+//
+// The weight rows and the A_H entries a wave needs are the same at every
+// position, so the persistent kernel copies them into LDS once per launch
+// (state_cache_load); the q values of the gate update are loaded before the
+// barrier that precedes the phase (state_prefetch).
+constexpr int SP_EL = 2;  // gate-update elements per thread whose q values are prefetched
+
+struct StatePre {
+    float qv[SP_EL][3];
+};
+
+__device__ inline int state_rows(const Params &p) { return p.r + 3 * p.h; }
+
 template <typename WT>
-__device__ void phase_state(const Params &p, int blk, int nblk, int q, float *smem, float *S_lds)
+__device__ inline size_t state_row_off(const Params &p, int m)
 {
+    return m < p.r ? static_cast<size_t>(m) * (p.d + p.h) + p.d : static_cast<size_t>(m - p.r) * p.h;
+}
+
+// Loads for phase_state(q) that depend on nothing computed after the previous
+// barrier: the q values of this thread's first gate-update elements.
+template <typename WT>
+__device__ __forceinline__ void state_prefetch(const Params &p, int q, StatePre &pre)
+{
+    const int h = p.h;
+    const int nb0 = p.B < BC ? p.B : BC;
+#pragma unroll
+    for (int e = 0; e < SP_EL; ++e) {
+        const int i = threadIdx.x + e * NT;
+        if (i < nb0 * h) {
+            const float *qv = q_slot(p, q) + static_cast<size_t>(i / h) * 3 * h;
+            const int j = i % h;
+            pre.qv[e][0] = xld(&qv[j]);
+            pre.qv[e][1] = xld(&qv[h + j]);
+            pre.qv[e][2] = xld(&qv[2 * h + j]);
+        }
+    }
+}
+
+// Rows of the state phase handled by each wave of a persistent launch, and the
+// LDS it takes to keep them: the rows (WT) plus their A_H entries for every
+// position and batch row (u rows only).
+__host__ __device__ inline int state_rows_per_wave(int r, int h, int nblk)
+{
+    return (r + 3 * h + nblk * NWAVE - 1) / (nblk * NWAVE);
+}
+__host__ __device__ inline int state_cache_floats(int r, int h, int K, int nblk, int wbytes)
+{
+    const int rpw = state_rows_per_wave(r, h, nblk);
+    return NWAVE * rpw * (h * wbytes / 4 + K * BC);
+}
+
+// Once per persistent launch, after the prologue barrier: each wave copies its
+// state rows and their A_H entries into LDS.
+template <typename WT>
+__device__ __forceinline__ void state_cache_load(const Params &p, int blk, int nblk, float *cache)
+{
+    constexpr int EPC = WT16<WT>::EPC;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int h = p.h, R = state_rows(p), rpw = state_rows_per_wave(p.r, h, nblk);
+    const int row_words = h * static_cast<int>(sizeof(WT)) / 4;
+    uint4 *wc = reinterpret_cast<uint4 *>(cache);
+    float *ac = cache + NWAVE * rpw * row_words;
+    for (int k = 0; k < rpw; ++k) {
+        const int m = blk * NWAVE + wave + k * nblk * NWAVE;
+        if (m >= R)
+            break;
+        const void *W = m < p.r ? p.W1 : p.W_hh;
+        const size_t off = state_row_off<WT>(p, m);
+        for (int ch = lane; ch < h / EPC; ch += 64)
+            wc[(wave * rpw + k) * (h / EPC) + ch] = ld16<WT>(W, off + static_cast<size_t>(ch) * EPC);
+        if (m < p.r)
+            for (int i = lane; i < p.K * p.B; i += 64) {
+                const int qq = i / p.B, b = i % p.B;
+                ac[((wave * rpw + k) * p.K + qq) * BC + b] = xld(&p.A_H[(static_cast<size_t>(b) * p.K + qq) * p.r + m]);
+            }
+    }
+}
+
+template <typename WT>
+__device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, int q, float *smem, float *S_lds,
+                                            const StatePre *pre, const float *cache, bool cached,
+                                            const int *atok = nullptr)
+{
+    constexpr int EPC = WT16<WT>::EPC;
     const int h = p.h, h3 = 3 * h, r = p.r;
     int *tok = reinterpret_cast<int *>(smem + smem_off_tok());
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     float *qn_all = q_slot(p, q + 1);
-    if (p.persistent && q >= 1 && blk == 0)
-        write_tokens(p, q - 1);
+    const int R = state_rows(p), nch = h / EPC;
     for (int b0 = 0; b0 < p.B; b0 += BC) {
         const int nb = (p.B - b0) < BC ? (p.B - b0) : BC;
         __syncthreads();
         if (p.persistent) {
             if (p.P && threadIdx.x < nb)
-                tok[threadIdx.x] = gru_input_token(p, q, b0 + threadIdx.x);
+                tok[threadIdx.x] = gru_input_token(p, q, b0 + threadIdx.x, atok ? atok + b0 : nullptr);
             __syncthreads();
-            for (int i = threadIdx.x; i < nb * h; i += NT) {
+            // the first SP_EL elements of this thread use the q values prefetched before the barrier
+#pragma unroll
+            for (int e = 0; e < SP_EL; ++e) {
+                const int i = threadIdx.x + e * NT;
+                if (i < nb * h) {
+                    const int bb = i / h, j = i % h, b = b0 + bb;
+                    const float sprev = (q == 0) ? state_prev(p, 0, b, j) : S_lds[bb * h + j];
+                    float sn;
+                    if (pre && b0 == 0) {
+                        float gr, gz, gn;
+                        if (p.P) {
+                            const float *prow = p.P + static_cast<size_t>(tok[bb]) * h3;
+                            gr = prow[j];
+                            gz = prow[h + j];
+                            gn = prow[2 * h + j];
+                        } else {
+                            const float *g = p.g_buf + static_cast<size_t>(b) * h3;
+                            gr = xld(&g[j]);
+                            gz = xld(&g[h + j]);
+                            gn = xld(&g[2 * h + j]);
+                        }
+                        const float rg = sigmoidf_(gr + pre->qv[e][0]);
+                        const float zg = sigmoidf_(gz + pre->qv[e][1]);
+                        const float ng = tanhf(gn + rg * pre->qv[e][2]);
+                        sn = (1.f - zg) * ng + zg * sprev;
+                    } else {
+                        sn = gate_update(p, q, b, j, p.P ? tok[bb] : 0, sprev);
+                    }
+                    S_lds[bb * h + j] = sn;  // each thread reads only the entry it writes
+                    if (blk == 0) {
+                        xst(&S_slot(p, q)[static_cast<size_t>(b) * h + j], sn);
+                        if (p.S_out)
+                            p.S_out[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
+                    }
+                }
+            }
+            for (int i = threadIdx.x + SP_EL * NT; i < nb * h; i += NT) {
                 const int bb = i / h, j = i % h, b = b0 + bb;
                 const float sprev = (q == 0) ? state_prev(p, 0, b, j) : S_lds[bb * h + j];
                 const float sn = gate_update(p, q, b, j, p.P ? tok[bb] : 0, sprev);
-                S_lds[bb * h + j] = sn;  // each thread reads only the entry it writes
+                S_lds[bb * h + j] = sn;
                 if (blk == 0) {
                     xst(&S_slot(p, q)[static_cast<size_t>(b) * h + j], sn);
                     if (p.S_out)
@@ -339,22 +460,41 @@ __device__ void phase_state(const Params &p, int blk, int nblk, int q, float *sm
                 S_lds[i] = xld(&S_slot(p, q)[static_cast<size_t>(b0) * h + i]);
         }
         __syncthreads();
-        const int R = r + h3;
-        for (int m = blk * NWAVE + wave; m < R; m += nblk * NWAVE) {
+        // dot rows of this wave: k-th row m = m0 + k * mstep; when `cached` (persistent
+        // launch) the row and its A_H entries come from LDS at `cache`
+        const int m0 = blk * NWAVE + wave, mstep = nblk * NWAVE;
+        const int rpw = state_rows_per_wave(r, h, nblk);
+        const uint4 *wc = reinterpret_cast<const uint4 *>(cache);
+        const float *ac = cache + NWAVE * rpw * (h * static_cast<int>(sizeof(WT)) / 4);
+#pragma unroll 1
+        for (int k = 0, m = m0; m < R; ++k, m += mstep) {
             const bool is_u = m < r;
             const void *W = is_u ? p.W1 : p.W_hh;
-            const size_t off = is_u ? static_cast<size_t>(m) * (p.d + h) + p.d : static_cast<size_t>(m - r) * h;
+            const size_t off = state_row_off<WT>(p, m);
             const float bias = (!is_u && p.b_hh) ? WT16<WT>::one(p.b_hh, m - r) : 0.f;
+            const uint4 *wrow = wc + (wave * rpw + k) * nch;
+#pragma unroll 1
             for (int bb = 0; bb < nb; ++bb) {
+                const int b = b0 + bb;
+                float ah = 0.f;
+                if (is_u)
+                    ah = cached ? ac[((wave * rpw + k) * p.K + q) * BC + b]
+                                : xld(&p.A_H[(static_cast<size_t>(b) * p.K + q) * r + m]);
                 const float *s = S_lds + bb * h;
-                const float dot = wave_dot<WT>(W, off, h, [&](int e, float *x) {
-                    for (int i2 = 0; i2 < WT16<WT>::EPC; ++i2)
-                        x[i2] = s[e + i2];
-                });
+                float acc = 0.f;
+#pragma unroll 2
+                for (int ch = lane; ch < nch; ch += 64) {
+                    float x[EPC];
+#pragma unroll
+                    for (int i2 = 0; i2 < EPC; ++i2)
+                        x[i2] = s[ch * EPC + i2];
+                    const uint4 wq = cached ? wrow[ch] : ld16<WT>(W, off + static_cast<size_t>(ch) * EPC);
+                    acc = dot_chunk<WT>(wq, x, acc);
+                }
+                const float dot = wave_sum(acc);
                 if (lane == 0) {
-                    const int b = b0 + bb;
                     if (is_u) {
-                        const float a = xld(&p.A_H[(static_cast<size_t>(b) * p.K + q) * r + m]) + dot;
+                        const float a = ah + dot;
                         const float u = a * sigmoidf_(a);
                         xst(&p.u_buf[static_cast<size_t>(b) * r + m], u);
                         if (p.u_out)
@@ -379,7 +519,7 @@ __device__ void phase_state(const Params &p, int blk, int nblk, int q, float *sm
 template <typename WT, int LPR, int NL>
 struct W2Rows {
     static constexpr int RPW = 64 / LPR;  // rows per wave per group
-    static constexpr int UG = 2;          // row groups per batch
+    static constexpr int UG = 1;          // row groups per batch
 
     __device__ static inline void load(uint4 (&w)[UG][NL], const void *W2, int r, long long v0, int n, int base,
                                        int rw, int sub, int stride)
@@ -423,10 +563,32 @@ struct W2Rows {
 };
 
 template <typename WT, int LPR, int NL>
-__device__ void phase_w2(const Params &p, int blk, int nblk, int pos, float *smem)
+struct W2Pre {
+    uint4 w[W2Rows<WT, LPR, NL>::UG][NL];
+};
+
+// First batch of this wave's W2 rows for position-independent reuse: the
+// persistent kernel issues it before the barrier that precedes phase_w2.
+template <typename WT, int LPR, int NL>
+__device__ __forceinline__ void w2_prefetch(const Params &p, int blk, int nblk, W2Pre<WT, LPR, NL> &pre)
+{
+    using R = W2Rows<WT, LPR, NL>;
+    const long long v0 = static_cast<long long>(p.V) * blk / nblk;
+    const int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    R::load(pre.w, p.W2, p.r, v0, n, wave * R::RPW, lane / LPR, lane % LPR, NWAVE * R::RPW);
+}
+
+// With local_keys (persistent launch), the block's argmax key of each batch row
+// goes to local_keys[bb] in LDS (18-bit index form, see grid_argmax_sync)
+// instead of the global partial slots.
+template <typename WT, int LPR, int NL>
+__device__ __forceinline__ void phase_w2(const Params &p, int blk, int nblk, int pos, float *smem, const W2Pre<WT, LPR, NL> *pre,
+                         uint64_t *local_keys)
 {
     using R = W2Rows<WT, LPR, NL>;
     constexpr int RPW = R::RPW;
+    constexpr int LB = 2;  // L_base values per thread (first batch row of the pass) loaded up front
     const int r = p.r;
     const long long v0 = static_cast<long long>(p.V) * blk / nblk;
     const long long v1 = static_cast<long long>(p.V) * (blk + 1) / nblk;
@@ -445,7 +607,21 @@ __device__ void phase_w2(const Params &p, int blk, int nblk, int pos, float *sme
         const int nb = (p.B - b0) < BC ? (p.B - b0) : BC;
         uint4 wa[R::UG][NL], wb[R::UG][NL];
         int base = wave * RPW;
-        R::load(wa, p.W2, r, v0, n, base, rw, sub, stride);
+        if (pre && b0 == 0) {
+#pragma unroll
+            for (int ug = 0; ug < R::UG; ++ug)
+#pragma unroll
+                for (int q = 0; q < NL; ++q)
+                    wa[ug][q] = pre->w[ug][q];
+        } else {
+            R::load(wa, p.W2, r, v0, n, base, rw, sub, stride);
+        }
+        float lbv[LB];
+#pragma unroll
+        for (int e = 0; e < LB; ++e) {
+            const int i = threadIdx.x + e * NT;
+            lbv[e] = i < n ? p.L_base[(static_cast<size_t>(b0) * p.K + pos) * p.V + v0 + i] : 0.f;
+        }
         __syncthreads();
         for (int i = threadIdx.x; i < nb * r; i += NT)
             u_lds[i] = xld(&p.u_buf[static_cast<size_t>(b0) * r + i]);
@@ -465,28 +641,36 @@ __device__ void phase_w2(const Params &p, int blk, int nblk, int pos, float *sme
         }
         __syncthreads();
         for (int bb = 0; bb < nb; ++bb) {
-            const int b = b0 + bb;
-            const float *lb = p.L_base + (static_cast<size_t>(b) * p.K + pos) * p.V + v0;
-            float *lf = p.L_final ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * p.V + v0 : nullptr;
-            uint64_t best = 0;
-            for (int i = threadIdx.x; i < n; i += NT) {
-                const float v = lb[i] + lbuf[bb * rows_cap + i];
-                if (lf)
-                    lf[i] = v;
-                const uint64_t key = argmax_key(v, static_cast<uint32_t>(v0 + i));
-                best = key > best ? key : best;
+            {
+                const int b = b0 + bb;
+                const float *lb = p.L_base + (static_cast<size_t>(b) * p.K + pos) * p.V + v0;
+                float *lf = p.L_final ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * p.V + v0 : nullptr;
+                uint64_t best = 0;
+                for (int i = threadIdx.x, e = 0; i < n; i += NT, ++e) {
+                    float base_logit = (bb == 0 && e == 0) ? lbv[0] : (bb == 0 && e == 1) ? lbv[1] : 0.f;
+                    if (bb != 0 || e >= LB)
+                        base_logit = lb[i];
+                    const float v = base_logit + lbuf[bb * rows_cap + i];
+                    if (lf)
+                        lf[i] = v;
+                    const uint64_t key = argmax_key(v, static_cast<uint32_t>(v0 + i));
+                    best = key > best ? key : best;
+                }
+                best = wave_max_u64(best);
+                if (lane == 0)
+                    kred[wave] = best;
+                __syncthreads();
+                if (threadIdx.x == 0) {
+                    uint64_t m = 0;
+                    for (int w = 0; w < NWAVE; ++w)
+                        m = kred[w] > m ? kred[w] : m;
+                    if (local_keys)
+                        local_keys[bb] = m ? (m & KEY_ORD_MASK) | (KEY_IDX_MASK - key_index(m)) : 0ull;
+                    else
+                        __hip_atomic_fetch_max(key_slot(p, pos, g, b), m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                __syncthreads();
             }
-            best = wave_max_u64(best);
-            if (lane == 0)
-                kred[wave] = best;
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                uint64_t m = 0;
-                for (int w = 0; w < NWAVE; ++w)
-                    m = kred[w] > m ? kred[w] : m;
-                __hip_atomic_fetch_max(key_slot(p, pos, g, b), m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            __syncthreads();
         }
     }
 }

@@ -26,10 +26,12 @@ using namespace dh;
 // kernels
 // ============================================================================
 
-__global__ __launch_bounds__(256) void k_clear_state(unsigned *bar, unsigned *flags)
+__global__ __launch_bounds__(256) void k_clear_state(unsigned *bar, uint64_t *asy, unsigned *flags)
 {
     for (int i = threadIdx.x; i < BAR_WORDS_ALL; i += blockDim.x)
         bar[i] = 0u;
+    for (int i = threadIdx.x; i < ASYNC_WORDS; i += blockDim.x)
+        asy[i] = 0ull;
     if (threadIdx.x == 0)
         *flags = 0u;
 }
@@ -80,42 +82,58 @@ __global__ __launch_bounds__(256) void k_fold(const void *E, const void *W_ih, c
 }
 
 // Whole block draft in one cooperative launch.  Barriers per call:
-// 2 + K + (K - 1) with the folded table, 2 + K + 2 (K - 1) without.
+// 2 + K + (K - 1) with the folded table, 2 + K + 2 (K - 1) without.  The
+// barrier after each W2 phase also reduces the greedy argmax.
 template <typename WT, int LPR, int NL>
 __global__ __launch_bounds__(NT) void k_persistent(Params p)
 {
     extern __shared__ float smem[];
     const int blk = blockIdx.x, nblk = gridDim.x;
     float *S_lds = smem + smem_off_S(p.r, (p.V + nblk - 1) / nblk);
+    float *cache = S_lds + BC * p.h;  // state rows and A_H entries (state_cache_load)
+    int *atok = reinterpret_cast<int *>(smem + smem_off_tok()) + ATOK_OFF;
+    int *bad = atok + BC;  // block 0: rows whose token ids are invalid
+    uint64_t *local_keys = reinterpret_cast<uint64_t *>(smem);  // the reduction area is free inside the loop
     unsigned gen = barrier_gen_init(p.bar);
-    if (blk == 0)
+    if (blk == 0) {
         prologue_bookkeeping(p);
+        if (threadIdx.x < p.B)
+            bad[threadIdx.x] = row_bad(p, threadIdx.x) ? 1 : 0;
+    }
     phase_ah<WT>(p, blk, nblk, smem);
     phase_q_init<WT>(p, blk, nblk);
     if (!p.P)
         phase_g<WT>(p, blk, nblk, 0, smem);
     if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
         return;
-    phase_state<WT>(p, blk, nblk, 0, smem, S_lds);
+    StatePre spre;
+    W2Pre<WT, LPR, NL> wpre;
+    state_cache_load<WT>(p, blk, nblk, cache);
+    state_prefetch<WT>(p, 0, spre);
+    phase_state<WT>(p, blk, nblk, 0, smem, S_lds, &spre, cache, true);
+    w2_prefetch<WT, LPR, NL>(p, blk, nblk, wpre);
     if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
         return;
     for (int pos = 0; pos < p.K; ++pos) {
-        phase_w2<WT, LPR, NL>(p, blk, nblk, pos, smem);
-        if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+        phase_w2<WT, LPR, NL>(p, blk, nblk, pos, smem, &wpre, local_keys);
+        if (pos + 1 < p.K)
+            state_prefetch<WT>(p, pos + 1, spre);
+        if (!grid_argmax_sync(p.asy, gen, local_keys, p.B, atok, p.spin_limit, p.flags))
             return;
+        if (blk == 0 && threadIdx.x < p.B)
+            p.tokens[static_cast<size_t>(threadIdx.x) * p.K + pos] = bad[threadIdx.x] ? -1 : atok[threadIdx.x];
         if (pos + 1 < p.K) {
             if (!p.P) {
-                phase_g<WT>(p, blk, nblk, pos + 1, smem);
+                phase_g<WT>(p, blk, nblk, pos + 1, smem, atok);
                 if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
                     return;
             }
-            phase_state<WT>(p, blk, nblk, pos + 1, smem, S_lds);
+            phase_state<WT>(p, blk, nblk, pos + 1, smem, S_lds, &spre, cache, true, atok);
+            w2_prefetch<WT, LPR, NL>(p, blk, nblk, wpre);
             if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
                 return;
         }
     }
-    if (blk == 0)
-        write_tokens(p, p.K - 1);
 }
 
 template <typename WT>
@@ -140,14 +158,15 @@ template <typename WT>
 __global__ __launch_bounds__(NT) void k_step_state(Params p, int q)
 {
     extern __shared__ float smem[];
-    phase_state<WT>(p, blockIdx.x, gridDim.x, q, smem, smem + smem_off_S(p.r, 0));
+    phase_state<WT>(p, blockIdx.x, gridDim.x, q, smem, smem + smem_off_S(p.r, 0), nullptr, smem, false);
 }
 
 template <typename WT, int LPR, int NL>
 __global__ __launch_bounds__(NT) void k_step_w2(Params p, int pos)
 {
     extern __shared__ float smem[];
-    phase_w2<WT, LPR, NL>(p, blockIdx.x, gridDim.x, pos, smem);
+    phase_w2<WT, LPR, NL>(p, blockIdx.x, gridDim.x, pos, smem, static_cast<const W2Pre<WT, LPR, NL> *>(nullptr),
+                          nullptr);
 }
 
 template <typename WT>
@@ -214,7 +233,7 @@ constexpr int W2_STEP_ROWS = 128;  // vocabulary rows per block in stepwise W2 l
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t bar, flags, keys, A_H, S_buf, u_buf, q_buf, g_buf, P, total;
+    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, q_buf, g_buf, P, total;
 };
 
 Layout layout_of(const domino_head_config &c)
@@ -223,6 +242,8 @@ Layout layout_of(const domino_head_config &c)
     size_t off = 0;
     L.bar = off;
     off = align_up(off + sizeof(unsigned) * BAR_WORDS_ALL);
+    L.asy = off;
+    off = align_up(off + sizeof(uint64_t) * ASYNC_WORDS);
     L.flags = off;
     off = align_up(off + 64);
     L.keys = off;
@@ -424,13 +445,16 @@ int domino_head_create(const domino_head_config *cfg, void *workspace, size_t wo
         hd->spin_limit = static_cast<unsigned>(std::strtoul(s, nullptr, 10));
     // persistent launch: one block per compute unit, all co-resident
     const int rows_cap = (cfg->V + cus - 1) / cus;
-    hd->persist_smem = sizeof(float) * smem_floats(cfg->r, cfg->h, rows_cap);
+    hd->persist_smem = sizeof(float) * (smem_floats(cfg->r, cfg->h, rows_cap) +
+                                        state_cache_floats(cfg->r, cfg->h, cfg->K, cus,
+                                                           cfg->wdtype == DOMINO_BF16 ? 2 : 4));
     int per_cu = 0;
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern.persistent, NT, hd->persist_smem);
-    hd->persist_grid =
-        (e == hipSuccess && per_cu >= 1 && cus <= MAX_GRID && hd->persist_smem + 1024 <= static_cast<size_t>(lds_max))
-            ? cus
-            : 0;
+    // the argmax barrier packs token ids into 18 bits
+    hd->persist_grid = (e == hipSuccess && per_cu >= 1 && cus <= MAX_GRID && cfg->V <= (1 << 18) &&
+                        hd->persist_smem + 1024 <= static_cast<size_t>(lds_max))
+                           ? cus
+                           : 0;
     *out = hd;
     return DOMINO_OK;
 }
@@ -474,6 +498,7 @@ static Params make_params(domino_head_t hd, int B, const void *H, const float *L
     p.g_buf = reinterpret_cast<float *>(hd->ws + hd->L.g_buf);
     p.keys = reinterpret_cast<uint64_t *>(hd->ws + hd->L.keys);
     p.bar = reinterpret_cast<unsigned *>(hd->ws + hd->L.bar);
+    p.asy = reinterpret_cast<uint64_t *>(hd->ws + hd->L.asy);
     p.flags = reinterpret_cast<unsigned *>(hd->ws + hd->L.flags);
     p.spin_limit = hd->spin_limit;
     p.persistent = persistent ? 1 : 0;
@@ -523,6 +548,7 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!hd->state_ready) {
         hipLaunchKernelGGL(k_clear_state, dim3(1), dim3(256), 0, st, reinterpret_cast<unsigned *>(hd->ws + hd->L.bar),
+                           reinterpret_cast<uint64_t *>(hd->ws + hd->L.asy),
                            reinterpret_cast<unsigned *>(hd->ws + hd->L.flags));
         HIP_TRY(hipGetLastError(), "launch k_clear_state");
         hd->state_ready = true;

@@ -47,6 +47,32 @@ def logical_bytes(sh, B, store_logits=False, fold=False):
     return total, K * (V * r * s + B * V * 4)
 
 
+def kernel_source_hash():
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "causal_draft_correction_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, exec_name, fold):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, when it was taken
+    on the current kernel sources and the same workload; else None."""
+    import glob
+
+    cur = kernel_source_hash()
+    for f in glob.glob(os.path.join(ROOT, "profiles", "*_counters.json")):
+        with open(f) as fh:
+            d = json.load(fh)
+        if (d.get("kernel_source_sha256_16") == cur and d.get("workload") == workload and
+                d.get("exec") == exec_name and bool(d.get("fold_embedding")) == fold):
+            return d["traffic_bytes_per_launch"]
+    return None
+
+
 def cpu_baseline(w, inp, budget_s):
     """The fp64 oracle as it stands, on this host's cores, on row 0 of the workload."""
     import oracle
@@ -74,6 +100,8 @@ def main():
                     help="do not precompute the folded input-gate table (GRU input GEMV every step)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="run one plain device copy of MIB MiB before timing (reference for profiler byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -110,6 +138,15 @@ def main():
     if args.mode == "auto":
         exec_name = "persistent" if wl.B <= 8 else "stepwise"
 
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        eprint("bench: calibration copy of %d MiB done" % args.calibrate_copy)
+        del src, dst
+
     for _ in range(args.warmup):
         head.draft(H, L, lt, out=out)
     torch.cuda.synchronize()
@@ -136,7 +173,7 @@ def main():
     total_bytes, w2l_bytes = logical_bytes(sh, wl.B, args.store_logits, fold)
     achieved = total_bytes / (avg_ms * 1e-3) / 1e9
     w2l = w2l_bytes / (avg_ms * 1e-3) / 1e9
-    traffic = None
+    traffic = measured_traffic(wl.name, exec_name, fold) if exec_name == "persistent" else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -165,7 +202,9 @@ def main():
                    "kernel_avg_us": avg_ms * 1e3, "w2_lbase_GBps": w2l,
                    "w2_lbase_frac_of_hbm_peak": w2l / HBM_PEAK_GBPS},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes": total_bytes, "kernel": "k_persistent" if exec_name == "persistent"
+                     else "stepwise launches (whole call)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -95,6 +95,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_b1")
     ap.add_argument("--mode", default="auto", choices=["auto", "persistent", "stepwise"])
+    ap.add_argument("--stream-w2", action="store_true",
+                    help="persistent launch: stream W2 every position instead of keeping it on chip")
     ap.add_argument("--store-logits", action="store_true")
     ap.add_argument("--no-fold", action="store_true",
                     help="do not precompute the folded input-gate table (GRU input GEMV every step)")
@@ -124,8 +126,8 @@ def main():
     mode = {"auto": dca.EXEC_AUTO, "persistent": dca.EXEC_PERSISTENT, "stepwise": dca.EXEC_STEPWISE}[args.mode]
     fold = not args.no_fold
     t_create = time.perf_counter()
-    head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B, exec_mode=mode,
-                          fold_embedding=fold)
+    head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B,
+                          exec_mode=mode | (dca.EXEC_STREAM_W2 if args.stream_w2 else 0), fold_embedding=fold)
     torch.cuda.synchronize()
     t_create = time.perf_counter() - t_create
     H = dca.device_tensor(inp.H)
@@ -198,7 +200,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "K": sh.K, "V": sh.V, "d": sh.d, "h": sh.h, "r": sh.r,
                    "weights": sh.wdtype, "exec": exec_name, "store_logits": bool(args.store_logits),
-                   "fold_embedding": fold, "create_s": t_create,
+                   "fold_embedding": fold, "w2_on_chip": not args.stream_w2, "create_s": t_create,
                    "kernel_avg_us": avg_ms * 1e3, "w2_lbase_GBps": w2l,
                    "w2_lbase_frac_of_hbm_peak": w2l / HBM_PEAK_GBPS},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -7,9 +7,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace dh {
+// Threads per block and the namespace of the device code built for it: the
+// library compiles these headers twice, 512 threads (namespace dh) and 256
+// threads (namespace dh256, for the kernel that keeps W2 in registers).
+#ifndef DH_NT
+#define DH_NT 512
+#endif
+#ifndef DH_NS
+#define DH_NS dh
+#endif
 
-constexpr int NT = 512;           // threads per block (8 waves)
+namespace DH_NS {
+
+constexpr int NT = DH_NT;         // threads per block
 constexpr int NWAVE = NT / 64;
 constexpr int NG = 16;            // barrier groups = partial argmax slots per position
 constexpr int MAXK = 16;          // largest block size
@@ -368,4 +378,4 @@ __device__ inline bool grid_argmax_sync(uint64_t *asy, unsigned &gen, const uint
     return s_ok != 0;
 }
 
-}  // namespace dh
+}  // namespace DH_NS

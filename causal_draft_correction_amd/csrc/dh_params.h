@@ -1,0 +1,33 @@
+// Arguments of one block draft, shared by every kernel of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dhp {
+
+struct Params {
+    int d, h, r, V, K, B, maxB;
+    const void *W1, *W2, *W_ih, *W_hh, *b_ih, *b_hh, *E;
+    const float *P;  // folded input-gate table [V, 3h] or nullptr
+    const void *H;
+    const float *L_base;
+    const int *last_tok, *teacher;
+    const float *S_init;
+    int *tokens;
+    float *L_final, *S_out, *u_out;
+    // workspace
+    float *A_H;      // [maxB, K, r]
+    float *S_buf;    // [2, maxB, h]  state carried between stepwise launches
+    float *u_buf;    // [maxB, r]
+    float *q_buf;    // [2, maxB, 3h] W_hh S + b_hh
+    float *g_buf;    // [maxB, 3h]    W_ih E[x] + b_ih (when not folded)
+    uint64_t *keys;  // [K, NG, maxB] partial argmax keys
+    unsigned *bar;   // barrier words
+    uint64_t *asy;   // argmax barrier words
+    unsigned *flags; // device flags
+    unsigned spin_limit;
+    int persistent;  // 1: blocks keep the state in LDS between phases
+};
+
+}  // namespace dhp

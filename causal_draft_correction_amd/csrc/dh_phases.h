@@ -24,32 +24,11 @@
 #pragma once
 
 #include "dh_common.h"
+#include "dh_params.h"
 
-namespace dh {
+namespace DH_NS {
 
-struct Params {
-    int d, h, r, V, K, B, maxB;
-    const void *W1, *W2, *W_ih, *W_hh, *b_ih, *b_hh, *E;
-    const float *P;  // folded input-gate table [V, 3h] or nullptr
-    const void *H;
-    const float *L_base;
-    const int *last_tok, *teacher;
-    const float *S_init;
-    int *tokens;
-    float *L_final, *S_out, *u_out;
-    // workspace
-    float *A_H;      // [maxB, K, r]
-    float *S_buf;    // [2, maxB, h]  state carried between stepwise launches
-    float *u_buf;    // [maxB, r]
-    float *q_buf;    // [2, maxB, 3h] W_hh S + b_hh
-    float *g_buf;    // [maxB, 3h]    W_ih E[x] + b_ih (when not folded)
-    uint64_t *keys;  // [K, NG, maxB] partial argmax keys
-    unsigned *bar;   // barrier words
-    uint64_t *asy;   // argmax barrier words
-    unsigned *flags; // device flags
-    unsigned spin_limit;
-    int persistent;  // 1: blocks keep the state in LDS between phases
-};
+using dhp::Params;
 
 // ---- shared-memory layout (floats) ----------------------------------------------
 // red [256] | kred [2*NWAVE] | tok [TOK_SLOTS] | u_lds [BC*r] | lbuf [BC*rows_cap] | S_lds [BC*h]
@@ -316,7 +295,7 @@ __device__ __forceinline__ void phase_update(const Params &p, int blk, int nblk,
 // position, so the persistent kernel copies them into LDS once per launch
 // (state_cache_load); the q values of the gate update are loaded before the
 // barrier that precedes the phase (state_prefetch).
-constexpr int SP_EL = 2;  // gate-update elements per thread whose q values are prefetched
+constexpr int SP_EL = 1024 / NT;  // gate-update elements per thread whose q values are prefetched
 
 struct StatePre {
     float qv[SP_EL][3];
@@ -508,6 +487,70 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
     }
 }
 
+// Epilogue of the W2 phase for batch rows b0..b0+nb-1 of block blk: lbuf holds
+// the block's W2 u dot products; add L_base (the first LB values per thread of
+// batch row b0 come prefetched in lbv), store L_final, reduce the block's
+// greedy argmax key and publish it (LDS local_keys, or the global partial slot).
+constexpr int W2_LB = 1024 / NT;
+__device__ __forceinline__ void w2_epilogue(const Params &p, int blk, int nblk, int pos, float *smem, int b0, int nb,
+                                            const float (&lbv)[W2_LB], uint64_t *local_keys)
+{
+    const long long v0 = static_cast<long long>(p.V) * blk / nblk;
+    const int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0);
+    const int rows_cap = (p.V + nblk - 1) / nblk;
+    uint64_t *kred = reinterpret_cast<uint64_t *>(smem + 256);
+    const float *lbuf = smem + smem_off_lbuf(p.r);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = blk % NG;
+    for (int bb = 0; bb < nb; ++bb) {
+        const int b = b0 + bb;
+        const float *lb = p.L_base + (static_cast<size_t>(b) * p.K + pos) * p.V + v0;
+        float *lf = p.L_final ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * p.V + v0 : nullptr;
+        uint64_t best = 0;
+        for (int i = threadIdx.x, e = 0; i < n; i += NT, ++e) {
+            float base_logit = 0.f;
+#pragma unroll
+            for (int ee = 0; ee < W2_LB; ++ee)
+                if (bb == 0 && e == ee)
+                    base_logit = lbv[ee];
+            if (bb != 0 || e >= W2_LB)
+                base_logit = lb[i];
+            const float v = base_logit + lbuf[bb * rows_cap + i];
+            if (lf)
+                lf[i] = v;
+            const uint64_t key = argmax_key(v, static_cast<uint32_t>(v0 + i));
+            best = key > best ? key : best;
+        }
+        best = wave_max_u64(best);
+        if (lane == 0)
+            kred[wave] = best;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint64_t m = 0;
+            for (int w = 0; w < NWAVE; ++w)
+                m = kred[w] > m ? kred[w] : m;
+            if (local_keys)
+                local_keys[bb] = m ? (m & KEY_ORD_MASK) | (KEY_IDX_MASK - key_index(m)) : 0ull;
+            else
+                __hip_atomic_fetch_max(key_slot(p, pos, g, b), m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+    }
+}
+
+// L_base values of batch row b0 this thread adds in the epilogue, loaded early.
+__device__ __forceinline__ void w2_lbase_prefetch(const Params &p, int blk, int nblk, int pos, int b0,
+                                                  float (&lbv)[W2_LB])
+{
+    const long long v0 = static_cast<long long>(p.V) * blk / nblk;
+    const int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0);
+#pragma unroll
+    for (int e = 0; e < W2_LB; ++e) {
+        const int i = threadIdx.x + e * NT;
+        lbv[e] = i < n ? p.L_base[(static_cast<size_t>(b0) * p.K + pos) * p.V + v0 + i] : 0.f;
+    }
+}
+
 // ---- phase: L_p = L_base_p + W2 u_p and the greedy argmax ------------------------
 // Block blk owns vocabulary rows [v0, v1).  A wave reads 64/LPR rows at a time,
 // LPR lanes per row, each lane NL 16-byte chunks (coalesced: the LPR lanes of a
@@ -588,18 +631,15 @@ __device__ __forceinline__ void phase_w2(const Params &p, int blk, int nblk, int
 {
     using R = W2Rows<WT, LPR, NL>;
     constexpr int RPW = R::RPW;
-    constexpr int LB = 2;  // L_base values per thread (first batch row of the pass) loaded up front
     const int r = p.r;
     const long long v0 = static_cast<long long>(p.V) * blk / nblk;
     const long long v1 = static_cast<long long>(p.V) * (blk + 1) / nblk;
     const int n = static_cast<int>(v1 - v0);
     const int rows_cap = (p.V + nblk - 1) / nblk;
-    uint64_t *kred = reinterpret_cast<uint64_t *>(smem + 256);
     float *u_lds = smem + smem_off_u();
     float *lbuf = smem + smem_off_lbuf(r);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % LPR, rw = lane / LPR;
-    const int g = blk % NG;
     const int stride = NWAVE * RPW;   // rows between consecutive groups of one wave
     const int bstride = R::UG * stride;
 
@@ -616,12 +656,8 @@ __device__ __forceinline__ void phase_w2(const Params &p, int blk, int nblk, int
         } else {
             R::load(wa, p.W2, r, v0, n, base, rw, sub, stride);
         }
-        float lbv[LB];
-#pragma unroll
-        for (int e = 0; e < LB; ++e) {
-            const int i = threadIdx.x + e * NT;
-            lbv[e] = i < n ? p.L_base[(static_cast<size_t>(b0) * p.K + pos) * p.V + v0 + i] : 0.f;
-        }
+        float lbv[W2_LB];
+        w2_lbase_prefetch(p, blk, nblk, pos, b0, lbv);
         __syncthreads();
         for (int i = threadIdx.x; i < nb * r; i += NT)
             u_lds[i] = xld(&p.u_buf[static_cast<size_t>(b0) * r + i]);
@@ -640,39 +676,199 @@ __device__ __forceinline__ void phase_w2(const Params &p, int blk, int nblk, int
             base = nnbase;
         }
         __syncthreads();
-        for (int bb = 0; bb < nb; ++bb) {
-            {
-                const int b = b0 + bb;
-                const float *lb = p.L_base + (static_cast<size_t>(b) * p.K + pos) * p.V + v0;
-                float *lf = p.L_final ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * p.V + v0 : nullptr;
-                uint64_t best = 0;
-                for (int i = threadIdx.x, e = 0; i < n; i += NT, ++e) {
-                    float base_logit = (bb == 0 && e == 0) ? lbv[0] : (bb == 0 && e == 1) ? lbv[1] : 0.f;
-                    if (bb != 0 || e >= LB)
-                        base_logit = lb[i];
-                    const float v = base_logit + lbuf[bb * rows_cap + i];
-                    if (lf)
-                        lf[i] = v;
-                    const uint64_t key = argmax_key(v, static_cast<uint32_t>(v0 + i));
-                    best = key > best ? key : best;
-                }
-                best = wave_max_u64(best);
-                if (lane == 0)
-                    kred[wave] = best;
-                __syncthreads();
-                if (threadIdx.x == 0) {
-                    uint64_t m = 0;
-                    for (int w = 0; w < NWAVE; ++w)
-                        m = kred[w] > m ? kred[w] : m;
-                    if (local_keys)
-                        local_keys[bb] = m ? (m & KEY_ORD_MASK) | (KEY_IDX_MASK - key_index(m)) : 0ull;
-                    else
-                        __hip_atomic_fetch_max(key_slot(p, pos, g, b), m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-                __syncthreads();
-            }
-        }
+        w2_epilogue(p, blk, nblk, pos, smem, b0, nb, lbv, local_keys);
     }
 }
 
-}  // namespace dh
+// ---- W2 phase with the block's W2 slice resident on chip (bf16, r = 32 * KS) -------
+// The block's rows [v0, v1) form 16-row tiles.  Tile t is held by wave t % NWAVE:
+// its first RT tiles in registers (wt), the rest in LDS (`tl`, LT_MAX tiles),
+// all loaded once per launch.  Per position each wave multiplies its tiles with
+// u on the matrix cores (v_mfma_f32_16x16x32_bf16): A = 16 W2 rows x 32 of r,
+// B = 32 of r x 16 columns, where column b (< 8) carries bf16(u_b) and column
+// 8 + b carries bf16(u_b - bf16(u_b)); adding the two result columns gives
+// W2 u_b with float32-level accuracy.  Lane l holds A row l%16 and B column l%16
+// at r offsets (l/16)*8 .. +8 of each 32-wide step, and result rows
+// (l/16)*4 + i of column l%16.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int RT, int KS>
+struct W2Resident {
+    uint4 wt[RT][KS];
+};
+
+__device__ inline uint32_t bf16_rne_bits(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ inline int w2_tiles(const Params &p, int blk, int nblk)
+{
+    const long long v0 = static_cast<long long>(p.V) * blk / nblk;
+    const int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0);
+    return (n + 15) / 16;
+}
+
+// A operand of tile t, step kk for this lane (zero beyond the block's rows).
+template <int KS>
+__device__ inline uint4 w2_tile_chunk(const Params &p, long long v0, int n, int t, int kk)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = t * 16 + (lane & 15);
+    if (row >= n)
+        return make_uint4(0u, 0u, 0u, 0u);
+    return ld16<bf16s>(p.W2, static_cast<size_t>(v0 + row) * (32 * KS) + kk * 32 + (lane >> 4) * 8);
+}
+
+template <int RT, int KS>
+__device__ __forceinline__ void w2_resident_load(const Params &p, int blk, int nblk, W2Resident<RT, KS> &res,
+                                                 uint4 *tl)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long long v0 = static_cast<long long>(p.V) * blk / nblk;
+    const int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0);
+    const int T = (n + 15) / 16;
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+        const int t = wave + j * NWAVE;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+            res.wt[j][kk] = t < T ? w2_tile_chunk<KS>(p, v0, n, t, kk) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    for (int t = NWAVE * RT + wave; t < T; t += NWAVE) {
+        const int slot = t - NWAVE * RT;
+        for (int kk = 0; kk < KS; ++kk)
+            tl[(slot * KS + kk) * 64 + lane] = w2_tile_chunk<KS>(p, v0, n, t, kk);
+    }
+}
+
+// Sum the hi and lo result columns of one tile and write W2 u to lbuf.
+__device__ inline void w2_tile_store(const f32x4_t &acc, float *lbuf, int rows_cap, int nb, int n, int t)
+{
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float v = acc[i] + __shfl_xor(acc[i], 8);  // hi column + lo column
+        const int row = t * 16 + (lane >> 4) * 4 + i;
+        if (col < nb && row < n)
+            lbuf[col * rows_cap + row] = v;
+    }
+}
+
+template <int KS>
+__device__ inline void w2_tile_mma(const uint4 (&a)[KS], const uint4 (&bop)[KS], float *lbuf, int rows_cap, int nb,
+                                   int n, int t)
+{
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[kk]),
+                                                      __builtin_bit_cast(bf16x8_t, bop[kk]), acc, 0, 0, 0);
+    w2_tile_store(acc, lbuf, rows_cap, nb, n, t);
+}
+
+template <int RT, int KS>
+__device__ __forceinline__ void phase_w2_resident(const Params &p, int blk, int nblk, int pos, float *smem,
+                                                  const W2Resident<RT, KS> &res, const uint4 *tl,
+                                                  uint64_t *local_keys)
+{
+    const int r = 32 * KS;
+    const long long v0 = static_cast<long long>(p.V) * blk / nblk;
+    const int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0);
+    const int T = (n + 15) / 16;
+    const int rows_cap = (p.V + nblk - 1) / nblk;
+    // B operand in LDS, [kk][lane] (16 bytes each), built once per block in the u area
+    static_assert(KS * 64 * 4 <= BC * 32 * KS && (KS * 64) % NT == 0, "operand must fit the u area");
+    uint4 *bop_lds = reinterpret_cast<uint4 *>(smem + smem_off_u());
+    float *lbuf = smem + smem_off_lbuf(r);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nb = p.B;  // persistent launches take B <= BC
+    float lbv[W2_LB];
+    w2_lbase_prefetch(p, blk, nblk, pos, 0, lbv);
+    __syncthreads();
+    // stage u in the B-operand area, pull each thread's inputs into registers, then
+    // overwrite the area with the operand: column c < 8 carries bf16(u_c), column
+    // 8 + c carries bf16(u_c - bf16(u_c))
+    constexpr int EPT = KS * 64 / NT;  // operand entries per thread
+    float *u_stage = reinterpret_cast<float *>(bop_lds);
+    for (int i = threadIdx.x; i < nb * r; i += NT)
+        u_stage[i] = xld(&p.u_buf[i]);
+    __syncthreads();
+    float xv[EPT][8];
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int e = threadIdx.x + q * NT;
+        const int kk = e >> 6, l = e & 63, b = l & 7;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            xv[q][j] = b < nb ? u_stage[b * r + kk * 32 + (l >> 4) * 8 + j] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int e = threadIdx.x + q * NT;
+        const int col = e & 15;
+        uint32_t hv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t xh = bf16_rne_bits(xv[q][j]);
+            hv[j] = col < 8 ? xh : bf16_rne_bits(xv[q][j] - __uint_as_float(xh << 16));
+        }
+        bop_lds[e] = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
+                                hv[6] | (hv[7] << 16));
+    }
+    __syncthreads();
+    uint4 bop[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+        bop[kk] = bop_lds[kk * 64 + lane];
+    // register tiles in groups of GR: independent accumulators, steps interleaved
+    constexpr int GR = 4;
+#pragma unroll
+    for (int g0 = 0; g0 < RT; g0 += GR) {
+        f32x4_t acc[GR];
+#pragma unroll
+        for (int j = 0; j < GR; ++j)
+            acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int j = 0; j < GR; ++j)
+                if (g0 + j < RT)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, res.wt[g0 + j < RT ? g0 + j : 0][kk]),
+                        __builtin_bit_cast(bf16x8_t, bop[kk]), acc[j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < GR; ++j) {
+            const int t = wave + (g0 + j) * NWAVE;
+            if (g0 + j < RT && t < T)
+                w2_tile_store(acc[j], lbuf, rows_cap, nb, n, t);
+        }
+    }
+    // LDS tiles, two at a time
+#pragma unroll 1
+    for (int t = NWAVE * RT + wave; t < T; t += 2 * NWAVE) {
+        const int s0 = t - NWAVE * RT, s1 = s0 + NWAVE;
+        const bool two = t + NWAVE < T;
+        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl[(s0 * KS + kk) * 64 + lane]),
+                                                         __builtin_bit_cast(bf16x8_t, bop[kk]), a0, 0, 0, 0);
+            if (two)
+                a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, tl[(s1 * KS + kk) * 64 + lane]), __builtin_bit_cast(bf16x8_t, bop[kk]),
+                    a1, 0, 0, 0);
+        }
+        w2_tile_store(a0, lbuf, rows_cap, nb, n, t);
+        if (two)
+            w2_tile_store(a1, lbuf, rows_cap, nb, n, t + NWAVE);
+    }
+    __syncthreads();
+    w2_epilogue(p, blk, nblk, pos, smem, 0, nb, lbv, local_keys);
+}
+
+}  // namespace DH_NS

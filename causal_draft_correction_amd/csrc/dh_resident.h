@@ -1,0 +1,12 @@
+// Host entry points of the resident-W2 persistent kernel (domino_head_res.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace dhres {
+int threads();            // threads per block of the kernel
+int r_supported();        // the rank it is built for
+const void *kernel();     // kernel function, launched with one block per compute unit
+size_t smem_bytes(int r, int h, int K, int V, int nblk);  // dynamic LDS of one block
+}  // namespace dhres

@@ -19,6 +19,7 @@
 
 #include "../../include/domino_head.h"
 #include "dh_phases.h"
+#include "dh_resident.h"
 
 using namespace dh;
 
@@ -135,6 +136,7 @@ __global__ __launch_bounds__(NT) void k_persistent(Params p)
         }
     }
 }
+
 
 template <typename WT>
 __global__ __launch_bounds__(NT) void k_step_prologue(Params p)
@@ -294,7 +296,7 @@ int validate_config(const domino_head_config *c)
         if (!aligned16(ptrs[i]))
             return fail(DOMINO_EINVAL, "%s is not 16-byte aligned", names[i]);
     }
-    if (c->flags & ~(DOMINO_EXEC_PERSISTENT | DOMINO_EXEC_STEPWISE | DOMINO_FOLD_EMBED))
+    if (c->flags & ~(DOMINO_EXEC_PERSISTENT | DOMINO_EXEC_STEPWISE | DOMINO_FOLD_EMBED | DOMINO_EXEC_STREAM_W2))
         return fail(DOMINO_EINVAL, "unknown flags 0x%x", c->flags);
     if ((c->flags & DOMINO_EXEC_PERSISTENT) && (c->flags & DOMINO_EXEC_STEPWISE))
         return fail(DOMINO_EINVAL, "flags ask for both persistent and stepwise execution");
@@ -366,6 +368,8 @@ struct domino_head {
     int cus;
     int persist_grid;      // blocks of the persistent launch (0: cannot be co-resident)
     size_t persist_smem;
+    int res_grid;          // blocks of the resident-W2 persistent launch (0: not usable)
+    size_t res_smem;
     bool state_ready;      // barrier words and flags cleared on the device
     hipStream_t last_stream;
     unsigned spin_limit;
@@ -455,6 +459,16 @@ int domino_head_create(const domino_head_config *cfg, void *workspace, size_t wo
                         hd->persist_smem + 1024 <= static_cast<size_t>(lds_max))
                            ? cus
                            : 0;
+    // resident-W2 variant: bf16, r = 256, one 256-thread block per compute unit
+    hd->res_grid = 0;
+    if (cfg->wdtype == DOMINO_BF16 && cfg->r == dhres::r_supported() && hd->persist_grid) {
+        hd->res_smem = dhres::smem_bytes(cfg->r, cfg->h, cfg->K, cfg->V, cus);
+        int per_cu_r = 0;
+        hipError_t er = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_r, dhres::kernel(), dhres::threads(),
+                                                                     hd->res_smem);
+        if (er == hipSuccess && per_cu_r >= 1 && hd->res_smem + 1024 <= static_cast<size_t>(lds_max))
+            hd->res_grid = cus;
+    }
     *out = hd;
     return DOMINO_OK;
 }
@@ -557,9 +571,15 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
     hd->last_stream = st;
     if (persistent) {
         void *args[] = {&p};
-        HIP_TRY(hipLaunchCooperativeKernel(hd->kern.persistent, dim3(hd->persist_grid), dim3(NT), args,
-                                           static_cast<unsigned>(hd->persist_smem), st),
-                "hipLaunchCooperativeKernel(persistent)");
+        if (hd->res_grid && !(c.flags & DOMINO_EXEC_STREAM_W2)) {
+            HIP_TRY(hipLaunchCooperativeKernel(dhres::kernel(), dim3(hd->res_grid), dim3(dhres::threads()), args,
+                                               static_cast<unsigned>(hd->res_smem), st),
+                    "hipLaunchCooperativeKernel(persistent, resident W2)");
+        } else {
+            HIP_TRY(hipLaunchCooperativeKernel(hd->kern.persistent, dim3(hd->persist_grid), dim3(NT), args,
+                                               static_cast<unsigned>(hd->persist_smem), st),
+                    "hipLaunchCooperativeKernel(persistent)");
+        }
         return DOMINO_OK;
     }
     // stepwise: prologue, update(0), state(0), then per position w2 [, g], update, state

@@ -1,0 +1,91 @@
+// The persistent draft kernel that keeps each block's W2 slice on chip, built
+// for 256-thread blocks: one wave per SIMD, so each wave may hold up to 512
+// registers, enough for its share of the slice (RES_RT tiles of 16 rows x 256).
+#define DH_NT 256
+#define DH_NS dh256
+#include "dh_phases.h"
+#include "dh_resident.h"
+
+namespace DH_NS {
+
+// Same draft with the block's W2 slice resident on chip and multiplied on the
+// matrix cores (bf16 weights, r = 32 * KS, B <= BC).  The slice is loaded once,
+// overlapped with the prologue; every position then reads it from registers
+// and LDS instead of streaming 2 r V bytes from HBM.
+template <int RT, int KS>
+__global__ __launch_bounds__(NT) void k_persistent_res(Params p)
+{
+    extern __shared__ float smem[];
+    const int blk = blockIdx.x, nblk = gridDim.x;
+    float *S_lds = smem + smem_off_S(p.r, (p.V + nblk - 1) / nblk);
+    float *cache = S_lds + BC * p.h;
+    uint4 *tl = reinterpret_cast<uint4 *>(cache + state_cache_floats(p.r, p.h, p.K, nblk, 2));
+    int *atok = reinterpret_cast<int *>(smem + smem_off_tok()) + ATOK_OFF;
+    int *bad = atok + BC;
+    uint64_t *local_keys = reinterpret_cast<uint64_t *>(smem);
+    unsigned gen = barrier_gen_init(p.bar);
+    if (blk == 0) {
+        prologue_bookkeeping(p);
+        if (threadIdx.x < p.B)
+            bad[threadIdx.x] = row_bad(p, threadIdx.x) ? 1 : 0;
+    }
+    phase_ah<bf16s>(p, blk, nblk, smem);
+    phase_q_init<bf16s>(p, blk, nblk);
+    if (!p.P)
+        phase_g<bf16s>(p, blk, nblk, 0, smem);
+    // the slice load overlaps the first barrier and state phase
+    W2Resident<RT, KS> res;
+    w2_resident_load<RT, KS>(p, blk, nblk, res, tl);
+    if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+        return;
+    StatePre spre;
+    state_cache_load<bf16s>(p, blk, nblk, cache);
+    state_prefetch<bf16s>(p, 0, spre);
+    phase_state<bf16s>(p, blk, nblk, 0, smem, S_lds, &spre, cache, true);
+    if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+        return;
+    for (int pos = 0; pos < p.K; ++pos) {
+        phase_w2_resident<RT, KS>(p, blk, nblk, pos, smem, res, tl, local_keys);
+        if (pos + 1 < p.K)
+            state_prefetch<bf16s>(p, pos + 1, spre);
+        if (!grid_argmax_sync(p.asy, gen, local_keys, p.B, atok, p.spin_limit, p.flags))
+            return;
+        if (blk == 0 && threadIdx.x < p.B)
+            p.tokens[static_cast<size_t>(threadIdx.x) * p.K + pos] = bad[threadIdx.x] ? -1 : atok[threadIdx.x];
+        if (pos + 1 < p.K) {
+            if (!p.P) {
+                phase_g<bf16s>(p, blk, nblk, pos + 1, smem, atok);
+                if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+                    return;
+            }
+            phase_state<bf16s>(p, blk, nblk, pos + 1, smem, S_lds, &spre, cache, true, atok);
+            if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+                return;
+        }
+    }
+}
+
+
+constexpr int RES_RT = 8;   // W2 tiles per wave kept in registers (4 waves x 8 x 16 rows = 512 rows; the rest in LDS)
+constexpr int RES_KS = 8;   // 32-wide steps of r: r = 256
+
+}  // namespace DH_NS
+
+namespace dhres {
+
+using namespace dh256;
+
+int threads() { return NT; }
+int r_supported() { return 32 * RES_KS; }
+const void *kernel() { return reinterpret_cast<const void *>(&k_persistent_res<RES_RT, RES_KS>); }
+
+size_t smem_bytes(int r, int h, int K, int V, int nblk)
+{
+    const int rows_cap = (V + nblk - 1) / nblk;
+    const int tiles = (rows_cap + 15) / 16;
+    const int lds_tiles = tiles > NWAVE * RES_RT ? tiles - NWAVE * RES_RT : 0;
+    return sizeof(float) * (smem_floats(r, h, rows_cap) + state_cache_floats(r, h, K, nblk, 2)) +
+           static_cast<size_t>(lds_tiles) * RES_KS * 64 * 16;
+}
+
+}  // namespace dhres

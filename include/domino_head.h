@@ -59,6 +59,8 @@ extern "C" {
 #define DOMINO_EXEC_AUTO 0u        /* pick per call from B */
 #define DOMINO_EXEC_PERSISTENT 1u  /* one cooperative launch covering all K positions */
 #define DOMINO_EXEC_STEPWISE 2u    /* one launch per phase and position */
+#define DOMINO_EXEC_STREAM_W2 8u   /* persistent launch: stream W2 from memory at every position instead of
+                                      keeping the slice on chip (bf16, r = 256); for comparison */
 #define DOMINO_FOLD_EMBED 4u       /* precompute P = E W_ih^T + b_ih ([V, 3h] float32, in the workspace) at
                                       create time, so each GRU step gathers one row of P instead of
                                       multiplying W_ih by the embedding row (same values up to rounding) */

@@ -257,3 +257,24 @@ def test_accept_len_bit_exact(B, K):
     ref = oracle.accept_len(draft, tgt)
     assert np.array_equal(got, ref)
     assert got[0] == K
+
+
+# ------------------------------------------------------------------ resident W2 (bf16, r = 256)
+@pytest.mark.parametrize("V,B,fold", [(5003, 1, True), (5003, 3, False), (5003, 8, True), (140000, 2, True)])
+def test_resident_w2_slice_matches_oracle(V, B, fold):
+    """r = 256 bf16 heads keep each block's W2 slice on chip and multiply it on the
+    matrix cores (u split into bf16 hi + lo parts).  V = 140000 puts tiles beyond the
+    register share into LDS.  Compared with the oracle, with the streaming launch and
+    run to run."""
+    sh = ds.HeadShape(d=128, h=64, r=256, V=V, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 60), gru_sensitive=True)
+    inp = ds.make_inputs(sh, B, (9, 61), sigma=0.5, peak="none")
+    head = make_head(w, B, dca.EXEC_PERSISTENT, fold=fold)
+    run_both_protocols(w, inp, head, label="resident V=%d B=%d fold=%d" % (V, B, fold))
+    a, _ = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
+    b, _ = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
+    for k in ("tokens", "L_final", "S", "u"):
+        assert np.array_equal(a[k], b[k]), k
+    st = make_head(w, B, dca.EXEC_PERSISTENT | dca.EXEC_STREAM_W2, fold=fold)
+    c, _ = gpu_draft(st, inp.H, inp.L_base, inp.last_tok)
+    assert np.abs(c["L_final"] - a["L_final"]).max() < 1e-4

@@ -58,9 +58,9 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, exec_name, fold):
+def measured_traffic(workload, exec_name, fold, w2_on_chip):
     """HBM bytes per launch from the committed rocprofv3 counter summary, when it was taken
-    on the current kernel sources and the same workload; else None."""
+    on the current kernel sources, the same workload and the same launch; else None."""
     import glob
 
     cur = kernel_source_hash()
@@ -68,7 +68,8 @@ def measured_traffic(workload, exec_name, fold):
         with open(f) as fh:
             d = json.load(fh)
         if (d.get("kernel_source_sha256_16") == cur and d.get("workload") == workload and
-                d.get("exec") == exec_name and bool(d.get("fold_embedding")) == fold):
+                d.get("exec") == exec_name and bool(d.get("fold_embedding")) == fold and
+                bool(d.get("w2_on_chip")) == w2_on_chip):
             return d["traffic_bytes_per_launch"]
     return None
 
@@ -136,9 +137,8 @@ def main():
     out = {"tokens": torch.empty((wl.B, sh.K), dtype=torch.int32, device="cuda")}
     if args.store_logits:
         out["L_final"] = torch.empty((wl.B, sh.K, sh.V), dtype=torch.float32, device="cuda")
-    exec_name = args.mode
-    if args.mode == "auto":
-        exec_name = "persistent" if wl.B <= 8 else "stepwise"
+    info = head.exec_info(wl.B)
+    exec_name = "persistent" if info["persistent"] else "stepwise"
 
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20) // 4
@@ -175,7 +175,12 @@ def main():
     total_bytes, w2l_bytes = logical_bytes(sh, wl.B, args.store_logits, fold)
     achieved = total_bytes / (avg_ms * 1e-3) / 1e9
     w2l = w2l_bytes / (avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(wl.name, exec_name, fold) if exec_name == "persistent" else None
+    w2_on_chip = info["w2_resident"]
+    traffic = measured_traffic(wl.name, exec_name, fold, w2_on_chip) if exec_name == "persistent" else None
+    if exec_name == "persistent":
+        kname = "k_persistent_res" if w2_on_chip else "k_persistent"
+    else:
+        kname = "stepwise launches (whole call)"
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -200,13 +205,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "K": sh.K, "V": sh.V, "d": sh.d, "h": sh.h, "r": sh.r,
                    "weights": sh.wdtype, "exec": exec_name, "store_logits": bool(args.store_logits),
-                   "fold_embedding": fold, "w2_on_chip": not args.stream_w2, "create_s": t_create,
+                   "fold_embedding": fold, "w2_on_chip": w2_on_chip, "create_s": t_create,
                    "kernel_avg_us": avg_ms * 1e3, "w2_lbase_GBps": w2l,
                    "w2_lbase_frac_of_hbm_peak": w2l / HBM_PEAK_GBPS},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "algorithmic_bytes": total_bytes, "kernel": "k_persistent" if exec_name == "persistent"
-                     else "stepwise launches (whole call)"},
+                     "algorithmic_bytes": total_bytes, "kernel": kname},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -29,7 +29,8 @@ FLAG_SYNC_TIMEOUT = 2
 ERRORS = {-1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP", -5: "EDEVICE"}
 
 SYMBOLS = ("domino_head_workspace_size", "domino_head_create", "domino_head_draft", "domino_accept_len",
-           "domino_head_check_error", "domino_head_param_count", "domino_head_destroy", "domino_last_error")
+           "domino_head_check_error", "domino_head_exec_info", "domino_head_param_count", "domino_head_destroy",
+           "domino_last_error")
 
 
 class DominoError(RuntimeError):
@@ -64,6 +65,8 @@ def load_library(path: str = LIB_PATH):
     lib.domino_head_draft.argtypes = [P, I32, P, P, P, P, P, P, P, P, P, P]
     lib.domino_accept_len.argtypes = [I32, I32, P, P, P, P]
     lib.domino_head_check_error.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
+    PI = ctypes.POINTER(ctypes.c_int32)
+    lib.domino_head_exec_info.argtypes = [P, I32, PI, PI, PI]
     lib.domino_head_param_count.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_int64)]
     lib.domino_head_destroy.argtypes = [P]
     lib.domino_head_destroy.restype = None
@@ -183,6 +186,13 @@ class DominoHead:
             self._h, B, _ptr(H), _ptr(L_base), _ptr(last_tok), _ptr(teacher), _ptr(S_init), _ptr(out["tokens"]),
             _ptr(out.get("L_final")), _ptr(out.get("S")), _ptr(out.get("u")), _stream_handle()))
         return out
+
+    def exec_info(self, B: int = None) -> dict:
+        """Launch a draft of B rows takes: {"persistent", "w2_resident", "grid"} (host only)."""
+        B = self.max_batch if B is None else B
+        v = [ctypes.c_int32() for _ in range(3)]
+        _check(load_library().domino_head_exec_info(self._h, B, *[ctypes.byref(x) for x in v]))
+        return {"persistent": bool(v[0].value), "w2_resident": bool(v[1].value), "grid": int(v[2].value)}
 
     def check_error(self) -> int:
         """Synchronize, return and clear the device flags (raises DominoError if any is set)."""

@@ -17,6 +17,13 @@
 #define DH_NS dh
 #endif
 
+// Optional instrumentation: a translation unit may define DH_TRACE(slot) before
+// including these headers to record timestamps at the marked points of the
+// persistent kernels (slot = 32 * position + point).  The default is a no-op.
+#ifndef DH_TRACE
+#define DH_TRACE(slot) ((void)(slot))
+#endif
+
 namespace DH_NS {
 
 constexpr int NT = DH_NT;         // threads per block
@@ -104,24 +111,103 @@ __device__ inline void ld_f32(const float *p, float *o)
     }
 }
 
+// ---- cross-lane exchange without LDS traffic --------------------------------
+// DPP lane permutations (within 16-lane rows) and the gfx950 row-swap
+// instructions.  Lane layouts, for lane i:
+constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1,0,3,2]: reads lane i ^ 1
+constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2,3,0,1]: reads lane i ^ 2
+constexpr int DPP_HALF_MIRROR = 0x141;  // reads lane 7 - i within each group of 8
+constexpr int DPP_ROW_MIRROR = 0x140;   // reads lane 15 - i within each row of 16
+constexpr int DPP_ROW_ROR8 = 0x128;     // reads lane (i + 8) mod 16 within each row of 16
+
+template <int CTRL>
+__device__ inline uint32_t dpp_u32(uint32_t v)
+{
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ inline float dpp_f32(float v) { return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v))); }
+template <int CTRL>
+__device__ inline uint64_t dpp_u64(uint64_t v)
+{
+    return (static_cast<uint64_t>(dpp_u32<CTRL>(static_cast<uint32_t>(v >> 32))) << 32) |
+           dpp_u32<CTRL>(static_cast<uint32_t>(v));
+}
+
+// v_permlane16_swap with both operands v: every lane of the row pair {0,1}
+// (and {2,3}) gets the value of the even row in `even` and of the odd row in `odd`.
+__device__ inline void row_pair_values(uint32_t v, uint32_t &even, uint32_t &odd)
+{
+    const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    even = s[0];
+    odd = s[1];
+}
+// v_permlane32_swap with both operands v: every lane gets the value of its
+// lane in the lower half (`lo`) and in the upper half (`hi`).
+__device__ inline void half_values(uint32_t v, uint32_t &lo, uint32_t &hi)
+{
+    const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    lo = s[0];
+    hi = s[1];
+}
+
+// Sum over the 2^k lanes of aligned groups (GROUP = 2, 4, 8 or 16 lanes).
+// Every lane of a group gets bit-identical sums: each step adds two partial
+// sums that a lane and its partner hold in swapped order.
+template <int GROUP>
+__device__ inline float group_sum(float v)
+{
+    static_assert(GROUP == 1 || GROUP == 2 || GROUP == 4 || GROUP == 8 || GROUP == 16, "group of 1..16 lanes");
+    if constexpr (GROUP >= 2)
+        v += dpp_f32<DPP_QUAD_XOR1>(v);
+    if constexpr (GROUP >= 4)
+        v += dpp_f32<DPP_QUAD_XOR2>(v);
+    if constexpr (GROUP >= 8)
+        v += dpp_f32<DPP_HALF_MIRROR>(v);
+    if constexpr (GROUP >= 16)
+        v += dpp_f32<DPP_ROW_MIRROR>(v);
+    return v;
+}
+
+// Sum over the wave, bit-identical in every lane.
 __device__ inline float wave_sum(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o);
-    return v;
+    v = group_sum<16>(v);
+    uint32_t a, b;
+    row_pair_values(__float_as_uint(v), a, b);
+    v = __uint_as_float(a) + __uint_as_float(b);
+    half_values(__float_as_uint(v), a, b);
+    return __uint_as_float(a) + __uint_as_float(b);
+}
+
+__device__ inline uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Max over the four lanes i, i+16, i+32, i+48 (the same position in each row).
+__device__ inline uint64_t rows_max_u64(uint64_t v)
+{
+    uint32_t el, ol, eh, oh;
+    row_pair_values(static_cast<uint32_t>(v), el, ol);
+    row_pair_values(static_cast<uint32_t>(v >> 32), eh, oh);
+    v = max_u64((static_cast<uint64_t>(eh) << 32) | el, (static_cast<uint64_t>(oh) << 32) | ol);
+    half_values(static_cast<uint32_t>(v), el, ol);
+    half_values(static_cast<uint32_t>(v >> 32), eh, oh);
+    return max_u64((static_cast<uint64_t>(eh) << 32) | el, (static_cast<uint64_t>(oh) << 32) | ol);
 }
 
 __device__ inline uint64_t wave_max_u64(uint64_t v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o);
-        uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o);
-        uint64_t w = (static_cast<uint64_t>(hi) << 32) | lo;
-        v = w > v ? w : v;
-    }
-    return v;
+    v = max_u64(v, dpp_u64<DPP_QUAD_XOR1>(v));
+    v = max_u64(v, dpp_u64<DPP_QUAD_XOR2>(v));
+    v = max_u64(v, dpp_u64<DPP_HALF_MIRROR>(v));
+    v = max_u64(v, dpp_u64<DPP_ROW_MIRROR>(v));
+    return rows_max_u64(v);
+}
+
+// bfloat16 bits of x, rounded to nearest even (finite x).
+__device__ inline uint32_t bf16_rne_bits(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
 // Sums M per-thread values over the block in a fixed order.  Results land in
@@ -155,13 +241,10 @@ __device__ inline float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
 // (NaN above +inf, -0 folded into +0); low word prefers the lower index.
 __device__ inline uint64_t argmax_key(float f, uint32_t idx)
 {
-    uint32_t ord;
-    if (f != f) {
-        ord = 0xFFFFFFFFu;
-    } else {
-        uint32_t bits = (f == 0.f) ? 0u : __float_as_uint(f);
-        ord = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
-    }
+    // selects only (no branches)
+    const uint32_t bits = (f == 0.f) ? 0u : __float_as_uint(f);
+    uint32_t ord = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+    ord = (f != f) ? 0xFFFFFFFFu : ord;
     return (static_cast<uint64_t>(ord) << 32) | (0xFFFFFFFFu - idx);
 }
 
@@ -186,94 +269,97 @@ __device__ inline float xld(const float *p)
 }
 
 // ---------------------------------------------------------------------------
-// Grid barrier for a cooperative launch (one block per compute unit).
+// Grid barrier for a cooperative launch (every block resident), in two halves
+// so that loads of data published before the previous barrier can be issued
+// between them.
 // Arrival: every thread waits for its own memory operations to complete, the
 // block syncs, and thread 0 writes the new generation into the block's own
-// arrival slot (no contended counter).  Block 0 polls all slots; when every
-// block has arrived it writes the generation into NG release words (one per
-// group of blocks, on separate cache lines) that the other blocks poll.
-// Layout of `bar` (uints): release word g at g*BAR_STRIDE, arrival slots from
-// BAR_SLOTS.  Generations only grow, so the words carry over between launches
-// and need clearing only once.  Spins are bounded: past `spin_limit` polls the
-// block sets DOMINO_FLAG_SYNC_TIMEOUT (bit 1) and grid_sync returns false in
-// every thread of that block; the caller must then leave the kernel.
+// arrival slot.  Wait: every block polls every slot itself (thread i polls
+// slots i, i + NT, ...) until each holds at least the new generation; there is
+// no central block and no release word.  Layout of `bar` (uints): arrival
+// slot of block b at BAR_SLOTS + b.  Generations only grow: a block starts a
+// launch from the value of its own slot, and at the end of a launch writes its
+// final generation there (barrier_finish), so every slot agrees at the next
+// launch and the words need clearing only once.  Spins are bounded: a slot
+// not reached after `spin_limit` polls sets DOMINO_FLAG_SYNC_TIMEOUT (bit 1)
+// and the wait returns false in every thread of that block; the caller must
+// then leave the kernel.
 // ---------------------------------------------------------------------------
 constexpr int BAR_SLOTS = NG * BAR_STRIDE;
 constexpr int MAX_GRID = 1024;
 constexpr int BAR_WORDS_ALL = BAR_SLOTS + MAX_GRID;
 
-__device__ inline unsigned *bar_release(unsigned *bar, int g) { return bar + g * BAR_STRIDE; }
+__device__ inline unsigned *bar_slots(unsigned *bar) { return bar + BAR_SLOTS; }
 
 __device__ inline unsigned barrier_gen_init(unsigned *bar)
 {
-    return __hip_atomic_load(bar_release(bar, blockIdx.x % NG), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(&bar_slots(bar)[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// End of a launch: record the block's final generation in its slot.
+__device__ inline void barrier_finish(unsigned *bar, unsigned gen)
+{
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&bar_slots(bar)[blockIdx.x], gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // `gen` is tracked identically by every thread of the block.
-__device__ inline bool grid_sync(unsigned *bar, unsigned &gen, unsigned spin_limit, unsigned *flags)
+__device__ inline void grid_arrive(unsigned *bar, unsigned gen)
 {
-    __shared__ int s_ok;
-    const unsigned next = gen + 1;
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
-    unsigned *slots = bar + BAR_SLOTS;
     if (threadIdx.x == 0)
-        __hip_atomic_store(&slots[blockIdx.x], next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&bar_slots(bar)[blockIdx.x], gen + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    DH_TRACE((static_cast<int>(gen + 1) - 4) / 2 * 32 + 24);
+}
+
+__device__ inline bool grid_wait(unsigned *bar, unsigned &gen, unsigned spin_limit, unsigned *flags)
+{
+    const unsigned next = gen + 1;
+    const unsigned *slots = bar_slots(bar);
     int ok = 1;
-    if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < static_cast<int>(gridDim.x); i += NT) {
         unsigned spins = 0;
-        for (;;) {
-            int mine = 1;
-            for (int i = threadIdx.x; i < static_cast<int>(gridDim.x); i += blockDim.x)
-                if (__hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != next)
-                    mine = 0;
-            if (__syncthreads_and(mine))
-                break;
+        while (static_cast<int>(__hip_atomic_load(const_cast<unsigned *>(&slots[i]), __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT) - next) < 0) {
             if (++spins > spin_limit) {
-                ok = 0;
-                break;
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        if (threadIdx.x < NG)
-            __hip_atomic_store(bar_release(bar, threadIdx.x), next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (!ok && threadIdx.x == 0)
-            __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (threadIdx.x == 0) {
-        unsigned spins = 0;
-        const unsigned *rel = bar_release(bar, blockIdx.x % NG);
-        while (__hip_atomic_load(const_cast<unsigned *>(rel), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != next) {
-            if (++spins > spin_limit) {
-                __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 ok = 0;
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        s_ok = ok;
     }
     gen = next;
-    __syncthreads();
+    DH_TRACE((static_cast<int>(next) - 4) / 2 * 32 + 26);
+    const int all = __syncthreads_and(ok);
+    if (!all && threadIdx.x == 0)
+        __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    return s_ok != 0;
+    DH_TRACE((static_cast<int>(next) - 4) / 2 * 32 + 27);
+    return all != 0;
+}
+
+__device__ inline bool grid_sync(unsigned *bar, unsigned &gen, unsigned spin_limit, unsigned *flags)
+{
+    grid_arrive(bar, gen);
+    return grid_wait(bar, gen, spin_limit, flags);
 }
 
 // ---------------------------------------------------------------------------
 // Barrier that also reduces the greedy argmax (persistent launch, V <= 2^18).
-// Each block arrives by storing, for each of its nb batch rows, its local
-// argmax key into its own 64-bit arrival word, with the 14 spare high bits of
-// the index field replaced by the generation (an index below 2^18 leaves the
-// top 14 of its 32 bits unused).  Block 0 polls all arrival words; the poll
-// that sees every word at the new generation also holds every partial key, so
-// it reduces them directly and releases the barrier with 64-bit words
-// {generation, token} (one per batch row and group).  Every block leaves with
-// the tokens of this position in tok[0..nb).  Arrival words: aslot[blk*BC + b];
-// release words: arel[g*ASYNC_STRIDE + b].
+// Arrival: each block stores, for each of its nb batch rows, its local argmax
+// key into its own 64-bit word, with the 14 spare high bits of the index
+// field replaced by the generation (an index below 2^18 leaves the top 14 of
+// its 32 bits unused).  The key is the only payload, so arrival needs no wait
+// for earlier memory operations.  Wait: every block reads every word until it
+// carries the new generation and reduces the keys itself, leaving the tokens
+// of this position in tok[0..nb).  Generations compare modulo 2^14 (a word is
+// ready when it is at most 2^13 ahead).  A word is rewritten only at the next
+// argmax barrier, which no block reaches before every block has passed the
+// grid barrier in between.  Arrival words: asy[blk*BC + b].
 // ---------------------------------------------------------------------------
-constexpr int ASYNC_STRIDE = 32;  // u64 per release group (256 bytes)
-constexpr int ASYNC_WORDS = MAX_GRID * BC + NG * ASYNC_STRIDE;
+constexpr int ASYNC_WORDS = MAX_GRID * BC;
 constexpr uint64_t KEY_ORD_MASK = 0xFFFFFFFF00000000ull;
 constexpr uint64_t KEY_IDX_MASK = 0x3FFFFull;
 
@@ -282,100 +368,80 @@ __device__ inline uint64_t argmax_key18(float f, uint32_t idx)
     return (argmax_key(f, 0) & KEY_ORD_MASK) | (KEY_IDX_MASK - idx);
 }
 
-__device__ inline bool grid_argmax_sync(uint64_t *asy, unsigned &gen, const uint64_t *local_key, int nb, int *tok,
-                                        unsigned spin_limit, unsigned *flags)
+// local_key[b] must have been written by thread b, or before a block sync.
+__device__ inline void argmax_arrive(uint64_t *asy, unsigned gen, const uint64_t *local_key, int nb)
 {
-    __shared__ int s_ok;
+    const uint64_t g14 = static_cast<uint64_t>((gen + 1) & 0x3FFFu) << 18;
+    if (threadIdx.x < nb)
+        __hip_atomic_store(&asy[blockIdx.x * BC + threadIdx.x],
+                           (local_key[threadIdx.x] & (KEY_ORD_MASK | KEY_IDX_MASK)) | g14, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    DH_TRACE((static_cast<int>(gen + 1) - 3) / 2 * 32 + 8);
+}
+
+__device__ inline bool argmax_wait(const uint64_t *asy, unsigned &gen, int nb, int *tok, unsigned spin_limit,
+                                   unsigned *flags)
+{
     __shared__ uint64_t s_red[NWAVE * BC];
     const unsigned next = gen + 1;
-    const uint64_t g14 = static_cast<uint64_t>(next & 0x3FFFu) << 18;
-    uint64_t *aslot = asy;
-    uint64_t *arel = asy + MAX_GRID * BC;
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
-    if (threadIdx.x < nb) {
-        const uint64_t k = local_key[threadIdx.x];
-        __hip_atomic_store(&aslot[blockIdx.x * BC + threadIdx.x], (k & (KEY_ORD_MASK | KEY_IDX_MASK)) | g14,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    const unsigned g14 = next & 0x3FFFu;
+    const int total = static_cast<int>(gridDim.x) * nb;
+    uint64_t best[BC];
+#pragma unroll
+    for (int b = 0; b < BC; ++b)
+        best[b] = 0;
     int ok = 1;
-    if (blockIdx.x == 0) {
-        const int total = static_cast<int>(gridDim.x) * nb;
-        uint64_t best[BC];
+    for (int e = threadIdx.x; e < total; e += NT) {
+        const int blk = e / nb, b = e % nb;
+        const uint64_t *wp = &asy[blk * BC + b];
+        uint64_t w;
         unsigned spins = 0;
         for (;;) {
-            int mine = 1;
-#pragma unroll
-            for (int b = 0; b < BC; ++b)
-                best[b] = 0;
-            for (int e = threadIdx.x; e < total; e += blockDim.x) {
-                const int blk = e / nb, b = e % nb;
-                const uint64_t w = __hip_atomic_load(&aslot[blk * BC + b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (((w >> 18) & 0x3FFFu) != (next & 0x3FFFu))
-                    mine = 0;
-                const uint64_t k = w & (KEY_ORD_MASK | KEY_IDX_MASK);
-#pragma unroll
-                for (int bb = 0; bb < BC; ++bb)
-                    if (bb == b && k > best[bb])
-                        best[bb] = k;
-            }
-            if (__syncthreads_and(mine))
+            w = __hip_atomic_load(const_cast<uint64_t *>(wp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (((static_cast<unsigned>(w >> 18) - g14) & 0x3FFFu) < 0x2000u)
                 break;
             if (++spins > spin_limit) {
-                ok = 0;
-                break;
-            }
-        }
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-        for (int b = 0; b < BC; ++b) {
-            const uint64_t m = wave_max_u64(best[b]);
-            if (lane == 0)
-                s_red[wave * BC + b] = m;
-        }
-        __syncthreads();
-        if (threadIdx.x < nb) {
-            uint64_t m = 0;
-            for (int w = 0; w < NWAVE; ++w)
-                m = s_red[w * BC + threadIdx.x] > m ? s_red[w * BC + threadIdx.x] : m;
-            const uint32_t t = m ? static_cast<uint32_t>(KEY_IDX_MASK - (m & KEY_IDX_MASK)) : 0u;
-            const uint64_t rel = (static_cast<uint64_t>(next) << 32) | t;
-            for (int g = 0; g < NG; ++g)
-                __hip_atomic_store(&arel[g * ASYNC_STRIDE + threadIdx.x], rel, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (!ok && threadIdx.x == 0)
-            __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (threadIdx.x == 0) {
-        const int g = blockIdx.x % NG;
-        unsigned spins = 0;
-        for (;;) {
-            int done = 1;
-            for (int b = 0; b < nb; ++b) {
-                const uint64_t w =
-                    __hip_atomic_load(&arel[g * ASYNC_STRIDE + b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (static_cast<unsigned>(w >> 32) != next)
-                    done = 0;
-                else
-                    tok[b] = static_cast<int>(static_cast<uint32_t>(w));
-            }
-            if (done)
-                break;
-            if (++spins > spin_limit) {
-                __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 ok = 0;
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        s_ok = ok;
+        const uint64_t k = w & (KEY_ORD_MASK | KEY_IDX_MASK);
+#pragma unroll
+        for (int bb = 0; bb < BC; ++bb)
+            if (bb == b)
+                best[bb] = max_u64(best[bb], k);
+    }
+    DH_TRACE((static_cast<int>(next) - 3) / 2 * 32 + 11);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int b = 0; b < BC; ++b) {
+        if (b < nb) {
+            const uint64_t m = wave_max_u64(best[b]);
+            if (lane == 0)
+                s_red[wave * BC + b] = m;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < nb) {
+        uint64_t m = 0;
+        for (int w = 0; w < NWAVE; ++w)
+            m = max_u64(m, s_red[w * BC + threadIdx.x]);
+        tok[threadIdx.x] = m ? static_cast<int>(KEY_IDX_MASK - (m & KEY_IDX_MASK)) : 0;
     }
     gen = next;
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    return s_ok != 0;
+    const int all = __syncthreads_and(ok);
+    if (!all && threadIdx.x == 0)
+        __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    DH_TRACE((static_cast<int>(next) - 3) / 2 * 32 + 12);
+    return all != 0;
+}
+
+__device__ inline bool grid_argmax_sync(uint64_t *asy, unsigned &gen, const uint64_t *local_key, int nb, int *tok,
+                                        unsigned spin_limit, unsigned *flags)
+{
+    argmax_arrive(asy, gen, local_key, nb);
+    return argmax_wait(asy, gen, nb, tok, spin_limit, flags);
 }
 
 }  // namespace DH_NS

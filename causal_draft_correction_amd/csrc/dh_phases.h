@@ -361,11 +361,15 @@ __device__ __forceinline__ void state_cache_load(const Params &p, int blk, int n
         const size_t off = state_row_off<WT>(p, m);
         for (int ch = lane; ch < h / EPC; ch += 64)
             wc[(wave * rpw + k) * (h / EPC) + ch] = ld16<WT>(W, off + static_cast<size_t>(ch) * EPC);
-        if (m < p.r)
+        if (m < p.r) {
             for (int i = lane; i < p.K * p.B; i += 64) {
                 const int qq = i / p.B, b = i % p.B;
                 ac[((wave * rpw + k) * p.K + qq) * BC + b] = xld(&p.A_H[(static_cast<size_t>(b) * p.K + qq) * p.r + m]);
             }
+        } else if (lane == 0) {
+            // W_hh rows need no A_H entries: their slot holds the b_hh entry instead
+            ac[(wave * rpw + k) * p.K * BC] = p.b_hh ? WT16<WT>::one(p.b_hh, m - p.r) : 0.f;
+        }
     }
 }
 
@@ -380,6 +384,8 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     float *qn_all = q_slot(p, q + 1);
     const int R = state_rows(p), nch = h / EPC;
+    const int tslot = (q - 1) * 32 + 16;
+    DH_TRACE(tslot);
     for (int b0 = 0; b0 < p.B; b0 += BC) {
         const int nb = (p.B - b0) < BC ? (p.B - b0) : BC;
         __syncthreads();
@@ -387,6 +393,7 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
             if (p.P && threadIdx.x < nb)
                 tok[threadIdx.x] = gru_input_token(p, q, b0 + threadIdx.x, atok ? atok + b0 : nullptr);
             __syncthreads();
+            DH_TRACE(tslot + 1);
             // the first SP_EL elements of this thread use the q values prefetched before the barrier
 #pragma unroll
             for (int e = 0; e < SP_EL; ++e) {
@@ -438,7 +445,9 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
             for (int i = threadIdx.x; i < nb * h; i += NT)
                 S_lds[i] = xld(&S_slot(p, q)[static_cast<size_t>(b0) * h + i]);
         }
+        DH_TRACE(tslot + 2);
         __syncthreads();
+        DH_TRACE(tslot + 3);
         // dot rows of this wave: k-th row m = m0 + k * mstep; when `cached` (persistent
         // launch) the row and its A_H entries come from LDS at `cache`
         const int m0 = blk * NWAVE + wave, mstep = nblk * NWAVE;
@@ -450,7 +459,9 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
             const bool is_u = m < r;
             const void *W = is_u ? p.W1 : p.W_hh;
             const size_t off = state_row_off<WT>(p, m);
-            const float bias = (!is_u && p.b_hh) ? WT16<WT>::one(p.b_hh, m - r) : 0.f;
+            float bias = 0.f;
+            if (!is_u)
+                bias = cached ? ac[(wave * rpw + k) * p.K * BC] : (p.b_hh ? WT16<WT>::one(p.b_hh, m - r) : 0.f);
             const uint4 *wrow = wc + (wave * rpw + k) * nch;
 #pragma unroll 1
             for (int bb = 0; bb < nb; ++bb) {
@@ -476,6 +487,15 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                         const float a = ah + dot;
                         const float u = a * sigmoidf_(a);
                         xst(&p.u_buf[static_cast<size_t>(b) * r + m], u);
+                        if (p.ub16) {
+                            const uint32_t hi = bf16_rne_bits(u);
+                            const uint32_t lo = bf16_rne_bits(u - __uint_as_float(hi << 16));
+                            const size_t o = static_cast<size_t>(b) * r + m;
+                            __hip_atomic_store(&p.ub16[o], static_cast<uint16_t>(hi), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                            __hip_atomic_store(&p.ub16[static_cast<size_t>(p.maxB) * r + o], static_cast<uint16_t>(lo),
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        }
                         if (p.u_out)
                             p.u_out[(static_cast<size_t>(b) * p.K + q) * r + m] = u;
                     } else {
@@ -485,6 +505,7 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
             }
         }
     }
+    DH_TRACE(tslot + 4);
 }
 
 // Epilogue of the W2 phase for batch rows b0..b0+nb-1 of block blk: lbuf holds
@@ -595,9 +616,7 @@ struct W2Rows {
 #pragma unroll
                 for (int q = 0; q < NL; ++q)
                     acc = dot_chunk<WT>(w[ug][q], u_lds + bb * r + (q * LPR + sub) * EPC, acc);
-#pragma unroll
-                for (int o = 1; o < LPR; o <<= 1)
-                    acc += __shfl_xor(acc, o);
+                acc = group_sum<LPR>(acc);
                 if (sub == 0 && row < n)
                     lbuf[bb * rows_cap + row] = acc;
             }
@@ -682,14 +701,15 @@ __device__ __forceinline__ void phase_w2(const Params &p, int blk, int nblk, int
 
 // ---- W2 phase with the block's W2 slice resident on chip (bf16, r = 32 * KS) -------
 // The block's rows [v0, v1) form 16-row tiles.  Tile t is held by wave t % NWAVE:
-// its first RT tiles in registers (wt), the rest in LDS (`tl`, LT_MAX tiles),
-// all loaded once per launch.  Per position each wave multiplies its tiles with
-// u on the matrix cores (v_mfma_f32_16x16x32_bf16): A = 16 W2 rows x 32 of r,
-// B = 32 of r x 16 columns, where column b (< 8) carries bf16(u_b) and column
-// 8 + b carries bf16(u_b - bf16(u_b)); adding the two result columns gives
-// W2 u_b with float32-level accuracy.  Lane l holds A row l%16 and B column l%16
-// at r offsets (l/16)*8 .. +8 of each 32-wide step, and result rows
-// (l/16)*4 + i of column l%16.
+// its first RT tiles in registers (wt), the rest in LDS (`tl`), all loaded once
+// per launch.  Per position each wave multiplies its tiles with u on the matrix
+// cores (v_mfma_f32_16x16x32_bf16): A = 16 W2 rows x 32 of r, B = 32 of r x 16
+// columns, where column b (< 8) carries bf16(u_b) and column 8 + b carries
+// bf16(u_b - bf16(u_b)) (the u operand planes written by phase_state); adding
+// the two result columns gives W2 u_b with float32-level accuracy.  Lane l
+// holds A row l%16 and B column l%16 at r offsets (l/16)*8 .. +8 of each
+// 32-wide step, and result rows (l/16)*4 + i of column l%16.  The epilogue
+// (L_base add, L_final store, greedy argmax) runs on the result registers.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -697,19 +717,6 @@ template <int RT, int KS>
 struct W2Resident {
     uint4 wt[RT][KS];
 };
-
-__device__ inline uint32_t bf16_rne_bits(float x)
-{
-    uint32_t u = __float_as_uint(x);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ inline int w2_tiles(const Params &p, int blk, int nblk)
-{
-    const long long v0 = static_cast<long long>(p.V) * blk / nblk;
-    const int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0);
-    return (n + 15) / 16;
-}
 
 // A operand of tile t, step kk for this lane (zero beyond the block's rows).
 template <int KS>
@@ -744,30 +751,48 @@ __device__ __forceinline__ void w2_resident_load(const Params &p, int blk, int n
     }
 }
 
-// Sum the hi and lo result columns of one tile and write W2 u to lbuf.
-__device__ inline void w2_tile_store(const f32x4_t &acc, float *lbuf, int rows_cap, int nb, int n, int t)
+// The block's L_base slice of position pos ([b][i] at lbuf[b * rows_cap + i])
+// copied into LDS by direct global-to-LDS loads: nothing waits for them here;
+// the next grid barrier (which waits for all of a thread's memory operations)
+// completes them.
+__device__ __forceinline__ void lbase_to_lds(const Params &p, int blk, int nblk, int pos, float *smem)
 {
-    const int lane = threadIdx.x & 63;
-    const int col = lane & 15;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float v = acc[i] + __shfl_xor(acc[i], 8);  // hi column + lo column
-        const int row = t * 16 + (lane >> 4) * 4 + i;
-        if (col < nb && row < n)
-            lbuf[col * rows_cap + row] = v;
+    typedef __attribute__((address_space(3))) void lds_void;
+    const long long v0 = static_cast<long long>(p.V) * blk / nblk;
+    const int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0);
+    const int rows_cap = (p.V + nblk - 1) / nblk;
+    float *dst = smem + smem_off_lbuf(p.r);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int bb = 0; bb < p.B; ++bb) {
+        const float *src = p.L_base + (static_cast<size_t>(bb) * p.K + pos) * p.V + v0;
+        for (int c = wave * 64; c < n; c += NT) {
+            if (c + lane < n)
+                __builtin_amdgcn_global_load_lds(src + c + lane, (lds_void *)(dst + bb * rows_cap + c), 4, 0, 0);
+        }
     }
 }
 
-template <int KS>
-__device__ inline void w2_tile_mma(const uint4 (&a)[KS], const uint4 (&bop)[KS], float *lbuf, int rows_cap, int nb,
-                                   int n, int t)
+// Epilogue of one result tile: W2 u = hi column + lo column (DPP from the lane
+// 8 columns away), plus L_base from LDS; folds the greedy keys of the lane's
+// column into `best` and stores L_final if requested.  Branch-free except for
+// the L_final store: lanes outside the batch rows or the block's rows read an
+// in-range LDS entry and contribute key 0.
+__device__ inline void w2_tile_keys(const Params &p, const f32x4_t &acc, const float *lbase, float *lf, long long v0,
+                                    int rows_cap, int nb, int n, int t, uint64_t &best)
 {
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const int lane = threadIdx.x & 63, col = lane & 15;
+    const int cc = col < nb ? col : nb - 1;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[kk]),
-                                                      __builtin_bit_cast(bf16x8_t, bop[kk]), acc, 0, 0, 0);
-    w2_tile_store(acc, lbuf, rows_cap, nb, n, t);
+    for (int i = 0; i < 4; ++i) {
+        const float w = acc[i] + dpp_f32<DPP_ROW_ROR8>(acc[i]);
+        const int row = t * 16 + (lane >> 4) * 4 + i;
+        const bool ok = col < nb && row < n;
+        const float v = lbase[cc * rows_cap + (row < n ? row : n - 1)] + w;
+        if (lf && ok)
+            lf[static_cast<size_t>(col) * p.K * p.V + row] = v;
+        const uint64_t key = argmax_key(v, static_cast<uint32_t>(v0 + row));
+        best = max_u64(best, ok ? key : 0ull);
+    }
 }
 
 template <int RT, int KS>
@@ -776,55 +801,40 @@ __device__ __forceinline__ void phase_w2_resident(const Params &p, int blk, int 
                                                   uint64_t *local_keys)
 {
     const int r = 32 * KS;
-    const long long v0 = static_cast<long long>(p.V) * blk / nblk;
-    const int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0);
+    int v0i = static_cast<int>(static_cast<long long>(p.V) * blk / nblk);  // V < 2^31
+    int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0i);
+    // opaque per call: keeps the compiler from hoisting the per-row index and
+    // bound values of every tile out of the position loop into spilled registers
+    asm volatile("" : "+s"(v0i), "+s"(n));
+    const long long v0 = v0i;
     const int T = (n + 15) / 16;
     const int rows_cap = (p.V + nblk - 1) / nblk;
-    // B operand in LDS, [kk][lane] (16 bytes each), built once per block in the u area
-    static_assert(KS * 64 * 4 <= BC * 32 * KS && (KS * 64) % NT == 0, "operand must fit the u area");
-    uint4 *bop_lds = reinterpret_cast<uint4 *>(smem + smem_off_u());
-    float *lbuf = smem + smem_off_lbuf(r);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float *lbase = smem + smem_off_lbuf(r);
+    uint64_t *kred = reinterpret_cast<uint64_t *>(smem + 32);  // after local_keys (BC u64 at smem)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15;
     const int nb = p.B;  // persistent launches take B <= BC
-    float lbv[W2_LB];
-    w2_lbase_prefetch(p, blk, nblk, pos, 0, lbv);
-    __syncthreads();
-    // stage u in the B-operand area, pull each thread's inputs into registers, then
-    // overwrite the area with the operand: column c < 8 carries bf16(u_c), column
-    // 8 + c carries bf16(u_c - bf16(u_c))
-    constexpr int EPT = KS * 64 / NT;  // operand entries per thread
-    float *u_stage = reinterpret_cast<float *>(bop_lds);
-    for (int i = threadIdx.x; i < nb * r; i += NT)
-        u_stage[i] = xld(&p.u_buf[i]);
-    __syncthreads();
-    float xv[EPT][8];
-#pragma unroll
-    for (int q = 0; q < EPT; ++q) {
-        const int e = threadIdx.x + q * NT;
-        const int kk = e >> 6, l = e & 63, b = l & 7;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            xv[q][j] = b < nb ? u_stage[b * r + kk * 32 + (l >> 4) * 8 + j] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < EPT; ++q) {
-        const int e = threadIdx.x + q * NT;
-        const int col = e & 15;
-        uint32_t hv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t xh = bf16_rne_bits(xv[q][j]);
-            hv[j] = col < 8 ? xh : bf16_rne_bits(xv[q][j] - __uint_as_float(xh << 16));
-        }
-        bop_lds[e] = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
-                                hv[6] | (hv[7] << 16));
-    }
-    __syncthreads();
+    float *lf = p.L_final ? p.L_final + static_cast<size_t>(pos) * p.V + v0 : nullptr;
+    DH_TRACE(pos * 32);
+    // B operand straight from the u operand planes: column col reads plane col / 8
+    // (hi, lo) of batch row col % 8, 8 bf16 values per 32-wide step
     uint4 bop[KS];
+    {
+        const int b = col & 7;
+        const uint64_t *src = reinterpret_cast<const uint64_t *>(
+            p.ub16 + (static_cast<size_t>(col >> 3) * p.maxB + b) * r + (lane >> 4) * 8);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-        bop[kk] = bop_lds[kk * 64 + lane];
+        for (int kk = 0; kk < KS; ++kk) {
+            if (b < nb) {
+                const uint64_t x = ld_agent_u64(src + kk * 8), y = ld_agent_u64(src + kk * 8 + 1);
+                bop[kk] = make_uint4(static_cast<uint32_t>(x), static_cast<uint32_t>(x >> 32), static_cast<uint32_t>(y),
+                                     static_cast<uint32_t>(y >> 32));
+            } else {
+                bop[kk] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    }
+    DH_TRACE(pos * 32 + 2);
+    uint64_t best = 0;
     // register tiles in groups of GR: independent accumulators, steps interleaved
     constexpr int GR = 4;
 #pragma unroll
@@ -845,9 +855,10 @@ __device__ __forceinline__ void phase_w2_resident(const Params &p, int blk, int 
         for (int j = 0; j < GR; ++j) {
             const int t = wave + (g0 + j) * NWAVE;
             if (g0 + j < RT && t < T)
-                w2_tile_store(acc[j], lbuf, rows_cap, nb, n, t);
+                w2_tile_keys(p, acc[j], lbase, lf, v0, rows_cap, nb, n, t, best);
         }
     }
+    DH_TRACE(pos * 32 + 3);
     // LDS tiles, two at a time
 #pragma unroll 1
     for (int t = NWAVE * RT + wave; t < T; t += 2 * NWAVE) {
@@ -863,12 +874,23 @@ __device__ __forceinline__ void phase_w2_resident(const Params &p, int blk, int 
                     __builtin_bit_cast(bf16x8_t, tl[(s1 * KS + kk) * 64 + lane]), __builtin_bit_cast(bf16x8_t, bop[kk]),
                     a1, 0, 0, 0);
         }
-        w2_tile_store(a0, lbuf, rows_cap, nb, n, t);
+        w2_tile_keys(p, a0, lbase, lf, v0, rows_cap, nb, n, t, best);
         if (two)
-            w2_tile_store(a1, lbuf, rows_cap, nb, n, t + NWAVE);
+            w2_tile_keys(p, a1, lbase, lf, v0, rows_cap, nb, n, t + NWAVE, best);
     }
+    DH_TRACE(pos * 32 + 4);
+    // block's key per batch row: over the lanes of a column, then over the waves
+    best = rows_max_u64(best);
+    if (lane < nb)
+        kred[wave * BC + lane] = best;
     __syncthreads();
-    w2_epilogue(p, blk, nblk, pos, smem, 0, nb, lbv, local_keys);
+    if (threadIdx.x < nb) {
+        uint64_t m = 0;
+        for (int w = 0; w < NWAVE; ++w)
+            m = max_u64(m, kred[w * BC + threadIdx.x]);
+        local_keys[threadIdx.x] = m ? (m & KEY_ORD_MASK) | (KEY_IDX_MASK - key_index(m)) : 0ull;
+    }
+    DH_TRACE(pos * 32 + 5);
 }
 
 }  // namespace DH_NS

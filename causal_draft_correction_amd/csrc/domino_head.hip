@@ -112,14 +112,17 @@ __global__ __launch_bounds__(NT) void k_persistent(Params p)
     state_cache_load<WT>(p, blk, nblk, cache);
     state_prefetch<WT>(p, 0, spre);
     phase_state<WT>(p, blk, nblk, 0, smem, S_lds, &spre, cache, true);
+    grid_arrive(p.bar, gen);
     w2_prefetch<WT, LPR, NL>(p, blk, nblk, wpre);
-    if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+    if (!grid_wait(p.bar, gen, p.spin_limit, p.flags))
         return;
     for (int pos = 0; pos < p.K; ++pos) {
         phase_w2<WT, LPR, NL>(p, blk, nblk, pos, smem, &wpre, local_keys);
+        // loads of data published before the previous barrier go between arrival and wait
+        argmax_arrive(p.asy, gen, local_keys, p.B);
         if (pos + 1 < p.K)
             state_prefetch<WT>(p, pos + 1, spre);
-        if (!grid_argmax_sync(p.asy, gen, local_keys, p.B, atok, p.spin_limit, p.flags))
+        if (!argmax_wait(p.asy, gen, p.B, atok, p.spin_limit, p.flags))
             return;
         if (blk == 0 && threadIdx.x < p.B)
             p.tokens[static_cast<size_t>(threadIdx.x) * p.K + pos] = bad[threadIdx.x] ? -1 : atok[threadIdx.x];
@@ -130,11 +133,13 @@ __global__ __launch_bounds__(NT) void k_persistent(Params p)
                     return;
             }
             phase_state<WT>(p, blk, nblk, pos + 1, smem, S_lds, &spre, cache, true, atok);
+            grid_arrive(p.bar, gen);
             w2_prefetch<WT, LPR, NL>(p, blk, nblk, wpre);
-            if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+            if (!grid_wait(p.bar, gen, p.spin_limit, p.flags))
                 return;
         }
     }
+    barrier_finish(p.bar, gen);
 }
 
 
@@ -235,7 +240,7 @@ constexpr int W2_STEP_ROWS = 128;  // vocabulary rows per block in stepwise W2 l
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, q_buf, g_buf, P, total;
+    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, ub16, q_buf, g_buf, P, total;
 };
 
 Layout layout_of(const domino_head_config &c)
@@ -256,6 +261,8 @@ Layout layout_of(const domino_head_config &c)
     off = align_up(off + sizeof(float) * 2 * static_cast<size_t>(c.max_batch) * c.h);
     L.u_buf = off;
     off = align_up(off + sizeof(float) * static_cast<size_t>(c.max_batch) * c.r);
+    L.ub16 = off;
+    off = align_up(off + sizeof(uint16_t) * 2 * static_cast<size_t>(c.max_batch) * c.r);
     L.q_buf = off;
     off = align_up(off + sizeof(float) * 2 * static_cast<size_t>(c.max_batch) * 3 * c.h);
     L.g_buf = off;
@@ -374,6 +381,23 @@ struct domino_head {
     hipStream_t last_stream;
     unsigned spin_limit;
 };
+
+// Launch taken by a draft of B rows: the single cooperative launch (persistent) or the
+// per-step launches; the persistent one keeps W2 on chip (resident) when that variant
+// fits.  Returns false when the handle forces a persistent launch that cannot run.
+static bool choose_launch(const domino_head *hd, int B, bool *persistent, bool *resident)
+{
+    const unsigned fl = hd->cfg.flags;
+    bool pers = (fl & DOMINO_EXEC_PERSISTENT) ? true : (fl & DOMINO_EXEC_STEPWISE) ? false : B <= BC;
+    if (pers && (hd->persist_grid == 0 || B > BC)) {
+        if (fl & DOMINO_EXEC_PERSISTENT)
+            return false;
+        pers = false;
+    }
+    *persistent = pers;
+    *resident = pers && hd->res_grid > 0 && !(fl & DOMINO_EXEC_STREAM_W2);
+    return true;
+}
 
 extern "C" {
 
@@ -546,19 +570,9 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
     if (dev != hd->device)
         return fail(DOMINO_EINVAL, "current device %d differs from the handle's device %d", dev, hd->device);
 
-    bool persistent;
-    if (c.flags & DOMINO_EXEC_PERSISTENT)
-        persistent = true;
-    else if (c.flags & DOMINO_EXEC_STEPWISE)
-        persistent = false;
-    else
-        persistent = B <= BC;
-    if (persistent && (hd->persist_grid == 0 || B > BC)) {
-        if (c.flags & DOMINO_EXEC_PERSISTENT)
-            return fail(DOMINO_EUNSUPPORTED, "persistent launch needs B <= %d and one resident block per compute unit",
-                        BC);
-        persistent = false;
-    }
+    bool persistent, resident;
+    if (!choose_launch(hd, B, &persistent, &resident))
+        return fail(DOMINO_EUNSUPPORTED, "persistent launch needs B <= %d and one resident block per compute unit", BC);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!hd->state_ready) {
         hipLaunchKernelGGL(k_clear_state, dim3(1), dim3(256), 0, st, reinterpret_cast<unsigned *>(hd->ws + hd->L.bar),
@@ -568,10 +582,12 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
         hd->state_ready = true;
     }
     Params p = make_params(hd, B, H, L_base, last_tok, teacher, S_init, tokens, L_final, S_out, u_out, persistent);
+    if (resident)
+        p.ub16 = reinterpret_cast<uint16_t *>(hd->ws + hd->L.ub16);
     hd->last_stream = st;
     if (persistent) {
         void *args[] = {&p};
-        if (hd->res_grid && !(c.flags & DOMINO_EXEC_STREAM_W2)) {
+        if (resident) {
             HIP_TRY(hipLaunchCooperativeKernel(dhres::kernel(), dim3(hd->res_grid), dim3(dhres::threads()), args,
                                                static_cast<unsigned>(hd->res_smem), st),
                     "hipLaunchCooperativeKernel(persistent, resident W2)");
@@ -638,6 +654,24 @@ int domino_accept_len(int32_t B, int32_t K, const int32_t *draft, const int32_t 
     hipLaunchKernelGGL(k_accept_len, dim3((B + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), B, K,
                        draft, target, out_len);
     HIP_TRY(hipGetLastError(), "launch k_accept_len");
+    return DOMINO_OK;
+}
+
+int domino_head_exec_info(domino_head_t hd, int32_t B, int32_t *persistent, int32_t *w2_resident, int32_t *grid)
+{
+    if (!hd)
+        return fail(DOMINO_EINVAL, "handle is NULL");
+    if (B < 1 || B > hd->cfg.max_batch)
+        return fail(DOMINO_EINVAL, "B=%d outside [1, max_batch=%d]", B, hd->cfg.max_batch);
+    bool pers, res;
+    if (!choose_launch(hd, B, &pers, &res))
+        return fail(DOMINO_EUNSUPPORTED, "persistent launch needs B <= %d and one resident block per compute unit", BC);
+    if (persistent)
+        *persistent = pers;
+    if (w2_resident)
+        *w2_resident = res;
+    if (grid)
+        *grid = !pers ? 0 : res ? hd->res_grid : hd->persist_grid;
     return DOMINO_OK;
 }
 

@@ -31,6 +31,7 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
     }
     phase_ah<bf16s>(p, blk, nblk, smem);
     phase_q_init<bf16s>(p, blk, nblk);
+    lbase_to_lds(p, blk, nblk, 0, smem);
     if (!p.P)
         phase_g<bf16s>(p, blk, nblk, 0, smem);
     // the slice load overlaps the first barrier and state phase
@@ -46,9 +47,14 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
         return;
     for (int pos = 0; pos < p.K; ++pos) {
         phase_w2_resident<RT, KS>(p, blk, nblk, pos, smem, res, tl, local_keys);
-        if (pos + 1 < p.K)
+        // loads of data published before the previous barrier (and of inputs) go
+        // between arrival and wait
+        argmax_arrive(p.asy, gen, local_keys, p.B);
+        if (pos + 1 < p.K) {
             state_prefetch<bf16s>(p, pos + 1, spre);
-        if (!grid_argmax_sync(p.asy, gen, local_keys, p.B, atok, p.spin_limit, p.flags))
+            lbase_to_lds(p, blk, nblk, pos + 1, smem);
+        }
+        if (!argmax_wait(p.asy, gen, p.B, atok, p.spin_limit, p.flags))
             return;
         if (blk == 0 && threadIdx.x < p.B)
             p.tokens[static_cast<size_t>(threadIdx.x) * p.K + pos] = bad[threadIdx.x] ? -1 : atok[threadIdx.x];
@@ -63,6 +69,7 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
                 return;
         }
     }
+    barrier_finish(p.bar, gen);
 }
 
 

@@ -143,6 +143,17 @@ int domino_accept_len(int32_t B, int32_t K, const int32_t *draft, const int32_t 
  */
 int domino_head_check_error(domino_head_t hd, uint32_t *device_flags);
 
+/*
+ * Host only, no device work.  Which launch domino_head_draft takes for B rows
+ * on this handle: *persistent = 1 for the single cooperative launch that runs
+ * the whole drafting loop, 0 for one launch per step; *w2_resident = 1 when
+ * that persistent launch keeps each block's share of W2 on chip across the K
+ * positions instead of re-reading it; *grid = blocks of the persistent launch
+ * (0 for the per-step launches).  Output pointers may be NULL.  Same errors as
+ * domino_head_draft for B and for a forced persistent launch that cannot run.
+ */
+int domino_head_exec_info(domino_head_t hd, int32_t B, int32_t *persistent, int32_t *w2_resident, int32_t *grid);
+
 /* Host only.  Parameters of the head: r(d+h) + V r + 3h d + 3h h (+ 6h if GRU biases are given). */
 int domino_head_param_count(const domino_head_config *cfg, int64_t *n);
 

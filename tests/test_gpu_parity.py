@@ -270,11 +270,16 @@ def test_resident_w2_slice_matches_oracle(V, B, fold):
     w = ds.make_weights(sh, (9, 60), gru_sensitive=True)
     inp = ds.make_inputs(sh, B, (9, 61), sigma=0.5, peak="none")
     head = make_head(w, B, dca.EXEC_PERSISTENT, fold=fold)
+    info = head.exec_info(B)
+    assert info["persistent"] and info["w2_resident"] and info["grid"] > 0, info
     run_both_protocols(w, inp, head, label="resident V=%d B=%d fold=%d" % (V, B, fold))
     a, _ = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
     b, _ = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
     for k in ("tokens", "L_final", "S", "u"):
         assert np.array_equal(a[k], b[k]), k
     st = make_head(w, B, dca.EXEC_PERSISTENT | dca.EXEC_STREAM_W2, fold=fold)
+    assert st.exec_info(B)["w2_resident"] is False
+    assert make_head(w, B, dca.EXEC_STEPWISE, fold=fold).exec_info(B) == {"persistent": False, "w2_resident": False,
+                                                                          "grid": 0}
     c, _ = gpu_draft(st, inp.H, inp.L_base, inp.last_tok)
     assert np.abs(c["L_final"] - a["L_final"]).max() < 1e-4

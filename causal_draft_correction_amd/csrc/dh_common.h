@@ -351,10 +351,9 @@ __device__ inline bool grid_sync(unsigned *bar, unsigned &gen, unsigned spin_lim
 // Arrival: each block stores, for each of its nb batch rows, its local argmax
 // key into its own 64-bit word, with the 14 spare high bits of the index
 // field replaced by the generation (an index below 2^18 leaves the top 14 of
-// its 32 bits unused).  The key is the only payload, so arrival needs no wait
-// for earlier memory operations.  Wait: every block reads every word until it
+// its 32 bits unused).  Wait: every block reads every word until it
 // carries the new generation and reduces the keys itself, leaving the tokens
-// of this position in tok[0..nb).  Generations compare modulo 2^14 (a word is
+// of this position in tok[0..nb) (tok[b] written by thread b).  Generations compare modulo 2^14 (a word is
 // ready when it is at most 2^13 ahead).  A word is rewritten only at the next
 // argmax barrier, which no block reaches before every block has passed the
 // grid barrier in between.  Arrival words: asy[blk*BC + b].
@@ -369,14 +368,19 @@ __device__ inline uint64_t argmax_key18(float f, uint32_t idx)
 }
 
 // local_key[b] must have been written by thread b, or before a block sync.
+// Arrival also publishes the block's earlier stores (like grid_arrive): after
+// the wait every block sees them.
 __device__ inline void argmax_arrive(uint64_t *asy, unsigned gen, const uint64_t *local_key, int nb)
 {
     const uint64_t g14 = static_cast<uint64_t>((gen + 1) & 0x3FFFu) << 18;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
     if (threadIdx.x < nb)
         __hip_atomic_store(&asy[blockIdx.x * BC + threadIdx.x],
                            (local_key[threadIdx.x] & (KEY_ORD_MASK | KEY_IDX_MASK)) | g14, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-    DH_TRACE((static_cast<int>(gen + 1) - 3) / 2 * 32 + 8);
+    DH_TRACE((static_cast<int>(gen + 1) - 2) * 32 + 8);
 }
 
 __device__ inline bool argmax_wait(const uint64_t *asy, unsigned &gen, int nb, int *tok, unsigned spin_limit,
@@ -412,7 +416,7 @@ __device__ inline bool argmax_wait(const uint64_t *asy, unsigned &gen, int nb, i
             if (bb == b)
                 best[bb] = max_u64(best[bb], k);
     }
-    DH_TRACE((static_cast<int>(next) - 3) / 2 * 32 + 11);
+    DH_TRACE((static_cast<int>(next) - 2) * 32 + 11);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int b = 0; b < BC; ++b) {
@@ -433,7 +437,7 @@ __device__ inline bool argmax_wait(const uint64_t *asy, unsigned &gen, int nb, i
     const int all = __syncthreads_and(ok);
     if (!all && threadIdx.x == 0)
         __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    DH_TRACE((static_cast<int>(next) - 3) / 2 * 32 + 12);
+    DH_TRACE((static_cast<int>(next) - 2) * 32 + 12);
     return all != 0;
 }
 

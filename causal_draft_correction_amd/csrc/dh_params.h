@@ -20,7 +20,8 @@ struct Params {
     float *A_H;      // [maxB, K, r]
     float *S_buf;    // [2, maxB, h]  state carried between stepwise launches
     float *u_buf;    // [maxB, r]
-    uint16_t *ub16;  // [2, maxB, r] bf16 hi and lo parts of u (matrix-core operand) or nullptr
+    uint32_t *utag;  // [2, maxB, r] u as matrix-core operand: words (tag << 16) | bf16 bits of the
+                     // hi part (plane 0) and lo part (plane 1) of u, or nullptr
     float *q_buf;    // [2, maxB, 3h] W_hh S + b_hh
     float *g_buf;    // [maxB, 3h]    W_ih E[x] + b_ih (when not folded)
     uint64_t *keys;  // [K, NG, maxB] partial argmax keys

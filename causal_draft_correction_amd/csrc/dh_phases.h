@@ -42,6 +42,8 @@ __host__ __device__ inline int smem_off_tok() { return 256 + 2 * NWAVE; }
 __host__ __device__ inline int smem_off_u() { return 256 + 2 * NWAVE + TOK_SLOTS; }
 __host__ __device__ inline int smem_off_lbuf(int r) { return smem_off_u() + BC * r; }
 __host__ __device__ inline int smem_off_S(int r, int rows_cap) { return smem_off_lbuf(r) + BC * rows_cap; }
+// Row stride of lbuf: the block's vocabulary rows, padded to whole 16-row tiles.
+__host__ __device__ inline int lbuf_stride(int V, int nblk) { return ((V + nblk - 1) / nblk + 15) & ~15; }
 __host__ __device__ inline int smem_floats_small() { return smem_off_u(); }
 __host__ __device__ inline int smem_floats_w2(int r, int rows_cap) { return smem_off_S(r, rows_cap); }
 __host__ __device__ inline int smem_floats(int r, int h, int rows_cap) { return smem_off_S(r, rows_cap) + BC * h; }
@@ -208,7 +210,7 @@ __device__ __forceinline__ void phase_g(const Params &p, int blk, int nblk, int 
         const int nb = (p.B - b0) < BC ? (p.B - b0) : BC;
         __syncthreads();
         if (threadIdx.x < nb)
-            tok[threadIdx.x] = gru_input_token(p, q, b0 + threadIdx.x, atok ? atok + b0 : nullptr);
+            tok[threadIdx.x] = gru_input_token(p, q, b0 + threadIdx.x, atok);
         __syncthreads();
         for (int m = blk * NWAVE + wave; m < h3; m += nblk * NWAVE) {
             const float bias = p.b_ih ? WT16<WT>::one(p.b_ih, m) : 0.f;
@@ -373,14 +375,17 @@ __device__ __forceinline__ void state_cache_load(const Params &p, int blk, int n
     }
 }
 
+// With p.utag (resident launch) u_q is published as tagged operand words
+// instead of u_buf: (tag << 16) | bf16 bits, hi part in plane 0 and lo part
+// (u - hi) in plane 1; readers poll for `tag`.
 template <typename WT>
 __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, int q, float *smem, float *S_lds,
                                             const StatePre *pre, const float *cache, bool cached,
-                                            const int *atok = nullptr)
+                                            const int *atok = nullptr, unsigned tag = 0)
 {
     constexpr int EPC = WT16<WT>::EPC;
     const int h = p.h, h3 = 3 * h, r = p.r;
-    int *tok = reinterpret_cast<int *>(smem + smem_off_tok());
+    (void)smem;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     float *qn_all = q_slot(p, q + 1);
     const int R = state_rows(p), nch = h / EPC;
@@ -388,11 +393,10 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
     DH_TRACE(tslot);
     for (int b0 = 0; b0 < p.B; b0 += BC) {
         const int nb = (p.B - b0) < BC ? (p.B - b0) : BC;
-        __syncthreads();
         if (p.persistent) {
-            if (p.P && threadIdx.x < nb)
-                tok[threadIdx.x] = gru_input_token(p, q, b0 + threadIdx.x, atok ? atok + b0 : nullptr);
-            __syncthreads();
+            // B <= BC: one chunk.  Each thread takes the GRU input token itself
+            // (atok entries were written before the argmax barrier's last block
+            // sync); the state never leaves the block, so S_buf is not written.
             DH_TRACE(tslot + 1);
             // the first SP_EL elements of this thread use the q values prefetched before the barrier
 #pragma unroll
@@ -401,11 +405,12 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                 if (i < nb * h) {
                     const int bb = i / h, j = i % h, b = b0 + bb;
                     const float sprev = (q == 0) ? state_prev(p, 0, b, j) : S_lds[bb * h + j];
+                    const int tokb = p.P ? gru_input_token(p, q, b, atok) : 0;
                     float sn;
                     if (pre && b0 == 0) {
                         float gr, gz, gn;
                         if (p.P) {
-                            const float *prow = p.P + static_cast<size_t>(tok[bb]) * h3;
+                            const float *prow = p.P + static_cast<size_t>(tokb) * h3;
                             gr = prow[j];
                             gz = prow[h + j];
                             gn = prow[2 * h + j];
@@ -420,28 +425,23 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                         const float ng = tanhf(gn + rg * pre->qv[e][2]);
                         sn = (1.f - zg) * ng + zg * sprev;
                     } else {
-                        sn = gate_update(p, q, b, j, p.P ? tok[bb] : 0, sprev);
+                        sn = gate_update(p, q, b, j, tokb, sprev);
                     }
                     S_lds[bb * h + j] = sn;  // each thread reads only the entry it writes
-                    if (blk == 0) {
-                        xst(&S_slot(p, q)[static_cast<size_t>(b) * h + j], sn);
-                        if (p.S_out)
-                            p.S_out[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
-                    }
+                    if (blk == 0 && p.S_out)
+                        p.S_out[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
                 }
             }
             for (int i = threadIdx.x + SP_EL * NT; i < nb * h; i += NT) {
                 const int bb = i / h, j = i % h, b = b0 + bb;
                 const float sprev = (q == 0) ? state_prev(p, 0, b, j) : S_lds[bb * h + j];
-                const float sn = gate_update(p, q, b, j, p.P ? tok[bb] : 0, sprev);
+                const float sn = gate_update(p, q, b, j, p.P ? gru_input_token(p, q, b, atok) : 0, sprev);
                 S_lds[bb * h + j] = sn;
-                if (blk == 0) {
-                    xst(&S_slot(p, q)[static_cast<size_t>(b) * h + j], sn);
-                    if (p.S_out)
-                        p.S_out[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
-                }
+                if (blk == 0 && p.S_out)
+                    p.S_out[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
             }
         } else {
+            __syncthreads();  // S_lds of the previous chunk is no longer read
             for (int i = threadIdx.x; i < nb * h; i += NT)
                 S_lds[i] = xld(&S_slot(p, q)[static_cast<size_t>(b0) * h + i]);
         }
@@ -449,57 +449,72 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
         __syncthreads();
         DH_TRACE(tslot + 3);
         // dot rows of this wave: k-th row m = m0 + k * mstep; when `cached` (persistent
-        // launch) the row and its A_H entries come from LDS at `cache`
+        // launch) the row and its A_H entries come from LDS at `cache`.  Rows go in
+        // groups of RG: the S chunks are read once per group and the RG sums are
+        // reduced together (each row's sum is formed in the same order as alone).
+        constexpr int RG = 4;
         const int m0 = blk * NWAVE + wave, mstep = nblk * NWAVE;
         const int rpw = state_rows_per_wave(r, h, nblk);
         const uint4 *wc = reinterpret_cast<const uint4 *>(cache);
         const float *ac = cache + NWAVE * rpw * (h * static_cast<int>(sizeof(WT)) / 4);
 #pragma unroll 1
-        for (int k = 0, m = m0; m < R; ++k, m += mstep) {
-            const bool is_u = m < r;
-            const void *W = is_u ? p.W1 : p.W_hh;
-            const size_t off = state_row_off<WT>(p, m);
-            float bias = 0.f;
-            if (!is_u)
-                bias = cached ? ac[(wave * rpw + k) * p.K * BC] : (p.b_hh ? WT16<WT>::one(p.b_hh, m - r) : 0.f);
-            const uint4 *wrow = wc + (wave * rpw + k) * nch;
+        for (int k0 = 0; m0 + k0 * mstep < R; k0 += RG) {
 #pragma unroll 1
             for (int bb = 0; bb < nb; ++bb) {
                 const int b = b0 + bb;
-                float ah = 0.f;
-                if (is_u)
-                    ah = cached ? ac[((wave * rpw + k) * p.K + q) * BC + b]
-                                : xld(&p.A_H[(static_cast<size_t>(b) * p.K + q) * r + m]);
                 const float *s = S_lds + bb * h;
-                float acc = 0.f;
+                float acc[RG];
+#pragma unroll
+                for (int j = 0; j < RG; ++j)
+                    acc[j] = 0.f;
 #pragma unroll 2
                 for (int ch = lane; ch < nch; ch += 64) {
                     float x[EPC];
 #pragma unroll
                     for (int i2 = 0; i2 < EPC; ++i2)
                         x[i2] = s[ch * EPC + i2];
-                    const uint4 wq = cached ? wrow[ch] : ld16<WT>(W, off + static_cast<size_t>(ch) * EPC);
-                    acc = dot_chunk<WT>(wq, x, acc);
+#pragma unroll
+                    for (int j = 0; j < RG; ++j) {
+                        const int k = k0 + j, m = m0 + k * mstep;
+                        if (m < R) {
+                            const uint4 wq = cached ? wc[(wave * rpw + k) * nch + ch]
+                                                    : ld16<WT>(m < r ? p.W1 : p.W_hh,
+                                                               state_row_off<WT>(p, m) + static_cast<size_t>(ch) * EPC);
+                            acc[j] = dot_chunk<WT>(wq, x, acc[j]);
+                        }
+                    }
                 }
-                const float dot = wave_sum(acc);
-                if (lane == 0) {
-                    if (is_u) {
-                        const float a = ah + dot;
+                float dot[RG];
+#pragma unroll
+                for (int j = 0; j < RG; ++j)
+                    dot[j] = wave_sum(acc[j]);
+#pragma unroll
+                for (int j = 0; j < RG; ++j) {
+                    const int k = k0 + j, m = m0 + k * mstep;
+                    if (lane != 0 || m >= R)
+                        continue;
+                    if (m < r) {
+                        const float ah = cached ? ac[((wave * rpw + k) * p.K + q) * BC + b]
+                                                : xld(&p.A_H[(static_cast<size_t>(b) * p.K + q) * r + m]);
+                        const float a = ah + dot[j];
                         const float u = a * sigmoidf_(a);
-                        xst(&p.u_buf[static_cast<size_t>(b) * r + m], u);
-                        if (p.ub16) {
+                        if (p.utag) {
                             const uint32_t hi = bf16_rne_bits(u);
                             const uint32_t lo = bf16_rne_bits(u - __uint_as_float(hi << 16));
+                            const uint32_t t16 = (tag & 0xFFFFu) << 16;
                             const size_t o = static_cast<size_t>(b) * r + m;
-                            __hip_atomic_store(&p.ub16[o], static_cast<uint16_t>(hi), __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-                            __hip_atomic_store(&p.ub16[static_cast<size_t>(p.maxB) * r + o], static_cast<uint16_t>(lo),
+                            __hip_atomic_store(&p.utag[o], t16 | hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            __hip_atomic_store(&p.utag[static_cast<size_t>(p.maxB) * r + o], t16 | lo,
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        } else {
+                            xst(&p.u_buf[static_cast<size_t>(b) * r + m], u);
                         }
                         if (p.u_out)
                             p.u_out[(static_cast<size_t>(b) * p.K + q) * r + m] = u;
                     } else {
-                        xst(&qn_all[static_cast<size_t>(b) * h3 + (m - r)], dot + bias);
+                        const float bias =
+                            cached ? ac[(wave * rpw + k) * p.K * BC] : (p.b_hh ? WT16<WT>::one(p.b_hh, m - r) : 0.f);
+                        xst(&qn_all[static_cast<size_t>(b) * h3 + (m - r)], dot[j] + bias);
                     }
                 }
             }
@@ -518,7 +533,7 @@ __device__ __forceinline__ void w2_epilogue(const Params &p, int blk, int nblk, 
 {
     const long long v0 = static_cast<long long>(p.V) * blk / nblk;
     const int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0);
-    const int rows_cap = (p.V + nblk - 1) / nblk;
+    const int rows_cap = lbuf_stride(p.V, nblk);
     uint64_t *kred = reinterpret_cast<uint64_t *>(smem + 256);
     const float *lbuf = smem + smem_off_lbuf(p.r);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -654,7 +669,7 @@ __device__ __forceinline__ void phase_w2(const Params &p, int blk, int nblk, int
     const long long v0 = static_cast<long long>(p.V) * blk / nblk;
     const long long v1 = static_cast<long long>(p.V) * (blk + 1) / nblk;
     const int n = static_cast<int>(v1 - v0);
-    const int rows_cap = (p.V + nblk - 1) / nblk;
+    const int rows_cap = lbuf_stride(p.V, nblk);
     float *u_lds = smem + smem_off_u();
     float *lbuf = smem + smem_off_lbuf(r);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -752,15 +767,14 @@ __device__ __forceinline__ void w2_resident_load(const Params &p, int blk, int n
 }
 
 // The block's L_base slice of position pos ([b][i] at lbuf[b * rows_cap + i])
-// copied into LDS by direct global-to-LDS loads: nothing waits for them here;
-// the next grid barrier (which waits for all of a thread's memory operations)
-// completes them.
+// copied into LDS by direct global-to-LDS loads: nothing waits for them here
+// (the compiler waits for them before the next LDS access of the thread).
 __device__ __forceinline__ void lbase_to_lds(const Params &p, int blk, int nblk, int pos, float *smem)
 {
     typedef __attribute__((address_space(3))) void lds_void;
     const long long v0 = static_cast<long long>(p.V) * blk / nblk;
     const int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0);
-    const int rows_cap = (p.V + nblk - 1) / nblk;
+    const int rows_cap = lbuf_stride(p.V, nblk);
     float *dst = smem + smem_off_lbuf(p.r);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int bb = 0; bb < p.B; ++bb) {
@@ -772,22 +786,32 @@ __device__ __forceinline__ void lbase_to_lds(const Params &p, int blk, int nblk,
     }
 }
 
-// Epilogue of one result tile: W2 u = hi column + lo column (DPP from the lane
-// 8 columns away), plus L_base from LDS; folds the greedy keys of the lane's
-// column into `best` and stores L_final if requested.  Branch-free except for
-// the L_final store: lanes outside the batch rows or the block's rows read an
-// in-range LDS entry and contribute key 0.
-__device__ inline void w2_tile_keys(const Params &p, const f32x4_t &acc, const float *lbase, float *lf, long long v0,
-                                    int rows_cap, int nb, int n, int t, uint64_t &best)
+// L_base values of the four result rows this lane holds in tile t (one 16-byte
+// LDS read; rows_cap is a multiple of 16, so every tile row lies inside the
+// batch row's stride, and lanes of columns >= nb read row nb - 1).
+__device__ inline float4 w2_tile_lbase(const float *lbase, int rows_cap, int nb, int t)
 {
     const int lane = threadIdx.x & 63, col = lane & 15;
     const int cc = col < nb ? col : nb - 1;
+    return *reinterpret_cast<const float4 *>(lbase + cc * rows_cap + t * 16 + (lane >> 4) * 4);
+}
+
+// Epilogue of one result tile: W2 u = hi column + lo column (DPP from the lane
+// 8 columns away), plus L_base (lb, from w2_tile_lbase); folds the greedy keys
+// of the lane's column into `best` and stores L_final if requested.
+// Branch-free except for the L_final store: lanes outside the batch rows or
+// the block's rows contribute key 0.
+__device__ inline void w2_tile_keys(const Params &p, const f32x4_t &acc, const float4 &lb, float *lf, long long v0,
+                                    int nb, int n, int t, uint64_t &best)
+{
+    const int lane = threadIdx.x & 63, col = lane & 15;
+    const float lbv[4] = {lb.x, lb.y, lb.z, lb.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float w = acc[i] + dpp_f32<DPP_ROW_ROR8>(acc[i]);
         const int row = t * 16 + (lane >> 4) * 4 + i;
         const bool ok = col < nb && row < n;
-        const float v = lbase[cc * rows_cap + (row < n ? row : n - 1)] + w;
+        const float v = lbv[i] + w;
         if (lf && ok)
             lf[static_cast<size_t>(col) * p.K * p.V + row] = v;
         const uint64_t key = argmax_key(v, static_cast<uint32_t>(v0 + row));
@@ -795,10 +819,12 @@ __device__ inline void w2_tile_keys(const Params &p, const f32x4_t &acc, const f
     }
 }
 
+// Returns false (and sets DOMINO_FLAG_SYNC_TIMEOUT) when the u operand words
+// of this position (tag `tag`) did not all arrive within the spin limit.
 template <int RT, int KS>
-__device__ __forceinline__ void phase_w2_resident(const Params &p, int blk, int nblk, int pos, float *smem,
+__device__ __forceinline__ bool phase_w2_resident(const Params &p, int blk, int nblk, int pos, float *smem,
                                                   const W2Resident<RT, KS> &res, const uint4 *tl,
-                                                  uint64_t *local_keys)
+                                                  uint64_t *local_keys, unsigned tag)
 {
     const int r = 32 * KS;
     int v0i = static_cast<int>(static_cast<long long>(p.V) * blk / nblk);  // V < 2^31
@@ -808,30 +834,62 @@ __device__ __forceinline__ void phase_w2_resident(const Params &p, int blk, int 
     asm volatile("" : "+s"(v0i), "+s"(n));
     const long long v0 = v0i;
     const int T = (n + 15) / 16;
-    const int rows_cap = (p.V + nblk - 1) / nblk;
+    const int rows_cap = lbuf_stride(p.V, nblk);
     const float *lbase = smem + smem_off_lbuf(r);
     uint64_t *kred = reinterpret_cast<uint64_t *>(smem + 32);  // after local_keys (BC u64 at smem)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15;
     const int nb = p.B;  // persistent launches take B <= BC
     float *lf = p.L_final ? p.L_final + static_cast<size_t>(pos) * p.V + v0 : nullptr;
     DH_TRACE(pos * 32);
-    // B operand straight from the u operand planes: column col reads plane col / 8
-    // (hi, lo) of batch row col % 8, 8 bf16 values per 32-wide step
+    // L_base slice into LDS first: the compiler makes the next LDS access wait for
+    // these loads, which then overlap the wait for u below (the LDS tiles are
+    // read only after it)
+    lbase_to_lds(p, blk, nblk, pos, smem);
+    // B operand from the tagged u words: column col reads plane col / 8 (hi, lo)
+    // of batch row col % 8, 8 words per 32-wide step; poll until every word
+    // carries this position's tag
     uint4 bop[KS];
+    int ok = 1;
     {
         const int b = col & 7;
         const uint64_t *src = reinterpret_cast<const uint64_t *>(
-            p.ub16 + (static_cast<size_t>(col >> 3) * p.maxB + b) * r + (lane >> 4) * 8);
+            p.utag + (static_cast<size_t>(col >> 3) * p.maxB + b) * r + (lane >> 4) * 8);
+        const uint32_t want = tag & 0xFFFFu;
+        if (b < nb) {
+            unsigned spins = 0;
+            for (;;) {
+                uint32_t bad = 0;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            if (b < nb) {
-                const uint64_t x = ld_agent_u64(src + kk * 8), y = ld_agent_u64(src + kk * 8 + 1);
-                bop[kk] = make_uint4(static_cast<uint32_t>(x), static_cast<uint32_t>(x >> 32), static_cast<uint32_t>(y),
-                                     static_cast<uint32_t>(y >> 32));
-            } else {
-                bop[kk] = make_uint4(0u, 0u, 0u, 0u);
+                for (int kk = 0; kk < KS; ++kk) {
+                    uint32_t h[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint64_t w = ld_agent_u64(src + kk * 16 + c);
+                        const uint32_t w0 = static_cast<uint32_t>(w), w1 = static_cast<uint32_t>(w >> 32);
+                        bad |= ((w0 >> 16) ^ want) | ((w1 >> 16) ^ want);
+                        h[c] = (w0 & 0xFFFFu) | (w1 << 16);
+                    }
+                    bop[kk] = make_uint4(h[0], h[1], h[2], h[3]);
+                }
+                if (!bad)
+                    break;
+                if (++spins > p.spin_limit) {
+                    ok = 0;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
             }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk)
+                bop[kk] = make_uint4(0u, 0u, 0u, 0u);
         }
+    }
+    DH_TRACE(pos * 32 + 1);
+    if (!__syncthreads_and(ok)) {
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_or(p.flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
     }
     DH_TRACE(pos * 32 + 2);
     uint64_t best = 0;
@@ -840,9 +898,13 @@ __device__ __forceinline__ void phase_w2_resident(const Params &p, int blk, int 
 #pragma unroll
     for (int g0 = 0; g0 < RT; g0 += GR) {
         f32x4_t acc[GR];
+        float4 lb[GR];
 #pragma unroll
-        for (int j = 0; j < GR; ++j)
+        for (int j = 0; j < GR; ++j) {
             acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const int t = wave + (g0 + j) * NWAVE;
+            lb[j] = w2_tile_lbase(lbase, rows_cap, nb, t < T ? t : 0);
+        }
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
@@ -855,7 +917,7 @@ __device__ __forceinline__ void phase_w2_resident(const Params &p, int blk, int 
         for (int j = 0; j < GR; ++j) {
             const int t = wave + (g0 + j) * NWAVE;
             if (g0 + j < RT && t < T)
-                w2_tile_keys(p, acc[j], lbase, lf, v0, rows_cap, nb, n, t, best);
+                w2_tile_keys(p, acc[j], lb[j], lf, v0, nb, n, t, best);
         }
     }
     DH_TRACE(pos * 32 + 3);
@@ -865,6 +927,8 @@ __device__ __forceinline__ void phase_w2_resident(const Params &p, int blk, int 
         const int s0 = t - NWAVE * RT, s1 = s0 + NWAVE;
         const bool two = t + NWAVE < T;
         f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        const float4 lb0 = w2_tile_lbase(lbase, rows_cap, nb, t);
+        const float4 lb1 = w2_tile_lbase(lbase, rows_cap, nb, two ? t + NWAVE : t);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl[(s0 * KS + kk) * 64 + lane]),
@@ -874,9 +938,9 @@ __device__ __forceinline__ void phase_w2_resident(const Params &p, int blk, int 
                     __builtin_bit_cast(bf16x8_t, tl[(s1 * KS + kk) * 64 + lane]), __builtin_bit_cast(bf16x8_t, bop[kk]),
                     a1, 0, 0, 0);
         }
-        w2_tile_keys(p, a0, lbase, lf, v0, rows_cap, nb, n, t, best);
+        w2_tile_keys(p, a0, lb0, lf, v0, nb, n, t, best);
         if (two)
-            w2_tile_keys(p, a1, lbase, lf, v0, rows_cap, nb, n, t + NWAVE, best);
+            w2_tile_keys(p, a1, lb1, lf, v0, nb, n, t + NWAVE, best);
     }
     DH_TRACE(pos * 32 + 4);
     // block's key per batch row: over the lanes of a column, then over the waves
@@ -891,6 +955,7 @@ __device__ __forceinline__ void phase_w2_resident(const Params &p, int blk, int 
         local_keys[threadIdx.x] = m ? (m & KEY_ORD_MASK) | (KEY_IDX_MASK - key_index(m)) : 0ull;
     }
     DH_TRACE(pos * 32 + 5);
+    return true;
 }
 
 }  // namespace DH_NS

@@ -27,12 +27,17 @@ using namespace dh;
 // kernels
 // ============================================================================
 
-__global__ __launch_bounds__(256) void k_clear_state(unsigned *bar, uint64_t *asy, unsigned *flags)
+// Barrier words, argmax words, u operand words (tag 0: generations restart
+// at 0 and the first tag a launch polls for is at least 1) and device flags.
+__global__ __launch_bounds__(256) void k_clear_state(unsigned *bar, uint64_t *asy, uint32_t *utag, int n_utag,
+                                                     unsigned *flags)
 {
     for (int i = threadIdx.x; i < BAR_WORDS_ALL; i += blockDim.x)
         bar[i] = 0u;
     for (int i = threadIdx.x; i < ASYNC_WORDS; i += blockDim.x)
         asy[i] = 0ull;
+    for (int i = threadIdx.x; i < n_utag; i += blockDim.x)
+        utag[i] = 0u;
     if (threadIdx.x == 0)
         *flags = 0u;
 }
@@ -90,7 +95,7 @@ __global__ __launch_bounds__(NT) void k_persistent(Params p)
 {
     extern __shared__ float smem[];
     const int blk = blockIdx.x, nblk = gridDim.x;
-    float *S_lds = smem + smem_off_S(p.r, (p.V + nblk - 1) / nblk);
+    float *S_lds = smem + smem_off_S(p.r, lbuf_stride(p.V, nblk));
     float *cache = S_lds + BC * p.h;  // state rows and A_H entries (state_cache_load)
     int *atok = reinterpret_cast<int *>(smem + smem_off_tok()) + ATOK_OFF;
     int *bad = atok + BC;  // block 0: rows whose token ids are invalid
@@ -240,7 +245,7 @@ constexpr int W2_STEP_ROWS = 128;  // vocabulary rows per block in stepwise W2 l
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, ub16, q_buf, g_buf, P, total;
+    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, utag, q_buf, g_buf, P, total;
 };
 
 Layout layout_of(const domino_head_config &c)
@@ -261,8 +266,8 @@ Layout layout_of(const domino_head_config &c)
     off = align_up(off + sizeof(float) * 2 * static_cast<size_t>(c.max_batch) * c.h);
     L.u_buf = off;
     off = align_up(off + sizeof(float) * static_cast<size_t>(c.max_batch) * c.r);
-    L.ub16 = off;
-    off = align_up(off + sizeof(uint16_t) * 2 * static_cast<size_t>(c.max_batch) * c.r);
+    L.utag = off;
+    off = align_up(off + sizeof(uint32_t) * 2 * static_cast<size_t>(c.max_batch) * c.r);
     L.q_buf = off;
     off = align_up(off + sizeof(float) * 2 * static_cast<size_t>(c.max_batch) * 3 * c.h);
     L.g_buf = off;
@@ -472,7 +477,7 @@ int domino_head_create(const domino_head_config *cfg, void *workspace, size_t wo
     if (const char *s = std::getenv("DOMINO_BARRIER_SPIN_LIMIT"))
         hd->spin_limit = static_cast<unsigned>(std::strtoul(s, nullptr, 10));
     // persistent launch: one block per compute unit, all co-resident
-    const int rows_cap = (cfg->V + cus - 1) / cus;
+    const int rows_cap = lbuf_stride(cfg->V, cus);
     hd->persist_smem = sizeof(float) * (smem_floats(cfg->r, cfg->h, rows_cap) +
                                         state_cache_floats(cfg->r, cfg->h, cfg->K, cus,
                                                            cfg->wdtype == DOMINO_BF16 ? 2 : 4));
@@ -577,13 +582,14 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
     if (!hd->state_ready) {
         hipLaunchKernelGGL(k_clear_state, dim3(1), dim3(256), 0, st, reinterpret_cast<unsigned *>(hd->ws + hd->L.bar),
                            reinterpret_cast<uint64_t *>(hd->ws + hd->L.asy),
+                           reinterpret_cast<uint32_t *>(hd->ws + hd->L.utag), 2 * c.max_batch * c.r,
                            reinterpret_cast<unsigned *>(hd->ws + hd->L.flags));
         HIP_TRY(hipGetLastError(), "launch k_clear_state");
         hd->state_ready = true;
     }
     Params p = make_params(hd, B, H, L_base, last_tok, teacher, S_init, tokens, L_final, S_out, u_out, persistent);
     if (resident)
-        p.ub16 = reinterpret_cast<uint16_t *>(hd->ws + hd->L.ub16);
+        p.utag = reinterpret_cast<uint32_t *>(hd->ws + hd->L.utag);
     hd->last_stream = st;
     if (persistent) {
         void *args[] = {&p};
@@ -606,7 +612,7 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
     const int g_w2 = (c.V + W2_STEP_ROWS - 1) / W2_STEP_ROWS;
     const int g_upd = (B * c.h + NT - 1) / NT;
     const size_t sm_small = sizeof(float) * smem_floats_small();
-    const size_t sm_w2 = sizeof(float) * smem_floats_w2(c.r, (c.V + g_w2 - 1) / g_w2);
+    const size_t sm_w2 = sizeof(float) * smem_floats_w2(c.r, lbuf_stride(c.V, g_w2));
     const size_t sm_state = sizeof(float) * smem_floats(c.r, c.h, 0);
     {
         void *args[] = {&p};

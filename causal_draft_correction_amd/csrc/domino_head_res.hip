@@ -17,7 +17,7 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
 {
     extern __shared__ float smem[];
     const int blk = blockIdx.x, nblk = gridDim.x;
-    float *S_lds = smem + smem_off_S(p.r, (p.V + nblk - 1) / nblk);
+    float *S_lds = smem + smem_off_S(p.r, lbuf_stride(p.V, nblk));
     float *cache = S_lds + BC * p.h;
     uint4 *tl = reinterpret_cast<uint4 *>(cache + state_cache_floats(p.r, p.h, p.K, nblk, 2));
     int *atok = reinterpret_cast<int *>(smem + smem_off_tok()) + ATOK_OFF;
@@ -31,7 +31,6 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
     }
     phase_ah<bf16s>(p, blk, nblk, smem);
     phase_q_init<bf16s>(p, blk, nblk);
-    lbase_to_lds(p, blk, nblk, 0, smem);
     if (!p.P)
         phase_g<bf16s>(p, blk, nblk, 0, smem);
     // the slice load overlaps the first barrier and state phase
@@ -39,34 +38,29 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
     w2_resident_load<RT, KS>(p, blk, nblk, res, tl);
     if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
         return;
-    StatePre spre;
+    // from here on one barrier per position: the argmax barrier, which also
+    // publishes the q values of the state phase before it; u travels in tagged
+    // words that the W2 phase polls (tag = barrier generation of its position)
     state_cache_load<bf16s>(p, blk, nblk, cache);
-    state_prefetch<bf16s>(p, 0, spre);
-    phase_state<bf16s>(p, blk, nblk, 0, smem, S_lds, &spre, cache, true);
-    if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
-        return;
+    phase_state<bf16s>(p, blk, nblk, 0, smem, S_lds, nullptr, cache, true, nullptr, gen);
     for (int pos = 0; pos < p.K; ++pos) {
-        phase_w2_resident<RT, KS>(p, blk, nblk, pos, smem, res, tl, local_keys);
-        // loads of data published before the previous barrier (and of inputs) go
-        // between arrival and wait
+        if (!phase_w2_resident<RT, KS>(p, blk, nblk, pos, smem, res, tl, local_keys, gen))
+            return;
         argmax_arrive(p.asy, gen, local_keys, p.B);
-        if (pos + 1 < p.K) {
-            state_prefetch<bf16s>(p, pos + 1, spre);
-            lbase_to_lds(p, blk, nblk, pos + 1, smem);
-        }
         if (!argmax_wait(p.asy, gen, p.B, atok, p.spin_limit, p.flags))
             return;
         if (blk == 0 && threadIdx.x < p.B)
             p.tokens[static_cast<size_t>(threadIdx.x) * p.K + pos] = bad[threadIdx.x] ? -1 : atok[threadIdx.x];
+        DH_TRACE(pos * 32 + 13);
         if (pos + 1 < p.K) {
             if (!p.P) {
                 phase_g<bf16s>(p, blk, nblk, pos + 1, smem, atok);
                 if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
                     return;
             }
-            phase_state<bf16s>(p, blk, nblk, pos + 1, smem, S_lds, &spre, cache, true, atok);
-            if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
-                return;
+            // q of this step is visible only after the argmax barrier: its loads go out
+            // together with those of the P row
+            phase_state<bf16s>(p, blk, nblk, pos + 1, smem, S_lds, nullptr, cache, true, atok, gen);
         }
     }
     barrier_finish(p.bar, gen);
@@ -88,8 +82,8 @@ const void *kernel() { return reinterpret_cast<const void *>(&k_persistent_res<R
 
 size_t smem_bytes(int r, int h, int K, int V, int nblk)
 {
-    const int rows_cap = (V + nblk - 1) / nblk;
-    const int tiles = (rows_cap + 15) / 16;
+    const int rows_cap = lbuf_stride(V, nblk);
+    const int tiles = rows_cap / 16;
     const int lds_tiles = tiles > NWAVE * RES_RT ? tiles - NWAVE * RES_RT : 0;
     return sizeof(float) * (smem_floats(r, h, rows_cap) + state_cache_floats(r, h, K, nblk, 2)) +
            static_cast<size_t>(lds_tiles) * RES_KS * 64 * 16;

@@ -118,7 +118,6 @@ constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1,0,3,2]: reads lane i ^ 1
 constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2,3,0,1]: reads lane i ^ 2
 constexpr int DPP_HALF_MIRROR = 0x141;  // reads lane 7 - i within each group of 8
 constexpr int DPP_ROW_MIRROR = 0x140;   // reads lane 15 - i within each row of 16
-constexpr int DPP_ROW_ROR8 = 0x128;     // reads lane (i + 8) mod 16 within each row of 16
 
 template <int CTRL>
 __device__ inline uint32_t dpp_u32(uint32_t v)
@@ -268,6 +267,29 @@ __device__ inline float xld(const float *p)
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Block-wide failure flag of a persistent kernel (bounded waits that timed
+// out).  Cleared once at kernel start (block_fail_init, before the first block
+// sync) and never reset: a failure ends the kernel.  block_failed() costs one
+// block sync instead of the three of __syncthreads_and.
+__device__ inline int &block_fail_word()
+{
+    __shared__ int w;
+    return w;
+}
+__device__ inline void block_fail_init()
+{
+    if (threadIdx.x == 0)
+        block_fail_word() = 0;
+    __syncthreads();
+}
+__device__ inline bool block_failed(int ok)
+{
+    if (!ok)
+        block_fail_word() = 1;
+    __syncthreads();
+    return block_fail_word() != 0;
+}
+
 // ---------------------------------------------------------------------------
 // Grid barrier for a cooperative launch (every block resident), in two halves
 // so that loads of data published before the previous barrier can be issued
@@ -332,12 +354,12 @@ __device__ inline bool grid_wait(unsigned *bar, unsigned &gen, unsigned spin_lim
     }
     gen = next;
     DH_TRACE((static_cast<int>(next) - 4) / 2 * 32 + 26);
-    const int all = __syncthreads_and(ok);
-    if (!all && threadIdx.x == 0)
+    const bool failed = block_failed(ok);
+    if (failed && threadIdx.x == 0)
         __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     DH_TRACE((static_cast<int>(next) - 4) / 2 * 32 + 27);
-    return all != 0;
+    return !failed;
 }
 
 __device__ inline bool grid_sync(unsigned *bar, unsigned &gen, unsigned spin_limit, unsigned *flags)
@@ -353,7 +375,7 @@ __device__ inline bool grid_sync(unsigned *bar, unsigned &gen, unsigned spin_lim
 // field replaced by the generation (an index below 2^18 leaves the top 14 of
 // its 32 bits unused).  Wait: every block reads every word until it
 // carries the new generation and reduces the keys itself, leaving the tokens
-// of this position in tok[0..nb) (tok[b] written by thread b).  Generations compare modulo 2^14 (a word is
+// of this position in tok[0..nb) (visible to the whole block on return).  Generations compare modulo 2^14 (a word is
 // ready when it is at most 2^13 ahead).  A word is rewritten only at the next
 // argmax barrier, which no block reaches before every block has passed the
 // grid barrier in between.  Arrival words: asy[blk*BC + b].
@@ -426,19 +448,19 @@ __device__ inline bool argmax_wait(const uint64_t *asy, unsigned &gen, int nb, i
                 s_red[wave * BC + b] = m;
         }
     }
-    __syncthreads();
+    gen = next;
+    const bool failed = block_failed(ok);  // also the sync after the s_red writes
     if (threadIdx.x < nb) {
         uint64_t m = 0;
         for (int w = 0; w < NWAVE; ++w)
             m = max_u64(m, s_red[w * BC + threadIdx.x]);
         tok[threadIdx.x] = m ? static_cast<int>(KEY_IDX_MASK - (m & KEY_IDX_MASK)) : 0;
     }
-    gen = next;
-    const int all = __syncthreads_and(ok);
-    if (!all && threadIdx.x == 0)
+    if (failed && threadIdx.x == 0)
         __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();  // tok visible to the block
     DH_TRACE((static_cast<int>(next) - 2) * 32 + 12);
-    return all != 0;
+    return !failed;
 }
 
 __device__ inline bool grid_argmax_sync(uint64_t *asy, unsigned &gen, const uint64_t *local_key, int nb, int *tok,

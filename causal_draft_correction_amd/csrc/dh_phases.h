@@ -450,15 +450,19 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
         DH_TRACE(tslot + 3);
         // dot rows of this wave: k-th row m = m0 + k * mstep; when `cached` (persistent
         // launch) the row and its A_H entries come from LDS at `cache`.  Rows go in
-        // groups of RG: the S chunks are read once per group and the RG sums are
+        // groups of up to RG: the S chunks are read once per group and the sums are
         // reduced together (each row's sum is formed in the same order as alone).
+        // The wave's u rows (m < r) form the first groups, so u is published before
+        // the q rows are computed.
         constexpr int RG = 4;
         const int m0 = blk * NWAVE + wave, mstep = nblk * NWAVE;
         const int rpw = state_rows_per_wave(r, h, nblk);
+        const int ku = m0 < r ? (r - m0 + mstep - 1) / mstep : 0;  // this wave's u rows
         const uint4 *wc = reinterpret_cast<const uint4 *>(cache);
         const float *ac = cache + NWAVE * rpw * (h * static_cast<int>(sizeof(WT)) / 4);
 #pragma unroll 1
-        for (int k0 = 0; m0 + k0 * mstep < R; k0 += RG) {
+        for (int k0 = 0, kend = 0; m0 + k0 * mstep < R; k0 = kend) {
+            kend = k0 < ku ? (ku < k0 + RG ? ku : k0 + RG) : k0 + RG;
 #pragma unroll 1
             for (int bb = 0; bb < nb; ++bb) {
                 const int b = b0 + bb;
@@ -476,7 +480,7 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
 #pragma unroll
                     for (int j = 0; j < RG; ++j) {
                         const int k = k0 + j, m = m0 + k * mstep;
-                        if (m < R) {
+                        if (k < kend && m < R) {
                             const uint4 wq = cached ? wc[(wave * rpw + k) * nch + ch]
                                                     : ld16<WT>(m < r ? p.W1 : p.W_hh,
                                                                state_row_off<WT>(p, m) + static_cast<size_t>(ch) * EPC);
@@ -491,7 +495,7 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
 #pragma unroll
                 for (int j = 0; j < RG; ++j) {
                     const int k = k0 + j, m = m0 + k * mstep;
-                    if (lane != 0 || m >= R)
+                    if (lane != 0 || k >= kend || m >= R)
                         continue;
                     if (m < r) {
                         const float ah = cached ? ac[((wave * rpw + k) * p.K + q) * BC + b]
@@ -786,37 +790,54 @@ __device__ __forceinline__ void lbase_to_lds(const Params &p, int blk, int nblk,
     }
 }
 
-// L_base values of the four result rows this lane holds in tile t (one 16-byte
-// LDS read; rows_cap is a multiple of 16, so every tile row lies inside the
-// batch row's stride, and lanes of columns >= nb read row nb - 1).
-__device__ inline float4 w2_tile_lbase(const float *lbase, int rows_cap, int nb, int t)
+// Running greedy argmax of one lane: order word of the best value (as in
+// argmax_key: NaN highest, -0 as +0; 0 = none yet) and its vocabulary index.
+// A lane sees its rows in increasing order, so keeping the first of equal
+// values keeps the lowest index.
+struct LaneBest {
+    uint32_t ord = 0, idx = 0;
+};
+
+// Result tiles are D = U W2_tile^T (16 x 16): lane l holds D rows (l/16)*4 + i,
+// i = 0..3, of column l%16 (the tile's vocabulary row l%16).  U row c < 8 is the
+// hi part of batch row c, row 8 + c its lo part, so batch row b's hi values sit
+// in acc[b % 4] of lanes 16*(b/4) + 0..15 and its lo values 32 lanes higher.
+// w2_hilo returns hi + lo of component i in both halves of the wave.
+__device__ inline float w2_hilo(const f32x4_t &acc, int i)
 {
-    const int lane = threadIdx.x & 63, col = lane & 15;
-    const int cc = col < nb ? col : nb - 1;
-    return *reinterpret_cast<const float4 *>(lbase + cc * rows_cap + t * 16 + (lane >> 4) * 4);
+    const float x = i == 0 ? acc[0] : i == 1 ? acc[1] : i == 2 ? acc[2] : acc[3];
+    uint32_t lo, hi;
+    half_values(__float_as_uint(x), lo, hi);
+    return __uint_as_float(lo) + __uint_as_float(hi);
 }
 
-// Epilogue of one result tile: W2 u = hi column + lo column (DPP from the lane
-// 8 columns away), plus L_base (lb, from w2_tile_lbase); folds the greedy keys
-// of the lane's column into `best` and stores L_final if requested.
-// Branch-free except for the L_final store: lanes outside the batch rows or
-// the block's rows contribute key 0.
-__device__ inline void w2_tile_keys(const Params &p, const f32x4_t &acc, const float4 &lb, float *lf, long long v0,
-                                    int nb, int n, int t, uint64_t &best)
+// Packs one batch row's values of four tiles (from w2_hilo, in lane row 0 of
+// each, or lane row 1 when `upper`, i.e. batch rows 4..7) into one register:
+// tile j's vocabulary row r at lane 16 j + r.
+__device__ inline float w2_pack4(float s0, float s1, float s2, float s3, bool upper)
 {
-    const int lane = threadIdx.x & 63, col = lane & 15;
-    const float lbv[4] = {lb.x, lb.y, lb.z, lb.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float w = acc[i] + dpp_f32<DPP_ROW_ROR8>(acc[i]);
-        const int row = t * 16 + (lane >> 4) * 4 + i;
-        const bool ok = col < nb && row < n;
-        const float v = lbv[i] + w;
-        if (lf && ok)
-            lf[static_cast<size_t>(col) * p.K * p.V + row] = v;
-        const uint64_t key = argmax_key(v, static_cast<uint32_t>(v0 + row));
-        best = max_u64(best, ok ? key : 0ull);
-    }
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(s0), __float_as_uint(s1), false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s2), __float_as_uint(s3), false, false);
+    const uint32_t x = upper ? a[1] : a[0], y = upper ? c[1] : c[0];  // {t0, t1, t0, t1}, {t2, t3, t2, t3}
+    const auto d = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+    return __uint_as_float(d[0]);
+}
+
+// Folds one packed value (W2 u of vocabulary row v0 + row) plus its L_base
+// value into `best` and stores L_final (lf: the batch row's L_final slice of
+// this block, or null).  Lanes with !ok take order 0 (never selected).
+__device__ inline void w2_key(float w, float lbv, float *lf, int v0, int row, bool ok, LaneBest &best)
+{
+    const float v = lbv + w;
+    if (lf && ok)
+        lf[row] = v;
+    const uint32_t bits = __float_as_uint(v + 0.f);  // -0 + +0 = +0
+    uint32_t ord = bits ^ (static_cast<uint32_t>(static_cast<int32_t>(bits) >> 31) | 0x80000000u);
+    ord = (v != v) ? 0xFFFFFFFFu : ord;
+    ord = ok ? ord : 0u;
+    const bool take = ord > best.ord;
+    best.idx = take ? static_cast<uint32_t>(v0 + row) : best.idx;
+    best.ord = take ? ord : best.ord;
 }
 
 // Returns false (and sets DOMINO_FLAG_SYNC_TIMEOUT) when the u operand words
@@ -841,13 +862,9 @@ __device__ __forceinline__ bool phase_w2_resident(const Params &p, int blk, int 
     const int nb = p.B;  // persistent launches take B <= BC
     float *lf = p.L_final ? p.L_final + static_cast<size_t>(pos) * p.V + v0 : nullptr;
     DH_TRACE(pos * 32);
-    // L_base slice into LDS first: the compiler makes the next LDS access wait for
-    // these loads, which then overlap the wait for u below (the LDS tiles are
-    // read only after it)
-    lbase_to_lds(p, blk, nblk, pos, smem);
-    // B operand from the tagged u words: column col reads plane col / 8 (hi, lo)
-    // of batch row col % 8, 8 words per 32-wide step; poll until every word
-    // carries this position's tag
+    // A operand (U) from the tagged u words: lane row col = lane % 16 reads plane
+    // col / 8 (hi, lo) of batch row col % 8, 8 words per 32-wide step; poll until
+    // every word carries this position's tag
     uint4 bop[KS];
     int ok = 1;
     {
@@ -886,67 +903,85 @@ __device__ __forceinline__ bool phase_w2_resident(const Params &p, int blk, int 
         }
     }
     DH_TRACE(pos * 32 + 1);
-    if (!__syncthreads_and(ok)) {
+    if (block_failed(ok)) {
         if (threadIdx.x == 0)
             __hip_atomic_fetch_or(p.flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return false;
     }
     DH_TRACE(pos * 32 + 2);
-    uint64_t best = 0;
-    // register tiles in groups of GR: independent accumulators, steps interleaved
+    // per batch row: the lane's running best (batch rows beyond nb stay empty)
+    LaneBest best[BC];
+    const int jl = lane >> 4, rl = lane & 15;  // packed layout: tile j = jl of a group, row rl
+    // register tiles in groups of GR = 4: independent accumulators, steps interleaved
     constexpr int GR = 4;
+    static_assert(RT % GR == 0, "register tiles come in groups of four");
 #pragma unroll
     for (int g0 = 0; g0 < RT; g0 += GR) {
-        f32x4_t acc[GR];
-        float4 lb[GR];
+        const int row = (wave + (g0 + jl) * NWAVE) * 16 + rl;  // this lane's packed row
+        const bool inb = row < n;
+        float lbv[BC];
 #pragma unroll
-        for (int j = 0; j < GR; ++j) {
+        for (int b = 0; b < BC; ++b)
+            lbv[b] = b < nb ? lbase[b * rows_cap + (inb ? row : 0)] : 0.f;
+        f32x4_t acc[GR];
+#pragma unroll
+        for (int j = 0; j < GR; ++j)
             acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            const int t = wave + (g0 + j) * NWAVE;
-            lb[j] = w2_tile_lbase(lbase, rows_cap, nb, t < T ? t : 0);
-        }
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
             for (int j = 0; j < GR; ++j)
-                if (g0 + j < RT)
-                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, res.wt[g0 + j < RT ? g0 + j : 0][kk]),
-                        __builtin_bit_cast(bf16x8_t, bop[kk]), acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bop[kk]),
+                                                                __builtin_bit_cast(bf16x8_t, res.wt[g0 + j][kk]),
+                                                                acc[j], 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < GR; ++j) {
-            const int t = wave + (g0 + j) * NWAVE;
-            if (g0 + j < RT && t < T)
-                w2_tile_keys(p, acc[j], lb[j], lf, v0, nb, n, t, best);
+        for (int b = 0; b < BC; ++b) {
+            if (b < nb) {
+                const float w = w2_pack4(w2_hilo(acc[0], b & 3), w2_hilo(acc[1], b & 3), w2_hilo(acc[2], b & 3),
+                                         w2_hilo(acc[3], b & 3), b >= 4);
+                w2_key(w, lbv[b], lf ? lf + static_cast<size_t>(b) * p.K * p.V : nullptr, v0i, row, inb, best[b]);
+            }
         }
     }
     DH_TRACE(pos * 32 + 3);
-    // LDS tiles, two at a time
+    // LDS tiles, one at a time: the tile's chunks are read together, then multiplied;
+    // only lane row 0 of the packed layout carries rows
 #pragma unroll 1
-    for (int t = NWAVE * RT + wave; t < T; t += 2 * NWAVE) {
-        const int s0 = t - NWAVE * RT, s1 = s0 + NWAVE;
-        const bool two = t + NWAVE < T;
-        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-        const float4 lb0 = w2_tile_lbase(lbase, rows_cap, nb, t);
-        const float4 lb1 = w2_tile_lbase(lbase, rows_cap, nb, two ? t + NWAVE : t);
+    for (int t = NWAVE * RT + wave; t < T; t += NWAVE) {
+        const int sl = t - NWAVE * RT;
+        uint4 a[KS];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl[(s0 * KS + kk) * 64 + lane]),
-                                                         __builtin_bit_cast(bf16x8_t, bop[kk]), a0, 0, 0, 0);
-            if (two)
-                a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, tl[(s1 * KS + kk) * 64 + lane]), __builtin_bit_cast(bf16x8_t, bop[kk]),
-                    a1, 0, 0, 0);
+        for (int kk = 0; kk < KS; ++kk)
+            a[kk] = tl[(sl * KS + kk) * 64 + lane];
+        const int row = t * 16 + rl;
+        const bool inb = jl == 0 && row < n;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bop[kk]),
+                                                          __builtin_bit_cast(bf16x8_t, a[kk]), acc, 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < BC; ++b) {
+            if (b < nb) {
+                const float lb = lbase[b * rows_cap + (inb ? row : 0)];
+                const float s0 = w2_hilo(acc, b & 3);
+                const float w = w2_pack4(s0, s0, s0, s0, b >= 4);
+                w2_key(w, lb, lf ? lf + static_cast<size_t>(b) * p.K * p.V : nullptr, v0i, row, inb, best[b]);
+            }
         }
-        w2_tile_keys(p, a0, lb0, lf, v0, nb, n, t, best);
-        if (two)
-            w2_tile_keys(p, a1, lb1, lf, v0, nb, n, t + NWAVE, best);
     }
     DH_TRACE(pos * 32 + 4);
-    // block's key per batch row: over the lanes of a column, then over the waves
-    best = rows_max_u64(best);
-    if (lane < nb)
-        kred[wave * BC + lane] = best;
+    // block's key per batch row: over the wave, then over the waves
+#pragma unroll
+    for (int b = 0; b < BC; ++b) {
+        if (b < nb) {
+            uint64_t key = best[b].ord ? (static_cast<uint64_t>(best[b].ord) << 32) | (0xFFFFFFFFu - best[b].idx)
+                                       : 0ull;
+            key = wave_max_u64(key);
+            if (lane == 0)
+                kred[wave * BC + b] = key;
+        }
+    }
     __syncthreads();
     if (threadIdx.x < nb) {
         uint64_t m = 0;

@@ -101,6 +101,7 @@ __global__ __launch_bounds__(NT) void k_persistent(Params p)
     int *bad = atok + BC;  // block 0: rows whose token ids are invalid
     uint64_t *local_keys = reinterpret_cast<uint64_t *>(smem);  // the reduction area is free inside the loop
     unsigned gen = barrier_gen_init(p.bar);
+    block_fail_init();
     if (blk == 0) {
         prologue_bookkeeping(p);
         if (threadIdx.x < p.B)

@@ -24,6 +24,7 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
     int *bad = atok + BC;
     uint64_t *local_keys = reinterpret_cast<uint64_t *>(smem);
     unsigned gen = barrier_gen_init(p.bar);
+    block_fail_init();
     if (blk == 0) {
         prologue_bookkeeping(p);
         if (threadIdx.x < p.B)
@@ -31,6 +32,7 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
     }
     phase_ah<bf16s>(p, blk, nblk, smem);
     phase_q_init<bf16s>(p, blk, nblk);
+    lbase_to_lds(p, blk, nblk, 0, smem);
     if (!p.P)
         phase_g<bf16s>(p, blk, nblk, 0, smem);
     // the slice load overlaps the first barrier and state phase
@@ -47,6 +49,10 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
         if (!phase_w2_resident<RT, KS>(p, blk, nblk, pos, smem, res, tl, local_keys, gen))
             return;
         argmax_arrive(p.asy, gen, local_keys, p.B);
+        // L_base of the next position goes to LDS while the barrier is awaited (the
+        // compiler makes the thread's next LDS access wait for these loads)
+        if (pos + 1 < p.K)
+            lbase_to_lds(p, blk, nblk, pos + 1, smem);
         if (!argmax_wait(p.asy, gen, p.B, atok, p.spin_limit, p.flags))
             return;
         if (blk == 0 && threadIdx.x < p.B)

@@ -842,11 +842,14 @@ __device__ inline void w2_key(float w, float lbv, float *lf, int v0, int row, bo
 
 // Returns false (and sets DOMINO_FLAG_SYNC_TIMEOUT) when the u operand words
 // of this position (tag `tag`) did not all arrive within the spin limit.
-template <int RT, int KS>
+// NB: largest batch the instantiation handles (B <= NB <= BC); per-row
+// registers are sized by it.
+template <int RT, int KS, int NB>
 __device__ __forceinline__ bool phase_w2_resident(const Params &p, int blk, int nblk, int pos, float *smem,
                                                   const W2Resident<RT, KS> &res, const uint4 *tl,
                                                   uint64_t *local_keys, unsigned tag)
 {
+    static_assert(NB >= 1 && NB <= BC, "batch rows of one persistent launch");
     const int r = 32 * KS;
     int v0i = static_cast<int>(static_cast<long long>(p.V) * blk / nblk);  // V < 2^31
     int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0i);
@@ -859,7 +862,7 @@ __device__ __forceinline__ bool phase_w2_resident(const Params &p, int blk, int 
     const float *lbase = smem + smem_off_lbuf(r);
     uint64_t *kred = reinterpret_cast<uint64_t *>(smem + 32);  // after local_keys (BC u64 at smem)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15;
-    const int nb = p.B;  // persistent launches take B <= BC
+    const int nb = p.B;  // B <= NB
     float *lf = p.L_final ? p.L_final + static_cast<size_t>(pos) * p.V + v0 : nullptr;
     DH_TRACE(pos * 32);
     // A operand (U) from the tagged u words: lane row col = lane % 16 reads plane
@@ -910,18 +913,18 @@ __device__ __forceinline__ bool phase_w2_resident(const Params &p, int blk, int 
     }
     DH_TRACE(pos * 32 + 2);
     // per batch row: the lane's running best (batch rows beyond nb stay empty)
-    LaneBest best[BC];
+    LaneBest best[NB];
     const int jl = lane >> 4, rl = lane & 15;  // packed layout: tile j = jl of a group, row rl
     // register tiles in groups of GR = 4: independent accumulators, steps interleaved
     constexpr int GR = 4;
-    static_assert(RT % GR == 0, "register tiles come in groups of four");
 #pragma unroll
     for (int g0 = 0; g0 < RT; g0 += GR) {
+        const int G = RT - g0 < GR ? RT - g0 : GR;  // tiles in this group
         const int row = (wave + (g0 + jl) * NWAVE) * 16 + rl;  // this lane's packed row
-        const bool inb = row < n;
-        float lbv[BC];
+        const bool inb = jl < G && row < n;
+        float lbv[NB];
 #pragma unroll
-        for (int b = 0; b < BC; ++b)
+        for (int b = 0; b < NB; ++b)
             lbv[b] = b < nb ? lbase[b * rows_cap + (inb ? row : 0)] : 0.f;
         f32x4_t acc[GR];
 #pragma unroll
@@ -931,11 +934,12 @@ __device__ __forceinline__ bool phase_w2_resident(const Params &p, int blk, int 
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
             for (int j = 0; j < GR; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bop[kk]),
-                                                                __builtin_bit_cast(bf16x8_t, res.wt[g0 + j][kk]),
-                                                                acc[j], 0, 0, 0);
+                if (j < G)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, bop[kk]), __builtin_bit_cast(bf16x8_t, res.wt[g0 + (j < G ? j : 0)][kk]),
+                        acc[j], 0, 0, 0);
 #pragma unroll
-        for (int b = 0; b < BC; ++b) {
+        for (int b = 0; b < NB; ++b) {
             if (b < nb) {
                 const float w = w2_pack4(w2_hilo(acc[0], b & 3), w2_hilo(acc[1], b & 3), w2_hilo(acc[2], b & 3),
                                          w2_hilo(acc[3], b & 3), b >= 4);
@@ -961,7 +965,7 @@ __device__ __forceinline__ bool phase_w2_resident(const Params &p, int blk, int 
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bop[kk]),
                                                           __builtin_bit_cast(bf16x8_t, a[kk]), acc, 0, 0, 0);
 #pragma unroll
-        for (int b = 0; b < BC; ++b) {
+        for (int b = 0; b < NB; ++b) {
             if (b < nb) {
                 const float lb = lbase[b * rows_cap + (inb ? row : 0)];
                 const float s0 = w2_hilo(acc, b & 3);
@@ -973,7 +977,7 @@ __device__ __forceinline__ bool phase_w2_resident(const Params &p, int blk, int 
     DH_TRACE(pos * 32 + 4);
     // block's key per batch row: over the wave, then over the waves
 #pragma unroll
-    for (int b = 0; b < BC; ++b) {
+    for (int b = 0; b < NB; ++b) {
         if (b < nb) {
             uint64_t key = best[b].ord ? (static_cast<uint64_t>(best[b].ord) << 32) | (0xFFFFFFFFu - best[b].idx)
                                        : 0ull;

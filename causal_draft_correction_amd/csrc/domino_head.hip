@@ -493,10 +493,15 @@ int domino_head_create(const domino_head_config *cfg, void *workspace, size_t wo
     hd->res_grid = 0;
     if (cfg->wdtype == DOMINO_BF16 && cfg->r == dhres::r_supported() && hd->persist_grid) {
         hd->res_smem = dhres::smem_bytes(cfg->r, cfg->h, cfg->K, cfg->V, cus);
-        int per_cu_r = 0;
-        hipError_t er = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_r, dhres::kernel(), dhres::threads(),
-                                                                     hd->res_smem);
-        if (er == hipSuccess && per_cu_r >= 1 && hd->res_smem + 1024 <= static_cast<size_t>(lds_max))
+        // both instantiations (B = 1 and B <= 8) must fit one block per compute unit
+        bool fits = hd->res_smem + 1024 <= static_cast<size_t>(lds_max);
+        for (int b : {1, BC}) {
+            int per_cu_r = 0;
+            hipError_t er = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_r, dhres::kernel(b), dhres::threads(),
+                                                                         hd->res_smem);
+            fits = fits && er == hipSuccess && per_cu_r >= 1;
+        }
+        if (fits)
             hd->res_grid = cus;
     }
     *out = hd;
@@ -595,7 +600,7 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
     if (persistent) {
         void *args[] = {&p};
         if (resident) {
-            HIP_TRY(hipLaunchCooperativeKernel(dhres::kernel(), dim3(hd->res_grid), dim3(dhres::threads()), args,
+            HIP_TRY(hipLaunchCooperativeKernel(dhres::kernel(B), dim3(hd->res_grid), dim3(dhres::threads()), args,
                                                static_cast<unsigned>(hd->res_smem), st),
                     "hipLaunchCooperativeKernel(persistent, resident W2)");
         } else {

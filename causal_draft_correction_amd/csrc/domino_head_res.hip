@@ -12,7 +12,7 @@ namespace DH_NS {
 // matrix cores (bf16 weights, r = 32 * KS, B <= BC).  The slice is loaded once,
 // overlapped with the prologue; every position then reads it from registers
 // and LDS instead of streaming 2 r V bytes from HBM.
-template <int RT, int KS>
+template <int RT, int KS, int NB>
 __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
 {
     extern __shared__ float smem[];
@@ -46,34 +46,40 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
     state_cache_load<bf16s>(p, blk, nblk, cache);
     phase_state<bf16s>(p, blk, nblk, 0, smem, S_lds, nullptr, cache, true, nullptr, gen);
     for (int pos = 0; pos < p.K; ++pos) {
-        if (!phase_w2_resident<RT, KS>(p, blk, nblk, pos, smem, res, tl, local_keys, gen))
+        // the output and exchange pointers pass through an opaque copy each position,
+        // so the per-thread addresses derived from them are recomputed here instead of
+        // being hoisted out of the loop into (spilled) registers
+        Params pl = p;
+        asm volatile("" : "+s"(pl.asy), "+s"(pl.tokens), "+s"(pl.utag), "+s"(pl.q_buf), "+s"(pl.P), "+s"(pl.L_final),
+                          "+s"(pl.S_out), "+s"(pl.u_out), "+s"(pl.L_base));
+        if (!phase_w2_resident<RT, KS, NB>(pl, blk, nblk, pos, smem, res, tl, local_keys, gen))
             return;
-        argmax_arrive(p.asy, gen, local_keys, p.B);
+        argmax_arrive(pl.asy, gen, local_keys, pl.B);
         // L_base of the next position goes to LDS while the barrier is awaited (the
         // compiler makes the thread's next LDS access wait for these loads)
-        if (pos + 1 < p.K)
-            lbase_to_lds(p, blk, nblk, pos + 1, smem);
-        if (!argmax_wait(p.asy, gen, p.B, atok, p.spin_limit, p.flags))
+        if (pos + 1 < pl.K)
+            lbase_to_lds(pl, blk, nblk, pos + 1, smem);
+        if (!argmax_wait(pl.asy, gen, pl.B, atok, pl.spin_limit, pl.flags))
             return;
-        if (blk == 0 && threadIdx.x < p.B)
-            p.tokens[static_cast<size_t>(threadIdx.x) * p.K + pos] = bad[threadIdx.x] ? -1 : atok[threadIdx.x];
+        if (blk == 0 && threadIdx.x < pl.B)
+            pl.tokens[static_cast<size_t>(threadIdx.x) * pl.K + pos] = bad[threadIdx.x] ? -1 : atok[threadIdx.x];
         DH_TRACE(pos * 32 + 13);
-        if (pos + 1 < p.K) {
-            if (!p.P) {
-                phase_g<bf16s>(p, blk, nblk, pos + 1, smem, atok);
-                if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+        if (pos + 1 < pl.K) {
+            if (!pl.P) {
+                phase_g<bf16s>(pl, blk, nblk, pos + 1, smem, atok);
+                if (!grid_sync(pl.bar, gen, pl.spin_limit, pl.flags))
                     return;
             }
             // q of this step is visible only after the argmax barrier: its loads go out
             // together with those of the P row
-            phase_state<bf16s>(p, blk, nblk, pos + 1, smem, S_lds, nullptr, cache, true, atok, gen);
+            phase_state<bf16s>(pl, blk, nblk, pos + 1, smem, S_lds, nullptr, cache, true, atok, gen);
         }
     }
     barrier_finish(p.bar, gen);
 }
 
 
-constexpr int RES_RT = 8;   // W2 tiles per wave kept in registers (4 waves x 8 x 16 rows = 512 rows; the rest in LDS)
+constexpr int RES_RT = 10;  // W2 tiles per wave kept in registers (4 waves x 10 x 16 rows = 640 rows; the rest in LDS)
 constexpr int RES_KS = 8;   // 32-wide steps of r: r = 256
 
 }  // namespace DH_NS
@@ -84,7 +90,12 @@ using namespace dh256;
 
 int threads() { return NT; }
 int r_supported() { return 32 * RES_KS; }
-const void *kernel() { return reinterpret_cast<const void *>(&k_persistent_res<RES_RT, RES_KS>); }
+// B = 1 (the common case) gets an instantiation whose per-row registers hold one row
+const void *kernel(int B)
+{
+    return B <= 1 ? reinterpret_cast<const void *>(&k_persistent_res<RES_RT, RES_KS, 1>)
+                  : reinterpret_cast<const void *>(&k_persistent_res<RES_RT, RES_KS, BC>);
+}
 
 size_t smem_bytes(int r, int h, int K, int V, int nblk)
 {

@@ -260,12 +260,14 @@ def test_accept_len_bit_exact(B, K):
 
 
 # ------------------------------------------------------------------ resident W2 (bf16, r = 256)
-@pytest.mark.parametrize("V,B,fold", [(5003, 1, True), (5003, 3, False), (5003, 8, True), (140000, 2, True)])
+@pytest.mark.parametrize("V,B,fold", [(5003, 1, True), (5003, 3, False), (5003, 8, True), (160000, 2, True),
+                                      (160000, 6, False)])
 def test_resident_w2_slice_matches_oracle(V, B, fold):
     """r = 256 bf16 heads keep each block's W2 slice on chip and multiply it on the
-    matrix cores (u split into bf16 hi + lo parts).  V = 140000 puts tiles beyond the
-    register share into LDS.  Compared with the oracle, with the streaming launch and
-    run to run."""
+    matrix cores (u split into bf16 hi + lo parts).  V = 160000 (625 rows per block
+    on 256 compute units) puts tiles beyond the register share into LDS; B = 6 uses
+    batch rows 4..5 of the packed epilogue.  Compared with the oracle, with the
+    streaming launch and run to run."""
     sh = ds.HeadShape(d=128, h=64, r=256, V=V, K=16, wdtype="bf16")
     w = ds.make_weights(sh, (9, 60), gru_sensitive=True)
     inp = ds.make_inputs(sh, B, (9, 61), sigma=0.5, peak="none")

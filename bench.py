@@ -98,6 +98,9 @@ def main():
     ap.add_argument("--mode", default="auto", choices=["auto", "persistent", "stepwise"])
     ap.add_argument("--stream-w2", action="store_true",
                     help="persistent launch: stream W2 every position instead of keeping it on chip")
+    ap.add_argument("--plain-launch", action="store_true",
+                    help="persistent launch as an ordinary kernel launch (caller guarantees no concurrent waiting "
+                         "kernels); the default is a cooperative launch")
     ap.add_argument("--store-logits", action="store_true")
     ap.add_argument("--no-fold", action="store_true",
                     help="do not precompute the folded input-gate table (GRU input GEMV every step)")
@@ -128,7 +131,8 @@ def main():
     fold = not args.no_fold
     t_create = time.perf_counter()
     head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B,
-                          exec_mode=mode | (dca.EXEC_STREAM_W2 if args.stream_w2 else 0), fold_embedding=fold)
+                          exec_mode=mode | (dca.EXEC_STREAM_W2 if args.stream_w2 else 0) |
+                          (dca.EXEC_PLAIN_LAUNCH if args.plain_launch else 0), fold_embedding=fold)
     torch.cuda.synchronize()
     t_create = time.perf_counter() - t_create
     H = dca.device_tensor(inp.H)
@@ -205,7 +209,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "K": sh.K, "V": sh.V, "d": sh.d, "h": sh.h, "r": sh.r,
                    "weights": sh.wdtype, "exec": exec_name, "store_logits": bool(args.store_logits),
-                   "fold_embedding": fold, "w2_on_chip": w2_on_chip, "create_s": t_create,
+                   "fold_embedding": fold, "w2_on_chip": w2_on_chip,
+                   "launch": "plain" if args.plain_launch else "cooperative", "create_s": t_create,
                    "kernel_avg_us": avg_ms * 1e3, "w2_lbase_GBps": w2l,
                    "w2_lbase_frac_of_hbm_peak": w2l / HBM_PEAK_GBPS},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

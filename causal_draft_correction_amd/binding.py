@@ -23,6 +23,7 @@ EXEC_PERSISTENT = 1
 EXEC_STEPWISE = 2
 FOLD_EMBED = 4
 EXEC_STREAM_W2 = 8
+EXEC_PLAIN_LAUNCH = 16
 FLAG_BAD_TOKEN = 1
 FLAG_SYNC_TIMEOUT = 2
 

@@ -309,7 +309,8 @@ int validate_config(const domino_head_config *c)
         if (!aligned16(ptrs[i]))
             return fail(DOMINO_EINVAL, "%s is not 16-byte aligned", names[i]);
     }
-    if (c->flags & ~(DOMINO_EXEC_PERSISTENT | DOMINO_EXEC_STEPWISE | DOMINO_FOLD_EMBED | DOMINO_EXEC_STREAM_W2))
+    if (c->flags & ~(DOMINO_EXEC_PERSISTENT | DOMINO_EXEC_STEPWISE | DOMINO_FOLD_EMBED | DOMINO_EXEC_STREAM_W2 |
+                     DOMINO_EXEC_PLAIN_LAUNCH))
         return fail(DOMINO_EINVAL, "unknown flags 0x%x", c->flags);
     if ((c->flags & DOMINO_EXEC_PERSISTENT) && (c->flags & DOMINO_EXEC_STEPWISE))
         return fail(DOMINO_EINVAL, "flags ask for both persistent and stepwise execution");
@@ -599,15 +600,14 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
     hd->last_stream = st;
     if (persistent) {
         void *args[] = {&p};
-        if (resident) {
-            HIP_TRY(hipLaunchCooperativeKernel(dhres::kernel(B), dim3(hd->res_grid), dim3(dhres::threads()), args,
-                                               static_cast<unsigned>(hd->res_smem), st),
-                    "hipLaunchCooperativeKernel(persistent, resident W2)");
-        } else {
-            HIP_TRY(hipLaunchCooperativeKernel(hd->kern.persistent, dim3(hd->persist_grid), dim3(NT), args,
-                                               static_cast<unsigned>(hd->persist_smem), st),
-                    "hipLaunchCooperativeKernel(persistent)");
-        }
+        const void *fn = resident ? dhres::kernel(B) : hd->kern.persistent;
+        const dim3 grid(resident ? hd->res_grid : hd->persist_grid);
+        const dim3 block(resident ? dhres::threads() : NT);
+        const unsigned smem = static_cast<unsigned>(resident ? hd->res_smem : hd->persist_smem);
+        if (c.flags & DOMINO_EXEC_PLAIN_LAUNCH)
+            HIP_TRY(hipLaunchKernel(fn, grid, block, args, smem, st), "hipLaunchKernel(persistent)");
+        else
+            HIP_TRY(hipLaunchCooperativeKernel(fn, grid, block, args, smem, st), "hipLaunchCooperativeKernel(persistent)");
         return DOMINO_OK;
     }
     // stepwise: prologue, update(0), state(0), then per position w2 [, g], update, state

@@ -64,6 +64,13 @@ extern "C" {
 #define DOMINO_FOLD_EMBED 4u       /* precompute P = E W_ih^T + b_ih ([V, 3h] float32, in the workspace) at
                                       create time, so each GRU step gathers one row of P instead of
                                       multiplying W_ih by the embedding row (same values up to rounding) */
+#define DOMINO_EXEC_PLAIN_LAUNCH 16u /* persistent launch as an ordinary kernel launch instead of a
+                                      cooperative one (about 17 us less dispatch time per call).  Its
+                                      blocks (one per compute unit) wait for each other, so the caller
+                                      guarantees that no other kernel that waits for other work (in
+                                      particular no other persistent draft) runs on the device at the
+                                      same time; otherwise the bounded waits time out and the call
+                                      reports DOMINO_FLAG_SYNC_TIMEOUT */
 
 /*
  * Head configuration.  All weight pointers are DEVICE pointers, borrowed for

@@ -279,6 +279,10 @@ def test_resident_w2_slice_matches_oracle(V, B, fold):
     b, _ = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
     for k in ("tokens", "L_final", "S", "u"):
         assert np.array_equal(a[k], b[k]), k
+    pl = make_head(w, B, dca.EXEC_PERSISTENT | dca.EXEC_PLAIN_LAUNCH, fold=fold)
+    d, _ = gpu_draft(pl, inp.H, inp.L_base, inp.last_tok)
+    for k in ("tokens", "L_final", "S", "u"):
+        assert np.array_equal(a[k], d[k]), "plain launch " + k
     st = make_head(w, B, dca.EXEC_PERSISTENT | dca.EXEC_STREAM_W2, fold=fold)
     assert st.exec_info(B)["w2_resident"] is False
     assert make_head(w, B, dca.EXEC_STEPWISE, fold=fold).exec_info(B) == {"persistent": False, "w2_resident": False,

@@ -20,6 +20,7 @@
 #include "../../include/domino_head.h"
 #include "dh_phases.h"
 #include "dh_resident.h"
+#include "dh_batched.h"
 
 using namespace dh;
 
@@ -629,9 +630,16 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
                                 sm_small, st), "launch update");
         HIP_TRY(hipLaunchKernel(hd->kern.state, dim3(g_rows), dim3(NT), sargs, sm_state, st), "launch state");
     }
+    // bf16 heads with r = 256 take the matrix-core W2 kernel
+    const bool w2_mfma = c.wdtype == DOMINO_BF16 && c.r == dhbat::r_supported();
     for (int pos = 0; pos < c.K; ++pos) {
         void *args[] = {&p, &pos};
-        HIP_TRY(hipLaunchKernel(hd->kern.w2, dim3(g_w2), dim3(NT), args, sm_w2, st), "launch w2");
+        if (w2_mfma)
+            HIP_TRY(hipLaunchKernel(dhbat::w2_kernel(), dim3(dhbat::w2_grid(B, hd->cus)), dim3(dhbat::threads()), args,
+                                    0, st),
+                    "launch w2 (matrix cores)");
+        else
+            HIP_TRY(hipLaunchKernel(hd->kern.w2, dim3(g_w2), dim3(NT), args, sm_w2, st), "launch w2");
         if (pos + 1 < c.K) {
             int q = pos + 1;
             void *gargs[] = {&p, &q};

@@ -289,3 +289,36 @@ def test_resident_w2_slice_matches_oracle(V, B, fold):
                                                                           "grid": 0}
     c, _ = gpu_draft(st, inp.H, inp.L_base, inp.last_tok)
     assert np.abs(c["L_final"] - a["L_final"]).max() < 1e-4
+
+
+# ------------------------------------------------------------------ batched W2 on the matrix cores (r = 256)
+@pytest.mark.parametrize("V,B,fold", [(20011, 9, True), (20011, 40, False), (7001, 130, True)])
+def test_batched_w2_matrix_cores_match_oracle(V, B, fold):
+    """Stepwise launches of bf16 r = 256 heads run W2 as a matrix-core GEMM (u as bf16
+    hi + lo operand rows, fused L_base add and argmax).  B = 40 leaves a partial
+    32-row group, B = 130 a second 128-row batch tile with two rows."""
+    sh = ds.HeadShape(d=128, h=64, r=256, V=V, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 70), gru_sensitive=True)
+    inp = ds.make_inputs(sh, B, (9, 71), sigma=0.5, peak="none")
+    head = make_head(w, B, dca.EXEC_STEPWISE, fold=fold)
+    assert head.exec_info(B) == {"persistent": False, "w2_resident": False, "grid": 0}
+    run_both_protocols(w, inp, head, label="batched W2 V=%d B=%d fold=%d" % (V, B, fold))
+    a, _ = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
+    b, _ = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
+    for k in ("tokens", "L_final", "S", "u"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_batched_w2_equals_resident_kernel_bitwise():
+    """Both matrix-core W2 paths form each logit as L_base + (hi + lo) from the same
+    instruction on the same operands, and share the state phase arithmetic: the
+    stepwise launches and the resident persistent launch agree bitwise."""
+    sh = ds.HeadShape(d=128, h=64, r=256, V=9001, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 72), gru_sensitive=True)
+    inp = ds.make_inputs(sh, 4, (9, 73), sigma=0.5, peak="none")
+    pers = make_head(w, 4, dca.EXEC_PERSISTENT, fold=True)
+    assert pers.exec_info(4)["w2_resident"]
+    a, _ = gpu_draft(pers, inp.H, inp.L_base, inp.last_tok)
+    c, _ = gpu_draft(make_head(w, 4, dca.EXEC_STEPWISE, fold=True), inp.H, inp.L_base, inp.last_tok)
+    for k in ("tokens", "L_final", "S", "u"):
+        assert np.array_equal(a[k], c[k]), k

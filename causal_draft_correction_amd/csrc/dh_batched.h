@@ -1,9 +1,17 @@
 // Host entry points of the batched matrix-core W2 kernel (domino_head_bat.hip).
 #pragma once
 
+#include <stddef.h>
+
 namespace dhbat {
 int r_supported();         // the rank it is built for
 int threads();             // threads per block
 const void *w2_kernel();   // k_w2_mfma: arguments (Params, int position)
+int w2_threads();          // its threads per block
+size_t w2_smem();          // its dynamic LDS per block
 int w2_grid(int B, int cus);  // blocks for B batch rows on cus compute units
+const void *state_kernel();   // k_state_mfma (bf16 weights): arguments (Params, int step q)
+int state_grid(int B, int r, int h);
+const void *ah_kernel();      // k_ah_mfma (bf16 H and W1, d and r multiples of 32): arguments (Params)
+int ah_grid(int B, int K, int r);
 }  // namespace dhbat

@@ -23,6 +23,7 @@ struct Params {
     uint32_t *utag;  // [2, maxB, r] u as matrix-core operand: words (tag << 16) | bf16 bits of the
                      // hi part (plane 0) and lo part (plane 1) of u, or nullptr
     float *q_buf;    // [2, maxB, 3h] W_hh S + b_hh
+    uint16_t *s_hl;  // [2, maxB, h] bf16 hi and lo parts of S (matrix-core state dots) or nullptr
     float *g_buf;    // [maxB, 3h]    W_ih E[x] + b_ih (when not folded)
     uint64_t *keys;  // [K, NG, maxB] partial argmax keys
     unsigned *bar;   // barrier words
@@ -30,6 +31,7 @@ struct Params {
     unsigned *flags; // device flags
     unsigned spin_limit;
     int persistent;  // 1: blocks keep the state in LDS between phases
+    int ah_external; // 1: A_H is computed by its own (matrix-core) launch, not by the prologue
 };
 
 }  // namespace dhp

@@ -156,7 +156,8 @@ __global__ __launch_bounds__(NT) void k_step_prologue(Params p)
     extern __shared__ float smem[];
     if (blockIdx.x == 0)
         prologue_bookkeeping(p);
-    phase_ah<WT>(p, blockIdx.x, gridDim.x, smem);
+    if (!p.ah_external)
+        phase_ah<WT>(p, blockIdx.x, gridDim.x, smem);
     phase_q_init<WT>(p, blockIdx.x, gridDim.x);
     if (!p.P)
         phase_g<WT>(p, blockIdx.x, gridDim.x, 0, smem);
@@ -247,7 +248,7 @@ constexpr int W2_STEP_ROWS = 128;  // vocabulary rows per block in stepwise W2 l
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, utag, q_buf, g_buf, P, total;
+    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, utag, s_hl, q_buf, g_buf, P, total;
 };
 
 Layout layout_of(const domino_head_config &c)
@@ -270,6 +271,8 @@ Layout layout_of(const domino_head_config &c)
     off = align_up(off + sizeof(float) * static_cast<size_t>(c.max_batch) * c.r);
     L.utag = off;
     off = align_up(off + sizeof(uint32_t) * 2 * static_cast<size_t>(c.max_batch) * c.r);
+    L.s_hl = off;
+    off = align_up(off + sizeof(uint16_t) * 2 * static_cast<size_t>(c.max_batch) * c.h);
     L.q_buf = off;
     off = align_up(off + sizeof(float) * 2 * static_cast<size_t>(c.max_batch) * 3 * c.h);
     L.g_buf = off;
@@ -621,6 +624,25 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
     const size_t sm_small = sizeof(float) * smem_floats_small();
     const size_t sm_w2 = sizeof(float) * smem_floats_w2(c.r, lbuf_stride(c.V, g_w2));
     const size_t sm_state = sizeof(float) * smem_floats(c.r, c.h, 0);
+    // larger batches of bf16 heads take the matrix-core state dots (S passed as bf16 hi/lo planes)
+    const bool state_mfma = c.wdtype == DOMINO_BF16 && c.r % 32 == 0 && c.h % 32 == 0 && B > BC;
+    if (state_mfma)
+        p.s_hl = reinterpret_cast<uint16_t *>(hd->ws + hd->L.s_hl);
+    auto launch_state = [&](void **sargs) -> hipError_t {
+        if (state_mfma)
+            return hipLaunchKernel(dhbat::state_kernel(), dim3(dhbat::state_grid(B, c.r, c.h)),
+                                   dim3(dhbat::threads()), sargs, 0, st);
+        return hipLaunchKernel(hd->kern.state, dim3(g_rows), dim3(NT), sargs, sm_state, st);
+    };
+    // larger batches of bf16 heads: A_H on the matrix cores (H rows x W1_H rows), its own launch
+    const bool ah_mfma = c.wdtype == DOMINO_BF16 && c.d % 32 == 0 && c.r % 32 == 0 && B > BC;
+    if (ah_mfma) {
+        p.ah_external = 1;
+        void *args[] = {&p};
+        HIP_TRY(hipLaunchKernel(dhbat::ah_kernel(), dim3(dhbat::ah_grid(B, c.K, c.r)), dim3(dhbat::threads()), args, 0,
+                                st),
+                "launch A_H (matrix cores)");
+    }
     {
         void *args[] = {&p};
         HIP_TRY(hipLaunchKernel(hd->kern.prologue, dim3(g_pro), dim3(NT), args, sm_small, st), "launch prologue");
@@ -628,15 +650,15 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
         void *sargs[] = {&p, &q};
         HIP_TRY(hipLaunchKernel(reinterpret_cast<const void *>(&k_step_update), dim3(g_upd), dim3(NT), sargs,
                                 sm_small, st), "launch update");
-        HIP_TRY(hipLaunchKernel(hd->kern.state, dim3(g_rows), dim3(NT), sargs, sm_state, st), "launch state");
+        HIP_TRY(launch_state(sargs), "launch state");
     }
     // bf16 heads with r = 256 take the matrix-core W2 kernel
     const bool w2_mfma = c.wdtype == DOMINO_BF16 && c.r == dhbat::r_supported();
     for (int pos = 0; pos < c.K; ++pos) {
         void *args[] = {&p, &pos};
         if (w2_mfma)
-            HIP_TRY(hipLaunchKernel(dhbat::w2_kernel(), dim3(dhbat::w2_grid(B, hd->cus)), dim3(dhbat::threads()), args,
-                                    0, st),
+            HIP_TRY(hipLaunchKernel(dhbat::w2_kernel(), dim3(dhbat::w2_grid(B, hd->cus)), dim3(dhbat::w2_threads()),
+                                    args, dhbat::w2_smem(), st),
                     "launch w2 (matrix cores)");
         else
             HIP_TRY(hipLaunchKernel(hd->kern.w2, dim3(g_w2), dim3(NT), args, sm_w2, st), "launch w2");
@@ -647,7 +669,7 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
                 HIP_TRY(hipLaunchKernel(hd->kern.g, dim3(g_g), dim3(NT), gargs, sm_small, st), "launch g");
             HIP_TRY(hipLaunchKernel(reinterpret_cast<const void *>(&k_step_update), dim3(g_upd), dim3(NT), gargs,
                                     sm_small, st), "launch update");
-            HIP_TRY(hipLaunchKernel(hd->kern.state, dim3(g_rows), dim3(NT), gargs, sm_state, st), "launch state");
+            HIP_TRY(launch_state(gargs), "launch state");
         }
     }
     {

@@ -11,43 +11,59 @@
 
 namespace DH_NS {
 
-// Work split.  A block takes a batch tile of up to 128 rows (bt) and a
-// contiguous vocabulary range (vb of nvb); its four waves take 32-row batch
-// groups of the tile and split the range into 64-row chunks when the tile has
-// fewer than four groups.  A wave keeps its 32 batch rows of u in registers
-// as four matrix-core A operands: A tile a holds batch rows a*8 .. a*8+7 as
-// bf16 hi parts in rows 0..7 and lo parts (u - hi) in rows 8..15, so the two
-// results of a batch row come out 32 lanes apart and are added (the same
-// operand form and order as the resident kernel, so both give the same
-// values).  For each 64-row chunk the wave multiplies the A tiles with four
-// 16-row W2 tiles (v_mfma_f32_16x16x32_bf16, D = A W2_tile^T), adds hi + lo,
-// packs two A tiles per register and folds L_base, the optional L_final
-// store and the greedy argmax.  Each lane keeps the running best of its eight
-// batch rows; at the end the 16 lanes of a batch row reduce it and one lane
-// folds it into the partial key slot of group blockIdx % NG with an atomic max.
+// Work split.  A block (512 threads, two waves per SIMD) takes a batch tile
+// of up to 128 rows (bt) and a contiguous vocabulary range (vb of nvb).  Its
+// eight waves take 16-row batch groups of the tile (ng groups) and, when the
+// tile has fewer than eight groups, split each vocabulary chunk's 16-row tiles
+// between nvs = 8 / ng wave sets.  A wave keeps its 16 batch rows of u in
+// registers as two matrix-core A operands: A tile a holds batch rows a*8 ..
+// a*8+7 as bf16 hi parts in rows 0..7 and lo parts (u - hi) in rows 8..15
+// (the operand form of the resident kernel).  Chunks of CR vocabulary rows of
+// W2 are staged through LDS in the B-operand layout ([tile][step][lane], 16
+// bytes each), double buffered: the next chunk is loaded into registers while
+// the current one is multiplied (v_mfma_f32_16x16x32_bf16, D = A W2_tile^T),
+// then written to the other buffer.  The epilogue adds each batch row's hi and
+// lo results, which one v_permlane32_swap of the two A tiles' results lines up
+// (sum hi + lo, the resident kernel's order), adds L_base (prefetched a chunk
+// ahead), stores L_final if requested and folds the greedy argmax into a
+// running best per lane.  At the end the 16 lanes of a batch row reduce it and
+// one lane folds it into the partial key slot of group blockIdx % NG.
+constexpr int BNT = 512;  // threads per block of the batched W2 kernel
+constexpr int XCDS = 8;   // accelerator dies (XCDs) of the MI355X, each with its own L2
+constexpr int BNW = BNT / 64;
+
 template <int KS>
-__global__ __launch_bounds__(NT) void k_w2_mfma(Params p, int pos)
+__global__ __launch_bounds__(BNT) void k_w2_mfma(Params p, int pos)
 {
+    extern __shared__ uint4 wlds[];  // 2 buffers of (CR/16) * KS * 64 uint4
     const int r = 32 * KS;
     const int B = p.B, V = p.V;
-    const int nbt = (B + 127) / 128;
-    const int bt = blockIdx.x % nbt, vb = blockIdx.x / nbt, nvb = gridDim.x / nbt;
-    if (vb >= nvb)
-        return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rows = B - bt * 128 < 128 ? B - bt * 128 : 128;  // batch rows of this tile
-    const int ng = rows <= 32 ? 1 : rows <= 64 ? 2 : 4;         // 32-row groups (waves per chunk)
-    const int grp = wave % ng, vs = wave / ng, nvs = 4 / ng;
-    const int row0 = bt * 128 + grp * 32;                       // first batch row of the wave
+    // XCD-aware split: blocks go round-robin over the XCDs, so block i runs on XCD
+    // i % XCDS; the nbt batch tiles of one vocabulary range get consecutive
+    // indices within one XCD and read that range's W2 through its L2 together
+    const int nbt = (B + 127) / 128, nvb = gridDim.x / nbt;  // nvb is a multiple of XCDS
+    const int xcd = blockIdx.x % XCDS, j = blockIdx.x / XCDS;
+    const int bt = j % nbt, vb = (j / nbt) * XCDS + xcd;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15;
+    const int rows = B - bt * 128 < 128 ? B - bt * 128 : 128;
+    const int need = (rows + 15) / 16;
+    const int ng = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;  // 16-row batch groups
+    const int nvs = BNW / ng;                                         // wave sets per chunk
+    const int grp = wave % ng, vs = wave / ng;
+    const int CR = nvs <= 4 ? 64 : 128;  // chunk rows
+    const int VTG = (CR / 16) / nvs;     // 16-row tiles per wave set
+    const int row0 = bt * 128 + grp * 16;
     const long long v0 = static_cast<long long>(V) * vb / nvb;
     const int n = static_cast<int>(static_cast<long long>(V) * (vb + 1) / nvb - v0);
-    const int col = lane & 15;
+    const int nchunk = (n + CR - 1) / CR;
     const int g = blockIdx.x % NG;
+    const int slots = (CR / 16) * KS * 64;  // uint4 per chunk
+    const int per_thread = slots / BNT;     // 4 or 8
 
-    // A operands: u of batch row row0 + a*8 + (col & 7), hi part for col < 8, lo part otherwise
-    uint4 ua[4][KS];
+    // A operands of this wave
+    uint4 ua[2][KS];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < 2; ++a) {
         const int b = row0 + a * 8 + (col & 7);
         const bool hi = col < 8;
         const float *src = p.u_buf + static_cast<size_t>(b < B ? b : 0) * r + (lane >> 4) * 8;
@@ -64,96 +80,283 @@ __global__ __launch_bounds__(NT) void k_w2_mfma(Params p, int pos)
                 for (int j = 0; j < 8; ++j)
                     x[j] = 0.f;
             }
-            uint32_t h[8];
+            uint32_t hv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t xh = bf16_rne_bits(x[j]);
-                h[j] = hi ? xh : bf16_rne_bits(x[j] - __uint_as_float(xh << 16));
+                hv[j] = hi ? xh : bf16_rne_bits(x[j] - __uint_as_float(xh << 16));
             }
-            ua[a][kk] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+            ua[a][kk] = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
+                                   hv[6] | (hv[7] << 16));
         }
     }
 
-    // lane's batch rows in the packed epilogue: pair pp packs A tiles 2pp (lanes 0..31)
-    // and 2pp+1 (lanes 32..63); row i of four per lane
-    int brow[2][4];
+    // staging: slot s of a chunk = (tile, step, lane) -> 16 bytes of W2
+    auto stage_load = [&](int c, uint4 (&st)[8]) {
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp)
+        for (int j = 0; j < 8; ++j) {
+            if (j < per_thread) {
+                const int s = threadIdx.x + j * BNT;
+                const int vt = s / (KS * 64), kk = (s / 64) % KS, ln = s & 63;
+                const int vr = c * CR + vt * 16 + (ln & 15);
+                st[j] = vr < n ? ld16<bf16s>(p.W2, static_cast<size_t>(v0 + vr) * r + kk * 32 + (ln >> 4) * 8)
+                               : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    };
+    auto stage_store = [&](int buf, const uint4 (&st)[8]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            brow[pp][i] = row0 + (2 * pp + (lane >> 5)) * 8 + ((lane >> 4) & 1) * 4 + i;
-    LaneBest best[2][4];
-
-#pragma unroll 1
-    for (int c0 = vs * 64; c0 < n; c0 += nvs * 64) {
-        // L_base of the epilogue values, issued first
-        float lb[2][4][4];  // [pp][vt][i]
+        for (int j = 0; j < 8; ++j)
+            if (j < per_thread)
+                wlds[buf * slots + threadIdx.x + j * BNT] = st[j];
+    };
+    // this lane's batch row in the combined results: A tile (lane / 32), row i of four
+    int brow[4];
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
+    for (int i = 0; i < 4; ++i)
+        brow[i] = row0 + (lane >> 5) * 8 + ((lane >> 4) & 1) * 4 + i;
+    // L_base of this lane's epilogue values for chunk c (tile index vt of the wave set)
+    auto lbase_load = [&](int c, float (&lb)[4][4]) {
 #pragma unroll
-            for (int vt = 0; vt < 4; ++vt)
+        for (int vt = 0; vt < 4; ++vt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int b = brow[pp][i], vr = c0 + vt * 16 + col;
+            for (int i = 0; i < 4; ++i) {
+                if (vt < VTG) {
+                    const int b = brow[i], vr = c * CR + (vs * VTG + vt) * 16 + col;
                     const size_t o = (static_cast<size_t>(b < B ? b : 0) * p.K + pos) * V + v0 + (vr < n ? vr : 0);
-                    lb[pp][vt][i] = p.L_base[o];
+                    lb[vt][i] = __builtin_nontemporal_load(p.L_base + o);  // streamed once
                 }
-        f32x4_t acc[4][4];  // [a][vt]
+            }
+    };
+
+    LaneBest best[4];
+    uint4 st[8];
+    float lbc[4][4], lbn[4][4];
+    if (nchunk > 0) {
+        stage_load(0, st);
+        lbase_load(0, lbc);
+        stage_store(0, st);
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 0; c < nchunk; ++c) {
+        const int buf = c & 1;
+        const bool more = c + 1 < nchunk;
+        if (more) {
+            stage_load(c + 1, st);
+            lbase_load(c + 1, lbn);
+        }
+        f32x4_t acc[2][4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int vt = 0; vt < 4; ++vt)
                 acc[a][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const uint4 *wb = wlds + buf * slots;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            uint4 wb[4];
+        for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
             for (int vt = 0; vt < 4; ++vt) {
-                const int vr = c0 + vt * 16 + col;
-                wb[vt] = vr < n ? ld16<bf16s>(p.W2, static_cast<size_t>(v0 + vr) * r + kk * 32 + (lane >> 4) * 8)
-                                : make_uint4(0u, 0u, 0u, 0u);
+                if (vt < VTG) {
+                    const uint4 w = wb[((vs * VTG + vt) * KS + kk) * 64 + lane];
+#pragma unroll
+                    for (int a = 0; a < 2; ++a)
+                        acc[a][vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ua[a][kk]),
+                                                                            __builtin_bit_cast(bf16x8_t, w),
+                                                                            acc[a][vt], 0, 0, 0);
+                }
             }
+#pragma unroll
+        for (int vt = 0; vt < 4; ++vt) {
+            if (vt < VTG) {
+                const int vr = c * CR + (vs * VTG + vt) * 16 + col;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    // {hi of tile 0, hi of tile 1} + {lo of tile 0, lo of tile 1}
+                    const auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0][vt][i]),
+                                                                    __float_as_uint(acc[1][vt][i]), false, false);
+                    const float w = __uint_as_float(d[0]) + __uint_as_float(d[1]);
+                    const int b = brow[i];
+                    const bool ok = b < B && vr < n;
+                    float *lf = p.L_final ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * V + v0 : nullptr;
+                    w2_key(w, lbc[vt][i], lf, static_cast<int>(v0), vr, ok, best[i]);
+                }
+            }
+        }
+        if (more) {
+            stage_store(buf ^ 1, st);
 #pragma unroll
             for (int vt = 0; vt < 4; ++vt)
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
-                    acc[a][vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ua[a][kk]),
-                                                                        __builtin_bit_cast(bf16x8_t, wb[vt]),
-                                                                        acc[a][vt], 0, 0, 0);
+                for (int i = 0; i < 4; ++i)
+                    lbc[vt][i] = lbn[vt][i];
         }
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-            for (int vt = 0; vt < 4; ++vt) {
-                const int vr = c0 + vt * 16 + col;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x0 = w2_hilo(acc[2 * pp][vt], i), x1 = w2_hilo(acc[2 * pp + 1][vt], i);
-                    const auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x1), false,
-                                                                    false);
-                    const int b = brow[pp][i];
-                    const bool ok = b < B && vr < n;
-                    float *lf = p.L_final ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * V + v0 : nullptr;
-                    w2_key(__uint_as_float(d[0]), lb[pp][vt][i], lf, static_cast<int>(v0), vr, ok, best[pp][i]);
-                }
-            }
+        __syncthreads();
     }
     // each batch row's best over its 16 lanes, folded into the partial key slot
 #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint64_t key = best[i].ord ? (static_cast<uint64_t>(best[i].ord) << 32) | (0xFFFFFFFFu - best[i].idx) : 0ull;
+        key = max_u64(key, dpp_u64<DPP_QUAD_XOR1>(key));
+        key = max_u64(key, dpp_u64<DPP_QUAD_XOR2>(key));
+        key = max_u64(key, dpp_u64<DPP_HALF_MIRROR>(key));
+        key = max_u64(key, dpp_u64<DPP_ROW_MIRROR>(key));
+        const int b = brow[i];
+        if (col == 0 && b < B && key)
+            __hip_atomic_fetch_max(key_slot(p, pos, g, b), key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// State-phase dot products of the stepwise launches at larger B, on the matrix
+// cores (same quantities as phase_state):
+//   u_q[b][m]      = SiLU(A_H[b][q][m] + sum_k W1[m][d + k] S_q[b][k])   (m < r)
+//   q_{q+1}[b][m'] = sum_k W_hh[m'][k] S_q[b][k] + b_hh[m']             (m' = m - r)
+// A operand: S_q as bf16 hi + lo rows of 8 batch rows (planes written by the
+// update launch); B operand: 16 weight rows.  A block takes 32 batch rows and
+// 128 weight rows (32 per wave); the K loop runs over h in 32-wide steps.
+template <typename WT>
+__global__ __launch_bounds__(NT) void k_state_mfma(Params p, int q)
+{
+    const int h = p.h, r = p.r, R = r + 3 * p.h, B = p.B;
+    const int nbg = (B + 31) / 32;
+    const int bg = blockIdx.x % nbg, wb = blockIdx.x / nbg;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15;
+    const int mw = wb * 128 + wave * 32;  // first weight row of the wave
+    if (mw >= R)
+        return;
+    const int b0 = bg * 32;
+    // operand sources of this lane
+    const uint16_t *arow[4];
+    bool aok[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int b = b0 + a * 8 + (col & 7);
+        aok[a] = b < B;
+        arow[a] = p.s_hl + (static_cast<size_t>(col >> 3) * p.maxB + (aok[a] ? b : 0)) * h + (lane >> 4) * 8;
+    }
+    const bf16s *wrow[2];
+    bool wok[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int m = mw + t * 16 + col;
+        wok[t] = m < R;
+        const int mm = wok[t] ? m : 0;
+        wrow[t] = mm < r ? static_cast<const bf16s *>(p.W1) + static_cast<size_t>(mm) * (p.d + h) + p.d
+                         : static_cast<const bf16s *>(p.W_hh) + static_cast<size_t>(mm - r) * h;
+        wrow[t] += (lane >> 4) * 8;
+    }
+    f32x4_t acc[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            acc[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < h; k += 32) {
+        uint4 av[4], wv[2];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+            av[a] = aok[a] ? *reinterpret_cast<const uint4 *>(arow[a] + k) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            wv[t] = wok[t] ? *reinterpret_cast<const uint4 *>(wrow[t] + k) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[a]),
+                                                                   __builtin_bit_cast(bf16x8_t, wv[t]), acc[a][t], 0,
+                                                                   0, 0);
+    }
+    const int h3 = 3 * h;
+    float *qn = q_slot(p, q + 1);
+#pragma unroll
     for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint64_t key = best[pp][i].ord ? (static_cast<uint64_t>(best[pp][i].ord) << 32) |
-                                                 (0xFFFFFFFFu - best[pp][i].idx)
-                                           : 0ull;
-            key = max_u64(key, dpp_u64<DPP_QUAD_XOR1>(key));
-            key = max_u64(key, dpp_u64<DPP_QUAD_XOR2>(key));
-            key = max_u64(key, dpp_u64<DPP_HALF_MIRROR>(key));
-            key = max_u64(key, dpp_u64<DPP_ROW_MIRROR>(key));
-            const int b = brow[pp][i];
-            if (col == 0 && b < B && key)
-                __hip_atomic_fetch_max(key_slot(p, pos, g, b), key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int t = 0; t < 2; ++t) {
+            const int m = mw + t * 16 + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x0 = w2_hilo(acc[2 * pp][t], i), x1 = w2_hilo(acc[2 * pp + 1][t], i);
+                const auto dd = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x1), false,
+                                                                 false);
+                const float dot = __uint_as_float(dd[0]);
+                const int b = b0 + (2 * pp + (lane >> 5)) * 8 + ((lane >> 4) & 1) * 4 + i;
+                if (b >= B || m >= R)
+                    continue;
+                if (m < r) {
+                    const float a_ = p.A_H[(static_cast<size_t>(b) * p.K + q) * r + m] + dot;
+                    const float u = a_ * sigmoidf_(a_);
+                    p.u_buf[static_cast<size_t>(b) * r + m] = u;
+                    if (p.u_out)
+                        p.u_out[(static_cast<size_t>(b) * p.K + q) * r + m] = u;
+                } else {
+                    const float bias = p.b_hh ? WT16<WT>::one(p.b_hh, m - r) : 0.f;
+                    qn[static_cast<size_t>(b) * h3 + (m - r)] = dot + bias;
+                }
+            }
         }
+}
+
+// A_H = W1[:, :d] H for every position on the matrix cores (same quantity as
+// phase_ah): rows R = b * K + i of H (bf16, [B*K, d]) times rows m of W1's
+// first d columns; A_H[R][m] in fp32.  A wave takes 32 H rows x 32 W1 rows
+// (2 x 2 tiles of v_mfma_f32_16x16x32_bf16), the K loop runs over d.
+template <typename WT>
+__global__ __launch_bounds__(NT) void k_ah_mfma(Params p)
+{
+    const int d = p.d, r = p.r, M = p.B * p.K;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15;
+    const int tiles_n = r / 32;
+    const int wt = blockIdx.x * NWAVE + wave;
+    const int tm = wt / tiles_n, tn = wt % tiles_n;
+    const int R0 = tm * 32, m0 = tn * 32;
+    if (R0 >= M)
+        return;
+    const bf16s *arow[2];
+    bool aok[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int R = R0 + a * 16 + col;
+        aok[a] = R < M;
+        arow[a] = static_cast<const bf16s *>(p.H) + static_cast<size_t>(aok[a] ? R : 0) * d + (lane >> 4) * 8;
+    }
+    const bf16s *wrow[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        wrow[t] = static_cast<const bf16s *>(p.W1) + static_cast<size_t>(m0 + t * 16 + col) * (d + p.h) + (lane >> 4) * 8;
+    f32x4_t acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            acc[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < d; k += 32) {
+        uint4 av[2], wv[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+            av[a] = aok[a] ? *reinterpret_cast<const uint4 *>(arow[a] + k) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            wv[t] = *reinterpret_cast<const uint4 *>(wrow[t] + k);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[a]),
+                                                                   __builtin_bit_cast(bf16x8_t, wv[t]), acc[a][t], 0,
+                                                                   0, 0);
+    }
+    // D: lane l holds H rows (l/16)*4 + i of the A tile, W1 row l%16 of the B tile
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int R = R0 + a * 16 + (lane >> 4) * 4 + i;
+                if (R < M)
+                    p.A_H[static_cast<size_t>(R) * r + m0 + t * 16 + col] = acc[a][t][i];
+            }
 }
 
 constexpr int BAT_KS = 8;  // r = 256
@@ -167,12 +370,20 @@ using namespace dh256;
 int r_supported() { return 32 * BAT_KS; }
 int threads() { return NT; }
 const void *w2_kernel() { return reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS>); }
+int w2_threads() { return BNT; }
 // one block per compute unit: batch tiles times vocabulary ranges
 int w2_grid(int B, int cus)
 {
     const int nbt = (B + 127) / 128;
-    const int nvb = (cus + nbt - 1) / nbt;
+    int nvb = (cus + nbt - 1) / nbt;
+    nvb = (nvb + XCDS - 1) / XCDS * XCDS;
     return nbt * nvb;
 }
+// two chunk buffers of up to 128 rows x 256 bf16
+size_t w2_smem() { return 2 * sizeof(uint4) * (128 / 16) * BAT_KS * 64; }
+const void *state_kernel() { return reinterpret_cast<const void *>(&k_state_mfma<bf16s>); }
+const void *ah_kernel() { return reinterpret_cast<const void *>(&k_ah_mfma<bf16s>); }
+int ah_grid(int B, int K, int r) { return ((B * K + 31) / 32 * (r / 32) + NWAVE - 1) / NWAVE; }
+int state_grid(int B, int r, int h) { return ((B + 31) / 32) * ((r + 3 * h + 127) / 128); }
 
 }  // namespace dhbat

@@ -295,8 +295,9 @@ def test_resident_w2_slice_matches_oracle(V, B, fold):
 @pytest.mark.parametrize("V,B,fold", [(20011, 9, True), (20011, 40, False), (7001, 130, True)])
 def test_batched_w2_matrix_cores_match_oracle(V, B, fold):
     """Stepwise launches of bf16 r = 256 heads run W2 as a matrix-core GEMM (u as bf16
-    hi + lo operand rows, fused L_base add and argmax).  B = 40 leaves a partial
-    32-row group, B = 130 a second 128-row batch tile with two rows."""
+    hi + lo operand rows, fused L_base add and argmax); above 8 rows the state-phase
+    dot products also run on the matrix cores (S as bf16 hi + lo).  B = 40 leaves a
+    partial 32-row group, B = 130 a second 128-row batch tile with two rows."""
     sh = ds.HeadShape(d=128, h=64, r=256, V=V, K=16, wdtype="bf16")
     w = ds.make_weights(sh, (9, 70), gru_sensitive=True)
     inp = ds.make_inputs(sh, B, (9, 71), sigma=0.5, peak="none")

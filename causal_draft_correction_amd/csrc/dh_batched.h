@@ -6,8 +6,9 @@
 namespace dhbat {
 int r_supported();         // the rank it is built for
 int threads();             // threads per block
-const void *w2_kernel();   // k_w2_mfma: arguments (Params, int position)
-int w2_threads();          // its threads per block
+const void *w2_kernel(int B);  // k_w2_mfma for B rows: arguments (Params, int position, int groups)
+int w2_groups(int B);           // its third argument
+int w2_threads(int B);     // its threads per block
 size_t w2_smem();          // its dynamic LDS per block
 int w2_grid(int B, int cus);  // blocks for B batch rows on cus compute units
 const void *state_kernel();   // k_state_mfma (bf16 weights): arguments (Params, int step q)

@@ -654,11 +654,13 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
     }
     // bf16 heads with r = 256 take the matrix-core W2 kernel
     const bool w2_mfma = c.wdtype == DOMINO_BF16 && c.r == dhbat::r_supported();
+    int w2_groups = w2_mfma ? dhbat::w2_groups(B) : 0;
     for (int pos = 0; pos < c.K; ++pos) {
         void *args[] = {&p, &pos};
+        void *margs[] = {&p, &pos, &w2_groups};
         if (w2_mfma)
-            HIP_TRY(hipLaunchKernel(dhbat::w2_kernel(), dim3(dhbat::w2_grid(B, hd->cus)), dim3(dhbat::w2_threads()),
-                                    args, dhbat::w2_smem(), st),
+            HIP_TRY(hipLaunchKernel(dhbat::w2_kernel(B), dim3(dhbat::w2_grid(B, hd->cus)), dim3(dhbat::w2_threads(B)),
+                                    margs, dhbat::w2_smem(), st),
                     "launch w2 (matrix cores)");
         else
             HIP_TRY(hipLaunchKernel(hd->kern.w2, dim3(g_w2), dim3(NT), args, sm_w2, st), "launch w2");

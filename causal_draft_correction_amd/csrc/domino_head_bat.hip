@@ -11,31 +11,34 @@
 
 namespace DH_NS {
 
-// Work split.  A block (512 threads, two waves per SIMD) takes a batch tile
-// of up to 128 rows (bt) and a contiguous vocabulary range (vb of nvb).  Its
-// eight waves take 16-row batch groups of the tile (ng groups) and, when the
-// tile has fewer than eight groups, split each vocabulary chunk's 16-row tiles
-// between nvs = 8 / ng wave sets.  A wave keeps its 16 batch rows of u in
-// registers as two matrix-core A operands: A tile a holds batch rows a*8 ..
-// a*8+7 as bf16 hi parts in rows 0..7 and lo parts (u - hi) in rows 8..15
-// (the operand form of the resident kernel).  Chunks of CR vocabulary rows of
-// W2 are staged through LDS in the B-operand layout ([tile][step][lane], 16
-// bytes each), double buffered: the next chunk is loaded into registers while
-// the current one is multiplied (v_mfma_f32_16x16x32_bf16, D = A W2_tile^T),
-// then written to the other buffer.  The epilogue adds each batch row's hi and
-// lo results, which one v_permlane32_swap of the two A tiles' results lines up
-// (sum hi + lo, the resident kernel's order), adds L_base (prefetched a chunk
-// ahead), stores L_final if requested and folds the greedy argmax into a
-// running best per lane.  At the end the 16 lanes of a batch row reduce it and
-// one lane folds it into the partial key slot of group blockIdx % NG.
-constexpr int BNT = 512;  // threads per block of the batched W2 kernel
+// Work split.  A block of NTH threads takes a batch tile of up to 128 rows (bt)
+// and a contiguous vocabulary range (vb of nvb).  Its waves take AT*8-row batch
+// groups of the tile (ng groups) and, when the tile has fewer groups than
+// waves, split each vocabulary chunk's 16-row tiles between nvs = waves / ng
+// wave sets (VTG tiles each).  A wave keeps its batch rows of u in registers
+// as AT matrix-core A operands: A tile a holds batch rows a*8 .. a*8+7 as bf16
+// hi parts in rows 0..7 and lo parts (u - hi) in rows 8..15 (the operand form
+// of the resident kernel).  Chunks of W2 are staged through LDS in the
+// B-operand layout ([tile][step][lane], 16 bytes each), double buffered, with
+// the registers of the chunk after next loaded while the current chunk is
+// multiplied (v_mfma_f32_16x16x32_bf16, D = A W2_tile^T).  The epilogue adds
+// each batch row's hi and lo results, which one v_permlane32_swap of two A
+// tiles' results lines up (sum hi + lo, the resident kernel's order), adds
+// L_base (loaded two chunks ahead), stores L_final if requested and folds the
+// greedy argmax into a running best per lane.  At the end the 16 lanes of a
+// batch row reduce it and one lane folds it into the partial key slot of group
+// blockIdx % NG.  Two configurations: 512 threads with AT = 2 (two waves per
+// SIMD; up to 128 rows) and 256 threads with AT = 4 (one wave per SIMD, half
+// the LDS operand traffic per result); the host uses the first.
 constexpr int XCDS = 8;   // accelerator dies (XCDs) of the MI355X, each with its own L2
-constexpr int BNW = BNT / 64;
 
-template <int KS>
-__global__ __launch_bounds__(BNT) void k_w2_mfma(Params p, int pos)
+template <int KS, int VTG, int AT, int NTH>
+__global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng)
 {
-    extern __shared__ uint4 wlds[];  // 2 buffers of (CR/16) * KS * 64 uint4
+    static_assert(AT == 2 || AT == 4, "A tiles per wave");
+    constexpr int NWV = NTH / 64;
+    constexpr int NP = AT / 2;  // A-tile pairs
+    extern __shared__ uint4 wlds[];  // 2 chunk buffers
     const int r = 32 * KS;
     const int B = p.B, V = p.V;
     // XCD-aware split: blocks go round-robin over the XCDs, so block i runs on XCD
@@ -45,25 +48,22 @@ __global__ __launch_bounds__(BNT) void k_w2_mfma(Params p, int pos)
     const int xcd = blockIdx.x % XCDS, j = blockIdx.x / XCDS;
     const int bt = j % nbt, vb = (j / nbt) * XCDS + xcd;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15;
-    const int rows = B - bt * 128 < 128 ? B - bt * 128 : 128;
-    const int need = (rows + 15) / 16;
-    const int ng = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;  // 16-row batch groups
-    const int nvs = BNW / ng;                                         // wave sets per chunk
+    const int nvs = NWV / ng;
     const int grp = wave % ng, vs = wave / ng;
-    const int CR = nvs <= 4 ? 64 : 128;  // chunk rows
-    const int VTG = (CR / 16) / nvs;     // 16-row tiles per wave set
-    const int row0 = bt * 128 + grp * 16;
+    const int CRr = nvs * VTG * 16;  // chunk rows
+    const int row0 = bt * 128 + grp * AT * 8;
     const long long v0 = static_cast<long long>(V) * vb / nvb;
     const int n = static_cast<int>(static_cast<long long>(V) * (vb + 1) / nvb - v0);
-    const int nchunk = (n + CR - 1) / CR;
+    const int nchunk = (n + CRr - 1) / CRr;
     const int g = blockIdx.x % NG;
-    const int slots = (CR / 16) * KS * 64;  // uint4 per chunk
-    const int per_thread = slots / BNT;     // 4 or 8
+    const int slots = (CRr / 16) * KS * 64;  // uint4 per chunk
+    constexpr int PT = 8;                    // staging registers per thread (max)
+    const int per_thread = slots / NTH;
 
     // A operands of this wave
-    uint4 ua[2][KS];
+    uint4 ua[AT][KS];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < AT; ++a) {
         const int b = row0 + a * 8 + (col & 7);
         const bool hi = col < 8;
         const float *src = p.u_buf + static_cast<size_t>(b < B ? b : 0) * r + (lane >> 4) * 8;
@@ -77,14 +77,14 @@ __global__ __launch_bounds__(BNT) void k_w2_mfma(Params p, int pos)
                 x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
             } else {
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    x[j] = 0.f;
+                for (int jj = 0; jj < 8; ++jj)
+                    x[jj] = 0.f;
             }
             uint32_t hv[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t xh = bf16_rne_bits(x[j]);
-                hv[j] = hi ? xh : bf16_rne_bits(x[j] - __uint_as_float(xh << 16));
+            for (int jj = 0; jj < 8; ++jj) {
+                const uint32_t xh = bf16_rne_bits(x[jj]);
+                hv[jj] = hi ? xh : bf16_rne_bits(x[jj] - __uint_as_float(xh << 16));
             }
             ua[a][kk] = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
                                    hv[6] | (hv[7] << 16));
@@ -92,119 +92,129 @@ __global__ __launch_bounds__(BNT) void k_w2_mfma(Params p, int pos)
     }
 
     // staging: slot s of a chunk = (tile, step, lane) -> 16 bytes of W2
-    auto stage_load = [&](int c, uint4 (&st)[8]) {
+    auto stage_load = [&](int c, uint4 (&st)[PT]) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (j < per_thread) {
-                const int s = threadIdx.x + j * BNT;
+        for (int jj = 0; jj < PT; ++jj) {
+            if (jj < per_thread) {
+                const int s = threadIdx.x + jj * NTH;
                 const int vt = s / (KS * 64), kk = (s / 64) % KS, ln = s & 63;
-                const int vr = c * CR + vt * 16 + (ln & 15);
-                st[j] = vr < n ? ld16<bf16s>(p.W2, static_cast<size_t>(v0 + vr) * r + kk * 32 + (ln >> 4) * 8)
-                               : make_uint4(0u, 0u, 0u, 0u);
+                const int vr = c * CRr + vt * 16 + (ln & 15);
+                st[jj] = vr < n ? ld16<bf16s>(p.W2, static_cast<size_t>(v0 + vr) * r + kk * 32 + (ln >> 4) * 8)
+                                : make_uint4(0u, 0u, 0u, 0u);
             }
         }
     };
-    auto stage_store = [&](int buf, const uint4 (&st)[8]) {
+    auto stage_store = [&](int buf, const uint4 (&st)[PT]) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < per_thread)
-                wlds[buf * slots + threadIdx.x + j * BNT] = st[j];
+        for (int jj = 0; jj < PT; ++jj)
+            if (jj < per_thread)
+                wlds[buf * slots + threadIdx.x + jj * NTH] = st[jj];
     };
-    // this lane's batch row in the combined results: A tile (lane / 32), row i of four
-    int brow[4];
+    // this lane's batch rows in the combined results: pair pp packs A tiles 2pp
+    // (lanes 0..31) and 2pp+1 (lanes 32..63), row i of four
+    int brow[NP][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        brow[i] = row0 + (lane >> 5) * 8 + ((lane >> 4) & 1) * 4 + i;
-    // L_base of this lane's epilogue values for chunk c (tile index vt of the wave set)
-    auto lbase_load = [&](int c, float (&lb)[4][4]) {
+    for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
-        for (int vt = 0; vt < 4; ++vt)
+        for (int i = 0; i < 4; ++i)
+            brow[pp][i] = row0 + (2 * pp + (lane >> 5)) * 8 + ((lane >> 4) & 1) * 4 + i;
+    // L_base of this lane's epilogue values for chunk c
+    auto lbase_load = [&](int c, float (&lb)[NP][VTG][4]) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (vt < VTG) {
-                    const int b = brow[i], vr = c * CR + (vs * VTG + vt) * 16 + col;
+        for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+            for (int vt = 0; vt < VTG; ++vt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int b = brow[pp][i], vr = c * CRr + (vs * VTG + vt) * 16 + col;
                     const size_t o = (static_cast<size_t>(b < B ? b : 0) * p.K + pos) * V + v0 + (vr < n ? vr : 0);
-                    lb[vt][i] = __builtin_nontemporal_load(p.L_base + o);  // streamed once
+                    lb[pp][vt][i] = __builtin_nontemporal_load(p.L_base + o);  // streamed once
                 }
-            }
     };
 
-    LaneBest best[4];
-    uint4 st[8];
-    float lbc[4][4], lbn[4][4];
+    LaneBest best[NP][4];
+    // two chunks in flight: the W2 registers and the L_base values of chunk c+2 are
+    // loaded while chunk c is multiplied; register sets alternate with the chunk
+    // parity (the loop is unrolled by two so the sets are fixed)
+    uint4 st[2][PT];
+    float lb[2][NP][VTG][4];
     if (nchunk > 0) {
-        stage_load(0, st);
-        lbase_load(0, lbc);
-        stage_store(0, st);
+        stage_load(0, st[0]);
+        lbase_load(0, lb[0]);
+        stage_store(0, st[0]);
+    }
+    if (nchunk > 1) {
+        stage_load(1, st[1]);
+        lbase_load(1, lb[1]);
     }
     __syncthreads();
-#pragma unroll 1
-    for (int c = 0; c < nchunk; ++c) {
-        const int buf = c & 1;
-        const bool more = c + 1 < nchunk;
-        if (more) {
-            stage_load(c + 1, st);
-            lbase_load(c + 1, lbn);
-        }
-        f32x4_t acc[2][4];
+    auto step = [&](int c, int P) {
+        if (c + 2 < nchunk)
+            stage_load(c + 2, st[P]);
+        f32x4_t acc[AT][VTG];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < AT; ++a)
 #pragma unroll
-            for (int vt = 0; vt < 4; ++vt)
+            for (int vt = 0; vt < VTG; ++vt)
                 acc[a][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const uint4 *wb = wlds + buf * slots;
+        const uint4 *wb = wlds + P * slots;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-            for (int vt = 0; vt < 4; ++vt) {
-                if (vt < VTG) {
-                    const uint4 w = wb[((vs * VTG + vt) * KS + kk) * 64 + lane];
+            for (int vt = 0; vt < VTG; ++vt) {
+                const uint4 w = wb[((vs * VTG + vt) * KS + kk) * 64 + lane];
 #pragma unroll
-                    for (int a = 0; a < 2; ++a)
-                        acc[a][vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ua[a][kk]),
-                                                                            __builtin_bit_cast(bf16x8_t, w),
-                                                                            acc[a][vt], 0, 0, 0);
-                }
+                for (int a = 0; a < AT; ++a)
+                    acc[a][vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ua[a][kk]),
+                                                                        __builtin_bit_cast(bf16x8_t, w), acc[a][vt],
+                                                                        0, 0, 0);
             }
 #pragma unroll
-        for (int vt = 0; vt < 4; ++vt) {
-            if (vt < VTG) {
-                const int vr = c * CR + (vs * VTG + vt) * 16 + col;
+        for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+            for (int vt = 0; vt < VTG; ++vt) {
+                const int vr = c * CRr + (vs * VTG + vt) * 16 + col;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    // {hi of tile 0, hi of tile 1} + {lo of tile 0, lo of tile 1}
-                    const auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0][vt][i]),
-                                                                    __float_as_uint(acc[1][vt][i]), false, false);
+                    // {hi of tile 2pp, hi of tile 2pp+1} + {lo of tile 2pp, lo of tile 2pp+1}
+                    const auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[2 * pp][vt][i]),
+                                                                    __float_as_uint(acc[2 * pp + 1][vt][i]), false,
+                                                                    false);
                     const float w = __uint_as_float(d[0]) + __uint_as_float(d[1]);
-                    const int b = brow[i];
+                    const int b = brow[pp][i];
                     const bool ok = b < B && vr < n;
                     float *lf = p.L_final ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * V + v0 : nullptr;
-                    w2_key(w, lbc[vt][i], lf, static_cast<int>(v0), vr, ok, best[i]);
+                    w2_key(w, lb[P][pp][vt][i], lf, static_cast<int>(v0), vr, ok, best[pp][i]);
                 }
             }
-        }
-        if (more) {
-            stage_store(buf ^ 1, st);
-#pragma unroll
-            for (int vt = 0; vt < 4; ++vt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    lbc[vt][i] = lbn[vt][i];
-        }
+        if (c + 2 < nchunk)
+            lbase_load(c + 2, lb[P]);
+        if (c + 1 < nchunk)
+            stage_store(P ^ 1, st[P ^ 1]);
         __syncthreads();
+    };
+#pragma unroll 1
+    for (int c = 0; c < nchunk; c += 2) {
+        step(c, 0);
+        if (c + 1 < nchunk)
+            step(c + 1, 1);
     }
     // each batch row's best over its 16 lanes, folded into the partial key slot
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint64_t key = best[i].ord ? (static_cast<uint64_t>(best[i].ord) << 32) | (0xFFFFFFFFu - best[i].idx) : 0ull;
-        key = max_u64(key, dpp_u64<DPP_QUAD_XOR1>(key));
-        key = max_u64(key, dpp_u64<DPP_QUAD_XOR2>(key));
-        key = max_u64(key, dpp_u64<DPP_HALF_MIRROR>(key));
-        key = max_u64(key, dpp_u64<DPP_ROW_MIRROR>(key));
-        const int b = brow[i];
-        if (col == 0 && b < B && key)
-            __hip_atomic_fetch_max(key_slot(p, pos, g, b), key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint64_t key = best[pp][i].ord ? (static_cast<uint64_t>(best[pp][i].ord) << 32) |
+                                                 (0xFFFFFFFFu - best[pp][i].idx)
+                                           : 0ull;
+            key = max_u64(key, dpp_u64<DPP_QUAD_XOR1>(key));
+            key = max_u64(key, dpp_u64<DPP_QUAD_XOR2>(key));
+            key = max_u64(key, dpp_u64<DPP_HALF_MIRROR>(key));
+            key = max_u64(key, dpp_u64<DPP_ROW_MIRROR>(key));
+            const int b = brow[pp][i];
+            if (col == 0 && b < B && key)
+                __hip_atomic_fetch_max(key_slot(p, pos, g, b), key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
 }
 
 // State-phase dot products of the stepwise launches at larger B, on the matrix
@@ -369,8 +379,26 @@ using namespace dh256;
 
 int r_supported() { return 32 * BAT_KS; }
 int threads() { return NT; }
-const void *w2_kernel() { return reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS>); }
-int w2_threads() { return BNT; }
+// Launch shape of the batched W2 kernel for B rows: 512 threads (2 A tiles per
+// wave, two waves per SIMD) with ng 16-row groups per batch tile.  (Four A tiles
+// per wave in 256-thread blocks halve the LDS operand traffic but, with one wave
+// per SIMD, measured 123 us against 85 us per 8B position at B = 256.)
+struct W2Shape {
+    const void *fn;
+    int threads, ng;
+};
+static W2Shape w2_shape(int B)
+{
+    const int need = ((B < 128 ? B : 128) + 15) / 16;
+    const int ng = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+    const void *fn = ng == 8   ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 4, 2, 512>)
+                     : ng == 4 ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 2, 2, 512>)
+                               : reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 1, 2, 512>);
+    return {fn, 512, ng};
+}
+const void *w2_kernel(int B) { return w2_shape(B).fn; }
+int w2_groups(int B) { return w2_shape(B).ng; }
+int w2_threads(int B) { return w2_shape(B).threads; }
 // one block per compute unit: batch tiles times vocabulary ranges
 int w2_grid(int B, int cus)
 {

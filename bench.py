@@ -47,6 +47,20 @@ def logical_bytes(sh, B, store_logits=False, fold=False):
     return total, K * (V * r * s + B * V * 4)
 
 
+def algorithmic_flops(sh, B, fold=False):
+    """Useful FLOPs of one call (the matrix-core path computes W2 and the state dot
+    products twice, on bf16 hi and lo parts; that is not counted).  Returns
+    (W2 only, all contractions: W2 + W1 + GRU)."""
+    K, V, r, h, d = sh.K, sh.V, sh.r, sh.h, sh.d
+    w2 = 2 * B * r * V * K
+    w1 = 2 * B * r * (d + h) * K
+    gru = 2 * B * 3 * h * h * K + (0 if fold else 2 * B * 3 * h * d * K)
+    return w2, w2 + w1 + gru
+
+
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
 def kernel_source_hash():
     import glob
     import hashlib
@@ -186,6 +200,12 @@ def main():
     else:
         kname = "stepwise launches (whole call)"
 
+    f_w2, f_all = algorithmic_flops(sh, wl.B, fold)
+    mfma = {"w2_tflops": f_w2 / (avg_ms * 1e-3) / 1e12, "all_tflops": f_all / (avg_ms * 1e-3) / 1e12,
+            "peak_tflops": MFMA_PEAK_TFLOPS}
+    mfma["w2_frac"] = mfma["w2_tflops"] / MFMA_PEAK_TFLOPS
+    mfma["all_frac"] = mfma["all_tflops"] / MFMA_PEAK_TFLOPS
+
     cpu = None
     if not args.no_cpu_baseline:
         eprint("bench: timing the fp64 oracle on the host (cpu_baseline)")
@@ -212,7 +232,7 @@ def main():
                    "fold_embedding": fold, "w2_on_chip": w2_on_chip,
                    "launch": "plain" if args.plain_launch else "cooperative", "create_s": t_create,
                    "kernel_avg_us": avg_ms * 1e3, "w2_lbase_GBps": w2l,
-                   "w2_lbase_frac_of_hbm_peak": w2l / HBM_PEAK_GBPS},
+                   "w2_lbase_frac_of_hbm_peak": w2l / HBM_PEAK_GBPS, "matrix_core_use": mfma},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes": total_bytes, "kernel": kname},

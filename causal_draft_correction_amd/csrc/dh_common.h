@@ -376,11 +376,19 @@ __device__ inline bool grid_sync(unsigned *bar, unsigned &gen, unsigned spin_lim
 // its 32 bits unused).  Wait: every block reads every word until it
 // carries the new generation and reduces the keys itself, leaving the tokens
 // of this position in tok[0..nb) (visible to the whole block on return).  Generations compare modulo 2^14 (a word is
-// ready when it is at most 2^13 ahead).  A word is rewritten only at the next
-// argmax barrier, which no block reaches before every block has passed the
-// grid barrier in between.  Arrival words: asy[blk*BC + b].
+// ready when it is at most 2^13 ahead).  The words of even and odd generations
+// are kept apart: a block may arrive at the next argmax barrier while a slower
+// one still reads the words of this one (nothing between two argmax barriers
+// waits for every block), but it cannot arrive at the one after before every
+// block has arrived at the next, which each does only after its wait here.
+// Arrival words: asy[(gen & 1) * MAX_GRID * BC + blk * BC + b].
 // ---------------------------------------------------------------------------
-constexpr int ASYNC_WORDS = MAX_GRID * BC;
+constexpr int ASYNC_WORDS = 2 * MAX_GRID * BC;
+
+__device__ inline size_t argmax_word(unsigned gen, int blk, int b)
+{
+    return static_cast<size_t>(gen & 1u) * (MAX_GRID * BC) + static_cast<size_t>(blk) * BC + b;
+}
 constexpr uint64_t KEY_ORD_MASK = 0xFFFFFFFF00000000ull;
 constexpr uint64_t KEY_IDX_MASK = 0x3FFFFull;
 
@@ -398,10 +406,14 @@ __device__ inline void argmax_arrive(uint64_t *asy, unsigned gen, const uint64_t
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
-    if (threadIdx.x < nb)
-        __hip_atomic_store(&asy[blockIdx.x * BC + threadIdx.x],
-                           (local_key[threadIdx.x] & (KEY_ORD_MASK | KEY_IDX_MASK)) | g14, __ATOMIC_RELAXED,
+    // the words of rows nb..BC-1 get the generation too (with key 0): every word
+    // is then at most one generation old, and a later launch with more rows never
+    // takes one written many launches ago for a current one
+    if (threadIdx.x < BC) {
+        const uint64_t k = threadIdx.x < nb ? local_key[threadIdx.x] & (KEY_ORD_MASK | KEY_IDX_MASK) : 0;
+        __hip_atomic_store(&asy[argmax_word(gen + 1, blockIdx.x, threadIdx.x)], k | g14, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+    }
     DH_TRACE((static_cast<int>(gen + 1) - 2) * 32 + 8);
 }
 
@@ -419,7 +431,7 @@ __device__ inline bool argmax_wait(const uint64_t *asy, unsigned &gen, int nb, i
     int ok = 1;
     for (int e = threadIdx.x; e < total; e += NT) {
         const int blk = e / nb, b = e % nb;
-        const uint64_t *wp = &asy[blk * BC + b];
+        const uint64_t *wp = &asy[argmax_word(next, blk, b)];
         uint64_t w;
         unsigned spins = 0;
         for (;;) {

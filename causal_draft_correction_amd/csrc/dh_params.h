@@ -32,6 +32,7 @@ struct Params {
     unsigned spin_limit;
     int persistent;  // 1: blocks keep the state in LDS between phases
     int ah_external; // 1: A_H is computed by its own (matrix-core) launch, not by the prologue
+    int bf16w;       // 1: weights are bf16, 0: float32
 };
 
 }  // namespace dhp

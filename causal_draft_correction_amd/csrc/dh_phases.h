@@ -140,11 +140,18 @@ __device__ inline float wave_dot(const void *W, size_t off, int n, XF xf)
     return wave_sum(acc);
 }
 
+// A_H sums have one layout in every kernel: AH_LANES partial sums, lane t taking
+// the 8- or 4-element chunks t, t + AH_LANES, ... of the row, reduced by wave
+// (64 lanes) and then over the waves in order.  Threads beyond AH_LANES add
+// zeros, so each entry is the same bits whatever the block size.
+constexpr int AH_LANES = 256;
+
 // ---- phase: A_H = W1[:, :d] H for every position ------------------------------
 template <typename WT>
 __device__ __forceinline__ void phase_ah(const Params &p, int blk, int nblk, float *red)
 {
     constexpr int EPC = WT16<WT>::EPC;
+    static_assert(NT >= AH_LANES, "block too small for the A_H sum layout");
     const int nch = p.d / EPC;
     const int ntask = p.B * p.r;
     for (int task = blk; task < ntask; task += nblk) {
@@ -153,7 +160,7 @@ __device__ __forceinline__ void phase_ah(const Params &p, int blk, int nblk, flo
 #pragma unroll
         for (int i = 0; i < MAXK; ++i)
             acc[i] = 0.f;
-        for (int c = threadIdx.x; c < nch; c += NT) {
+        for (int c = threadIdx.x; threadIdx.x < AH_LANES && c < nch; c += AH_LANES) {
             float w[EPC];
             WT16<WT>::unpack(ld16<WT>(p.W1, static_cast<size_t>(k) * (p.d + p.h) + static_cast<size_t>(c) * EPC), w);
 #pragma unroll
@@ -226,6 +233,14 @@ __device__ __forceinline__ void phase_g(const Params &p, int blk, int nblk, int 
     }
 }
 
+// Entry m of b_hh (0 without biases), either weight type.
+__device__ inline float bias_hh(const Params &p, int m)
+{
+    if (!p.b_hh)
+        return 0.f;
+    return p.bf16w ? WT16<bf16s>::one(p.b_hh, m) : WT16<float>::one(p.b_hh, m);
+}
+
 // ---- GRU gate update of one state entry ---------------------------------------------
 // S_q[b][j] from g (P row or g_buf), q_{q-1} (W_hh S_{q-1} + b_hh) and S_{q-1}[b][j].
 __device__ inline float gate_update(const Params &p, int q, int b, int j, int tokb, float sprev)
@@ -243,8 +258,18 @@ __device__ inline float gate_update(const Params &p, int q, int b, int j, int to
         gz = xld(&g[h + j]);
         gn = xld(&g[2 * h + j]);
     }
-    const float *qv = q_slot(p, q) + static_cast<size_t>(b) * h3;
-    const float qr = xld(&qv[j]), qz = xld(&qv[h + j]), qn = xld(&qv[2 * h + j]);
+    float qr, qz, qn;
+    if (q == 0 && !p.S_init) {
+        // W_hh S_init + b_hh with S_init = 0 is b_hh itself
+        qr = bias_hh(p, j);
+        qz = bias_hh(p, h + j);
+        qn = bias_hh(p, 2 * h + j);
+    } else {
+        const float *qv = q_slot(p, q) + static_cast<size_t>(b) * h3;
+        qr = xld(&qv[j]);
+        qz = xld(&qv[h + j]);
+        qn = xld(&qv[2 * h + j]);
+    }
     const float rg = sigmoidf_(gr + qr);
     const float zg = sigmoidf_(gz + qz);
     const float ng = tanhf(gn + rg * qn);
@@ -337,6 +362,11 @@ __device__ __forceinline__ void state_prefetch(const Params &p, int q, StatePre 
     }
 }
 
+// State rows of a wave: m0, m0 + NWAVE * nblk, ... with m0 = state_row0.  The
+// numbering is wave-major, so the r u rows (the first rows) are spread over all
+// blocks instead of filling the first r / NWAVE of them.
+__host__ __device__ inline int state_row0(int blk, int nblk, int wave) { return wave * nblk + blk; }
+
 // Rows of the state phase handled by each wave of a persistent launch, and the
 // LDS it takes to keep them: the rows (WT) plus their A_H entries for every
 // position and batch row (u rows only).
@@ -352,8 +382,9 @@ __host__ __device__ inline int state_cache_floats(int r, int h, int K, int nblk,
 
 // Once per persistent launch, after the prologue barrier: each wave copies its
 // state rows and their A_H entries into LDS.
+// with_ah = false leaves the A_H entries to ah_local_to_cache.
 template <typename WT>
-__device__ __forceinline__ void state_cache_load(const Params &p, int blk, int nblk, float *cache)
+__device__ __forceinline__ void state_cache_load(const Params &p, int blk, int nblk, float *cache, bool with_ah = true)
 {
     constexpr int EPC = WT16<WT>::EPC;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -362,7 +393,7 @@ __device__ __forceinline__ void state_cache_load(const Params &p, int blk, int n
     uint4 *wc = reinterpret_cast<uint4 *>(cache);
     float *ac = cache + NWAVE * rpw * row_words;
     for (int k = 0; k < rpw; ++k) {
-        const int m = blk * NWAVE + wave + k * nblk * NWAVE;
+        const int m = state_row0(blk, nblk, wave) + k * nblk * NWAVE;
         if (m >= R)
             break;
         const void *W = m < p.r ? p.W1 : p.W_hh;
@@ -370,7 +401,7 @@ __device__ __forceinline__ void state_cache_load(const Params &p, int blk, int n
         for (int ch = lane; ch < h / EPC; ch += 64)
             wc[(wave * rpw + k) * (h / EPC) + ch] = ld16<WT>(W, off + static_cast<size_t>(ch) * EPC);
         if (m < p.r) {
-            for (int i = lane; i < p.K * p.B; i += 64) {
+            for (int i = lane; with_ah && i < p.K * p.B; i += 64) {
                 const int qq = i / p.B, b = i % p.B;
                 ac[((wave * rpw + k) * p.K + qq) * BC + b] = xld(&p.A_H[(static_cast<size_t>(b) * p.K + qq) * p.r + m]);
             }
@@ -381,13 +412,121 @@ __device__ __forceinline__ void state_cache_load(const Params &p, int blk, int n
     }
 }
 
+// A_H entries of the block's u rows for batch row 0, computed by the block itself
+// into the owner waves' cache slots (persistent launch at B = 1: each u row has
+// one owner wave, so nothing crosses blocks): A_H[0][i][m] = W1[m][0:d] . H[0][i].
+// Wave w takes the positions i = w, w + NWAVE, ...  Each lane keeps the partial
+// sums of the AH_LANES / 64 lanes at its index in the A_H sum layout, over the
+// same chunks in the same order, and reduces them in the same order, so the
+// entries equal phase_ah's bit for bit.  All loads of a row are issued
+// before the first product.
+template <typename WT>
+__device__ __forceinline__ void ah_local_to_cache(const Params &p, int blk, int nblk, float *cache)
+{
+    constexpr int EPC = WT16<WT>::EPC;
+    constexpr int PW = MAXK / NWAVE;   // positions per wave
+    constexpr int KK = 2;              // AH_LANES-chunk strides loaded together
+    constexpr int VW = AH_LANES / 64;  // waves of the sum layout
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int h = p.h, d = p.d, rpw = state_rows_per_wave(p.r, h, nblk), mstep = nblk * NWAVE;
+    const int nch = d / EPC;
+    float *ac = cache + NWAVE * rpw * (h * static_cast<int>(sizeof(WT)) / 4);
+    for (int ow = 0; ow < NWAVE; ++ow) {
+        for (int k = 0; k < rpw; ++k) {
+            const int m = state_row0(blk, nblk, ow) + k * mstep;
+            if (m >= p.r)
+                break;
+            float acc[PW][VW];
+#pragma unroll
+            for (int t = 0; t < PW; ++t)
+#pragma unroll
+                for (int vw = 0; vw < VW; ++vw)
+                    acc[t][vw] = 0.f;
+            for (int c0 = 0; c0 < nch; c0 += KK * AH_LANES) {
+                uint4 wv[KK][VW], xv[KK][VW][PW];
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+                    for (int vw = 0; vw < VW; ++vw) {
+                        const int c = c0 + kk * AH_LANES + vw * 64 + lane;
+                        if (c < nch) {
+                            wv[kk][vw] = ld16<WT>(p.W1, static_cast<size_t>(m) * (d + h) + static_cast<size_t>(c) * EPC);
+#pragma unroll
+                            for (int t = 0; t < PW; ++t)
+                                if (wave + t * NWAVE < p.K)
+                                    xv[kk][vw][t] = ld16<WT>(p.H, static_cast<size_t>(wave + t * NWAVE) * d +
+                                                                      static_cast<size_t>(c) * EPC);
+                        }
+                    }
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+                    for (int vw = 0; vw < VW; ++vw) {
+                        const int c = c0 + kk * AH_LANES + vw * 64 + lane;
+                        if (c < nch) {
+                            float w[EPC];
+                            WT16<WT>::unpack(wv[kk][vw], w);
+#pragma unroll
+                            for (int t = 0; t < PW; ++t) {
+                                if (wave + t * NWAVE < p.K) {
+                                    float x[EPC];
+                                    WT16<WT>::unpack(xv[kk][vw][t], x);
+#pragma unroll
+                                    for (int e = 0; e < EPC; ++e)
+                                        acc[t][vw] = fmaf(w[e], x[e], acc[t][vw]);
+                                }
+                            }
+                        }
+                    }
+            }
+#pragma unroll
+            for (int t = 0; t < PW; ++t) {
+                const int i = wave + t * NWAVE;
+                if (i < p.K) {
+                    float sum = 0.f;
+#pragma unroll
+                    for (int vw = 0; vw < VW; ++vw)
+                        sum += wave_sum(acc[t][vw]);
+                    if (lane == 0)
+                        ac[((ow * rpw + k) * p.K + i) * BC] = sum;
+                }
+            }
+        }
+    }
+}
+
+// A launch with B rows writes no tagged u words of rows B..min(BC, maxB)-1.  At
+// its end they get the launch's last tag, so every word holds a tag at most one
+// launch old: the tags a later launch polls for all lie ahead of it, whatever
+// its B.
+__device__ inline void utag_refresh(const Params &p, int blk, int nblk, unsigned last_tag)
+{
+    const int rows = (p.maxB < BC ? p.maxB : BC) - p.B;
+    if (rows <= 0)
+        return;
+    const uint32_t t16 = (last_tag & 0xFFFFu) << 16;
+    const size_t base = static_cast<size_t>(p.B) * p.r, n = static_cast<size_t>(rows) * p.r;
+    const size_t plane = static_cast<size_t>(p.maxB) * p.r;
+    for (size_t i = static_cast<size_t>(blk) * NT + threadIdx.x; i < n; i += static_cast<size_t>(nblk) * NT) {
+        __hip_atomic_store(&p.utag[base + i], t16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.utag[plane + base + i], t16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // With p.utag (resident launch) u_q is published as tagged operand words
 // instead of u_buf: (tag << 16) | bf16 bits, hi part in plane 0 and lo part
 // (u - hi) in plane 1; readers poll for `tag`.
-template <typename WT>
+struct NoHook {
+    __device__ void operator()() const {}
+};
+
+// after_gate() runs between the gate update and the dot products (a persistent
+// kernel issues its long loads there, after the gate update's latency-critical ones).
+template <typename WT, typename AfterGate = NoHook>
 __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, int q, float *smem, float *S_lds,
                                             const StatePre *pre, const float *cache, bool cached,
-                                            const int *atok = nullptr, unsigned tag = 0)
+                                            const int *atok = nullptr, unsigned tag = 0,
+                                            AfterGate after_gate = AfterGate())
 {
     constexpr int EPC = WT16<WT>::EPC;
     const int h = p.h, h3 = 3 * h, r = p.r;
@@ -452,6 +591,7 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                 S_lds[i] = xld(&S_slot(p, q)[static_cast<size_t>(b0) * h + i]);
         }
         DH_TRACE(tslot + 2);
+        after_gate();
         __syncthreads();
         DH_TRACE(tslot + 3);
         // dot rows of this wave: k-th row m = m0 + k * mstep; when `cached` (persistent
@@ -461,7 +601,7 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
         // The wave's u rows (m < r) form the first groups, so u is published before
         // the q rows are computed.
         constexpr int RG = 4;
-        const int m0 = blk * NWAVE + wave, mstep = nblk * NWAVE;
+        const int m0 = state_row0(blk, nblk, wave), mstep = nblk * NWAVE;
         const int rpw = state_rows_per_wave(r, h, nblk);
         const int ku = m0 < r ? (r - m0 + mstep - 1) / mstep : 0;  // this wave's u rows
         const uint4 *wc = reinterpret_cast<const uint4 *>(cache);

@@ -521,6 +521,7 @@ static Params make_params(domino_head_t hd, int B, const void *H, const float *L
 {
     const domino_head_config &c = hd->cfg;
     Params p{};
+    p.bf16w = c.wdtype == DOMINO_BF16 ? 1 : 0;
     p.d = c.d;
     p.h = c.h;
     p.r = c.r;

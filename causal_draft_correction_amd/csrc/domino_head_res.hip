@@ -23,6 +23,7 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
     int *atok = reinterpret_cast<int *>(smem + smem_off_tok()) + ATOK_OFF;
     int *bad = atok + BC;
     uint64_t *local_keys = reinterpret_cast<uint64_t *>(smem);
+    DH_TRACE(511);
     unsigned gen = barrier_gen_init(p.bar);
     block_fail_init();
     if (blk == 0) {
@@ -30,21 +31,40 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
         if (threadIdx.x < p.B)
             bad[threadIdx.x] = row_bad(p, threadIdx.x) ? 1 : 0;
     }
-    phase_ah<bf16s>(p, blk, nblk, smem);
-    phase_q_init<bf16s>(p, blk, nblk);
-    lbase_to_lds(p, blk, nblk, 0, smem);
-    if (!p.P)
-        phase_g<bf16s>(p, blk, nblk, 0, smem);
-    // the slice load overlaps the first barrier and state phase
+    // u words of a position carry tag gen + 1 (gen: the barrier generation when its
+    // state phase runs), never 0, the value cleared words hold
     W2Resident<RT, KS> res;
-    w2_resident_load<RT, KS>(p, blk, nblk, res, tl);
-    if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
-        return;
+    if (NB == 1 && !p.S_init && p.P) {
+        // one batch row, no initial state, folded table: the prologue needs no grid
+        // barrier.  Each wave computes the A_H entries of its own u rows, q_0 is
+        // b_hh, and the W2 slice load is issued after the anchor gate update's
+        // loads, so it overlaps the dot products and the first u exchange
+        lbase_to_lds(p, blk, nblk, 0, smem);
+        state_cache_load<bf16s>(p, blk, nblk, cache, false);
+        ah_local_to_cache<bf16s>(p, blk, nblk, cache);
+        DH_TRACE(508);
+        DH_TRACE(510);
+        phase_state<bf16s>(p, blk, nblk, 0, smem, S_lds, nullptr, cache, true, nullptr, gen + 1,
+                           [&] { w2_resident_load<RT, KS>(p, blk, nblk, res, tl); });
+    } else {
+        phase_ah<bf16s>(p, blk, nblk, smem);
+        phase_q_init<bf16s>(p, blk, nblk);
+        lbase_to_lds(p, blk, nblk, 0, smem);
+        if (!p.P)
+            phase_g<bf16s>(p, blk, nblk, 0, smem);
+        // the slice load overlaps the first barrier
+        w2_resident_load<RT, KS>(p, blk, nblk, res, tl);
+        DH_TRACE(508);
+        if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+            return;
+        DH_TRACE(510);
+        state_cache_load<bf16s>(p, blk, nblk, cache);
+        phase_state<bf16s>(p, blk, nblk, 0, smem, S_lds, nullptr, cache, true, nullptr, gen + 1);
+    }
     // from here on one barrier per position: the argmax barrier, which also
     // publishes the q values of the state phase before it; u travels in tagged
-    // words that the W2 phase polls (tag = barrier generation of its position)
-    state_cache_load<bf16s>(p, blk, nblk, cache);
-    phase_state<bf16s>(p, blk, nblk, 0, smem, S_lds, nullptr, cache, true, nullptr, gen);
+    // words that the W2 phase polls
+    DH_TRACE(509);
     for (int pos = 0; pos < p.K; ++pos) {
         // the output and exchange pointers pass through an opaque copy each position,
         // so the per-thread addresses derived from them are recomputed here instead of
@@ -52,7 +72,7 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
         Params pl = p;
         asm volatile("" : "+s"(pl.asy), "+s"(pl.tokens), "+s"(pl.utag), "+s"(pl.q_buf), "+s"(pl.P), "+s"(pl.L_final),
                           "+s"(pl.S_out), "+s"(pl.u_out), "+s"(pl.L_base));
-        if (!phase_w2_resident<RT, KS, NB>(pl, blk, nblk, pos, smem, res, tl, local_keys, gen))
+        if (!phase_w2_resident<RT, KS, NB>(pl, blk, nblk, pos, smem, res, tl, local_keys, gen + 1))
             return;
         argmax_arrive(pl.asy, gen, local_keys, pl.B);
         // L_base of the next position goes to LDS while the barrier is awaited (the
@@ -72,9 +92,11 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
             }
             // q of this step is visible only after the argmax barrier: its loads go out
             // together with those of the P row
-            phase_state<bf16s>(pl, blk, nblk, pos + 1, smem, S_lds, nullptr, cache, true, atok, gen);
+            phase_state<bf16s>(pl, blk, nblk, pos + 1, smem, S_lds, nullptr, cache, true, atok, gen + 1);
         }
     }
+    // the last position's tag is gen
+    utag_refresh(p, blk, nblk, gen);
     barrier_finish(p.bar, gen);
 }
 

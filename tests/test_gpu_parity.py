@@ -310,16 +310,52 @@ def test_batched_w2_matrix_cores_match_oracle(V, B, fold):
         assert np.array_equal(a[k], b[k]), k
 
 
-def test_batched_w2_equals_resident_kernel_bitwise():
+@pytest.mark.parametrize("B", [1, 4])
+def test_batched_w2_equals_resident_kernel_bitwise(B):
     """Both matrix-core W2 paths form each logit as L_base + (hi + lo) from the same
-    instruction on the same operands, and share the state phase arithmetic: the
-    stepwise launches and the resident persistent launch agree bitwise."""
-    sh = ds.HeadShape(d=128, h=64, r=256, V=9001, K=16, wdtype="bf16")
+    instruction on the same operands, and share the state phase arithmetic (at
+    B = 1 the resident launch forms A_H inside each block, in phase_ah's order):
+    the stepwise launches and the resident persistent launch agree bitwise."""
+    sh = ds.HeadShape(d=5136, h=64, r=256, V=9001, K=16, wdtype="bf16")
     w = ds.make_weights(sh, (9, 72), gru_sensitive=True)
-    inp = ds.make_inputs(sh, 4, (9, 73), sigma=0.5, peak="none")
+    inp = ds.make_inputs(sh, B, (9, 73), sigma=0.5, peak="none")
     pers = make_head(w, 4, dca.EXEC_PERSISTENT, fold=True)
-    assert pers.exec_info(4)["w2_resident"]
+    assert pers.exec_info(B)["w2_resident"]
     a, _ = gpu_draft(pers, inp.H, inp.L_base, inp.last_tok)
     c, _ = gpu_draft(make_head(w, 4, dca.EXEC_STEPWISE, fold=True), inp.H, inp.L_base, inp.last_tok)
     for k in ("tokens", "L_final", "S", "u"):
         assert np.array_equal(a[k], c[k]), k
+
+
+def test_resident_handle_with_varying_batch():
+    """One handle drafting many blocks with few rows and then one with more rows.
+    The exchange words of rows a launch does not draft are left from earlier
+    launches; they must never pass for current ones, however many launches lie
+    between (the 16-bit u tags and the 14-bit argmax generations wrap).  4095
+    single-row blocks bring the barrier generation past 2^16 before the
+    three-row block, which must equal the same block drafted on a fresh handle."""
+    sh = ds.HeadShape(d=128, h=64, r=256, V=9001, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 80), gru_sensitive=True)
+    inp3 = ds.make_inputs(sh, 3, (9, 81), sigma=0.5, peak="none")
+    inp1 = ds.make_inputs(sh, 1, (9, 82), sigma=0.5, peak="none")
+    head = make_head(w, 4, dca.EXEC_PERSISTENT, fold=True)
+    assert head.exec_info(1)["w2_resident"] and head.exec_info(3)["w2_resident"]
+    H1, L1 = dca.device_tensor(inp1.H), dca.device_tensor(inp1.L_base)
+    t1 = dca.device_tensor(np.asarray(inp1.last_tok, np.int32))
+    out = {"tokens": torch.empty((1, sh.K), dtype=torch.int32, device=H1.device)}
+    for i in range(4095):
+        head.draft(H1, L1, t1, out=out)
+        if i % 1024 == 0:
+            log("single-row draft %d" % i)
+    torch.cuda.synchronize()
+    assert head.check_error() == 0
+    one, _ = gpu_draft(make_head(w, 1, dca.EXEC_PERSISTENT, fold=True), inp1.H, inp1.L_base, inp1.last_tok,
+                       want_logits=False, want_state=False)
+    assert np.array_equal(out["tokens"].cpu().numpy(), one["tokens"])
+    a, flags = gpu_draft(head, inp3.H, inp3.L_base, inp3.last_tok)
+    assert flags == 0
+    b, _ = gpu_draft(make_head(w, 4, dca.EXEC_PERSISTENT, fold=True), inp3.H, inp3.L_base, inp3.last_tok)
+    for k in ("tokens", "L_final", "S", "u"):
+        assert np.array_equal(a[k], b[k]), k
+    o = oracle.draft(w, inp3.H, inp3.L_base, inp3.last_tok)
+    compare_free_running(o, a)

@@ -646,7 +646,9 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
     }
     {
         void *args[] = {&p};
-        HIP_TRY(hipLaunchKernel(hd->kern.prologue, dim3(g_pro), dim3(NT), args, sm_small, st), "launch prologue");
+        // with A_H from its own launch the prologue only covers the 3h rows of q_0 (and g_0)
+        const int g = ah_mfma ? (h3 + NWAVE - 1) / NWAVE : g_pro;
+        HIP_TRY(hipLaunchKernel(hd->kern.prologue, dim3(g), dim3(NT), args, sm_small, st), "launch prologue");
         int q = 0;
         void *sargs[] = {&p, &q};
         HIP_TRY(hipLaunchKernel(reinterpret_cast<const void *>(&k_step_update), dim3(g_upd), dim3(NT), sargs,

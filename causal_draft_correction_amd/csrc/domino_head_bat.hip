@@ -217,23 +217,87 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng)
         }
 }
 
+// Tile order for a launch of n one-tile blocks: blocks are dealt to the XCDs
+// round robin (block b runs on XCD b % XCDS), so block b takes tile
+// (b % XCDS) * (n / XCDS) + b / XCDS, giving each XCD a contiguous range of
+// tiles whose shared operand rows stay in its own L2.
+__device__ inline int xcd_tile(int b, int n) { return n % XCDS ? b : (b % XCDS) * (n / XCDS) + b / XCDS; }
+
+// Split-K matrix-core tile shared by the A_H and state launches: the block's
+// four waves take consecutive quarters of the K steps (32 wide) of one output
+// tile of NA x NB 16x16 blocks, each wave issuing the loads of up to KU steps
+// before its first product; wave 0 then adds the partial tiles in wave order.
+// ld(s, av, bv) loads step s's operands of this lane.  Returns true in wave 0,
+// whose acc holds the tile.
+template <int NA, int NB, int KU, typename Ld>
+__device__ __forceinline__ bool splitk_tile(int nst, Ld ld, f32x4_t (&acc)[NA][NB], f32x4_t *part)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int t = 0; t < NB; ++t)
+            acc[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int per = (nst + NWAVE - 1) / NWAVE;
+    const int s0 = wave * per, s1 = s0 + per < nst ? s0 + per : nst;
+    for (int sb = s0; sb < s1; sb += KU) {
+        uint4 av[KU][NA], bv[KU][NB];
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+            if (sb + u < s1)
+                ld(sb + u, av[u], bv[u]);
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+            if (sb + u < s1)
+#pragma unroll
+                for (int t = 0; t < NB; ++t)
+#pragma unroll
+                    for (int a = 0; a < NA; ++a)
+                        acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u][a]),
+                                                                           __builtin_bit_cast(bf16x8_t, bv[u][t]),
+                                                                           acc[a][t], 0, 0, 0);
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int t = 0; t < NB; ++t)
+                part[((wave - 1) * NA * NB + a * NB + t) * 64 + lane] = acc[a][t];
+    }
+    __syncthreads();
+    if (wave > 0)
+        return false;
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w)
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int t = 0; t < NB; ++t) {
+                const f32x4_t v = part[((w - 1) * NA * NB + a * NB + t) * 64 + lane];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[a][t][i] += v[i];
+            }
+    return true;
+}
+
 // State-phase dot products of the stepwise launches at larger B, on the matrix
 // cores (same quantities as phase_state):
 //   u_q[b][m]      = SiLU(A_H[b][q][m] + sum_k W1[m][d + k] S_q[b][k])   (m < r)
 //   q_{q+1}[b][m'] = sum_k W_hh[m'][k] S_q[b][k] + b_hh[m']             (m' = m - r)
 // A operand: S_q as bf16 hi + lo rows of 8 batch rows (planes written by the
 // update launch); B operand: 16 weight rows.  A block takes 32 batch rows and
-// 128 weight rows (32 per wave); the K loop runs over h in 32-wide steps.
-template <typename WT>
+// 32 weight rows (split-K over h).
+template <typename WT, int KU = 8>
 __global__ __launch_bounds__(NT) void k_state_mfma(Params p, int q)
 {
+    __shared__ f32x4_t part[(NWAVE - 1) * 4 * 2 * 64];
     const int h = p.h, r = p.r, R = r + 3 * p.h, B = p.B;
-    const int nbg = (B + 31) / 32;
-    const int bg = blockIdx.x % nbg, wb = blockIdx.x / nbg;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15;
-    const int mw = wb * 128 + wave * 32;  // first weight row of the wave
-    if (mw >= R)
-        return;
+    const int nbg = (B + 31) / 32, nwb = (R + 31) / 32;
+    const int tile = xcd_tile(blockIdx.x, nbg * nwb);
+    const int bg = tile % nbg, wb = tile / nbg;
+    const int lane = threadIdx.x & 63, col = lane & 15;
+    const int mw = wb * 32;  // first weight row of the block
     const int b0 = bg * 32;
     // operand sources of this lane
     const uint16_t *arow[4];
@@ -256,27 +320,20 @@ __global__ __launch_bounds__(NT) void k_state_mfma(Params p, int q)
         wrow[t] += (lane >> 4) * 8;
     }
     f32x4_t acc[4][2];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-            acc[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < h; k += 32) {
-        uint4 av[4], wv[2];
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-            av[a] = aok[a] ? *reinterpret_cast<const uint4 *>(arow[a] + k) : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-            wv[t] = wok[t] ? *reinterpret_cast<const uint4 *>(wrow[t] + k) : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
+    const bool lead = splitk_tile<4, 2, KU>(
+        h / 32,
+        [&](int s, uint4(&av)[4], uint4(&wv)[2]) {
+            const int k = s * 32;
 #pragma unroll
             for (int a = 0; a < 4; ++a)
-                acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[a]),
-                                                                   __builtin_bit_cast(bf16x8_t, wv[t]), acc[a][t], 0,
-                                                                   0, 0);
-    }
+                av[a] = aok[a] ? *reinterpret_cast<const uint4 *>(arow[a] + k) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                wv[t] = wok[t] ? *reinterpret_cast<const uint4 *>(wrow[t] + k) : make_uint4(0u, 0u, 0u, 0u);
+        },
+        acc, part);
+    if (!lead)
+        return;
     const int h3 = 3 * h;
     float *qn = q_slot(p, q + 1);
 #pragma unroll
@@ -309,19 +366,18 @@ __global__ __launch_bounds__(NT) void k_state_mfma(Params p, int q)
 
 // A_H = W1[:, :d] H for every position on the matrix cores (same quantity as
 // phase_ah): rows R = b * K + i of H (bf16, [B*K, d]) times rows m of W1's
-// first d columns; A_H[R][m] in fp32.  A wave takes 32 H rows x 32 W1 rows
-// (2 x 2 tiles of v_mfma_f32_16x16x32_bf16), the K loop runs over d.
-template <typename WT>
+// first d columns; A_H[R][m] in fp32.  A block takes 32 H rows x 32 W1 rows
+// (2 x 2 tiles of v_mfma_f32_16x16x32_bf16, split-K over d).
+template <typename WT, int KU = 8>
 __global__ __launch_bounds__(NT) void k_ah_mfma(Params p)
 {
+    __shared__ f32x4_t part[(NWAVE - 1) * 2 * 2 * 64];
     const int d = p.d, r = p.r, M = p.B * p.K;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15;
-    const int tiles_n = r / 32;
-    const int wt = blockIdx.x * NWAVE + wave;
-    const int tm = wt / tiles_n, tn = wt % tiles_n;
+    const int lane = threadIdx.x & 63, col = lane & 15;
+    const int tiles_n = r / 32, tiles_m = (M + 31) / 32;
+    const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+    const int tm = tile / tiles_n, tn = tile % tiles_n;
     const int R0 = tm * 32, m0 = tn * 32;
-    if (R0 >= M)
-        return;
     const bf16s *arow[2];
     bool aok[2];
 #pragma unroll
@@ -335,27 +391,20 @@ __global__ __launch_bounds__(NT) void k_ah_mfma(Params p)
     for (int t = 0; t < 2; ++t)
         wrow[t] = static_cast<const bf16s *>(p.W1) + static_cast<size_t>(m0 + t * 16 + col) * (d + p.h) + (lane >> 4) * 8;
     f32x4_t acc[2][2];
+    const bool lead = splitk_tile<2, 2, KU>(
+        d / 32,
+        [&](int s, uint4(&av)[2], uint4(&wv)[2]) {
+            const int k = s * 32;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-            acc[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < d; k += 32) {
-        uint4 av[2], wv[2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-            av[a] = aok[a] ? *reinterpret_cast<const uint4 *>(arow[a] + k) : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-            wv[t] = *reinterpret_cast<const uint4 *>(wrow[t] + k);
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
+            for (int a = 0; a < 2; ++a)
+                av[a] = aok[a] ? *reinterpret_cast<const uint4 *>(arow[a] + k) : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
-                acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[a]),
-                                                                   __builtin_bit_cast(bf16x8_t, wv[t]), acc[a][t], 0,
-                                                                   0, 0);
-    }
+                wv[t] = *reinterpret_cast<const uint4 *>(wrow[t] + k);
+        },
+        acc, part);
+    if (!lead)
+        return;
     // D: lane l holds H rows (l/16)*4 + i of the A tile, W1 row l%16 of the B tile
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -411,7 +460,7 @@ int w2_grid(int B, int cus)
 size_t w2_smem() { return 2 * sizeof(uint4) * (128 / 16) * BAT_KS * 64; }
 const void *state_kernel() { return reinterpret_cast<const void *>(&k_state_mfma<bf16s>); }
 const void *ah_kernel() { return reinterpret_cast<const void *>(&k_ah_mfma<bf16s>); }
-int ah_grid(int B, int K, int r) { return ((B * K + 31) / 32 * (r / 32) + NWAVE - 1) / NWAVE; }
-int state_grid(int B, int r, int h) { return ((B + 31) / 32) * ((r + 3 * h + 127) / 128); }
+int ah_grid(int B, int K, int r) { return (B * K + 31) / 32 * (r / 32); }
+int state_grid(int B, int r, int h) { return ((B + 31) / 32) * ((r + 3 * h + 31) / 32); }
 
 }  // namespace dhbat

@@ -314,6 +314,50 @@ def geometric_prefix_targets(draft: np.ndarray, key, V: int, mean: float = 7.0):
     return tgt, ks
 
 
+@dataclasses.dataclass
+class VerifyInputs:
+    draft: np.ndarray    # [B, K] int32
+    logits: np.ndarray   # [B, K+1, V] float32 target logits
+    planted: np.ndarray  # [B, K+1] int32 token planted on top of each logits row
+    k: np.ndarray        # [B] int32 planted accept length
+
+
+def make_verify_inputs(B: int, K: int, V: int, key, sigma: float = 3.0, peak_height: float = 6.0,
+                       mean: float = 7.0) -> VerifyInputs:
+    """Inputs of the greedy verify step for B drafted blocks of K tokens.
+
+    Row b (key + [b]): draft ~ Zipf(1.1) token ids from key+[b,0]; the target's
+    tokens come from ``geometric_prefix_targets`` (key+[1]): equal to the draft
+    for the first k_b positions (k_b ~ Geometric, mean ``mean``, truncated to K),
+    different at position k_b, uniform afterwards, plus a uniform token for row
+    K (key+[b,2]).  Each logits row is N(0, sigma^2) noise (key+[b,3]) with the
+    target's token set ``peak_height`` above the row's noise maximum, the same
+    planting as the base logits of the draft workloads.
+    """
+    draft = np.empty((B, K), np.int32)
+    for b in range(B):
+        draft[b] = _zipf_ids(_rng(list(key) + [b, 0]), K, V).astype(np.int32)
+    tgt, ks = geometric_prefix_targets(draft, list(key) + [1], V, mean)
+    planted = np.empty((B, K + 1), np.int32)
+    planted[:, :K] = tgt
+    logits = np.empty((B, K + 1, V), np.float32)
+
+    def one(b):
+        planted[b, K] = int(_rng(list(key) + [b, 2]).integers(0, V))
+        L = logits[b]
+        _rng(list(key) + [b, 3]).standard_normal(out=L, dtype=np.float32)
+        L *= np.float32(sigma)
+        top = L.max(axis=1)
+        L[np.arange(K + 1), planted[b]] = top + np.float32(peak_height)
+
+    if B == 1:
+        one(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(one, range(B)))
+    return VerifyInputs(draft, logits, planted, ks)
+
+
 def digest(*arrays) -> str:
     """Short content hash used by the determinism tests."""
     hsh = hashlib.sha256()

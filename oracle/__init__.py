@@ -6,9 +6,9 @@ library never calls it, and this package never loads the HIP library.
 
 Two independent implementations live here:
 
-* ``draft`` / ``accept_len`` / ``param_count``: the plain C oracle
+* ``draft`` / ``accept_len`` / ``verify`` / ``param_count``: the plain C oracle
   (domino_oracle.c), loops in double, called through ctypes;
 * ``oracle.numpy_ref``: a vectorised NumPy float64 rewrite used only to
   cross-check the C oracle on small shapes.
 """
-from .core import draft, accept_len, param_count, build, lib_path, max_threads  # noqa: F401
+from .core import draft, accept_len, verify, param_count, build, lib_path, max_threads  # noqa: F401

@@ -54,6 +54,8 @@ def _load():
         lib.oracle_draft_row.restype = ctypes.c_int
         lib.oracle_accept_len.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, P]
         lib.oracle_accept_len.restype = None
+        lib.oracle_verify.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
+        lib.oracle_verify.restype = None
         lib.oracle_param_count.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int32]
         lib.oracle_param_count.restype = ctypes.c_int64
         lib.oracle_max_threads.argtypes = []
@@ -137,6 +139,24 @@ def accept_len(draft_tokens, target_tokens) -> np.ndarray:
     out = np.empty(d.shape[0], np.int32)
     lib.oracle_accept_len(d.shape[0], d.shape[1], _ptr(d), _ptr(t), _ptr(out))
     return out
+
+
+def verify(logits, draft_tokens) -> dict:
+    """Greedy verify step: logits [B, K+1, V] float32, draft [B, K] int32.
+
+    Returns target [B, K+1], accept [B] and next [B] (int32), see oracle_verify.
+    """
+    lib = _load()
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    d = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    B, K = d.shape
+    assert lg.ndim == 3 and lg.shape[0] == B and lg.shape[1] == K + 1
+    V = lg.shape[2]
+    tgt = np.empty((B, K + 1), np.int32)
+    acc = np.empty(B, np.int32)
+    nxt = np.empty(B, np.int32)
+    lib.oracle_verify(B, K, V, _ptr(lg), _ptr(d), _ptr(tgt), _ptr(acc), _ptr(nxt))
+    return dict(target=tgt, accept=acc, next=nxt)
 
 
 def param_count(d: int, h: int, r: int, V: int, with_bias: bool = False) -> int:

@@ -233,6 +233,49 @@ void oracle_accept_len(int32_t B, int32_t K, const int32_t *draft, const int32_t
     }
 }
 
+/*
+ * Greedy verify step for one drafted block (paper.oopus.info review, section
+ * 一: the target model checks the whole draft in one parallel pass and keeps
+ * what it would have produced; researchpapers.dev summary, 关键结果 and
+ * 常见问题: every accepted token is exactly the target's own token).
+ *   logits [B, K+1, V] float32: row j scores the token that follows the
+ *          context plus draft[b][0..j-1] (row K follows the whole draft)
+ *   draft  [B, K] int32
+ * Outputs:
+ *   target [B, K+1] int32 (may be NULL): the target's greedy token of each
+ *          row, with the draft's argmax rules (beats(); lowest index on ties)
+ *   accept [B] int32: first j < K with draft[b][j] != target[b][j], else K
+ *   next   [B] int32: target[b][accept[b]], the token the target itself puts
+ *          after the accepted prefix (the anchor of the next block)
+ * Reading taken: the committed tokens of a step are the accepted prefix plus
+ * that one target token; the pages do not spell out the extra token, but it
+ * is the target's own greedy choice, so committing it keeps the output
+ * identical to plain greedy decoding by the target.
+ */
+void oracle_verify(int32_t B, int32_t K, int32_t V, const float *logits, const int32_t *draft, int32_t *target,
+                   int32_t *accept, int32_t *next)
+{
+    int32_t *t = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K + 1));
+    for (int32_t b = 0; b < B; ++b) {
+        for (int32_t j = 0; j <= K; ++j) {
+            const float *row = logits + ((size_t)b * (K + 1) + j) * (size_t)V;
+            int32_t best = 0;
+            for (int32_t v = 1; v < V; ++v)
+                if (beats(row[v], row[best]))
+                    best = v;
+            t[j] = best;
+            if (target)
+                target[(size_t)b * (K + 1) + j] = best;
+        }
+        int32_t a = 0;
+        while (a < K && draft[(size_t)b * K + a] == t[a])
+            ++a;
+        accept[b] = a;
+        next[b] = t[a];
+    }
+    free(t);
+}
+
 /* Head parameters: W1 [r, d+h], W2 [V, r], W_ih [3h, d], W_hh [3h, h] (+ 2 x 3h GRU biases). */
 int64_t oracle_param_count(int64_t d, int64_t h, int64_t r, int64_t V, int32_t with_bias)
 {

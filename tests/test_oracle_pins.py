@@ -352,3 +352,81 @@ def test_thread_count_does_not_change_results():
     b = oracle.draft(w, inp.H, inp.L_base, inp.last_tok, threads=7)
     for k in ("tokens", "L_final", "S", "u", "gap"):
         np.testing.assert_array_equal(a[k], b[k])
+
+
+# ---- greedy verify step (review section 一; summary, 关键结果 and 常见问题) ----
+
+def test_V1_verify_target_tokens_are_numpy_argmax():
+    """The target's greedy token of each row equals numpy.argmax on the float32
+    logits, including planted ties (lowest index), NaN (the first NaN), a row
+    of +-0, a row of -inf and the last index."""
+    g = np.random.default_rng(7)
+    B, K, V = 3, 5, 29
+    lg = (g.standard_normal((B, K + 1, V)) * 3).astype(np.float32)
+    lg[0, 0, [4, 9, 20]] = 50.0                  # exact tie: 4 wins
+    lg[0, 1, 11] = np.nan
+    lg[0, 1, 3] = np.nan                         # first NaN: 3
+    lg[0, 2] = 0.0
+    lg[0, 2, :7] = -0.0                          # -0 == +0: index 0
+    lg[1, 0] = -np.inf                           # all -inf: index 0
+    lg[1, 1, V - 1] = 99.0                       # last index
+    lg[2, 3, 0] = np.inf
+    lg[2, 3, 5] = np.inf                         # +inf tie: 0
+    draft = g.integers(0, V, size=(B, K)).astype(np.int32)
+    r = oracle.verify(lg, draft)
+    assert np.array_equal(r["target"], np.argmax(lg, axis=-1).astype(np.int32))
+
+
+def test_V2_verify_accept_and_next_on_constructed_blocks():
+    """Planted target tokens (generator construction, not the oracle): the accept
+    length equals the constructed k (target equals the draft on the first k
+    positions and differs at k), and the committed token is the planted token of
+    row k -- the target's own choice after the accepted prefix."""
+    vi = ds.make_verify_inputs(24, 16, 997, (21, 0))
+    r = oracle.verify(vi.logits, vi.draft)
+    assert np.array_equal(r["target"], vi.planted)
+    assert np.array_equal(r["accept"], np.minimum(vi.k, 16))
+    assert np.array_equal(r["next"], vi.planted[np.arange(24), vi.k])
+    assert (vi.k == 16).any() and (vi.k == 0).any()  # both ends of the range occur
+    # all drafts accepted: the committed token is the argmax of the extra row K
+    full = oracle.verify(vi.logits, vi.planted[:, :16])
+    assert np.array_equal(full["accept"], np.full(24, 16))
+    assert np.array_equal(full["next"], vi.planted[:, 16])
+
+
+def test_V3_speculative_loop_reproduces_greedy_decoding():
+    """Lossless property stated by the pages (summary, 关键结果 and 常见问题:
+    every accepted token is the target's own): with a toy greedy target whose
+    logits depend on the last two tokens, drafting noisy guesses, verifying them
+    and committing accept + the verify token reproduces plain greedy decoding
+    token for token, whatever the guesses."""
+    V, K, N = 11, 5, 60
+    g = np.random.default_rng(3)
+    table = g.standard_normal((V, V, V)).astype(np.float32)
+
+    def logits_after(seq):
+        return table[seq[-2], seq[-1]]
+
+    ref = [1, 2]
+    while len(ref) < 2 + N:
+        ref.append(int(np.argmax(logits_after(ref))))
+    for p_wrong in (0.0, 0.3, 1.0):
+        seq = [1, 2]
+        steps = 0
+        while len(seq) < 2 + N:
+            # guesses: the true continuation, each token corrupted with probability p_wrong
+            guess, ctx = [], list(seq)
+            for _ in range(K):
+                t = int(np.argmax(logits_after(ctx)))
+                if g.random() < p_wrong:
+                    t = (t + 1 + int(g.integers(0, V - 1))) % V
+                guess.append(t)
+                ctx.append(t)
+            rows = np.stack([logits_after(seq + guess[:j]) for j in range(K + 1)])[None]
+            r = oracle.verify(rows, np.asarray([guess], np.int32))
+            a = int(r["accept"][0])
+            seq += guess[:a] + [int(r["next"][0])]
+            steps += 1
+        assert seq[:2 + N] == ref, "p_wrong=%g" % p_wrong
+        if p_wrong == 0.0:
+            assert steps == -(-N // (K + 1))  # every step commits K + 1 tokens

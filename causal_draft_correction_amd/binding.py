@@ -30,8 +30,8 @@ FLAG_SYNC_TIMEOUT = 2
 ERRORS = {-1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP", -5: "EDEVICE"}
 
 SYMBOLS = ("domino_head_workspace_size", "domino_head_create", "domino_head_draft", "domino_accept_len",
-           "domino_head_check_error", "domino_head_exec_info", "domino_head_param_count", "domino_head_destroy",
-           "domino_last_error")
+           "domino_verify_workspace_size", "domino_verify", "domino_head_check_error", "domino_head_exec_info",
+           "domino_head_param_count", "domino_head_destroy", "domino_last_error")
 
 
 class DominoError(RuntimeError):
@@ -65,6 +65,8 @@ def load_library(path: str = LIB_PATH):
     lib.domino_head_create.argtypes = [ctypes.POINTER(Config), P, ctypes.c_size_t, ctypes.POINTER(P)]
     lib.domino_head_draft.argtypes = [P, I32, P, P, P, P, P, P, P, P, P, P]
     lib.domino_accept_len.argtypes = [I32, I32, P, P, P, P]
+    lib.domino_verify_workspace_size.argtypes = [I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.domino_verify.argtypes = [I32, I32, I32, P, P, P, ctypes.c_size_t, P, P, P, P]
     lib.domino_head_check_error.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
     PI = ctypes.POINTER(ctypes.c_int32)
     lib.domino_head_exec_info.argtypes = [P, I32, PI, PI, PI]
@@ -221,4 +223,42 @@ def accept_len(draft: torch.Tensor, target: torch.Tensor, out: Optional[torch.Te
         if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("accept_len takes contiguous CUDA int32 tensors")
     _check(load_library().domino_accept_len(B, K, _ptr(draft), _ptr(target), _ptr(out), _stream_handle()))
+    return out
+
+
+def verify_workspace_size(B: int, K: int, V: int) -> int:
+    """Bytes of device workspace `verify` needs for B blocks of K tokens over V (host only)."""
+    n = ctypes.c_size_t()
+    _check(load_library().domino_verify_workspace_size(B, K, V, ctypes.byref(n)))
+    return int(n.value)
+
+
+def verify(logits: torch.Tensor, draft: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+           want_target: bool = True, out: Optional[dict] = None) -> dict:
+    """Greedy verify step, asynchronous on the current stream.
+
+    logits [B, K+1, V] float32 and draft [B, K] int32 (contiguous CUDA tensors).  Returns
+    {"accept": [B], "next": [B]} (int32) and, with want_target, {"target": [B, K+1]}.
+    ``workspace`` (uint8, at least verify_workspace_size bytes) and ``out`` may be preallocated.
+    """
+    if logits.dim() != 3 or draft.dim() != 2 or logits.shape[0] != draft.shape[0] or \
+            logits.shape[1] != draft.shape[1] + 1:
+        raise ValueError("logits must be [B, K+1, V] and draft [B, K]")
+    B, K = draft.shape
+    V = logits.shape[2]
+    for name, t, dt in (("logits", logits, torch.float32), ("draft", draft, torch.int32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s: expected a contiguous CUDA %s tensor" % (name, dt))
+    dev = logits.device
+    need = verify_workspace_size(B, K, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    out = {} if out is None else dict(out)
+    out.setdefault("accept", torch.empty(B, dtype=torch.int32, device=dev))
+    out.setdefault("next", torch.empty(B, dtype=torch.int32, device=dev))
+    if want_target:
+        out.setdefault("target", torch.empty((B, K + 1), dtype=torch.int32, device=dev))
+    _check(load_library().domino_verify(B, K, V, _ptr(logits), _ptr(draft), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _ptr(out.get("target")),
+                                        _ptr(out["accept"]), _ptr(out["next"]), _stream_handle()))
     return out

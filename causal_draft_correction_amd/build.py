@@ -10,6 +10,7 @@ SRC_DIR = os.path.join(HERE, "csrc")
 MAIN_SRC = os.path.join(SRC_DIR, "domino_head.hip")
 RES_SRC = os.path.join(SRC_DIR, "domino_head_res.hip")
 BAT_SRC = os.path.join(SRC_DIR, "domino_head_bat.hip")
+VER_SRC = os.path.join(SRC_DIR, "domino_verify.hip")
 LIB = os.path.join(HERE, "libdomino_head.so")
 ARCH = "gfx950"
 
@@ -41,7 +42,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wall", "-Wno-unused-function", MAIN_SRC, RES_SRC, BAT_SRC, "-o", tmp]
+           "-Wall", "-Wno-unused-function", MAIN_SRC, RES_SRC, BAT_SRC, VER_SRC, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (res.stderr or "").splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:

@@ -21,6 +21,7 @@
 #include "dh_phases.h"
 #include "dh_resident.h"
 #include "dh_batched.h"
+#include "dh_verify.h"
 
 using namespace dh;
 
@@ -701,6 +702,52 @@ int domino_accept_len(int32_t B, int32_t K, const int32_t *draft, const int32_t 
     hipLaunchKernelGGL(k_accept_len, dim3((B + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), B, K,
                        draft, target, out_len);
     HIP_TRY(hipGetLastError(), "launch k_accept_len");
+    return DOMINO_OK;
+}
+
+static int verify_args(int32_t B, int32_t K, int32_t V)
+{
+    if (B < 0)
+        return fail(DOMINO_EINVAL, "B=%d < 0", B);
+    if (K < 1 || K > MAXK)
+        return fail(DOMINO_EINVAL, "K=%d outside [1, %d]", K, MAXK);
+    if (V < 1)
+        return fail(DOMINO_EINVAL, "V=%d < 1", V);
+    if (static_cast<long long>(B) * (K + 1) * dhverify::chunks(B, K, V) > 0x7FFFFFFFll)
+        return fail(DOMINO_EUNSUPPORTED, "B=%d too large for one launch", B);
+    return DOMINO_OK;
+}
+
+int domino_verify_workspace_size(int32_t B, int32_t K, int32_t V, size_t *bytes)
+{
+    const int rc = verify_args(B, K, V);
+    if (rc)
+        return rc;
+    if (!bytes)
+        return fail(DOMINO_EINVAL, "bytes is NULL");
+    *bytes = B ? dhverify::workspace_bytes(B, K, V) : 0;
+    return DOMINO_OK;
+}
+
+int domino_verify(int32_t B, int32_t K, int32_t V, const float *logits, const int32_t *draft, void *workspace,
+                  size_t workspace_bytes, int32_t *target, int32_t *accept, int32_t *next, void *stream)
+{
+    const int rc = verify_args(B, K, V);
+    if (rc)
+        return rc;
+    if (B == 0)
+        return DOMINO_OK;
+    if (!logits || !draft || !workspace || !accept || !next)
+        return fail(DOMINO_EINVAL, "NULL pointer");
+    if (!aligned16(logits) || !aligned16(draft) || !aligned16(workspace) || !aligned16(accept) ||
+        !aligned16(next) || (target && !aligned16(target)))
+        return fail(DOMINO_EINVAL, "pointers must be 16-byte aligned");
+    const size_t need = dhverify::workspace_bytes(B, K, V);
+    if (workspace_bytes < need)
+        return fail(DOMINO_EWORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    HIP_TRY(dhverify::launch(B, K, V, logits, draft, static_cast<uint64_t *>(workspace), target, accept, next,
+                             static_cast<hipStream_t>(stream)),
+            "launch verify");
     return DOMINO_OK;
 }
 

@@ -1,0 +1,147 @@
+// Greedy verify step of speculative decoding on the device.
+//
+// The target model checks a whole drafted block in one parallel pass and keeps
+// what it would have produced itself (paper.oopus.info review, section 一);
+// every accepted token is the target's own (researchpapers.dev summary, 关键结果
+// and 常见问题).  For B drafted blocks of K tokens and the target's logits rows
+// [B, K+1, V] (row j scores the token after the context plus the first j draft
+// tokens; row K follows the whole draft):
+//     target[b][j] = argmax_v logits[b][j][v]     (lowest index on ties, a NaN
+//                                                  above every number, -0 == +0)
+//     accept[b]    = first j < K with draft[b][j] != target[b][j], else K
+//     next[b]      = target[b][accept[b]]          (committed after the prefix)
+//
+// The argmax reads 4 V bytes per row once, so it is bound by HBM bandwidth.
+// k_verify_rows splits each row into `nch` chunks, one 256-thread block per
+// (row, chunk) so that even B = 1 fills the chip, keeps eight 16-byte
+// non-temporal loads per thread in flight and writes one packed key per block
+// to the workspace (nothing to clear: every key slot is written).
+// k_verify_final reduces the keys of one batch row in one wave.
+#define DH_NT 256
+#define DH_NS dhv
+#include "dh_common.h"
+#include "dh_verify.h"
+
+namespace DH_NS {
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+constexpr int VF_UNROLL = 8;          // 16-byte loads per thread in flight
+constexpr int VF_MIN_CHUNK = 4096;    // floats per block at least (16 KiB)
+constexpr int VF_TARGET_BLOCKS = 2048;
+
+__global__ __launch_bounds__(NT) void k_verify_rows(const float *logits, int V, int nch, int chunk, uint64_t *keys)
+{
+    __shared__ uint64_t red[NWAVE];
+    const int row = blockIdx.x / nch, c = blockIdx.x % nch;
+    const int v0 = c * chunk, v1 = v0 + chunk < V ? v0 + chunk : V;
+    const float *src = logits + static_cast<size_t>(row) * V;
+    uint64_t best = 0;
+    if ((V & 3) == 0) {
+        // rows are 16-byte aligned and chunk is a multiple of 4, so every load
+        // below lies inside [v0, v1)
+        constexpr int STEP = NT * 4;
+        for (int v = v0 + threadIdx.x * 4; v < v1; v += STEP * VF_UNROLL) {
+            f4v x[VF_UNROLL];
+#pragma unroll
+            for (int u = 0; u < VF_UNROLL; ++u)
+                if (v + u * STEP < v1)
+                    x[u] = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(src + v + u * STEP));
+#pragma unroll
+            for (int u = 0; u < VF_UNROLL; ++u)
+                if (v + u * STEP < v1) {
+                    const uint32_t i = static_cast<uint32_t>(v + u * STEP);
+                    best = max_u64(best, argmax_key(x[u].x, i));
+                    best = max_u64(best, argmax_key(x[u].y, i + 1));
+                    best = max_u64(best, argmax_key(x[u].z, i + 2));
+                    best = max_u64(best, argmax_key(x[u].w, i + 3));
+                }
+        }
+    } else {
+        for (int v = v0 + threadIdx.x; v < v1; v += NT)
+            best = max_u64(best, argmax_key(__builtin_nontemporal_load(src + v), static_cast<uint32_t>(v)));
+    }
+    best = wave_max_u64(best);
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t m = red[0];
+#pragma unroll
+        for (int w = 1; w < NWAVE; ++w)
+            m = max_u64(m, red[w]);
+        keys[blockIdx.x] = m;  // 0 only for a chunk past the end of the row
+    }
+}
+
+// One wave per batch row: the K+1 target tokens, the accepted prefix and the
+// token committed after it.
+__global__ __launch_bounds__(NT) void k_verify_final(int B, int K, int nch, const uint64_t *keys,
+                                                     const int32_t *draft, int32_t *target, int32_t *accept,
+                                                     int32_t *next)
+{
+    const int lane = threadIdx.x & 63;
+    const int b = blockIdx.x * NWAVE + (threadIdx.x >> 6);
+    if (b >= B)
+        return;
+    int a = -1, nt = 0;
+    for (int j = 0; j <= K; ++j) {
+        const uint64_t *kr = keys + (static_cast<size_t>(b) * (K + 1) + j) * nch;
+        uint64_t m = 0;
+        for (int c = lane; c < nch; c += 64)
+            m = max_u64(m, kr[c]);
+        m = wave_max_u64(m);
+        m = __shfl(m, 0);  // lane 0 holds the wave's max
+        const int t = static_cast<int>(key_index(m));
+        if (lane == 0 && target)
+            target[static_cast<size_t>(b) * (K + 1) + j] = t;
+        // the first position whose draft token differs from the target's (or K)
+        if (a < 0 && (j == K || draft[static_cast<size_t>(b) * K + j] != t)) {
+            a = j;
+            nt = t;
+        }
+    }
+    if (lane == 0) {
+        accept[b] = a;
+        next[b] = nt;
+    }
+}
+
+}  // namespace DH_NS
+
+namespace dhverify {
+
+using namespace dhv;
+
+int chunks(int B, int K, int V)
+{
+    const long long rows = static_cast<long long>(B) * (K + 1);
+    long long n = (VF_TARGET_BLOCKS + rows - 1) / (rows > 0 ? rows : 1);
+    const long long cap = V / VF_MIN_CHUNK > 1 ? V / VF_MIN_CHUNK : 1;
+    if (n > cap)
+        n = cap;
+    return n < 1 ? 1 : static_cast<int>(n);
+}
+
+size_t workspace_bytes(int B, int K, int V)
+{
+    return sizeof(uint64_t) * static_cast<size_t>(B) * (K + 1) * chunks(B, K, V);
+}
+
+hipError_t launch(int B, int K, int V, const float *logits, const int32_t *draft, uint64_t *keys, int32_t *target,
+                  int32_t *accept, int32_t *next, hipStream_t st)
+{
+    const int nch = chunks(B, K, V);
+    int chunk = (V + nch - 1) / nch;
+    chunk = (chunk + 3) & ~3;
+    const unsigned grid = static_cast<unsigned>(static_cast<size_t>(B) * (K + 1) * nch);
+    hipLaunchKernelGGL(k_verify_rows, dim3(grid), dim3(NT), 0, st, logits, V, nch, chunk, keys);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_verify_final, dim3((B + NWAVE - 1) / NWAVE), dim3(NT), 0, st, B, K, nch,
+                       static_cast<const uint64_t *>(keys), draft, target, accept, next);
+    return hipGetLastError();
+}
+
+}  // namespace dhverify

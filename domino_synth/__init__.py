@@ -291,7 +291,7 @@ def geometric_prefix_targets(draft: np.ndarray, key, V: int, mean: float = 7.0):
     """Synthetic verifier tokens for accept-length tests.
 
     For row b, k_b ~ Geometric on {0,1,...} with mean ``mean`` (p = 1/(mean+1)),
-    truncated to K.  target[b, :k] = draft[b, :k]; if k < K, target[b, k] is a
+    truncated to K (K when V = 1).  target[b, :k] = draft[b, :k]; if k < K, target[b, k] is a
     uniform token redrawn until it differs from draft[b, k]; positions after k
     are uniform.  Returns (target [B,K] int32, k [B] int32).
     """
@@ -303,7 +303,7 @@ def geometric_prefix_targets(draft: np.ndarray, key, V: int, mean: float = 7.0):
     for b in range(B):
         g = _rng(list(key) + [b])
         k = int(g.geometric(p)) - 1  # numpy's geometric has support {1,2,...}
-        k = min(k, K)
+        k = min(k, K) if V > 1 else K  # with one token id no position can differ
         row = g.integers(0, V, size=K).astype(np.int32)
         row[:k] = draft[b, :k]
         if k < K:

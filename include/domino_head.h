@@ -144,6 +144,37 @@ int domino_accept_len(int32_t B, int32_t K, const int32_t *draft, const int32_t 
                       void *stream);
 
 /*
+ * Greedy verify step of speculative decoding (paper.oopus.info review, section
+ * 一: the target model checks the whole drafted block in one parallel pass and
+ * keeps what it would have produced itself; researchpapers.dev summary, 关键结果
+ * and 常见问题: every accepted token is the target's own).  Device pointers:
+ *   logits   [B, K+1, V] float32  target logits; row j scores the token after
+ *                                 the context plus draft[b][0..j-1], row K
+ *                                 follows the whole draft
+ *   draft    [B, K] int32         the drafted block (e.g. domino_head_draft's
+ *                                 tokens; -1 entries simply never match)
+ *   workspace                     >= domino_verify_workspace_size(B, K, V) bytes,
+ *                                 scratch for this call (contents need no
+ *                                 initialisation and are not read afterwards)
+ * Outputs (device):
+ *   target   [B, K+1] int32       NULL = not stored; argmax of each row, with
+ *                                 the draft's rules (lowest index on ties, a
+ *                                 NaN above every number, -0 == +0)
+ *   accept   [B] int32            first j < K with draft[b][j] != target[b][j],
+ *                                 else K
+ *   next     [B] int32            target[b][accept[b]]: the target's token after
+ *                                 the accepted prefix; the step commits
+ *                                 draft[b][0..accept-1] and then this token,
+ *                                 which is the next block's last_tok
+ * 0 <= B; 1 <= K <= 16; V >= 1.  B = 0 is a no-op.  All pointers 16-byte
+ * aligned; outputs may not alias inputs or the workspace.  Two kernel launches,
+ * asynchronous on `stream`; no allocation, no synchronization.
+ */
+int domino_verify_workspace_size(int32_t B, int32_t K, int32_t V, size_t *bytes);
+int domino_verify(int32_t B, int32_t K, int32_t V, const float *logits, const int32_t *draft, void *workspace,
+                  size_t workspace_bytes, int32_t *target, int32_t *accept, int32_t *next, void *stream);
+
+/*
  * Synchronizes the stream of the handle's last draft, reads and clears the
  * device flags (DOMINO_FLAG_*) into *device_flags (may be NULL) and resets
  * the handle's barrier state.  Returns DOMINO_EDEVICE if any flag was set.

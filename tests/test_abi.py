@@ -124,3 +124,25 @@ def test_binding_refuses_to_run_without_the_library(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         binding.load_library(str(tmp_path / "missing.so"))
+
+
+def test_verify_workspace_size_and_host_validation():
+    lib = dca.load_library()
+    n = ctypes.c_size_t()
+    assert lib.domino_verify_workspace_size(32, 16, 151936, ctypes.byref(n)) == 0
+    assert n.value > 0 and n.value % 8 == 0
+    assert lib.domino_verify_workspace_size(0, 16, 151936, ctypes.byref(n)) == 0 and n.value == 0
+    assert dca.verify_workspace_size(1, 16, 151936) >= 17 * 8  # one key per target row at least
+    assert lib.domino_verify_workspace_size(-1, 16, 100, ctypes.byref(n)) == -1
+    assert lib.domino_verify_workspace_size(1, 0, 100, ctypes.byref(n)) == -1
+    assert lib.domino_verify_workspace_size(1, 17, 100, ctypes.byref(n)) == -1
+    assert lib.domino_verify_workspace_size(1, 4, 0, ctypes.byref(n)) == -1
+    assert lib.domino_verify_workspace_size(1, 4, 100, None) == -1
+    # host-side checks come before any device work
+    assert lib.domino_verify(0, 16, 100, None, None, None, 0, None, None, None, None) == 0  # B = 0: no-op
+    assert lib.domino_verify(1, 16, 100, None, 16, 32, 1024, None, 48, 64, None) == -1     # NULL logits
+    assert lib.domino_verify(1, 16, 100, 16, 32, 48, 1024, None, 64, None, None) == -1     # NULL next
+    assert lib.domino_verify(1, 16, 100, 18, 32, 48, 1024, None, 64, 80, None) == -1       # misaligned
+    need = dca.verify_workspace_size(2, 16, 100)
+    assert lib.domino_verify(2, 16, 100, 16, 32, 48, need - 8, None, 64, 80, None) == -3   # small workspace
+    assert b"workspace" in lib.domino_last_error()

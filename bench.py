@@ -103,6 +103,103 @@ def cpu_baseline(w, inp, budget_s):
     return n, el, oracle.max_threads()
 
 
+def run_verify(args, wl):
+    """The greedy verify step on the workload's B, K and V: target logits [B, K+1, V] and the
+    drafted tokens [B, K] resident on the device, one domino_verify call per step."""
+    import numpy as np
+    import torch
+
+    import causal_draft_correction_amd as dca
+    import domino_synth as ds
+
+    sh = wl.shape
+    B, K, V = wl.B, sh.K, sh.V
+    eprint("bench: generating verify inputs (B=%d, K=%d, V=%d)" % (B, K, V))
+    vi = ds.make_verify_inputs(B, K, V, list(wl.row_key) + [7])
+    lg = dca.device_tensor(vi.logits)
+    dr = dca.device_tensor(vi.draft)
+    ws = torch.empty(max(dca.verify_workspace_size(B, K, V), 16), dtype=torch.uint8, device="cuda")
+    if args.calibrate_copy:
+        src = torch.ones(args.calibrate_copy * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
+    out = {"accept": torch.empty(B, dtype=torch.int32, device="cuda"),
+           "next": torch.empty(B, dtype=torch.int32, device="cuda"),
+           "target": torch.empty((B, K + 1), dtype=torch.int32, device="cuda")}
+    for _ in range(args.warmup):
+        dca.verify(lg, dr, ws, out=out)
+    torch.cuda.synchronize()
+    # the planted construction fixes the accept lengths
+    assert np.array_equal(out["accept"].cpu().numpy(), np.minimum(vi.k, K))
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        dca.verify(lg, dr, ws, out=out)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_ms = float(np.mean(per_call_ms))
+    cold_us = None
+    if args.cold_calls > 0:
+        evict = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.cold_calls)]
+        for i in range(args.cold_calls):
+            evict.fill_(float(i))
+            cev[i][0].record(stream)
+            dca.verify(lg, dr, ws, out=out)
+            cev[i][1].record(stream)
+        torch.cuda.synchronize()
+        cold_us = float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e3
+        del evict
+    # algorithmic bytes: every logit once, the draft, the outputs
+    total_bytes = B * (K + 1) * V * 4 + B * K * 4 + B * (K + 1) * 4 + 2 * B * 4
+    achieved = total_bytes / (avg_ms * 1e-3) / 1e9
+    name = "verify_" + wl.name
+    traffic = measured_traffic(name, "verify", False, False)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = min(B, 4)
+        n = 0
+        t1 = time.perf_counter()
+        while True:
+            oracle.verify(vi.logits[:rows], vi.draft[:rows])
+            n += rows
+            el = time.perf_counter() - t1
+            if el >= min(args.cpu_budget, 5.0):
+                break
+        cpu = {"value": n / el, "unit": "blocks/s", "cores": 1, "kind": "oracle",
+               "sample": "%d verify steps of %d-row slices of the same inputs (K=%d, V=%d), C oracle, one thread" % (
+                   n // rows, rows, K, V)}
+    rec = {
+        "metric": "greedy verify: drafted blocks checked per second (K+1 target rows of V logits each) at 1 GPU",
+        "value": B * args.steps / wall,
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "B": B, "K": K, "V": V, "call_avg_us": avg_ms * 1e3,
+                   "warm_us_per_call_median": float(np.median(per_call_ms)) * 1e3,
+                   "cold_us_per_call_median": cold_us},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic, "algorithmic_bytes": total_bytes,
+                     "kernel": "k_verify_rows + k_verify_final"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +217,8 @@ def main():
                     help="do not precompute the folded input-gate table (GRU input GEMV every step)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--verify", action="store_true",
+                    help="time the greedy verify step (domino_verify) on the workload's B, K and V instead")
     ap.add_argument("--cold-calls", type=int, default=20,
                     help="calls timed one by one after writing a 512 MiB buffer that evicts the caches "
                          "(the serving case: the target model's verify pass runs between two drafts)")
@@ -140,6 +239,9 @@ def main():
 
     torch.cuda.set_device(0)
     wl = ds.WORKLOADS[args.workload]
+    if args.verify:
+        run_verify(args, wl)
+        return
     sh = wl.shape
     eprint("bench: generating %s (B=%d, d=%d, h=%d, r=%d, V=%d, %s)" % (wl.name, wl.B, sh.d, sh.h, sh.r, sh.V,
                                                                       sh.wdtype))

@@ -16,7 +16,7 @@
 // (row, chunk) so that even B = 1 fills the chip, keeps eight 16-byte
 // non-temporal loads per thread in flight and writes one packed key per block
 // to the workspace (nothing to clear: every key slot is written).
-// k_verify_final reduces the keys of one batch row in one wave.
+// k_verify_final reduces the keys of one batch row in one block.
 #define DH_NT 256
 #define DH_NS dhv
 #include "dh_common.h"
@@ -74,33 +74,32 @@ __global__ __launch_bounds__(NT) void k_verify_rows(const float *logits, int V, 
     }
 }
 
-// One wave per batch row: the K+1 target tokens, the accepted prefix and the
-// token committed after it.
-__global__ __launch_bounds__(NT) void k_verify_final(int B, int K, int nch, const uint64_t *keys,
-                                                     const int32_t *draft, int32_t *target, int32_t *accept,
-                                                     int32_t *next)
+// One block per batch row: every thread loads its share of the row's (K+1) nch
+// keys at once and folds them into the K+1 LDS slots; then lane j of wave 0
+// takes row j's token, and one ballot finds the first draft token that differs.
+__global__ __launch_bounds__(NT) void k_verify_final(int K, int nch, const uint64_t *keys, const int32_t *draft,
+                                                     int32_t *target, int32_t *accept, int32_t *next)
 {
-    const int lane = threadIdx.x & 63;
-    const int b = blockIdx.x * NWAVE + (threadIdx.x >> 6);
-    if (b >= B)
+    __shared__ unsigned long long best[MAXK + 1];
+    const int b = blockIdx.x, lane = threadIdx.x & 63;
+    const int n = (K + 1) * nch;
+    const uint64_t *kb = keys + static_cast<size_t>(b) * n;
+    // the draft tokens go out with the key loads
+    const int dj = (threadIdx.x < K) ? draft[static_cast<size_t>(b) * K + threadIdx.x] : 0;
+    if (threadIdx.x <= K)
+        best[threadIdx.x] = 0ull;
+    __syncthreads();
+    for (int e = threadIdx.x; e < n; e += NT)
+        atomicMax(&best[e / nch], static_cast<unsigned long long>(kb[e]));
+    __syncthreads();
+    if (threadIdx.x >= 64)
         return;
-    int a = -1, nt = 0;
-    for (int j = 0; j <= K; ++j) {
-        const uint64_t *kr = keys + (static_cast<size_t>(b) * (K + 1) + j) * nch;
-        uint64_t m = 0;
-        for (int c = lane; c < nch; c += 64)
-            m = max_u64(m, kr[c]);
-        m = wave_max_u64(m);
-        m = __shfl(m, 0);  // lane 0 holds the wave's max
-        const int t = static_cast<int>(key_index(m));
-        if (lane == 0 && target)
-            target[static_cast<size_t>(b) * (K + 1) + j] = t;
-        // the first position whose draft token differs from the target's (or K)
-        if (a < 0 && (j == K || draft[static_cast<size_t>(b) * K + j] != t)) {
-            a = j;
-            nt = t;
-        }
-    }
+    const int t = lane <= K ? static_cast<int>(key_index(best[lane])) : 0;
+    if (target && lane <= K)
+        target[static_cast<size_t>(b) * (K + 1) + lane] = t;
+    const uint64_t differ = __ballot(lane < K && dj != t);
+    const int a = differ ? __ffsll(static_cast<unsigned long long>(differ)) - 1 : K;
+    const int nt = __shfl(t, a);
     if (lane == 0) {
         accept[b] = a;
         next[b] = nt;
@@ -139,8 +138,8 @@ hipError_t launch(int B, int K, int V, const float *logits, const int32_t *draft
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(k_verify_final, dim3((B + NWAVE - 1) / NWAVE), dim3(NT), 0, st, B, K, nch,
-                       static_cast<const uint64_t *>(keys), draft, target, accept, next);
+    hipLaunchKernelGGL(k_verify_final, dim3(B), dim3(NT), 0, st, K, nch, static_cast<const uint64_t *>(keys), draft,
+                       target, accept, next);
     return hipGetLastError();
 }
 

@@ -217,6 +217,10 @@ def main():
                     help="do not precompute the folded input-gate table (GRU input GEMV every step)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--teacher", action="store_true",
+                    help="teacher-forced drafting: a seeded uniform teacher token row per batch row")
+    ap.add_argument("--position-batched", action="store_true",
+                    help="with --teacher: the GRU chain first, then one W2 launch for all positions (B <= 8 too)")
     ap.add_argument("--verify", action="store_true",
                     help="time the greedy verify step (domino_verify) on the workload's B, K and V instead")
     ap.add_argument("--cold-calls", type=int, default=20,
@@ -251,17 +255,22 @@ def main():
     t_create = time.perf_counter()
     head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B,
                           exec_mode=mode | (dca.EXEC_STREAM_W2 if args.stream_w2 else 0) |
-                          (dca.EXEC_PLAIN_LAUNCH if args.plain_launch else 0), fold_embedding=fold)
+                          (dca.EXEC_PLAIN_LAUNCH if args.plain_launch else 0) |
+                          (dca.EXEC_POSITION_BATCHED if args.position_batched else 0), fold_embedding=fold)
     torch.cuda.synchronize()
     t_create = time.perf_counter() - t_create
     H = dca.device_tensor(inp.H)
     L = dca.device_tensor(inp.L_base)
     lt = dca.device_tensor(inp.last_tok)
+    teacher = dca.device_tensor(ds.uniform_tokens(list(wl.row_key) + [9], (wl.B, sh.K), sh.V)) if args.teacher else None
     out = {"tokens": torch.empty((wl.B, sh.K), dtype=torch.int32, device="cuda")}
     if args.store_logits:
         out["L_final"] = torch.empty((wl.B, sh.K, sh.V), dtype=torch.float32, device="cuda")
     info = head.exec_info(wl.B)
     exec_name = "persistent" if info["persistent"] else "stepwise"
+    if args.teacher and (args.position_batched or not info["persistent"]):
+        info = dict(info, persistent=False, w2_resident=False)
+        exec_name = "stepwise, position-batched"
 
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20) // 4
@@ -273,7 +282,7 @@ def main():
         del src, dst
 
     for _ in range(args.warmup):
-        head.draft(H, L, lt, out=out)
+        head.draft(H, L, lt, teacher=teacher, out=out)
     torch.cuda.synchronize()
     assert head.check_error() == 0
     eprint("bench: warmup done, timing %d steps" % args.steps)
@@ -284,7 +293,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        head.draft(H, L, lt, out=out)
+        head.draft(H, L, lt, teacher=teacher, out=out)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -303,7 +312,7 @@ def main():
         for i in range(args.cold_calls):
             evict.fill_(float(i))
             cev[i][0].record(stream)
-            head.draft(H, L, lt, out=out)
+            head.draft(H, L, lt, teacher=teacher, out=out)
             cev[i][1].record(stream)
         torch.cuda.synchronize()
         assert head.check_error() == 0
@@ -353,6 +362,7 @@ def main():
                    "weights": sh.wdtype, "exec": exec_name, "store_logits": bool(args.store_logits),
                    "fold_embedding": fold, "w2_on_chip": w2_on_chip,
                    "launch": "plain" if args.plain_launch else "cooperative", "create_s": t_create,
+                   "teacher_forced": bool(args.teacher),
                    "kernel_avg_us": avg_ms * 1e3, "warm_us_per_call_median": float(np.median(per_call_ms)) * 1e3,
                    "cold_us_per_call_median": cold_us, "w2_lbase_GBps": w2l,
                    "w2_lbase_frac_of_hbm_peak": w2l / HBM_PEAK_GBPS, "matrix_core_use": mfma},

@@ -24,6 +24,7 @@ EXEC_STEPWISE = 2
 FOLD_EMBED = 4
 EXEC_STREAM_W2 = 8
 EXEC_PLAIN_LAUNCH = 16
+EXEC_POSITION_BATCHED = 32
 FLAG_BAD_TOKEN = 1
 FLAG_SYNC_TIMEOUT = 2
 

@@ -197,6 +197,29 @@ __global__ __launch_bounds__(NT) void k_step_final(Params p)
     write_tokens(p, p.K - 1);
 }
 
+// Position-batched launches: zero the partial keys of the one W2 launch over
+// n = B K rows, whose slots are keys[g * n + row].
+__global__ __launch_bounds__(NT) void k_keys_zero(uint64_t *keys, int n)
+{
+    for (int i = blockIdx.x * NT + threadIdx.x; i < n; i += gridDim.x * NT)
+        keys[i] = 0ull;
+}
+
+// Position-batched launches: tokens[b][pos] from the partial keys of row
+// b K + pos (p is the call's own Params: B rows, K positions).
+__global__ __launch_bounds__(NT) void k_rows_tokens(Params p)
+{
+    const int n = p.B * p.K;
+    for (int i = blockIdx.x * NT + threadIdx.x; i < n; i += gridDim.x * NT) {
+        uint64_t best = 0;
+        for (int g = 0; g < NG; ++g) {
+            const uint64_t k = ld_agent_u64(p.keys + static_cast<size_t>(g) * n + i);
+            best = k > best ? k : best;
+        }
+        p.tokens[i] = row_bad(p, i / p.K) ? -1 : (best ? static_cast<int>(key_index(best)) : 0);
+    }
+}
+
 // Verify-side accept length: one thread per row.
 __global__ __launch_bounds__(256) void k_accept_len(int B, int K, const int *__restrict__ draft,
                                                     const int *__restrict__ target, int *__restrict__ out)
@@ -249,7 +272,7 @@ constexpr int W2_STEP_ROWS = 128;  // vocabulary rows per block in stepwise W2 l
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, utag, s_hl, q_buf, g_buf, P, total;
+    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, u_all, utag, s_hl, q_buf, g_buf, P, total;
 };
 
 Layout layout_of(const domino_head_config &c)
@@ -270,6 +293,8 @@ Layout layout_of(const domino_head_config &c)
     off = align_up(off + sizeof(float) * 2 * static_cast<size_t>(c.max_batch) * c.h);
     L.u_buf = off;
     off = align_up(off + sizeof(float) * static_cast<size_t>(c.max_batch) * c.r);
+    L.u_all = off;  // u of every position for the position-batched W2 launch
+    off = align_up(off + sizeof(float) * static_cast<size_t>(c.max_batch) * c.K * c.r);
     L.utag = off;
     off = align_up(off + sizeof(uint32_t) * 2 * static_cast<size_t>(c.max_batch) * c.r);
     L.s_hl = off;
@@ -315,7 +340,7 @@ int validate_config(const domino_head_config *c)
             return fail(DOMINO_EINVAL, "%s is not 16-byte aligned", names[i]);
     }
     if (c->flags & ~(DOMINO_EXEC_PERSISTENT | DOMINO_EXEC_STEPWISE | DOMINO_FOLD_EMBED | DOMINO_EXEC_STREAM_W2 |
-                     DOMINO_EXEC_PLAIN_LAUNCH))
+                     DOMINO_EXEC_PLAIN_LAUNCH | DOMINO_EXEC_POSITION_BATCHED))
         return fail(DOMINO_EINVAL, "unknown flags 0x%x", c->flags);
     if ((c->flags & DOMINO_EXEC_PERSISTENT) && (c->flags & DOMINO_EXEC_STEPWISE))
         return fail(DOMINO_EINVAL, "flags ask for both persistent and stepwise execution");
@@ -591,6 +616,8 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
     bool persistent, resident;
     if (!choose_launch(hd, B, &persistent, &resident))
         return fail(DOMINO_EUNSUPPORTED, "persistent launch needs B <= %d and one resident block per compute unit", BC);
+    if (teacher && (c.flags & DOMINO_EXEC_POSITION_BATCHED))
+        persistent = resident = false;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!hd->state_ready) {
         hipLaunchKernelGGL(k_clear_state, dim3(1), dim3(256), 0, st, reinterpret_cast<unsigned *>(hd->ws + hd->L.bar),
@@ -616,7 +643,13 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
             HIP_TRY(hipLaunchCooperativeKernel(fn, grid, block, args, smem, st), "hipLaunchCooperativeKernel(persistent)");
         return DOMINO_OK;
     }
-    // stepwise: prologue, update(0), state(0), then per position w2 [, g], update, state
+    // stepwise: prologue, update(0), state(0), then per position w2 [, g], update, state.
+    // With a teacher no state waits for an argmax: the chain runs first, writing u of
+    // every position (to the caller's u_out or the workspace), and the W2 products of
+    // all positions follow as one launch.
+    const bool pos_batched = teacher != nullptr;
+    if (pos_batched && !p.u_out)
+        p.u_out = reinterpret_cast<float *>(hd->ws + hd->L.u_all);
     const int h3 = 3 * c.h;
     const int g_pro = std::max(B * c.r, (h3 + NWAVE - 1) / NWAVE);
     const int g_rows = (c.r + h3 + NWAVE - 1) / NWAVE;
@@ -658,16 +691,18 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
     }
     // bf16 heads with r = 256 take the matrix-core W2 kernel
     const bool w2_mfma = c.wdtype == DOMINO_BF16 && c.r == dhbat::r_supported();
-    int w2_groups = w2_mfma ? dhbat::w2_groups(B) : 0;
-    for (int pos = 0; pos < c.K; ++pos) {
-        void *args[] = {&p, &pos};
-        void *margs[] = {&p, &pos, &w2_groups};
+    auto launch_w2 = [&](Params &pw, int rows, int pos) -> hipError_t {
+        int groups = w2_mfma ? dhbat::w2_groups(rows) : 0;
+        void *args[] = {&pw, &pos};
+        void *margs[] = {&pw, &pos, &groups};
         if (w2_mfma)
-            HIP_TRY(hipLaunchKernel(dhbat::w2_kernel(B), dim3(dhbat::w2_grid(B, hd->cus)), dim3(dhbat::w2_threads(B)),
-                                    margs, dhbat::w2_smem(), st),
-                    "launch w2 (matrix cores)");
-        else
-            HIP_TRY(hipLaunchKernel(hd->kern.w2, dim3(g_w2), dim3(NT), args, sm_w2, st), "launch w2");
+            return hipLaunchKernel(dhbat::w2_kernel(rows), dim3(dhbat::w2_grid(rows, hd->cus)),
+                                   dim3(dhbat::w2_threads(rows)), margs, dhbat::w2_smem(), st);
+        return hipLaunchKernel(hd->kern.w2, dim3(g_w2), dim3(NT), args, sm_w2, st);
+    };
+    for (int pos = 0; pos < c.K; ++pos) {
+        if (!pos_batched)
+            HIP_TRY(launch_w2(p, B, pos), "launch w2");
         if (pos + 1 < c.K) {
             int q = pos + 1;
             void *gargs[] = {&p, &q};
@@ -678,7 +713,26 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
             HIP_TRY(launch_state(gargs), "launch state");
         }
     }
-    {
+    if (pos_batched) {
+        // one W2 launch over the B K rows (b, pos): with K = 1 and B K rows the L_base,
+        // L_final and u layouts [B, K, *] are those of B K single-position rows, and the
+        // partial keys of row i sit at keys[g * B K + i]
+        const int rows = B * c.K;
+        Params pw = p;
+        pw.B = pw.maxB = rows;
+        pw.K = 1;
+        pw.u_buf = p.u_out;
+        pw.u_out = nullptr;
+        pw.S_out = nullptr;
+        const int nk = NG * rows;
+        hipLaunchKernelGGL(k_keys_zero, dim3(std::min((nk + NT - 1) / NT, 1024)), dim3(NT), 0, st, p.keys, nk);
+        HIP_TRY(hipGetLastError(), "launch key clear");
+        HIP_TRY(launch_w2(pw, rows, 0), "launch w2 (all positions)");
+        void *args[] = {&p};
+        HIP_TRY(hipLaunchKernel(reinterpret_cast<const void *>(&k_rows_tokens), dim3(std::min((rows + NT - 1) / NT, 1024)),
+                                dim3(NT), args, 0, st),
+                "launch tokens");
+    } else {
         void *args[] = {&p};
         HIP_TRY(hipLaunchKernel(reinterpret_cast<const void *>(&k_step_final), dim3(1), dim3(NT), args, 0, st),
                 "launch final");

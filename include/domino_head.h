@@ -72,6 +72,14 @@ extern "C" {
                                       same time; otherwise the bounded waits time out and the call
                                       reports DOMINO_FLAG_SYNC_TIMEOUT */
 
+#define DOMINO_EXEC_POSITION_BATCHED 32u /* with a teacher: take the step launches even for B <= 8.  With
+                                      a teacher the states of all positions follow from the given
+                                      tokens alone, so the step launches run the GRU chain first and
+                                      then the W2 products of all K positions as one launch over B*K
+                                      rows (W2 read once instead of K times); they always do this
+                                      when a teacher is given.  Same values as the per-position
+                                      launches, bit for bit */
+
 /*
  * Head configuration.  All weight pointers are DEVICE pointers, borrowed for
  * the lifetime of the handle (never copied, never written), stored in

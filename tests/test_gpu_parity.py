@@ -359,3 +359,45 @@ def test_resident_handle_with_varying_batch():
         assert np.array_equal(a[k], b[k]), k
     o = oracle.draft(w, inp3.H, inp3.L_base, inp3.last_tok)
     compare_free_running(o, a)
+
+
+@pytest.mark.parametrize("wd,V,B", [("bf16", 9001, 3), ("f32", 3001, 2)])
+def test_position_batched_teacher_forcing_equals_per_position(wd, V, B):
+    """With a teacher the step launches run the GRU chain first and then one W2
+    launch over all B*K (row, position) pairs.  The products are the same
+    instructions on the same operands as per position, so the result equals the
+    persistent (per-position) launch bit for bit: matrix-core W2 for the bf16
+    r = 256 head, the VALU W2 kernel for the fp32 head."""
+    sh = ds.HeadShape(d=1040 if wd == "bf16" else 136, h=64, r=256 if wd == "bf16" else 32, V=V, K=16, wdtype=wd)
+    w = ds.make_weights(sh, (9, 90), gru_sensitive=True)
+    inp = ds.make_inputs(sh, B, (9, 91), sigma=0.5, peak="none")
+    y = ds.uniform_tokens((9, 92), (B, 16), V)
+    a, fa = gpu_draft(make_head(w, 4, dca.EXEC_PERSISTENT, fold=True), inp.H, inp.L_base, inp.last_tok, teacher=y)
+    pb = make_head(w, 4, dca.EXEC_POSITION_BATCHED, fold=True)
+    assert pb.exec_info(B)["persistent"]  # exec_info reports the launch without a teacher
+    c, fc = gpu_draft(pb, inp.H, inp.L_base, inp.last_tok, teacher=y)
+    assert fa == 0 and fc == 0
+    for k in ("tokens", "L_final", "S", "u"):
+        assert np.array_equal(a[k], c[k]), k
+    # without u_out the u of every position goes through the workspace
+    d, _ = gpu_draft(pb, inp.H, inp.L_base, inp.last_tok, teacher=y, want_state=False)
+    assert np.array_equal(d["tokens"], a["tokens"]) and np.array_equal(d["L_final"], a["L_final"])
+
+
+def test_position_batched_teacher_forcing_matches_oracle_at_larger_batch():
+    """B = 40 with a teacher (matrix-core launches over 640 rows), against the
+    oracle's teacher-forced draft; one row has an invalid teacher id."""
+    sh = ds.HeadShape(d=256, h=64, r=256, V=7001, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 93), gru_sensitive=True)
+    B = 40
+    inp = ds.make_inputs(sh, B, (9, 94), sigma=0.5, peak="none")
+    y = ds.uniform_tokens((9, 95), (B, 16), sh.V)
+    y[7, 3] = sh.V + 5
+    head = make_head(w, B, dca.EXEC_AUTO, fold=True)
+    g, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok, teacher=y)
+    assert flags == dca.FLAG_BAD_TOKEN
+    assert (g["tokens"][7] == -1).all()
+    good = [b for b in range(B) if b != 7]
+    o = oracle.draft(w, inp.H[good], inp.L_base[good], inp.last_tok[good], teacher=y[good])
+    sub = {k: v[good] for k, v in g.items()}
+    compare_teacher_forced(o, sub)

@@ -25,7 +25,7 @@ def eprint(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def logical_bytes(sh, B, store_logits=False, fold=False):
+def logical_bytes(sh, B, store_logits=False, fold=False, lbase_bytes=4):
     """Algorithmic bytes of one block draft: every operand each step reads once.
 
     Per position (K of them): W2 [V,r], the L_base slice [B,V] fp32 and the state
@@ -33,18 +33,19 @@ def logical_bytes(sh, B, store_logits=False, fold=False):
     tokens): W_hh [3h,h] and both bias vectors, plus the input part: W_ih [3h,d]
     and the gathered embedding rows [B,d], or with the folded table one gathered
     row of P [B,3h] fp32.  Once per call: the H columns of W1 [r,d], H [B,K,d] and
-    the tokens [B,K].  Returns (total, w2_and_lbase).
+    the tokens [B,K].  L_base takes ``lbase_bytes`` per value (2 for bf16 input).
+    Returns (total, w2_and_lbase).
     """
     s = 4 if sh.wdtype == "f32" else 2
     K, V, r, h, d = sh.K, sh.V, sh.r, sh.h, sh.d
-    per_pos = V * r * s + B * V * 4 + r * h * s
+    per_pos = V * r * s + B * V * lbase_bytes + r * h * s
     gru_in = B * 3 * h * 4 if fold else 3 * h * d * s + B * d * s
     per_gru = gru_in + 3 * h * h * s + 6 * h * s
     once = r * d * s + B * K * d * s + B * K * 4
     total = K * per_pos + K * per_gru + once
     if store_logits:
         total += B * K * V * 4
-    return total, K * (V * r * s + B * V * 4)
+    return total, K * (V * r * s + B * V * lbase_bytes)
 
 
 def algorithmic_flops(sh, B, fold=False):
@@ -221,6 +222,8 @@ def main():
                     help="teacher-forced drafting: a seeded uniform teacher token row per batch row")
     ap.add_argument("--position-batched", action="store_true",
                     help="with --teacher: the GRU chain first, then one W2 launch for all positions (B <= 8 too)")
+    ap.add_argument("--lbase-bf16", action="store_true",
+                    help="L_base given as bfloat16 (DOMINO_LBASE_BF16): the workload's base logits rounded to bf16")
     ap.add_argument("--verify", action="store_true",
                     help="time the greedy verify step (domino_verify) on the workload's B, K and V instead")
     ap.add_argument("--cold-calls", type=int, default=20,
@@ -256,11 +259,12 @@ def main():
     head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B,
                           exec_mode=mode | (dca.EXEC_STREAM_W2 if args.stream_w2 else 0) |
                           (dca.EXEC_PLAIN_LAUNCH if args.plain_launch else 0) |
-                          (dca.EXEC_POSITION_BATCHED if args.position_batched else 0), fold_embedding=fold)
+                          (dca.EXEC_POSITION_BATCHED if args.position_batched else 0), fold_embedding=fold,
+                          lbase_bf16=args.lbase_bf16)
     torch.cuda.synchronize()
     t_create = time.perf_counter() - t_create
     H = dca.device_tensor(inp.H)
-    L = dca.device_tensor(inp.L_base)
+    L = dca.device_tensor(ds.round_to_bf16_bits(inp.L_base) if args.lbase_bf16 else inp.L_base)
     lt = dca.device_tensor(inp.last_tok)
     teacher = dca.device_tensor(ds.uniform_tokens(list(wl.row_key) + [9], (wl.B, sh.K), sh.V)) if args.teacher else None
     out = {"tokens": torch.empty((wl.B, sh.K), dtype=torch.int32, device="cuda")}
@@ -321,11 +325,12 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     blocks_per_s = wl.B * args.steps / wall
 
-    total_bytes, w2l_bytes = logical_bytes(sh, wl.B, args.store_logits, fold)
+    total_bytes, w2l_bytes = logical_bytes(sh, wl.B, args.store_logits, fold, 2 if args.lbase_bf16 else 4)
     achieved = total_bytes / (avg_ms * 1e-3) / 1e9
     w2l = w2l_bytes / (avg_ms * 1e-3) / 1e9
     w2_on_chip = info["w2_resident"]
-    traffic = measured_traffic(wl.name, exec_name, fold, w2_on_chip) if exec_name == "persistent" else None
+    traffic = (measured_traffic(wl.name, exec_name, fold, w2_on_chip)
+               if exec_name == "persistent" and not args.lbase_bf16 and not args.teacher else None)
     if exec_name == "persistent":
         kname = "k_persistent_res" if w2_on_chip else "k_persistent"
     else:
@@ -362,7 +367,7 @@ def main():
                    "weights": sh.wdtype, "exec": exec_name, "store_logits": bool(args.store_logits),
                    "fold_embedding": fold, "w2_on_chip": w2_on_chip,
                    "launch": "plain" if args.plain_launch else "cooperative", "create_s": t_create,
-                   "teacher_forced": bool(args.teacher),
+                   "teacher_forced": bool(args.teacher), "lbase_dtype": "bf16" if args.lbase_bf16 else "f32",
                    "kernel_avg_us": avg_ms * 1e3, "warm_us_per_call_median": float(np.median(per_call_ms)) * 1e3,
                    "cold_us_per_call_median": cold_us, "w2_lbase_GBps": w2l,
                    "w2_lbase_frac_of_hbm_peak": w2l / HBM_PEAK_GBPS, "matrix_core_use": mfma},

@@ -25,6 +25,7 @@ FOLD_EMBED = 4
 EXEC_STREAM_W2 = 8
 EXEC_PLAIN_LAUNCH = 16
 EXEC_POSITION_BATCHED = 32
+LBASE_BF16 = 64
 FLAG_BAD_TOKEN = 1
 FLAG_SYNC_TIMEOUT = 2
 
@@ -111,7 +112,7 @@ class DominoHead:
     """
 
     def __init__(self, weights: dict, K: int = 16, max_batch: int = 1, exec_mode: int = EXEC_AUTO,
-                 fold_embedding: bool = False):
+                 fold_embedding: bool = False, lbase_bf16: bool = False):
         lib = load_library()
         W1 = weights["W1"]
         wdtype = DOMINO_F32 if W1.dtype == torch.float32 else DOMINO_BF16
@@ -132,7 +133,8 @@ class DominoHead:
         self.max_batch = max_batch
         self.wdtype = wdtype
         self._weights = dict(weights)
-        flags = exec_mode | (FOLD_EMBED if fold_embedding else 0)
+        self.lbase_dtype = torch.bfloat16 if lbase_bf16 else torch.float32
+        flags = exec_mode | (FOLD_EMBED if fold_embedding else 0) | (LBASE_BF16 if lbase_bf16 else 0)
         self.cfg = Config(d, h, r, V, K, max_batch, wdtype, flags, _ptr(W1), _ptr(weights["W2"]),
                           _ptr(weights["W_ih"]), _ptr(weights["W_hh"]), _ptr(weights.get("b_ih")),
                           _ptr(weights.get("b_hh")), _ptr(weights["E"]))
@@ -180,7 +182,7 @@ class DominoHead:
             if "u" not in out:
                 out["u"] = torch.empty((B, self.K, self.r), dtype=torch.float32, device=dev)
         self._check_tensor("H", H, (B, self.K, self.d), _weight_dtype(self.wdtype))
-        self._check_tensor("L_base", L_base, (B, self.K, self.V), torch.float32)
+        self._check_tensor("L_base", L_base, (B, self.K, self.V), self.lbase_dtype)
         self._check_tensor("last_tok", last_tok, (B,), torch.int32)
         if teacher is not None:
             self._check_tensor("teacher", teacher, (B, self.K), torch.int32)

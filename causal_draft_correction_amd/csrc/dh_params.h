@@ -11,7 +11,7 @@ struct Params {
     const void *W1, *W2, *W_ih, *W_hh, *b_ih, *b_hh, *E;
     const float *P;  // folded input-gate table [V, 3h] or nullptr
     const void *H;
-    const float *L_base;
+    const void *L_base;  // [B, K, V] float32, or bfloat16 bits when lbase_bf16
     const int *last_tok, *teacher;
     const float *S_init;
     int *tokens;
@@ -33,6 +33,7 @@ struct Params {
     int persistent;  // 1: blocks keep the state in LDS between phases
     int ah_external; // 1: A_H is computed by its own (matrix-core) launch, not by the prologue
     int bf16w;       // 1: weights are bf16, 0: float32
+    int lbase_bf16;  // 1: L_base holds bfloat16 bit patterns
 };
 
 }  // namespace dhp

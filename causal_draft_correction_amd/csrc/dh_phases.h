@@ -52,6 +52,14 @@ __host__ __device__ inline int smem_floats(int r, int h, int rows_cap) { return 
 
 __device__ inline bool tok_ok(int t, int V) { return t >= 0 && t < V; }
 
+// Element i of L_base, float32 or bfloat16 (widened exactly).
+__device__ inline float lbase_at(const Params &p, size_t i)
+{
+    if (p.lbase_bf16)
+        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(p.L_base)[i]) << 16);
+    return static_cast<const float *>(p.L_base)[i];
+}
+
 // A row is invalid when its anchor or a used teacher token is outside [0, V).
 __device__ inline bool row_bad(const Params &p, int b)
 {
@@ -690,7 +698,7 @@ __device__ __forceinline__ void w2_epilogue(const Params &p, int blk, int nblk, 
     const int g = blk % NG;
     for (int bb = 0; bb < nb; ++bb) {
         const int b = b0 + bb;
-        const float *lb = p.L_base + (static_cast<size_t>(b) * p.K + pos) * p.V + v0;
+        const size_t lb = (static_cast<size_t>(b) * p.K + pos) * p.V + v0;
         float *lf = p.L_final ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * p.V + v0 : nullptr;
         uint64_t best = 0;
         for (int i = threadIdx.x, e = 0; i < n; i += NT, ++e) {
@@ -700,7 +708,7 @@ __device__ __forceinline__ void w2_epilogue(const Params &p, int blk, int nblk, 
                 if (bb == 0 && e == ee)
                     base_logit = lbv[ee];
             if (bb != 0 || e >= W2_LB)
-                base_logit = lb[i];
+                base_logit = lbase_at(p, lb + i);
             const float v = base_logit + lbuf[bb * rows_cap + i];
             if (lf)
                 lf[i] = v;
@@ -733,7 +741,7 @@ __device__ __forceinline__ void w2_lbase_prefetch(const Params &p, int blk, int 
 #pragma unroll
     for (int e = 0; e < W2_LB; ++e) {
         const int i = threadIdx.x + e * NT;
-        lbv[e] = i < n ? p.L_base[(static_cast<size_t>(b0) * p.K + pos) * p.V + v0 + i] : 0.f;
+        lbv[e] = i < n ? lbase_at(p, (static_cast<size_t>(b0) * p.K + pos) * p.V + v0 + i) : 0.f;
     }
 }
 
@@ -927,8 +935,19 @@ __device__ __forceinline__ void lbase_to_lds(const Params &p, int blk, int nblk,
     const int rows_cap = lbuf_stride(p.V, nblk);
     float *dst = smem + smem_off_lbuf(p.r);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (p.lbase_bf16) {
+        // bf16 input: loaded, widened and stored, so the LDS copy is float32 as above
+        // (this waits for its loads, which the argmax barrier wait around it covers)
+        for (int bb = 0; bb < p.B; ++bb) {
+            const uint16_t *src = static_cast<const uint16_t *>(p.L_base) + (static_cast<size_t>(bb) * p.K + pos) * p.V + v0;
+#pragma unroll 4
+            for (int c = threadIdx.x; c < n; c += NT)
+                dst[bb * rows_cap + c] = __uint_as_float(static_cast<uint32_t>(src[c]) << 16);
+        }
+        return;
+    }
     for (int bb = 0; bb < p.B; ++bb) {
-        const float *src = p.L_base + (static_cast<size_t>(bb) * p.K + pos) * p.V + v0;
+        const float *src = static_cast<const float *>(p.L_base) + (static_cast<size_t>(bb) * p.K + pos) * p.V + v0;
         for (int c = wave * 64; c < n; c += NT) {
             if (c + lane < n)
                 __builtin_amdgcn_global_load_lds(src + c + lane, (lds_void *)(dst + bb * rows_cap + c), 4, 0, 0);

@@ -340,7 +340,7 @@ int validate_config(const domino_head_config *c)
             return fail(DOMINO_EINVAL, "%s is not 16-byte aligned", names[i]);
     }
     if (c->flags & ~(DOMINO_EXEC_PERSISTENT | DOMINO_EXEC_STEPWISE | DOMINO_FOLD_EMBED | DOMINO_EXEC_STREAM_W2 |
-                     DOMINO_EXEC_PLAIN_LAUNCH | DOMINO_EXEC_POSITION_BATCHED))
+                     DOMINO_EXEC_PLAIN_LAUNCH | DOMINO_EXEC_POSITION_BATCHED | DOMINO_LBASE_BF16))
         return fail(DOMINO_EINVAL, "unknown flags 0x%x", c->flags);
     if ((c->flags & DOMINO_EXEC_PERSISTENT) && (c->flags & DOMINO_EXEC_STEPWISE))
         return fail(DOMINO_EINVAL, "flags ask for both persistent and stepwise execution");
@@ -541,7 +541,7 @@ int domino_head_create(const domino_head_config *cfg, void *workspace, size_t wo
 
 void domino_head_destroy(domino_head_t hd) { delete hd; }
 
-static Params make_params(domino_head_t hd, int B, const void *H, const float *L_base, const int32_t *last_tok,
+static Params make_params(domino_head_t hd, int B, const void *H, const void *L_base, const int32_t *last_tok,
                           const int32_t *teacher, const float *S_init, int32_t *tokens, float *L_final, float *S_out,
                           float *u_out, bool persistent)
 {
@@ -565,6 +565,7 @@ static Params make_params(domino_head_t hd, int B, const void *H, const float *L
     p.P = (c.flags & DOMINO_FOLD_EMBED) ? reinterpret_cast<const float *>(hd->ws + hd->L.P) : nullptr;
     p.H = H;
     p.L_base = L_base;
+    p.lbase_bf16 = (hd->cfg.flags & DOMINO_LBASE_BF16) ? 1 : 0;
     p.last_tok = last_tok;
     p.teacher = teacher;
     p.S_init = S_init;
@@ -586,7 +587,7 @@ static Params make_params(domino_head_t hd, int B, const void *H, const float *L
     return p;
 }
 
-int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L_base, const int32_t *last_tok,
+int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_base, const int32_t *last_tok,
                       const int32_t *teacher, const float *S_init, int32_t *tokens, float *L_final, float *S_out,
                       float *u_out, void *stream)
 {
@@ -696,7 +697,7 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L
         void *args[] = {&pw, &pos};
         void *margs[] = {&pw, &pos, &groups};
         if (w2_mfma)
-            return hipLaunchKernel(dhbat::w2_kernel(rows), dim3(dhbat::w2_grid(rows, hd->cus)),
+            return hipLaunchKernel(dhbat::w2_kernel(rows, pw.lbase_bf16 != 0), dim3(dhbat::w2_grid(rows, hd->cus)),
                                    dim3(dhbat::w2_threads(rows)), margs, dhbat::w2_smem(), st);
         return hipLaunchKernel(hd->kern.w2, dim3(g_w2), dim3(NT), args, sm_w2, st);
     };

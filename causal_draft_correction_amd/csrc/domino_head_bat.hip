@@ -32,7 +32,7 @@ namespace DH_NS {
 // the LDS operand traffic per result); the host uses the first.
 constexpr int XCDS = 8;   // accelerator dies (XCDs) of the MI355X, each with its own L2
 
-template <int KS, int VTG, int AT, int NTH>
+template <int KS, int VTG, int AT, int NTH, bool LB16>
 __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng)
 {
     static_assert(AT == 2 || AT == 4, "A tiles per wave");
@@ -128,7 +128,13 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng)
                 for (int i = 0; i < 4; ++i) {
                     const int b = brow[pp][i], vr = c * CRr + (vs * VTG + vt) * 16 + col;
                     const size_t o = (static_cast<size_t>(b < B ? b : 0) * p.K + pos) * V + v0 + (vr < n ? vr : 0);
-                    lb[pp][vt][i] = __builtin_nontemporal_load(p.L_base + o);  // streamed once
+                    // streamed once.  A bf16 row segment of a tile is 32 bytes, half a
+                    // 64-byte sector: those loads stay cached so the other half hits
+                    if constexpr (LB16)
+                        lb[pp][vt][i] = __uint_as_float(
+                            static_cast<uint32_t>(static_cast<const uint16_t *>(p.L_base)[o]) << 16);
+                    else
+                        lb[pp][vt][i] = __builtin_nontemporal_load(static_cast<const float *>(p.L_base) + o);
                 }
     };
 
@@ -436,16 +442,20 @@ struct W2Shape {
     const void *fn;
     int threads, ng;
 };
-static W2Shape w2_shape(int B)
+template <bool LB16>
+static const void *w2_fn(int ng)
+{
+    return ng == 8   ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 4, 2, 512, LB16>)
+           : ng == 4 ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 2, 2, 512, LB16>)
+                     : reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 1, 2, 512, LB16>);
+}
+static W2Shape w2_shape(int B, bool lb16 = false)
 {
     const int need = ((B < 128 ? B : 128) + 15) / 16;
     const int ng = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
-    const void *fn = ng == 8   ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 4, 2, 512>)
-                     : ng == 4 ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 2, 2, 512>)
-                               : reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 1, 2, 512>);
-    return {fn, 512, ng};
+    return {lb16 ? w2_fn<true>(ng) : w2_fn<false>(ng), 512, ng};
 }
-const void *w2_kernel(int B) { return w2_shape(B).fn; }
+const void *w2_kernel(int B, bool lbase_bf16) { return w2_shape(B, lbase_bf16).fn; }
 int w2_groups(int B) { return w2_shape(B).ng; }
 int w2_threads(int B) { return w2_shape(B).threads; }
 // one block per compute unit: batch tiles times vocabulary ranges

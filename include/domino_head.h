@@ -80,6 +80,11 @@ extern "C" {
                                       when a teacher is given.  Same values as the per-position
                                       launches, bit for bit */
 
+#define DOMINO_LBASE_BF16 64u         /* domino_head_draft's L_base holds bfloat16 bit patterns instead of
+                                      float32: half the bytes of the base-logit stream, which dominates
+                                      at large B.  Every path widens each value exactly, so the draft
+                                      equals a float32 call on the widened values bit for bit */
+
 /*
  * Head configuration.  All weight pointers are DEVICE pointers, borrowed for
  * the lifetime of the handle (never copied, never written), stored in
@@ -118,7 +123,8 @@ int domino_head_create(const domino_head_config *cfg, void *workspace, size_t wo
 /*
  * Draft one block for B rows (1 <= B <= max_batch).  Device pointers:
  *   H        [B, K, d]  wdtype     backbone hidden states of the block
- *   L_base   [B, K, V]  float32    backbone base logits of the block
+ *   L_base   [B, K, V]  float32    backbone base logits of the block (bfloat16
+ *                                  bit patterns with DOMINO_LBASE_BF16)
  *   last_tok [B]        int32      last confirmed token (anchor GRU input)
  *   teacher  [B, K]     int32      NULL = free running; else teacher forcing:
  *                                  teacher[b][p] replaces t_p as GRU input for
@@ -136,7 +142,7 @@ int domino_head_create(const domino_head_config *cfg, void *workspace, size_t wo
  * Bad token ids and barrier timeouts never abort: they set device flags read
  * by domino_head_check_error.
  */
-int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const float *L_base, const int32_t *last_tok,
+int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_base, const int32_t *last_tok,
                       const int32_t *teacher, const float *S_init, int32_t *tokens, float *L_final, float *S_out,
                       float *u_out, void *stream);
 

@@ -26,9 +26,9 @@ def log(msg):
     sys.stdout.flush()
 
 
-def make_head(w, max_batch, exec_mode=dca.EXEC_AUTO, K=None, fold=False):
+def make_head(w, max_batch, exec_mode=dca.EXEC_AUTO, K=None, fold=False, lbase_bf16=False):
     return dca.DominoHead(dca.head_weights_to_device(w), K=K or w.shape.K, max_batch=max_batch, exec_mode=exec_mode,
-                          fold_embedding=fold)
+                          fold_embedding=fold, lbase_bf16=lbase_bf16)
 
 
 def gpu_draft(head, H, L_base, last_tok, teacher=None, S_init=None, want_logits=True, want_state=True,

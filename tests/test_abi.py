@@ -66,7 +66,7 @@ def test_workspace_size_accepts_valid_config_and_grows_with_batch():
     (dict(K=0), -1), (dict(K=17), -1), (dict(max_batch=0), -1), (dict(max_batch=1025), -1), (dict(V=0), -1),
     (dict(d=12), -2), (dict(h=20), -2), (dict(r=12), -2), (dict(r=24), -2), (dict(wdtype=7), -2),
     (dict(wdtype=dca.DOMINO_BF16, r=4), -2), (dict(W2=None), -1), (dict(E=8), -1), (dict(flags=3), -1),
-    (dict(flags=64), -1),
+    (dict(flags=128), -1),
 ])
 def test_config_validation_codes(kw, code):
     rc, _ = ws_size(cfg(**kw))

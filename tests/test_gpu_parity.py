@@ -401,3 +401,48 @@ def test_position_batched_teacher_forcing_matches_oracle_at_larger_batch():
     o = oracle.draft(w, inp.H[good], inp.L_base[good], inp.last_tok[good], teacher=y[good])
     sub = {k: v[good] for k, v in g.items()}
     compare_teacher_forced(o, sub)
+
+
+BF16_LBASE_CASES = {
+    # name: (wdtype, d, h, r, V, B, max_batch, exec mode, fold, teacher)
+    "resident_b1": ("bf16", 1040, 64, 256, 5003, 1, 4, dca.EXEC_PERSISTENT, True, False),
+    "resident_b3": ("bf16", 1040, 64, 256, 5003, 3, 4, dca.EXEC_PERSISTENT, True, False),
+    "resident_lds_tiles": ("bf16", 256, 64, 256, 160000, 2, 2, dca.EXEC_PERSISTENT, True, False),
+    "resident_unfolded": ("bf16", 256, 64, 256, 5003, 1, 1, dca.EXEC_PERSISTENT, False, False),
+    "streamed_w2": ("bf16", 256, 64, 256, 5003, 2, 2, dca.EXEC_PERSISTENT | dca.EXEC_STREAM_W2, True, False),
+    "batched_matrix_cores": ("bf16", 256, 64, 256, 20011, 40, 40, dca.EXEC_AUTO, True, False),
+    "position_batched": ("bf16", 256, 64, 256, 7001, 9, 9, dca.EXEC_AUTO, True, True),
+    "f32_stepwise": ("f32", 136, 64, 32, 3001, 3, 4, dca.EXEC_STEPWISE, False, False),
+    "f32_persistent": ("f32", 136, 64, 32, 3001, 3, 4, dca.EXEC_PERSISTENT, True, False),
+}
+
+
+@pytest.mark.parametrize("case", sorted(BF16_LBASE_CASES))
+def test_bf16_lbase_equals_float32_of_the_same_values(case):
+    """With DOMINO_LBASE_BF16 every path widens each base logit exactly, so a call
+    with bf16 L_base equals a float32 call on the widened values bit for bit."""
+    wd, d, h, r, V, B, mb, mode, fold, tf = BF16_LBASE_CASES[case]
+    sh = ds.HeadShape(d=d, h=h, r=r, V=V, K=16, wdtype=wd)
+    w = ds.make_weights(sh, (9, 100), gru_sensitive=True)
+    inp = ds.make_inputs(sh, B, (9, 101), sigma=0.5, peak="none")
+    L16 = ds.round_to_bf16_bits(inp.L_base)
+    L32 = ds.bf16_bits_to_f32(L16)
+    y = ds.uniform_tokens((9, 102), (B, 16), V) if tf else None
+    a, fa = gpu_draft(make_head(w, mb, mode, fold=fold, lbase_bf16=True), inp.H, L16, inp.last_tok, teacher=y)
+    b, fb = gpu_draft(make_head(w, mb, mode, fold=fold), inp.H, L32, inp.last_tok, teacher=y)
+    assert fa == 0 and fb == 0
+    for k in ("tokens", "L_final", "S", "u"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_bf16_lbase_resident_matches_oracle():
+    sh = ds.HeadShape(d=256, h=64, r=256, V=5003, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 103), gru_sensitive=True)
+    inp = ds.make_inputs(sh, 3, (9, 104), sigma=0.5, peak="none")
+    L16 = ds.round_to_bf16_bits(inp.L_base)
+    inp32 = ds.BlockInputs(inp.H, ds.bf16_bits_to_f32(L16), inp.last_tok, inp.temperature, inp.peak_ids)
+    head = make_head(w, 3, dca.EXEC_PERSISTENT, fold=True, lbase_bf16=True)
+    o = oracle.draft(w, inp32.H, inp32.L_base, inp32.last_tok)
+    g, flags = gpu_draft(head, inp.H, L16, inp.last_tok)
+    assert flags == 0
+    compare_free_running(o, g)

@@ -244,6 +244,31 @@ def test_qwen3_8b_batched_sampled_rows(w8b, name, rows):
     assert np.array_equal(got, oracle.accept_len(g["tokens"], tgt))
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("name,rows,variant", [("qwen3_8b_b32", [0, 19, 31], "teacher"),
+                                               ("qwen3_8b_b256", [0, 128, 255], "lbase_bf16")])
+def test_qwen3_8b_batched_variants_sampled_rows(w8b, name, rows, variant):
+    """The launches the benchmark times with --teacher (position-batched W2 over 512 rows)
+    and with --lbase-bf16, at full size; the oracle checks sampled rows."""
+    wl = ds.WORKLOADS[name]
+    sh = wl.shape
+    inp = ds.make_inputs(sh, wl.B, wl.row_key, wl.sigma, wl.peak, wl.peak_height, wl.temperature)
+    sub = ds.make_inputs(sh, rows, wl.row_key, wl.sigma, wl.peak, wl.peak_height, wl.temperature)
+    if variant == "teacher":
+        y = ds.uniform_tokens(list(wl.row_key) + [9], (wl.B, sh.K), sh.V)
+        g, flags = gpu_draft(make_head(w8b, wl.B), inp.H, inp.L_base, inp.last_tok, teacher=y, rows=rows)
+        assert flags == 0
+        o = oracle.draft(w8b, sub.H, sub.L_base, sub.last_tok, teacher=y[rows])
+        compare_teacher_forced(o, g)
+    else:
+        L16 = ds.round_to_bf16_bits(inp.L_base)
+        g, flags = gpu_draft(make_head(w8b, wl.B, lbase_bf16=True), inp.H, L16, inp.last_tok, rows=rows)
+        assert flags == 0
+        o = oracle.draft(w8b, sub.H, ds.bf16_bits_to_f32(L16[rows]), sub.last_tok)
+        div = compare_free_running(o, g)
+        log("%s bf16 L_base sampled rows %s: diverged=%d" % (name, rows, div))
+
+
 # ------------------------------------------------------------------ accept length
 @pytest.mark.parametrize("B,K", [(1, 16), (37, 16), (256, 16), (1000, 16), (300, 5), (7, 1)])
 def test_accept_len_bit_exact(B, K):

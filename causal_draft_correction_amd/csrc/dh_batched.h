@@ -12,7 +12,7 @@ int w2_groups(int B);           // its third argument
 int w2_threads(int B);     // its threads per block
 size_t w2_smem();          // its dynamic LDS per block
 int w2_grid(int B, int cus);  // blocks for B batch rows on cus compute units
-const void *state_kernel();   // k_state_mfma (bf16 weights): arguments (Params, int step q)
+const void *state_kernel(int B, int h);  // state dots on the matrix cores (bf16 weights): arguments (Params, int q)
 int state_grid(int B, int r, int h);
 const void *ah_kernel();      // k_ah_mfma (bf16 H and W1, d and r multiples of 32): arguments (Params)
 int ah_grid(int B, int K, int r);

@@ -666,7 +666,7 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
         p.s_hl = reinterpret_cast<uint16_t *>(hd->ws + hd->L.s_hl);
     auto launch_state = [&](void **sargs) -> hipError_t {
         if (state_mfma)
-            return hipLaunchKernel(dhbat::state_kernel(), dim3(dhbat::state_grid(B, c.r, c.h)),
+            return hipLaunchKernel(dhbat::state_kernel(B, c.h), dim3(dhbat::state_grid(B, c.r, c.h)),
                                    dim3(dhbat::threads()), sargs, 0, st);
         return hipLaunchKernel(hd->kern.state, dim3(g_rows), dim3(NT), sargs, sm_state, st);
     };

@@ -370,6 +370,144 @@ __global__ __launch_bounds__(NT) void k_state_mfma(Params p, int q)
         }
 }
 
+// The same state dots with the operands staged in LDS (h a multiple of 256).  A
+// block takes 64 batch rows (8 A tiles of S hi/lo rows) x 64 weight rows (4 B
+// tiles).  The h reduction runs in stages of 64 (two 32-wide steps); a stage's
+// 24 operand blocks (per step: 8 A + 4 B tiles, 1 KB each in the matrix-core
+// operand layout) are copied by 16-byte direct global-to-LDS loads, three stages
+// ahead, into a ring of four LDS buffers, so the loads use no registers and the
+// S rows are read once per block instead of once per wave.  Each wave multiplies
+// 4 A tiles x 2 B tiles; one barrier per stage.  The products run over k in
+// the same order as in k_state_mfma's single pass.
+constexpr int SL_BLOCKS = 12;                // operand blocks per step: 8 A + 4 B tiles
+constexpr int SL_STAGE = 2 * SL_BLOCKS * 64; // uint4 per stage (two steps)
+
+template <typename WT>
+__global__ __launch_bounds__(NT) void k_state_lds(Params p, int q)
+{
+    typedef __attribute__((address_space(3))) void lds_void;
+    __shared__ uint4 ring0[SL_STAGE], ring1[SL_STAGE], ring2[SL_STAGE], ring3[SL_STAGE];
+    static_assert(NWAVE == 4, "four waves: 2 x 2 over the A and B tiles");
+    const int h = p.h, r = p.r, R = r + 3 * p.h, B = p.B;
+    const int nbg = (B + 63) / 64, nwb = (R + 63) / 64;
+    const int tile = xcd_tile(blockIdx.x, nbg * nwb);
+    const int bg = tile % nbg, wbk = tile / nbg;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15;
+    const int b0 = bg * 64, mw = wbk * 64;
+    const int NS = h / 64;  // stages, a multiple of 4
+    // this lane's source of the 6 operand blocks this wave copies per stage:
+    // block j = wave * 6 + u = step * 12 + t, t < 8: A tile t, else B tile t - 8.
+    // Rows past B or R repeat the last row (their results are not stored).
+    const uint16_t *src[6];
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+        const int j = wave * 6 + u, ks = j / SL_BLOCKS, t = j % SL_BLOCKS, i = lane & 15;
+        const uint16_t *base;
+        if (t < 8) {
+            const int b = b0 + t * 8 + (i & 7) < B ? b0 + t * 8 + (i & 7) : B - 1;
+            base = p.s_hl + (static_cast<size_t>(i >> 3) * p.maxB + b) * h;
+        } else {
+            const int m = mw + (t - 8) * 16 + i < R ? mw + (t - 8) * 16 + i : R - 1;
+            base = m < r ? static_cast<const uint16_t *>(p.W1) + static_cast<size_t>(m) * (p.d + h) + p.d
+                         : static_cast<const uint16_t *>(p.W_hh) + static_cast<size_t>(m - r) * h;
+        }
+        src[u] = base + ks * 32 + (lane >> 4) * 8;
+    }
+    auto issue = [&](int s, uint4 *ring) {
+#pragma unroll
+        for (int u = 0; u < 6; ++u)
+            __builtin_amdgcn_global_load_lds(src[u] + s * 64, (lds_void *)(ring + (wave * 6 + u) * 64), 16, 0, 0);
+    };
+    const int wa = wave & 1, wb = wave >> 1;
+    f32x4_t acc[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            acc[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const uint4 *ring) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            uint4 av[4], bv[2];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                av[a] = ring[(ks * SL_BLOCKS + wa * 4 + a) * 64 + lane];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                bv[t] = ring[(ks * SL_BLOCKS + 8 + wb * 2 + t) * 64 + lane];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[a]),
+                                                                       __builtin_bit_cast(bf16x8_t, bv[t]), acc[a][t],
+                                                                       0, 0, 0);
+        }
+    };
+    // wait until at most `later` stages of this wave's copies are outstanding (6 loads
+    // each), then a barrier: every wave has waited for its own copies of the stage, so
+    // the stage is in LDS for all of them.  The barrier is the bare instruction: a
+    // __syncthreads() would also wait for the copies of the later stages.  Each wave's
+    // reads of the previous buffer have returned (the products used them) before it
+    // arrives, so the buffer the next copy overwrites is free.
+    auto arrive = [&](int later) {
+        // s_waitcnt vmcnt(N): expcnt and lgkmcnt left at their maxima
+        if (later >= 2)
+            __builtin_amdgcn_s_waitcnt(12 | (7 << 4) | (15 << 8));
+        else if (later == 1)
+            __builtin_amdgcn_s_waitcnt(6 | (7 << 4) | (15 << 8));
+        else
+            __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    auto step = [&](int s, const uint4 *cur, uint4 *nxt) {
+        arrive((NS - 1 - s) < 2 ? NS - 1 - s : 2);
+        if (s + 3 < NS)
+            issue(s + 3, nxt);  // the buffer of stage s - 1, which every wave has finished
+        compute(cur);
+    };
+    issue(0, ring0);
+    issue(1, ring1);
+    issue(2, ring2);
+#pragma unroll 1
+    for (int s = 0; s < NS; s += 4) {
+        step(s, ring0, ring3);
+        step(s + 1, ring1, ring0);
+        step(s + 2, ring2, ring1);
+        step(s + 3, ring3, ring2);
+    }
+    const int h3 = 3 * h;
+    float *qn = q_slot(p, q + 1);
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int m = mw + (wb * 2 + t) * 16 + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x0 = w2_hilo(acc[2 * pp][t], i), x1 = w2_hilo(acc[2 * pp + 1][t], i);
+                const auto dd = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x1), false,
+                                                                 false);
+                const float dot = __uint_as_float(dd[0]);
+                const int b = b0 + (wa * 4 + 2 * pp + (lane >> 5)) * 8 + ((lane >> 4) & 1) * 4 + i;
+                if (b >= B || m >= R)
+                    continue;
+                if (m < r) {
+                    const float a_ = p.A_H[(static_cast<size_t>(b) * p.K + q) * r + m] + dot;
+                    const float u = a_ * sigmoidf_(a_);
+                    p.u_buf[static_cast<size_t>(b) * r + m] = u;
+                    if (p.u_out)
+                        p.u_out[(static_cast<size_t>(b) * p.K + q) * r + m] = u;
+                } else {
+                    const float bias = p.b_hh ? WT16<WT>::one(p.b_hh, m - r) : 0.f;
+                    qn[static_cast<size_t>(b) * h3 + (m - r)] = dot + bias;
+                }
+            }
+        }
+}
+
 // A_H = W1[:, :d] H for every position on the matrix cores (same quantity as
 // phase_ah): rows R = b * K + i of H (bf16, [B*K, d]) times rows m of W1's
 // first d columns; A_H[R][m] in fp32.  A block takes 32 H rows x 32 W1 rows
@@ -468,9 +606,21 @@ int w2_grid(int B, int cus)
 }
 // two chunk buffers of up to 128 rows x 256 bf16
 size_t w2_smem() { return 2 * sizeof(uint4) * (128 / 16) * BAT_KS * 64; }
-const void *state_kernel() { return reinterpret_cast<const void *>(&k_state_mfma<bf16s>); }
+// B >= 64 and h a multiple of 256: the LDS-staged kernel (64-row batch tiles); otherwise
+// the split-K one (32-row tiles: more blocks at smaller B).  Measured at 8B shapes: the
+// staged launch takes 22 us against 31 us at B = 256, while at B = 32 a whole call took
+// 877 us with it against 805 us without.
+static bool state_staged(int B, int h) { return B >= 64 && h % 256 == 0; }
+const void *state_kernel(int B, int h)
+{
+    return state_staged(B, h) ? reinterpret_cast<const void *>(&k_state_lds<bf16s>)
+                              : reinterpret_cast<const void *>(&k_state_mfma<bf16s>);
+}
 const void *ah_kernel() { return reinterpret_cast<const void *>(&k_ah_mfma<bf16s>); }
 int ah_grid(int B, int K, int r) { return (B * K + 31) / 32 * (r / 32); }
-int state_grid(int B, int r, int h) { return ((B + 31) / 32) * ((r + 3 * h + 31) / 32); }
+int state_grid(int B, int r, int h)
+{
+    return state_staged(B, h) ? ((B + 63) / 64) * ((r + 3 * h + 63) / 64) : ((B + 31) / 32) * ((r + 3 * h + 31) / 32);
+}
 
 }  // namespace dhbat

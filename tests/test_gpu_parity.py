@@ -471,3 +471,16 @@ def test_bf16_lbase_resident_matches_oracle():
     g, flags = gpu_draft(head, inp.H, L16, inp.last_tok)
     assert flags == 0
     compare_free_running(o, g)
+
+
+@pytest.mark.parametrize("B", [64, 70])
+def test_lds_staged_state_dots_match_oracle(B):
+    """h = 256 and B >= 64 take the LDS-staged state launch: a ragged batch tile
+    (B = 70) and a ragged weight tile (r + 3h = 800 rows), against the oracle in
+    both protocols."""
+    sh = ds.HeadShape(d=256, h=256, r=32, V=3001, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 110), gru_sensitive=True)
+    inp = ds.make_inputs(sh, B, (9, 111), sigma=0.5, peak="none")
+    head = make_head(w, B, dca.EXEC_AUTO, fold=True)
+    assert not head.exec_info(B)["persistent"]
+    run_both_protocols(w, inp, head, label="staged state dots B=%d" % B)

@@ -1,12 +1,20 @@
-// Domino head drafting library for MI355X (gfx950): kernels and the C ABI.
+// Domino head drafting library for MI355X (gfx950): the host side of the C ABI
+// and the kernels built for 512-thread blocks.
 //
-// Two orchestrations of the same phases (dh_phases.h):
-//   * persistent: one cooperative launch of one block per compute unit runs
-//     the whole block draft, phases separated by a two-level grid barrier
-//     (48 barriers for K = 16);
-//   * stepwise: one launch per phase and position on the caller's stream.
-// Both run identical per-element arithmetic, so their outputs are bitwise
-// equal.  The verify-side prefix match is a separate small kernel.
+// Launch kinds over the same phases (dh_phases.h), chosen per call
+// (domino_head_exec_info reports which):
+//   * persistent, B <= 8: one launch of one block per compute unit runs the
+//     whole block draft.  bf16 heads with r = 256 keep each block's W2 slice on
+//     chip (domino_head_res.hip); other heads stream W2 every position
+//     (k_persistent here).  One argmax barrier per position, plus a grid barrier
+//     after each state phase when W2 is streamed;
+//   * step launches: one launch per phase and position on the caller's stream;
+//     larger bf16 batches run W2, the state dots and A_H on the matrix cores
+//     (domino_head_bat.hip), and with a teacher the W2 products of all positions
+//     form a single launch.
+// Where two launch kinds can run the same call they form every value with the
+// same arithmetic, so their outputs are bitwise equal (tested).  The verify
+// step is in domino_verify.hip; the prefix match (k_accept_len) is here.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>

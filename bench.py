@@ -222,6 +222,8 @@ def main():
                     help="teacher-forced drafting: a seeded uniform teacher token row per batch row")
     ap.add_argument("--position-batched", action="store_true",
                     help="with --teacher: the GRU chain first, then one W2 launch for all positions (B <= 8 too)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one draft call in a HIP graph (torch.cuda.CUDAGraph) and replay it per step")
     ap.add_argument("--lbase-bf16", action="store_true",
                     help="L_base given as bfloat16 (DOMINO_LBASE_BF16): the workload's base logits rounded to bf16")
     ap.add_argument("--verify", action="store_true",
@@ -285,8 +287,23 @@ def main():
         eprint("bench: calibration copy of %d MiB done" % args.calibrate_copy)
         del src, dst
 
-    for _ in range(args.warmup):
+    def call():
         head.draft(H, L, lt, teacher=teacher, out=out)
+
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                call()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        torch.cuda.synchronize()
+        call = graph.replay  # noqa: F811
+    for _ in range(args.warmup):
+        call()
     torch.cuda.synchronize()
     assert head.check_error() == 0
     eprint("bench: warmup done, timing %d steps" % args.steps)
@@ -297,7 +314,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        head.draft(H, L, lt, teacher=teacher, out=out)
+        call()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -316,7 +333,7 @@ def main():
         for i in range(args.cold_calls):
             evict.fill_(float(i))
             cev[i][0].record(stream)
-            head.draft(H, L, lt, teacher=teacher, out=out)
+            call()
             cev[i][1].record(stream)
         torch.cuda.synchronize()
         assert head.check_error() == 0
@@ -368,6 +385,7 @@ def main():
                    "fold_embedding": fold, "w2_on_chip": w2_on_chip,
                    "launch": "plain" if args.plain_launch else "cooperative", "create_s": t_create,
                    "teacher_forced": bool(args.teacher), "lbase_dtype": "bf16" if args.lbase_bf16 else "f32",
+                   "hip_graph": bool(args.graph),
                    "kernel_avg_us": avg_ms * 1e3, "warm_us_per_call_median": float(np.median(per_call_ms)) * 1e3,
                    "cold_us_per_call_median": cold_us, "w2_lbase_GBps": w2l,
                    "w2_lbase_frac_of_hbm_peak": w2l / HBM_PEAK_GBPS, "matrix_core_use": mfma},

@@ -484,3 +484,47 @@ def test_lds_staged_state_dots_match_oracle(B):
     head = make_head(w, B, dca.EXEC_AUTO, fold=True)
     assert not head.exec_info(B)["persistent"]
     run_both_protocols(w, inp, head, label="staged state dots B=%d" % B)
+
+
+@pytest.mark.parametrize("case", ["step_launches_b40", "resident_plain_launch_b3"])
+def test_hip_graph_replay_matches_eager(case):
+    """A draft call captured in a HIP graph (no memset nodes: the library clears with
+    kernels) replayed several times, with eager draft calls of other inputs on the same
+    handle in between; every replay equals the eager result bitwise."""
+    sh = ds.HeadShape(d=256, h=64, r=256, V=7001, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 120), gru_sensitive=True)
+    if case == "step_launches_b40":
+        B, mode = 40, dca.EXEC_AUTO
+    else:
+        B, mode = 3, dca.EXEC_PERSISTENT | dca.EXEC_PLAIN_LAUNCH
+    head = make_head(w, B, mode, fold=True)
+    inp = ds.make_inputs(sh, B, (9, 121), sigma=0.5, peak="none")
+    other = ds.make_inputs(sh, B, (9, 122), sigma=0.5, peak="none")
+    ref, _ = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
+    H, L, lt = dca.device_tensor(inp.H), dca.device_tensor(inp.L_base), dca.device_tensor(inp.last_tok)
+    Ho, Lo, lto = dca.device_tensor(other.H), dca.device_tensor(other.L_base), dca.device_tensor(other.last_tok)
+    dev = H.device
+    gout = {"tokens": torch.empty((B, 16), dtype=torch.int32, device=dev),
+            "L_final": torch.empty((B, 16, sh.V), dtype=torch.float32, device=dev),
+            "S": torch.empty((B, 16, sh.h), dtype=torch.float32, device=dev),
+            "u": torch.empty((B, 16, sh.r), dtype=torch.float32, device=dev)}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            head.draft(H, L, lt, want_logits=True, want_state=True, out=gout)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        head.draft(H, L, lt, want_logits=True, want_state=True, out=gout)
+    for rep in range(3):
+        for k in gout:
+            gout[k].fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ("tokens", "L_final", "S", "u"):
+            assert np.array_equal(gout[k].cpu().numpy(), ref[k]), "replay %d: %s" % (rep, k)
+        eager = head.draft(Ho, Lo, lto, want_logits=True)  # other work on the same handle in between
+        torch.cuda.synchronize()
+        assert eager["tokens"].shape == (B, 16)
+    assert head.check_error() == 0

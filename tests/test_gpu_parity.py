@@ -528,3 +528,33 @@ def test_hip_graph_replay_matches_eager(case):
         torch.cuda.synchronize()
         assert eager["tokens"].shape == (B, 16)
     assert head.check_error() == 0
+
+
+def test_side_streams_and_two_handles_concurrently():
+    """Calls are ordered on the caller's stream: a draft on a side stream equals the
+    default-stream result, and two handles drafting on two streams at once (step
+    launches) each equal their own sequential result."""
+    sh = ds.HeadShape(d=256, h=64, r=256, V=7001, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 130), gru_sensitive=True)
+    B = 24
+    ia = ds.make_inputs(sh, B, (9, 131), sigma=0.5, peak="none")
+    ib = ds.make_inputs(sh, B, (9, 132), sigma=0.5, peak="none")
+    ha, hb = make_head(w, B, fold=True), make_head(w, B, fold=True)
+    ra, _ = gpu_draft(ha, ia.H, ia.L_base, ia.last_tok)
+    rb, _ = gpu_draft(hb, ib.H, ib.L_base, ib.last_tok)
+    dev = [dca.device_tensor(x) for x in (ia.H, ia.L_base, ia.last_tok, ib.H, ib.L_base, ib.last_tok)]
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(3):
+        with torch.cuda.stream(sa):
+            oa = ha.draft(dev[0], dev[1], dev[2], want_logits=True, want_state=True)
+        with torch.cuda.stream(sb):
+            ob = hb.draft(dev[3], dev[4], dev[5], want_logits=True, want_state=True)
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    for oa, ob in outs:
+        for k in ("tokens", "L_final", "S", "u"):
+            assert np.array_equal(oa[k].cpu().numpy(), ra[k]), k
+            assert np.array_equal(ob[k].cpu().numpy(), rb[k]), k
+    assert ha.check_error() == 0 and hb.check_error() == 0

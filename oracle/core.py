@@ -36,7 +36,7 @@ class _Head(ctypes.Structure):
                 ("V", ctypes.c_int32), ("K", ctypes.c_int32), ("wdtype", ctypes.c_int32),
                 ("W1", ctypes.c_void_p), ("W2", ctypes.c_void_p), ("W_ih", ctypes.c_void_p),
                 ("W_hh", ctypes.c_void_p), ("b_ih", ctypes.c_void_p), ("b_hh", ctypes.c_void_p),
-                ("E", ctypes.c_void_p)]
+                ("E", ctypes.c_void_p), ("markov", ctypes.c_int32)]
 
 
 _lib = None
@@ -77,12 +77,13 @@ def _weight_dtype(shape):
 
 
 def draft(weights, H, L_base, last_tok, teacher=None, S_init=None, want_logits=True, want_state=True,
-          threads: Optional[int] = None):
+          threads: Optional[int] = None, markov: bool = False):
     """Run the oracle on every row of the given arrays.
 
     weights: domino_synth.HeadWeights (or any object with .shape and the seven arrays)
     H [n,K,d] (weight storage dtype), L_base [n,K,V] float32, last_tok [n] int32,
     teacher [n,K] int32 or None, S_init [n,h] float32 or None.
+    markov: the Markov head (every GRU step from the zero state; S_init must be None).
 
     Returns a dict: tokens [n,K] int32, gap [n,K] float64, flags [n] int32 and,
     when requested, L_final [n,K,V] float64, S [n,K,h] float64 (S_0..S_{K-1}),
@@ -95,8 +96,10 @@ def draft(weights, H, L_base, last_tok, teacher=None, S_init=None, want_logits=T
     for name in ("W1", "W2", "W_ih", "W_hh", "b_ih", "b_hh", "E"):
         a = getattr(weights, name)
         arrs[name] = None if a is None else np.ascontiguousarray(a, dtype=wdt)
+    assert not (markov and S_init is not None), "a Markov head has no initial state"
     head = _Head(sh.d, sh.h, sh.r, sh.V, sh.K, 0 if sh.wdtype == "f32" else 1,
-                 *[_ptr(arrs[k]) for k in ("W1", "W2", "W_ih", "W_hh", "b_ih", "b_hh", "E")])
+                 *[_ptr(arrs[k]) for k in ("W1", "W2", "W_ih", "W_hh", "b_ih", "b_hh", "E")],
+                 1 if markov else 0)
     H = np.ascontiguousarray(H, dtype=wdt)
     L_base = np.ascontiguousarray(L_base, dtype=np.float32)
     last_tok = np.ascontiguousarray(last_tok, dtype=np.int32)

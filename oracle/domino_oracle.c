@@ -44,7 +44,15 @@
  *     every number and the first NaN wins.  The decision is taken on the
  *     logits rounded to float32, the precision the GPU path decides in;
  *   - a last_tok or a used teacher token outside [0, V) makes the row
- *     invalid: all its tokens are -1 and the function returns 1.
+ *     invalid: all its tokens are -1 and the function returns 1;
+ *   - Markov head (markov != 0).  The news.sig.ai article (section
+ *     从Domino看DSpark) says DSpark ships a Markov head as its default beside
+ *     an RNN head, and that Domino's causal encoder corresponds to the RNN
+ *     head; it gives no formula.  Reading taken: a Markov head
+ *     conditions each position on the preceding token alone, so the causal
+ *     state is the same GRU cell applied to that token's embedding from a
+ *     zero state, S_i = GRU(E[x_i], 0) (S_0 = GRU(E[last_tok], 0)); nothing
+ *     is carried from earlier positions and S_init is not used.
  *
  * Arithmetic: every weight and input is widened from its stored bits
  * (float32 or bfloat16) to double; every dot product sums in ascending index
@@ -63,6 +71,7 @@ typedef struct {
     int32_t d, h, r, V, K;
     int32_t wdtype; /* 0: float32 storage, 1: bfloat16 bit patterns (uint16) */
     const void *W1, *W2, *W_ih, *W_hh, *b_ih, *b_hh, *E;
+    int32_t markov; /* 1: Markov head, every GRU step starts from the zero state */
 } oracle_head;
 
 static double widen(const void *base, int32_t wdtype, size_t idx)
@@ -121,7 +130,7 @@ static int beats(float a, float b)
  *   H        [K, d]   wdtype storage
  *   L_base   [K, V]   float32
  *   teacher  [K] or NULL; entries 0..K-2 (tokens y_1..y_{K-1}) are used
- *   S_init   [h] float32 or NULL
+ *   S_init   [h] float32 or NULL (not used by a Markov head)
  * Outputs (any pointer but tokens may be NULL):
  *   tokens [K] int32; L_final [K, V] double; gap [K] double (top1 - top2 of
  *   L_final in double, top2 over the other entries); S_out [K, h] double
@@ -148,12 +157,13 @@ int oracle_draft_row(const oracle_head *hd, const void *H, const float *L_base, 
 
     double *s = (double *)malloc(sizeof(double) * (size_t)h);
     double *s_next = (double *)malloc(sizeof(double) * (size_t)h);
+    double *zero = (double *)calloc((size_t)h, sizeof(double));
     double *cat = (double *)malloc(sizeof(double) * (size_t)(d + h));
     double *u = (double *)malloc(sizeof(double) * (size_t)r);
     double *lf = (double *)malloc(sizeof(double) * (size_t)V);
 
     for (int32_t j = 0; j < h; ++j)
-        s[j] = S_init ? (double)S_init[j] : 0.0;
+        s[j] = (S_init && !hd->markov) ? (double)S_init[j] : 0.0;
     /* anchor step: S_0 = GRU(E[last_tok], S_init) */
     gru_cell(hd, last_tok, s, s_next, nthreads);
     memcpy(s, s_next, sizeof(double) * (size_t)h);
@@ -210,12 +220,14 @@ int oracle_draft_row(const oracle_head *hd, const void *H, const float *L_base, 
             memcpy(L_final + (size_t)i * V, lf, sizeof(double) * (size_t)V);
         if (i + 1 < K) {
             int32_t x_tok = teacher ? teacher[i] : best;
-            gru_cell(hd, x_tok, s, s_next, nthreads);
+            /* recurrent head: from S_{i-1}; Markov head: from the zero state */
+            gru_cell(hd, x_tok, hd->markov ? zero : s, s_next, nthreads);
             memcpy(s, s_next, sizeof(double) * (size_t)h);
         }
     }
     free(s);
     free(s_next);
+    free(zero);
     free(cat);
     free(u);
     free(lf);

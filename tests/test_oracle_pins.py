@@ -430,3 +430,131 @@ def test_V3_speculative_loop_reproduces_greedy_decoding():
         assert seq[:2 + N] == ref, "p_wrong=%g" % p_wrong
         if p_wrong == 0.0:
             assert steps == -(-N // (K + 1))  # every step commits K + 1 tokens
+
+
+# ---------------------------------------------------------------- Markov head
+# The article (section 从Domino看DSpark) names a Markov head, the default of
+# DSpark, beside an RNN head that corresponds to Domino's causal encoder; it
+# gives no formula.  Reading: each position is conditioned on the preceding
+# token alone, S_i = GRU(E[x_i], 0) with x_0 = last_tok.
+
+def gru_cell64(w):
+    sh = w.shape
+    cell = torch.nn.GRUCell(sh.d, sh.h, bias=True, dtype=torch.float64)
+    with torch.no_grad():
+        cell.weight_ih.copy_(torch.from_numpy(weights_f64(w, "W_ih")))
+        cell.weight_hh.copy_(torch.from_numpy(weights_f64(w, "W_hh")))
+        cell.bias_ih.copy_(torch.from_numpy(weights_f64(w, "b_ih")))
+        cell.bias_hh.copy_(torch.from_numpy(weights_f64(w, "b_hh")))
+    return cell
+
+
+def test_M1_markov_equals_recurrent_when_no_state_is_carried():
+    """With W_hh = 0 and the update gate shut (its W_ih rows zero, its input bias
+    -1e4, so z = 0 exactly in double), the recurrent cell's new state n no longer
+    depends on the old one: the recurrent head and the Markov head then give
+    bitwise the same tokens, logits and states.  With the recurrence switched back
+    on they differ, so the Markov flag really changes the state feed."""
+    sh = small_shape(V=43, d=24, h=16, r=8)
+    w = ds.make_weights(sh, (9, 40), gru_sensitive=True)
+    inp = ds.make_inputs(sh, 3, (9, 41), sigma=0.3, peak="none")
+    rec = oracle.draft(w, inp.H, inp.L_base, inp.last_tok)
+    mk = oracle.draft(w, inp.H, inp.L_base, inp.last_tok, markov=True)
+    assert np.abs(rec["S"][:, 1:] - mk["S"][:, 1:]).max() > 1e-3
+    np.testing.assert_array_equal(rec["S"][:, 0], mk["S"][:, 0])  # anchor: both start from zero
+    h = sh.h
+    w.W_hh = zero_like(w.W_hh)
+    w.W_ih[h:2 * h] = 0.0
+    w.b_ih[h:2 * h] = -1e4
+    w.b_hh[h:2 * h] = 0.0
+    rec = oracle.draft(w, inp.H, inp.L_base, inp.last_tok)
+    mk = oracle.draft(w, inp.H, inp.L_base, inp.last_tok, markov=True)
+    for k in ("tokens", "L_final", "S", "u"):
+        np.testing.assert_array_equal(rec[k], mk[k])
+
+
+@pytest.mark.parametrize("wdtype,teacher", [("f32", False), ("bf16", False), ("f32", True)])
+def test_M2_markov_states_are_grucell_from_zero(wdtype, teacher):
+    """Markov head: S_i equals torch.nn.GRUCell (float64) applied to E[x_i] with a
+    zero hidden state, x_0 = last_tok and x_i the draft token (or teacher token) of
+    position i - 1, and each correction equals W2 SiLU(W1 [H_i; S_i]) evaluated with
+    torch.nn.functional (review, section 二 formula)."""
+    sh = small_shape(V=41, d=24, h=16, r=8, wdtype=wdtype)
+    w = ds.make_weights(sh, (9, 42), gru_sensitive=True)
+    inp = ds.make_inputs(sh, 2, (9, 43), sigma=0.3, peak="none")
+    y = ds.uniform_tokens((9, 44), (2, sh.K), sh.V) if teacher else None
+    o = oracle.draft(w, inp.H, inp.L_base, inp.last_tok, teacher=y, markov=True)
+    cell = gru_cell64(w)
+    E = torch.from_numpy(weights_f64(w, "E"))
+    W1 = torch.from_numpy(weights_f64(w, "W1"))
+    W2 = torch.from_numpy(weights_f64(w, "W2"))
+    H = inp.H.astype(np.float64) if wdtype == "f32" else ds.bf16_bits_to_f32(inp.H).astype(np.float64)
+    zero = torch.zeros(1, sh.h, dtype=torch.float64)
+    for b in range(2):
+        for i in range(sh.K):
+            x = int(inp.last_tok[b]) if i == 0 else int(y[b, i - 1] if teacher else o["tokens"][b, i - 1])
+            with torch.no_grad():
+                s = cell(E[x][None], zero)[0]
+                cat = torch.cat([torch.from_numpy(H[b, i]), s])
+                corr = torch.nn.functional.linear(torch.nn.functional.silu(torch.nn.functional.linear(cat, W1)), W2)
+            np.testing.assert_allclose(o["S"][b, i], s.numpy(), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(o["L_final"][b, i] - inp.L_base[b, i], corr.numpy(), rtol=0, atol=1e-12)
+
+
+def test_M3_markov_position_depends_only_on_the_preceding_token():
+    """Teacher forced Markov head: changing the teacher token of position j changes
+    the logits of position j + 1 and of no other position (bitwise); the recurrent
+    head changes every later position."""
+    sh = small_shape(V=47, d=24, h=16, r=8)
+    w = ds.make_weights(sh, (9, 45), gru_sensitive=True)
+    inp = ds.make_inputs(sh, 1, (9, 46), sigma=0.3, peak="none")
+    y = ds.uniform_tokens((9, 47), (1, sh.K), sh.V)
+    j = 5
+    y2 = y.copy()
+    y2[0, j] = (y[0, j] + 1) % sh.V
+    a = oracle.draft(w, inp.H, inp.L_base, inp.last_tok, teacher=y, markov=True)["L_final"][0]
+    b = oracle.draft(w, inp.H, inp.L_base, inp.last_tok, teacher=y2, markov=True)["L_final"][0]
+    changed = [i for i in range(sh.K) if not np.array_equal(a[i], b[i])]
+    assert changed == [j + 1]
+    ra = oracle.draft(w, inp.H, inp.L_base, inp.last_tok, teacher=y)["L_final"][0]
+    rb = oracle.draft(w, inp.H, inp.L_base, inp.last_tok, teacher=y2)["L_final"][0]
+    assert [i for i in range(sh.K) if not np.array_equal(ra[i], rb[i])] == list(range(j + 1, sh.K))
+
+
+def test_M4_markov_low_rank_input_is_a_per_token_table():
+    """Since S_i is a function of one token, W1 [H_i; S_i] = W1_H H_i + M[x_i] with a
+    per-token table M[t] = W1_S GRU(E[t], 0) (V x r).  The oracle's u equals SiLU of
+    that sum with M built for every token by torch (float64)."""
+    sh = small_shape(V=29, d=24, h=16, r=8)
+    w = ds.make_weights(sh, (9, 48), gru_sensitive=True)
+    inp = ds.make_inputs(sh, 2, (9, 49), sigma=0.3, peak="none")
+    o = oracle.draft(w, inp.H, inp.L_base, inp.last_tok, markov=True)
+    cell = gru_cell64(w)
+    E = torch.from_numpy(weights_f64(w, "E"))
+    W1 = weights_f64(w, "W1")
+    with torch.no_grad():
+        S_all = cell(E, torch.zeros(sh.V, sh.h, dtype=torch.float64)).numpy()
+    M = S_all @ W1[:, sh.d:].T
+    for b in range(2):
+        A = inp.H[b].astype(np.float64) @ W1[:, :sh.d].T
+        x = np.concatenate([[inp.last_tok[b]], o["tokens"][b, :-1]])
+        np.testing.assert_allclose(o["u"][b], silu64(A + M[x]), rtol=0, atol=1e-12)
+
+
+def test_M5_markov_brute_force_fixed_point_is_the_greedy_draft():
+    """Markov head, tiny vocabulary: exactly one teacher sequence in V^(K-1) is a
+    fixed point of teacher forcing, and it is the free-running greedy draft."""
+    sh = small_shape(V=5, d=8, h=8, r=4, K=5)
+    w = ds.make_weights(sh, (9, 50), gru_sensitive=True)
+    w.W1[:, sh.d:] *= 4.0
+    inp = ds.make_inputs(sh, 1, (9, 51), sigma=0.2, peak="none")
+    fr = oracle.draft(w, inp.H, inp.L_base, inp.last_tok, markov=True)["tokens"][0]
+    seqs = np.array(list(itertools.product(range(sh.V), repeat=sh.K - 1)), dtype=np.int32)
+    teach = np.concatenate([seqs, np.zeros((len(seqs), 1), np.int32)], axis=1)
+    n = len(seqs)
+    out = oracle.draft(w, np.repeat(inp.H, n, 0), np.repeat(inp.L_base, n, 0), np.repeat(inp.last_tok, n),
+                       teacher=teach, want_logits=False, want_state=False, threads=1, markov=True)["tokens"]
+    fixed = [j for j in range(n) if np.array_equal(out[j, :sh.K - 1], seqs[j])]
+    assert len(fixed) == 1
+    np.testing.assert_array_equal(out[fixed[0]], fr)
+    assert len({tuple(x) for x in out}) > 1

@@ -25,7 +25,7 @@ def eprint(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def logical_bytes(sh, B, store_logits=False, fold=False, lbase_bytes=4):
+def logical_bytes(sh, B, store_logits=False, fold=False, lbase_bytes=4, markov=False):
     """Algorithmic bytes of one block draft: every operand each step reads once.
 
     Per position (K of them): W2 [V,r], the L_base slice [B,V] fp32 and the state
@@ -34,13 +34,19 @@ def logical_bytes(sh, B, store_logits=False, fold=False, lbase_bytes=4):
     and the gathered embedding rows [B,d], or with the folded table one gathered
     row of P [B,3h] fp32.  Once per call: the H columns of W1 [r,d], H [B,K,d] and
     the tokens [B,K].  L_base takes ``lbase_bytes`` per value (2 for bf16 input).
+    Markov head: no GRU step and no W1_S product; each position gathers one row of
+    the per-token table M [B,r] fp32 instead.
     Returns (total, w2_and_lbase).
     """
     s = 4 if sh.wdtype == "f32" else 2
     K, V, r, h, d = sh.K, sh.V, sh.r, sh.h, sh.d
-    per_pos = V * r * s + B * V * lbase_bytes + r * h * s
-    gru_in = B * 3 * h * 4 if fold else 3 * h * d * s + B * d * s
-    per_gru = gru_in + 3 * h * h * s + 6 * h * s
+    if markov:
+        per_pos = V * r * s + B * V * lbase_bytes + B * r * 4
+        per_gru = 0
+    else:
+        per_pos = V * r * s + B * V * lbase_bytes + r * h * s
+        gru_in = B * 3 * h * 4 if fold else 3 * h * d * s + B * d * s
+        per_gru = gru_in + 3 * h * h * s + 6 * h * s
     once = r * d * s + B * K * d * s + B * K * 4
     total = K * per_pos + K * per_gru + once
     if store_logits:
@@ -48,12 +54,14 @@ def logical_bytes(sh, B, store_logits=False, fold=False, lbase_bytes=4):
     return total, K * (V * r * s + B * V * lbase_bytes)
 
 
-def algorithmic_flops(sh, B, fold=False):
+def algorithmic_flops(sh, B, fold=False, markov=False):
     """Useful FLOPs of one call (the matrix-core path computes W2 and the state dot
     products twice, on bf16 hi and lo parts; that is not counted).  Returns
     (W2 only, all contractions: W2 + W1 + GRU)."""
     K, V, r, h, d = sh.K, sh.V, sh.r, sh.h, sh.d
     w2 = 2 * B * r * V * K
+    if markov:  # only the H columns of W1; the state part is a table gather
+        return w2, w2 + 2 * B * r * d * K
     w1 = 2 * B * r * (d + h) * K
     gru = 2 * B * 3 * h * h * K + (0 if fold else 2 * B * 3 * h * d * K)
     return w2, w2 + w1 + gru
@@ -89,14 +97,15 @@ def measured_traffic(workload, exec_name, fold, w2_on_chip):
     return None
 
 
-def cpu_baseline(w, inp, budget_s):
+def cpu_baseline(w, inp, budget_s, markov=False):
     """The fp64 oracle as it stands, on this host's cores, on row 0 of the workload."""
     import oracle
 
     n = 0
     t0 = time.perf_counter()
     while True:
-        oracle.draft(w, inp.H[:1], inp.L_base[:1], inp.last_tok[:1], want_logits=False, want_state=False)
+        oracle.draft(w, inp.H[:1], inp.L_base[:1], inp.last_tok[:1], want_logits=False, want_state=False,
+                     markov=markov)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -226,6 +235,8 @@ def main():
                     help="capture one draft call in a HIP graph (torch.cuda.CUDAGraph) and replay it per step")
     ap.add_argument("--lbase-bf16", action="store_true",
                     help="L_base given as bfloat16 (DOMINO_LBASE_BF16): the workload's base logits rounded to bf16")
+    ap.add_argument("--markov", action="store_true",
+                    help="the Markov head (each position conditioned on the preceding token alone)")
     ap.add_argument("--verify", action="store_true",
                     help="time the greedy verify step (domino_verify) on the workload's B, K and V instead")
     ap.add_argument("--cold-calls", type=int, default=20,
@@ -256,13 +267,13 @@ def main():
                                                                       sh.wdtype))
     w, inp = ds.make_workload(wl.name)
     mode = {"auto": dca.EXEC_AUTO, "persistent": dca.EXEC_PERSISTENT, "stepwise": dca.EXEC_STEPWISE}[args.mode]
-    fold = not args.no_fold
+    fold = not args.no_fold and not args.markov
     t_create = time.perf_counter()
     head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B,
                           exec_mode=mode | (dca.EXEC_STREAM_W2 if args.stream_w2 else 0) |
                           (dca.EXEC_PLAIN_LAUNCH if args.plain_launch else 0) |
                           (dca.EXEC_POSITION_BATCHED if args.position_batched else 0), fold_embedding=fold,
-                          lbase_bf16=args.lbase_bf16)
+                          lbase_bf16=args.lbase_bf16, markov=args.markov)
     torch.cuda.synchronize()
     t_create = time.perf_counter() - t_create
     H = dca.device_tensor(inp.H)
@@ -342,18 +353,19 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     blocks_per_s = wl.B * args.steps / wall
 
-    total_bytes, w2l_bytes = logical_bytes(sh, wl.B, args.store_logits, fold, 2 if args.lbase_bf16 else 4)
+    total_bytes, w2l_bytes = logical_bytes(sh, wl.B, args.store_logits, fold, 2 if args.lbase_bf16 else 4,
+                                           args.markov)
     achieved = total_bytes / (avg_ms * 1e-3) / 1e9
     w2l = w2l_bytes / (avg_ms * 1e-3) / 1e9
     w2_on_chip = info["w2_resident"]
-    traffic = (measured_traffic(wl.name, exec_name, fold, w2_on_chip)
+    traffic = (measured_traffic(wl.name + ("_markov" if args.markov else ""), exec_name, fold, w2_on_chip)
                if exec_name == "persistent" and not args.lbase_bf16 and not args.teacher else None)
     if exec_name == "persistent":
-        kname = "k_persistent_res" if w2_on_chip else "k_persistent"
+        kname = ("k_markov_res" if args.markov else "k_persistent_res") if w2_on_chip else "k_persistent"
     else:
         kname = "stepwise launches (whole call)"
 
-    f_w2, f_all = algorithmic_flops(sh, wl.B, fold)
+    f_w2, f_all = algorithmic_flops(sh, wl.B, fold, args.markov)
     mfma = {"w2_tflops": f_w2 / (avg_ms * 1e-3) / 1e12, "all_tflops": f_all / (avg_ms * 1e-3) / 1e12,
             "peak_tflops": MFMA_PEAK_TFLOPS}
     mfma["w2_frac"] = mfma["w2_tflops"] / MFMA_PEAK_TFLOPS
@@ -362,10 +374,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         eprint("bench: timing the fp64 oracle on the host (cpu_baseline)")
-        n, el, threads = cpu_baseline(w, inp, args.cpu_budget)
+        n, el, threads = cpu_baseline(w, inp, args.cpu_budget, args.markov)
         cpu = {"value": n / el, "unit": "blocks/s", "cores": threads, "kind": "oracle",
-               "sample": "%d block draft(s) of row 0 of %s (free running, K=%d, V=%d), fp64 C oracle" % (
-                   n, wl.name, sh.K, sh.V)}
+               "sample": "%d block draft(s) of row 0 of %s (free running, K=%d, V=%d%s), fp64 C oracle" % (
+                   n, wl.name, sh.K, sh.V, ", Markov head" if args.markov else "")}
 
     rec = {
         "metric": "Domino-head draft blocks/sec (16 tok, V=151936) + achieved HBM GB/s at 1 GPU",
@@ -385,6 +397,7 @@ def main():
                    "fold_embedding": fold, "w2_on_chip": w2_on_chip,
                    "launch": "plain" if args.plain_launch else "cooperative", "create_s": t_create,
                    "teacher_forced": bool(args.teacher), "lbase_dtype": "bf16" if args.lbase_bf16 else "f32",
+                   "head": "markov" if args.markov else "recurrent (GRU)",
                    "hip_graph": bool(args.graph),
                    "kernel_avg_us": avg_ms * 1e3, "warm_us_per_call_median": float(np.median(per_call_ms)) * 1e3,
                    "cold_us_per_call_median": cold_us, "w2_lbase_GBps": w2l,

@@ -26,6 +26,7 @@ EXEC_STREAM_W2 = 8
 EXEC_PLAIN_LAUNCH = 16
 EXEC_POSITION_BATCHED = 32
 LBASE_BF16 = 64
+MARKOV = 128
 FLAG_BAD_TOKEN = 1
 FLAG_SYNC_TIMEOUT = 2
 
@@ -106,13 +107,17 @@ class DominoHead:
     fold_embedding: precompute the folded input-gate table P = E W_ih^T + b_ih ([V, 3h] float32 in the
     workspace) once, so each GRU step gathers a row of P instead of a W_ih matrix-vector product.
 
+    markov: the Markov head (DOMINO_MARKOV): each position's state is the GRU step on the preceding
+    token from the zero state, S_p = GRU(E[x_p], 0), gathered from a per-token table filled at create.
+    Such a head takes no S_init and returns no S (``want_state`` then gives u only).
+
     weights: dict with W1 [r,d+h], W2 [V,r], W_ih [3h,d], W_hh [3h,h], b_ih/b_hh [3h] (or None) and
     E [V,d], all contiguous CUDA tensors of one dtype (float32 or bfloat16).  The tensors must stay
     alive and unmodified while the head exists (the object keeps references).
     """
 
     def __init__(self, weights: dict, K: int = 16, max_batch: int = 1, exec_mode: int = EXEC_AUTO,
-                 fold_embedding: bool = False, lbase_bf16: bool = False):
+                 fold_embedding: bool = False, lbase_bf16: bool = False, markov: bool = False):
         lib = load_library()
         W1 = weights["W1"]
         wdtype = DOMINO_F32 if W1.dtype == torch.float32 else DOMINO_BF16
@@ -134,7 +139,9 @@ class DominoHead:
         self.wdtype = wdtype
         self._weights = dict(weights)
         self.lbase_dtype = torch.bfloat16 if lbase_bf16 else torch.float32
-        flags = exec_mode | (FOLD_EMBED if fold_embedding else 0) | (LBASE_BF16 if lbase_bf16 else 0)
+        self.markov = markov
+        flags = (exec_mode | (FOLD_EMBED if fold_embedding else 0) | (LBASE_BF16 if lbase_bf16 else 0) |
+                 (MARKOV if markov else 0))
         self.cfg = Config(d, h, r, V, K, max_batch, wdtype, flags, _ptr(W1), _ptr(weights["W2"]),
                           _ptr(weights["W_ih"]), _ptr(weights["W_hh"]), _ptr(weights.get("b_ih")),
                           _ptr(weights.get("b_hh")), _ptr(weights["E"]))
@@ -177,7 +184,7 @@ class DominoHead:
         if want_logits and "L_final" not in out:
             out["L_final"] = torch.empty((B, self.K, self.V), dtype=torch.float32, device=dev)
         if want_state:
-            if "S" not in out:
+            if "S" not in out and not self.markov:
                 out["S"] = torch.empty((B, self.K, self.h), dtype=torch.float32, device=dev)
             if "u" not in out:
                 out["u"] = torch.empty((B, self.K, self.r), dtype=torch.float32, device=dev)

@@ -10,6 +10,7 @@ struct Params {
     int d, h, r, V, K, B, maxB;
     const void *W1, *W2, *W_ih, *W_hh, *b_ih, *b_hh, *E;
     const float *P;  // folded input-gate table [V, 3h] or nullptr
+    const float *M;  // Markov head: per-token table [V, r] = W1_S GRU(E[t], 0), or nullptr (recurrent head)
     const void *H;
     const void *L_base;  // [B, K, V] float32, or bfloat16 bits when lbase_bf16
     const int *last_tok, *teacher;

@@ -105,6 +105,18 @@ __device__ inline int gru_input_token(const Params &p, int q, int b, const int *
     return tok_ok(t, p.V) ? t : 0;
 }
 
+// Markov head (news.sig.ai article, section 从Domino看DSpark, names it beside
+// the recurrent head without a formula).  Reading: position q is conditioned on
+// the token before it alone, S_q = GRU(E[x_q], 0), so W1_S S_q is row x_q of
+// the per-token table M = W1_S GRU(E[t], 0) filled at create, and
+//   u_q = SiLU(A_H[q] + M[x_q]).
+// `ah` is A_H[b][q][m]; x a valid token id (gru_input_token clamps).
+__device__ inline float markov_u(const Params &p, float ah, int m, int x)
+{
+    const float a = ah + p.M[static_cast<size_t>(x) * p.r + m];
+    return a * sigmoidf_(a);
+}
+
 // Publish tokens[:, pos] once position pos is complete (one block).
 __device__ inline void write_tokens(const Params &p, int pos)
 {
@@ -1009,10 +1021,13 @@ __device__ inline void w2_key(float w, float lbv, float *lf, int v0, int row, bo
 // of this position (tag `tag`) did not all arrive within the spin limit.
 // NB: largest batch the instantiation handles (B <= NB <= BC); per-row
 // registers are sized by it.
+// u_src (LDS, [nb][r] floats, or nullptr): the block computed u itself (Markov
+// head); the operand is then formed from it with the same hi/lo split.
 template <int RT, int KS, int NB>
 __device__ __forceinline__ bool phase_w2_resident(const Params &p, int blk, int nblk, int pos, float *smem,
                                                   const W2Resident<RT, KS> &res, const uint4 *tl,
-                                                  uint64_t *local_keys, unsigned tag)
+                                                  uint64_t *local_keys, unsigned tag,
+                                                  const float *u_src = nullptr)
 {
     static_assert(NB >= 1 && NB <= BC, "batch rows of one persistent launch");
     const int r = 32 * KS;
@@ -1035,7 +1050,30 @@ __device__ __forceinline__ bool phase_w2_resident(const Params &p, int blk, int 
     // every word carries this position's tag
     uint4 bop[KS];
     int ok = 1;
-    {
+    if (u_src) {
+        const int b = col & 7;
+        const bool hi = col < 8;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            uint32_t hv[8];
+            if (b < nb) {
+                const float4 x0 = *reinterpret_cast<const float4 *>(u_src + b * r + kk * 32 + (lane >> 4) * 8);
+                const float4 x1 = *reinterpret_cast<const float4 *>(u_src + b * r + kk * 32 + (lane >> 4) * 8 + 4);
+                const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const uint32_t xh = bf16_rne_bits(x[jj]);
+                    hv[jj] = hi ? xh : bf16_rne_bits(x[jj] - __uint_as_float(xh << 16));
+                }
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj)
+                    hv[jj] = 0u;
+            }
+            bop[kk] = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
+                                 hv[6] | (hv[7] << 16));
+        }
+    } else {
         const int b = col & 7;
         const uint64_t *src = reinterpret_cast<const uint64_t *>(
             p.utag + (static_cast<size_t>(col >> 3) * p.maxB + b) * r + (lane >> 4) * 8);

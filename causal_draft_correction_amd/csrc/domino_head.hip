@@ -97,6 +97,63 @@ __global__ __launch_bounds__(256) void k_fold(const void *E, const void *W_ih, c
         }
 }
 
+// Markov table, create time, for a chunk of n tokens whose folded gate rows
+// Pc = E W_ih^T + b_ih are given: the zero-state GRU step of each token,
+//   Sc[t][j] = (1 - z) n,  r = sig(g_r + b_hr), z = sig(g_z + b_hz), n = tanh(g_n + r b_hn)
+// (W_hh times the zero state vanishes; the z * 0 term is dropped).
+template <typename WT>
+__global__ __launch_bounds__(256) void k_markov_state(const float *Pc, const void *b_hh, float *Sc, int n, int h)
+{
+    const size_t total = static_cast<size_t>(n) * h;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+         i += static_cast<size_t>(gridDim.x) * 256) {
+        const size_t t = i / h;
+        const int j = static_cast<int>(i % h);
+        const float *g = Pc + t * 3 * h;
+        const float br = b_hh ? WT16<WT>::one(b_hh, j) : 0.f;
+        const float bz = b_hh ? WT16<WT>::one(b_hh, h + j) : 0.f;
+        const float bn = b_hh ? WT16<WT>::one(b_hh, 2 * h + j) : 0.f;
+        const float rg = sigmoidf_(g[j] + br);
+        const float zg = sigmoidf_(g[h + j] + bz);
+        const float ng = tanhf(g[2 * h + j] + rg * bn);
+        Sc[i] = (1.f - zg) * ng;
+    }
+}
+
+// Create time: the state columns of W1 as a contiguous float32 [r, h] matrix.
+template <typename WT>
+__global__ __launch_bounds__(256) void k_w1s_widen(const void *W1, float *W1S, int r, int d, int h)
+{
+    const size_t total = static_cast<size_t>(r) * h;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+         i += static_cast<size_t>(gridDim.x) * 256)
+        W1S[i] = WT16<WT>::one(W1, (i / h) * (d + h) + d + i % h);
+}
+
+// Markov head, step launches: u of position q (q >= 0, into u_buf for the W2
+// launch that follows) or of every position (q < 0, teacher forcing), from A_H
+// and the table row of the preceding token (markov_u); also into u_out when
+// given.  With q >= 1, block 0 first publishes tokens[:, q-1].
+__global__ __launch_bounds__(NT) void k_markov_u(Params p, int q)
+{
+    if (q >= 1 && blockIdx.x == 0)
+        write_tokens(p, q - 1);
+    const int r = p.r, nq = q < 0 ? p.K : 1;
+    const size_t total = static_cast<size_t>(p.B) * nq * r;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * NT + threadIdx.x; i < total;
+         i += static_cast<size_t>(gridDim.x) * NT) {
+        const int m = static_cast<int>(i % r);
+        const int bq = static_cast<int>(i / r);
+        const int b = bq / nq, qq = q < 0 ? bq % nq : q;
+        const size_t o = (static_cast<size_t>(b) * p.K + qq) * r + m;
+        const float u = markov_u(p, xld(&p.A_H[o]), m, gru_input_token(p, qq, b));
+        if (q >= 0)
+            p.u_buf[static_cast<size_t>(b) * r + m] = u;
+        if (p.u_out)
+            p.u_out[o] = u;
+    }
+}
+
 // Whole block draft in one cooperative launch.  Barriers per call:
 // 2 + K + (K - 1) with the folded table, 2 + K + 2 (K - 1) without.  The
 // barrier after each W2 phase also reduces the greedy argmax.
@@ -167,6 +224,8 @@ __global__ __launch_bounds__(NT) void k_step_prologue(Params p)
         prologue_bookkeeping(p);
     if (!p.ah_external)
         phase_ah<WT>(p, blockIdx.x, gridDim.x, smem);
+    if (p.M)
+        return;  // Markov head: no recurrent state
     phase_q_init<WT>(p, blockIdx.x, gridDim.x);
     if (!p.P)
         phase_g<WT>(p, blockIdx.x, gridDim.x, 0, smem);
@@ -280,8 +339,13 @@ constexpr int W2_STEP_ROWS = 128;  // vocabulary rows per block in stepwise W2 l
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, u_all, utag, s_hl, q_buf, g_buf, P, total;
+    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, u_all, utag, s_hl, q_buf, g_buf, P, M, mk_tmp, total;
 };
+
+// Markov table fill: tokens per chunk (create-time region: folded gate rows and
+// zero-state GRU rows of one chunk, plus W1_S as float32)
+constexpr int MARKOV_CHUNK = 8192;
+int markov_chunk(const domino_head_config &c) { return std::min(c.V, MARKOV_CHUNK); }
 
 Layout layout_of(const domino_head_config &c)
 {
@@ -314,6 +378,14 @@ Layout layout_of(const domino_head_config &c)
     L.P = off;
     if (c.flags & DOMINO_FOLD_EMBED)
         off = align_up(off + sizeof(float) * static_cast<size_t>(c.V) * 3 * c.h);
+    L.M = off;
+    L.mk_tmp = off;
+    if (c.flags & DOMINO_MARKOV) {
+        off = align_up(off + sizeof(float) * static_cast<size_t>(c.V) * c.r);
+        L.mk_tmp = off;
+        const size_t ch = static_cast<size_t>(markov_chunk(c));
+        off = align_up(off + sizeof(float) * (ch * 3 * c.h + ch * c.h + static_cast<size_t>(c.r) * c.h));
+    }
     L.total = off;
     return L;
 }
@@ -348,8 +420,10 @@ int validate_config(const domino_head_config *c)
             return fail(DOMINO_EINVAL, "%s is not 16-byte aligned", names[i]);
     }
     if (c->flags & ~(DOMINO_EXEC_PERSISTENT | DOMINO_EXEC_STEPWISE | DOMINO_FOLD_EMBED | DOMINO_EXEC_STREAM_W2 |
-                     DOMINO_EXEC_PLAIN_LAUNCH | DOMINO_EXEC_POSITION_BATCHED | DOMINO_LBASE_BF16))
+                     DOMINO_EXEC_PLAIN_LAUNCH | DOMINO_EXEC_POSITION_BATCHED | DOMINO_LBASE_BF16 | DOMINO_MARKOV))
         return fail(DOMINO_EINVAL, "unknown flags 0x%x", c->flags);
+    if ((c->flags & DOMINO_MARKOV) && (c->flags & (DOMINO_FOLD_EMBED | DOMINO_EXEC_STREAM_W2)))
+        return fail(DOMINO_EINVAL, "DOMINO_MARKOV does not combine with DOMINO_FOLD_EMBED or DOMINO_EXEC_STREAM_W2");
     if ((c->flags & DOMINO_EXEC_PERSISTENT) && (c->flags & DOMINO_EXEC_STEPWISE))
         return fail(DOMINO_EINVAL, "flags ask for both persistent and stepwise execution");
     return DOMINO_OK;
@@ -369,11 +443,40 @@ hipError_t launch_fold(const domino_head_config &c, float *P)
     return e != hipSuccess ? e : hipStreamSynchronize(nullptr);
 }
 
+// Markov table M = W1_S GRU(E[t], 0) for every token, in chunks of tokens:
+// folded gate rows (k_fold), zero-state GRU rows (k_markov_state), then the
+// product with W1_S (k_fold on float32 operands, no bias).  Null stream, waited for.
+template <typename WT>
+hipError_t launch_markov(const domino_head_config &c, float *M, float *tmp)
+{
+    const int ch = markov_chunk(c), h = c.h, n3 = 3 * c.h;
+    float *Pc = tmp;
+    float *Sc = Pc + static_cast<size_t>(ch) * n3;
+    float *W1S = Sc + static_cast<size_t>(ch) * h;
+    const size_t esz = c.wdtype == DOMINO_BF16 ? 2 : 4;
+    hipLaunchKernelGGL(k_w1s_widen<WT>, dim3(256), dim3(256), 0, nullptr, c.W1, W1S, c.r, c.d, h);
+    hipError_t e = hipGetLastError();
+    for (int t0 = 0; t0 < c.V && e == hipSuccess; t0 += ch) {
+        const int n = std::min(ch, c.V - t0);
+        const void *Et = static_cast<const char *>(c.E) + static_cast<size_t>(t0) * c.d * esz;
+        hipLaunchKernelGGL(k_fold<WT>, dim3((n3 + 63) / 64, (n + 63) / 64), dim3(256), 0, nullptr, Et, c.W_ih, c.b_ih,
+                           Pc, n, c.d, n3);
+        hipLaunchKernelGGL(k_markov_state<WT>, dim3(1024), dim3(256), 0, nullptr, Pc, c.b_hh, Sc, n, h);
+        hipLaunchKernelGGL(k_fold<float>, dim3((c.r + 63) / 64, (n + 63) / 64), dim3(256), 0, nullptr, Sc, W1S,
+                           nullptr, M + static_cast<size_t>(t0) * c.r, n, h, c.r);
+        e = hipGetLastError();
+    }
+    return e != hipSuccess ? e : hipStreamSynchronize(nullptr);
+}
+
+typedef hipError_t (*MarkovLaunch)(const domino_head_config &c, float *M, float *tmp);
+
 struct Kernels {
     const void *persistent;
     const void *w2;
     const void *prologue, *state, *g;
     FoldLaunch fold;
+    MarkovLaunch markov;
 };
 
 template <typename WT, int LPR, int NL>
@@ -383,7 +486,7 @@ Kernels kernels_for()
                    reinterpret_cast<const void *>(&k_step_w2<WT, LPR, NL>),
                    reinterpret_cast<const void *>(&k_step_prologue<WT>),
                    reinterpret_cast<const void *>(&k_step_state<WT>), reinterpret_cast<const void *>(&k_step_g<WT>),
-                   &launch_fold<WT>};
+                   &launch_fold<WT>, &launch_markov<WT>};
 }
 
 template <typename WT>
@@ -433,6 +536,15 @@ struct domino_head {
 static bool choose_launch(const domino_head *hd, int B, bool *persistent, bool *resident)
 {
     const unsigned fl = hd->cfg.flags;
+    if (fl & DOMINO_MARKOV) {
+        // a Markov head takes its resident-W2 kernel (bf16, r = 256, B <= 8) or the step launches
+        const bool can = hd->res_grid > 0 && B <= BC;
+        const bool pers = (fl & DOMINO_EXEC_PERSISTENT) ? true : (fl & DOMINO_EXEC_STEPWISE) ? false : can;
+        if (pers && !can)
+            return false;
+        *persistent = *resident = pers;
+        return true;
+    }
     bool pers = (fl & DOMINO_EXEC_PERSISTENT) ? true : (fl & DOMINO_EXEC_STEPWISE) ? false : B <= BC;
     if (pers && (hd->persist_grid == 0 || B > BC)) {
         if (fl & DOMINO_EXEC_PERSISTENT)
@@ -503,6 +615,11 @@ int domino_head_create(const domino_head_config *cfg, void *workspace, size_t wo
         // one-time table P = E W_ih^T + b_ih on the null stream, waited for here
         HIP_TRY(kern.fold(*cfg, reinterpret_cast<float *>(static_cast<char *>(workspace) + L.P)), "folded gate table");
     }
+    if (cfg->flags & DOMINO_MARKOV) {
+        HIP_TRY(kern.markov(*cfg, reinterpret_cast<float *>(static_cast<char *>(workspace) + L.M),
+                            reinterpret_cast<float *>(static_cast<char *>(workspace) + L.mk_tmp)),
+                "Markov table");
+    }
     domino_head *hd = new domino_head{};
     hd->cfg = *cfg;
     hd->ws = static_cast<char *>(workspace);
@@ -536,7 +653,8 @@ int domino_head_create(const domino_head_config *cfg, void *workspace, size_t wo
         bool fits = hd->res_smem + 1024 <= static_cast<size_t>(lds_max);
         for (int b : {1, BC}) {
             int per_cu_r = 0;
-            hipError_t er = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_r, dhres::kernel(b), dhres::threads(),
+            const void *fn = (cfg->flags & DOMINO_MARKOV) ? dhres::markov_kernel(b) : dhres::kernel(b);
+            hipError_t er = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_r, fn, dhres::threads(),
                                                                          hd->res_smem);
             fits = fits && er == hipSuccess && per_cu_r >= 1;
         }
@@ -571,6 +689,7 @@ static Params make_params(domino_head_t hd, int B, const void *H, const void *L_
     p.b_hh = c.b_hh;
     p.E = c.E;
     p.P = (c.flags & DOMINO_FOLD_EMBED) ? reinterpret_cast<const float *>(hd->ws + hd->L.P) : nullptr;
+    p.M = (c.flags & DOMINO_MARKOV) ? reinterpret_cast<const float *>(hd->ws + hd->L.M) : nullptr;
     p.H = H;
     p.L_base = L_base;
     p.lbase_bf16 = (hd->cfg.flags & DOMINO_LBASE_BF16) ? 1 : 0;
@@ -617,6 +736,9 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
     for (int i = 0; i < 5; ++i)
         if (opt[i] && !aligned16(opt[i]))
             return fail(DOMINO_EINVAL, "%s is not 16-byte aligned", opt_names[i]);
+    const bool markov = (c.flags & DOMINO_MARKOV) != 0;
+    if (markov && (S_init || S_out))
+        return fail(DOMINO_EINVAL, "a Markov head has no recurrent state: S_init and S_out must be NULL");
     int dev = -1;
     HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
     if (dev != hd->device)
@@ -637,12 +759,12 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
         hd->state_ready = true;
     }
     Params p = make_params(hd, B, H, L_base, last_tok, teacher, S_init, tokens, L_final, S_out, u_out, persistent);
-    if (resident)
+    if (resident && !markov)
         p.utag = reinterpret_cast<uint32_t *>(hd->ws + hd->L.utag);
     hd->last_stream = st;
     if (persistent) {
         void *args[] = {&p};
-        const void *fn = resident ? dhres::kernel(B) : hd->kern.persistent;
+        const void *fn = resident ? (markov ? dhres::markov_kernel(B) : dhres::kernel(B)) : hd->kern.persistent;
         const dim3 grid(resident ? hd->res_grid : hd->persist_grid);
         const dim3 block(resident ? dhres::threads() : NT);
         const unsigned smem = static_cast<unsigned>(resident ? hd->res_smem : hd->persist_smem);
@@ -687,17 +809,6 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
                                 st),
                 "launch A_H (matrix cores)");
     }
-    {
-        void *args[] = {&p};
-        // with A_H from its own launch the prologue only covers the 3h rows of q_0 (and g_0)
-        const int g = ah_mfma ? (h3 + NWAVE - 1) / NWAVE : g_pro;
-        HIP_TRY(hipLaunchKernel(hd->kern.prologue, dim3(g), dim3(NT), args, sm_small, st), "launch prologue");
-        int q = 0;
-        void *sargs[] = {&p, &q};
-        HIP_TRY(hipLaunchKernel(reinterpret_cast<const void *>(&k_step_update), dim3(g_upd), dim3(NT), sargs,
-                                sm_small, st), "launch update");
-        HIP_TRY(launch_state(sargs), "launch state");
-    }
     // bf16 heads with r = 256 take the matrix-core W2 kernel
     const bool w2_mfma = c.wdtype == DOMINO_BF16 && c.r == dhbat::r_supported();
     auto launch_w2 = [&](Params &pw, int rows, int pos) -> hipError_t {
@@ -709,17 +820,51 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
                                    dim3(dhbat::w2_threads(rows)), margs, dhbat::w2_smem(), st);
         return hipLaunchKernel(hd->kern.w2, dim3(g_w2), dim3(NT), args, sm_w2, st);
     };
-    for (int pos = 0; pos < c.K; ++pos) {
-        if (!pos_batched)
-            HIP_TRY(launch_w2(p, B, pos), "launch w2");
-        if (pos + 1 < c.K) {
-            int q = pos + 1;
-            void *gargs[] = {&p, &q};
-            if (!p.P)
-                HIP_TRY(hipLaunchKernel(hd->kern.g, dim3(g_g), dim3(NT), gargs, sm_small, st), "launch g");
-            HIP_TRY(hipLaunchKernel(reinterpret_cast<const void *>(&k_step_update), dim3(g_upd), dim3(NT), gargs,
-                                    sm_small, st), "launch update");
-            HIP_TRY(launch_state(gargs), "launch state");
+    if (markov) {
+        // Markov head: the prologue (A_H unless computed above, key clearing), then per
+        // position the u launch (table gather) and the W2 launch; with a teacher, u of
+        // every position in one launch and the position-batched W2 launch
+        void *args[] = {&p};
+        HIP_TRY(hipLaunchKernel(hd->kern.prologue, dim3(ah_mfma ? 1 : B * c.r), dim3(NT), args, sm_small, st),
+                "launch prologue");
+        const int nu = pos_batched ? B * c.K * c.r : B * c.r;
+        const dim3 gu(std::min((nu + NT - 1) / NT, 2048));
+        if (pos_batched) {
+            int q = -1;
+            void *uargs[] = {&p, &q};
+            HIP_TRY(hipLaunchKernel(reinterpret_cast<const void *>(&k_markov_u), gu, dim3(NT), uargs, 0, st),
+                    "launch Markov u (all positions)");
+        } else {
+            for (int pos = 0; pos < c.K; ++pos) {
+                int q = pos;
+                void *uargs[] = {&p, &q};
+                HIP_TRY(hipLaunchKernel(reinterpret_cast<const void *>(&k_markov_u), gu, dim3(NT), uargs, 0, st),
+                        "launch Markov u");
+                HIP_TRY(launch_w2(p, B, pos), "launch w2");
+            }
+        }
+    } else {
+        void *args[] = {&p};
+        // with A_H from its own launch the prologue only covers the 3h rows of q_0 (and g_0)
+        const int g = ah_mfma ? (h3 + NWAVE - 1) / NWAVE : g_pro;
+        HIP_TRY(hipLaunchKernel(hd->kern.prologue, dim3(g), dim3(NT), args, sm_small, st), "launch prologue");
+        int q = 0;
+        void *sargs[] = {&p, &q};
+        HIP_TRY(hipLaunchKernel(reinterpret_cast<const void *>(&k_step_update), dim3(g_upd), dim3(NT), sargs,
+                                sm_small, st), "launch update");
+        HIP_TRY(launch_state(sargs), "launch state");
+        for (int pos = 0; pos < c.K; ++pos) {
+            if (!pos_batched)
+                HIP_TRY(launch_w2(p, B, pos), "launch w2");
+            if (pos + 1 < c.K) {
+                int q = pos + 1;
+                void *gargs[] = {&p, &q};
+                if (!p.P)
+                    HIP_TRY(hipLaunchKernel(hd->kern.g, dim3(g_g), dim3(NT), gargs, sm_small, st), "launch g");
+                HIP_TRY(hipLaunchKernel(reinterpret_cast<const void *>(&k_step_update), dim3(g_upd), dim3(NT), gargs,
+                                        sm_small, st), "launch update");
+                HIP_TRY(launch_state(gargs), "launch state");
+            }
         }
     }
     if (pos_batched) {

@@ -101,6 +101,81 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
 }
 
 
+// Markov head (markov_u): the same resident-W2 draft with the state phase
+// replaced by a table gather.  Every block forms u of every batch row itself
+// from A_H and the table row of the preceding token, so no value crosses
+// blocks between the argmax barrier and the W2 phase; the only exchange per
+// position is the argmax barrier.  The prologue computes A_H over the grid and
+// ends with one grid barrier (the W2 slice load overlaps it).
+template <int RT, int KS, int NB>
+__global__ __launch_bounds__(NT) void k_markov_res(Params p)
+{
+    extern __shared__ float smem[];
+    const int blk = blockIdx.x, nblk = gridDim.x;
+    // LDS as in k_persistent_res (the tiles beyond the register share at the same
+    // offset); the state regions are unused
+    float *S_lds = smem + smem_off_S(p.r, lbuf_stride(p.V, nblk));
+    float *cache = S_lds + BC * p.h;
+    uint4 *tl = reinterpret_cast<uint4 *>(cache + state_cache_floats(p.r, p.h, p.K, nblk, 2));
+    float *u_lds = smem + smem_off_u();  // [BC][r]
+    int *atok = reinterpret_cast<int *>(smem + smem_off_tok()) + ATOK_OFF;
+    int *bad = atok + BC;
+    uint64_t *local_keys = reinterpret_cast<uint64_t *>(smem);
+    const int r = p.r;
+    unsigned gen = barrier_gen_init(p.bar);
+    block_fail_init();
+    if (blk == 0) {
+        prologue_bookkeeping(p);
+        if (threadIdx.x < p.B)
+            bad[threadIdx.x] = row_bad(p, threadIdx.x) ? 1 : 0;
+    }
+    W2Resident<RT, KS> res;
+    phase_ah<bf16s>(p, blk, nblk, smem);
+    lbase_to_lds(p, blk, nblk, 0, smem);
+    w2_resident_load<RT, KS>(p, blk, nblk, res, tl);
+    if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+        return;
+    // thread m < r forms u[b][m]; its A_H entries of the coming position are
+    // loaded one position ahead (during the argmax barrier wait)
+    const int m = threadIdx.x;
+    float ah[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        ah[b] = (b < p.B && m < r) ? xld(&p.A_H[static_cast<size_t>(b) * p.K * r + m]) : 0.f;
+    for (int pos = 0; pos < p.K; ++pos) {
+        Params pl = p;
+        asm volatile("" : "+s"(pl.asy), "+s"(pl.tokens), "+s"(pl.L_final), "+s"(pl.u_out), "+s"(pl.L_base),
+                          "+s"(pl.M));
+        if (m < r) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (b < pl.B) {
+                    const float u = markov_u(pl, ah[b], m, gru_input_token(pl, pos, b, atok));
+                    u_lds[b * r + m] = u;
+                    if (blk == 0 && pl.u_out)
+                        pl.u_out[(static_cast<size_t>(b) * pl.K + pos) * r + m] = u;
+                }
+            }
+        }
+        __syncthreads();
+        if (!phase_w2_resident<RT, KS, NB>(pl, blk, nblk, pos, smem, res, tl, local_keys, 0u, u_lds))
+            return;
+        argmax_arrive(pl.asy, gen, local_keys, pl.B);
+        if (pos + 1 < pl.K) {
+            lbase_to_lds(pl, blk, nblk, pos + 1, smem);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                if (b < pl.B && m < r)
+                    ah[b] = xld(&pl.A_H[(static_cast<size_t>(b) * pl.K + pos + 1) * r + m]);
+        }
+        if (!argmax_wait(pl.asy, gen, pl.B, atok, pl.spin_limit, pl.flags))
+            return;
+        if (blk == 0 && threadIdx.x < pl.B)
+            pl.tokens[static_cast<size_t>(threadIdx.x) * pl.K + pos] = bad[threadIdx.x] ? -1 : atok[threadIdx.x];
+    }
+    barrier_finish(p.bar, gen);
+}
+
 constexpr int RES_RT = 10;  // W2 tiles per wave kept in registers (4 waves x 10 x 16 rows = 640 rows; the rest in LDS)
 constexpr int RES_KS = 8;   // 32-wide steps of r: r = 256
 
@@ -117,6 +192,12 @@ const void *kernel(int B)
 {
     return B <= 1 ? reinterpret_cast<const void *>(&k_persistent_res<RES_RT, RES_KS, 1>)
                   : reinterpret_cast<const void *>(&k_persistent_res<RES_RT, RES_KS, BC>);
+}
+// the Markov head's kernel (same LDS size and grid)
+const void *markov_kernel(int B)
+{
+    return B <= 1 ? reinterpret_cast<const void *>(&k_markov_res<RES_RT, RES_KS, 1>)
+                  : reinterpret_cast<const void *>(&k_markov_res<RES_RT, RES_KS, BC>);
 }
 
 size_t smem_bytes(int r, int h, int K, int V, int nblk)

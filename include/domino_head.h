@@ -85,6 +85,20 @@ extern "C" {
                                       at large B.  Every path widens each value exactly, so the draft
                                       equals a float32 call on the widened values bit for bit */
 
+/* ---- config.flags bit that changes the model ---- */
+#define DOMINO_MARKOV 128u            /* Markov head instead of the recurrent one.  The news.sig.ai
+                                      article (section 从Domino看DSpark) names a Markov head, DSpark's
+                                      default, beside an RNN head that corresponds to Domino's causal
+                                      encoder, and gives no formula.  Reading taken: each position is
+                                      conditioned on the token before it alone, S_p = GRU(E[x_p], 0)
+                                      with x_0 = last_tok and x_p = t_{p-1} (or teacher[p-1]), so
+                                      W1_S S_p is a row of the per-token table M = W1_S GRU(E[t], 0)
+                                      ([V, r] float32 in the workspace, filled at create) and
+                                      u_p = SiLU(W1_H H_p + M[x_p]).  The same weights serve both
+                                      heads.  Not combinable with DOMINO_FOLD_EMBED or
+                                      DOMINO_EXEC_STREAM_W2; domino_head_draft then takes no S_init
+                                      and writes no S_out (both must be NULL) */
+
 /*
  * Head configuration.  All weight pointers are DEVICE pointers, borrowed for
  * the lifetime of the handle (never copied, never written), stored in
@@ -112,8 +126,10 @@ int domino_head_workspace_size(const domino_head_config *cfg, size_t *bytes);
 /*
  * Validates cfg and binds the caller-allocated device `workspace` (>=
  * domino_head_workspace_size bytes, 256-byte aligned, not shared with another
- * handle).  No allocation.  Without DOMINO_FOLD_EMBED no device work either;
- * with it, one kernel fills the folded table on the null stream and create
+ * handle).  No allocation.  Without DOMINO_FOLD_EMBED or DOMINO_MARKOV no
+ * device work either; with one of them, kernels fill the folded table (or the
+ * Markov table, in chunks of tokens through a create-time region of the
+ * workspace) on the null stream and create
  * waits for it.  On success *out is a new handle; release it with
  * domino_head_destroy.  The workspace state is cleared by the first draft.
  */

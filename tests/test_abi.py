@@ -66,7 +66,8 @@ def test_workspace_size_accepts_valid_config_and_grows_with_batch():
     (dict(K=0), -1), (dict(K=17), -1), (dict(max_batch=0), -1), (dict(max_batch=1025), -1), (dict(V=0), -1),
     (dict(d=12), -2), (dict(h=20), -2), (dict(r=12), -2), (dict(r=24), -2), (dict(wdtype=7), -2),
     (dict(wdtype=dca.DOMINO_BF16, r=4), -2), (dict(W2=None), -1), (dict(E=8), -1), (dict(flags=3), -1),
-    (dict(flags=128), -1),
+    (dict(flags=256), -1), (dict(flags=dca.MARKOV | dca.FOLD_EMBED), -1),
+    (dict(flags=dca.MARKOV | dca.EXEC_STREAM_W2), -1),
 ])
 def test_config_validation_codes(kw, code):
     rc, _ = ws_size(cfg(**kw))
@@ -80,6 +81,15 @@ def test_fold_flag_adds_the_gate_table_to_the_workspace():
     assert rc == rc2 == 0
     assert folded - plain >= 1000 * 3 * 32 * 4
     assert ws_size(cfg(flags=dca.FOLD_EMBED | dca.EXEC_PERSISTENT))[0] == 0
+
+
+def test_markov_flag_adds_the_token_table_to_the_workspace():
+    """The Markov head's table M [V, r] float32 lives in the workspace, plus a
+    create-time region for one chunk of tokens."""
+    rc, plain = ws_size(cfg(V=1000, h=32, r=16))
+    rc2, mk = ws_size(cfg(V=1000, h=32, r=16, flags=dca.MARKOV))
+    assert rc == rc2 == 0
+    assert mk - plain >= 1000 * 16 * 4 + 1000 * 4 * 32 * 4
 
 
 def test_param_count_closed_form():

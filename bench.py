@@ -70,13 +70,20 @@ def algorithmic_flops(sh, B, fold=False, markov=False):
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
 
-def kernel_source_hash():
-    import glob
+# Sources each timed kernel is compiled from: a counter summary stays valid while these
+# files are unchanged (changes elsewhere in the library do not touch the kernel).
+KERNEL_SOURCES = {
+    "persistent": ["domino_head_res.hip", "dh_resident.h", "dh_phases.h", "dh_common.h", "dh_params.h"],
+    "verify": ["domino_verify.hip", "dh_verify.h", "dh_common.h"],
+}
+
+
+def kernel_source_hash(kind="persistent"):
     import hashlib
 
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "causal_draft_correction_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "causal_draft_correction_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -86,7 +93,7 @@ def measured_traffic(workload, exec_name, fold, w2_on_chip):
     on the current kernel sources, the same workload and the same launch; else None."""
     import glob
 
-    cur = kernel_source_hash()
+    cur = kernel_source_hash("verify" if exec_name == "verify" else "persistent")
     for f in glob.glob(os.path.join(ROOT, "profiles", "*_counters.json")):
         with open(f) as fh:
             d = json.load(fh)

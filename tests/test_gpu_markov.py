@@ -210,3 +210,58 @@ def test_markov_qwen3_8b_b32_sampled_rows(w8b):
     o = oracle.draft(w8b, sub.H, sub.L_base, sub.last_tok, markov=True)
     div = check_free_running(o, g)
     log("markov 8B B=32 sampled rows %s: diverged=%d" % (rows, div))
+
+
+@pytest.mark.parametrize("B,mode", [(1, dca.EXEC_AUTO), (3, dca.EXEC_PERSISTENT | dca.EXEC_PLAIN_LAUNCH),
+                                    (12, dca.EXEC_AUTO)])
+def test_markov_bf16_lbase_and_plain_launch_equal_float32(B, mode):
+    """bf16 base logits are widened exactly on the Markov paths too (resident kernel and
+    matrix-core step launches), and a plain launch equals the cooperative one: the
+    outputs equal a float32, cooperative call on the widened values bit for bit."""
+    sh = ds.HeadShape(d=256, h=128, r=256, V=9001, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 73), gru_sensitive=True)
+    inp = ds.make_inputs(sh, B, (9, 74), sigma=0.5, peak="none")
+    L16 = ds.round_to_bf16_bits(inp.L_base)
+    a, fa = gpu_draft(markov_head(w, B, mode, lbase_bf16=True), inp.H, L16, inp.last_tok)
+    b, fb = gpu_draft(markov_head(w, B), inp.H, ds.bf16_bits_to_f32(L16), inp.last_tok)
+    assert fa == 0 and fb == 0
+    for k in ("tokens", "L_final", "u"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("B,mode", [(3, dca.EXEC_PERSISTENT | dca.EXEC_PLAIN_LAUNCH), (40, dca.EXEC_AUTO)])
+def test_markov_hip_graph_replay_matches_eager(B, mode):
+    """A Markov draft captured in a HIP graph and replayed three times, with eager drafts
+    of other inputs on the same handle in between, equals the eager result bitwise."""
+    sh = ds.HeadShape(d=256, h=64, r=256, V=7001, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 75), gru_sensitive=True)
+    head = markov_head(w, B, mode)
+    inp = ds.make_inputs(sh, B, (9, 76), sigma=0.5, peak="none")
+    other = ds.make_inputs(sh, B, (9, 77), sigma=0.5, peak="none")
+    ref, _ = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
+    H, L, lt = dca.device_tensor(inp.H), dca.device_tensor(inp.L_base), dca.device_tensor(inp.last_tok)
+    Ho, Lo, lto = dca.device_tensor(other.H), dca.device_tensor(other.L_base), dca.device_tensor(other.last_tok)
+    dev = H.device
+    gout = {"tokens": torch.empty((B, 16), dtype=torch.int32, device=dev),
+            "L_final": torch.empty((B, 16, sh.V), dtype=torch.float32, device=dev),
+            "u": torch.empty((B, 16, sh.r), dtype=torch.float32, device=dev)}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            head.draft(H, L, lt, want_logits=True, want_state=True, out=gout)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        head.draft(H, L, lt, want_logits=True, want_state=True, out=gout)
+    for rep in range(3):
+        for k in gout:
+            gout[k].fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ("tokens", "L_final", "u"):
+            assert np.array_equal(gout[k].cpu().numpy(), ref[k]), "replay %d: %s" % (rep, k)
+        eager = head.draft(Ho, Lo, lto, want_logits=True)
+        torch.cuda.synchronize()
+        assert eager["tokens"].shape == (B, 16)
+    assert head.check_error() == 0

@@ -317,7 +317,8 @@ def test_resident_w2_slice_matches_oracle(V, B, fold):
 
 
 # ------------------------------------------------------------------ batched W2 on the matrix cores (r = 256)
-@pytest.mark.parametrize("V,B,fold", [(20011, 9, True), (20011, 40, False), (7001, 130, True)])
+@pytest.mark.parametrize("V,B,fold", [(20011, 9, True), (20011, 40, False), (7001, 130, True), (7001, 128, True),
+                                      (20011, 256, False)])
 def test_batched_w2_matrix_cores_match_oracle(V, B, fold):
     """Stepwise launches of bf16 r = 256 heads run W2 as a matrix-core GEMM (u as bf16
     hi + lo operand rows, fused L_base add and argmax); above 8 rows the state-phase
@@ -333,6 +334,33 @@ def test_batched_w2_matrix_cores_match_oracle(V, B, fold):
     b, _ = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
     for k in ("tokens", "L_final", "S", "u"):
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("B", [40, 128])
+def test_batched_w2_zero_correction_ties_nan_signed_zero(B):
+    """Matrix-core W2 launches (B = 128: W2 streamed into registers; B = 40: staged
+    through LDS) with W2 = 0: L_final equals L_base (up to the sign of zero) and the
+    tokens follow numpy.argmax: the first of equal maxima, the first NaN, -0 == +0, and
+    index 0 for a row of -inf, with specials placed across vocabulary ranges."""
+    sh = ds.HeadShape(d=128, h=64, r=256, V=7001, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 74))
+    w.W2 = np.zeros_like(w.W2)
+    inp = ds.make_inputs(sh, B, (9, 75), sigma=2.0, peak="none")
+    L = inp.L_base.copy()
+    L[0, 1, [5, 6999]] = 100.0       # tie across the first and last vocabulary ranges
+    L[1, 2, :] = -1.0
+    L[1, 2, [3000, 77]] = [-0.0, 0.0]  # -0 == +0: the lower index wins
+    L[2, 3, [4000, 900]] = np.nan      # first NaN wins
+    L[2, 3, 10] = np.inf
+    L[B - 1, 4, :] = -np.inf           # all -inf: index 0
+    L[B - 1, 5, 6000] = np.inf
+    head = make_head(w, B, dca.EXEC_STEPWISE, fold=True)
+    g, flags = gpu_draft(head, inp.H, L, inp.last_tok)
+    assert flags == 0
+    np.testing.assert_array_equal(g["tokens"], np.argmax(L, axis=-1))
+    assert g["tokens"][0, 1] == 5 and g["tokens"][1, 2] == 77 and g["tokens"][2, 3] == 900
+    assert g["tokens"][B - 1, 4] == 0 and g["tokens"][B - 1, 5] == 6000
+    assert np.array_equal(np.nan_to_num(g["L_final"], nan=1e30), np.nan_to_num(L, nan=1e30))
 
 
 @pytest.mark.parametrize("B", [1, 4])
@@ -386,19 +414,21 @@ def test_resident_handle_with_varying_batch():
     compare_free_running(o, a)
 
 
-@pytest.mark.parametrize("wd,V,B", [("bf16", 9001, 3), ("f32", 3001, 2)])
+@pytest.mark.parametrize("wd,V,B", [("bf16", 9001, 3), ("f32", 3001, 2), ("bf16", 9001, 8)])
 def test_position_batched_teacher_forcing_equals_per_position(wd, V, B):
     """With a teacher the step launches run the GRU chain first and then one W2
     launch over all B*K (row, position) pairs.  The products are the same
     instructions on the same operands as per position, so the result equals the
     persistent (per-position) launch bit for bit: matrix-core W2 for the bf16
-    r = 256 head, the VALU W2 kernel for the fp32 head."""
+    r = 256 head (at B = 8 the 128 rows take the kernel that streams W2 into
+    registers), the VALU W2 kernel for the fp32 head."""
     sh = ds.HeadShape(d=1040 if wd == "bf16" else 136, h=64, r=256 if wd == "bf16" else 32, V=V, K=16, wdtype=wd)
     w = ds.make_weights(sh, (9, 90), gru_sensitive=True)
     inp = ds.make_inputs(sh, B, (9, 91), sigma=0.5, peak="none")
     y = ds.uniform_tokens((9, 92), (B, 16), V)
-    a, fa = gpu_draft(make_head(w, 4, dca.EXEC_PERSISTENT, fold=True), inp.H, inp.L_base, inp.last_tok, teacher=y)
-    pb = make_head(w, 4, dca.EXEC_POSITION_BATCHED, fold=True)
+    mb = max(B, 4)
+    a, fa = gpu_draft(make_head(w, mb, dca.EXEC_PERSISTENT, fold=True), inp.H, inp.L_base, inp.last_tok, teacher=y)
+    pb = make_head(w, mb, dca.EXEC_POSITION_BATCHED, fold=True)
     assert pb.exec_info(B)["persistent"]  # exec_info reports the launch without a teacher
     c, fc = gpu_draft(pb, inp.H, inp.L_base, inp.last_tok, teacher=y)
     assert fa == 0 and fc == 0
@@ -437,6 +467,8 @@ BF16_LBASE_CASES = {
     "streamed_w2": ("bf16", 256, 64, 256, 5003, 2, 2, dca.EXEC_PERSISTENT | dca.EXEC_STREAM_W2, True, False),
     "batched_matrix_cores": ("bf16", 256, 64, 256, 20011, 40, 40, dca.EXEC_AUTO, True, False),
     "position_batched": ("bf16", 256, 64, 256, 7001, 9, 9, dca.EXEC_AUTO, True, True),
+    "position_batched_b8": ("bf16", 256, 64, 256, 7001, 8, 8, dca.EXEC_POSITION_BATCHED, True, True),
+    "batched_b128": ("bf16", 256, 64, 256, 7001, 128, 128, dca.EXEC_AUTO, True, False),
     "f32_stepwise": ("f32", 136, 64, 32, 3001, 3, 4, dca.EXEC_STEPWISE, False, False),
     "f32_persistent": ("f32", 136, 64, 32, 3001, 3, 4, dca.EXEC_PERSISTENT, True, False),
 }

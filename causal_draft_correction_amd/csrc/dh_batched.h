@@ -6,8 +6,9 @@
 namespace dhbat {
 int r_supported();         // the rank it is built for
 int threads();             // threads per block
-const void *w2_kernel(int B, bool lbase_bf16);  // k_w2_mfma for B rows (L_base float32 or bf16):
-                                               // arguments (Params, int position, int groups)
+const void *w2_kernel(int B, bool lbase_bf16, bool store_logits);  // k_w2_mfma for B rows (L_base float32
+                                               // or bf16; L_final stored or not): arguments
+                                               // (Params, int position, int groups)
 int w2_groups(int B);           // its third argument
 int w2_threads(int B);     // its threads per block
 size_t w2_smem();          // its dynamic LDS per block

@@ -816,7 +816,8 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
         void *args[] = {&pw, &pos};
         void *margs[] = {&pw, &pos, &groups};
         if (w2_mfma)
-            return hipLaunchKernel(dhbat::w2_kernel(rows, pw.lbase_bf16 != 0), dim3(dhbat::w2_grid(rows, hd->cus)),
+            return hipLaunchKernel(dhbat::w2_kernel(rows, pw.lbase_bf16 != 0, pw.L_final != nullptr),
+                                   dim3(dhbat::w2_grid(rows, hd->cus)),
                                    dim3(dhbat::w2_threads(rows)), margs, dhbat::w2_smem(), st);
         return hipLaunchKernel(hd->kern.w2, dim3(g_w2), dim3(NT), args, sm_w2, st);
     };

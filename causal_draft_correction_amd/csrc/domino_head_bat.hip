@@ -32,12 +32,14 @@ namespace DH_NS {
 // the LDS operand traffic per result); the host uses the first.
 constexpr int XCDS = 8;   // accelerator dies (XCDs) of the MI355X, each with its own L2
 
-template <int KS, int VTG, int AT, int NTH, bool LB16>
-__global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng)
+template <int KS, int VTG, int NVS, int AT, int NTH, bool LB16, bool ST>
+__global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
 {
     static_assert(AT == 2 || AT == 4, "A tiles per wave");
     constexpr int NWV = NTH / 64;
     constexpr int NP = AT / 2;  // A-tile pairs
+    constexpr int ng = NWV / NVS;  // batch groups of a tile (the host passes the same in ng_arg)
+    (void)ng_arg;
     extern __shared__ uint4 wlds[];  // 2 chunk buffers
     const int r = 32 * KS;
     const int B = p.B, V = p.V;
@@ -48,17 +50,18 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng)
     const int xcd = blockIdx.x % XCDS, j = blockIdx.x / XCDS;
     const int bt = j % nbt, vb = (j / nbt) * XCDS + xcd;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15;
-    const int nvs = NWV / ng;
     const int grp = wave % ng, vs = wave / ng;
-    const int CRr = nvs * VTG * 16;  // chunk rows
+    constexpr int CRr = NVS * VTG * 16;  // chunk rows
     const int row0 = bt * 128 + grp * AT * 8;
     const long long v0 = static_cast<long long>(V) * vb / nvb;
     const int n = static_cast<int>(static_cast<long long>(V) * (vb + 1) / nvb - v0);
+    if (n <= 0)
+        return;  // an empty range (V below the number of ranges)
     const int nchunk = (n + CRr - 1) / CRr;
     const int g = blockIdx.x % NG;
-    const int slots = (CRr / 16) * KS * 64;  // uint4 per chunk
-    constexpr int PT = 8;                    // staging registers per thread (max)
-    const int per_thread = slots / NTH;
+    constexpr int slots = (CRr / 16) * KS * 64;  // uint4 per chunk
+    constexpr int PT = slots / NTH;              // staging registers per thread
+    static_assert(slots % NTH == 0, "chunk slots per thread");
 
     // A operands of this wave
     uint4 ua[AT][KS];
@@ -91,24 +94,23 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng)
         }
     }
 
-    // staging: slot s of a chunk = (tile, step, lane) -> 16 bytes of W2
+    // staging: slot s of a chunk = (tile, step, lane) -> 16 bytes of W2.  Every load
+    // is issued on every path (rows past the range read the range's first row, whose
+    // results are masked), so the compiler's wait counts stay exact: a conditional
+    // load makes it wait for every load in flight, the chunks loaded ahead included
     auto stage_load = [&](int c, uint4 (&st)[PT]) {
 #pragma unroll
         for (int jj = 0; jj < PT; ++jj) {
-            if (jj < per_thread) {
-                const int s = threadIdx.x + jj * NTH;
-                const int vt = s / (KS * 64), kk = (s / 64) % KS, ln = s & 63;
-                const int vr = c * CRr + vt * 16 + (ln & 15);
-                st[jj] = vr < n ? ld16<bf16s>(p.W2, static_cast<size_t>(v0 + vr) * r + kk * 32 + (ln >> 4) * 8)
-                                : make_uint4(0u, 0u, 0u, 0u);
-            }
+            const int s = threadIdx.x + jj * NTH;
+            const int vt = s / (KS * 64), kk = (s / 64) % KS, ln = s & 63;
+            const int vr = c * CRr + vt * 16 + (ln & 15);
+            st[jj] = ld16<bf16s>(p.W2, static_cast<size_t>(v0 + (vr < n ? vr : 0)) * r + kk * 32 + (ln >> 4) * 8);
         }
     };
     auto stage_store = [&](int buf, const uint4 (&st)[PT]) {
 #pragma unroll
         for (int jj = 0; jj < PT; ++jj)
-            if (jj < per_thread)
-                wlds[buf * slots + threadIdx.x + jj * NTH] = st[jj];
+            wlds[buf * slots + threadIdx.x + jj * NTH] = st[jj];
     };
     // this lane's batch rows in the combined results: pair pp packs A tiles 2pp
     // (lanes 0..31) and 2pp+1 (lanes 32..63), row i of four
@@ -144,19 +146,15 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng)
     // parity (the loop is unrolled by two so the sets are fixed)
     uint4 st[2][PT];
     float lb[2][NP][VTG][4];
-    if (nchunk > 0) {
-        stage_load(0, st[0]);
-        lbase_load(0, lb[0]);
-        stage_store(0, st[0]);
-    }
-    if (nchunk > 1) {
-        stage_load(1, st[1]);
-        lbase_load(1, lb[1]);
-    }
+    const int clast = nchunk - 1;  // loads past the last chunk repeat it
+    stage_load(0, st[0]);
+    lbase_load(0, lb[0]);
+    stage_store(0, st[0]);
+    stage_load(1 < clast ? 1 : clast, st[1]);
+    lbase_load(1 < clast ? 1 : clast, lb[1]);
     __syncthreads();
     auto step = [&](int c, int P) {
-        if (c + 2 < nchunk)
-            stage_load(c + 2, st[P]);
+        stage_load(c + 2 < clast ? c + 2 : clast, st[P]);
         f32x4_t acc[AT][VTG];
 #pragma unroll
         for (int a = 0; a < AT; ++a)
@@ -189,14 +187,12 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng)
                     const float w = __uint_as_float(d[0]) + __uint_as_float(d[1]);
                     const int b = brow[pp][i];
                     const bool ok = b < B && vr < n;
-                    float *lf = p.L_final ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * V + v0 : nullptr;
+                    float *lf = ST ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * V + v0 : nullptr;
                     w2_key(w, lb[P][pp][vt][i], lf, static_cast<int>(v0), vr, ok, best[pp][i]);
                 }
             }
-        if (c + 2 < nchunk)
-            lbase_load(c + 2, lb[P]);
-        if (c + 1 < nchunk)
-            stage_store(P ^ 1, st[P ^ 1]);
+        lbase_load(c + 2 < clast ? c + 2 : clast, lb[P]);
+        stage_store(P ^ 1, st[P ^ 1]);
         __syncthreads();
     };
 #pragma unroll 1
@@ -580,20 +576,25 @@ struct W2Shape {
     const void *fn;
     int threads, ng;
 };
-template <bool LB16>
+// ng batch groups of 16 rows per 128-row tile; the 8 waves form 8 / ng wave sets that
+// split each 64-row chunk (128 rows for ng = 1)
+template <bool LB16, bool ST>
 static const void *w2_fn(int ng)
 {
-    return ng == 8   ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 4, 2, 512, LB16>)
-           : ng == 4 ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 2, 2, 512, LB16>)
-                     : reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 1, 2, 512, LB16>);
+    return ng == 8   ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 4, 1, 2, 512, LB16, ST>)
+           : ng == 4 ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 2, 2, 2, 512, LB16, ST>)
+           : ng == 2 ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 1, 4, 2, 512, LB16, ST>)
+                     : reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 1, 8, 2, 512, LB16, ST>);
 }
-static W2Shape w2_shape(int B, bool lb16 = false)
+static W2Shape w2_shape(int B, bool lb16 = false, bool store = false)
 {
     const int need = ((B < 128 ? B : 128) + 15) / 16;
     const int ng = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
-    return {lb16 ? w2_fn<true>(ng) : w2_fn<false>(ng), 512, ng};
+    const void *fn = lb16 ? (store ? w2_fn<true, true>(ng) : w2_fn<true, false>(ng))
+                          : (store ? w2_fn<false, true>(ng) : w2_fn<false, false>(ng));
+    return {fn, 512, ng};
 }
-const void *w2_kernel(int B, bool lbase_bf16) { return w2_shape(B, lbase_bf16).fn; }
+const void *w2_kernel(int B, bool lbase_bf16, bool store_logits) { return w2_shape(B, lbase_bf16, store_logits).fn; }
 int w2_groups(int B) { return w2_shape(B).ng; }
 int w2_threads(int B) { return w2_shape(B).threads; }
 // one block per compute unit: batch tiles times vocabulary ranges

@@ -244,10 +244,12 @@ __device__ __forceinline__ bool splitk_tile(int nst, Ld ld, f32x4_t (&acc)[NA][N
     const int s0 = wave * per, s1 = s0 + per < nst ? s0 + per : nst;
     for (int sb = s0; sb < s1; sb += KU) {
         uint4 av[KU][NA], bv[KU][NB];
+        // every load is issued (steps past s1 repeat the last one and are not
+        // multiplied), so the compiler waits for each step's operands alone instead
+        // of for every load in flight
 #pragma unroll
         for (int u = 0; u < KU; ++u)
-            if (sb + u < s1)
-                ld(sb + u, av[u], bv[u]);
+            ld(sb + u < s1 ? sb + u : s1 - 1, av[u], bv[u]);
 #pragma unroll
         for (int u = 0; u < KU; ++u)
             if (sb + u < s1)
@@ -290,6 +292,62 @@ __device__ __forceinline__ bool splitk_tile(int nst, Ld ld, f32x4_t (&acc)[NA][N
 // A operand: S_q as bf16 hi + lo rows of 8 batch rows (planes written by the
 // update launch); B operand: 16 weight rows.  A block takes 32 batch rows and
 // 32 weight rows (split-K over h).
+// Epilogue of the state dot products: u = SiLU(A_H + dot) for rows m < r, the
+// next step's q = dot + b_hh for the W_hh rows.  acc holds four 8-row batch tiles
+// (hi rows 0..7, lo rows 8..15 of each) by two 16-row weight tiles; weight row m =
+// mbase + t*16 + col, batch row b = bbase + (2pp + (lane >> 5))*8 + ((lane >> 4) & 1)*4 + i.
+// The A_H and bias values are loaded first, every load on every path (clamped
+// indices, unused values dropped), so the compiler waits once for all of them
+// instead of once per conditional load.
+template <typename WT>
+__device__ __forceinline__ void state_epilogue(const Params &p, int q, const f32x4_t (&acc)[4][2], int mbase,
+                                               int bbase)
+{
+    const int lane = threadIdx.x & 63, col = lane & 15;
+    const int h = p.h, r = p.r, R = r + 3 * p.h, B = p.B, h3 = 3 * h;
+    float *qn = q_slot(p, q + 1);
+    float ahv[2][2][4], bias[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int m = mbase + t * 16 + col;
+        const int mq = (m >= r && m < R) ? m - r : 0;
+        const int mu = m < r ? m : 0;
+        bias[t] = p.b_hh ? WT16<WT>::one(p.b_hh, mq) : 0.f;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int b = bbase + (2 * pp + (lane >> 5)) * 8 + ((lane >> 4) & 1) * 4 + i;
+                ahv[pp][t][i] = p.A_H[(static_cast<size_t>(b < B ? b : 0) * p.K + q) * r + mu];
+            }
+    }
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int m = mbase + t * 16 + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x0 = w2_hilo(acc[2 * pp][t], i), x1 = w2_hilo(acc[2 * pp + 1][t], i);
+                const auto dd = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x1), false,
+                                                                 false);
+                const float dot = __uint_as_float(dd[0]);
+                const int b = bbase + (2 * pp + (lane >> 5)) * 8 + ((lane >> 4) & 1) * 4 + i;
+                if (b >= B || m >= R)
+                    continue;
+                if (m < r) {
+                    const float a_ = ahv[pp][t][i] + dot;
+                    const float u = a_ * sigmoidf_(a_);
+                    p.u_buf[static_cast<size_t>(b) * r + m] = u;
+                    if (p.u_out)
+                        p.u_out[(static_cast<size_t>(b) * p.K + q) * r + m] = u;
+                } else {
+                    qn[static_cast<size_t>(b) * h3 + (m - r)] = dot + bias[t];
+                }
+            }
+        }
+}
+
 template <typename WT, int KU = 8>
 __global__ __launch_bounds__(NT) void k_state_mfma(Params p, int q)
 {
@@ -326,44 +384,18 @@ __global__ __launch_bounds__(NT) void k_state_mfma(Params p, int q)
         h / 32,
         [&](int s, uint4(&av)[4], uint4(&wv)[2]) {
             const int k = s * 32;
+            // rows past B or R read row 0 (clamped pointers); their results are not stored
 #pragma unroll
             for (int a = 0; a < 4; ++a)
-                av[a] = aok[a] ? *reinterpret_cast<const uint4 *>(arow[a] + k) : make_uint4(0u, 0u, 0u, 0u);
+                av[a] = *reinterpret_cast<const uint4 *>(arow[a] + k);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
-                wv[t] = wok[t] ? *reinterpret_cast<const uint4 *>(wrow[t] + k) : make_uint4(0u, 0u, 0u, 0u);
+                wv[t] = *reinterpret_cast<const uint4 *>(wrow[t] + k);
         },
         acc, part);
     if (!lead)
         return;
-    const int h3 = 3 * h;
-    float *qn = q_slot(p, q + 1);
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int m = mw + t * 16 + col;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float x0 = w2_hilo(acc[2 * pp][t], i), x1 = w2_hilo(acc[2 * pp + 1][t], i);
-                const auto dd = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x1), false,
-                                                                 false);
-                const float dot = __uint_as_float(dd[0]);
-                const int b = b0 + (2 * pp + (lane >> 5)) * 8 + ((lane >> 4) & 1) * 4 + i;
-                if (b >= B || m >= R)
-                    continue;
-                if (m < r) {
-                    const float a_ = p.A_H[(static_cast<size_t>(b) * p.K + q) * r + m] + dot;
-                    const float u = a_ * sigmoidf_(a_);
-                    p.u_buf[static_cast<size_t>(b) * r + m] = u;
-                    if (p.u_out)
-                        p.u_out[(static_cast<size_t>(b) * p.K + q) * r + m] = u;
-                } else {
-                    const float bias = p.b_hh ? WT16<WT>::one(p.b_hh, m - r) : 0.f;
-                    qn[static_cast<size_t>(b) * h3 + (m - r)] = dot + bias;
-                }
-            }
-        }
+    state_epilogue<WT>(p, q, acc, mw, b0);
 }
 
 // The same state dots with the operands staged in LDS (h a multiple of 256).  A
@@ -388,7 +420,7 @@ __global__ __launch_bounds__(NT) void k_state_lds(Params p, int q)
     const int nbg = (B + 63) / 64, nwb = (R + 63) / 64;
     const int tile = xcd_tile(blockIdx.x, nbg * nwb);
     const int bg = tile % nbg, wbk = tile / nbg;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int b0 = bg * 64, mw = wbk * 64;
     const int NS = h / 64;  // stages, a multiple of 4
     // this lane's source of the 6 operand blocks this wave copies per stage:
@@ -474,34 +506,7 @@ __global__ __launch_bounds__(NT) void k_state_lds(Params p, int q)
         step(s + 2, ring2, ring1);
         step(s + 3, ring3, ring2);
     }
-    const int h3 = 3 * h;
-    float *qn = q_slot(p, q + 1);
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int m = mw + (wb * 2 + t) * 16 + col;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float x0 = w2_hilo(acc[2 * pp][t], i), x1 = w2_hilo(acc[2 * pp + 1][t], i);
-                const auto dd = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x1), false,
-                                                                 false);
-                const float dot = __uint_as_float(dd[0]);
-                const int b = b0 + (wa * 4 + 2 * pp + (lane >> 5)) * 8 + ((lane >> 4) & 1) * 4 + i;
-                if (b >= B || m >= R)
-                    continue;
-                if (m < r) {
-                    const float a_ = p.A_H[(static_cast<size_t>(b) * p.K + q) * r + m] + dot;
-                    const float u = a_ * sigmoidf_(a_);
-                    p.u_buf[static_cast<size_t>(b) * r + m] = u;
-                    if (p.u_out)
-                        p.u_out[(static_cast<size_t>(b) * p.K + q) * r + m] = u;
-                } else {
-                    const float bias = p.b_hh ? WT16<WT>::one(p.b_hh, m - r) : 0.f;
-                    qn[static_cast<size_t>(b) * h3 + (m - r)] = dot + bias;
-                }
-            }
-        }
+    state_epilogue<WT>(p, q, acc, mw + wb * 32, b0 + wa * 32);
 }
 
 // A_H = W1[:, :d] H for every position on the matrix cores (same quantity as
@@ -535,9 +540,10 @@ __global__ __launch_bounds__(NT) void k_ah_mfma(Params p)
         d / 32,
         [&](int s, uint4(&av)[2], uint4(&wv)[2]) {
             const int k = s * 32;
+            // rows past B K read row 0 (clamped pointer); their results are not stored
 #pragma unroll
             for (int a = 0; a < 2; ++a)
-                av[a] = aok[a] ? *reinterpret_cast<const uint4 *>(arow[a] + k) : make_uint4(0u, 0u, 0u, 0u);
+                av[a] = *reinterpret_cast<const uint4 *>(arow[a] + k);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
                 wv[t] = *reinterpret_cast<const uint4 *>(wrow[t] + k);

@@ -24,7 +24,10 @@ struct Params {
     uint32_t *utag;  // [2, maxB, r] u as matrix-core operand: words (tag << 16) | bf16 bits of the
                      // hi part (plane 0) and lo part (plane 1) of u, or nullptr
     float *q_buf;    // [2, maxB, 3h] W_hh S + b_hh
-    uint16_t *s_hl;  // [2, maxB, h] bf16 hi and lo parts of S (matrix-core state dots) or nullptr
+    uint16_t *s_hl;  // [2, maxB, ldw] bf16 hi and lo parts of S (matrix-core state dots) or nullptr
+    const uint16_t *wst;  // [r + 3h, ldw] bf16: the W1_S rows, then the W_hh rows, with a padded
+                          // row stride (matrix-core state dots), or nullptr
+    int ldw;              // row stride of s_hl and wst in elements
     float *g_buf;    // [maxB, 3h]    W_ih E[x] + b_ih (when not folded)
     uint64_t *keys;  // [K, NG, maxB] partial argmax keys
     unsigned *bar;   // barrier words

@@ -325,10 +325,11 @@ __device__ __forceinline__ void phase_update(const Params &p, int blk, int nblk,
             xst(&S_slot(p, q)[static_cast<size_t>(b) * h + j], sn);
             if (p.S_out)
                 p.S_out[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
-            if (p.s_hl) {  // operand planes for the matrix-core state dots
+            if (p.s_hl) {  // operand planes for the matrix-core state dots (row stride ldw)
                 const uint32_t hi = bf16_rne_bits(sn);
-                p.s_hl[e] = static_cast<uint16_t>(hi);
-                p.s_hl[static_cast<size_t>(p.maxB) * h + e] =
+                const size_t o = static_cast<size_t>(b) * p.ldw + j;
+                p.s_hl[o] = static_cast<uint16_t>(hi);
+                p.s_hl[static_cast<size_t>(p.maxB) * p.ldw + o] =
                     static_cast<uint16_t>(bf16_rne_bits(sn - __uint_as_float(hi << 16)));
             }
         }

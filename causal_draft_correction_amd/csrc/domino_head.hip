@@ -120,6 +120,22 @@ __global__ __launch_bounds__(256) void k_markov_state(const float *Pc, const voi
     }
 }
 
+// Create time: the W1_S rows, then the W_hh rows, into wst [r + 3h, ldw] (bf16
+// bits), zero padded.
+__global__ __launch_bounds__(256) void k_pack_state_rows(const uint16_t *W1, const uint16_t *W_hh, uint16_t *wst,
+                                                         int r, int d, int h, int ldw)
+{
+    const size_t total = static_cast<size_t>(r + 3 * h) * ldw;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+         i += static_cast<size_t>(gridDim.x) * 256) {
+        const int m = static_cast<int>(i / ldw), j = static_cast<int>(i % ldw);
+        uint16_t v = 0;
+        if (j < h)
+            v = m < r ? W1[static_cast<size_t>(m) * (d + h) + d + j] : W_hh[static_cast<size_t>(m - r) * h + j];
+        wst[i] = v;
+    }
+}
+
 // Create time: the state columns of W1 as a contiguous float32 [r, h] matrix.
 template <typename WT>
 __global__ __launch_bounds__(256) void k_w1s_widen(const void *W1, float *W1S, int r, int d, int h)
@@ -339,8 +355,18 @@ constexpr int W2_STEP_ROWS = 128;  // vocabulary rows per block in stepwise W2 l
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, u_all, utag, s_hl, q_buf, g_buf, P, M, mk_tmp, total;
+    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, u_all, utag, s_hl, q_buf, g_buf, P, M, mk_tmp, wst, total;
 };
+
+// Packed state-dot rows for the matrix-core state launches (bf16 heads): the rows of
+// W1_S and W_hh copied with a row stride 64 bytes past a multiple of 256 bytes, so the
+// rows a tile reads together do not all start on the same memory channel (the
+// caller's 2 KiB rows at h = 1024 do)
+bool packed_state_rows(const domino_head_config &c)
+{
+    return c.wdtype == DOMINO_BF16 && c.r % 32 == 0 && c.h % 32 == 0 && c.max_batch > BC;
+}
+int packed_ldw(const domino_head_config &c) { return (c.h + 127) / 128 * 128 + 32; }
 
 // Markov table fill: tokens per chunk (create-time region: folded gate rows and
 // zero-state GRU rows of one chunk, plus W1_S as float32)
@@ -369,8 +395,9 @@ Layout layout_of(const domino_head_config &c)
     off = align_up(off + sizeof(float) * static_cast<size_t>(c.max_batch) * c.K * c.r);
     L.utag = off;
     off = align_up(off + sizeof(uint32_t) * 2 * static_cast<size_t>(c.max_batch) * c.r);
-    L.s_hl = off;
-    off = align_up(off + sizeof(uint16_t) * 2 * static_cast<size_t>(c.max_batch) * c.h);
+    L.s_hl = off;  // rows of packed_ldw elements (used only with packed state rows)
+    off = align_up(off + sizeof(uint16_t) * 2 * static_cast<size_t>(c.max_batch) *
+                             (packed_state_rows(c) ? packed_ldw(c) : c.h));
     L.q_buf = off;
     off = align_up(off + sizeof(float) * 2 * static_cast<size_t>(c.max_batch) * 3 * c.h);
     L.g_buf = off;
@@ -378,6 +405,9 @@ Layout layout_of(const domino_head_config &c)
     L.P = off;
     if (c.flags & DOMINO_FOLD_EMBED)
         off = align_up(off + sizeof(float) * static_cast<size_t>(c.V) * 3 * c.h);
+    L.wst = off;
+    if (packed_state_rows(c))
+        off = align_up(off + sizeof(uint16_t) * static_cast<size_t>(c.r + 3 * c.h) * packed_ldw(c));
     L.M = off;
     L.mk_tmp = off;
     if (c.flags & DOMINO_MARKOV) {
@@ -615,6 +645,14 @@ int domino_head_create(const domino_head_config *cfg, void *workspace, size_t wo
         // one-time table P = E W_ih^T + b_ih on the null stream, waited for here
         HIP_TRY(kern.fold(*cfg, reinterpret_cast<float *>(static_cast<char *>(workspace) + L.P)), "folded gate table");
     }
+    if (packed_state_rows(*cfg)) {
+        hipLaunchKernelGGL(k_pack_state_rows, dim3(1024), dim3(256), 0, nullptr, static_cast<const uint16_t *>(cfg->W1),
+                           static_cast<const uint16_t *>(cfg->W_hh),
+                           reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + L.wst), cfg->r, cfg->d, cfg->h,
+                           packed_ldw(*cfg));
+        HIP_TRY(hipGetLastError(), "launch k_pack_state_rows");
+        HIP_TRY(hipStreamSynchronize(nullptr), "packed state rows");
+    }
     if (cfg->flags & DOMINO_MARKOV) {
         HIP_TRY(kern.markov(*cfg, reinterpret_cast<float *>(static_cast<char *>(workspace) + L.M),
                             reinterpret_cast<float *>(static_cast<char *>(workspace) + L.mk_tmp)),
@@ -792,8 +830,11 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
     const size_t sm_state = sizeof(float) * smem_floats(c.r, c.h, 0);
     // larger batches of bf16 heads take the matrix-core state dots (S passed as bf16 hi/lo planes)
     const bool state_mfma = c.wdtype == DOMINO_BF16 && c.r % 32 == 0 && c.h % 32 == 0 && B > BC;
-    if (state_mfma)
+    if (state_mfma) {
         p.s_hl = reinterpret_cast<uint16_t *>(hd->ws + hd->L.s_hl);
+        p.wst = reinterpret_cast<const uint16_t *>(hd->ws + hd->L.wst);  // state_mfma implies packed rows
+        p.ldw = packed_ldw(c);
+    }
     auto launch_state = [&](void **sargs) -> hipError_t {
         if (state_mfma)
             return hipLaunchKernel(dhbat::state_kernel(B, c.h), dim3(dhbat::state_grid(B, c.r, c.h)),

@@ -366,7 +366,7 @@ __global__ __launch_bounds__(NT) void k_state_mfma(Params p, int q)
     for (int a = 0; a < 4; ++a) {
         const int b = b0 + a * 8 + (col & 7);
         aok[a] = b < B;
-        arow[a] = p.s_hl + (static_cast<size_t>(col >> 3) * p.maxB + (aok[a] ? b : 0)) * h + (lane >> 4) * 8;
+        arow[a] = p.s_hl + (static_cast<size_t>(col >> 3) * p.maxB + (aok[a] ? b : 0)) * p.ldw + (lane >> 4) * 8;
     }
     const bf16s *wrow[2];
     bool wok[2];
@@ -375,8 +375,9 @@ __global__ __launch_bounds__(NT) void k_state_mfma(Params p, int q)
         const int m = mw + t * 16 + col;
         wok[t] = m < R;
         const int mm = wok[t] ? m : 0;
-        wrow[t] = mm < r ? static_cast<const bf16s *>(p.W1) + static_cast<size_t>(mm) * (p.d + h) + p.d
-                         : static_cast<const bf16s *>(p.W_hh) + static_cast<size_t>(mm - r) * h;
+        wrow[t] = p.wst ? reinterpret_cast<const bf16s *>(p.wst) + static_cast<size_t>(mm) * p.ldw
+                  : mm < r ? static_cast<const bf16s *>(p.W1) + static_cast<size_t>(mm) * (p.d + h) + p.d
+                           : static_cast<const bf16s *>(p.W_hh) + static_cast<size_t>(mm - r) * h;
         wrow[t] += (lane >> 4) * 8;
     }
     f32x4_t acc[4][2];
@@ -433,11 +434,12 @@ __global__ __launch_bounds__(NT) void k_state_lds(Params p, int q)
         const uint16_t *base;
         if (t < 8) {
             const int b = b0 + t * 8 + (i & 7) < B ? b0 + t * 8 + (i & 7) : B - 1;
-            base = p.s_hl + (static_cast<size_t>(i >> 3) * p.maxB + b) * h;
+            base = p.s_hl + (static_cast<size_t>(i >> 3) * p.maxB + b) * p.ldw;
         } else {
             const int m = mw + (t - 8) * 16 + i < R ? mw + (t - 8) * 16 + i : R - 1;
-            base = m < r ? static_cast<const uint16_t *>(p.W1) + static_cast<size_t>(m) * (p.d + h) + p.d
-                         : static_cast<const uint16_t *>(p.W_hh) + static_cast<size_t>(m - r) * h;
+            base = p.wst ? p.wst + static_cast<size_t>(m) * p.ldw
+                   : m < r ? static_cast<const uint16_t *>(p.W1) + static_cast<size_t>(m) * (p.d + h) + p.d
+                           : static_cast<const uint16_t *>(p.W_hh) + static_cast<size_t>(m - r) * h;
         }
         src[u] = base + ks * 32 + (lane >> 4) * 8;
     }

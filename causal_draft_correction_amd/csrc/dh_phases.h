@@ -563,48 +563,63 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
             // B <= BC: one chunk.  Each thread takes the GRU input token itself
             // (atok entries were written before the argmax barrier's last block
             // sync); the state never leaves the block, so S_buf is not written.
+            // Elements go in batches of SP_EL per thread: every load of a batch (the
+            // gate inputs, q, the previous state) is issued before any is used, at
+            // clamped indices for elements past the end, so the batch costs one
+            // memory round trip instead of one per element.  The first batch takes
+            // the q values prefetched before the barrier when given.
             DH_TRACE(tslot + 1);
-            // the first SP_EL elements of this thread use the q values prefetched before the barrier
+            const int ne = nb * h;
+            for (int i0 = threadIdx.x; i0 < ne; i0 += SP_EL * NT) {
+                float gv[SP_EL][3], qv[SP_EL][3], sp[SP_EL];
 #pragma unroll
-            for (int e = 0; e < SP_EL; ++e) {
-                const int i = threadIdx.x + e * NT;
-                if (i < nb * h) {
-                    const int bb = i / h, j = i % h, b = b0 + bb;
-                    const float sprev = (q == 0) ? state_prev(p, 0, b, j) : S_lds[bb * h + j];
-                    const int tokb = p.P ? gru_input_token(p, q, b, atok) : 0;
-                    float sn;
-                    if (pre && b0 == 0) {
-                        float gr, gz, gn;
-                        if (p.P) {
-                            const float *prow = p.P + static_cast<size_t>(tokb) * h3;
-                            gr = prow[j];
-                            gz = prow[h + j];
-                            gn = prow[2 * h + j];
-                        } else {
-                            const float *g = p.g_buf + static_cast<size_t>(b) * h3;
-                            gr = xld(&g[j]);
-                            gz = xld(&g[h + j]);
-                            gn = xld(&g[2 * h + j]);
-                        }
-                        const float rg = sigmoidf_(gr + pre->qv[e][0]);
-                        const float zg = sigmoidf_(gz + pre->qv[e][1]);
-                        const float ng = tanhf(gn + rg * pre->qv[e][2]);
-                        sn = (1.f - zg) * ng + zg * sprev;
+                for (int e = 0; e < SP_EL; ++e) {
+                    const int i = i0 + e * NT;
+                    const int ic = i < ne ? i : 0;
+                    const int bb = ic / h, j = ic % h, b = b0 + bb;
+                    sp[e] = (q == 0) ? state_prev(p, 0, b, j) : S_lds[bb * h + j];
+                    if (p.P) {
+                        const float *prow = p.P + static_cast<size_t>(gru_input_token(p, q, b, atok)) * h3;
+                        gv[e][0] = prow[j];
+                        gv[e][1] = prow[h + j];
+                        gv[e][2] = prow[2 * h + j];
                     } else {
-                        sn = gate_update(p, q, b, j, tokb, sprev);
+                        const float *g = p.g_buf + static_cast<size_t>(b) * h3;
+                        gv[e][0] = xld(&g[j]);
+                        gv[e][1] = xld(&g[h + j]);
+                        gv[e][2] = xld(&g[2 * h + j]);
                     }
-                    S_lds[bb * h + j] = sn;  // each thread reads only the entry it writes
-                    if (blk == 0 && p.S_out)
-                        p.S_out[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
+                    if (pre && b0 == 0 && i0 == static_cast<int>(threadIdx.x)) {
+                        qv[e][0] = pre->qv[e][0];
+                        qv[e][1] = pre->qv[e][1];
+                        qv[e][2] = pre->qv[e][2];
+                    } else if (q == 0 && !p.S_init) {
+                        // W_hh S_init + b_hh with S_init = 0 is b_hh itself
+                        qv[e][0] = bias_hh(p, j);
+                        qv[e][1] = bias_hh(p, h + j);
+                        qv[e][2] = bias_hh(p, 2 * h + j);
+                    } else {
+                        const float *qq = q_slot(p, q) + static_cast<size_t>(b) * h3;
+                        qv[e][0] = xld(&qq[j]);
+                        qv[e][1] = xld(&qq[h + j]);
+                        qv[e][2] = xld(&qq[2 * h + j]);
+                    }
                 }
-            }
-            for (int i = threadIdx.x + SP_EL * NT; i < nb * h; i += NT) {
-                const int bb = i / h, j = i % h, b = b0 + bb;
-                const float sprev = (q == 0) ? state_prev(p, 0, b, j) : S_lds[bb * h + j];
-                const float sn = gate_update(p, q, b, j, p.P ? gru_input_token(p, q, b, atok) : 0, sprev);
-                S_lds[bb * h + j] = sn;
-                if (blk == 0 && p.S_out)
-                    p.S_out[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
+#pragma unroll
+                for (int e = 0; e < SP_EL; ++e) {
+                    const int i = i0 + e * NT;
+                    if (i < ne) {
+                        const int bb = i / h, j = i % h, b = b0 + bb;
+                        // the cell of gate_update, on the values loaded above
+                        const float rg = sigmoidf_(gv[e][0] + qv[e][0]);
+                        const float zg = sigmoidf_(gv[e][1] + qv[e][1]);
+                        const float ng = tanhf(gv[e][2] + rg * qv[e][2]);
+                        const float sn = (1.f - zg) * ng + zg * sp[e];
+                        S_lds[bb * h + j] = sn;  // each thread reads only the entries it writes
+                        if (blk == 0 && p.S_out)
+                            p.S_out[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
+                    }
+                }
             }
         } else {
             __syncthreads();  // S_lds of the previous chunk is no longer read

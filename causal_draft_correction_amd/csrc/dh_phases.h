@@ -23,6 +23,8 @@
 //     state for itself: S never has to cross blocks in the persistent launch.
 #pragma once
 
+#include <type_traits>
+
 #include "dh_common.h"
 #include "dh_params.h"
 
@@ -551,7 +553,6 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
 {
     constexpr int EPC = WT16<WT>::EPC;
     const int h = p.h, h3 = 3 * h, r = p.r;
-    (void)smem;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     float *qn_all = q_slot(p, q + 1);
     const int R = state_rows(p), nch = h / EPC;
@@ -570,7 +571,16 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
             // the q values prefetched before the barrier when given.
             DH_TRACE(tslot + 1);
             const int ne = nb * h;
-            for (int i0 = threadIdx.x; i0 < ne; i0 += SP_EL * NT) {
+            // the GRU input token of each row, once, into LDS: the batch loads below
+            // then depend on an LDS read only
+            int *tokl = reinterpret_cast<int *>(smem + smem_off_tok());
+            if (p.P && static_cast<int>(threadIdx.x) < nb)
+                tokl[threadIdx.x] = gru_input_token(p, q, b0 + threadIdx.x, atok);
+            __syncthreads();
+            // qmode 0: q prefetched before the barrier (first batch), 1: q = b_hh (zero
+            // initial state), 2: q loaded; one branch per batch, none per element
+            auto batch = [&](auto qmode, int i0) {
+                constexpr int QM = decltype(qmode)::value;
                 float gv[SP_EL][3], qv[SP_EL][3], sp[SP_EL];
 #pragma unroll
                 for (int e = 0; e < SP_EL; ++e) {
@@ -579,7 +589,7 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                     const int bb = ic / h, j = ic % h, b = b0 + bb;
                     sp[e] = (q == 0) ? state_prev(p, 0, b, j) : S_lds[bb * h + j];
                     if (p.P) {
-                        const float *prow = p.P + static_cast<size_t>(gru_input_token(p, q, b, atok)) * h3;
+                        const float *prow = p.P + static_cast<size_t>(tokl[bb]) * h3;
                         gv[e][0] = prow[j];
                         gv[e][1] = prow[h + j];
                         gv[e][2] = prow[2 * h + j];
@@ -589,11 +599,11 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                         gv[e][1] = xld(&g[h + j]);
                         gv[e][2] = xld(&g[2 * h + j]);
                     }
-                    if (pre && b0 == 0 && i0 == static_cast<int>(threadIdx.x)) {
+                    if constexpr (QM == 0) {
                         qv[e][0] = pre->qv[e][0];
                         qv[e][1] = pre->qv[e][1];
                         qv[e][2] = pre->qv[e][2];
-                    } else if (q == 0 && !p.S_init) {
+                    } else if constexpr (QM == 1) {
                         // W_hh S_init + b_hh with S_init = 0 is b_hh itself
                         qv[e][0] = bias_hh(p, j);
                         qv[e][1] = bias_hh(p, h + j);
@@ -620,6 +630,15 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                             p.S_out[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
                     }
                 }
+            };
+            const bool use_pre = pre && b0 == 0, qbias = q == 0 && !p.S_init;
+            for (int i0 = threadIdx.x, it = 0; i0 < ne; i0 += SP_EL * NT, ++it) {
+                if (use_pre && it == 0)
+                    batch(std::integral_constant<int, 0>(), i0);
+                else if (qbias)
+                    batch(std::integral_constant<int, 1>(), i0);
+                else
+                    batch(std::integral_constant<int, 2>(), i0);
             }
         } else {
             __syncthreads();  // S_lds of the previous chunk is no longer read

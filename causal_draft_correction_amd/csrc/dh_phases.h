@@ -80,14 +80,18 @@ __device__ inline uint64_t *key_slot(const Params &p, int pos, int g, int b)
     return p.keys + (static_cast<size_t>(pos) * NG + g) * p.maxB + b;
 }
 
-// Greedy token of position `pos` for row b: max over the NG partial keys.
+// Greedy token of position `pos` for row b: max over the NG partial keys.  All
+// NG loads are issued before the first is used (one memory round trip).
 __device__ inline int key_token(const Params &p, int pos, int b)
 {
+    uint64_t k[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+        k[g] = ld_agent_u64(key_slot(p, pos, g, b));
     uint64_t best = 0;
-    for (int g = 0; g < NG; ++g) {
-        uint64_t k = ld_agent_u64(key_slot(p, pos, g, b));
-        best = k > best ? k : best;
-    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+        best = k[g] > best ? k[g] : best;
     return best ? static_cast<int>(key_index(best)) : 0;
 }
 

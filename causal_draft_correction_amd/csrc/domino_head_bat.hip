@@ -161,18 +161,27 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
 #pragma unroll
             for (int vt = 0; vt < VTG; ++vt)
                 acc[a][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const uint4 *wb = wlds + P * slots;
+        // the W2 operands of step kk + 1 are read from LDS while step kk is multiplied
+        const uint4 *wb = wlds + P * slots + (vs * VTG * KS) * 64 + lane;
+        uint4 wf[2][VTG];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
+        for (int vt = 0; vt < VTG; ++vt)
+            wf[0][vt] = wb[(vt * KS) * 64];
 #pragma unroll
-            for (int vt = 0; vt < VTG; ++vt) {
-                const uint4 w = wb[((vs * VTG + vt) * KS + kk) * 64 + lane];
+        for (int kk = 0; kk < KS; ++kk) {
+            if (kk + 1 < KS) {
+#pragma unroll
+                for (int vt = 0; vt < VTG; ++vt)
+                    wf[(kk + 1) & 1][vt] = wb[(vt * KS + kk + 1) * 64];
+            }
+#pragma unroll
+            for (int vt = 0; vt < VTG; ++vt)
 #pragma unroll
                 for (int a = 0; a < AT; ++a)
                     acc[a][vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ua[a][kk]),
-                                                                        __builtin_bit_cast(bf16x8_t, w), acc[a][vt],
-                                                                        0, 0, 0);
-            }
+                                                                        __builtin_bit_cast(bf16x8_t, wf[kk & 1][vt]),
+                                                                        acc[a][vt], 0, 0, 0);
+        }
 #pragma unroll
         for (int pp = 0; pp < NP; ++pp)
 #pragma unroll

@@ -236,13 +236,24 @@ template <typename WT>
 __global__ __launch_bounds__(NT) void k_step_prologue(Params p)
 {
     extern __shared__ float smem[];
-    if (blockIdx.x == 0)
-        prologue_bookkeeping(p);
+    // the partial keys of every position, zeroed by all blocks (the launches that
+    // fold into them come later on the stream); block 0 flags invalid rows
+    const size_t nkeys = static_cast<size_t>(p.K) * NG * p.maxB;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * NT + threadIdx.x; i < nkeys;
+         i += static_cast<size_t>(gridDim.x) * NT)
+        p.keys[i] = 0ull;
+    if (blockIdx.x == 0) {
+        for (int b = threadIdx.x; b < p.B; b += NT)
+            if (row_bad(p, b))
+                __hip_atomic_fetch_or(p.flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (!p.ah_external)
         phase_ah<WT>(p, blockIdx.x, gridDim.x, smem);
     if (p.M)
         return;  // Markov head: no recurrent state
-    phase_q_init<WT>(p, blockIdx.x, gridDim.x);
+    // q_0 = W_hh S_init + b_hh; without S_init the gate update reads b_hh itself
+    if (p.S_init)
+        phase_q_init<WT>(p, blockIdx.x, gridDim.x);
     if (!p.P)
         phase_g<WT>(p, blockIdx.x, gridDim.x, 0, smem);
 }

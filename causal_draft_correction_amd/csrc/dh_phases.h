@@ -475,14 +475,16 @@ __device__ __forceinline__ void ah_local_to_cache(const Params &p, int blk, int 
                 for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
                     for (int vw = 0; vw < VW; ++vw) {
+                        // every load is issued (chunks past d and positions past K read
+                        // chunk 0 / position 0 and are not multiplied), so they all go out
+                        // before the first product instead of one branch at a time
                         const int c = c0 + kk * AH_LANES + vw * 64 + lane;
-                        if (c < nch) {
-                            wv[kk][vw] = ld16<WT>(p.W1, static_cast<size_t>(m) * (d + h) + static_cast<size_t>(c) * EPC);
+                        const int cc = c < nch ? c : 0;
+                        wv[kk][vw] = ld16<WT>(p.W1, static_cast<size_t>(m) * (d + h) + static_cast<size_t>(cc) * EPC);
 #pragma unroll
-                            for (int t = 0; t < PW; ++t)
-                                if (wave + t * NWAVE < p.K)
-                                    xv[kk][vw][t] = ld16<WT>(p.H, static_cast<size_t>(wave + t * NWAVE) * d +
-                                                                      static_cast<size_t>(c) * EPC);
+                        for (int t = 0; t < PW; ++t) {
+                            const int ii = wave + t * NWAVE < p.K ? wave + t * NWAVE : 0;
+                            xv[kk][vw][t] = ld16<WT>(p.H, static_cast<size_t>(ii) * d + static_cast<size_t>(cc) * EPC);
                         }
                     }
 #pragma unroll

@@ -419,14 +419,42 @@ __device__ __forceinline__ void state_cache_load(const Params &p, int blk, int n
     const int row_words = h * static_cast<int>(sizeof(WT)) / 4;
     uint4 *wc = reinterpret_cast<uint4 *>(cache);
     float *ac = cache + NWAVE * rpw * row_words;
+    constexpr int CPL = (2048 / EPC + 63) / 64;  // 16-byte chunks per lane of a row at the largest h
+    constexpr int RB = 16 / CPL;                 // rows whose loads go out together (16 registers of 16 bytes)
+    const int nchk = h / EPC, m0 = state_row0(blk, nblk, wave), mstep = nblk * NWAVE;
+    for (int k0 = 0; k0 < rpw && m0 + k0 * mstep < R; k0 += RB) {
+        // the loads of RB rows first, every one issued (rows past the wave's last and
+        // chunks past h read the group's first row / chunk 0), then the LDS stores
+        uint4 v[RB][CPL];
+#pragma unroll
+        for (int kk = 0; kk < RB; ++kk) {
+            const int k = k0 + kk, m = m0 + k * mstep;
+            const int mc = (k < rpw && m < R) ? m : m0 + k0 * mstep;
+            const void *W = mc < p.r ? p.W1 : p.W_hh;
+            const size_t off = state_row_off<WT>(p, mc);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int ch = lane + c * 64;
+                v[kk][c] = ld16<WT>(W, off + static_cast<size_t>(ch < nchk ? ch : 0) * EPC);
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < RB; ++kk) {
+            const int k = k0 + kk, m = m0 + k * mstep;
+            if (k < rpw && m < R) {
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const int ch = lane + c * 64;
+                    if (ch < nchk)
+                        wc[(wave * rpw + k) * nchk + ch] = v[kk][c];
+                }
+            }
+        }
+    }
     for (int k = 0; k < rpw; ++k) {
-        const int m = state_row0(blk, nblk, wave) + k * nblk * NWAVE;
+        const int m = m0 + k * mstep;
         if (m >= R)
             break;
-        const void *W = m < p.r ? p.W1 : p.W_hh;
-        const size_t off = state_row_off<WT>(p, m);
-        for (int ch = lane; ch < h / EPC; ch += 64)
-            wc[(wave * rpw + k) * (h / EPC) + ch] = ld16<WT>(W, off + static_cast<size_t>(ch) * EPC);
         if (m < p.r) {
             for (int i = lane; with_ah && i < p.K * p.B; i += 64) {
                 const int qq = i / p.B, b = i % p.B;

@@ -621,7 +621,9 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                     const int i = i0 + e * NT;
                     const int ic = i < ne ? i : 0;
                     const int bb = ic / h, j = ic % h, b = b0 + bb;
-                    sp[e] = (q == 0) ? state_prev(p, 0, b, j) : S_lds[bb * h + j];
+                    // (an element past the end reads no S_lds entry: that entry belongs to
+                    // another thread, which may be writing it)
+                    sp[e] = (q == 0) ? state_prev(p, 0, b, j) : (i < ne ? S_lds[bb * h + j] : 0.f);
                     if (p.P) {
                         const float *prow = p.P + static_cast<size_t>(tokl[bb]) * h3;
                         gv[e][0] = prow[j];

@@ -15,6 +15,7 @@ size_t w2_smem();          // its dynamic LDS per block
 int w2_grid(int B, int cus);  // blocks for B batch rows on cus compute units
 const void *state_kernel(int B, int h);  // state dots on the matrix cores (bf16 weights): arguments (Params, int q)
 int state_grid(int B, int r, int h);
-const void *ah_kernel();      // k_ah_mfma (bf16 H and W1, d and r multiples of 32): arguments (Params)
+const void *ah_kernel(int B, int K, int r);  // k_ah_mfma for B K rows (bf16 H and W1, d and r multiples
+                                             // of 32): arguments (Params)
 int ah_grid(int B, int K, int r);
 }  // namespace dhbat

@@ -857,7 +857,8 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
     if (ah_mfma) {
         p.ah_external = 1;
         void *args[] = {&p};
-        HIP_TRY(hipLaunchKernel(dhbat::ah_kernel(), dim3(dhbat::ah_grid(B, c.K, c.r)), dim3(dhbat::threads()), args, 0,
+        HIP_TRY(hipLaunchKernel(dhbat::ah_kernel(B, c.K, c.r), dim3(dhbat::ah_grid(B, c.K, c.r)), dim3(dhbat::threads()),
+                                args, 0,
                                 st),
                 "launch A_H (matrix cores)");
     }

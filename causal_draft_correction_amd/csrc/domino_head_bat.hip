@@ -526,39 +526,39 @@ __global__ __launch_bounds__(NT) void k_state_lds(Params p, int q)
 // phase_ah): rows R = b * K + i of H (bf16, [B*K, d]) times rows m of W1's
 // first d columns; A_H[R][m] in fp32.  A block takes 32 H rows x 32 W1 rows
 // (2 x 2 tiles of v_mfma_f32_16x16x32_bf16, split-K over d).
-template <typename WT, int KU = 8>
+// NA x NB 16-row tiles per block (32 x 32 below 2048 rows; 64 x 64 from there,
+// which halves the operand rows each output reads through L2)
+template <typename WT, int NA, int NB, int KU>
 __global__ __launch_bounds__(NT) void k_ah_mfma(Params p)
 {
-    __shared__ f32x4_t part[(NWAVE - 1) * 2 * 2 * 64];
+    __shared__ f32x4_t part[(NWAVE - 1) * NA * NB * 64];
     const int d = p.d, r = p.r, M = p.B * p.K;
     const int lane = threadIdx.x & 63, col = lane & 15;
-    const int tiles_n = r / 32, tiles_m = (M + 31) / 32;
+    const int tiles_n = r / (NB * 16), tiles_m = (M + NA * 16 - 1) / (NA * 16);
     const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
     const int tm = tile / tiles_n, tn = tile % tiles_n;
-    const int R0 = tm * 32, m0 = tn * 32;
-    const bf16s *arow[2];
-    bool aok[2];
+    const int R0 = tm * NA * 16, m0 = tn * NB * 16;
+    const bf16s *arow[NA];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < NA; ++a) {
         const int R = R0 + a * 16 + col;
-        aok[a] = R < M;
-        arow[a] = static_cast<const bf16s *>(p.H) + static_cast<size_t>(aok[a] ? R : 0) * d + (lane >> 4) * 8;
+        arow[a] = static_cast<const bf16s *>(p.H) + static_cast<size_t>(R < M ? R : 0) * d + (lane >> 4) * 8;
     }
-    const bf16s *wrow[2];
+    const bf16s *wrow[NB];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NB; ++t)
         wrow[t] = static_cast<const bf16s *>(p.W1) + static_cast<size_t>(m0 + t * 16 + col) * (d + p.h) + (lane >> 4) * 8;
-    f32x4_t acc[2][2];
-    const bool lead = splitk_tile<2, 2, KU>(
+    f32x4_t acc[NA][NB];
+    const bool lead = splitk_tile<NA, NB, KU>(
         d / 32,
-        [&](int s, uint4(&av)[2], uint4(&wv)[2]) {
+        [&](int s, uint4(&av)[NA], uint4(&wv)[NB]) {
             const int k = s * 32;
             // rows past B K read row 0 (clamped pointer); their results are not stored
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int a = 0; a < NA; ++a)
                 av[a] = *reinterpret_cast<const uint4 *>(arow[a] + k);
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < NB; ++t)
                 wv[t] = *reinterpret_cast<const uint4 *>(wrow[t] + k);
         },
         acc, part);
@@ -566,9 +566,9 @@ __global__ __launch_bounds__(NT) void k_ah_mfma(Params p)
         return;
     // D: lane l holds H rows (l/16)*4 + i of the A tile, W1 row l%16 of the B tile
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < NB; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int R = R0 + a * 16 + (lane >> 4) * 4 + i;
@@ -636,8 +636,16 @@ const void *state_kernel(int B, int h)
     return state_staged(B, h) ? reinterpret_cast<const void *>(&k_state_lds<bf16s>)
                               : reinterpret_cast<const void *>(&k_state_mfma<bf16s>);
 }
-const void *ah_kernel() { return reinterpret_cast<const void *>(&k_ah_mfma<bf16s>); }
-int ah_grid(int B, int K, int r) { return (B * K + 31) / 32 * (r / 32); }
+static bool ah_wide(int B, int K, int r) { return B * K >= 2048 && r % 64 == 0; }
+const void *ah_kernel(int B, int K, int r)
+{
+    return ah_wide(B, K, r) ? reinterpret_cast<const void *>(&k_ah_mfma<bf16s, 4, 4, 4>)
+                            : reinterpret_cast<const void *>(&k_ah_mfma<bf16s, 2, 2, 8>);
+}
+int ah_grid(int B, int K, int r)
+{
+    return ah_wide(B, K, r) ? (B * K + 63) / 64 * (r / 64) : (B * K + 31) / 32 * (r / 32);
+}
 int state_grid(int B, int r, int h)
 {
     return state_staged(B, h) ? ((B + 63) / 64) * ((r + 3 * h + 63) / 64) : ((B + 31) / 32) * ((r + 3 * h + 31) / 32);

@@ -21,11 +21,12 @@ namespace DH_NS {
 // of the resident kernel).  Chunks of W2 are staged through LDS in the
 // B-operand layout ([tile][step][lane], 16 bytes each), double buffered, with
 // the registers of the chunk after next loaded while the current chunk is
-// multiplied (v_mfma_f32_16x16x32_bf16, D = A W2_tile^T).  The epilogue adds
-// each batch row's hi and lo results, which one v_permlane32_swap of two A
-// tiles' results lines up (sum hi + lo, the resident kernel's order), adds
-// L_base (loaded two chunks ahead, through the cache), stores L_final if requested and folds the
-// greedy argmax into a running best per lane.  At the end the 16 lanes of a
+// multiplied (v_mfma_f32_16x16x32_bf16, D = A W2_tile^T).  The epilogue of a
+// chunk runs one step late, beside the next chunk's products: it adds each
+// batch row's hi and lo results, which one v_permlane32_swap of two A tiles'
+// results lines up (sum hi + lo, the resident kernel's order), adds L_base
+// (loaded a step ahead, through the cache), stores L_final if requested and
+// folds the greedy argmax into a running best per lane.  At the end the 16 lanes of a
 // batch row reduce it and one lane folds it into the partial key slot of group
 // blockIdx % NG.  Two configurations: 512 threads with AT = 2 (two waves per
 // SIMD; up to 128 rows) and 256 threads with AT = 4 (one wave per SIMD, half
@@ -143,26 +144,77 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
     };
 
     LaneBest best[NP][4];
-    // two chunks in flight: the W2 registers and the L_base values of chunk c+2 are
-    // loaded while chunk c is multiplied; register sets alternate with the chunk
-    // parity (the loop is unrolled by two so the sets are fixed)
-    uint4 st[2][PT];
+    // Software pipeline over chunks, unrolled by two so register sets are fixed
+    // by the chunk parity P.  Step c: the W2 registers of chunk c+1 (loaded one
+    // step ago) go to LDS buffer P^1, whose chunk c-1 every wave multiplied before
+    // the last barrier, and chunk c+2 is loaded into the same registers; chunk c
+    // is multiplied into accumulator set P while the epilogue of chunk c-1 runs
+    // from set P^1 (independent instructions, so the compiler interleaves the
+    // products with the vector work); then L_base of chunk c+1 is loaded into
+    // the value set just consumed, a full step before its epilogue.
+    uint4 st[PT];
     float lb[2][NP][VTG][4];
-    const int clast = nchunk - 1;  // loads past the last chunk repeat it
-    stage_load(0, st[0]);
-    lbase_load(0, lb[0]);
-    stage_store(0, st[0]);
-    stage_load(1 < clast ? 1 : clast, st[1]);
-    lbase_load(1 < clast ? 1 : clast, lb[1]);
-    __syncthreads();
-    auto step = [&](int c, int P) {
-        stage_load(c + 2 < clast ? c + 2 : clast, st[P]);
-        f32x4_t acc[AT][VTG];
+    f32x4_t acc[2][AT][VTG];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+            for (int vt = 0; vt < VTG; ++vt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lb[s2][pp][vt][i] = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int a = 0; a < AT; ++a)
 #pragma unroll
             for (int vt = 0; vt < VTG; ++vt)
-                acc[a][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                acc[s2][a][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int clast = nchunk - 1;  // loads past the last chunk repeat it
+    // the loads in flight when the loop starts are in the order of those at a
+    // step's end (W2 registers, then L_base), so the first step's wait for the
+    // W2 registers does not also take in the L_base loads
+    stage_load(0, st);
+    stage_store(0, st);
+    stage_load(1 < clast ? 1 : clast, st);
+    lbase_load(0, lb[0]);
+    __syncthreads();
+    // epilogue of chunk c (c < 0: no chunk, every value masked) from accumulator
+    // set S and L_base set S
+    auto epilogue = [&](int c, int S) {
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+            for (int vt = 0; vt < VTG; ++vt) {
+                const int vr = c * CRr + (vs * VTG + vt) * 16 + col;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    // {hi of tile 2pp, hi of tile 2pp+1} + {lo of tile 2pp, lo of tile 2pp+1}
+                    const auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[S][2 * pp][vt][i]),
+                                                                    __float_as_uint(acc[S][2 * pp + 1][vt][i]), false,
+                                                                    false);
+                    const float w = __uint_as_float(d[0]) + __uint_as_float(d[1]);
+                    const int b = brow[pp][i];
+                    // c < 0 gives vr < 0, out of range as unsigned; no short-circuit
+                    // branch, so the epilogue stays in the products' basic block
+                    const bool ok = (b < B) & (static_cast<unsigned>(vr) < static_cast<unsigned>(n));
+                    float *lf = ST ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * V + v0 : nullptr;
+                    w2_key(w, lb[S][pp][vt][i], lf, static_cast<int>(v0), vr, ok, best[pp][i]);
+                }
+            }
+    };
+    auto step = [&](int c, int P) {
+        stage_store(P ^ 1, st);
+        stage_load(c + 2 < clast ? c + 2 : clast, st);
+        // keep these loads at the top of the step: the next step's first
+        // instructions wait for them
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int a = 0; a < AT; ++a)
+#pragma unroll
+            for (int vt = 0; vt < VTG; ++vt)
+                acc[P][a][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         // the W2 operands of step kk + 1 are read from LDS while step kk is multiplied
         const uint4 *wb = wlds + P * slots + (vs * VTG * KS) * 64 + lane;
         uint4 wf[2][VTG];
@@ -180,38 +232,29 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
             for (int vt = 0; vt < VTG; ++vt)
 #pragma unroll
                 for (int a = 0; a < AT; ++a)
-                    acc[a][vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ua[a][kk]),
-                                                                        __builtin_bit_cast(bf16x8_t, wf[kk & 1][vt]),
-                                                                        acc[a][vt], 0, 0, 0);
+                    acc[P][a][vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, ua[a][kk]), __builtin_bit_cast(bf16x8_t, wf[kk & 1][vt]),
+                        acc[P][a][vt], 0, 0, 0);
         }
-#pragma unroll
-        for (int pp = 0; pp < NP; ++pp)
-#pragma unroll
-            for (int vt = 0; vt < VTG; ++vt) {
-                const int vr = c * CRr + (vs * VTG + vt) * 16 + col;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // {hi of tile 2pp, hi of tile 2pp+1} + {lo of tile 2pp, lo of tile 2pp+1}
-                    const auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[2 * pp][vt][i]),
-                                                                    __float_as_uint(acc[2 * pp + 1][vt][i]), false,
-                                                                    false);
-                    const float w = __uint_as_float(d[0]) + __uint_as_float(d[1]);
-                    const int b = brow[pp][i];
-                    const bool ok = b < B && vr < n;
-                    float *lf = ST ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * V + v0 : nullptr;
-                    w2_key(w, lb[P][pp][vt][i], lf, static_cast<int>(v0), vr, ok, best[pp][i]);
-                }
-            }
-        lbase_load(c + 2 < clast ? c + 2 : clast, lb[P]);
-        stage_store(P ^ 1, st[P ^ 1]);
+        epilogue(c - 1, P ^ 1);
+        lbase_load(c + 1 < clast ? c + 1 : clast, lb[P ^ 1]);
         __syncthreads();
     };
+    // both steps of a loop iteration run unconditionally: with the second one
+    // optional, the compiler's wait counts at the loop head would also cover the
+    // path that skips it, and the first step would wait for its own L_base loads
+    int c = 0;
 #pragma unroll 1
-    for (int c = 0; c < nchunk; c += 2) {
+    for (; c + 1 < nchunk; c += 2) {
         step(c, 0);
-        if (c + 1 < nchunk)
-            step(c + 1, 1);
+        step(c + 1, 1);
     }
+    if (c < nchunk)
+        step(c, 0);
+    if (clast & 1)
+        epilogue(clast, 1);
+    else
+        epilogue(clast, 0);
     // each batch row's best over its 16 lanes, folded into the partial key slot
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp)

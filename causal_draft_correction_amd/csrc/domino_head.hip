@@ -863,7 +863,8 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
                 "launch A_H (matrix cores)");
     }
     // bf16 heads with r = 256 take the matrix-core W2 kernel
-    const bool w2_mfma = c.wdtype == DOMINO_BF16 && c.r == dhbat::r_supported();
+    // (its load offsets are 32-bit: V < 2^22)
+    const bool w2_mfma = c.wdtype == DOMINO_BF16 && c.r == dhbat::r_supported() && c.V < (1 << 22);
     auto launch_w2 = [&](Params &pw, int rows, int pos) -> hipError_t {
         int groups = w2_mfma ? dhbat::w2_groups(rows) : 0;
         void *args[] = {&pw, &pos};

@@ -50,7 +50,8 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
     const int nbt = (B + 127) / 128, nvb = gridDim.x / nbt;  // nvb is a multiple of XCDS
     const int xcd = blockIdx.x % XCDS, j = blockIdx.x / XCDS;
     const int bt = j % nbt, vb = (j / nbt) * XCDS + xcd;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15;
+    const int lane = threadIdx.x & 63, col = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int grp = wave % ng, vs = wave / ng;
     constexpr int CRr = NVS * VTG * 16;  // chunk rows
     const int row0 = bt * 128 + grp * AT * 8;
@@ -96,16 +97,23 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
     }
 
     // staging: slot s of a chunk = (tile, step, lane) -> 16 bytes of W2.  Every load
-    // is issued on every path (rows past the range read the range's first row, whose
-    // results are masked), so the compiler's wait counts stay exact: a conditional
-    // load makes it wait for every load in flight, the chunks loaded ahead included
+    // is issued on every path, so the compiler's wait counts stay exact: a conditional
+    // load makes it wait for every load in flight, the chunks loaded ahead included.
+    // Both streams are read through buffer resources whose record counts end at the
+    // data: a load past the records returns 0 without touching memory, so rows past
+    // the range or past B need no clamped index (their results are masked).  W2: from
+    // the range's first row, n rows.  The lane's part of every offset is a constant;
+    // the rest is uniform.
+    const __amdgpu_buffer_rsrc_t w2r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(static_cast<const uint16_t *>(p.W2)) + v0 * r, 0, n * r * 2, 0x00020000);
+    const uint32_t w2lane = static_cast<uint32_t>(((lane & 15) * r + (lane >> 4) * 8) * 2);
     auto stage_load = [&](int c, uint4 (&st)[PT]) {
 #pragma unroll
         for (int jj = 0; jj < PT; ++jj) {
-            const int s = threadIdx.x + jj * NTH;
-            const int vt = s / (KS * 64), kk = (s / 64) % KS, ln = s & 63;
-            const int vr = c * CRr + vt * 16 + (ln & 15);
-            st[jj] = ld16<bf16s>(p.W2, static_cast<size_t>(v0 + (vr < n ? vr : 0)) * r + kk * 32 + (ln >> 4) * 8);
+            // slot s = threadIdx.x + jj * NTH: 64-lane group wo = s / 64 is uniform
+            const int wo = wave + jj * NWV, vt = wo / KS, kk = wo % KS;
+            const uint32_t off = static_cast<uint32_t>(((c * CRr + vt * 16) * r + kk * 32) * 2) + w2lane;
+            st[jj] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(w2r, off, 0, 0));
         }
     };
     auto stage_store = [&](int buf, const uint4 (&st)[PT]) {
@@ -121,26 +129,41 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             brow[pp][i] = row0 + (2 * pp + (lane >> 5)) * 8 + ((lane >> 4) & 1) * 4 + i;
-    // L_base of this lane's epilogue values for chunk c
+    // L_base of this lane's epilogue values for chunk c: a buffer resource from the
+    // wave's first batch row at this position to the end of L_base (batch rows past B
+    // lie past it; at most 2^32 - 1 bytes, more than the wave's 16 rows span)
+    constexpr int LES = LB16 ? 2 : 4;
+    const long long lfirst = (static_cast<long long>(row0) * p.K + pos) * V + v0;
+    const long long lleft = (static_cast<long long>(B) * p.K * V - lfirst) * LES;
+    const __amdgpu_buffer_rsrc_t lbr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(static_cast<const char *>(p.L_base)) + (lleft > 0 ? lfirst * LES : 0), 0,
+        static_cast<int>(static_cast<uint32_t>(lleft <= 0 ? 0 : lleft > 0xFFFFFFFFll ? 0xFFFFFFFFll : lleft)),
+        0x00020000);
+    // offsets in 32 bits (the host takes this kernel only for V < 2^22)
+    const uint32_t KV = static_cast<uint32_t>(p.K) * static_cast<uint32_t>(V);
+    const uint32_t lblane = (static_cast<uint32_t>((lane >> 5) * 8 + ((lane >> 4) & 1) * 4) * KV + col) * LES;
     auto lbase_load = [&](int c, float (&lb)[NP][VTG][4]) {
 #pragma unroll
         for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
-            for (int vt = 0; vt < VTG; ++vt)
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t off =
+                    lblane + (static_cast<uint32_t>(16 * pp + i) * KV + static_cast<uint32_t>(c * CRr + vs * VTG * 16)) * LES;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int b = brow[pp][i], vr = c * CRr + (vs * VTG + vt) * 16 + col;
-                    const size_t o = (static_cast<size_t>(b < B ? b : 0) * p.K + pos) * V + v0 + (vr < n ? vr : 0);
+                for (int vt = 0; vt < VTG; ++vt) {
                     // streamed once, but through the cache: one load covers a 64-byte row
                     // segment of a tile (32 bytes in bf16) and the next tile's load the
                     // rest of the line, which then hits (non-temporal loads measured 8%
                     // slower per call at B = 256)
                     if constexpr (LB16)
                         lb[pp][vt][i] = __uint_as_float(
-                            static_cast<uint32_t>(static_cast<const uint16_t *>(p.L_base)[o]) << 16);
+                            static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(lbr, off + vt * 16 * LES, 0, 0))
+                            << 16);
                     else
-                        lb[pp][vt][i] = static_cast<const float *>(p.L_base)[o];
+                        lb[pp][vt][i] =
+                            __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lbr, off + vt * 16 * LES, 0, 0));
                 }
+            }
     };
 
     LaneBest best[NP][4];
@@ -197,8 +220,10 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
                     const float w = __uint_as_float(d[0]) + __uint_as_float(d[1]);
                     const int b = brow[pp][i];
                     // c < 0 gives vr < 0, out of range as unsigned; no short-circuit
-                    // branch, so the epilogue stays in the products' basic block
-                    const bool ok = (b < B) & (static_cast<unsigned>(vr) < static_cast<unsigned>(n));
+                    // branch, so the epilogue stays in the products' basic block.  A
+                    // lane's batch row is fixed and a row past B is never folded into
+                    // a key, so without L_final stores only the vocabulary bound counts
+                    const bool ok = (!ST || b < B) & (static_cast<unsigned>(vr) < static_cast<unsigned>(n));
                     float *lf = ST ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * V + v0 : nullptr;
                     w2_key(w, lb[S][pp][vt][i], lf, static_cast<int>(v0), vr, ok, best[pp][i]);
                 }

@@ -16,21 +16,19 @@ namespace DH_NS {
 // groups of the tile (ng groups) and, when the tile has fewer groups than
 // waves, split each vocabulary chunk's 16-row tiles between nvs = waves / ng
 // wave sets (VTG tiles each).  A wave keeps its batch rows of u in registers
-// as AT matrix-core A operands: A tile a holds batch rows a*8 .. a*8+7 as bf16
-// hi parts in rows 0..7 and lo parts (u - hi) in rows 8..15 (the operand form
-// of the resident kernel).  Chunks of W2 are staged through LDS in the
-// B-operand layout ([tile][step][lane], 16 bytes each), double buffered, with
-// the registers of the chunk after next loaded while the current chunk is
-// multiplied (v_mfma_f32_16x16x32_bf16, D = A W2_tile^T).  The epilogue of a
-// chunk runs one step late, beside the next chunk's products: it adds each
-// batch row's hi and lo results, which one v_permlane32_swap of two A tiles'
-// results lines up (sum hi + lo, the resident kernel's order), adds L_base
-// (loaded a step ahead, through the cache), stores L_final if requested and
-// folds the greedy argmax into a running best per lane.  At the end the 16 lanes of a
-// batch row reduce it and one lane folds it into the partial key slot of group
-// blockIdx % NG.  Two configurations: 512 threads with AT = 2 (two waves per
-// SIMD; up to 128 rows) and 256 threads with AT = 4 (one wave per SIMD, half
-// the LDS operand traffic per result); the host uses the first.
+// as AT matrix-core A operands: A tile a holds batch rows a*8 .. a*8+7, row j's
+// bf16 hi part in operand row 2j and its lo part (u - hi) in row 2j+1, so each
+// result lane holds the hi and lo results of two batch rows side by side.
+// Chunks of W2 are staged through LDS in the B-operand layout ([tile][step]
+// [lane], 16 bytes each), double buffered, with the registers of the chunk after
+// next loaded while the current chunk is multiplied (v_mfma_f32_16x16x32_bf16,
+// D = A W2_tile^T).  The epilogue of a chunk runs one step late, beside the next
+// chunk's products: it adds each batch row's hi and lo results (hi + lo, the
+// resident kernel's order), adds L_base (loaded a step ahead, through the
+// cache), stores L_final if requested and folds the greedy argmax into a running
+// best per lane.  At the end the 16 lanes of a batch row reduce it and one lane
+// folds it into the partial key slot of group blockIdx % NG.  512 threads with
+// AT = 2: two waves per SIMD, up to 128 rows per tile.
 constexpr int XCDS = 8;   // accelerator dies (XCDs) of the MI355X, each with its own L2
 
 template <int KS, int VTG, int NVS, int AT, int NTH, bool LB16, bool ST>
@@ -38,7 +36,6 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
 {
     static_assert(AT == 2 || AT == 4, "A tiles per wave");
     constexpr int NWV = NTH / 64;
-    constexpr int NP = AT / 2;  // A-tile pairs
     constexpr int ng = NWV / NVS;  // batch groups of a tile (the host passes the same in ng_arg)
     (void)ng_arg;
     extern __shared__ uint4 wlds[];  // 2 chunk buffers
@@ -69,8 +66,10 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
     uint4 ua[AT][KS];
 #pragma unroll
     for (int a = 0; a < AT; ++a) {
-        const int b = row0 + a * 8 + (col & 7);
-        const bool hi = col < 8;
+        // operand row m = col: batch row a*8 + m/2, its hi part in even rows and its
+        // lo part in odd ones, so a result lane holds both halves of its rows
+        const int b = row0 + a * 8 + (col >> 1);
+        const bool hi = (col & 1) == 0;
         const float *src = p.u_buf + static_cast<size_t>(b < B ? b : 0) * r + (lane >> 4) * 8;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
@@ -121,14 +120,14 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
         for (int jj = 0; jj < PT; ++jj)
             wlds[buf * slots + threadIdx.x + jj * NTH] = st[jj];
     };
-    // this lane's batch rows in the combined results: pair pp packs A tiles 2pp
-    // (lanes 0..31) and 2pp+1 (lanes 32..63), row i of four
-    int brow[NP][4];
+    // this lane's batch rows: result rows 4*(lane/16) + i of A tile a are hi (i even)
+    // and lo (i odd) of batch row a*8 + 2*(lane/16) + i/2
+    int brow[AT][2];
 #pragma unroll
-    for (int pp = 0; pp < NP; ++pp)
+    for (int a = 0; a < AT; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            brow[pp][i] = row0 + (2 * pp + (lane >> 5)) * 8 + ((lane >> 4) & 1) * 4 + i;
+        for (int ii = 0; ii < 2; ++ii)
+            brow[a][ii] = row0 + a * 8 + 2 * (lane >> 4) + ii;
     // L_base of this lane's epilogue values for chunk c: a buffer resource from the
     // wave's first batch row at this position to the end of L_base (batch rows past B
     // lie past it; at most 2^32 - 1 bytes, more than the wave's 16 rows span)
@@ -141,14 +140,14 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
         0x00020000);
     // offsets in 32 bits (the host takes this kernel only for V < 2^22)
     const uint32_t KV = static_cast<uint32_t>(p.K) * static_cast<uint32_t>(V);
-    const uint32_t lblane = (static_cast<uint32_t>((lane >> 5) * 8 + ((lane >> 4) & 1) * 4) * KV + col) * LES;
-    auto lbase_load = [&](int c, float (&lb)[NP][VTG][4]) {
+    const uint32_t lblane = (static_cast<uint32_t>(2 * (lane >> 4)) * KV + col) * LES;
+    auto lbase_load = [&](int c, float (&lb)[AT][VTG][2]) {
 #pragma unroll
-        for (int pp = 0; pp < NP; ++pp)
+        for (int a = 0; a < AT; ++a)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int ii = 0; ii < 2; ++ii) {
                 const uint32_t off =
-                    lblane + (static_cast<uint32_t>(16 * pp + i) * KV + static_cast<uint32_t>(c * CRr + vs * VTG * 16)) * LES;
+                    lblane + (static_cast<uint32_t>(8 * a + ii) * KV + static_cast<uint32_t>(c * CRr + vs * VTG * 16)) * LES;
 #pragma unroll
                 for (int vt = 0; vt < VTG; ++vt) {
                     // streamed once, but through the cache: one load covers a 64-byte row
@@ -156,17 +155,17 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
                     // rest of the line, which then hits (non-temporal loads measured 8%
                     // slower per call at B = 256)
                     if constexpr (LB16)
-                        lb[pp][vt][i] = __uint_as_float(
+                        lb[a][vt][ii] = __uint_as_float(
                             static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(lbr, off + vt * 16 * LES, 0, 0))
                             << 16);
                     else
-                        lb[pp][vt][i] =
+                        lb[a][vt][ii] =
                             __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lbr, off + vt * 16 * LES, 0, 0));
                 }
             }
     };
 
-    LaneBest best[NP][4];
+    LaneBest best[AT][2];
     // Software pipeline over chunks, unrolled by two so register sets are fixed
     // by the chunk parity P.  Step c: the W2 registers of chunk c+1 (loaded one
     // step ago) go to LDS buffer P^1, whose chunk c-1 every wave multiplied before
@@ -176,17 +175,17 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
     // products with the vector work); then L_base of chunk c+1 is loaded into
     // the value set just consumed, a full step before its epilogue.
     uint4 st[PT];
-    float lb[2][NP][VTG][4];
+    float lb[2][AT][VTG][2];
     f32x4_t acc[2][AT][VTG];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int pp = 0; pp < NP; ++pp)
+        for (int a = 0; a < AT; ++a)
 #pragma unroll
             for (int vt = 0; vt < VTG; ++vt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    lb[s2][pp][vt][i] = 0.f;
+                for (int ii = 0; ii < 2; ++ii)
+                    lb[s2][a][vt][ii] = 0.f;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -207,25 +206,22 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
     // set S and L_base set S
     auto epilogue = [&](int c, int S) {
 #pragma unroll
-        for (int pp = 0; pp < NP; ++pp)
+        for (int a = 0; a < AT; ++a)
 #pragma unroll
             for (int vt = 0; vt < VTG; ++vt) {
                 const int vr = c * CRr + (vs * VTG + vt) * 16 + col;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // {hi of tile 2pp, hi of tile 2pp+1} + {lo of tile 2pp, lo of tile 2pp+1}
-                    const auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[S][2 * pp][vt][i]),
-                                                                    __float_as_uint(acc[S][2 * pp + 1][vt][i]), false,
-                                                                    false);
-                    const float w = __uint_as_float(d[0]) + __uint_as_float(d[1]);
-                    const int b = brow[pp][i];
+                for (int ii = 0; ii < 2; ++ii) {
+                    // hi + lo of the batch row (the resident kernel's order)
+                    const float w = acc[S][a][vt][2 * ii] + acc[S][a][vt][2 * ii + 1];
+                    const int b = brow[a][ii];
                     // c < 0 gives vr < 0, out of range as unsigned; no short-circuit
                     // branch, so the epilogue stays in the products' basic block.  A
                     // lane's batch row is fixed and a row past B is never folded into
                     // a key, so without L_final stores only the vocabulary bound counts
                     const bool ok = (!ST || b < B) & (static_cast<unsigned>(vr) < static_cast<unsigned>(n));
                     float *lf = ST ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * V + v0 : nullptr;
-                    w2_key(w, lb[S][pp][vt][i], lf, static_cast<int>(v0), vr, ok, best[pp][i]);
+                    w2_key(w, lb[S][a][vt][ii], lf, static_cast<int>(v0), vr, ok, best[a][ii]);
                 }
             }
     };
@@ -282,17 +278,17 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
         epilogue(clast, 0);
     // each batch row's best over its 16 lanes, folded into the partial key slot
 #pragma unroll
-    for (int pp = 0; pp < NP; ++pp)
+    for (int a = 0; a < AT; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint64_t key = best[pp][i].ord ? (static_cast<uint64_t>(best[pp][i].ord) << 32) |
-                                                 (0xFFFFFFFFu - best[pp][i].idx)
+        for (int ii = 0; ii < 2; ++ii) {
+            uint64_t key = best[a][ii].ord ? (static_cast<uint64_t>(best[a][ii].ord) << 32) |
+                                                 (0xFFFFFFFFu - best[a][ii].idx)
                                            : 0ull;
             key = max_u64(key, dpp_u64<DPP_QUAD_XOR1>(key));
             key = max_u64(key, dpp_u64<DPP_QUAD_XOR2>(key));
             key = max_u64(key, dpp_u64<DPP_HALF_MIRROR>(key));
             key = max_u64(key, dpp_u64<DPP_ROW_MIRROR>(key));
-            const int b = brow[pp][i];
+            const int b = brow[a][ii];
             if (col == 0 && b < B && key)
                 __hip_atomic_fetch_max(key_slot(p, pos, g, b), key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }

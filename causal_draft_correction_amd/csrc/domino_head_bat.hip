@@ -154,10 +154,11 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
                     // segment of a tile (32 bytes in bf16) and the next tile's load the
                     // rest of the line, which then hits (non-temporal loads measured 8%
                     // slower per call at B = 256)
+                    // bf16 values are kept as loaded and widened in the epilogue: a
+                    // conversion here would make the step wait for these loads
                     if constexpr (LB16)
                         lb[a][vt][ii] = __uint_as_float(
-                            static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(lbr, off + vt * 16 * LES, 0, 0))
-                            << 16);
+                            static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(lbr, off + vt * 16 * LES, 0, 0)));
                     else
                         lb[a][vt][ii] =
                             __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lbr, off + vt * 16 * LES, 0, 0));
@@ -221,7 +222,8 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
                     // a key, so without L_final stores only the vocabulary bound counts
                     const bool ok = (!ST || b < B) & (static_cast<unsigned>(vr) < static_cast<unsigned>(n));
                     float *lf = ST ? p.L_final + (static_cast<size_t>(b) * p.K + pos) * V + v0 : nullptr;
-                    w2_key(w, lb[S][a][vt][ii], lf, static_cast<int>(v0), vr, ok, best[a][ii]);
+                    const float lbv = LB16 ? __uint_as_float(__float_as_uint(lb[S][a][vt][ii]) << 16) : lb[S][a][vt][ii];
+                    w2_key(w, lbv, lf, static_cast<int>(v0), vr, ok, best[a][ii]);
                 }
             }
     };

@@ -376,14 +376,14 @@ __device__ __forceinline__ bool splitk_tile(int nst, Ld ld, f32x4_t (&acc)[NA][N
 // The A_H and bias values are loaded first, every load on every path (clamped
 // indices, unused values dropped), so the compiler waits once for all of them
 // instead of once per conditional load.
-template <typename WT>
-__device__ __forceinline__ void state_epilogue(const Params &p, int q, const f32x4_t (&acc)[4][2], int mbase,
+template <typename WT, int NP = 2>
+__device__ __forceinline__ void state_epilogue(const Params &p, int q, const f32x4_t (&acc)[2 * NP][2], int mbase,
                                                int bbase)
 {
     const int lane = threadIdx.x & 63, col = lane & 15;
     const int h = p.h, r = p.r, R = r + 3 * p.h, B = p.B, h3 = 3 * h;
     float *qn = q_slot(p, q + 1);
-    float ahv[2][2][4], bias[2];
+    float ahv[NP][2][4], bias[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int m = mbase + t * 16 + col;
@@ -391,7 +391,7 @@ __device__ __forceinline__ void state_epilogue(const Params &p, int q, const f32
         const int mu = m < r ? m : 0;
         bias[t] = p.b_hh ? WT16<WT>::one(p.b_hh, mq) : 0.f;
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
+        for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int b = bbase + (2 * pp + (lane >> 5)) * 8 + ((lane >> 4) & 1) * 4 + i;
@@ -399,7 +399,7 @@ __device__ __forceinline__ void state_epilogue(const Params &p, int q, const f32
             }
     }
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp)
+    for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int m = mbase + t * 16 + col;
@@ -477,15 +477,16 @@ __global__ __launch_bounds__(NT) void k_state_mfma(Params p, int q)
 }
 
 // The same state dots with the operands staged in LDS (h a multiple of 256).  A
-// block takes 64 batch rows (8 A tiles of S hi/lo rows) x 64 weight rows (4 B
-// tiles).  The h reduction runs in stages of 64 (two 32-wide steps); a stage's
-// 24 operand blocks (per step: 8 A + 4 B tiles, 1 KB each in the matrix-core
-// operand layout) are copied by 16-byte direct global-to-LDS loads, three stages
-// ahead, into a ring of four LDS buffers, so the loads use no registers and the
-// S rows are read once per block instead of once per wave.  Each wave multiplies
-// 4 A tiles x 2 B tiles; one barrier per stage.  The products run over k in
+// block takes 32 batch rows (4 A tiles of S hi/lo rows) x 64 weight rows (4 B
+// tiles): more blocks than compute units at B = 256, two resident per unit.  The
+// h reduction runs in stages of 64 (two 32-wide steps); a stage's 16 operand
+// blocks (per step: 4 A + 4 B tiles, 1 KB each in the matrix-core operand
+// layout) are copied by 16-byte direct global-to-LDS loads, three stages ahead,
+// into a ring of four LDS buffers, so the loads use no registers and the S rows
+// are read once per block instead of once per wave.  Each wave multiplies 2 A
+// tiles x 2 B tiles; one barrier per stage.  The products run over k in
 // the same order as in k_state_mfma's single pass.
-constexpr int SL_BLOCKS = 12;                // operand blocks per step: 8 A + 4 B tiles
+constexpr int SL_BLOCKS = 8;                 // operand blocks per step: 4 A + 4 B tiles
 constexpr int SL_STAGE = 2 * SL_BLOCKS * 64; // uint4 per stage (two steps)
 
 template <typename WT>
@@ -495,25 +496,25 @@ __global__ __launch_bounds__(NT) void k_state_lds(Params p, int q)
     __shared__ uint4 ring0[SL_STAGE], ring1[SL_STAGE], ring2[SL_STAGE], ring3[SL_STAGE];
     static_assert(NWAVE == 4, "four waves: 2 x 2 over the A and B tiles");
     const int h = p.h, r = p.r, R = r + 3 * p.h, B = p.B;
-    const int nbg = (B + 63) / 64, nwb = (R + 63) / 64;
+    const int nbg = (B + 31) / 32, nwb = (R + 63) / 64;
     const int tile = xcd_tile(blockIdx.x, nbg * nwb);
     const int bg = tile % nbg, wbk = tile / nbg;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int b0 = bg * 64, mw = wbk * 64;
+    const int b0 = bg * 32, mw = wbk * 64;
     const int NS = h / 64;  // stages, a multiple of 4
-    // this lane's source of the 6 operand blocks this wave copies per stage:
-    // block j = wave * 6 + u = step * 12 + t, t < 8: A tile t, else B tile t - 8.
+    // this lane's source of the 4 operand blocks this wave copies per stage:
+    // block j = wave * 4 + u = step * 8 + t, t < 4: A tile t, else B tile t - 4.
     // Rows past B or R repeat the last row (their results are not stored).
-    const uint16_t *src[6];
+    const uint16_t *src[4];
 #pragma unroll
-    for (int u = 0; u < 6; ++u) {
-        const int j = wave * 6 + u, ks = j / SL_BLOCKS, t = j % SL_BLOCKS, i = lane & 15;
+    for (int u = 0; u < 4; ++u) {
+        const int j = wave * 4 + u, ks = j / SL_BLOCKS, t = j % SL_BLOCKS, i = lane & 15;
         const uint16_t *base;
-        if (t < 8) {
+        if (t < 4) {
             const int b = b0 + t * 8 + (i & 7) < B ? b0 + t * 8 + (i & 7) : B - 1;
             base = p.s_hl + (static_cast<size_t>(i >> 3) * p.maxB + b) * p.ldw;
         } else {
-            const int m = mw + (t - 8) * 16 + i < R ? mw + (t - 8) * 16 + i : R - 1;
+            const int m = mw + (t - 4) * 16 + i < R ? mw + (t - 4) * 16 + i : R - 1;
             base = p.wst ? p.wst + static_cast<size_t>(m) * p.ldw
                    : m < r ? static_cast<const uint16_t *>(p.W1) + static_cast<size_t>(m) * (p.d + h) + p.d
                            : static_cast<const uint16_t *>(p.W_hh) + static_cast<size_t>(m - r) * h;
@@ -522,36 +523,36 @@ __global__ __launch_bounds__(NT) void k_state_lds(Params p, int q)
     }
     auto issue = [&](int s, uint4 *ring) {
 #pragma unroll
-        for (int u = 0; u < 6; ++u)
-            __builtin_amdgcn_global_load_lds(src[u] + s * 64, (lds_void *)(ring + (wave * 6 + u) * 64), 16, 0, 0);
+        for (int u = 0; u < 4; ++u)
+            __builtin_amdgcn_global_load_lds(src[u] + s * 64, (lds_void *)(ring + (wave * 4 + u) * 64), 16, 0, 0);
     };
     const int wa = wave & 1, wb = wave >> 1;
-    f32x4_t acc[4][2];
+    f32x4_t acc[2][2];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
             acc[a][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](const uint4 *ring) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            uint4 av[4], bv[2];
+            uint4 av[2], bv[2];
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-                av[a] = ring[(ks * SL_BLOCKS + wa * 4 + a) * 64 + lane];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-                bv[t] = ring[(ks * SL_BLOCKS + 8 + wb * 2 + t) * 64 + lane];
+            for (int a = 0; a < 2; ++a)
+                av[a] = ring[(ks * SL_BLOCKS + wa * 2 + a) * 64 + lane];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
+                bv[t] = ring[(ks * SL_BLOCKS + 4 + wb * 2 + t) * 64 + lane];
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
                     acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[a]),
                                                                        __builtin_bit_cast(bf16x8_t, bv[t]), acc[a][t],
                                                                        0, 0, 0);
         }
     };
-    // wait until at most `later` stages of this wave's copies are outstanding (6 loads
+    // wait until at most `later` stages of this wave's copies are outstanding (4 loads
     // each), then a barrier: every wave has waited for its own copies of the stage, so
     // the stage is in LDS for all of them.  The barrier is the bare instruction: a
     // __syncthreads() would also wait for the copies of the later stages.  Each wave's
@@ -560,9 +561,9 @@ __global__ __launch_bounds__(NT) void k_state_lds(Params p, int q)
     auto arrive = [&](int later) {
         // s_waitcnt vmcnt(N): expcnt and lgkmcnt left at their maxima
         if (later >= 2)
-            __builtin_amdgcn_s_waitcnt(12 | (7 << 4) | (15 << 8));
+            __builtin_amdgcn_s_waitcnt(8 | (7 << 4) | (15 << 8));
         else if (later == 1)
-            __builtin_amdgcn_s_waitcnt(6 | (7 << 4) | (15 << 8));
+            __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8));
         else
             __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
         asm volatile("" ::: "memory");
@@ -585,7 +586,7 @@ __global__ __launch_bounds__(NT) void k_state_lds(Params p, int q)
         step(s + 2, ring2, ring1);
         step(s + 3, ring3, ring2);
     }
-    state_epilogue<WT>(p, q, acc, mw + wb * 32, b0 + wa * 32);
+    state_epilogue<WT, 1>(p, q, acc, mw + wb * 32, b0 + wa * 16);
 }
 
 // A_H = W1[:, :d] H for every position on the matrix cores (same quantity as
@@ -714,7 +715,7 @@ int ah_grid(int B, int K, int r)
 }
 int state_grid(int B, int r, int h)
 {
-    return state_staged(B, h) ? ((B + 63) / 64) * ((r + 3 * h + 63) / 64) : ((B + 31) / 32) * ((r + 3 * h + 31) / 32);
+    return state_staged(B, h) ? ((B + 31) / 32) * ((r + 3 * h + 63) / 64) : ((B + 31) / 32) * ((r + 3 * h + 31) / 32);
 }
 
 }  // namespace dhbat

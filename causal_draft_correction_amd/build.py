@@ -4,15 +4,17 @@ from __future__ import annotations
 import os
 import shutil
 import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC_DIR = os.path.join(HERE, "csrc")
-MAIN_SRC = os.path.join(SRC_DIR, "domino_head.hip")
-RES_SRC = os.path.join(SRC_DIR, "domino_head_res.hip")
-BAT_SRC = os.path.join(SRC_DIR, "domino_head_bat.hip")
-VER_SRC = os.path.join(SRC_DIR, "domino_verify.hip")
+UNITS = ["domino_head.hip", "domino_head_res.hip", "domino_head_bat.hip", "domino_head_rb.hip", "domino_verify.hip"]
 LIB = os.path.join(HERE, "libdomino_head.so")
 ARCH = "gfx950"
+# packed-fp32 instructions are disabled in all device code
+FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",
+         "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]
 
 
 def hipcc() -> str:
@@ -37,18 +39,27 @@ def stale() -> bool:
     return any(os.path.getmtime(s) > t for s in sources())
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library for gfx950.  Packed-fp32 instructions are disabled."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wall", "-Wno-unused-function", MAIN_SRC, RES_SRC, BAT_SRC, VER_SRC, "-o", tmp]
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (res.stderr or "").splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + errs)
-    if verbose and errs.strip():
-        print(errs)
+    return errs
+
+
+def build(verbose: bool = False) -> str:
+    """Compile each translation unit for gfx950 (in parallel), then link the library."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="domino_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, u.replace(".hip", ".o")) for u in UNITS]
+        jobs = [[cc] + FLAGS + ["-c", os.path.join(SRC_DIR, u), "-o", o] for u, o in zip(UNITS, objs)]
+        workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            errs = list(ex.map(_run, jobs))
+        tmp = LIB + ".tmp%d" % os.getpid()
+        errs.append(_run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]))
+    if verbose and any(e.strip() for e in errs):
+        print("\n".join(e for e in errs if e.strip()))
     os.replace(tmp, LIB)
     return LIB
 

@@ -30,6 +30,10 @@ struct Params {
     int ldw;              // row stride of s_hl and wst in elements
     float *g_buf;    // [maxB, 3h]    W_ih E[x] + b_ih (when not folded)
     uint64_t *keys;  // [K, NG, maxB] partial argmax keys
+    uint64_t *bkeys; // batched resident launch: [maxB, grid] argmax key word of every block for every
+                     // batch row, generation-tagged
+    uint4 *uop;      // batched resident launch: u as the W2 products' operand, [maxB/16][hi, lo][r/32][64]
+                     // 16-byte chunks (8 bf16 of one batch row each), or nullptr
     unsigned *bar;   // barrier words
     uint64_t *asy;   // argmax barrier words
     unsigned *flags; // device flags

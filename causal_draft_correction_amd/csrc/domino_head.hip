@@ -30,6 +30,7 @@
 #include "dh_resident.h"
 #include "dh_batched.h"
 #include "dh_verify.h"
+#include "dh_rbatch.h"
 
 using namespace dh;
 
@@ -39,6 +40,15 @@ using namespace dh;
 
 // Barrier words, argmax words, u operand words (tag 0: generations restart
 // at 0 and the first tag a launch polls for is at least 1) and device flags.
+// Argmax words of the batched resident launch: tag 0, which no launch polls for
+// (every launch starts from a barrier generation of at least 0 and its first
+// poll expects a tag three generations later).
+__global__ __launch_bounds__(256) void k_clear_words(uint64_t *w, size_t n)
+{
+    for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<size_t>(gridDim.x) * 256)
+        w[i] = 0ull;
+}
+
 __global__ __launch_bounds__(256) void k_clear_state(unsigned *bar, uint64_t *asy, uint32_t *utag, int n_utag,
                                                      unsigned *flags)
 {
@@ -366,7 +376,8 @@ constexpr int W2_STEP_ROWS = 128;  // vocabulary rows per block in stepwise W2 l
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, u_all, utag, s_hl, q_buf, g_buf, P, M, mk_tmp, wst, total;
+    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, u_all, utag, s_hl, q_buf, g_buf, P, M, mk_tmp, wst, bkeys, uop,
+        total;
 };
 
 // Packed state-dot rows for the matrix-core state launches (bf16 heads): the rows of
@@ -419,6 +430,15 @@ Layout layout_of(const domino_head_config &c)
     L.wst = off;
     if (packed_state_rows(c))
         off = align_up(off + sizeof(uint16_t) * static_cast<size_t>(c.r + 3 * c.h) * packed_ldw(c));
+    // batched resident launch: argmax words [max_batch, MAX_GRID] and the u operand
+    // [max_batch / 16 groups][hi, lo][r / 32][64] x 16 bytes
+    L.bkeys = off;
+    L.uop = off;
+    if (packed_state_rows(c)) {
+        off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(c.max_batch) * MAX_GRID);
+        L.uop = off;
+        off = align_up(off + sizeof(uint16_t) * 2 * static_cast<size_t>((c.max_batch + 15) / 16 * 16) * c.r);
+    }
     L.M = off;
     L.mk_tmp = off;
     if (c.flags & DOMINO_MARKOV) {
@@ -565,6 +585,7 @@ struct domino_head {
     int persist_grid;      // blocks of the persistent launch (0: cannot be co-resident)
     size_t persist_smem;
     int res_grid;          // blocks of the resident-W2 persistent launch (0: not usable)
+    int rb_grid;           // blocks of the batched resident-W2 persistent launch (0: not usable)
     size_t res_smem;
     bool state_ready;      // barrier words and flags cleared on the device
     hipStream_t last_stream;
@@ -573,10 +594,19 @@ struct domino_head {
 
 // Launch taken by a draft of B rows: the single cooperative launch (persistent) or the
 // per-step launches; the persistent one keeps W2 on chip (resident) when that variant
-// fits.  Returns false when the handle forces a persistent launch that cannot run.
-static bool choose_launch(const domino_head *hd, int B, bool *persistent, bool *resident)
+// fits: up to BC rows the kernel that computes the whole state in every block, above
+// that (bf16, r = 256, folded table) the batched kernel (*batched) that distributes
+// the state update and the state dots.  Returns false when the handle forces a
+// persistent launch that cannot run.
+static bool choose_launch(const domino_head *hd, int B, bool *persistent, bool *resident, bool *batched)
 {
     const unsigned fl = hd->cfg.flags;
+    *batched = false;
+    if (!(fl & DOMINO_MARKOV) && B > BC && hd->rb_grid > 0 && B <= dhrb::max_batch() &&
+        !(fl & (DOMINO_EXEC_STEPWISE | DOMINO_EXEC_STREAM_W2))) {
+        *persistent = *resident = *batched = true;
+        return true;
+    }
     if (fl & DOMINO_MARKOV) {
         // a Markov head takes its resident-W2 kernel (bf16, r = 256, B <= 8) or the step launches
         const bool can = hd->res_grid > 0 && B <= BC;
@@ -710,6 +740,22 @@ int domino_head_create(const domino_head_config *cfg, void *workspace, size_t wo
         if (fits)
             hd->res_grid = cus;
     }
+    // batched resident-W2 variant (B > BC): bf16, r = 256, folded table, packed state
+    // rows, one 256-thread block per compute unit with static LDS only
+    hd->rb_grid = 0;
+    if (cfg->wdtype == DOMINO_BF16 && (cfg->flags & DOMINO_FOLD_EMBED) && !(cfg->flags & DOMINO_MARKOV) &&
+        packed_state_rows(*cfg) && dhrb::supports(cfg->d, cfg->h, cfg->r, cfg->V, cus)) {
+        bool fits = true;
+        for (int lb16 = 0; lb16 < 2; ++lb16)
+            for (int stl = 0; stl < 2; ++stl) {
+                int per_cu_b = 0;
+                hipError_t eb = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &per_cu_b, dhrb::kernel(lb16 != 0, stl != 0, cfg->V), dhrb::threads(), 0);
+                fits = fits && eb == hipSuccess && per_cu_b >= 1;
+            }
+        if (fits)
+            hd->rb_grid = cus;
+    }
     *out = hd;
     return DOMINO_OK;
 }
@@ -793,24 +839,62 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
     if (dev != hd->device)
         return fail(DOMINO_EINVAL, "current device %d differs from the handle's device %d", dev, hd->device);
 
-    bool persistent, resident;
-    if (!choose_launch(hd, B, &persistent, &resident))
-        return fail(DOMINO_EUNSUPPORTED, "persistent launch needs B <= %d and one resident block per compute unit", BC);
+    bool persistent, resident, batched;
+    if (!choose_launch(hd, B, &persistent, &resident, &batched))
+        return fail(DOMINO_EUNSUPPORTED, "persistent launch needs B <= %d, or a bf16 head with r = %d, the folded "
+                    "table and B <= %d, and one resident block per compute unit", BC, dhrb::r_supported(),
+                    dhrb::max_batch());
     if (teacher && (c.flags & DOMINO_EXEC_POSITION_BATCHED))
-        persistent = resident = false;
+        persistent = resident = batched = false;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (persistent && !(c.flags & DOMINO_EXEC_PLAIN_LAUNCH)) {
+        // a cooperative launch cannot be recorded into a HIP graph
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        HIP_TRY(hipStreamIsCapturing(st, &cap), "hipStreamIsCapturing");
+        if (cap != hipStreamCaptureStatusNone)
+            return fail(DOMINO_EUNSUPPORTED, "the persistent launch is cooperative and cannot be captured; create the "
+                        "handle with DOMINO_EXEC_PLAIN_LAUNCH or DOMINO_EXEC_STEPWISE to capture draft calls");
+    }
     if (!hd->state_ready) {
         hipLaunchKernelGGL(k_clear_state, dim3(1), dim3(256), 0, st, reinterpret_cast<unsigned *>(hd->ws + hd->L.bar),
                            reinterpret_cast<uint64_t *>(hd->ws + hd->L.asy),
                            reinterpret_cast<uint32_t *>(hd->ws + hd->L.utag), 2 * c.max_batch * c.r,
                            reinterpret_cast<unsigned *>(hd->ws + hd->L.flags));
         HIP_TRY(hipGetLastError(), "launch k_clear_state");
+        if (hd->L.uop > hd->L.bkeys) {
+            // with the barrier generations restarting at 0, no old argmax word may keep its tag
+            hipLaunchKernelGGL(k_clear_words, dim3(256), dim3(256), 0, st,
+                               reinterpret_cast<uint64_t *>(hd->ws + hd->L.bkeys),
+                               static_cast<size_t>(c.max_batch) * MAX_GRID);
+            HIP_TRY(hipGetLastError(), "launch k_clear_words");
+        }
         hd->state_ready = true;
     }
     Params p = make_params(hd, B, H, L_base, last_tok, teacher, S_init, tokens, L_final, S_out, u_out, persistent);
     if (resident && !markov)
         p.utag = reinterpret_cast<uint32_t *>(hd->ws + hd->L.utag);
     hd->last_stream = st;
+    if (batched) {
+        // A_H of every position on the matrix cores, then the one persistent launch
+        p.s_hl = reinterpret_cast<uint16_t *>(hd->ws + hd->L.s_hl);
+        p.wst = reinterpret_cast<const uint16_t *>(hd->ws + hd->L.wst);
+        p.ldw = packed_ldw(c);
+        p.bkeys = reinterpret_cast<uint64_t *>(hd->ws + hd->L.bkeys);
+        p.uop = reinterpret_cast<uint4 *>(hd->ws + hd->L.uop);
+        p.ah_external = 1;
+        void *args[] = {&p};
+        HIP_TRY(hipLaunchKernel(dhbat::ah_kernel(B, c.K, c.r), dim3(dhbat::ah_grid(B, c.K, c.r)),
+                                dim3(dhbat::threads()), args, 0, st),
+                "launch A_H (matrix cores)");
+        const void *fn = dhrb::kernel(p.lbase_bf16 != 0, L_final != nullptr, c.V);
+        if (c.flags & DOMINO_EXEC_PLAIN_LAUNCH)
+            HIP_TRY(hipLaunchKernel(fn, dim3(hd->rb_grid), dim3(dhrb::threads()), args, 0, st),
+                    "hipLaunchKernel(batched persistent)");
+        else
+            HIP_TRY(hipLaunchCooperativeKernel(fn, dim3(hd->rb_grid), dim3(dhrb::threads()), args, 0, st),
+                    "hipLaunchCooperativeKernel(batched persistent)");
+        return DOMINO_OK;
+    }
     if (persistent) {
         void *args[] = {&p};
         const void *fn = resident ? (markov ? dhres::markov_kernel(B) : dhres::kernel(B)) : hd->kern.persistent;
@@ -1020,15 +1104,17 @@ int domino_head_exec_info(domino_head_t hd, int32_t B, int32_t *persistent, int3
         return fail(DOMINO_EINVAL, "handle is NULL");
     if (B < 1 || B > hd->cfg.max_batch)
         return fail(DOMINO_EINVAL, "B=%d outside [1, max_batch=%d]", B, hd->cfg.max_batch);
-    bool pers, res;
-    if (!choose_launch(hd, B, &pers, &res))
-        return fail(DOMINO_EUNSUPPORTED, "persistent launch needs B <= %d and one resident block per compute unit", BC);
+    bool pers, res, bat;
+    if (!choose_launch(hd, B, &pers, &res, &bat))
+        return fail(DOMINO_EUNSUPPORTED, "persistent launch needs B <= %d, or a bf16 head with r = %d, the folded "
+                    "table and B <= %d, and one resident block per compute unit", BC, dhrb::r_supported(),
+                    dhrb::max_batch());
     if (persistent)
         *persistent = pers;
     if (w2_resident)
         *w2_resident = res;
     if (grid)
-        *grid = !pers ? 0 : res ? hd->res_grid : hd->persist_grid;
+        *grid = !pers ? 0 : bat ? hd->rb_grid : res ? hd->res_grid : hd->persist_grid;
     return DOMINO_OK;
 }
 
@@ -1038,7 +1124,9 @@ int domino_head_check_error(domino_head_t hd, uint32_t *device_flags)
         return fail(DOMINO_EINVAL, "handle is NULL");
     uint32_t f = 0;
     if (hd->state_ready) {
-        HIP_TRY(hipStreamSynchronize(hd->last_stream), "hipStreamSynchronize");
+        // every stream: drafts may also have run as replays of a captured graph on a
+        // stream other than the one of the last eager call
+        HIP_TRY(hipDeviceSynchronize(), "hipDeviceSynchronize");
         HIP_TRY(hipMemcpy(&f, hd->ws + hd->L.flags, sizeof f, hipMemcpyDeviceToHost), "hipMemcpy(flags)");
         // the next draft clears barrier words and flags before it runs
         hd->state_ready = false;

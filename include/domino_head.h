@@ -57,7 +57,10 @@ extern "C" {
 
 /* ---- config.flags bits (execution strategy; results do not depend on them) ---- */
 #define DOMINO_EXEC_AUTO 0u        /* pick per call from B */
-#define DOMINO_EXEC_PERSISTENT 1u  /* one cooperative launch covering all K positions */
+#define DOMINO_EXEC_PERSISTENT 1u  /* one cooperative launch covering all K positions: B <= 8, or (bf16
+                                      weights, r = 256, DOMINO_FOLD_EMBED, h a multiple of 64, d of 32)
+                                      B <= 256, where the GRU update and state products are spread over
+                                      the grid; either way each block keeps its W2 slice on chip */
 #define DOMINO_EXEC_STEPWISE 2u    /* one launch per phase and position */
 #define DOMINO_EXEC_STREAM_W2 8u   /* persistent launch: stream W2 from memory at every position instead of
                                       keeping the slice on chip (bf16, r = 256); for comparison */
@@ -205,9 +208,11 @@ int domino_verify(int32_t B, int32_t K, int32_t V, const float *logits, const in
                   size_t workspace_bytes, int32_t *target, int32_t *accept, int32_t *next, void *stream);
 
 /*
- * Synchronizes the stream of the handle's last draft, reads and clears the
- * device flags (DOMINO_FLAG_*) into *device_flags (may be NULL) and resets
- * the handle's barrier state.  Returns DOMINO_EDEVICE if any flag was set.
+ * Synchronizes the device (every stream, so drafts replayed from a captured
+ * HIP graph on any stream are included), reads and clears the device flags
+ * (DOMINO_FLAG_*) into *device_flags (may be NULL) and resets the handle's
+ * barrier state (the next draft clears it on the device before it runs).
+ * Returns DOMINO_EDEVICE if any flag was set.
  */
 int domino_head_check_error(domino_head_t hd, uint32_t *device_flags);
 
@@ -222,7 +227,13 @@ int domino_head_check_error(domino_head_t hd, uint32_t *device_flags);
  */
 int domino_head_exec_info(domino_head_t hd, int32_t B, int32_t *persistent, int32_t *w2_resident, int32_t *grid);
 
-/* Host only.  Parameters of the head: r(d+h) + V r + 3h d + 3h h (+ 6h if GRU biases are given). */
+/*
+ * Host only.  Parameters of the head: r(d+h) + V r + 3h d + 3h h (+ 6h if GRU
+ * biases are given); the embedding table E is the target's and not counted.
+ * The paper.oopus.info review (section 二, 第二步 Domino Head) puts the head at
+ * about 56 million parameters, 5.3% of the drafter: 55,934,976 (+6,144 biases)
+ * at d = 4096, h = 1024, r = 256, V = 151936.
+ */
 int domino_head_param_count(const domino_head_config *cfg, int64_t *n);
 
 /* Releases the handle (not the workspace or the weights).  NULL is a no-op. */

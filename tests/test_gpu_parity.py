@@ -439,16 +439,18 @@ def test_position_batched_teacher_forcing_equals_per_position(wd, V, B):
     assert np.array_equal(d["tokens"], a["tokens"]) and np.array_equal(d["L_final"], a["L_final"])
 
 
-def test_position_batched_teacher_forcing_matches_oracle_at_larger_batch():
-    """B = 40 with a teacher (matrix-core launches over 640 rows), against the
-    oracle's teacher-forced draft; one row has an invalid teacher id."""
+@pytest.mark.parametrize("mode", [dca.EXEC_POSITION_BATCHED, dca.EXEC_AUTO])
+def test_position_batched_teacher_forcing_matches_oracle_at_larger_batch(mode):
+    """B = 40 with a teacher (position-batched: matrix-core launches over 640 rows;
+    auto: the batched resident launch), against the oracle's teacher-forced draft;
+    one row has an invalid teacher id."""
     sh = ds.HeadShape(d=256, h=64, r=256, V=7001, K=16, wdtype="bf16")
     w = ds.make_weights(sh, (9, 93), gru_sensitive=True)
     B = 40
     inp = ds.make_inputs(sh, B, (9, 94), sigma=0.5, peak="none")
     y = ds.uniform_tokens((9, 95), (B, 16), sh.V)
     y[7, 3] = sh.V + 5
-    head = make_head(w, B, dca.EXEC_AUTO, fold=True)
+    head = make_head(w, B, mode, fold=True)
     g, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok, teacher=y)
     assert flags == dca.FLAG_BAD_TOKEN
     assert (g["tokens"][7] == -1).all()
@@ -465,10 +467,13 @@ BF16_LBASE_CASES = {
     "resident_lds_tiles": ("bf16", 256, 64, 256, 160000, 2, 2, dca.EXEC_PERSISTENT, True, False),
     "resident_unfolded": ("bf16", 256, 64, 256, 5003, 1, 1, dca.EXEC_PERSISTENT, False, False),
     "streamed_w2": ("bf16", 256, 64, 256, 5003, 2, 2, dca.EXEC_PERSISTENT | dca.EXEC_STREAM_W2, True, False),
-    "batched_matrix_cores": ("bf16", 256, 64, 256, 20011, 40, 40, dca.EXEC_AUTO, True, False),
-    "position_batched": ("bf16", 256, 64, 256, 7001, 9, 9, dca.EXEC_AUTO, True, True),
+    "batched_resident": ("bf16", 256, 64, 256, 20011, 40, 40, dca.EXEC_AUTO, True, False),
+    "batched_matrix_cores": ("bf16", 256, 64, 256, 20011, 40, 40, dca.EXEC_STEPWISE, True, False),
+    "batched_resident_teacher": ("bf16", 256, 64, 256, 7001, 9, 9, dca.EXEC_AUTO, True, True),
+    "position_batched": ("bf16", 256, 64, 256, 7001, 9, 9, dca.EXEC_POSITION_BATCHED, True, True),
     "position_batched_b8": ("bf16", 256, 64, 256, 7001, 8, 8, dca.EXEC_POSITION_BATCHED, True, True),
-    "batched_b128": ("bf16", 256, 64, 256, 7001, 128, 128, dca.EXEC_AUTO, True, False),
+    "batched_b128": ("bf16", 256, 64, 256, 7001, 128, 128, dca.EXEC_STEPWISE, True, False),
+    "batched_resident_b128": ("bf16", 256, 64, 256, 7008, 128, 128, dca.EXEC_AUTO, True, False),
     "f32_stepwise": ("f32", 136, 64, 32, 3001, 3, 4, dca.EXEC_STEPWISE, False, False),
     "f32_persistent": ("f32", 136, 64, 32, 3001, 3, 4, dca.EXEC_PERSISTENT, True, False),
 }
@@ -518,7 +523,7 @@ def test_lds_staged_state_dots_match_oracle(B):
     run_both_protocols(w, inp, head, label="staged state dots B=%d" % B)
 
 
-@pytest.mark.parametrize("case", ["step_launches_b40", "resident_plain_launch_b3"])
+@pytest.mark.parametrize("case", ["step_launches_b40", "resident_plain_launch_b3", "batched_resident_plain_launch_b40"])
 def test_hip_graph_replay_matches_eager(case):
     """A draft call captured in a HIP graph (no memset nodes: the library clears with
     kernels) replayed several times, with eager draft calls of other inputs on the same
@@ -526,7 +531,9 @@ def test_hip_graph_replay_matches_eager(case):
     sh = ds.HeadShape(d=256, h=64, r=256, V=7001, K=16, wdtype="bf16")
     w = ds.make_weights(sh, (9, 120), gru_sensitive=True)
     if case == "step_launches_b40":
-        B, mode = 40, dca.EXEC_AUTO
+        B, mode = 40, dca.EXEC_STEPWISE
+    elif case == "batched_resident_plain_launch_b40":
+        B, mode = 40, dca.EXEC_PLAIN_LAUNCH
     else:
         B, mode = 3, dca.EXEC_PERSISTENT | dca.EXEC_PLAIN_LAUNCH
     head = make_head(w, B, mode, fold=True)
@@ -571,7 +578,7 @@ def test_side_streams_and_two_handles_concurrently():
     B = 24
     ia = ds.make_inputs(sh, B, (9, 131), sigma=0.5, peak="none")
     ib = ds.make_inputs(sh, B, (9, 132), sigma=0.5, peak="none")
-    ha, hb = make_head(w, B, fold=True), make_head(w, B, fold=True)
+    ha, hb = make_head(w, B, dca.EXEC_STEPWISE, fold=True), make_head(w, B, dca.EXEC_STEPWISE, fold=True)
     ra, _ = gpu_draft(ha, ia.H, ia.L_base, ia.last_tok)
     rb, _ = gpu_draft(hb, ib.H, ib.L_base, ib.last_tok)
     dev = [dca.device_tensor(x) for x in (ia.H, ia.L_base, ia.last_tok, ib.H, ib.L_base, ib.last_tok)]

@@ -32,8 +32,12 @@ struct Params {
     uint64_t *keys;  // [K, NG, maxB] partial argmax keys
     uint64_t *bkeys; // batched resident launch: [maxB, grid] argmax key word of every block for every
                      // batch row, generation-tagged
-    uint4 *uop;      // batched resident launch: u as the W2 products' operand, [maxB/16][hi, lo][r/32][64]
-                     // 16-byte chunks (8 bf16 of one batch row each), or nullptr
+    uint4 *uop;      // batched resident launch: u as the W2 products' operand, one slot per position:
+                     // [K][rb_ngr][hi, lo][r/32][64] 16-byte chunks (8 bf16 of one batch row each)
+    uint16_t *rb_planes;  // batched resident launch: S as bf16 hi/lo planes, one slot per state:
+                          // [K + 1][2][rb_bmax][rb_ldp]
+    int rb_bmax, rb_ngr, rb_ldp;
+    unsigned *rb_ucnt;    // batched resident launch: [K] blocks whose u operand of the position is written
     unsigned *bar;   // barrier words
     uint64_t *asy;   // argmax barrier words
     unsigned *flags; // device flags

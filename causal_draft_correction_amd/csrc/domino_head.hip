@@ -377,7 +377,7 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
     size_t bar, asy, flags, keys, A_H, S_buf, u_buf, u_all, utag, s_hl, q_buf, g_buf, P, M, mk_tmp, wst, bkeys, uop,
-        total;
+        rbs, ucnt, total;
 };
 
 // Packed state-dot rows for the matrix-core state launches (bf16 heads): the rows of
@@ -389,6 +389,11 @@ bool packed_state_rows(const domino_head_config &c)
     return c.wdtype == DOMINO_BF16 && c.r % 32 == 0 && c.h % 32 == 0 && c.max_batch > BC;
 }
 int packed_ldw(const domino_head_config &c) { return (c.h + 127) / 128 * 128 + 32; }
+// batched resident launch: batch rows of its buffers, 16-row groups, and the row stride
+// of its S planes (elements; h a multiple of 64, so rows are whole 128-byte lines)
+int rb_bmax(const domino_head_config &c) { return std::min(c.max_batch, dhrb::max_batch()); }
+int rb_ngr(const domino_head_config &c) { return (rb_bmax(c) + 15) / 16; }
+int rb_ldp(const domino_head_config &c) { return c.h + 64; }
 
 // Markov table fill: tokens per chunk (create-time region: folded gate rows and
 // zero-state GRU rows of one chunk, plus W1_S as float32)
@@ -430,15 +435,22 @@ Layout layout_of(const domino_head_config &c)
     L.wst = off;
     if (packed_state_rows(c))
         off = align_up(off + sizeof(uint16_t) * static_cast<size_t>(c.r + 3 * c.h) * packed_ldw(c));
-    // batched resident launch: argmax words [max_batch, MAX_GRID] and the u operand
-    // [max_batch / 16 groups][hi, lo][r / 32][64] x 16 bytes
+    // batched resident launch: argmax words [max_batch, MAX_GRID], the u operand of
+    // every position [K][groups][hi, lo][r / 32][64] x 16 bytes, and the S planes of
+    // every state [K + 1][hi, lo][rows][rb_ldp] bf16
     L.bkeys = off;
     L.uop = off;
+    L.rbs = off;
     if (packed_state_rows(c)) {
         off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(c.max_batch) * MAX_GRID);
         L.uop = off;
-        off = align_up(off + sizeof(uint16_t) * 2 * static_cast<size_t>((c.max_batch + 15) / 16 * 16) * c.r);
+        off = align_up(off + sizeof(uint16_t) * 2 * static_cast<size_t>(c.K) * rb_ngr(c) * 16 * c.r);
+        L.rbs = off;
+        off = align_up(off + sizeof(uint16_t) * 2 * static_cast<size_t>(c.K + 1) * rb_bmax(c) * rb_ldp(c));
     }
+    L.ucnt = off;
+    if (packed_state_rows(c))
+        off = align_up(off + sizeof(unsigned) * MAXK);
     L.M = off;
     L.mk_tmp = off;
     if (c.flags & DOMINO_MARKOV) {
@@ -602,7 +614,12 @@ static bool choose_launch(const domino_head *hd, int B, bool *persistent, bool *
 {
     const unsigned fl = hd->cfg.flags;
     *batched = false;
+    // the batched persistent launch beats the step launches up to about B = 48 on a 256-CU device
+    // (8B-class head, K = 16); past that its per-position state products cost more than one
+    // extra launch per phase, so AUTO hands larger batches to the step launches
+    const int auto_max = 48;
     if (!(fl & DOMINO_MARKOV) && B > BC && hd->rb_grid > 0 && B <= dhrb::max_batch() &&
+        ((fl & DOMINO_EXEC_PERSISTENT) || B <= auto_max) &&
         !(fl & (DOMINO_EXEC_STEPWISE | DOMINO_EXEC_STREAM_W2))) {
         *persistent = *resident = *batched = true;
         return true;
@@ -881,6 +898,11 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
         p.ldw = packed_ldw(c);
         p.bkeys = reinterpret_cast<uint64_t *>(hd->ws + hd->L.bkeys);
         p.uop = reinterpret_cast<uint4 *>(hd->ws + hd->L.uop);
+        p.rb_planes = reinterpret_cast<uint16_t *>(hd->ws + hd->L.rbs);
+        p.rb_bmax = rb_bmax(c);
+        p.rb_ngr = rb_ngr(c);
+        p.rb_ldp = rb_ldp(c);
+        p.rb_ucnt = reinterpret_cast<unsigned *>(hd->ws + hd->L.ucnt);
         p.ah_external = 1;
         void *args[] = {&p};
         HIP_TRY(hipLaunchKernel(dhbat::ah_kernel(B, c.K, c.r), dim3(dhbat::ah_grid(B, c.K, c.r)),

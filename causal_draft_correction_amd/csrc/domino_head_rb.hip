@@ -7,9 +7,10 @@
 //   S_{p+1} = GRU(E[x_p], S_p)   (x_p = t_p, or the teacher token)
 // with the GRU input part a row of the folded table P = E W_ih^T + b_ih.
 //
-// One block per compute unit, four waves (one per SIMD, up to 512 registers
-// each).  Block b owns a contiguous range of 16-row vocabulary tiles; wave w
-// holds tiles w, w + 4, ... of it (RT per wave, 320 registers at r = 256).
+// One block per compute unit, eight waves (two per SIMD, up to 256 registers
+// each, so one wave's epilogue and copies overlap the other's matrix-core
+// products).  Block b owns a contiguous range of 16-row vocabulary tiles; wave w
+// holds tiles w, w + 8, ... of it (RT per wave, 160 registers at r = 256).
 // Per position the launch runs three phases separated by grid barriers:
 //   * W2 phase: for each group of 16 batch rows, D = W2_tile u^T on the matrix
 //     cores (v_mfma_f32_16x16x32_bf16, A = the register tile, B = u as bf16 hi
@@ -25,14 +26,22 @@
 //     previous state, which stays with its owner), writing S as float32 and as
 //     bf16 hi/lo planes;
 //   * state-dot phase: [u | q'] = S [B, h] x [W1_S; W_hh]^T on the matrix cores
-//     in jobs of 4 weight tiles x BJ batch tiles (S hi and lo staged in LDS,
-//     weight rows from L2), then u = SiLU(A_H + .) as the next W2 phase's bf16
-//     hi/lo operand and q' + b_hh for the next update.
-// Values that cross blocks (keys, q, the S planes, the u operand) are written
-// with agent-scope stores and read with agent-scope loads (or copies with the
-// same cache policy), which bypass the per-XCD L2 caches.
-#define DH_NT 256
-#define DH_NS dh256
+//     in jobs of 4 weight tiles x BJ batch tiles (S hi and lo staged in LDS four
+//     stages ahead, weight rows from L2; two waves per weight tile split each
+//     stage's two 32-wide steps), then u = SiLU(A_H + .) as the next W2 phase's
+//     bf16 hi/lo operand and q' + b_hh for the next update.
+// Values that cross blocks are written with agent-scope stores, which write
+// through the per-XCD L2 caches (not coherent with each other).  The argmax
+// words and q, each read by one block, are read with agent-scope loads, which
+// bypass them.  The S planes and the u operand, which many blocks read, have one
+// slot per state (per position) in the launch and are read with ordinary,
+// L2-cached copies, so the blocks of an XCD share each line: no L2 can hold a
+// stale copy of such a line, since the launch starts with an agent-scope acquire
+// (the L2s hold nothing written before it), nobody reads a slot before the grid
+// barrier that follows its writes, and every 128-byte line of a slot is written
+// by one block alone (a writer whose L2 keeps the line keeps all of it fresh).
+#define DH_NT 512
+#define DH_NS dhrbk
 #include "dh_phases.h"
 #include "dh_rbatch.h"
 
@@ -46,16 +55,17 @@
 namespace DH_NS {
 namespace rbk {
 
-constexpr int RT = 10;               // W2 tiles per wave in registers
+constexpr int RT = 5;                // W2 tiles per wave in registers
 constexpr int KS = 8;                // 32-wide steps of r
 constexpr int R = 32 * KS;           // r
 constexpr int TILES = NWAVE * RT;    // vocabulary tiles per block (40: 640 rows)
-constexpr int LROW = TILES * 16;     // L_base values of one batch row in LDS
+constexpr int LROW = TILES * 16;     // L_base values of one batch row (float32 rows in LDS)
+constexpr int LROW16 = LROW + 128;   // the same for bf16 rows, padded to whole copies per wave
 constexpr int LBUF = 16 * LROW * 4 / 16;  // uint4 per L_base buffer (16 rows of float32)
 constexpr int UCH = 2 * KS * 64;     // uint4 of one group's u operand (hi, lo)
 constexpr int MAXB = 256;            // batch rows of one launch
 constexpr int ROWS = 4;              // batch rows one block updates at most (B <= MAXB)
-constexpr int CPT = 2;               // 4-entry state chunks per thread at most
+constexpr int CPT = 1;               // 4-entry state chunks per thread at most
 constexpr unsigned AUX_SC1 = 16;     // cache policy of agent-scope coherent accesses (sc1)
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -99,7 +109,12 @@ __device__ inline void copy_lds16(const void *g, void *lds, unsigned aux_sc1)
         __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, 0);
 }
 __device__ inline void copy_lds4(const void *g, void *lds) { __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 4, 0, 0); }
-__device__ inline void copy_lds2(const void *g, void *lds) { __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 2, 0, 0); }
+
+// the same through a buffer resource (16 bytes at byte offset voff; past the records: zeros)
+__device__ inline void copy_lds16_buf(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, 0, 0, 0);
+}
 
 __device__ inline uint64_t pack4_bf16(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
@@ -122,7 +137,8 @@ __device__ inline Ctx make_ctx(const Params &p, int blk, int nblk)
     c.n = (16 * tb < p.V ? 16 * tb : p.V) - c.v0;
     if (c.n < 0)
         c.n = 0;
-    const int nc = p.B * p.h / 4, per = (nc + nblk - 1) / nblk;
+    // whole 16-chunk runs (64 entries: one 128-byte line of each plane) per block
+    const int nc = p.B * p.h / 4, per = ((nc + nblk - 1) / nblk + 15) & ~15;
     c.c0 = blk * per < nc ? blk * per : nc;
     c.c1 = c.c0 + per < nc ? c.c0 + per : nc;
     c.rb0 = c.c0 * 4 / p.h;
@@ -145,13 +161,42 @@ template <bool LB16, bool FAST>
 struct LbCopy {
     static constexpr int EL = LB16 ? 2 : 4;            // bytes per value
     static constexpr int PIECE = FAST ? 16 : EL;       // bytes per lane per copy
-    static constexpr int ROWB = LROW * EL;             // bytes of one LDS row
+    static constexpr int ROWV = LB16 ? LROW16 : LROW;  // values of one LDS row
+    static constexpr int ROWB = ROWV * EL;             // bytes of one LDS row
     static constexpr int NLD = 16 * ROWB / (64 * PIECE) / NWAVE;  // copies per thread per group
     static_assert(16 * ROWB % (64 * PIECE * NWAVE) == 0, "whole copies per wave");
+    static_assert(16 * ROWB <= LBUF * 16, "group fits one buffer");
+};
+
+// Byte offsets, from the first value of the group's first batch row at the
+// position, of this lane's 16-byte pieces (FAST copies): piece s = 64 i + lane of
+// copy i = wave * NLD + jj lands at LDS row s / (ROWB / 16), chunk s % (ROWB / 16),
+// whose value index within the block's range is (chunk ^ (row & 7)) * (16 / EL).
+// Rows past B and values past the tensor lie past the buffer resource's records
+// and read as 0 (their results are masked); values past the block's range are
+// other blocks' values, also masked.  The same at every group and position.
+template <bool LB16>
+struct LbOff {
+    using C = LbCopy<LB16, true>;
+    uint32_t off[C::NLD];
+    __device__ LbOff(const Params &p, int v0)
+    {
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+        const uint32_t rowstride = static_cast<uint32_t>(p.K) * static_cast<uint32_t>(p.V) * C::EL;
+#pragma unroll
+        for (int jj = 0; jj < C::NLD; ++jj) {
+            const int s = 64 * (wave * C::NLD + jj) + lane;
+            const int row = s / (C::ROWB / 16), ch = s % (C::ROWB / 16);
+            const int e = (ch ^ (row & 7)) * (16 / C::EL);
+            off[jj] = static_cast<uint32_t>(row) * rowstride + static_cast<uint32_t>(v0 + e) * C::EL;
+        }
+    }
 };
 
 template <bool LB16, bool FAST>
-__device__ __forceinline__ void lb_issue(const Params &p, const Ctx &c, int pos, int g, uint4 *buf)
+__device__ __forceinline__ void lb_issue(const Params &p, const Ctx &c, const LbOff<LB16> &lo, int pos, int g,
+                                         uint4 *buf)
 {
     using C = LbCopy<LB16, FAST>;
     const int lane = threadIdx.x & 63;
@@ -159,6 +204,18 @@ __device__ __forceinline__ void lb_issue(const Params &p, const Ctx &c, int pos,
     const char *base = static_cast<const char *>(p.L_base);
     const int ngr = (p.B + 15) / 16;
     g = g < ngr ? g : ngr - 1;
+    if constexpr (FAST) {
+        // buffer resource from the group's first row at this position to the end of L_base
+        const long long first = (static_cast<long long>(16 * g) * p.K + pos) * p.V;
+        const long long left = (static_cast<long long>(p.B) * p.K * p.V - first) * C::EL;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char *>(base) + first * C::EL, 0,
+            static_cast<int>(static_cast<uint32_t>(left > 0xFFFFFFFFll ? 0xFFFFFFFFll : left)), 0x00020000);
+#pragma unroll
+        for (int jj = 0; jj < C::NLD; ++jj)
+            copy_lds16_buf(rs, buf + 64 * (wave * C::NLD + jj), lo.off[jj]);
+        return;
+    }
     constexpr int VPC = 16 / C::EL;  // values per 16-byte chunk
     if constexpr (LB16 && !FAST) {
         constexpr int BATCH = 8;
@@ -168,7 +225,7 @@ __device__ __forceinline__ void lb_issue(const Params &p, const Ctx &c, int pos,
 #pragma unroll
             for (int jj = 0; jj < BATCH; ++jj) {
                 const int s = 64 * (wave * C::NLD + j0 + jj) + lane;
-                const int row = s / LROW, pr = s % LROW;
+                const int row = s / C::ROWV, pr = s % C::ROWV;
                 int e = ((pr / 8) ^ (row & 7)) * 8 + pr % 8;
                 e = e < c.n ? e : 0;
                 const int b = 16 * g + row < p.B ? 16 * g + row : p.B - 1;
@@ -186,28 +243,17 @@ __device__ __forceinline__ void lb_issue(const Params &p, const Ctx &c, int pos,
         const int s = 64 * i + lane;          // this lane's piece
         const int row = s / (C::ROWB / C::PIECE);
         const int pr = s % (C::ROWB / C::PIECE);  // piece within the LDS row
-        int e;                                    // value index within the block's range
-        if constexpr (FAST) {
-            e = ((pr ^ (row & 7)) * VPC);
-        } else {
-            constexpr int PPC = 16 / C::PIECE;    // pieces per chunk
-            e = ((pr / PPC) ^ (row & 7)) * VPC + pr % PPC;
-        }
+        constexpr int PPC = 16 / C::PIECE;        // pieces per chunk
+        int e = ((pr / PPC) ^ (row & 7)) * VPC + pr % PPC;  // value index within the block's range
         e = e < c.n ? e : 0;
         const int b = 16 * g + row < p.B ? 16 * g + row : p.B - 1;
         const char *src = base + ((static_cast<size_t>(b) * p.K + pos) * p.V + c.v0 + e) * C::EL;
-        char *dst = reinterpret_cast<char *>(buf) + i * 64 * C::PIECE;
-        if constexpr (C::PIECE == 16)
-            copy_lds16(src, dst, 0);
-        else if constexpr (C::PIECE == 4)
-            copy_lds4(src, dst);
-        else
-            copy_lds2(src, dst);
+        copy_lds4(src, reinterpret_cast<char *>(buf) + i * 64 * C::PIECE);
     }
 }
 
 // u operand of group g (16 KB, the layout of p.uop) into an LDS buffer: 4 copies per thread.
-__device__ __forceinline__ void u_issue(const Params &p, int g, uint4 *buf)
+__device__ __forceinline__ void u_issue(const Params &p, int pos, int g, uint4 *buf)
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -216,7 +262,7 @@ __device__ __forceinline__ void u_issue(const Params &p, int g, uint4 *buf)
 #pragma unroll
     for (int jj = 0; jj < UCH / 64 / NWAVE; ++jj) {
         const int i = wave * (UCH / 64 / NWAVE) + jj;
-        copy_lds16(p.uop + static_cast<size_t>(g) * UCH + 64 * i + lane, buf + 64 * i, 1);
+        copy_lds16(p.uop + (static_cast<size_t>(pos) * p.rb_ngr + g) * UCH + 64 * i + lane, buf + 64 * i, 0);
     }
 }
 
@@ -228,7 +274,7 @@ __device__ inline float4 lb_read(const uint4 *buf, int row, int t, int k)
     if constexpr (LB16) {
         const int chunk = (2 * t + (k >> 1)) ^ (row & 7);
         const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(buf) +
-                                                         (row * (LROW * 2 / 16) + chunk) * 16 + (k & 1) * 8);
+                                                         (row * (LROW16 * 2 / 16) + chunk) * 16 + (k & 1) * 8);
         return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u), __uint_as_float(v.y << 16),
                            __uint_as_float(v.y & 0xFFFF0000u));
     } else {
@@ -238,7 +284,7 @@ __device__ inline float4 lb_read(const uint4 *buf, int row, int t, int k)
 }
 
 // Products and epilogue of group g for this wave: result lane l holds vocabulary
-// rows 16 t + 4 (l / 16) + i (i = 0..3) of tile t = wave + 4 j for batch row
+// rows 16 t + 4 (l / 16) + i (i = 0..3) of tile t = wave + NWAVE j for batch row
 // 16 g + l % 16.  The lane keeps the first of its largest values (a NaN above every
 // number, the first NaN kept; -0 == +0 by the float compare); the wave's key for
 // each of the group's batch rows goes to kr[wave][0..15].
@@ -276,19 +322,33 @@ __device__ __forceinline__ void w2_group(const Params &p, const Ctx &c, const W2
         const int t = wave + NWAVE * j;
         const float4 lb = lb_read<LB16>(L, row, t, k);
         const float lv[4] = {lb.x, lb.y, lb.z, lb.w};
-        const bool full = 16 * (t + 1) <= c.n;  // uniform in the wave
+        // tiles wholly inside the block's range skip the per-value bound (uniform)
+        if (16 * (t + 1) <= c.n) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float v = acc[j][i] + lv[i];
-            const int vr = 16 * t + 4 * k + i;
-            const bool ok = full || vr < c.n;
-            if constexpr (ST) {
-                if (ok && b < p.B)
-                    lf[vr] = v;
+            for (int i = 0; i < 4; ++i) {
+                const float v = acc[j][i] + lv[i];
+                if constexpr (ST) {
+                    if (b < p.B)
+                        lf[16 * t + 4 * k + i] = v;
+                }
+                const bool take = !(v <= best) & (best == best);
+                best = take ? v : best;
+                bpos = take ? 4 * j + i : bpos;
             }
-            const bool take = !(v <= best) & (best == best) & ok;
-            best = take ? v : best;
-            bpos = take ? 4 * j + i : bpos;
+        } else if (16 * t < c.n) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v = acc[j][i] + lv[i];
+                const int vr = 16 * t + 4 * k + i;
+                const bool ok = vr < c.n;
+                if constexpr (ST) {
+                    if (ok && b < p.B)
+                        lf[vr] = v;
+                }
+                const bool take = !(v <= best) & (best == best) & ok;
+                best = take ? v : best;
+                bpos = take ? 4 * j + i : bpos;
+            }
         }
     }
     uint64_t key = 0;
@@ -304,6 +364,16 @@ __device__ __forceinline__ void w2_group(const Params &p, const Ctx &c, const W2
         kr[wave * 16 + lane] = key;
 }
 
+// Copies of the first two L_base groups of position pos (they depend on nothing
+// computed in the launch, so they go out before the wait for the u operand).
+template <bool LB16, bool FAST>
+__device__ __forceinline__ void w2_prefetch(const Params &p, const Ctx &c, int pos, uint4 *lbA, uint4 *lbB)
+{
+    const LbOff<LB16> lo(p, c.v0);
+    lb_issue<LB16, FAST>(p, c, lo, pos, 0, lbA);
+    lb_issue<LB16, FAST>(p, c, lo, pos, 1, lbB);
+}
+
 // The W2 phase of position pos: every group's products and argmax, then the
 // block's key word of every batch row, tagged `tag14`.
 template <bool LB16, bool FAST, bool ST>
@@ -313,7 +383,8 @@ __device__ __forceinline__ void w2_phase(const Params &p, const Ctx &c, const W2
 {
     using C = LbCopy<LB16, FAST>;
     const int ngr = (p.B + 15) / 16;
-    // block key of group gp from the four waves' keys (after a barrier)
+    const LbOff<LB16> lo(p, c.v0);
+    // block key of group gp from the waves' keys (after a barrier)
     auto fold = [&](int gp) {
         if (threadIdx.x < 16) {
             const uint64_t *kr = kred + (gp & 1) * NWAVE * 16;
@@ -325,20 +396,23 @@ __device__ __forceinline__ void w2_phase(const Params &p, const Ctx &c, const W2
         }
     };
     // group g: wait for its copies (those of the L_base group after it may stay in
-    // flight: they were issued last), meet the other waves, fold the previous group's
-    // keys, start the copies of u(g + 1) and L_base(g + 2), then the products
+    // flight: they were issued last; group 0's u copy was issued last, so it waits for
+    // all), meet the other waves, fold the previous group's keys, start the copies of
+    // u(g + 1) and L_base(g + 2), then the products
     auto iter = [&](int g, const uint4 *Lc, uint4 *Ln2, const uint4 *Uc, uint4 *Un) {
-        wait_vm<C::NLD>();
+        if (g == 0)
+            wait_vm<0>();
+        else
+            wait_vm<C::NLD>();
         bare_barrier();
         if (g >= 1)
             fold(g - 1);
-        u_issue(p, g + 1, Un);
-        lb_issue<LB16, FAST>(p, c, pos, g + 2, Ln2);
+        u_issue(p, pos, g + 1, Un);
+        lb_issue<LB16, FAST>(p, c, lo, pos, g + 2, Ln2);
         w2_group<LB16, ST>(p, c, res, pos, g, Lc, Uc, kred + (g & 1) * NWAVE * 16);
     };
-    lb_issue<LB16, FAST>(p, c, pos, 0, lbA);
-    u_issue(p, 0, uA);
-    lb_issue<LB16, FAST>(p, c, pos, 1, lbB);
+    // L_base groups 0 and 1 were issued by w2_prefetch
+    u_issue(p, pos, 0, uA);
     // group g uses L_base buffer g % 3 and u buffer g % 2
 #pragma unroll 1
     for (int g0 = 0; g0 < ngr; g0 += 6) {
@@ -362,6 +436,9 @@ __device__ __forceinline__ void w2_phase(const Params &p, const Ctx &c, const W2
     }
     __syncthreads();
     fold(ngr - 1);
+    // the state products (q) this block stored before are complete before its keys,
+    // which the update of the next position waits for
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int b = threadIdx.x; b < p.B; b += NT) {
         const uint64_t m = lkey[b];
@@ -439,7 +516,8 @@ __device__ __forceinline__ bool resolve(const Params &p, const Ctx &c, int pos, 
 __device__ __forceinline__ void update(const Params &p, const Ctx &c, int q, const int *rtok)
 {
     const int h = p.h, h3 = 3 * h;
-    uint16_t *plane_hi = p.s_hl, *plane_lo = p.s_hl + static_cast<size_t>(p.maxB) * p.ldw;
+    uint16_t *plane_hi = p.rb_planes + static_cast<size_t>(q + 1) * 2 * p.rb_bmax * p.rb_ldp;
+    uint16_t *plane_lo = plane_hi + static_cast<size_t>(p.rb_bmax) * p.rb_ldp;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
         const int cc = c.c0 + static_cast<int>(threadIdx.x) + u * NT;
@@ -504,77 +582,237 @@ __device__ __forceinline__ void update(const Params &p, const Ctx &c, int q, con
             hi[i] = bf16_rne_bits(sn[i]);
             lo[i] = bf16_rne_bits(sn[i] - __uint_as_float(hi[i] << 16));
         }
-        const size_t o = static_cast<size_t>(b) * p.ldw + j;
+        const size_t o = static_cast<size_t>(b) * p.rb_ldp + j;
         st_agent_u64(plane_hi + o, pack4_bf16(hi[0], hi[1], hi[2], hi[3]));
         st_agent_u64(plane_lo + o, pack4_bf16(lo[0], lo[1], lo[2], lo[3]));
     }
 }
 
 // ---- state-dot phase ------------------------------------------------------------------
-// Products of S_q with the packed state rows wst = [W1_S; W_hh] (R = r + 3h rows of
-// ldw bf16): a job is 4 weight tiles (one per wave, A operand from L2) x BJ batch
-// tiles (B operand: S hi and lo rows, staged in LDS).  The h reduction runs in stages
-// of 64 (two 32-wide steps); a stage's operands (BJ * 4 blocks of 1 KB) are copied by
-// direct global-to-LDS loads three stages ahead into a ring of four buffers, each
-// wave waiting for its own copies and meeting the others at a bare barrier.  The
-// weight operands of a stage are loaded into registers with the copies.  Every copy
-// and load is issued on every step (stages past the last repeat it), so the wait
-// counts are the same on every path.  q = -1: only the W_hh rows (q of S_init).
-template <int BJ>
-__device__ __forceinline__ void dots(const Params &p, int blk, int nblk, int q, uint4 *ring0, uint4 *ring1,
-                                     uint4 *ring2, uint4 *ring3)
+// Block b < (r + 3h) / 16 owns weight tile b: rows 16 b .. 16 b + 15 of the packed state
+// rows wst = [W1_S; W_hh]; wave w takes the 32-wide steps KSW w .. KSW w + KSW - 1 of the
+// h reduction (A operands loaded with the first round's copies).  Per state S_q the
+// block multiplies its tile with every batch row: in rounds of two 16-row batch tiles,
+// each wave copies the S hi and lo rows of its own steps into its own LDS region
+// (16 KB), waits for its own copies and multiplies; the eight partial
+// sums of each tile are added through LDS in wave order, and waves 0 and 1 finish the
+// two tiles: u = SiLU(A_H + .) as the W2 operand of position q (rows m < r) or
+// q' = . + b_hh for the next update.  The blocks of the u rows then count themselves
+// in rb_ucnt[q], which the W2 phase waits for.  q = -1: only the W_hh rows (q of S_init).
+constexpr int KSW = 4;  // 32-wide steps of h per wave (h <= 32 KSW NWAVE = 1024)
+
+struct DotW {
+    uint4 w[KSW];
+};
+
+__device__ __forceinline__ void dots_small(const Params &p, int blk, int q, uint4 *lbA, uint4 *lbB, uint4 *lbC,
+                                           uint4 *uA, uint4 *uB)
 {
     const int lane = threadIdx.x & 63, row = lane & 15, k = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int h = p.h, r = p.r, h3 = 3 * h;
-    const int Rall = r + h3, nwg = Rall / 64;
+    const int nwt = (r + h3) / 16, nks = h / 32, nbt = (p.B + 15) / 16;
+    const int m = 16 * blk + 4 * k;  // result rows of this lane: m .. m + 3
+    const bool urows = 16 * blk < r;
+    if (blk >= nwt || (q < 0 && urows))
+        return;
+    const uint16_t *plane[2] = {p.rb_planes + static_cast<size_t>(q + 1) * 2 * p.rb_bmax * p.rb_ldp,
+                                p.rb_planes + (static_cast<size_t>(q + 1) * 2 + 1) * p.rb_bmax * p.rb_ldp};
+    // this wave's LDS region: 2 tiles x hi/lo x KSW steps of 1 KB
+    uint4 *mine = wave < 2 ? lbA + wave * 1024 : wave < 4 ? lbB + (wave - 2) * 1024
+                : wave < 6 ? lbC + (wave - 4) * 1024 : wave == 6 ? uA : uB;
+    f32x4_t *red = reinterpret_cast<f32x4_t *>(uB);  // [2 tiles][NWAVE][64] partial sums
+    DotW dw;
+    for (int bt0 = 0; bt0 < nbt; bt0 += 2) {
+        const int ntl = nbt - bt0 < 2 ? nbt - bt0 : 2;
+        // every copy is issued (rows past B repeat row B - 1, steps past h repeat step
+        // 0; those results are not used): a copy in a branch would make the compiler
+        // wait for all copies in flight at the branch's end
+#pragma unroll
+        for (int tl = 0; tl < 2; ++tl) {
+            int b = 16 * (bt0 + tl) + row;
+            b = b < p.B ? b : p.B - 1;
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                for (int i = 0; i < KSW; ++i) {
+                    const int st = wave * KSW + i < nks ? wave * KSW + i : 0;
+                    copy_lds16(plane[hl] + static_cast<size_t>(b) * p.rb_ldp + 32 * st + 8 * k,
+                               mine + ((tl * 2 + hl) * KSW + i) * 64, 0);
+                }
+        }
+        // this wave's steps of the block's weight tile (steps past h repeat step 0,
+        // unused), and the A_H entries of the round's u rows (clamped when unused)
+        if (bt0 == 0) {
+#pragma unroll
+            for (int i = 0; i < KSW; ++i) {
+                const int st = wave * KSW + i < nks ? wave * KSW + i : 0;
+                dw.w[i] =
+                    *reinterpret_cast<const uint4 *>(p.wst + static_cast<size_t>(16 * blk + row) * p.ldw + 32 * st + 8 * k);
+            }
+        }
+        float4 ah = make_float4(0.f, 0.f, 0.f, 0.f);
+        {
+            int b = 16 * (bt0 + (wave & 1)) + row;
+            b = b < p.B ? b : p.B - 1;
+            ah = *reinterpret_cast<const float4 *>(p.A_H + (static_cast<size_t>(b) * p.K + (q > 0 ? q : 0)) * r +
+                                                   (urows ? m : 0));
+        }
+        if (bt0 == 0)
+            RB_MARK(64 * (q > 0 ? q : 0) + 40);
+        wait_vm<0>();
+        if (bt0 == 0)
+            RB_MARK(64 * (q > 0 ? q : 0) + 41);
+        f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int tl = 0; tl < 2; ++tl) {
+            if (tl >= ntl)
+                break;
+#pragma unroll
+            for (int i = 0; i < KSW; ++i) {
+                if (wave * KSW + i < nks) {
+#pragma unroll
+                    for (int hl = 0; hl < 2; ++hl)
+                        acc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, dw.w[i]),
+                            __builtin_bit_cast(bf16x8_t, mine[((tl * 2 + hl) * KSW + i) * 64 + lane]), acc[tl], 0, 0,
+                            0);
+                }
+            }
+        }
+        __syncthreads();  // every wave's region read (the partial sums go where wave 7's was)
+        if (bt0 == 0)
+            RB_MARK(64 * (q > 0 ? q : 0) + 42);
+#pragma unroll
+        for (int tl = 0; tl < 2; ++tl)
+            red[(tl * NWAVE + wave) * 64 + lane] = acc[tl];
+        __syncthreads();
+        if (wave < ntl) {
+            const int tl = wave;
+            f32x4_t sum = red[(tl * NWAVE) * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < NWAVE; ++w) {
+                const f32x4_t o = red[(tl * NWAVE + w) * 64 + lane];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sum[i] += o[i];
+            }
+            // lane holds weight rows m .. m + 3 of batch row b
+            const int b = 16 * (bt0 + tl) + row;
+            if (b < p.B) {
+                if (urows) {
+                    const float a4[4] = {ah.x + sum[0], ah.y + sum[1], ah.z + sum[2], ah.w + sum[3]};
+                    float u4[4];
+                    uint32_t hi[4], lo[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        u4[i] = a4[i] * sigmoidf_(a4[i]);
+                        hi[i] = bf16_rne_bits(u4[i]);
+                        lo[i] = bf16_rne_bits(u4[i] - __uint_as_float(hi[i] << 16));
+                    }
+                    if (p.u_out)
+                        *reinterpret_cast<float4 *>(p.u_out + (static_cast<size_t>(b) * p.K + q) * r + m) =
+                            make_float4(u4[0], u4[1], u4[2], u4[3]);
+                    // operand chunk of (batch row b, r offsets 8 (m / 8) .. + 8): group b / 16,
+                    // step m / 32, lane b % 16 + 16 ((m % 32) / 8); these four values are its
+                    // half (m % 8) / 4
+                    const size_t ch = ((static_cast<size_t>(q) * p.rb_ngr + (b >> 4)) * 2 * KS + (m >> 5)) * 64 +
+                                      (b & 15) + 16 * ((m & 31) >> 3);
+                    char *dst = reinterpret_cast<char *>(p.uop + ch) + (m & 7) * 2;
+                    st_agent_u64(dst, pack4_bf16(hi[0], hi[1], hi[2], hi[3]));
+                    st_agent_u64(dst + static_cast<size_t>(KS) * 64 * 16, pack4_bf16(lo[0], lo[1], lo[2], lo[3]));
+                } else {
+                    const int mq = m - r;
+                    const float4 v = make_float4(sum[0] + bias_hh(p, mq), sum[1] + bias_hh(p, mq + 1),
+                                                 sum[2] + bias_hh(p, mq + 2), sum[3] + bias_hh(p, mq + 3));
+                    st_agent_f4(q_slot(p, q + 1) + static_cast<size_t>(b) * h3 + mq, v);
+                }
+            }
+        }
+        __syncthreads();  // regions and partial sums free for the next round
+        if (bt0 == 0)
+            RB_MARK(64 * (q > 0 ? q : 0) + 43);
+    }
+    if (urows && q >= 0) {
+        // this block's share of u_q is written: count it
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_add(&p.rb_ucnt[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Larger batches: a job is 4 weight tiles x BJ batch tiles (2-D tiles: each block reads
+// a slice of S and a slice of the weights instead of all of S).  Waves w and w + 4 take
+// weight tile w % 4 (A operand from L2) and the first or second 32-wide step of each
+// 64-wide stage of the h reduction; the B operand (S hi and lo rows of the BJ batch
+// tiles) is staged in LDS: a stage's BJ * 4 blocks of 1 KB are copied three stages
+// ahead into a ring of four buffers, each wave waiting for its own copies and meeting
+// the others at a bare barrier.  Every copy and load is issued on every step (stages
+// past the last repeat it), so the wait counts are the same on every path.  At the end
+// waves 4..7 hand their partial sums to waves 0..3 through LDS.  Jobs of the u rows
+// count themselves in rb_ucnt[q].
+constexpr int DOTS_BJ = 4;
+__host__ __device__ inline bool dots_tiled(int B) { return (B + 15) / 16 > 4; }
+__host__ __device__ inline int u_producers(int B, int r)
+{
+    return dots_tiled(B) ? (r / 64) * (((B + 15) / 16 + DOTS_BJ - 1) / DOTS_BJ) : r / 16;
+}
+
+__device__ __forceinline__ void dots_2d(const Params &p, int blk, int nblk, int q, uint4 *ring0, uint4 *ring1,
+                                        uint4 *ring2, uint4 *ring3)
+{
+    constexpr int BJ = DOTS_BJ;
+    const int lane = threadIdx.x & 63, row = lane & 15, k = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int tw = wave & 3, ks = wave >> 2;
+    const int h = p.h, r = p.r, h3 = 3 * h;
+    const int nwg = (r + h3) / 64;
     const int nbt = (p.B + 15) / 16, nbj = (nbt + BJ - 1) / BJ;
     const int NS = h / 64;
-    const uint16_t *plane[2] = {p.s_hl, p.s_hl + static_cast<size_t>(p.maxB) * p.ldw};
-    constexpr int PER = BJ;  // copies per wave per stage (BJ * 4 blocks over 4 waves)
+    const uint16_t *plane[2] = {p.rb_planes + static_cast<size_t>(q + 1) * 2 * p.rb_bmax * p.rb_ldp,
+                                p.rb_planes + (static_cast<size_t>(q + 1) * 2 + 1) * p.rb_bmax * p.rb_ldp};
+    constexpr int NB1 = BJ * 4;                      // 1 KB operand blocks per stage: (bt, hi/lo, step)
+    constexpr int PER = (NB1 + NWAVE - 1) / NWAVE;   // copies per wave per stage
+    static_assert(NWAVE * PER <= 16, "copies fit one 16 KB ring buffer");
+    f32x4_t *xch = reinterpret_cast<f32x4_t *>(ring0);
     for (int job = blk; job < nwg * nbj; job += nblk) {
         const int wg = job / nbj, bj = job % nbj;
-        const int wt = wg * 4 + wave;  // this wave's weight tile
-        const bool active = !(q < 0 && wt * 16 < r);
-        // copy sources of this lane: block i = wave * PER + x = (bt * 2 + hilo) * 2 + ks
+        const int wt = wg * 4 + tw;  // this wave's weight tile
+        const bool urows = wg * 64 < r;
+        const bool active = !(q < 0 && urows);
         const uint16_t *src[PER];
 #pragma unroll
         for (int x = 0; x < PER; ++x) {
-            const int i = wave * PER + x, bt = i >> 2, hl = (i >> 1) & 1, ks = i & 1;
+            const int ib = (wave * PER + x) % NB1, bt = ib >> 2, hl = (ib >> 1) & 1, st = ib & 1;
             int b = (bj * BJ + bt) * 16 + row;
             b = b < p.B ? b : p.B - 1;
-            src[x] = plane[hl] + static_cast<size_t>(b) * p.ldw + 32 * ks + 8 * k;
+            src[x] = plane[hl] + static_cast<size_t>(b) * p.rb_ldp + 32 * st + 8 * k;
         }
-        const uint16_t *wrow = p.wst + static_cast<size_t>(wt * 16 + row) * p.ldw + 8 * k;
-        uint4 wa[4][2];
-        auto issue = [&](int s, uint4 *ring, uint4 (&w)[2]) {
+        const uint16_t *wrow = p.wst + static_cast<size_t>(wt * 16 + row) * p.ldw + 32 * ks + 8 * k;
+        uint4 wa[4];
+        auto issue = [&](int s, uint4 *ring, uint4 &w) {
             s = s < NS ? s : NS - 1;
 #pragma unroll
             for (int x = 0; x < PER; ++x)
-                copy_lds16(src[x] + 64 * s, ring + (wave * PER + x) * 64, 1);
-            w[0] = *reinterpret_cast<const uint4 *>(wrow + 64 * s);
-            w[1] = *reinterpret_cast<const uint4 *>(wrow + 64 * s + 32);
+                copy_lds16(src[x] + 64 * s, ring + (wave * PER + x) * 64, 0);
+            w = *reinterpret_cast<const uint4 *>(wrow + 64 * s);
         };
         f32x4_t acc[BJ];
 #pragma unroll
         for (int bt = 0; bt < BJ; ++bt)
             acc[bt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        auto compute = [&](const uint4 *ring, const uint4 (&w)[2]) {
+        auto compute = [&](const uint4 *ring, const uint4 &w) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+            for (int bt = 0; bt < BJ; ++bt)
 #pragma unroll
-                for (int bt = 0; bt < BJ; ++bt)
-#pragma unroll
-                    for (int hl = 0; hl < 2; ++hl)
-                        acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, w[ks]),
-                            __builtin_bit_cast(bf16x8_t, ring[((bt * 2 + hl) * 2 + ks) * 64 + lane]), acc[bt], 0, 0, 0);
+                for (int hl = 0; hl < 2; ++hl)
+                    acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, w),
+                        __builtin_bit_cast(bf16x8_t, ring[((bt * 2 + hl) * 2 + ks) * 64 + lane]), acc[bt], 0, 0, 0);
         };
-        // step s: wait until this wave's copies and loads of stage s are done (those of
-        // s + 1 and s + 2 may stay in flight), meet the other waves, issue stage s + 3
-        // into the buffer of stage s - 1, multiply stage s
-        auto step = [&](int s, const uint4 *cur, uint4 *nxt, const uint4 (&wc)[2], uint4 (&wn)[2]) {
-            wait_vm<2 * (PER + 2)>();
+        auto step = [&](int s, const uint4 *cur, uint4 *nxt, const uint4 &wc, uint4 &wn) {
+            wait_vm<2 * (PER + 1)>();
             bare_barrier();
             issue(s + 3, nxt, wn);
             if (active && s < NS)
@@ -590,59 +828,99 @@ __device__ __forceinline__ void dots(const Params &p, int blk, int nblk, int q, 
             step(s + 2, ring2, ring1, wa[2], wa[1]);
             step(s + 3, ring3, ring2, wa[3], wa[2]);
         }
-        // the repeated copies of the last steps land before the ring is reused
         wait_vm<0>();
         bare_barrier();
-        if (!active)
-            continue;
-        // epilogue: lane holds weight rows m = 16 wt + 4 k + i of batch row b
-        const int m = 16 * wt + 4 * k;
+        if (ks == 1) {
 #pragma unroll
-        for (int bt = 0; bt < BJ; ++bt) {
-            const int b = (bj * BJ + bt) * 16 + row;
-            if (b >= p.B)
-                continue;
-            if (m < r) {
-                const float4 ah = *reinterpret_cast<const float4 *>(p.A_H + (static_cast<size_t>(b) * p.K + q) * r + m);
-                const float a4[4] = {ah.x + acc[bt][0], ah.y + acc[bt][1], ah.z + acc[bt][2], ah.w + acc[bt][3]};
-                float u4[4];
-                uint32_t hi[4], lo[4];
+            for (int bt = 0; bt < BJ; ++bt)
+                xch[(tw * BJ + bt) * 64 + lane] = acc[bt];
+        }
+        __syncthreads();
+        if (ks == 0 && active) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    u4[i] = a4[i] * sigmoidf_(a4[i]);
-                    hi[i] = bf16_rne_bits(u4[i]);
-                    lo[i] = bf16_rne_bits(u4[i] - __uint_as_float(hi[i] << 16));
+            for (int bt = 0; bt < BJ; ++bt) {
+                const f32x4_t o = xch[(tw * BJ + bt) * 64 + lane];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[bt][i] += o[i];
+            }
+            const int m = 16 * wt + 4 * k;
+#pragma unroll
+            for (int bt = 0; bt < BJ; ++bt) {
+                const int b = (bj * BJ + bt) * 16 + row;
+                if (b >= p.B)
+                    continue;
+                if (m < r) {
+                    const float4 ah =
+                        *reinterpret_cast<const float4 *>(p.A_H + (static_cast<size_t>(b) * p.K + q) * r + m);
+                    const float a4[4] = {ah.x + acc[bt][0], ah.y + acc[bt][1], ah.z + acc[bt][2], ah.w + acc[bt][3]};
+                    float u4[4];
+                    uint32_t hi[4], lo[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        u4[i] = a4[i] * sigmoidf_(a4[i]);
+                        hi[i] = bf16_rne_bits(u4[i]);
+                        lo[i] = bf16_rne_bits(u4[i] - __uint_as_float(hi[i] << 16));
+                    }
+                    if (p.u_out)
+                        *reinterpret_cast<float4 *>(p.u_out + (static_cast<size_t>(b) * p.K + q) * r + m) =
+                            make_float4(u4[0], u4[1], u4[2], u4[3]);
+                    const size_t ch = ((static_cast<size_t>(q) * p.rb_ngr + (b >> 4)) * 2 * KS + (m >> 5)) * 64 +
+                                      (b & 15) + 16 * ((m & 31) >> 3);
+                    char *dst = reinterpret_cast<char *>(p.uop + ch) + (m & 7) * 2;
+                    st_agent_u64(dst, pack4_bf16(hi[0], hi[1], hi[2], hi[3]));
+                    st_agent_u64(dst + static_cast<size_t>(KS) * 64 * 16, pack4_bf16(lo[0], lo[1], lo[2], lo[3]));
+                } else {
+                    const int mq = m - r;
+                    const float4 v = make_float4(acc[bt][0] + bias_hh(p, mq), acc[bt][1] + bias_hh(p, mq + 1),
+                                                 acc[bt][2] + bias_hh(p, mq + 2), acc[bt][3] + bias_hh(p, mq + 3));
+                    st_agent_f4(q_slot(p, q + 1) + static_cast<size_t>(b) * h3 + mq, v);
                 }
-                if (p.u_out)
-                    *reinterpret_cast<float4 *>(p.u_out + (static_cast<size_t>(b) * p.K + q) * r + m) =
-                        make_float4(u4[0], u4[1], u4[2], u4[3]);
-                // operand chunk of (batch row b, r offsets 8 (m / 8) .. + 8): group b / 16,
-                // step m / 32, lane b % 16 + 16 ((m % 32) / 8); these four values are its
-                // half (m % 8) / 4
-                const size_t ch = (static_cast<size_t>(b >> 4) * 2 * KS + (m >> 5)) * 64 + (b & 15) + 16 * ((m & 31) >> 3);
-                char *dst = reinterpret_cast<char *>(p.uop + ch) + (m & 7) * 2;
-                st_agent_u64(dst, pack4_bf16(hi[0], hi[1], hi[2], hi[3]));
-                st_agent_u64(dst + static_cast<size_t>(KS) * 64 * 16, pack4_bf16(lo[0], lo[1], lo[2], lo[3]));
-            } else {
-                const int mq = m - r;
-                const float4 v = make_float4(acc[bt][0] + bias_hh(p, mq), acc[bt][1] + bias_hh(p, mq + 1),
-                                             acc[bt][2] + bias_hh(p, mq + 2), acc[bt][3] + bias_hh(p, mq + 3));
-                st_agent_f4(q_slot(p, q + 1) + static_cast<size_t>(b) * h3 + mq, v);
             }
         }
+        if (urows && q >= 0) {
+            // this job's share of u_q is written: count it
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_fetch_add(&p.rb_ucnt[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // the exchange buffer is the first ring buffer of the next job
+        __syncthreads();
     }
 }
 
-__device__ __forceinline__ void dots_any(const Params &p, int blk, int nblk, int q, uint4 *r0, uint4 *r1, uint4 *r2,
-                                         uint4 *r3)
+__device__ __forceinline__ void dots(const Params &p, int blk, int nblk, int q, uint4 *lbA, uint4 *lbB, uint4 *lbC,
+                                     uint4 *uA, uint4 *uB)
 {
-    const int nbt = (p.B + 15) / 16;
-    if (nbt >= 4)
-        dots<4>(p, blk, nblk, q, r0, r1, r2, r3);
-    else if (nbt >= 2)
-        dots<2>(p, blk, nblk, q, r0, r1, r2, r3);
+    if (dots_tiled(p.B))
+        dots_2d(p, blk, nblk, q, lbA, lbB, lbC, uA);
     else
-        dots<1>(p, blk, nblk, q, r0, r1, r2, r3);
+        dots_small(p, blk, q, lbA, lbB, lbC, uA, uB);
+}
+
+// The W2 phase of position q waits until every block of the u rows has written its
+// share of u_q.  False on a timeout.
+__device__ __forceinline__ bool wait_u(const Params &p, int q)
+{
+    int ok = 1;
+    if (threadIdx.x == 0) {
+        const unsigned want = static_cast<unsigned>(u_producers(p.B, p.r));
+        unsigned spins = 0;
+        while (__hip_atomic_load(&p.rb_ucnt[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+            if (++spins > p.spin_limit) {
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    if (block_failed(ok)) {
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_or(p.flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+    }
+    return true;
 }
 
 template <bool LB16, bool FAST, bool ST>
@@ -655,15 +933,21 @@ __global__ __launch_bounds__(NT) void k_persistent_rb(Params p)
     __shared__ uint64_t rred[NWAVE * ROWS];
     __shared__ int rtok[ROWS];
     const int blk = blockIdx.x, nblk = gridDim.x;
+    // nothing in this XCD's L2 predates the launch (see the header comment)
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     unsigned gen = barrier_gen_init(p.bar);
     block_fail_init();
     if (blk == 0) {
         for (int b = threadIdx.x; b < p.B; b += NT)
             if (row_bad(p, b))
                 __hip_atomic_fetch_or(p.flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the u counters of this launch start at 0 (the first increment follows a barrier)
+        if (threadIdx.x < static_cast<unsigned>(p.K))
+            __hip_atomic_store(&p.rb_ucnt[threadIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     const Ctx c = make_ctx(p, blk, nblk);
-    // the block's W2 slice: tile t = wave + 4 j in registers (zero past the range)
+    // the block's W2 slice: tile t = wave + NWAVE j in registers (zero past the range),
+    // and its tile of the state rows
     W2Resident<RT, KS> res;
     {
         const int wave = threadIdx.x >> 6;
@@ -678,10 +962,11 @@ __global__ __launch_bounds__(NT) void k_persistent_rb(Params p)
     }
     RB_MARK(1023);
     if (p.S_init) {
+        // q = W_hh S_init + b_hh for the anchor step
         update(p, c, -1, rtok);
         if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
             return;
-            dots_any(p, blk, nblk, -1, lbA, lbB, lbC, uA);
+        dots(p, blk, nblk, -1, lbA, lbB, lbC, uA, uB);
         if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
             return;
     }
@@ -690,18 +975,27 @@ __global__ __launch_bounds__(NT) void k_persistent_rb(Params p)
     if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
         return;
     RB_MARK(1021);
-    dots_any(p, blk, nblk, 0, lbA, lbB, lbC, uA);
+    dots(p, blk, nblk, 0, lbA, lbB, lbC, uA, uB);
     RB_MARK(1020);
-    if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
-        return;
-    RB_MARK(1019);
+    // per position: W2 phase (after the blocks of the u rows have written u), argmax
+    // words, update of the block's state entries, one grid barrier, state products
     for (int pos = 0; pos < p.K; ++pos) {
         // argmax words of this position carry tag gen + 1 (every block is at the same
-        // generation here; consecutive positions are two generations apart)
+        // generation here; consecutive positions are a generation apart)
         const uint32_t tag14 = (gen + 1) & 0x3FFFu;
+        // the pointers pass through an opaque copy each position, so the per-thread
+        // addresses derived from them are recomputed in each phase instead of being
+        // hoisted out of the loop into (spilled) registers
         Params pl = p;
-        asm volatile("" : "+s"(pl.L_base), "+s"(pl.L_final), "+s"(pl.uop), "+s"(pl.bkeys));
+        asm volatile("" : "+s"(pl.L_base), "+s"(pl.L_final), "+s"(pl.uop), "+s"(pl.bkeys), "+s"(pl.rb_planes),
+                          "+s"(pl.wst), "+s"(pl.A_H), "+s"(pl.q_buf), "+s"(pl.S_buf), "+s"(pl.P), "+s"(pl.tokens));
+        asm volatile("" : "+s"(pl.S_out), "+s"(pl.u_out), "+s"(pl.rb_ucnt), "+s"(pl.teacher), "+s"(pl.last_tok),
+                          "+s"(pl.b_hh), "+s"(pl.flags), "+s"(pl.bar));
+        w2_prefetch<LB16, FAST>(pl, c, pos, lbA, lbB);
         RB_MARK(64 * pos);
+        if (!wait_u(pl, pos))
+            return;
+        RB_MARK(64 * pos + 7);
         w2_phase<LB16, FAST, ST>(pl, c, res, pos, tag14, lbA, lbB, lbC, uA, uB, kred, lkey);
         RB_MARK(64 * pos + 1);
         if (!resolve(pl, c, pos, tag14, rtok, rred))
@@ -712,16 +1006,13 @@ __global__ __launch_bounds__(NT) void k_persistent_rb(Params p)
             RB_MARK(64 * pos + 3);
             if (!grid_sync(pl.bar, gen, pl.spin_limit, pl.flags))
                 return;
-                    RB_MARK(64 * pos + 4);
-            dots_any(pl, blk, nblk, pos + 1, lbA, lbB, lbC, uA);
+            RB_MARK(64 * pos + 4);
+            dots(pl, blk, nblk, pos + 1, lbA, lbB, lbC, uA, uB);
             RB_MARK(64 * pos + 5);
-            if (!grid_sync(pl.bar, gen, pl.spin_limit, pl.flags))
-                return;
-                    RB_MARK(64 * pos + 6);
         }
     }
     // words of rows this launch did not draft get a tag that no later poll expects
-    // (later launches poll for tags at least three generations past gen)
+    // (later launches poll for tags at least two generations past gen)
     for (int b = p.B + static_cast<int>(threadIdx.x); b < p.maxB; b += NT)
         st_agent_u64(&p.bkeys[static_cast<size_t>(b) * nblk + blk], static_cast<uint64_t>(gen & 0x3FFFu) << 18);
     barrier_finish(p.bar, gen);
@@ -732,7 +1023,7 @@ __global__ __launch_bounds__(NT) void k_persistent_rb(Params p)
 
 namespace dhrb {
 
-using namespace dh256;
+using namespace dhrbk;
 
 int threads() { return NT; }
 int r_supported() { return rbk::R; }

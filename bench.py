@@ -70,15 +70,24 @@ def algorithmic_flops(sh, B, fold=False, markov=False):
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
 
-# Sources each timed kernel is compiled from: a counter summary stays valid while these
+# Sources each timed launch kind is compiled from: a counter summary stays valid while these
 # files are unchanged (changes elsewhere in the library do not touch the kernel).
 KERNEL_SOURCES = {
-    "persistent": ["domino_head_res.hip", "dh_resident.h", "dh_phases.h", "dh_common.h", "dh_params.h"],
+    "persistent_res": ["domino_head_res.hip", "dh_resident.h", "dh_phases.h", "dh_common.h", "dh_params.h"],
+    "markov_res": ["domino_head_res.hip", "dh_resident.h", "dh_phases.h", "dh_common.h", "dh_params.h"],
+    "persistent_rb": ["domino_head_rb.hip", "dh_rbatch.h", "dh_phases.h", "dh_common.h", "dh_params.h"],
+    "persistent": ["domino_head.hip", "dh_phases.h", "dh_common.h", "dh_params.h"],
+    "stepwise": ["domino_head.hip", "domino_head_bat.hip", "dh_batched.h", "dh_phases.h", "dh_common.h",
+                 "dh_params.h"],
     "verify": ["domino_verify.hip", "dh_verify.h", "dh_common.h"],
 }
+# the kernel each persistent launch kind runs (the stepwise kind is a sequence of launches)
+KERNEL_NAMES = {"persistent_res": "k_persistent_res", "markov_res": "k_markov_res",
+                "persistent_rb": "k_persistent_rb", "persistent": "k_persistent",
+                "stepwise": "stepwise launches (whole call)"}
 
 
-def kernel_source_hash(kind="persistent"):
+def kernel_source_hash(kind):
     import hashlib
 
     h = hashlib.sha256()
@@ -88,24 +97,72 @@ def kernel_source_hash(kind="persistent"):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, exec_name, fold, w2_on_chip):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, when it was taken
-    on the current kernel sources, the same workload and the same launch; else None."""
+def measured_traffic(workload, kind, fold):
+    """HBM bytes per call from the committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE
+    over the call's launches, scaled by a plain copy of known size), when it was taken on the
+    current kernel sources, the same workload and the same launch kind; else None."""
     import glob
 
-    cur = kernel_source_hash("verify" if exec_name == "verify" else "persistent")
+    cur = kernel_source_hash(kind)
     for f in glob.glob(os.path.join(ROOT, "profiles", "*_counters.json")):
         with open(f) as fh:
             d = json.load(fh)
         if (d.get("kernel_source_sha256_16") == cur and d.get("workload") == workload and
-                d.get("exec") == exec_name and bool(d.get("fold_embedding")) == fold and
-                bool(d.get("w2_on_chip")) == w2_on_chip):
+                d.get("exec") == kind and bool(d.get("fold_embedding")) == fold):
             return d["traffic_bytes_per_launch"]
     return None
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count()
+
+
+def achievable_rates():
+    """What the box reaches on plain library work, beside the vendor peaks: a 1 GiB device
+    copy (read + write bytes / time) and a 8192^3 bf16 matrix product (torch.mm)."""
+    import torch
+
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    for _ in range(2):
+        dst.copy_(src)
+        torch.mm(a, b)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    for _ in range(5):
+        dst.copy_(src)
+    e[1].record()
+    for _ in range(5):
+        torch.mm(a, b)
+    e[2].record()
+    torch.cuda.synchronize()
+    copy_s = e[0].elapsed_time(e[1]) * 1e-3 / 5
+    mm_s = e[1].elapsed_time(e[2]) * 1e-3 / 5
+    del src, dst, a, b
+    return {"copy_GBps": 2 * n * 4 / copy_s / 1e9, "bf16_gemm_8192_TFLOPs": 2 * 8192 ** 3 / mm_s / 1e12}
+
+
 def cpu_baseline(w, inp, budget_s, markov=False):
-    """The fp64 oracle as it stands, on this host's cores, on row 0 of the workload."""
+    """The fp64 oracle as it stands, on this host's cores, on row 0 of the workload; then one
+    draft of the same row on one thread.  Returns (drafts, seconds, threads, one-thread seconds)."""
     import oracle
 
     n = 0
@@ -117,7 +174,10 @@ def cpu_baseline(w, inp, budget_s, markov=False):
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    return n, el, oracle.max_threads()
+    t1 = time.perf_counter()
+    oracle.draft(w, inp.H[:1], inp.L_base[:1], inp.last_tok[:1], want_logits=False, want_state=False,
+                 markov=markov, threads=1)
+    return n, el, oracle.max_threads(), time.perf_counter() - t1
 
 
 def run_verify(args, wl):
@@ -177,7 +237,7 @@ def run_verify(args, wl):
     total_bytes = B * (K + 1) * V * 4 + B * K * 4 + B * (K + 1) * 4 + 2 * B * 4
     achieved = total_bytes / (avg_ms * 1e-3) / 1e9
     name = "verify_" + wl.name
-    traffic = measured_traffic(name, "verify", False, False)
+    traffic = measured_traffic(name, "verify", False)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -234,6 +294,8 @@ def main():
                     help="do not precompute the folded input-gate table (GRU input GEMV every step)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the achievable copy / bf16 GEMM rates printed beside the vendor peaks")
     ap.add_argument("--teacher", action="store_true",
                     help="teacher-forced drafting: a seeded uniform teacher token row per batch row")
     ap.add_argument("--position-batched", action="store_true",
@@ -291,10 +353,19 @@ def main():
     if args.store_logits:
         out["L_final"] = torch.empty((wl.B, sh.K, sh.V), dtype=torch.float32, device="cuda")
     info = head.exec_info(wl.B)
+    if not info["persistent"]:
+        kind = "stepwise"
+    elif not info["w2_resident"]:
+        kind = "persistent"
+    elif wl.B > 8:
+        kind = "persistent_rb"
+    else:
+        kind = "markov_res" if args.markov else "persistent_res"
     exec_name = "persistent" if info["persistent"] else "stepwise"
     if args.teacher and (args.position_batched or not info["persistent"]):
         info = dict(info, persistent=False, w2_resident=False)
         exec_name = "stepwise, position-batched"
+        kind = "stepwise"
 
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20) // 4
@@ -365,12 +436,15 @@ def main():
     achieved = total_bytes / (avg_ms * 1e-3) / 1e9
     w2l = w2l_bytes / (avg_ms * 1e-3) / 1e9
     w2_on_chip = info["w2_resident"]
-    traffic = (measured_traffic(wl.name + ("_markov" if args.markov else ""), exec_name, fold, w2_on_chip)
-               if exec_name == "persistent" and not args.lbase_bf16 and not args.teacher else None)
-    if exec_name == "persistent":
-        kname = ("k_markov_res" if args.markov else "k_persistent_res") if w2_on_chip else "k_persistent"
-    else:
-        kname = "stepwise launches (whole call)"
+    # counters are taken on the plain fp32-L_base free-running call of each workload
+    traffic = (measured_traffic(wl.name + ("_markov" if args.markov else ""), kind, fold)
+               if not args.lbase_bf16 and not args.teacher and not args.store_logits and not args.graph else None)
+    kname = KERNEL_NAMES[kind]
+    hbm_actual = None if traffic is None else traffic / (avg_ms * 1e-3) / 1e9
+    # a persistent launch runs the K positions as one dependent chain inside one kernel: its time
+    # is set by the per-position latency (phases, grid barriers), not by HBM (the counters show
+    # HBM far from busy) or the matrix cores; the step launches at large B stream L_base and W2
+    bound = "latency" if info["persistent"] else "hbm"
 
     f_w2, f_all = algorithmic_flops(sh, wl.B, fold, args.markov)
     mfma = {"w2_tflops": f_w2 / (avg_ms * 1e-3) / 1e12, "all_tflops": f_all / (avg_ms * 1e-3) / 1e12,
@@ -381,11 +455,18 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         eprint("bench: timing the fp64 oracle on the host (cpu_baseline)")
-        n, el, threads = cpu_baseline(w, inp, args.cpu_budget, args.markov)
+        n, el, threads, one_s = cpu_baseline(w, inp, args.cpu_budget, args.markov)
         cpu = {"value": n / el, "unit": "blocks/s", "cores": threads, "kind": "oracle",
-               "sample": "%d block draft(s) of row 0 of %s (free running, K=%d, V=%d%s), fp64 C oracle" % (
-                   n, wl.name, sh.K, sh.V, ", Markov head" if args.markov else "")}
+               "sample": "%d block draft(s) of row 0 of %s (free running, K=%d, V=%d%s), fp64 C oracle on %d "
+                         "threads; then one draft of the same row on one thread" % (
+                             n, wl.name, sh.K, sh.V, ", Markov head" if args.markov else "", threads),
+               "cpu_model": cpu_model(), "host_cores": host_cores(), "one_thread_s_per_block": one_s}
+    calib = None
+    if not args.no_calibration:
+        eprint("bench: achievable copy and bf16 GEMM rates")
+        calib = achievable_rates()
 
+    cold_achieved = None if cold_us is None else total_bytes / (cold_us * 1e-6) / 1e9
     rec = {
         "metric": "Domino-head draft blocks/sec (16 tok, V=151936) + achieved HBM GB/s at 1 GPU",
         "value": blocks_per_s,
@@ -397,21 +478,32 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": sh.wdtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "K": sh.K, "V": sh.V, "d": sh.d, "h": sh.h, "r": sh.r,
-                   "weights": sh.wdtype, "exec": exec_name, "store_logits": bool(args.store_logits),
-                   "fold_embedding": fold, "w2_on_chip": w2_on_chip,
+                   "weights": sh.wdtype, "accumulate": "f32", "lbase_dtype": "bf16" if args.lbase_bf16 else "f32",
+                   "exec": exec_name, "kernel": kname, "grid": info["grid"],
+                   "store_logits": bool(args.store_logits), "fold_embedding": fold, "w2_on_chip": w2_on_chip,
                    "launch": "plain" if args.plain_launch else "cooperative", "create_s": t_create,
-                   "teacher_forced": bool(args.teacher), "lbase_dtype": "bf16" if args.lbase_bf16 else "f32",
+                   "teacher_forced": bool(args.teacher),
                    "head": "markov" if args.markov else "recurrent (GRU)",
                    "hip_graph": bool(args.graph),
-                   "kernel_avg_us": avg_ms * 1e3, "warm_us_per_call_median": float(np.median(per_call_ms)) * 1e3,
-                   "cold_us_per_call_median": cold_us, "w2_lbase_GBps": w2l,
-                   "w2_lbase_frac_of_hbm_peak": w2l / HBM_PEAK_GBPS, "matrix_core_use": mfma},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                   "call_avg_us": avg_ms * 1e3, "warm_us_per_call_median": float(np.median(per_call_ms)) * 1e3,
+                   "cold_us_per_call_median": cold_us, "us_per_position": avg_ms * 1e3 / sh.K,
+                   "w2_lbase_GBps": w2l, "w2_lbase_frac_of_hbm_peak": w2l / HBM_PEAK_GBPS,
+                   "matrix_core_use": mfma, "achievable": calib},
+        # achieved/frac: algorithmic bytes per call over the mean hipEvent call time of the timed
+        # steps (an effective rate: W2 that stays on chip counts once per position); the _cold
+        # figures repeat it on calls made after evicting L2 and MALL, the serving case;
+        # hbm_actual: the bytes the counters saw per call over the same mean call time
+        "roofline": {"bound": bound, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "algorithmic_bytes": total_bytes, "kernel": kname},
+                     "algorithmic_bytes": total_bytes, "kernel": kname,
+                     "achieved_cold": cold_achieved,
+                     "frac_cold": None if cold_achieved is None else cold_achieved / HBM_PEAK_GBPS,
+                     "hbm_actual_GBps": hbm_actual,
+                     "hbm_actual_frac": None if hbm_actual is None else hbm_actual / HBM_PEAK_GBPS,
+                     "us_per_position": avg_ms * 1e3 / sh.K},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

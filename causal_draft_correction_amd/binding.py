@@ -14,7 +14,8 @@ from typing import Optional
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdomino_head.so")
+# DOMINO_LIB names another build of the same sources (the host-sanitizer test uses it)
+LIB_PATH = os.environ.get("DOMINO_LIB") or os.path.join(HERE, "libdomino_head.so")
 
 DOMINO_F32 = 0
 DOMINO_BF16 = 1
@@ -34,7 +35,7 @@ ERRORS = {-1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP", -5: "E
 
 SYMBOLS = ("domino_head_workspace_size", "domino_head_create", "domino_head_draft", "domino_accept_len",
            "domino_verify_workspace_size", "domino_verify", "domino_head_check_error", "domino_head_exec_info",
-           "domino_head_param_count", "domino_head_destroy", "domino_last_error")
+           "domino_head_set_spin_limit", "domino_head_param_count", "domino_head_destroy", "domino_last_error")
 
 
 class DominoError(RuntimeError):
@@ -73,6 +74,7 @@ def load_library(path: str = LIB_PATH):
     lib.domino_head_check_error.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
     PI = ctypes.POINTER(ctypes.c_int32)
     lib.domino_head_exec_info.argtypes = [P, I32, PI, PI, PI]
+    lib.domino_head_set_spin_limit.argtypes = [P, ctypes.c_uint32]
     lib.domino_head_param_count.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_int64)]
     lib.domino_head_destroy.argtypes = [P]
     lib.domino_head_destroy.restype = None
@@ -195,6 +197,15 @@ class DominoHead:
             self._check_tensor("teacher", teacher, (B, self.K), torch.int32)
         if S_init is not None:
             self._check_tensor("S_init", S_init, (B, self.h), torch.float32)
+        # the kernels write these through raw pointers: a short or mistyped buffer would be overrun
+        shapes = {"tokens": ((B, self.K), torch.int32), "L_final": ((B, self.K, self.V), torch.float32),
+                  "S": ((B, self.K, self.h), torch.float32), "u": ((B, self.K, self.r), torch.float32)}
+        for k, t in out.items():
+            if k not in shapes:
+                raise ValueError("out: unknown entry %r (expected tokens, L_final, S, u)" % k)
+            if k == "S" and self.markov:
+                raise ValueError("out: a Markov head returns no S")
+            self._check_tensor("out[%r]" % k, t, *shapes[k])
         _check(load_library().domino_head_draft(
             self._h, B, _ptr(H), _ptr(L_base), _ptr(last_tok), _ptr(teacher), _ptr(S_init), _ptr(out["tokens"]),
             _ptr(out.get("L_final")), _ptr(out.get("S")), _ptr(out.get("u")), _stream_handle()))
@@ -207,6 +218,10 @@ class DominoHead:
         _check(load_library().domino_head_exec_info(self._h, B, *[ctypes.byref(x) for x in v]))
         return {"persistent": bool(v[0].value), "w2_resident": bool(v[1].value), "grid": int(v[2].value)}
 
+    def set_spin_limit(self, limit: int):
+        """Bound on the device-side waits of later drafts (0 forces the timeout path)."""
+        _check(load_library().domino_head_set_spin_limit(self._h, int(limit)))
+
     def check_error(self) -> int:
         """Synchronize, return and clear the device flags (raises DominoError if any is set)."""
         f = ctypes.c_uint32()
@@ -215,11 +230,13 @@ class DominoHead:
             _check(rc)
         return int(f.value)
 
-    @staticmethod
-    def _check_tensor(name, t, shape, dtype):
-        if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("%s: expected contiguous CUDA %s of shape %s, got %s %s" %
-                             (name, dtype, shape, t.dtype, tuple(t.shape)))
+    def _check_tensor(self, name, t, shape, dtype):
+        if (not isinstance(t, torch.Tensor) or t.dtype != dtype or tuple(t.shape) != tuple(shape) or
+                t.device != self.device or not t.is_contiguous()):
+            raise ValueError("%s: expected a contiguous %s tensor on %s of shape %s, got %s" %
+                             (name, dtype, self.device, shape,
+                              "%s %s on %s" % (t.dtype, tuple(t.shape), t.device) if isinstance(t, torch.Tensor)
+                              else type(t).__name__))
 
 
 def accept_len(draft: torch.Tensor, target: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:

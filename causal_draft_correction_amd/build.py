@@ -1,4 +1,6 @@
-"""Builds libdomino_head.so (HIP, gfx950) in the package directory."""
+"""Builds libdomino_head.so (HIP, gfx950) in the package directory, and beside it
+libdomino_trace.so: the same library with the persistent kernels' phase hooks
+recording device timestamps (read by phase_trace.py; never loaded otherwise)."""
 from __future__ import annotations
 
 import os
@@ -11,6 +13,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC_DIR = os.path.join(HERE, "csrc")
 UNITS = ["domino_head.hip", "domino_head_res.hip", "domino_head_bat.hip", "domino_head_rb.hip", "domino_verify.hip"]
 LIB = os.path.join(HERE, "libdomino_head.so")
+# the instrumented library: these units replace domino_head_res.hip and domino_head_rb.hip
+TRACE_UNITS = ["trace/trace_res.hip", "trace/trace_rb.hip"]
+TRACE_REPLACES = ["domino_head_res.hip", "domino_head_rb.hip"]
+TRACE_LIB = os.path.join(HERE, "libdomino_trace.so")
 ARCH = "gfx950"
 # packed-fp32 instructions are disabled in all device code
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",
@@ -47,20 +53,27 @@ def _run(cmd):
     return errs
 
 
-def build(verbose: bool = False) -> str:
-    """Compile each translation unit for gfx950 (in parallel), then link the library."""
+def build(verbose: bool = False, trace: bool = True) -> str:
+    """Compile each translation unit for gfx950 (in parallel), then link the library
+    (and, with `trace`, the instrumented library from the same objects)."""
     cc = hipcc()
+    units = UNITS + (TRACE_UNITS if trace else [])
     with tempfile.TemporaryDirectory(prefix="domino_build_") as tmpdir:
-        objs = [os.path.join(tmpdir, u.replace(".hip", ".o")) for u in UNITS]
-        jobs = [[cc] + FLAGS + ["-c", os.path.join(SRC_DIR, u), "-o", o] for u, o in zip(UNITS, objs)]
+        obj = {u: os.path.join(tmpdir, os.path.basename(u).replace(".hip", ".o")) for u in units}
+        jobs = [[cc] + FLAGS + ["-c", os.path.join(SRC_DIR, u), "-o", obj[u]] for u in units]
         workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
         with ThreadPoolExecutor(max_workers=workers) as ex:
             errs = list(ex.map(_run, jobs))
-        tmp = LIB + ".tmp%d" % os.getpid()
-        errs.append(_run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]))
+        links = [(LIB, [obj[u] for u in UNITS])]
+        if trace:
+            links.append((TRACE_LIB, [obj[u] for u in UNITS if u not in TRACE_REPLACES] +
+                          [obj[u] for u in TRACE_UNITS]))
+        for lib, objs in links:
+            tmp = lib + ".tmp%d" % os.getpid()
+            errs.append(_run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]))
+            os.replace(tmp, lib)
     if verbose and any(e.strip() for e in errs):
         print("\n".join(e for e in errs if e.strip()))
-    os.replace(tmp, LIB)
     return LIB
 
 

@@ -19,7 +19,8 @@
 
 // Optional instrumentation: a translation unit may define DH_TRACE(slot) before
 // including these headers to record timestamps at the marked points of the
-// persistent kernels (slot = 32 * position + point).  The default is a no-op.
+// resident persistent kernels (slot = 32 * position + point, -16..-12 for the
+// anchor step, 508..511 for the prologue).  The default is a no-op.
 #ifndef DH_TRACE
 #define DH_TRACE(slot) ((void)(slot))
 #endif
@@ -333,7 +334,6 @@ __device__ inline void grid_arrive(unsigned *bar, unsigned gen)
     __syncthreads();
     if (threadIdx.x == 0)
         __hip_atomic_store(&bar_slots(bar)[blockIdx.x], gen + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    DH_TRACE((static_cast<int>(gen + 1) - 4) / 2 * 32 + 24);
 }
 
 __device__ inline bool grid_wait(unsigned *bar, unsigned &gen, unsigned spin_limit, unsigned *flags)
@@ -353,12 +353,10 @@ __device__ inline bool grid_wait(unsigned *bar, unsigned &gen, unsigned spin_lim
         }
     }
     gen = next;
-    DH_TRACE((static_cast<int>(next) - 4) / 2 * 32 + 26);
     const bool failed = block_failed(ok);
     if (failed && threadIdx.x == 0)
         __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    DH_TRACE((static_cast<int>(next) - 4) / 2 * 32 + 27);
     return !failed;
 }
 
@@ -414,7 +412,6 @@ __device__ inline void argmax_arrive(uint64_t *asy, unsigned gen, const uint64_t
         __hip_atomic_store(&asy[argmax_word(gen + 1, blockIdx.x, threadIdx.x)], k | g14, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    DH_TRACE((static_cast<int>(gen + 1) - 2) * 32 + 8);
 }
 
 __device__ inline bool argmax_wait(const uint64_t *asy, unsigned &gen, int nb, int *tok, unsigned spin_limit,
@@ -450,7 +447,6 @@ __device__ inline bool argmax_wait(const uint64_t *asy, unsigned &gen, int nb, i
             if (bb == b)
                 best[bb] = max_u64(best[bb], k);
     }
-    DH_TRACE((static_cast<int>(next) - 2) * 32 + 11);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int b = 0; b < BC; ++b) {
@@ -471,7 +467,6 @@ __device__ inline bool argmax_wait(const uint64_t *asy, unsigned &gen, int nb, i
     if (failed && threadIdx.x == 0)
         __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();  // tok visible to the block
-    DH_TRACE((static_cast<int>(next) - 2) * 32 + 12);
     return !failed;
 }
 

@@ -1140,6 +1140,14 @@ int domino_head_exec_info(domino_head_t hd, int32_t B, int32_t *persistent, int3
     return DOMINO_OK;
 }
 
+int domino_head_set_spin_limit(domino_head_t hd, uint32_t limit)
+{
+    if (!hd)
+        return fail(DOMINO_EINVAL, "handle is NULL");
+    hd->spin_limit = limit;
+    return DOMINO_OK;
+}
+
 int domino_head_check_error(domino_head_t hd, uint32_t *device_flags)
 {
     if (!hd)

@@ -47,7 +47,7 @@
 
 // Optional instrumentation: a translation unit may define RB_MARK(slot) before
 // including this file to record timestamps at phase boundaries (slot = 64 *
-// position + point; the prologue uses slots 1018..1023).  The default is a no-op.
+// position + point; the prologue uses slots 1019..1023).  The default is a no-op.
 #ifndef RB_MARK
 #define RB_MARK(slot) ((void)(slot))
 #endif
@@ -933,6 +933,7 @@ __global__ __launch_bounds__(NT) void k_persistent_rb(Params p)
     __shared__ uint64_t rred[NWAVE * ROWS];
     __shared__ int rtok[ROWS];
     const int blk = blockIdx.x, nblk = gridDim.x;
+    RB_MARK(1019);
     // nothing in this XCD's L2 predates the launch (see the header comment)
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     unsigned gen = barrier_gen_init(p.bar);

@@ -33,6 +33,7 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
     }
     // u words of a position carry tag gen + 1 (gen: the barrier generation when its
     // state phase runs), never 0, the value cleared words hold
+    DH_TRACE(511);
     W2Resident<RT, KS> res;
     if (NB == 1 && !p.S_init && p.P) {
         // one batch row, no initial state, folded table: the prologue needs no grid

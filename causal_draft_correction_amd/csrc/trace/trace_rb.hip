@@ -1,0 +1,20 @@
+// The batched resident kernel with its RB_MARK hooks recording into trace_rb_buf.
+#include "trace_buf.h"
+
+__device__ unsigned long long trace_rb_buf[TRACE_BLOCKS * TRACE_SLOTS];
+#define RB_MARK(slot) TRACE_MARK(trace_rb_buf, 0, slot)
+
+#include "../domino_head_rb.hip"
+
+// Copies the whole buffer (TRACE_BLOCKS x TRACE_SLOTS u64, row per block) to `host`.
+extern "C" int domino_trace_read_rb(void *host)
+{
+    return static_cast<int>(hipMemcpyFromSymbol(host, HIP_SYMBOL(trace_rb_buf), sizeof(trace_rb_buf)));
+}
+
+// Zeroes the buffer (synchronous).
+extern "C" int domino_trace_clear_rb(void)
+{
+    static unsigned long long zero[TRACE_BLOCKS * TRACE_SLOTS];
+    return static_cast<int>(hipMemcpyToSymbol(HIP_SYMBOL(trace_rb_buf), zero, sizeof(zero)));
+}

@@ -1,0 +1,140 @@
+"""Per-phase timing of one persistent draft call, from device timestamps.
+
+Loads libdomino_trace.so (built beside libdomino_head.so by build.py: the same
+library with the phase hooks of the resident persistent kernels recording the
+100 MHz device clock per block), drafts a named synthetic workload a few
+times, then reads the timestamps of the last call and reports, per phase, the
+median over blocks (and the slowest block) of the time between its two marks.
+Positions 1..K-2 are summarised by the median over positions; the anchor step,
+the first and the last position are listed separately.
+
+    python -m causal_draft_correction_amd.phase_trace qwen3_8b_b1 [qwen3_8b_b32 ...] [--json]
+
+Only this tool loads the instrumented library; it needs a GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+TICK_US = 0.01  # the device clock runs at 100 MHz
+BLOCKS, SLOTS = 256, 1024
+
+# resident B <= 8 kernels (k_persistent_res): hook slot + 64 is the column
+RES_BIAS = 64
+# (name, first mark, second mark) relative to 32 * position
+RES_POSITION = [("w2_wait_u", 0, 1), ("w2_products", 2, 4), ("w2_block_key", 4, 5), ("argmax_exchange", 5, 13),
+                ("gru_gates", 16, 18), ("state_sync", 18, 19), ("state_dots", 19, 20), ("u_hop", 20, 32),
+                ("position", 0, 32)]
+RES_PROLOGUE = [("slice_and_loads_issued", 511, 508), ("anchor_step", -16, -12), ("prologue", 511, 509)]
+
+# batched kernel (k_persistent_rb): hook slot is the column; marks relative to 64 * position
+RB_POSITION = [("wait_u", 0, 7), ("w2", 7, 1), ("resolve", 1, 2), ("gru_update", 2, 3), ("grid_barrier", 3, 4),
+               ("state_dots", 4, 5), ("to_next_position", 5, 64), ("position", 0, 64)]
+RB_PROLOGUE = [("w2_slice_load", 1019, 1023), ("anchor_update", 1023, 1022), ("grid_barrier", 1022, 1021),
+               ("anchor_dots", 1021, 1020), ("prologue", 1019, 1020)]
+
+
+def _span(t, a, b):
+    d = (t[:, b] - t[:, a]).astype(np.float64) * TICK_US
+    return float(np.median(d)), float(d.max())
+
+
+def summarize(t, K, batched):
+    """t: [blocks, SLOTS] int64 timestamps of one call.  Returns a dict of phase -> [median, max] us."""
+    if batched:
+        col = lambda s: s  # noqa: E731
+        per, pro, stride, end = RB_POSITION, RB_PROLOGUE, 64, 64 * (K - 1) + 2
+        start = 1019
+    else:
+        col = lambda s: s + RES_BIAS  # noqa: E731
+        per, pro, stride, end = RES_POSITION, RES_PROLOGUE, 32, 32 * (K - 1) + 13
+        start = 511
+    out = {"kernel_us": round(float((t[:, col(end)].max() - t[:, col(start)].min()) * TICK_US), 1)}
+    out["prologue"] = {n: [round(x, 2) for x in _span(t, col(a), col(b))] for n, a, b in pro}
+    for p in sorted({0, K - 1}):
+        out["position_%d" % p] = {n: [round(x, 2) for x in _span(t, col(stride * p + a), col(stride * p + b))]
+                                  for n, a, b in per if stride * p + b <= end}
+    mids = range(1, K - 1)
+    if len(mids):
+        out["positions_1_to_%d_median" % (K - 2)] = {
+            n: [round(float(np.median([_span(t, col(stride * p + a), col(stride * p + b))[i] for p in mids])), 2)
+                for i in (0, 1)] for n, a, b in per}
+    return out
+
+
+def run(names, lib_path=None):
+    sys.path.insert(0, ROOT)
+    import torch
+
+    from causal_draft_correction_amd import binding
+
+    lib = binding.load_library(lib_path or os.path.join(HERE, "libdomino_trace.so"))
+    import causal_draft_correction_amd as dca
+    import domino_synth as ds
+
+    for f in ("domino_trace_read_res", "domino_trace_read_rb"):
+        getattr(lib, f).argtypes = [ctypes.c_void_p]
+    results = {}
+    for name in names:
+        wl = ds.WORKLOADS[name]
+        sh = wl.shape
+        w, inp = ds.make_workload(name)
+        head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B, fold_embedding=True)
+        info = head.exec_info(wl.B)
+        if not (info["persistent"] and info["w2_resident"]):
+            raise SystemExit("%s does not take a resident persistent launch (%s)" % (name, info))
+        batched = wl.B > 8
+        H, L, lt = dca.device_tensor(inp.H), dca.device_tensor(inp.L_base), dca.device_tensor(inp.last_tok)
+        out = {"tokens": torch.empty((wl.B, sh.K), dtype=torch.int32, device="cuda")}
+        for _ in range(3):
+            head.draft(H, L, lt, out=out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        head.draft(H, L, lt, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        assert head.check_error() == 0
+        buf = np.zeros(BLOCKS * SLOTS, np.uint64)
+        rc = (lib.domino_trace_read_rb if batched else lib.domino_trace_read_res)(buf.ctypes.data)
+        assert rc == 0, rc
+        t = buf.reshape(BLOCKS, SLOTS)[:min(info["grid"], BLOCKS)].astype(np.int64)
+        r = {"workload": name, "B": wl.B, "kernel": "k_persistent_rb" if batched else "k_persistent_res",
+             "grid": info["grid"], "call_us": round(e0.elapsed_time(e1) * 1e3, 1)}
+        r.update(summarize(t, sh.K, batched))
+        results[name] = r
+        del head
+    return results
+
+
+def to_markdown(r):
+    lines = ["### %s (B=%d, %s, %d blocks): call %.1f us, kernel %.1f us" % (
+        r["workload"], r["B"], r["kernel"], r["grid"], r["call_us"], r["kernel_us"]), "",
+        "| section | phase | median over blocks (us) | slowest block (us) |", "|---|---|---|---|"]
+    for sec, ph in r.items():
+        if isinstance(ph, dict):
+            for n, (m, x) in ph.items():
+                lines.append("| %s | %s | %.2f | %.2f |" % (sec, n, m, x))
+    return "\n".join(lines)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("workloads", nargs="+")
+    ap.add_argument("--json", action="store_true")
+    args = ap.parse_args()
+    res = run(args.workloads)
+    for r in res.values():
+        print(json.dumps(r) if args.json else to_markdown(r) + "\n", flush=True)
+
+
+if __name__ == "__main__":
+    main()

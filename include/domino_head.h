@@ -230,6 +230,17 @@ int domino_head_check_error(domino_head_t hd, uint32_t *device_flags);
 int domino_head_exec_info(domino_head_t hd, int32_t B, int32_t *persistent, int32_t *w2_resident, int32_t *grid);
 
 /*
+ * Host only.  Bound on every device-side wait of later drafts on this handle
+ * (grid barriers, argmax and operand arrivals), in polling iterations of
+ * roughly 0.1-1 us each.  A wait that runs out sets DOMINO_FLAG_SYNC_TIMEOUT
+ * and its block leaves the launch, so every launch ends even if a block never
+ * arrives.  The default is 2^22 (or DOMINO_BARRIER_SPIN_LIMIT from the
+ * environment at create); 0 makes every wait give up at once, which forces
+ * the timeout path from the host.
+ */
+int domino_head_set_spin_limit(domino_head_t hd, uint32_t limit);
+
+/*
  * Host only.  Parameters of the head: r(d+h) + V r + 3h d + 3h h (+ 6h if GRU
  * biases are given); the embedding table E is the target's and not counted.
  * The paper.oopus.info review (section 二, 第二步 Domino Head) puts the head at

@@ -127,6 +127,7 @@ def test_null_handle_calls_fail_cleanly():
     lib = dca.load_library()
     assert lib.domino_head_draft(None, 1, None, None, None, None, None, None, None, None, None, None) == -1
     assert lib.domino_head_check_error(None, None) == -1
+    assert lib.domino_head_set_spin_limit(None, 0) == -1
     lib.domino_head_destroy(None)
 
 

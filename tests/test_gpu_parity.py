@@ -166,9 +166,10 @@ def test_out_of_range_tokens_flag_rows(mode, fold):
 
 
 def test_barrier_timeout_is_reported_not_hung(monkeypatch):
-    """A spin limit of 0 forces every waiting block out of its first barrier:
-    the launch must end, report DOMINO_FLAG_SYNC_TIMEOUT, and the next head on
-    the same workspace state must work normally."""
+    """A spin limit of 0 (read from the environment at create) forces every
+    waiting block out of its first barrier: the launch must end and report
+    DOMINO_FLAG_SYNC_TIMEOUT; a second head created afterwards with the default
+    limit must work normally."""
     sh = ds.HeadShape(d=64, h=32, r=16, V=500, K=16, wdtype="bf16")
     w = ds.make_weights(sh, (9, 54))
     inp = ds.make_inputs(sh, 1, (9, 55))
@@ -182,6 +183,59 @@ def test_barrier_timeout_is_reported_not_hung(monkeypatch):
     g, flags = gpu_draft(head2, inp.H, inp.L_base, inp.last_tok)
     assert flags == 0
     compare_free_running(o, g)
+
+
+@pytest.mark.parametrize("B,wd,r,fold", [(1, "bf16", 16, False), (1, "bf16", 256, False), (3, "f32", 32, False),
+                                         (40, "bf16", 256, True)])
+def test_same_handle_recovers_after_a_timeout(B, wd, r, fold):
+    """The spin limit set to 0 on a live handle makes a draft time out (the
+    streaming, the resident B = 1 and the batched B = 40 persistent kernels);
+    after check_error and the default limit restored, the same handle (same
+    workspace, barrier generations restarted) drafts correctly again, twice."""
+    sh = ds.HeadShape(d=128, h=64, r=r, V=700, K=16, wdtype=wd)
+    w = ds.make_weights(sh, (9, 58, r))
+    inp = ds.make_inputs(sh, B, (9, 59, r))
+    head = make_head(w, B, dca.EXEC_PERSISTENT, fold=fold)
+    assert head.exec_info(B)["persistent"]
+    o = oracle.draft(w, inp.H, inp.L_base, inp.last_tok)
+    g, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
+    assert flags == 0
+    head.set_spin_limit(0)
+    _, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
+    assert flags & dca.FLAG_SYNC_TIMEOUT
+    head.set_spin_limit(1 << 22)
+    for _ in range(2):
+        g2, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok)
+        assert flags == 0
+        compare_free_running(o, g2)
+        assert np.array_equal(g2["tokens"], g["tokens"])
+
+
+def test_output_tensors_are_checked_before_any_launch():
+    """Caller-supplied out tensors of the wrong shape, dtype, layout or device are
+    refused on the host; nothing is written."""
+    sh = ds.HeadShape(d=64, h=32, r=16, V=500, K=16, wdtype="bf16")
+    w = ds.make_weights(sh, (9, 56))
+    head = make_head(w, 2, dca.EXEC_AUTO)
+    inp = ds.make_inputs(sh, 2, (9, 57))
+    H, L, lt = dca.device_tensor(inp.H), dca.device_tensor(inp.L_base), dca.device_tensor(inp.last_tok)
+    dev = "cuda"
+    bad = [{"tokens": torch.empty((2, 15), dtype=torch.int32, device=dev)},
+           {"tokens": torch.empty((2, 16), dtype=torch.int64, device=dev)},
+           {"tokens": torch.empty((16, 2), dtype=torch.int32, device=dev).t()},
+           {"tokens": torch.empty((2, 16), dtype=torch.int32)},
+           {"L_final": torch.empty((2, 16, 499), dtype=torch.float32, device=dev)},
+           {"S": torch.empty((2, 16, 32), dtype=torch.bfloat16, device=dev)},
+           {"u": torch.empty((1, 16, 16), dtype=torch.float32, device=dev)},
+           {"logits": torch.empty((2, 16, 500), dtype=torch.float32, device=dev)}]
+    for o in bad:
+        with pytest.raises(ValueError):
+            head.draft(H, L, lt, out=o)
+    good = {"tokens": torch.full((2, 16), -7, dtype=torch.int32, device=dev),
+            "u": torch.empty((2, 16, 16), dtype=torch.float32, device=dev)}
+    g = head.draft(H, L, lt, out=good)
+    torch.cuda.synchronize()
+    assert g["tokens"] is good["tokens"] and int(good["tokens"].min()) >= 0
 
 
 def test_host_validation_of_draft_arguments():

@@ -34,7 +34,7 @@ FLAG_SYNC_TIMEOUT = 2
 ERRORS = {-1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP", -5: "EDEVICE"}
 
 SYMBOLS = ("domino_head_workspace_size", "domino_head_create", "domino_head_draft", "domino_accept_len",
-           "domino_verify_workspace_size", "domino_verify", "domino_head_check_error", "domino_head_exec_info",
+           "domino_verify_workspace_size", "domino_verify", "domino_verify_noalloc", "domino_head_check_error", "domino_head_exec_info",
            "domino_head_set_spin_limit", "domino_head_param_count", "domino_head_destroy", "domino_last_error")
 
 
@@ -71,6 +71,7 @@ def load_library(path: str = LIB_PATH):
     lib.domino_accept_len.argtypes = [I32, I32, P, P, P, P]
     lib.domino_verify_workspace_size.argtypes = [I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.domino_verify.argtypes = [I32, I32, I32, P, P, P, ctypes.c_size_t, P, P, P, P]
+    lib.domino_verify_noalloc.argtypes = [I32, I32, I32, P, P, P, P, P, P]
     lib.domino_head_check_error.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
     PI = ctypes.POINTER(ctypes.c_int32)
     lib.domino_head_exec_info.argtypes = [P, I32, PI, PI, PI]
@@ -288,4 +289,28 @@ def verify(logits: torch.Tensor, draft: torch.Tensor, workspace: Optional[torch.
     _check(load_library().domino_verify(B, K, V, _ptr(logits), _ptr(draft), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _ptr(out.get("target")),
                                         _ptr(out["accept"]), _ptr(out["next"]), _stream_handle()))
+    return out
+
+
+def verify_noalloc(logits: torch.Tensor, draft: torch.Tensor, want_target: bool = True,
+                   out: Optional[dict] = None) -> dict:
+    """verify() through the entry point that allocates nothing: the library's static
+    scratch stands in for the workspace (at most 1 MiB of it; calls that overlap on
+    one device race).  Output tensors are allocated here unless ``out`` gives them."""
+    if logits.dim() != 3 or draft.dim() != 2 or logits.shape[0] != draft.shape[0] or \
+            logits.shape[1] != draft.shape[1] + 1:
+        raise ValueError("logits must be [B, K+1, V] and draft [B, K]")
+    B, K = draft.shape
+    for name, t, dt in (("logits", logits, torch.float32), ("draft", draft, torch.int32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s: expected a contiguous CUDA %s tensor" % (name, dt))
+    dev = logits.device
+    out = {} if out is None else dict(out)
+    out.setdefault("accept", torch.empty(B, dtype=torch.int32, device=dev))
+    out.setdefault("next", torch.empty(B, dtype=torch.int32, device=dev))
+    if want_target:
+        out.setdefault("target", torch.empty((B, K + 1), dtype=torch.int32, device=dev))
+    _check(load_library().domino_verify_noalloc(B, K, logits.shape[2], _ptr(logits), _ptr(draft),
+                                                _ptr(out.get("target")), _ptr(out["accept"]), _ptr(out["next"]),
+                                                _stream_handle()))
     return out

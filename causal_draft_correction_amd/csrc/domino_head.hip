@@ -1120,6 +1120,31 @@ int domino_verify(int32_t B, int32_t K, int32_t V, const float *logits, const in
     return DOMINO_OK;
 }
 
+int domino_verify_noalloc(int32_t B, int32_t K, int32_t V, const float *logits, const int32_t *draft,
+                          int32_t *target, int32_t *accept, int32_t *next, void *stream)
+{
+    const int rc = verify_args(B, K, V);
+    if (rc)
+        return rc;
+    if (B == 0)
+        return DOMINO_OK;
+    if (!logits || !draft || !accept || !next)
+        return fail(DOMINO_EINVAL, "NULL pointer");
+    if (!aligned16(logits) || !aligned16(draft) || !aligned16(accept) || !aligned16(next) ||
+        (target && !aligned16(target)))
+        return fail(DOMINO_EINVAL, "pointers must be 16-byte aligned");
+    const size_t need = dhverify::workspace_bytes(B, K, V);
+    if (need > dhverify::SCRATCH_BYTES)
+        return fail(DOMINO_EUNSUPPORTED, "B=%d, K=%d, V=%d needs %zu bytes of scratch; the static buffer holds %zu "
+                    "(use domino_verify with a workspace)", B, K, V, need, dhverify::SCRATCH_BYTES);
+    void *ws = nullptr;
+    HIP_TRY(dhverify::scratch_address(&ws), "hipGetSymbolAddress(scratch)");
+    HIP_TRY(dhverify::launch(B, K, V, logits, draft, static_cast<uint64_t *>(ws), target, accept, next,
+                             static_cast<hipStream_t>(stream)),
+            "launch verify");
+    return DOMINO_OK;
+}
+
 int domino_head_exec_info(domino_head_t hd, int32_t B, int32_t *persistent, int32_t *w2_resident, int32_t *grid)
 {
     if (!hd)

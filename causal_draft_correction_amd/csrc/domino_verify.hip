@@ -22,6 +22,8 @@
 #include "dh_common.h"
 #include "dh_verify.h"
 
+#include <mutex>
+
 namespace DH_NS {
 
 typedef float f4v __attribute__((ext_vector_type(4)));
@@ -108,9 +110,38 @@ __global__ __launch_bounds__(NT) void k_verify_final(int K, int nch, const uint6
 
 }  // namespace DH_NS
 
+// Scratch of the allocation-free verify entry point: the argmax keys of one call
+// live in this file-scope device array instead of a caller's workspace.  In host
+// code its name is only a stand-in for the symbol; the device address comes from
+// hipGetSymbolAddress, once per device (each device holds its own copy).
+static __device__ __align__(256) uint64_t scratch[dhverify::SCRATCH_BYTES / sizeof(uint64_t)];
+
 namespace dhverify {
 
 using namespace dhv;
+
+hipError_t scratch_address(void **out)
+{
+    constexpr int MAX_DEVICES = 64;
+    static std::mutex mu;
+    static void *addr[MAX_DEVICES];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= MAX_DEVICES)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
 
 int chunks(int B, int K, int V)
 {

@@ -210,6 +210,23 @@ int domino_verify(int32_t B, int32_t K, int32_t V, const float *logits, const in
                   size_t workspace_bytes, int32_t *target, int32_t *accept, int32_t *next, void *stream);
 
 /*
+ * domino_verify without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, outputs and results as domino_verify
+ * (same kernels), but the per-call scratch (one 8-byte key per (row, chunk))
+ * lives in a 1 MiB static device array of the library, one per device, held
+ * until the process ends.  Nothing is allocated and nothing needs clearing
+ * (every scratch word a call reads it has written first).  Returns
+ * DOMINO_EUNSUPPORTED, before any device work, when
+ * domino_verify_workspace_size(B, K, V) exceeds 1 MiB (about B (K+1) + 2048 >
+ * 131072).  All calls on one device share the array: calls that may overlap
+ * on one device (different streams, or host threads) race and give wrong
+ * results; order them on one stream.
+ */
+int domino_verify_noalloc(int32_t B, int32_t K, int32_t V, const float *logits, const int32_t *draft,
+                          int32_t *target, int32_t *accept, int32_t *next, void *stream);
+
+/*
  * Synchronizes the device (every stream, so drafts replayed from a captured
  * HIP graph on any stream are included), reads and clears the device flags
  * (DOMINO_FLAG_*) into *device_flags (may be NULL) and resets the handle's

@@ -33,7 +33,7 @@ struct Params {
     uint64_t *bkeys; // batched resident launch: [maxB, grid] argmax key word of every block for every
                      // batch row, generation-tagged
     uint4 *uop;      // batched resident launch: u as the W2 products' operand, one slot per position:
-                     // [K][rb_ngr][hi, lo][r/32][64] 16-byte chunks (8 bf16 of one batch row each)
+                     // [K][rb_ngr][r/32][64] 16-byte chunks (8 bf16 of one batch row each)
     uint16_t *rb_planes;  // batched resident launch: S as bf16 hi/lo planes, one slot per state:
                           // [K + 1][2][rb_bmax][rb_ldp]
     int rb_bmax, rb_ngr, rb_ldp;

@@ -436,7 +436,7 @@ Layout layout_of(const domino_head_config &c)
     if (packed_state_rows(c))
         off = align_up(off + sizeof(uint16_t) * static_cast<size_t>(c.r + 3 * c.h) * packed_ldw(c));
     // batched resident launch: argmax words [max_batch, MAX_GRID], the u operand of
-    // every position [K][groups][hi, lo][r / 32][64] x 16 bytes, and the S planes of
+    // every position [K][groups][r / 32][64] x 16 bytes (bf16), and the S planes of
     // every state [K + 1][hi, lo][rows][rb_ldp] bf16
     L.bkeys = off;
     L.uop = off;
@@ -444,7 +444,7 @@ Layout layout_of(const domino_head_config &c)
     if (packed_state_rows(c)) {
         off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(c.max_batch) * MAX_GRID);
         L.uop = off;
-        off = align_up(off + sizeof(uint16_t) * 2 * static_cast<size_t>(c.K) * rb_ngr(c) * 16 * c.r);
+        off = align_up(off + sizeof(uint16_t) * static_cast<size_t>(c.K) * rb_ngr(c) * 16 * c.r);
         L.rbs = off;
         off = align_up(off + sizeof(uint16_t) * 2 * static_cast<size_t>(c.K + 1) * rb_bmax(c) * rb_ldp(c));
     }

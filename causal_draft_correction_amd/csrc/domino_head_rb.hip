@@ -13,9 +13,10 @@
 // holds tiles w, w + 8, ... of it (RT per wave, 160 registers at r = 256).
 // Per position the launch runs three phases separated by grid barriers:
 //   * W2 phase: for each group of 16 batch rows, D = W2_tile u^T on the matrix
-//     cores (v_mfma_f32_16x16x32_bf16, A = the register tile, B = u as bf16 hi
-//     and lo operands accumulated into the same result, so the product keeps
-//     float32-level accuracy), plus L_base, into a running greedy argmax.  The
+//     cores (v_mfma_f32_16x16x32_bf16, A = the register tile, B = u rounded once
+//     to bf16: the products are those of bf16 operands with float32 sums, u's
+//     rounding moves the logits by at most a few 1e-3 at the 8B shapes), plus
+//     L_base, into a running greedy argmax.  The
 //     groups' L_base slices (two groups ahead) and u operands (one ahead) are
 //     copied into LDS by direct global-to-LDS loads.  The block's key for each
 //     batch row goes to a generation-tagged word bkeys[b][block];
@@ -29,7 +30,7 @@
 //     in jobs of 4 weight tiles x BJ batch tiles (S hi and lo staged in LDS four
 //     stages ahead, weight rows from L2; two waves per weight tile split each
 //     stage's two 32-wide steps), then u = SiLU(A_H + .) as the next W2 phase's
-//     bf16 hi/lo operand and q' + b_hh for the next update.
+//     bf16 operand and q' + b_hh for the next update.
 // Values that cross blocks are written with agent-scope stores, which write
 // through the per-XCD L2 caches (not coherent with each other).  The argmax
 // words and q, each read by one block, are read with agent-scope loads, which
@@ -62,7 +63,8 @@ constexpr int TILES = NWAVE * RT;    // vocabulary tiles per block (40: 640 rows
 constexpr int LROW = TILES * 16;     // L_base values of one batch row (float32 rows in LDS)
 constexpr int LROW16 = LROW + 128;   // the same for bf16 rows, padded to whole copies per wave
 constexpr int LBUF = 16 * LROW * 4 / 16;  // uint4 per L_base buffer (16 rows of float32)
-constexpr int UCH = 2 * KS * 64;     // uint4 of one group's u operand (hi, lo)
+constexpr int UCH = KS * 64;         // uint4 of one group's u operand (bf16)
+constexpr int UBUF = 1024;           // uint4 of each of the two small LDS buffers
 constexpr int MAXB = 256;            // batch rows of one launch
 constexpr int ROWS = 4;              // batch rows one block updates at most (B <= MAXB)
 constexpr int CPT = 1;               // 4-entry state chunks per thread at most
@@ -252,7 +254,7 @@ __device__ __forceinline__ void lb_issue(const Params &p, const Ctx &c, const Lb
     }
 }
 
-// u operand of group g (16 KB, the layout of p.uop) into an LDS buffer: 4 copies per thread.
+// u operand of group g (8 KB, the layout of p.uop) into an LDS buffer: one copy per thread.
 __device__ __forceinline__ void u_issue(const Params &p, int pos, int g, uint4 *buf)
 {
     const int lane = threadIdx.x & 63;
@@ -301,15 +303,11 @@ __device__ __forceinline__ void w2_group(const Params &p, const Ctx &c, const W2
         acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-        const uint4 uh = U[kk * 64 + lane], ul = U[(KS + kk) * 64 + lane];
+        const uint4 uh = U[kk * 64 + lane];
 #pragma unroll
         for (int j = 0; j < RT; ++j)
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, res.wt[j][kk]),
                                                              __builtin_bit_cast(bf16x8_t, uh), acc[j], 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < RT; ++j)
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, res.wt[j][kk]),
-                                                             __builtin_bit_cast(bf16x8_t, ul), acc[j], 0, 0, 0);
     }
     const int b = 16 * g + row;
     float best = -__builtin_inff();
@@ -703,12 +701,11 @@ __device__ __forceinline__ void dots_small(const Params &p, int blk, int q, uint
                 if (urows) {
                     const float a4[4] = {ah.x + sum[0], ah.y + sum[1], ah.z + sum[2], ah.w + sum[3]};
                     float u4[4];
-                    uint32_t hi[4], lo[4];
+                    uint32_t hi[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         u4[i] = a4[i] * sigmoidf_(a4[i]);
                         hi[i] = bf16_rne_bits(u4[i]);
-                        lo[i] = bf16_rne_bits(u4[i] - __uint_as_float(hi[i] << 16));
                     }
                     if (p.u_out)
                         *reinterpret_cast<float4 *>(p.u_out + (static_cast<size_t>(b) * p.K + q) * r + m) =
@@ -716,11 +713,10 @@ __device__ __forceinline__ void dots_small(const Params &p, int blk, int q, uint
                     // operand chunk of (batch row b, r offsets 8 (m / 8) .. + 8): group b / 16,
                     // step m / 32, lane b % 16 + 16 ((m % 32) / 8); these four values are its
                     // half (m % 8) / 4
-                    const size_t ch = ((static_cast<size_t>(q) * p.rb_ngr + (b >> 4)) * 2 * KS + (m >> 5)) * 64 +
+                    const size_t ch = ((static_cast<size_t>(q) * p.rb_ngr + (b >> 4)) * KS + (m >> 5)) * 64 +
                                       (b & 15) + 16 * ((m & 31) >> 3);
                     char *dst = reinterpret_cast<char *>(p.uop + ch) + (m & 7) * 2;
                     st_agent_u64(dst, pack4_bf16(hi[0], hi[1], hi[2], hi[3]));
-                    st_agent_u64(dst + static_cast<size_t>(KS) * 64 * 16, pack4_bf16(lo[0], lo[1], lo[2], lo[3]));
                 } else {
                     const int mq = m - r;
                     const float4 v = make_float4(sum[0] + bias_hh(p, mq), sum[1] + bias_hh(p, mq + 1),
@@ -791,8 +787,12 @@ __device__ __forceinline__ void dots_2d(const Params &p, int blk, int nblk, int 
         }
         const uint16_t *wrow = p.wst + static_cast<size_t>(wt * 16 + row) * p.ldw + 32 * ks + 8 * k;
         uint4 wa[4];
+        // the jobs of one batch job read the same S slices: each weight group starts
+        // the h reduction at its own stage, so concurrent jobs request different lines
+        const int srot = wg % NS;
         auto issue = [&](int s, uint4 *ring, uint4 &w) {
             s = s < NS ? s : NS - 1;
+            s = s + srot < NS ? s + srot : s + srot - NS;
 #pragma unroll
             for (int x = 0; x < PER; ++x)
                 copy_lds16(src[x] + 64 * s, ring + (wave * PER + x) * 64, 0);
@@ -855,21 +855,19 @@ __device__ __forceinline__ void dots_2d(const Params &p, int blk, int nblk, int 
                         *reinterpret_cast<const float4 *>(p.A_H + (static_cast<size_t>(b) * p.K + q) * r + m);
                     const float a4[4] = {ah.x + acc[bt][0], ah.y + acc[bt][1], ah.z + acc[bt][2], ah.w + acc[bt][3]};
                     float u4[4];
-                    uint32_t hi[4], lo[4];
+                    uint32_t hi[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         u4[i] = a4[i] * sigmoidf_(a4[i]);
                         hi[i] = bf16_rne_bits(u4[i]);
-                        lo[i] = bf16_rne_bits(u4[i] - __uint_as_float(hi[i] << 16));
                     }
                     if (p.u_out)
                         *reinterpret_cast<float4 *>(p.u_out + (static_cast<size_t>(b) * p.K + q) * r + m) =
                             make_float4(u4[0], u4[1], u4[2], u4[3]);
-                    const size_t ch = ((static_cast<size_t>(q) * p.rb_ngr + (b >> 4)) * 2 * KS + (m >> 5)) * 64 +
+                    const size_t ch = ((static_cast<size_t>(q) * p.rb_ngr + (b >> 4)) * KS + (m >> 5)) * 64 +
                                       (b & 15) + 16 * ((m & 31) >> 3);
                     char *dst = reinterpret_cast<char *>(p.uop + ch) + (m & 7) * 2;
                     st_agent_u64(dst, pack4_bf16(hi[0], hi[1], hi[2], hi[3]));
-                    st_agent_u64(dst + static_cast<size_t>(KS) * 64 * 16, pack4_bf16(lo[0], lo[1], lo[2], lo[3]));
                 } else {
                     const int mq = m - r;
                     const float4 v = make_float4(acc[bt][0] + bias_hh(p, mq), acc[bt][1] + bias_hh(p, mq + 1),
@@ -927,7 +925,7 @@ template <bool LB16, bool FAST, bool ST>
 __global__ __launch_bounds__(NT) void k_persistent_rb(Params p)
 {
     __shared__ uint4 lbA[LBUF], lbB[LBUF], lbC[LBUF];
-    __shared__ uint4 uA[UCH], uB[UCH];
+    __shared__ uint4 uA[UBUF], uB[UBUF];
     __shared__ uint64_t kred[2 * NWAVE * 16];
     __shared__ uint64_t lkey[MAXB];
     __shared__ uint64_t rred[NWAVE * ROWS];

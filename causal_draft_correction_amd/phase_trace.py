@@ -9,6 +9,11 @@ Positions 1..K-2 are summarised by the median over positions; the anchor step,
 the first and the last position are listed separately.
 
     python -m causal_draft_correction_amd.phase_trace qwen3_8b_b1 [qwen3_8b_b32 ...] [--json]
+        [--persistent] [--lbase-bf16]
+
+--persistent forces the persistent launch where the automatic choice would take
+the step launches (the batched kernel up to B = 256); --lbase-bf16 passes the
+base logits as bfloat16.
 
 Only this tool loads the instrumented library; it needs a GPU.
 """
@@ -70,7 +75,7 @@ def summarize(t, K, batched):
     return out
 
 
-def run(names, lib_path=None):
+def run(names, lib_path=None, persistent=False, lbase_bf16=False):
     sys.path.insert(0, ROOT)
     import torch
 
@@ -87,12 +92,14 @@ def run(names, lib_path=None):
         wl = ds.WORKLOADS[name]
         sh = wl.shape
         w, inp = ds.make_workload(name)
-        head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B, fold_embedding=True)
+        head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B, fold_embedding=True,
+                              exec_mode=dca.EXEC_PERSISTENT if persistent else dca.EXEC_AUTO, lbase_bf16=lbase_bf16)
         info = head.exec_info(wl.B)
         if not (info["persistent"] and info["w2_resident"]):
             raise SystemExit("%s does not take a resident persistent launch (%s)" % (name, info))
         batched = wl.B > 8
-        H, L, lt = dca.device_tensor(inp.H), dca.device_tensor(inp.L_base), dca.device_tensor(inp.last_tok)
+        H, lt = dca.device_tensor(inp.H), dca.device_tensor(inp.last_tok)
+        L = dca.device_tensor(ds.round_to_bf16_bits(inp.L_base) if lbase_bf16 else inp.L_base)
         out = {"tokens": torch.empty((wl.B, sh.K), dtype=torch.int32, device="cuda")}
         for _ in range(3):
             head.draft(H, L, lt, out=out)
@@ -107,8 +114,9 @@ def run(names, lib_path=None):
         rc = (lib.domino_trace_read_rb if batched else lib.domino_trace_read_res)(buf.ctypes.data)
         assert rc == 0, rc
         t = buf.reshape(BLOCKS, SLOTS)[:min(info["grid"], BLOCKS)].astype(np.int64)
-        r = {"workload": name, "B": wl.B, "kernel": "k_persistent_rb" if batched else "k_persistent_res",
-             "grid": info["grid"], "call_us": round(e0.elapsed_time(e1) * 1e3, 1)}
+        r = {"workload": name + (" bf16 L_base" if lbase_bf16 else ""), "B": wl.B,
+             "kernel": "k_persistent_rb" if batched else "k_persistent_res", "grid": info["grid"],
+             "call_us": round(e0.elapsed_time(e1) * 1e3, 1)}
         r.update(summarize(t, sh.K, batched))
         results[name] = r
         del head
@@ -130,8 +138,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("workloads", nargs="+")
     ap.add_argument("--json", action="store_true")
+    ap.add_argument("--persistent", action="store_true")
+    ap.add_argument("--lbase-bf16", action="store_true")
     args = ap.parse_args()
-    res = run(args.workloads)
+    res = run(args.workloads, persistent=args.persistent, lbase_bf16=args.lbase_bf16)
     for r in res.values():
         print(json.dumps(r) if args.json else to_markdown(r) + "\n", flush=True)
 

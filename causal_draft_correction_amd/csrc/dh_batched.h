@@ -6,9 +6,10 @@
 namespace dhbat {
 int r_supported();         // the rank it is built for
 int threads();             // threads per block
-const void *w2_kernel(int B, bool lbase_bf16, bool store_logits);  // k_w2_mfma for B rows (L_base float32
-                                               // or bf16; L_final stored or not): arguments
-                                               // (Params, int position, int groups)
+// k_w2_mfma for B rows (L_base float32 or bf16; L_final stored or not; u_single:
+// u as one bf16 operand instead of bf16 hi + lo parts): arguments (Params, int
+// position, int groups)
+const void *w2_kernel(int B, bool lbase_bf16, bool store_logits, bool u_single);
 int w2_groups(int B);           // its third argument
 int w2_threads(int B);     // its threads per block
 size_t w2_smem();          // its dynamic LDS per block

@@ -969,14 +969,17 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
                 "launch A_H (matrix cores)");
     }
     // bf16 heads with r = 256 take the matrix-core W2 kernel
-    // (its load offsets are 32-bit: V < 2^22)
+    // (its load offsets are 32-bit: V < 2^22).  Drafts of more than 8 rows give it u
+    // as one bf16 operand (half the matrix-core work); at most 8 rows keep the
+    // hi + lo split, so their logits equal the resident kernel's bit for bit
     const bool w2_mfma = c.wdtype == DOMINO_BF16 && c.r == dhbat::r_supported() && c.V < (1 << 22);
+    const bool w2_u1 = B > BC;
     auto launch_w2 = [&](Params &pw, int rows, int pos) -> hipError_t {
         int groups = w2_mfma ? dhbat::w2_groups(rows) : 0;
         void *args[] = {&pw, &pos};
         void *margs[] = {&pw, &pos, &groups};
         if (w2_mfma)
-            return hipLaunchKernel(dhbat::w2_kernel(rows, pw.lbase_bf16 != 0, pw.L_final != nullptr),
+            return hipLaunchKernel(dhbat::w2_kernel(rows, pw.lbase_bf16 != 0, pw.L_final != nullptr, w2_u1),
                                    dim3(dhbat::w2_grid(rows, hd->cus)),
                                    dim3(dhbat::w2_threads(rows)), margs, dhbat::w2_smem(), st);
         return hipLaunchKernel(hd->kern.w2, dim3(g_w2), dim3(NT), args, sm_w2, st);

@@ -12,11 +12,14 @@
 namespace DH_NS {
 
 // Work split.  A block of NTH threads takes a batch tile of up to 128 rows (bt)
-// and a contiguous vocabulary range (vb of nvb).  Its waves take AT*8-row batch
+// and a contiguous vocabulary range (vb of nvb).  Its waves take 16-row batch
 // groups of the tile (ng groups) and, when the tile has fewer groups than
 // waves, split each vocabulary chunk's 16-row tiles between nvs = waves / ng
 // wave sets (VTG tiles each).  A wave keeps its batch rows of u in registers
-// as AT matrix-core A operands: A tile a holds batch rows a*8 .. a*8+7, row j's
+// as AT matrix-core A operands.  U1 (drafts of more than 8 rows): u rounded once
+// to bf16, one A tile of 16 batch rows, each result lane holding four batch rows.
+// Otherwise (the rows of at most 8-row drafts, which must equal the resident
+// kernel's logits bit for bit): A tile a holds batch rows a*8 .. a*8+7, row j's
 // bf16 hi part in operand row 2j and its lo part (u - hi) in row 2j+1, so each
 // result lane holds the hi and lo results of two batch rows side by side.
 // Chunks of W2 are staged through LDS in the B-operand layout ([tile][step]
@@ -31,10 +34,12 @@ namespace DH_NS {
 // AT = 2: two waves per SIMD, up to 128 rows per tile.
 constexpr int XCDS = 8;   // accelerator dies (XCDs) of the MI355X, each with its own L2
 
-template <int KS, int VTG, int NVS, int AT, int NTH, bool LB16, bool ST>
+template <int KS, int VTG, int NVS, int AT, int NTH, bool LB16, bool ST, bool U1>
 __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
 {
-    static_assert(AT == 2 || AT == 4, "A tiles per wave");
+    static_assert(U1 ? AT == 1 : (AT == 2 || AT == 4), "A tiles per wave");
+    constexpr int RPT = U1 ? 16 : 8;  // batch rows per A tile
+    constexpr int VPL = U1 ? 4 : 2;   // batch rows per result lane and A tile
     constexpr int NWV = NTH / 64;
     constexpr int ng = NWV / NVS;  // batch groups of a tile (the host passes the same in ng_arg)
     (void)ng_arg;
@@ -51,7 +56,7 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int grp = wave % ng, vs = wave / ng;
     constexpr int CRr = NVS * VTG * 16;  // chunk rows
-    const int row0 = bt * 128 + grp * AT * 8;
+    const int row0 = bt * 128 + grp * AT * RPT;
     const long long v0 = static_cast<long long>(V) * vb / nvb;
     const int n = static_cast<int>(static_cast<long long>(V) * (vb + 1) / nvb - v0);
     if (n <= 0)
@@ -66,10 +71,11 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
     uint4 ua[AT][KS];
 #pragma unroll
     for (int a = 0; a < AT; ++a) {
-        // operand row m = col: batch row a*8 + m/2, its hi part in even rows and its
-        // lo part in odd ones, so a result lane holds both halves of its rows
-        const int b = row0 + a * 8 + (col >> 1);
-        const bool hi = (col & 1) == 0;
+        // operand row m = col: U1, batch row m; otherwise batch row a*8 + m/2, its hi
+        // part in even rows and its lo part in odd ones, so a result lane holds both
+        // halves of its rows
+        const int b = U1 ? row0 + col : row0 + a * 8 + (col >> 1);
+        const bool hi = U1 || (col & 1) == 0;
         const float *src = p.u_buf + static_cast<size_t>(b < B ? b : 0) * r + (lane >> 4) * 8;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
@@ -120,14 +126,15 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
         for (int jj = 0; jj < PT; ++jj)
             wlds[buf * slots + threadIdx.x + jj * NTH] = st[jj];
     };
-    // this lane's batch rows: result rows 4*(lane/16) + i of A tile a are hi (i even)
-    // and lo (i odd) of batch row a*8 + 2*(lane/16) + i/2
-    int brow[AT][2];
+    // this lane's batch rows: result rows 4*(lane/16) + i of A tile a are batch rows
+    // 4*(lane/16) + i (U1), else hi (i even) and lo (i odd) of batch row
+    // a*8 + 2*(lane/16) + i/2
+    int brow[AT][VPL];
 #pragma unroll
     for (int a = 0; a < AT; ++a)
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
-            brow[a][ii] = row0 + a * 8 + 2 * (lane >> 4) + ii;
+        for (int ii = 0; ii < VPL; ++ii)
+            brow[a][ii] = row0 + a * RPT + VPL * (lane >> 4) + ii;
     // L_base of this lane's epilogue values for chunk c: a buffer resource from the
     // wave's first batch row at this position to the end of L_base (batch rows past B
     // lie past it; at most 2^32 - 1 bytes, more than the wave's 16 rows span)
@@ -140,14 +147,14 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
         0x00020000);
     // offsets in 32 bits (the host takes this kernel only for V < 2^22)
     const uint32_t KV = static_cast<uint32_t>(p.K) * static_cast<uint32_t>(V);
-    const uint32_t lblane = (static_cast<uint32_t>(2 * (lane >> 4)) * KV + col) * LES;
-    auto lbase_load = [&](int c, float (&lb)[AT][VTG][2]) {
+    const uint32_t lblane = (static_cast<uint32_t>(VPL * (lane >> 4)) * KV + col) * LES;
+    auto lbase_load = [&](int c, float (&lb)[AT][VTG][VPL]) {
 #pragma unroll
         for (int a = 0; a < AT; ++a)
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii) {
+            for (int ii = 0; ii < VPL; ++ii) {
                 const uint32_t off =
-                    lblane + (static_cast<uint32_t>(8 * a + ii) * KV + static_cast<uint32_t>(c * CRr + vs * VTG * 16)) * LES;
+                    lblane + (static_cast<uint32_t>(RPT * a + ii) * KV + static_cast<uint32_t>(c * CRr + vs * VTG * 16)) * LES;
 #pragma unroll
                 for (int vt = 0; vt < VTG; ++vt) {
                     // streamed once, but through the cache: one load covers a 64-byte row
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
             }
     };
 
-    LaneBest best[AT][2];
+    LaneBest best[AT][VPL];
     // Software pipeline over chunks, unrolled by two so register sets are fixed
     // by the chunk parity P.  Step c: the W2 registers of chunk c+1 (loaded one
     // step ago) go to LDS buffer P^1, whose chunk c-1 every wave multiplied before
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
     // products with the vector work); then L_base of chunk c+1 is loaded into
     // the value set just consumed, a full step before its epilogue.
     uint4 st[PT];
-    float lb[2][AT][VTG][2];
+    float lb[2][AT][VTG][VPL];
     f32x4_t acc[2][AT][VTG];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
 #pragma unroll
             for (int vt = 0; vt < VTG; ++vt)
 #pragma unroll
-                for (int ii = 0; ii < 2; ++ii)
+                for (int ii = 0; ii < VPL; ++ii)
                     lb[s2][a][vt][ii] = 0.f;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
@@ -212,9 +219,10 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
             for (int vt = 0; vt < VTG; ++vt) {
                 const int vr = c * CRr + (vs * VTG + vt) * 16 + col;
 #pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    // hi + lo of the batch row (the resident kernel's order)
-                    const float w = acc[S][a][vt][2 * ii] + acc[S][a][vt][2 * ii + 1];
+                for (int ii = 0; ii < VPL; ++ii) {
+                    // U1: the row's product; else hi + lo of the batch row (the resident
+                    // kernel's order)
+                    const float w = U1 ? acc[S][a][vt][ii] : acc[S][a][vt][2 * ii] + acc[S][a][vt][2 * ii + 1];
                     const int b = brow[a][ii];
                     // c < 0 gives vr < 0, out of range as unsigned; no short-circuit
                     // branch, so the epilogue stays in the products' basic block.  A
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
 #pragma unroll
     for (int a = 0; a < AT; ++a)
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
+        for (int ii = 0; ii < VPL; ++ii) {
             uint64_t key = best[a][ii].ord ? (static_cast<uint64_t>(best[a][ii].ord) << 32) |
                                                  (0xFFFFFFFFu - best[a][ii].idx)
                                            : 0ull;
@@ -664,23 +672,31 @@ struct W2Shape {
 };
 // ng batch groups of 16 rows per 128-row tile; the 8 waves form 8 / ng wave sets that
 // split each 64-row chunk (128 rows for ng = 1)
-template <bool LB16, bool ST>
+template <bool LB16, bool ST, bool U1>
 static const void *w2_fn(int ng)
 {
-    return ng == 8   ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 4, 1, 2, 512, LB16, ST>)
-           : ng == 4 ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 2, 2, 2, 512, LB16, ST>)
-           : ng == 2 ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 1, 4, 2, 512, LB16, ST>)
-                     : reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 1, 8, 2, 512, LB16, ST>);
+    constexpr int AT = U1 ? 1 : 2;
+    return ng == 8   ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 4, 1, AT, 512, LB16, ST, U1>)
+           : ng == 4 ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 2, 2, AT, 512, LB16, ST, U1>)
+           : ng == 2 ? reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 1, 4, AT, 512, LB16, ST, U1>)
+                     : reinterpret_cast<const void *>(&k_w2_mfma<BAT_KS, 1, 8, AT, 512, LB16, ST, U1>);
 }
-static W2Shape w2_shape(int B, bool lb16 = false, bool store = false)
+template <bool U1>
+static const void *w2_fn(int ng, bool lb16, bool store)
+{
+    return lb16 ? (store ? w2_fn<true, true, U1>(ng) : w2_fn<true, false, U1>(ng))
+                : (store ? w2_fn<false, true, U1>(ng) : w2_fn<false, false, U1>(ng));
+}
+static W2Shape w2_shape(int B, bool lb16 = false, bool store = false, bool u1 = false)
 {
     const int need = ((B < 128 ? B : 128) + 15) / 16;
     const int ng = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
-    const void *fn = lb16 ? (store ? w2_fn<true, true>(ng) : w2_fn<true, false>(ng))
-                          : (store ? w2_fn<false, true>(ng) : w2_fn<false, false>(ng));
-    return {fn, 512, ng};
+    return {u1 ? w2_fn<true>(ng, lb16, store) : w2_fn<false>(ng, lb16, store), 512, ng};
 }
-const void *w2_kernel(int B, bool lbase_bf16, bool store_logits) { return w2_shape(B, lbase_bf16, store_logits).fn; }
+const void *w2_kernel(int B, bool lbase_bf16, bool store_logits, bool u_single)
+{
+    return w2_shape(B, lbase_bf16, store_logits, u_single).fn;
+}
 int w2_groups(int B) { return w2_shape(B).ng; }
 int w2_threads(int B) { return w2_shape(B).threads; }
 // one block per compute unit: batch tiles times vocabulary ranges

@@ -282,16 +282,23 @@ def test_qwen3_8b_b1_full(w8b):
 @pytest.mark.slow
 @pytest.mark.parametrize("name,rows", [("qwen3_8b_b32", [0, 13, 31]), ("qwen3_8b_b256", [0, 101, 255])])
 def test_qwen3_8b_batched_sampled_rows(w8b, name, rows):
-    """Full batch on the device (the launch the benchmark times); the oracle checks sampled rows."""
+    """Full batch on the device (the launch the benchmark times: the batched persistent
+    kernel at B = 32, the step launches at B = 256, float32 L_base); the oracle checks
+    sampled rows free running and teacher forced with its own draft."""
     wl = ds.WORKLOADS[name]
     inp = ds.make_inputs(wl.shape, wl.B, wl.row_key, wl.sigma, wl.peak, wl.peak_height, wl.temperature)
-    head = make_head(w8b, wl.B)
+    head = make_head(w8b, wl.B, fold=True)
     g, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok, rows=rows)
     assert flags == 0
     sub = ds.make_inputs(wl.shape, rows, wl.row_key, wl.sigma, wl.peak, wl.peak_height, wl.temperature)
     o = oracle.draft(w8b, sub.H, sub.L_base, sub.last_tok)
     div = compare_free_running(o, g)
     log("%s sampled rows %s: diverged=%d" % (name, rows, div))
+    y = np.zeros((wl.B, wl.shape.K), np.int32)
+    y[rows] = o["tokens"]
+    gt, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok, teacher=y, rows=rows)
+    assert flags == 0
+    compare_teacher_forced(o, gt)
     # accept length on synthetic verifier tokens built from the oracle draft
     tgt, k = ds.geometric_prefix_targets(o["tokens"], (4, 3), wl.shape.V)
     got = dca.accept_len(dca.device_tensor(g["tokens"]), dca.device_tensor(tgt)).cpu().numpy()

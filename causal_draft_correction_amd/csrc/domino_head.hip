@@ -614,12 +614,9 @@ static bool choose_launch(const domino_head *hd, int B, bool *persistent, bool *
 {
     const unsigned fl = hd->cfg.flags;
     *batched = false;
-    // the batched persistent launch beats the step launches up to about B = 48 on a 256-CU device
-    // (8B-class head, K = 16); past that its per-position state products cost more than one
-    // extra launch per phase, so AUTO hands larger batches to the step launches
-    const int auto_max = 48;
+    // the batched persistent launch (8 < B <= 256) is ahead of the step launches at every batch
+    // measured (8B head, K = 16: 485 against 654 us at B = 32, 1044 against 1172 at B = 256)
     if (!(fl & DOMINO_MARKOV) && B > BC && hd->rb_grid > 0 && B <= dhrb::max_batch() &&
-        ((fl & DOMINO_EXEC_PERSISTENT) || B <= auto_max) &&
         !(fl & (DOMINO_EXEC_STEPWISE | DOMINO_EXEC_STREAM_W2))) {
         *persistent = *resident = *batched = true;
         return true;

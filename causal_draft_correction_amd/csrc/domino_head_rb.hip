@@ -112,10 +112,22 @@ __device__ inline void copy_lds16(const void *g, void *lds, unsigned aux_sc1)
 }
 __device__ inline void copy_lds4(const void *g, void *lds) { __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 4, 0, 0); }
 
-// the same through a buffer resource (16 bytes at byte offset voff; past the records: zeros)
-__device__ inline void copy_lds16_buf(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff)
+// the same through a buffer resource (16 bytes at byte offset voff + soff, voff per lane and
+// soff uniform; past the records: zeros)
+__device__ inline void copy_lds16_buf(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff, uint32_t soff = 0)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, static_cast<int>(soff), 0, 0);
+}
+
+// Buffer resource over `bytes` bytes from `base` (loads past the end read 0).  Copies and
+// loads through it keep the base in scalar registers and take a 32-bit per-lane offset,
+// so no 64-bit address per lane is held (or spilled and reloaded between copies, which
+// would make the compiler wait for every copy in flight).
+__device__ inline __amdgpu_buffer_rsrc_t rsrc_of(const void *base, size_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
+                                             static_cast<int>(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull),
+                                             0x00020000);
 }
 
 __device__ inline uint64_t pack4_bf16(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
@@ -261,10 +273,11 @@ __device__ __forceinline__ void u_issue(const Params &p, int pos, int g, uint4 *
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int ngr = (p.B + 15) / 16;
     g = g < ngr ? g : ngr - 1;
+    const __amdgpu_buffer_rsrc_t rs = rsrc_of(p.uop + (static_cast<size_t>(pos) * p.rb_ngr + g) * UCH, UCH * 16);
 #pragma unroll
     for (int jj = 0; jj < UCH / 64 / NWAVE; ++jj) {
         const int i = wave * (UCH / 64 / NWAVE) + jj;
-        copy_lds16(p.uop + (static_cast<size_t>(pos) * p.rb_ngr + g) * UCH + 64 * i + lane, buf + 64 * i, 0);
+        copy_lds16_buf(rs, buf + 64 * i, static_cast<uint32_t>((64 * i + lane) * 16));
     }
 }
 
@@ -614,8 +627,11 @@ __device__ __forceinline__ void dots_small(const Params &p, int blk, int q, uint
     const bool urows = 16 * blk < r;
     if (blk >= nwt || (q < 0 && urows))
         return;
-    const uint16_t *plane[2] = {p.rb_planes + static_cast<size_t>(q + 1) * 2 * p.rb_bmax * p.rb_ldp,
-                                p.rb_planes + (static_cast<size_t>(q + 1) * 2 + 1) * p.rb_bmax * p.rb_ldp};
+    // the state slot's hi and lo planes through one buffer resource
+    const uint32_t plb = static_cast<uint32_t>(p.rb_bmax * p.rb_ldp * 2);  // bytes of one plane
+    const __amdgpu_buffer_rsrc_t prs =
+        rsrc_of(p.rb_planes + static_cast<size_t>(q + 1) * 2 * p.rb_bmax * p.rb_ldp, 2 * static_cast<size_t>(plb));
+    const __amdgpu_buffer_rsrc_t wrs = rsrc_of(p.wst, static_cast<size_t>(r + h3) * p.ldw * 2);
     // this wave's LDS region: 2 tiles x hi/lo x KSW steps of 1 KB
     uint4 *mine = wave < 2 ? lbA + wave * 1024 : wave < 4 ? lbB + (wave - 2) * 1024
                 : wave < 6 ? lbC + (wave - 4) * 1024 : wave == 6 ? uA : uB;
@@ -630,23 +646,24 @@ __device__ __forceinline__ void dots_small(const Params &p, int blk, int q, uint
         for (int tl = 0; tl < 2; ++tl) {
             int b = 16 * (bt0 + tl) + row;
             b = b < p.B ? b : p.B - 1;
+            // one per-lane offset per tile; the plane and step go in the uniform offset
+            const uint32_t lrow = static_cast<uint32_t>((b * p.rb_ldp + 8 * k) * 2);
 #pragma unroll
             for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
                 for (int i = 0; i < KSW; ++i) {
                     const int st = wave * KSW + i < nks ? wave * KSW + i : 0;
-                    copy_lds16(plane[hl] + static_cast<size_t>(b) * p.rb_ldp + 32 * st + 8 * k,
-                               mine + ((tl * 2 + hl) * KSW + i) * 64, 0);
+                    copy_lds16_buf(prs, mine + ((tl * 2 + hl) * KSW + i) * 64, lrow, hl * plb + st * 64);
                 }
         }
         // this wave's steps of the block's weight tile (steps past h repeat step 0,
         // unused), and the A_H entries of the round's u rows (clamped when unused)
         if (bt0 == 0) {
+            const uint32_t wrow = static_cast<uint32_t>(((16 * blk + row) * p.ldw + 8 * k) * 2);
 #pragma unroll
             for (int i = 0; i < KSW; ++i) {
                 const int st = wave * KSW + i < nks ? wave * KSW + i : 0;
-                dw.w[i] =
-                    *reinterpret_cast<const uint4 *>(p.wst + static_cast<size_t>(16 * blk + row) * p.ldw + 32 * st + 8 * k);
+                dw.w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wrow, st * 64, 0));
             }
         }
         float4 ah = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -766,8 +783,10 @@ __device__ __forceinline__ void dots_2d(const Params &p, int blk, int nblk, int 
     const int nwg = (r + h3) / 64;
     const int nbt = (p.B + 15) / 16, nbj = (nbt + BJ - 1) / BJ;
     const int NS = h / 64;
-    const uint16_t *plane[2] = {p.rb_planes + static_cast<size_t>(q + 1) * 2 * p.rb_bmax * p.rb_ldp,
-                                p.rb_planes + (static_cast<size_t>(q + 1) * 2 + 1) * p.rb_bmax * p.rb_ldp};
+    const uint32_t plb = static_cast<uint32_t>(p.rb_bmax * p.rb_ldp * 2);  // bytes of one plane
+    const __amdgpu_buffer_rsrc_t prs =
+        rsrc_of(p.rb_planes + static_cast<size_t>(q + 1) * 2 * p.rb_bmax * p.rb_ldp, 2 * static_cast<size_t>(plb));
+    const __amdgpu_buffer_rsrc_t wrs = rsrc_of(p.wst, static_cast<size_t>(r + h3) * p.ldw * 2);
     constexpr int NB1 = BJ * 4;                      // 1 KB operand blocks per stage: (bt, hi/lo, step)
     constexpr int PER = (NB1 + NWAVE - 1) / NWAVE;   // copies per wave per stage
     static_assert(NWAVE * PER <= 16, "copies fit one 16 KB ring buffer");
@@ -777,15 +796,16 @@ __device__ __forceinline__ void dots_2d(const Params &p, int blk, int nblk, int 
         const int wt = wg * 4 + tw;  // this wave's weight tile
         const bool urows = wg * 64 < r;
         const bool active = !(q < 0 && urows);
-        const uint16_t *src[PER];
+        uint32_t src[PER], srcs[PER];  // per-lane and uniform byte offsets in the planes' resource
 #pragma unroll
         for (int x = 0; x < PER; ++x) {
             const int ib = (wave * PER + x) % NB1, bt = ib >> 2, hl = (ib >> 1) & 1, st = ib & 1;
             int b = (bj * BJ + bt) * 16 + row;
             b = b < p.B ? b : p.B - 1;
-            src[x] = plane[hl] + static_cast<size_t>(b) * p.rb_ldp + 32 * st + 8 * k;
+            src[x] = static_cast<uint32_t>((b * p.rb_ldp + 8 * k) * 2);
+            srcs[x] = hl * plb + 64 * st;
         }
-        const uint16_t *wrow = p.wst + static_cast<size_t>(wt * 16 + row) * p.ldw + 32 * ks + 8 * k;
+        const uint32_t wrow = static_cast<uint32_t>(((wt * 16 + row) * p.ldw + 32 * ks + 8 * k) * 2);
         uint4 wa[4];
         // the jobs of one batch job read the same S slices: each weight group starts
         // the h reduction at its own stage, so concurrent jobs request different lines
@@ -795,8 +815,8 @@ __device__ __forceinline__ void dots_2d(const Params &p, int blk, int nblk, int 
             s = s + srot < NS ? s + srot : s + srot - NS;
 #pragma unroll
             for (int x = 0; x < PER; ++x)
-                copy_lds16(src[x] + 64 * s, ring + (wave * PER + x) * 64, 0);
-            w = *reinterpret_cast<const uint4 *>(wrow + 64 * s);
+                copy_lds16_buf(prs, ring + (wave * PER + x) * 64, src[x], srcs[x] + 128 * s);
+            w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wrow, 128 * s, 0));
         };
         f32x4_t acc[BJ];
 #pragma unroll

@@ -45,6 +45,10 @@ RB_POSITION = [("wait_u", 0, 7), ("w2", 7, 1), ("resolve", 1, 2), ("gru_update",
                ("state_dots", 4, 5), ("to_next_position", 5, 64), ("position", 0, 64)]
 RB_PROLOGUE = [("w2_slice_load", 1019, 1023), ("anchor_update", 1023, 1022), ("grid_barrier", 1022, 1021),
                ("anchor_dots", 1021, 1020), ("prologue", 1019, 1020)]
+# the state dots of up to four batch tiles (B <= 64) mark their first round at slots
+# 64 q + 40..43 of the state q they compute, i.e. 64 + 40.. after the position before it
+RB_SMALL_DOTS = [("dots_copies_issued", 4, 64 + 40), ("dots_copies_landed", 64 + 40, 64 + 41),
+                 ("dots_products", 64 + 41, 64 + 42), ("dots_reduce_store", 64 + 42, 64 + 43)]
 
 
 def _span(t, a, b):
@@ -52,11 +56,13 @@ def _span(t, a, b):
     return float(np.median(d)), float(d.max())
 
 
-def summarize(t, K, batched):
+def summarize(t, K, batched, small_dots=False):
     """t: [blocks, SLOTS] int64 timestamps of one call.  Returns a dict of phase -> [median, max] us."""
     if batched:
         col = lambda s: s  # noqa: E731
         per, pro, stride, end = RB_POSITION, RB_PROLOGUE, 64, 64 * (K - 1) + 2
+        if small_dots:
+            per = per + RB_SMALL_DOTS
         start = 1019
     else:
         col = lambda s: s + RES_BIAS  # noqa: E731
@@ -66,7 +72,7 @@ def summarize(t, K, batched):
     out["prologue"] = {n: [round(x, 2) for x in _span(t, col(a), col(b))] for n, a, b in pro}
     for p in sorted({0, K - 1}):
         out["position_%d" % p] = {n: [round(x, 2) for x in _span(t, col(stride * p + a), col(stride * p + b))]
-                                  for n, a, b in per if stride * p + b <= end}
+                                  for n, a, b in per if stride * p + max(a, b) <= end}
     mids = range(1, K - 1)
     if len(mids):
         out["positions_1_to_%d_median" % (K - 2)] = {
@@ -117,7 +123,14 @@ def run(names, lib_path=None, persistent=False, lbase_bf16=False):
         r = {"workload": name + (" bf16 L_base" if lbase_bf16 else ""), "B": wl.B,
              "kernel": "k_persistent_rb" if batched else "k_persistent_res", "grid": info["grid"],
              "call_us": round(e0.elapsed_time(e1) * 1e3, 1)}
+        # only blocks that compute state dots mark the small dots' rounds
+        nd = (sh.r + 3 * sh.h) // 16 if batched and wl.B <= 64 else 0
         r.update(summarize(t, sh.K, batched))
+        if nd:
+            r["state_dots_detail"] = summarize(t[:nd], sh.K, batched, small_dots=True)[
+                "positions_1_to_%d_median" % (sh.K - 2)]
+            r["state_dots_detail"] = {k: v for k, v in r["state_dots_detail"].items()
+                                      if k.startswith("dots_")}
         results[name] = r
         del head
     return results

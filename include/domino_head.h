@@ -57,8 +57,8 @@ extern "C" {
 
 /* ---- config.flags bits (execution strategy; results do not depend on them) ---- */
 #define DOMINO_EXEC_AUTO 0u        /* pick per call from B: the persistent launch for B <= 8, and for
-                                      8 < B <= 48 where the batched persistent launch is available (see
-                                      below); the step launches otherwise, which are faster above that */
+                                      8 < B <= 256 where the batched persistent launch is available (see
+                                      below); the step launches otherwise */
 #define DOMINO_EXEC_PERSISTENT 1u  /* one cooperative launch covering all K positions: B <= 8, or (bf16
                                       weights, r = 256, DOMINO_FOLD_EMBED, h a multiple of 64, d of 32)
                                       B <= 256, where the GRU update and state products are spread over

@@ -58,13 +58,12 @@ def test_exec_info_reports_the_batched_resident_launch():
     # past B = 256 a forced persistent launch is refused
     with pytest.raises(RuntimeError):
         head.exec_info(257)
-    # AUTO takes the batched launch up to B = 48 and the step launches above
+    # AUTO takes the batched launch for 8 < B <= 256 and the step launches above
     auto = batched_head(w, 300, dca.EXEC_AUTO)
-    for B in (9, 40, 48):
+    for B in (9, 40, 48, 49, 256):
         assert auto.exec_info(B) == {"persistent": True, "w2_resident": True, "grid": cus()}, B
     assert auto.exec_info(8)["w2_resident"] and auto.exec_info(8)["persistent"]
-    for B in (49, 256, 257):
-        assert auto.exec_info(B) == {"persistent": False, "w2_resident": False, "grid": 0}, B
+    assert auto.exec_info(257) == {"persistent": False, "w2_resident": False, "grid": 0}
     assert make_head(w, 40, fold=False).exec_info(40)["persistent"] is False
     assert make_head(w, 40, dca.EXEC_STEPWISE, fold=True).exec_info(40)["persistent"] is False
     # a forced persistent launch at B > 8 takes the batched kernel

@@ -280,14 +280,17 @@ def test_qwen3_8b_b1_full(w8b):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name,rows", [("qwen3_8b_b32", [0, 13, 31]), ("qwen3_8b_b256", [0, 101, 255])])
-def test_qwen3_8b_batched_sampled_rows(w8b, name, rows):
-    """Full batch on the device (the launch the benchmark times: the batched persistent
-    kernel at B = 32, the step launches at B = 256, float32 L_base); the oracle checks
-    sampled rows free running and teacher forced with its own draft."""
+@pytest.mark.parametrize("name,rows,mode", [("qwen3_8b_b32", [0, 13, 31], dca.EXEC_AUTO),
+                                            ("qwen3_8b_b256", [0, 101, 255], dca.EXEC_AUTO),
+                                            ("qwen3_8b_b256", [0, 77, 255], dca.EXEC_STEPWISE)])
+def test_qwen3_8b_batched_sampled_rows(w8b, name, rows, mode):
+    """Full batch on the device (AUTO: the launch the benchmark times, the batched
+    persistent kernel; and the step launches at B = 256), folded table, float32 L_base;
+    the oracle checks sampled rows free running and teacher forced with its own draft."""
     wl = ds.WORKLOADS[name]
     inp = ds.make_inputs(wl.shape, wl.B, wl.row_key, wl.sigma, wl.peak, wl.peak_height, wl.temperature)
-    head = make_head(w8b, wl.B, fold=True)
+    head = make_head(w8b, wl.B, mode, fold=True)
+    assert head.exec_info(wl.B)["persistent"] == (mode == dca.EXEC_AUTO)
     g, flags = gpu_draft(head, inp.H, inp.L_base, inp.last_tok, rows=rows)
     assert flags == 0
     sub = ds.make_inputs(wl.shape, rows, wl.row_key, wl.sigma, wl.peak, wl.peak_height, wl.temperature)
@@ -309,21 +312,21 @@ def test_qwen3_8b_batched_sampled_rows(w8b, name, rows):
 @pytest.mark.parametrize("name,rows,variant", [("qwen3_8b_b32", [0, 19, 31], "teacher"),
                                                ("qwen3_8b_b256", [0, 128, 255], "lbase_bf16")])
 def test_qwen3_8b_batched_variants_sampled_rows(w8b, name, rows, variant):
-    """The launches the benchmark times with --teacher (position-batched W2 over 512 rows)
-    and with --lbase-bf16, at full size; the oracle checks sampled rows."""
+    """The launches the benchmark times with --teacher and with --lbase-bf16 (the batched
+    persistent kernel, folded table), at full size; the oracle checks sampled rows."""
     wl = ds.WORKLOADS[name]
     sh = wl.shape
     inp = ds.make_inputs(sh, wl.B, wl.row_key, wl.sigma, wl.peak, wl.peak_height, wl.temperature)
     sub = ds.make_inputs(sh, rows, wl.row_key, wl.sigma, wl.peak, wl.peak_height, wl.temperature)
     if variant == "teacher":
         y = ds.uniform_tokens(list(wl.row_key) + [9], (wl.B, sh.K), sh.V)
-        g, flags = gpu_draft(make_head(w8b, wl.B), inp.H, inp.L_base, inp.last_tok, teacher=y, rows=rows)
+        g, flags = gpu_draft(make_head(w8b, wl.B, fold=True), inp.H, inp.L_base, inp.last_tok, teacher=y, rows=rows)
         assert flags == 0
         o = oracle.draft(w8b, sub.H, sub.L_base, sub.last_tok, teacher=y[rows])
         compare_teacher_forced(o, g)
     else:
         L16 = ds.round_to_bf16_bits(inp.L_base)
-        g, flags = gpu_draft(make_head(w8b, wl.B, lbase_bf16=True), inp.H, L16, inp.last_tok, rows=rows)
+        g, flags = gpu_draft(make_head(w8b, wl.B, fold=True, lbase_bf16=True), inp.H, L16, inp.last_tok, rows=rows)
         assert flags == 0
         o = oracle.draft(w8b, sub.H, ds.bf16_bits_to_f32(L16[rows]), sub.last_tok)
         div = compare_free_running(o, g)

@@ -187,13 +187,15 @@ struct LbCopy {
 // copy i = wave * NLD + jj lands at LDS row s / (ROWB / 16), chunk s % (ROWB / 16),
 // whose value index within the block's range is (chunk ^ (row & 7)) * (16 / EL).
 // Rows past B and values past the tensor lie past the buffer resource's records
-// and read as 0 (their results are masked); values past the block's range are
-// other blocks' values, also masked.  The same at every group and position.
+// and read as 0 (their results are masked).  Pieces past the block's n values
+// re-read the row's first piece (a line the copy fetches anyway), so the block
+// never pulls in another block's values; those LDS entries are masked too.  The
+// same at every group and position.
 template <bool LB16>
 struct LbOff {
     using C = LbCopy<LB16, true>;
     uint32_t off[C::NLD];
-    __device__ LbOff(const Params &p, int v0)
+    __device__ LbOff(const Params &p, int v0, int n)
     {
         const int lane = threadIdx.x & 63;
         const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -202,7 +204,8 @@ struct LbOff {
         for (int jj = 0; jj < C::NLD; ++jj) {
             const int s = 64 * (wave * C::NLD + jj) + lane;
             const int row = s / (C::ROWB / 16), ch = s % (C::ROWB / 16);
-            const int e = (ch ^ (row & 7)) * (16 / C::EL);
+            int e = (ch ^ (row & 7)) * (16 / C::EL);
+            e = e < n ? e : 0;
             off[jj] = static_cast<uint32_t>(row) * rowstride + static_cast<uint32_t>(v0 + e) * C::EL;
         }
     }
@@ -380,7 +383,7 @@ __device__ __forceinline__ void w2_group(const Params &p, const Ctx &c, const W2
 template <bool LB16, bool FAST>
 __device__ __forceinline__ void w2_prefetch(const Params &p, const Ctx &c, int pos, uint4 *lbA, uint4 *lbB)
 {
-    const LbOff<LB16> lo(p, c.v0);
+    const LbOff<LB16> lo(p, c.v0, c.n);
     lb_issue<LB16, FAST>(p, c, lo, pos, 0, lbA);
     lb_issue<LB16, FAST>(p, c, lo, pos, 1, lbB);
 }
@@ -394,7 +397,7 @@ __device__ __forceinline__ void w2_phase(const Params &p, const Ctx &c, const W2
 {
     using C = LbCopy<LB16, FAST>;
     const int ngr = (p.B + 15) / 16;
-    const LbOff<LB16> lo(p, c.v0);
+    const LbOff<LB16> lo(p, c.v0, c.n);
     // block key of group gp from the waves' keys (after a barrier)
     auto fold = [&](int gp) {
         if (threadIdx.x < 16) {

@@ -250,9 +250,25 @@ __device__ inline uint64_t argmax_key(float f, uint32_t idx)
 
 __device__ inline uint32_t key_index(uint64_t key) { return 0xFFFFFFFFu - static_cast<uint32_t>(key); }
 
+// The exchange words live in global memory.  Accesses through a global-address-space
+// pointer compile to global loads and stores, which count only against the vector
+// memory counter; through a generic pointer they become flat accesses, which also count
+// against the LDS counter, so every later wait for an LDS read would wait for them too
+// (an agent-scope store then costs a memory round trip at the next LDS read).
+template <typename T>
+__device__ inline __attribute__((address_space(1))) T *gmem(T *p)
+{
+    return (__attribute__((address_space(1))) T *)p;
+}
+template <typename T>
+__device__ inline const __attribute__((address_space(1))) T *gmem(const T *p)
+{
+    return (const __attribute__((address_space(1))) T *)p;
+}
+
 __device__ inline uint64_t ld_agent_u64(const uint64_t *p)
 {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(gmem(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -262,10 +278,10 @@ __device__ inline uint64_t ld_agent_u64(const uint64_t *p)
 // caches that are not coherent with each other.  The barrier below then only
 // has to order completed accesses; it needs no L2 write-back or invalidate.
 // ---------------------------------------------------------------------------
-__device__ inline void xst(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline void xst(float *p, float v) { __hip_atomic_store(gmem(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ inline float xld(const float *p)
 {
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(gmem(const_cast<float *>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Block-wide failure flag of a persistent kernel (bounded waits that timed
@@ -316,14 +332,14 @@ __device__ inline unsigned *bar_slots(unsigned *bar) { return bar + BAR_SLOTS; }
 
 __device__ inline unsigned barrier_gen_init(unsigned *bar)
 {
-    return __hip_atomic_load(&bar_slots(bar)[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(gmem(&bar_slots(bar)[blockIdx.x]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // End of a launch: record the block's final generation in its slot.
 __device__ inline void barrier_finish(unsigned *bar, unsigned gen)
 {
     if (threadIdx.x == 0)
-        __hip_atomic_store(&bar_slots(bar)[blockIdx.x], gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(gmem(&bar_slots(bar)[blockIdx.x]), gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // `gen` is tracked identically by every thread of the block.
@@ -333,7 +349,7 @@ __device__ inline void grid_arrive(unsigned *bar, unsigned gen)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     if (threadIdx.x == 0)
-        __hip_atomic_store(&bar_slots(bar)[blockIdx.x], gen + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(gmem(&bar_slots(bar)[blockIdx.x]), gen + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ inline bool grid_wait(unsigned *bar, unsigned &gen, unsigned spin_limit, unsigned *flags)
@@ -343,7 +359,7 @@ __device__ inline bool grid_wait(unsigned *bar, unsigned &gen, unsigned spin_lim
     int ok = 1;
     for (int i = threadIdx.x; i < static_cast<int>(gridDim.x); i += NT) {
         unsigned spins = 0;
-        while (static_cast<int>(__hip_atomic_load(const_cast<unsigned *>(&slots[i]), __ATOMIC_RELAXED,
+        while (static_cast<int>(__hip_atomic_load(gmem(const_cast<unsigned *>(&slots[i])), __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT) - next) < 0) {
             if (++spins > spin_limit) {
                 ok = 0;
@@ -355,7 +371,7 @@ __device__ inline bool grid_wait(unsigned *bar, unsigned &gen, unsigned spin_lim
     gen = next;
     const bool failed = block_failed(ok);
     if (failed && threadIdx.x == 0)
-        __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(gmem(flags), 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     return !failed;
 }
@@ -409,7 +425,7 @@ __device__ inline void argmax_arrive(uint64_t *asy, unsigned gen, const uint64_t
     // takes one written many launches ago for a current one
     if (threadIdx.x < BC) {
         const uint64_t k = threadIdx.x < nb ? local_key[threadIdx.x] & (KEY_ORD_MASK | KEY_IDX_MASK) : 0;
-        __hip_atomic_store(&asy[argmax_word(gen + 1, blockIdx.x, threadIdx.x)], k | g14, __ATOMIC_RELAXED,
+        __hip_atomic_store(gmem(&asy[argmax_word(gen + 1, blockIdx.x, threadIdx.x)]), k | g14, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -432,7 +448,7 @@ __device__ inline bool argmax_wait(const uint64_t *asy, unsigned &gen, int nb, i
         uint64_t w;
         unsigned spins = 0;
         for (;;) {
-            w = __hip_atomic_load(const_cast<uint64_t *>(wp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            w = __hip_atomic_load(gmem(const_cast<uint64_t *>(wp)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (((static_cast<unsigned>(w >> 18) - g14) & 0x3FFFu) < 0x2000u)
                 break;
             if (++spins > spin_limit) {
@@ -465,7 +481,7 @@ __device__ inline bool argmax_wait(const uint64_t *asy, unsigned &gen, int nb, i
         tok[threadIdx.x] = m ? static_cast<int>(KEY_IDX_MASK - (m & KEY_IDX_MASK)) : 0;
     }
     if (failed && threadIdx.x == 0)
-        __hip_atomic_fetch_or(flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(gmem(flags), 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();  // tok visible to the block
     return !failed;
 }

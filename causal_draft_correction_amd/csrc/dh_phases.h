@@ -136,12 +136,12 @@ __device__ inline void prologue_bookkeeping(const Params &p)
     const int n = p.K * NG;
     for (int i = threadIdx.x; i < n * p.B; i += NT) {
         const int slot = i / p.B, b = i % p.B;
-        __hip_atomic_store(p.keys + static_cast<size_t>(slot) * p.maxB + b, 0ull, __ATOMIC_RELAXED,
+        __hip_atomic_store(gmem(p.keys + static_cast<size_t>(slot) * p.maxB + b), 0ull, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
     for (int b = threadIdx.x; b < p.B; b += NT)
         if (row_bad(p, b))
-            __hip_atomic_fetch_or(p.flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(gmem(p.flags), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ inline float *q_slot(const Params &p, int s) { return p.q_buf + static_cast<size_t>(s & 1) * p.maxB * 3 * p.h; }
@@ -565,8 +565,8 @@ __device__ inline void utag_refresh(const Params &p, int blk, int nblk, unsigned
     const size_t base = static_cast<size_t>(p.B) * p.r, n = static_cast<size_t>(rows) * p.r;
     const size_t plane = static_cast<size_t>(p.maxB) * p.r;
     for (size_t i = static_cast<size_t>(blk) * NT + threadIdx.x; i < n; i += static_cast<size_t>(nblk) * NT) {
-        __hip_atomic_store(&p.utag[base + i], t16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.utag[plane + base + i], t16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(gmem(&p.utag[base + i]), t16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(gmem(&p.utag[plane + base + i]), t16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -744,8 +744,8 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                             const uint32_t lo = bf16_rne_bits(u - __uint_as_float(hi << 16));
                             const uint32_t t16 = (tag & 0xFFFFu) << 16;
                             const size_t o = static_cast<size_t>(b) * r + m;
-                            __hip_atomic_store(&p.utag[o], t16 | hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            __hip_atomic_store(&p.utag[static_cast<size_t>(p.maxB) * r + o], t16 | lo,
+                            __hip_atomic_store(gmem(&p.utag[o]), t16 | hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            __hip_atomic_store(gmem(&p.utag[static_cast<size_t>(p.maxB) * r + o]), t16 | lo,
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         } else {
                             xst(&p.u_buf[static_cast<size_t>(b) * r + m], u);
@@ -809,7 +809,7 @@ __device__ __forceinline__ void w2_epilogue(const Params &p, int blk, int nblk, 
             if (local_keys)
                 local_keys[bb] = m ? (m & KEY_ORD_MASK) | (KEY_IDX_MASK - key_index(m)) : 0ull;
             else
-                __hip_atomic_fetch_max(key_slot(p, pos, g, b), m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_max(gmem(key_slot(p, pos, g, b)), m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
     }
@@ -1182,7 +1182,7 @@ __device__ __forceinline__ bool phase_w2_resident(const Params &p, int blk, int 
     DH_TRACE(pos * 32 + 1);
     if (block_failed(ok)) {
         if (threadIdx.x == 0)
-            __hip_atomic_fetch_or(p.flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(gmem(p.flags), 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return false;
     }
     DH_TRACE(pos * 32 + 2);

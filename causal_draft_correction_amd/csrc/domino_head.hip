@@ -255,7 +255,7 @@ __global__ __launch_bounds__(NT) void k_step_prologue(Params p)
     if (blockIdx.x == 0) {
         for (int b = threadIdx.x; b < p.B; b += NT)
             if (row_bad(p, b))
-                __hip_atomic_fetch_or(p.flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_or(gmem(p.flags), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (!p.ah_external)
         phase_ah<WT>(p, blockIdx.x, gridDim.x, smem);

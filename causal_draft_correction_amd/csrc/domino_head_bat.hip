@@ -300,7 +300,7 @@ __global__ __launch_bounds__(NTH) void k_w2_mfma(Params p, int pos, int ng_arg)
             key = max_u64(key, dpp_u64<DPP_ROW_MIRROR>(key));
             const int b = brow[a][ii];
             if (col == 0 && b < B && key)
-                __hip_atomic_fetch_max(key_slot(p, pos, g, b), key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_max(gmem(key_slot(p, pos, g, b)), key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 }
 

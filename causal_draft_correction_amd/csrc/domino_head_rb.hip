@@ -88,7 +88,7 @@ __device__ inline void bare_barrier()
 
 __device__ inline void st_agent_u64(void *p, uint64_t v)
 {
-    __hip_atomic_store(static_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gmem(static_cast<uint64_t *>(p)), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline float4 ld_agent_f4(const float *p)
 {
@@ -507,7 +507,7 @@ __device__ __forceinline__ bool resolve(const Params &p, const Ctx &c, int pos, 
     const bool failed = block_failed(ok);
     if (failed) {
         if (threadIdx.x == 0)
-            __hip_atomic_fetch_or(p.flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(gmem(p.flags), 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return false;
     }
     if (static_cast<int>(threadIdx.x) < c.nrows) {
@@ -754,7 +754,7 @@ __device__ __forceinline__ void dots_small(const Params &p, int blk, int q, uint
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0)
-            __hip_atomic_fetch_add(&p.rb_ucnt[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(gmem(&p.rb_ucnt[q]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -904,7 +904,7 @@ __device__ __forceinline__ void dots_2d(const Params &p, int blk, int nblk, int 
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (threadIdx.x == 0)
-                __hip_atomic_fetch_add(&p.rb_ucnt[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(gmem(&p.rb_ucnt[q]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         // the exchange buffer is the first ring buffer of the next job
         __syncthreads();
@@ -928,7 +928,7 @@ __device__ __forceinline__ bool wait_u(const Params &p, int q)
     if (threadIdx.x == 0) {
         const unsigned want = static_cast<unsigned>(u_producers(p.B, p.r));
         unsigned spins = 0;
-        while (__hip_atomic_load(&p.rb_ucnt[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+        while (__hip_atomic_load(gmem(&p.rb_ucnt[q]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
             if (++spins > p.spin_limit) {
                 ok = 0;
                 break;
@@ -938,7 +938,7 @@ __device__ __forceinline__ bool wait_u(const Params &p, int q)
     }
     if (block_failed(ok)) {
         if (threadIdx.x == 0)
-            __hip_atomic_fetch_or(p.flags, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(gmem(p.flags), 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return false;
     }
     return true;
@@ -962,10 +962,10 @@ __global__ __launch_bounds__(NT) void k_persistent_rb(Params p)
     if (blk == 0) {
         for (int b = threadIdx.x; b < p.B; b += NT)
             if (row_bad(p, b))
-                __hip_atomic_fetch_or(p.flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_or(gmem(p.flags), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // the u counters of this launch start at 0 (the first increment follows a barrier)
         if (threadIdx.x < static_cast<unsigned>(p.K))
-            __hip_atomic_store(&p.rb_ucnt[threadIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(gmem(&p.rb_ucnt[threadIdx.x]), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     const Ctx c = make_ctx(p, blk, nblk);
     // the block's W2 slice: tile t = wave + NWAVE j in registers (zero past the range),

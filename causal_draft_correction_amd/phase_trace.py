@@ -9,11 +9,12 @@ Positions 1..K-2 are summarised by the median over positions; the anchor step,
 the first and the last position are listed separately.
 
     python -m causal_draft_correction_amd.phase_trace qwen3_8b_b1 [qwen3_8b_b32 ...] [--json]
-        [--persistent] [--lbase-bf16]
+        [--persistent] [--lbase-bf16] [--no-fold]
 
 --persistent forces the persistent launch where the automatic choice would take
 the step launches (the batched kernel up to B = 256); --lbase-bf16 passes the
-base logits as bfloat16.
+base logits as bfloat16; --no-fold drafts without the folded gate table (the GRU
+input product runs at every step; B <= 8 only).
 
 Only this tool loads the instrumented library; it needs a GPU.
 """
@@ -36,7 +37,7 @@ BLOCKS, SLOTS = 256, 1024
 RES_BIAS = 64
 # (name, first mark, second mark) relative to 32 * position
 RES_POSITION = [("w2_wait_u", 0, 1), ("w2_products", 2, 4), ("w2_block_key", 4, 5), ("argmax_exchange", 5, 13),
-                ("gru_gates", 16, 18), ("state_sync", 18, 19), ("state_dots", 19, 20), ("u_hop", 20, 32),
+                ("input_product", 13, 16), ("gru_gates", 16, 18), ("state_sync", 18, 19), ("state_dots", 19, 20), ("u_hop", 20, 32),
                 ("position", 0, 32)]
 RES_PROLOGUE = [("slice_and_loads_issued", 511, 508), ("anchor_step", -16, -12), ("prologue", 511, 509)]
 
@@ -81,7 +82,7 @@ def summarize(t, K, batched, small_dots=False):
     return out
 
 
-def run(names, lib_path=None, persistent=False, lbase_bf16=False):
+def run(names, lib_path=None, persistent=False, lbase_bf16=False, fold=True):
     sys.path.insert(0, ROOT)
     import torch
 
@@ -98,7 +99,7 @@ def run(names, lib_path=None, persistent=False, lbase_bf16=False):
         wl = ds.WORKLOADS[name]
         sh = wl.shape
         w, inp = ds.make_workload(name)
-        head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B, fold_embedding=True,
+        head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B, fold_embedding=fold,
                               exec_mode=dca.EXEC_PERSISTENT if persistent else dca.EXEC_AUTO, lbase_bf16=lbase_bf16)
         info = head.exec_info(wl.B)
         if not (info["persistent"] and info["w2_resident"]):
@@ -120,7 +121,7 @@ def run(names, lib_path=None, persistent=False, lbase_bf16=False):
         rc = (lib.domino_trace_read_rb if batched else lib.domino_trace_read_res)(buf.ctypes.data)
         assert rc == 0, rc
         t = buf.reshape(BLOCKS, SLOTS)[:min(info["grid"], BLOCKS)].astype(np.int64)
-        r = {"workload": name + (" bf16 L_base" if lbase_bf16 else ""), "B": wl.B,
+        r = {"workload": name + (" bf16 L_base" if lbase_bf16 else "") + ("" if fold else " unfolded"), "B": wl.B,
              "kernel": "k_persistent_rb" if batched else "k_persistent_res", "grid": info["grid"],
              "call_us": round(e0.elapsed_time(e1) * 1e3, 1)}
         # only blocks that compute state dots mark the small dots' rounds
@@ -153,8 +154,9 @@ def main():
     ap.add_argument("--json", action="store_true")
     ap.add_argument("--persistent", action="store_true")
     ap.add_argument("--lbase-bf16", action="store_true")
+    ap.add_argument("--no-fold", action="store_true")
     args = ap.parse_args()
-    res = run(args.workloads, persistent=args.persistent, lbase_bf16=args.lbase_bf16)
+    res = run(args.workloads, persistent=args.persistent, lbase_bf16=args.lbase_bf16, fold=not args.no_fold)
     for r in res.values():
         print(json.dumps(r) if args.json else to_markdown(r) + "\n", flush=True)
 

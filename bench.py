@@ -236,8 +236,10 @@ def run_verify(args, wl):
     # algorithmic bytes: every logit once, the draft, the outputs
     total_bytes = B * (K + 1) * V * 4 + B * K * 4 + B * (K + 1) * 4 + 2 * B * 4
     achieved = total_bytes / (avg_ms * 1e-3) / 1e9
+    achieved_cold = None if cold_us is None else total_bytes / (cold_us * 1e-6) / 1e9
     name = "verify_" + wl.name
     traffic = measured_traffic(name, "verify", False)
+    hbm_actual = None if traffic is None else traffic / (avg_ms * 1e-3) / 1e9
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -252,7 +254,7 @@ def run_verify(args, wl):
                 break
         cpu = {"value": n / el, "unit": "blocks/s", "cores": 1, "kind": "oracle",
                "sample": "%d verify steps of %d-row slices of the same inputs (K=%d, V=%d), C oracle, one thread" % (
-                   n // rows, rows, K, V)}
+                   n // rows, rows, K, V), "cpu_model": cpu_model(), "host_cores": host_cores()}
     rec = {
         "metric": "greedy verify: drafted blocks checked per second (K+1 target rows of V logits each) at 1 GPU",
         "value": B * args.steps / wall,
@@ -271,7 +273,10 @@ def run_verify(args, wl):
                    "cold_us_per_call_median": cold_us},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic, "algorithmic_bytes": total_bytes,
-                     "kernel": "k_verify_rows + k_verify_final"},
+                     "kernel": "k_verify_rows + k_verify_final", "achieved_cold": achieved_cold,
+                     "frac_cold": None if achieved_cold is None else achieved_cold / HBM_PEAK_GBPS,
+                     "hbm_actual_GBps": hbm_actual,
+                     "hbm_actual_frac": None if hbm_actual is None else hbm_actual / HBM_PEAK_GBPS},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
@@ -441,10 +446,11 @@ def main():
                if not args.lbase_bf16 and not args.teacher and not args.store_logits and not args.graph else None)
     kname = KERNEL_NAMES[kind]
     hbm_actual = None if traffic is None else traffic / (avg_ms * 1e-3) / 1e9
-    # a persistent launch runs the K positions as one dependent chain inside one kernel: its time
-    # is set by the per-position latency (phases, grid barriers), not by HBM (the counters show
-    # HBM far from busy) or the matrix cores; the step launches at large B stream L_base and W2
-    bound = "latency" if info["persistent"] else "hbm"
+    # a persistent launch runs the K positions as one dependent chain inside one kernel: up to
+    # B = 64 its time is set by the per-position latency (phases, grid barriers), not by HBM (the
+    # counters show it far from busy) or the matrix cores.  Larger batches stream L_base (155.6 MB
+    # per position at B = 256, half of each position's time), like the step launches
+    bound = "latency" if info["persistent"] and wl.B <= 64 else "hbm"
 
     f_w2, f_all = algorithmic_flops(sh, wl.B, fold, args.markov)
     mfma = {"w2_tflops": f_w2 / (avg_ms * 1e-3) / 1e12, "all_tflops": f_all / (avg_ms * 1e-3) / 1e12,

@@ -11,14 +11,17 @@
 // each, so one wave's epilogue and copies overlap the other's matrix-core
 // products).  Block b owns a contiguous range of 16-row vocabulary tiles; wave w
 // holds tiles w, w + 8, ... of it (RT per wave, 160 registers at r = 256).
-// Per position the launch runs three phases separated by grid barriers:
+// Per position the launch runs three phases.  The W2 phase starts once every
+// block of the u rows has counted itself in the position's arrival counter, the
+// update once every block's argmax word of its rows carries the position's tag,
+// and the state dots after one grid barrier:
 //   * W2 phase: for each group of 16 batch rows, D = W2_tile u^T on the matrix
 //     cores (v_mfma_f32_16x16x32_bf16, A = the register tile, B = u rounded once
 //     to bf16: the products are those of bf16 operands with float32 sums, u's
 //     rounding moves the logits by at most a few 1e-3 at the 8B shapes), plus
-//     L_base, into a running greedy argmax.  The
-//     groups' L_base slices (two groups ahead) and u operands (one ahead) are
-//     copied into LDS by direct global-to-LDS loads.  The block's key for each
+//     L_base, into a running greedy argmax.  The groups' L_base slices (two
+//     groups ahead) and u operands (one ahead) are copied into LDS by direct
+//     global-to-LDS loads through buffer resources.  The block's key for each
 //     batch row goes to a generation-tagged word bkeys[b][block];
 //   * update phase: every block owns a contiguous range of the B x h state
 //     entries; it reduces the argmax words of its rows (polling until all carry
@@ -26,11 +29,12 @@
 //     owns, and steps the GRU for its entries (P row, q = W_hh S + b_hh and the
 //     previous state, which stays with its owner), writing S as float32 and as
 //     bf16 hi/lo planes;
-//   * state-dot phase: [u | q'] = S [B, h] x [W1_S; W_hh]^T on the matrix cores
-//     in jobs of 4 weight tiles x BJ batch tiles (S hi and lo staged in LDS four
-//     stages ahead, weight rows from L2; two waves per weight tile split each
-//     stage's two 32-wide steps), then u = SiLU(A_H + .) as the next W2 phase's
-//     bf16 operand and q' + b_hh for the next update.
+//   * state-dot phase: [u | q'] = S [B, h] x [W1_S; W_hh]^T on the matrix cores,
+//     S as bf16 hi + lo operands.  Up to four 16-row batch tiles, block b takes
+//     weight tile b and its waves split h (dots_small); more tiles run as jobs of
+//     4 weight tiles x 4 batch tiles over the grid with S staged in LDS three
+//     stages ahead (dots_2d).  Then u = SiLU(A_H + .) as the next W2 phase's bf16
+//     operand, and q' + b_hh for the next update.
 // Values that cross blocks are written with agent-scope stores, which write
 // through the per-XCD L2 caches (not coherent with each other).  The argmax
 // words and q, each read by one block, are read with agent-scope loads, which
@@ -68,7 +72,6 @@ constexpr int UBUF = 1024;           // uint4 of each of the two small LDS buffe
 constexpr int MAXB = 256;            // batch rows of one launch
 constexpr int ROWS = 4;              // batch rows one block updates at most (B <= MAXB)
 constexpr int CPT = 1;               // 4-entry state chunks per thread at most
-constexpr unsigned AUX_SC1 = 16;     // cache policy of agent-scope coherent accesses (sc1)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -102,14 +105,7 @@ __device__ inline void st_agent_f4(float *p, float4 v)
     st_agent_u64(p, (static_cast<uint64_t>(__float_as_uint(v.y)) << 32) | __float_as_uint(v.x));
     st_agent_u64(p + 2, (static_cast<uint64_t>(__float_as_uint(v.w)) << 32) | __float_as_uint(v.z));
 }
-// Direct global-to-LDS copies of 16, 4 or 2 bytes per lane (lane l writes at lds + l * size)
-__device__ inline void copy_lds16(const void *g, void *lds, unsigned aux_sc1)
-{
-    if (aux_sc1)
-        __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, AUX_SC1);
-    else
-        __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, 0);
-}
+// Direct global-to-LDS copy of 4 bytes per lane (lane l writes at lds + 4 l)
 __device__ inline void copy_lds4(const void *g, void *lds) { __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 4, 0, 0); }
 
 // the same through a buffer resource (16 bytes at byte offset voff + soff, voff per lane and
@@ -1060,8 +1056,9 @@ bool supports(int d, int h, int r, int V, int grid)
     const long long T = (V + 15) / 16;
     if ((T + grid - 1) / grid > rbk::TILES || V >= (1 << 18))
         return false;
-    // state chunks and rows per block at the largest batch
-    const long long nc = static_cast<long long>(rbk::MAXB) * h / 4, per = (nc + grid - 1) / grid;
+    // state chunks and rows per block at the largest batch, in whole 16-chunk runs as the
+    // kernel splits them
+    const long long nc = static_cast<long long>(rbk::MAXB) * h / 4, per = ((nc + grid - 1) / grid + 15) & ~15ll;
     return per <= static_cast<long long>(rbk::CPT) * NT && per * 4 / h + 2 <= rbk::ROWS;
 }
 

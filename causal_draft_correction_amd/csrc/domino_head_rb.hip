@@ -126,6 +126,23 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc_of(const void *base, size_t bytes)
                                              0x00020000);
 }
 
+// Loads through global-address-space pointers: as flat loads (through a generic
+// pointer) they would also count against the LDS counter, and the next LDS read would
+// wait for them.
+typedef float f4n __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) f4n gf4n;
+__device__ inline float4 ld_f4(const float *p)
+{
+    const f4n v = *reinterpret_cast<const gf4n *>(gmem(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+// entry m of b_hh (bf16 heads only), 0 without biases
+__device__ inline float bias_hh_bf16(const Params &p, int m)
+{
+    return p.b_hh ? __uint_as_float(static_cast<uint32_t>(gmem(static_cast<const uint16_t *>(p.b_hh))[m]) << 16)
+                  : 0.f;
+}
+
 __device__ inline uint64_t pack4_bf16(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
     return static_cast<uint64_t>(a | (b << 16)) | (static_cast<uint64_t>(c | (d << 16)) << 32);
@@ -548,16 +565,16 @@ __device__ __forceinline__ void update(const Params &p, const Ctx &c, int q, con
                 x = rtok[b - c.rb0];
             x = tok_ok(x, p.V) ? x : 0;
             const float *prow = p.P + static_cast<size_t>(x) * h3 + j;
-            const float4 gr = *reinterpret_cast<const float4 *>(prow);
-            const float4 gz = *reinterpret_cast<const float4 *>(prow + h);
-            const float4 gn = *reinterpret_cast<const float4 *>(prow + 2 * h);
+            const float4 gr = ld_f4(prow);
+            const float4 gz = ld_f4(prow + h);
+            const float4 gn = ld_f4(prow + 2 * h);
             float4 qr, qz, qn;
             if (q == 0 && !p.S_init) {
                 // W_hh S_init + b_hh with S_init = 0 is b_hh itself
-                qr = make_float4(bias_hh(p, j), bias_hh(p, j + 1), bias_hh(p, j + 2), bias_hh(p, j + 3));
-                qz = make_float4(bias_hh(p, h + j), bias_hh(p, h + j + 1), bias_hh(p, h + j + 2), bias_hh(p, h + j + 3));
-                qn = make_float4(bias_hh(p, 2 * h + j), bias_hh(p, 2 * h + j + 1), bias_hh(p, 2 * h + j + 2),
-                                 bias_hh(p, 2 * h + j + 3));
+                qr = make_float4(bias_hh_bf16(p, j), bias_hh_bf16(p, j + 1), bias_hh_bf16(p, j + 2), bias_hh_bf16(p, j + 3));
+                qz = make_float4(bias_hh_bf16(p, h + j), bias_hh_bf16(p, h + j + 1), bias_hh_bf16(p, h + j + 2), bias_hh_bf16(p, h + j + 3));
+                qn = make_float4(bias_hh_bf16(p, 2 * h + j), bias_hh_bf16(p, 2 * h + j + 1), bias_hh_bf16(p, 2 * h + j + 2),
+                                 bias_hh_bf16(p, 2 * h + j + 3));
             } else {
                 const float *qv = q_slot(p, q) + static_cast<size_t>(b) * h3 + j;
                 qr = ld_agent_f4(qv);
@@ -569,7 +586,7 @@ __device__ __forceinline__ void update(const Params &p, const Ctx &c, int q, con
                 sp = p.S_init ? *reinterpret_cast<const float4 *>(p.S_init + static_cast<size_t>(b) * h + j)
                               : make_float4(0.f, 0.f, 0.f, 0.f);
             else
-                sp = *reinterpret_cast<const float4 *>(p.S_buf + static_cast<size_t>(b) * h + j);
+                sp = ld_f4(p.S_buf + static_cast<size_t>(b) * h + j);
             const float g3[3][4] = {{gr.x, gr.y, gr.z, gr.w}, {gz.x, gz.y, gz.z, gz.w}, {gn.x, gn.y, gn.z, gn.w}};
             const float q3[3][4] = {{qr.x, qr.y, qr.z, qr.w}, {qz.x, qz.y, qz.z, qz.w}, {qn.x, qn.y, qn.z, qn.w}};
             const float s4[4] = {sp.x, sp.y, sp.z, sp.w};
@@ -669,7 +686,7 @@ __device__ __forceinline__ void dots_small(const Params &p, int blk, int q, uint
         {
             int b = 16 * (bt0 + (wave & 1)) + row;
             b = b < p.B ? b : p.B - 1;
-            ah = *reinterpret_cast<const float4 *>(p.A_H + (static_cast<size_t>(b) * p.K + (q > 0 ? q : 0)) * r +
+            ah = ld_f4(p.A_H + (static_cast<size_t>(b) * p.K + (q > 0 ? q : 0)) * r +
                                                    (urows ? m : 0));
         }
         if (bt0 == 0)
@@ -735,8 +752,8 @@ __device__ __forceinline__ void dots_small(const Params &p, int blk, int q, uint
                     st_agent_u64(dst, pack4_bf16(hi[0], hi[1], hi[2], hi[3]));
                 } else {
                     const int mq = m - r;
-                    const float4 v = make_float4(sum[0] + bias_hh(p, mq), sum[1] + bias_hh(p, mq + 1),
-                                                 sum[2] + bias_hh(p, mq + 2), sum[3] + bias_hh(p, mq + 3));
+                    const float4 v = make_float4(sum[0] + bias_hh_bf16(p, mq), sum[1] + bias_hh_bf16(p, mq + 1),
+                                                 sum[2] + bias_hh_bf16(p, mq + 2), sum[3] + bias_hh_bf16(p, mq + 3));
                     st_agent_f4(q_slot(p, q + 1) + static_cast<size_t>(b) * h3 + mq, v);
                 }
             }
@@ -871,7 +888,7 @@ __device__ __forceinline__ void dots_2d(const Params &p, int blk, int nblk, int 
                     continue;
                 if (m < r) {
                     const float4 ah =
-                        *reinterpret_cast<const float4 *>(p.A_H + (static_cast<size_t>(b) * p.K + q) * r + m);
+                        ld_f4(p.A_H + (static_cast<size_t>(b) * p.K + q) * r + m);
                     const float a4[4] = {ah.x + acc[bt][0], ah.y + acc[bt][1], ah.z + acc[bt][2], ah.w + acc[bt][3]};
                     float u4[4];
                     uint32_t hi[4];
@@ -889,8 +906,8 @@ __device__ __forceinline__ void dots_2d(const Params &p, int blk, int nblk, int 
                     st_agent_u64(dst, pack4_bf16(hi[0], hi[1], hi[2], hi[3]));
                 } else {
                     const int mq = m - r;
-                    const float4 v = make_float4(acc[bt][0] + bias_hh(p, mq), acc[bt][1] + bias_hh(p, mq + 1),
-                                                 acc[bt][2] + bias_hh(p, mq + 2), acc[bt][3] + bias_hh(p, mq + 3));
+                    const float4 v = make_float4(acc[bt][0] + bias_hh_bf16(p, mq), acc[bt][1] + bias_hh_bf16(p, mq + 1),
+                                                 acc[bt][2] + bias_hh_bf16(p, mq + 2), acc[bt][3] + bias_hh_bf16(p, mq + 3));
                     st_agent_f4(q_slot(p, q + 1) + static_cast<size_t>(b) * h3 + mq, v);
                 }
             }

@@ -625,7 +625,8 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                     // another thread, which may be writing it)
                     sp[e] = (q == 0) ? state_prev(p, 0, b, j) : (i < ne ? S_lds[bb * h + j] : 0.f);
                     if (p.P) {
-                        const float *prow = p.P + static_cast<size_t>(tokl[bb]) * h3;
+                        // (global loads: as flat loads they would also hold up the LDS reads)
+                        const auto *prow = gmem(p.P + static_cast<size_t>(tokl[bb]) * h3);
                         gv[e][0] = prow[j];
                         gv[e][1] = prow[h + j];
                         gv[e][2] = prow[2 * h + j];
@@ -663,7 +664,7 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                         const float sn = (1.f - zg) * ng + zg * sp[e];
                         S_lds[bb * h + j] = sn;  // each thread reads only the entries it writes
                         if (blk == 0 && p.S_out)
-                            p.S_out[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
+                            gmem(p.S_out)[(static_cast<size_t>(b) * p.K + q) * h + j] = sn;
                     }
                 }
             };
@@ -751,7 +752,7 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                             xst(&p.u_buf[static_cast<size_t>(b) * r + m], u);
                         }
                         if (p.u_out)
-                            p.u_out[(static_cast<size_t>(b) * p.K + q) * r + m] = u;
+                            gmem(p.u_out)[(static_cast<size_t>(b) * p.K + q) * r + m] = u;
                     } else {
                         const float bias =
                             cached ? ac[(wave * rpw + k) * p.K * BC] : (p.b_hh ? WT16<WT>::one(p.b_hh, m - r) : 0.f);

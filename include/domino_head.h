@@ -55,7 +55,9 @@ extern "C" {
 #define DOMINO_FLAG_BAD_TOKEN 1u      /* a last_tok or used teacher id was outside [0, V) */
 #define DOMINO_FLAG_SYNC_TIMEOUT 2u   /* a grid barrier spin limit ran out; outputs invalid */
 
-/* ---- config.flags bits (execution strategy; results do not depend on them) ---- */
+/* ---- config.flags bits (execution strategy).  For B <= 8 every launch gives the same bits; for
+ * B > 8 the launches round u to one bf16 matrix-core operand and agree with each other up to the
+ * order of float32 sums (the logits move by at most about 1e-2 against the oracle either way) ---- */
 #define DOMINO_EXEC_AUTO 0u        /* pick per call from B: the persistent launch for B <= 8, and for
                                       8 < B <= 256 where the batched persistent launch is available (see
                                       below); the step launches otherwise */

@@ -9,12 +9,14 @@ Positions 1..K-2 are summarised by the median over positions; the anchor step,
 the first and the last position are listed separately.
 
     python -m causal_draft_correction_amd.phase_trace qwen3_8b_b1 [qwen3_8b_b32 ...] [--json]
-        [--persistent] [--lbase-bf16] [--no-fold]
+        [--persistent] [--lbase-bf16] [--no-fold] [--plain-launch]
 
 --persistent forces the persistent launch where the automatic choice would take
 the step launches (the batched kernel up to B = 256); --lbase-bf16 passes the
 base logits as bfloat16; --no-fold drafts without the folded gate table (the GRU
-input product runs at every step; B <= 8 only).
+input product runs at every step; B <= 8 only); --plain-launch starts the same
+kernel with an ordinary launch instead of a cooperative one (for a process that
+runs while another one that has made cooperative launches on the GPU is alive).
 
 Only this tool loads the instrumented library; it needs a GPU.
 """
@@ -82,7 +84,7 @@ def summarize(t, K, batched, small_dots=False):
     return out
 
 
-def run(names, lib_path=None, persistent=False, lbase_bf16=False, fold=True):
+def run(names, lib_path=None, persistent=False, lbase_bf16=False, fold=True, plain_launch=False):
     sys.path.insert(0, ROOT)
     import torch
 
@@ -99,8 +101,9 @@ def run(names, lib_path=None, persistent=False, lbase_bf16=False, fold=True):
         wl = ds.WORKLOADS[name]
         sh = wl.shape
         w, inp = ds.make_workload(name)
+        mode = (dca.EXEC_PERSISTENT if persistent else dca.EXEC_AUTO) | (dca.EXEC_PLAIN_LAUNCH if plain_launch else 0)
         head = dca.DominoHead(dca.head_weights_to_device(w), K=sh.K, max_batch=wl.B, fold_embedding=fold,
-                              exec_mode=dca.EXEC_PERSISTENT if persistent else dca.EXEC_AUTO, lbase_bf16=lbase_bf16)
+                              exec_mode=mode, lbase_bf16=lbase_bf16)
         info = head.exec_info(wl.B)
         if not (info["persistent"] and info["w2_resident"]):
             raise SystemExit("%s does not take a resident persistent launch (%s)" % (name, info))
@@ -155,8 +158,10 @@ def main():
     ap.add_argument("--persistent", action="store_true")
     ap.add_argument("--lbase-bf16", action="store_true")
     ap.add_argument("--no-fold", action="store_true")
+    ap.add_argument("--plain-launch", action="store_true")
     args = ap.parse_args()
-    res = run(args.workloads, persistent=args.persistent, lbase_bf16=args.lbase_bf16, fold=not args.no_fold)
+    res = run(args.workloads, persistent=args.persistent, lbase_bf16=args.lbase_bf16, fold=not args.no_fold,
+              plain_launch=args.plain_launch)
     for r in res.values():
         print(json.dumps(r) if args.json else to_markdown(r) + "\n", flush=True)
 

@@ -77,7 +77,12 @@ extern "C" {
                                       guarantees that no other kernel that waits for other work (in
                                       particular no other persistent draft) runs on the device at the
                                       same time; otherwise the bounded waits time out and the call
-                                      reports DOMINO_FLAG_SYNC_TIMEOUT */
+                                      reports DOMINO_FLAG_SYNC_TIMEOUT.  A process that needs the
+                                      persistent launch while another process that has made
+                                      cooperative launches on the same GPU is alive sets this flag:
+                                      the HIP runtime refuses that second process's cooperative
+                                      launches (the draft returns DOMINO_EHIP, "the operation cannot
+                                      be performed in the present state") */
 
 #define DOMINO_EXEC_POSITION_BATCHED 32u /* with a teacher: take the step launches even for B <= 8.  With
                                       a teacher the states of all positions follow from the given

@@ -2,7 +2,10 @@
 tracer reports for the resident B = 1 kernel and the batched kernel cover each
 position, and the instrumented library drafts the same tokens as the product
 library.  Runs the tracer in a child process (it loads the instrumented library in
-place of the product one)."""
+place of the product one).  The child starts its kernels with ordinary launches: while
+this test process, which has made cooperative launches, is alive, a cooperative launch
+from another process on the same GPU is refused (hipErrorIllegalState).  Its grid is one
+block per compute unit and this process is idle meanwhile, so every block is resident."""
 import json
 import os
 import subprocess
@@ -32,11 +35,12 @@ sys.path.insert(0, %(root)r)
 from causal_draft_correction_amd import phase_trace
 import causal_draft_correction_amd as dca
 import domino_synth as ds
-res = phase_trace.run([%(wl)r], persistent=True)
+res = phase_trace.run([%(wl)r], persistent=True, plain_launch=True)
 r = res[%(wl)r]
 # the instrumented library drafts like the product one: compare with the oracle's first token
 w, inp = ds.make_workload(%(wl)r)
-head = dca.DominoHead(dca.head_weights_to_device(w), K=w.shape.K, max_batch=inp.H.shape[0], fold_embedding=True)
+head = dca.DominoHead(dca.head_weights_to_device(w), K=w.shape.K, max_batch=inp.H.shape[0], fold_embedding=True,
+                      exec_mode=dca.EXEC_PLAIN_LAUNCH)
 out = head.draft(dca.device_tensor(inp.H), dca.device_tensor(inp.L_base), dca.device_tensor(inp.last_tok))
 torch.cuda.synchronize()
 r["tokens0"] = out["tokens"][:, 0].cpu().numpy().tolist()

@@ -730,6 +730,8 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
 #pragma unroll
                 for (int j = 0; j < RG; ++j)
                     dot[j] = wave_sum(acc[j]);
+                if (k0 == 0 && bb == 0)
+                    DH_TRACE(tslot + 5);
 #pragma unroll
                 for (int j = 0; j < RG; ++j) {
                     const int k = k0 + j, m = m0 + k * mstep;
@@ -759,6 +761,8 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                         xst(&qn_all[static_cast<size_t>(b) * h3 + (m - r)], dot[j] + bias);
                     }
                 }
+                if (k0 == 0 && bb == 0)
+                    DH_TRACE(tslot + 6);
             }
         }
     }

@@ -56,6 +56,13 @@
 #ifndef RB_MARK
 #define RB_MARK(slot) ((void)(slot))
 #endif
+// and RB_GMARK(i) to note the time of point i (< 32) of the W2 phase's groups (after
+// group g's wait: 2 g, after its products and epilogue: 2 g + 1), which RB_GFLUSH(pos,
+// n) records once the phase's copies are complete
+#ifndef RB_GMARK
+#define RB_GMARK(i) ((void)(i))
+#define RB_GFLUSH(pos, n) ((void)(pos), (void)(n))
+#endif
 
 namespace DH_NS {
 namespace rbk {
@@ -109,11 +116,15 @@ __device__ inline void st_agent_f4(float *p, float4 v)
 __device__ inline void copy_lds4(const void *g, void *lds) { __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 4, 0, 0); }
 
 // the same through a buffer resource (16 bytes at byte offset voff + soff, voff per lane and
-// soff uniform; past the records: zeros)
+// soff uniform; past the records: zeros).  CP: the load's cache-policy bits
+template <int CP = 0>
 __device__ inline void copy_lds16_buf(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff, uint32_t soff = 0)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, static_cast<int>(soff), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, static_cast<int>(soff), 0, CP);
 }
+// cache policy of the L_base copies: non-temporal (each value is read once), which
+// measured a little faster than the default policy
+constexpr int CP_STREAM = 2;
 
 // Buffer resource over `bytes` bytes from `base` (loads past the end read 0).  Copies and
 // loads through it keep the base in scalar registers and take a 32-bit per-lane offset,
@@ -243,7 +254,7 @@ __device__ __forceinline__ void lb_issue(const Params &p, const Ctx &c, const Lb
             static_cast<int>(static_cast<uint32_t>(left > 0xFFFFFFFFll ? 0xFFFFFFFFll : left)), 0x00020000);
 #pragma unroll
         for (int jj = 0; jj < C::NLD; ++jj)
-            copy_lds16_buf(rs, buf + 64 * (wave * C::NLD + jj), lo.off[jj]);
+            copy_lds16_buf<CP_STREAM>(rs, buf + 64 * (wave * C::NLD + jj), lo.off[jj]);
         return;
     }
     constexpr int VPC = 16 / C::EL;  // values per 16-byte chunk
@@ -316,7 +327,8 @@ __device__ inline float4 lb_read(const uint4 *buf, int row, int t, int k)
 
 // Products and epilogue of group g for this wave: result lane l holds vocabulary
 // rows 16 t + 4 (l / 16) + i (i = 0..3) of tile t = wave + NWAVE j for batch row
-// 16 g + l % 16.  The lane keeps the first of its largest values (a NaN above every
+// 16 g + l % 16.  The accumulators start at the lane's L_base values, so the products
+// add onto them.  The lane keeps the first of its largest values (a NaN above every
 // number, the first NaN kept; -0 == +0 by the float compare); the wave's key for
 // each of the group's batch rows goes to kr[wave][0..15].
 template <bool LB16, bool ST>
@@ -328,8 +340,10 @@ __device__ __forceinline__ void w2_group(const Params &p, const Ctx &c, const W2
     const int row = lane & 15, k = lane >> 4;
     f32x4_t acc[RT];
 #pragma unroll
-    for (int j = 0; j < RT; ++j)
-        acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < RT; ++j) {
+        const float4 lb = lb_read<LB16>(L, row, wave + NWAVE * j, k);
+        acc[j] = f32x4_t{lb.x, lb.y, lb.z, lb.w};
+    }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
         const uint4 uh = U[kk * 64 + lane];
@@ -347,13 +361,11 @@ __device__ __forceinline__ void w2_group(const Params &p, const Ctx &c, const W2
 #pragma unroll
     for (int j = 0; j < RT; ++j) {
         const int t = wave + NWAVE * j;
-        const float4 lb = lb_read<LB16>(L, row, t, k);
-        const float lv[4] = {lb.x, lb.y, lb.z, lb.w};
         // tiles wholly inside the block's range skip the per-value bound (uniform)
         if (16 * (t + 1) <= c.n) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float v = acc[j][i] + lv[i];
+                const float v = acc[j][i];
                 if constexpr (ST) {
                     if (b < p.B)
                         lf[16 * t + 4 * k + i] = v;
@@ -365,7 +377,7 @@ __device__ __forceinline__ void w2_group(const Params &p, const Ctx &c, const W2
         } else if (16 * t < c.n) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float v = acc[j][i] + lv[i];
+                const float v = acc[j][i];
                 const int vr = 16 * t + 4 * k + i;
                 const bool ok = vr < c.n;
                 if constexpr (ST) {
@@ -432,18 +444,19 @@ __device__ __forceinline__ void w2_phase(const Params &p, const Ctx &c, const W2
         else
             wait_vm<C::NLD>();
         bare_barrier();
+        RB_GMARK(2 * g);
         if (g >= 1)
             fold(g - 1);
         u_issue(p, pos, g + 1, Un);
         lb_issue<LB16, FAST>(p, c, lo, pos, g + 2, Ln2);
         w2_group<LB16, ST>(p, c, res, pos, g, Lc, Uc, kred + (g & 1) * NWAVE * 16);
+        RB_GMARK(2 * g + 1);
     };
     // L_base groups 0 and 1 were issued by w2_prefetch
     u_issue(p, pos, 0, uA);
     // group g uses L_base buffer g % 3 and u buffer g % 2
 #pragma unroll 1
     for (int g0 = 0; g0 < ngr; g0 += 6) {
-        RB_MARK(64 * pos + 8 + g0);
         iter(g0, lbA, lbC, uA, uB);
         if (g0 + 1 >= ngr)
             break;
@@ -467,6 +480,7 @@ __device__ __forceinline__ void w2_phase(const Params &p, const Ctx &c, const W2
     // which the update of the next position waits for
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    RB_GFLUSH(pos, 2 * ngr);
     for (int b = threadIdx.x; b < p.B; b += NT) {
         const uint64_t m = lkey[b];
         st_agent_u64(&p.bkeys[static_cast<size_t>(b) * gridDim.x + blockIdx.x],
@@ -854,18 +868,25 @@ __device__ __forceinline__ void dots_2d(const Params &p, int blk, int nblk, int 
             if (active && s < NS)
                 compute(cur, wc);
         };
+        const bool first = job == blk;
         issue(0, ring0, wa[0]);
         issue(1, ring1, wa[1]);
         issue(2, ring2, wa[2]);
+        if (first)
+            RB_MARK(64 * (q > 0 ? q : 0) + 40);
 #pragma unroll 1
         for (int s = 0; s < NS; s += 4) {
             step(s, ring0, ring3, wa[0], wa[3]);
+            if (first && s == 0)
+                RB_MARK(64 * (q > 0 ? q : 0) + 41);
             step(s + 1, ring1, ring0, wa[1], wa[0]);
             step(s + 2, ring2, ring1, wa[2], wa[1]);
             step(s + 3, ring3, ring2, wa[3], wa[2]);
         }
         wait_vm<0>();
         bare_barrier();
+        if (first)
+            RB_MARK(64 * (q > 0 ? q : 0) + 42);
         if (ks == 1) {
 #pragma unroll
             for (int bt = 0; bt < BJ; ++bt)
@@ -921,6 +942,8 @@ __device__ __forceinline__ void dots_2d(const Params &p, int blk, int nblk, int 
         }
         // the exchange buffer is the first ring buffer of the next job
         __syncthreads();
+        if (first)
+            RB_MARK(64 * (q > 0 ? q : 0) + 43);
     }
 }
 

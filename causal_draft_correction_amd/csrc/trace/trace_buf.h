@@ -18,3 +18,11 @@
         if (threadIdx.x == 0 && blockIdx.x < TRACE_BLOCKS && s_ >= 0 && s_ < TRACE_SLOTS)                \
             buf[blockIdx.x * TRACE_SLOTS + s_] = __builtin_amdgcn_s_memrealtime();                       \
     } while (0)
+
+// the same with a given value (a time noted earlier)
+#define TRACE_PUT(buf, bias, slot, value)                                                                \
+    do {                                                                                                 \
+        const int s_ = (slot) + (bias);                                                                  \
+        if (threadIdx.x == 0 && blockIdx.x < TRACE_BLOCKS && s_ >= 0 && s_ < TRACE_SLOTS)                \
+            buf[blockIdx.x * TRACE_SLOTS + s_] = (value);                                                \
+    } while (0)

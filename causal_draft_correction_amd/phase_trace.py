@@ -41,6 +41,9 @@ RES_BIAS = 64
 RES_POSITION = [("w2_wait_u", 0, 1), ("w2_products", 2, 4), ("w2_block_key", 4, 5), ("argmax_exchange", 5, 13),
                 ("input_product", 13, 16), ("gru_gates", 16, 18), ("state_sync", 18, 19), ("state_dots", 19, 20), ("u_hop", 20, 32),
                 ("position", 0, 32)]
+# wave 0's first group of state rows (its u row) in the state dots: products and
+# sums, the stores, then the other rows
+RES_DOTS = [("dots_first_group", 19, 21), ("dots_first_stores", 21, 22), ("dots_other_rows", 22, 20)]
 RES_PROLOGUE = [("slice_and_loads_issued", 511, 508), ("anchor_step", -16, -12), ("prologue", 511, 509)]
 
 # batched kernel (k_persistent_rb): hook slot is the column; marks relative to 64 * position
@@ -48,10 +51,13 @@ RB_POSITION = [("wait_u", 0, 7), ("w2", 7, 1), ("resolve", 1, 2), ("gru_update",
                ("state_dots", 4, 5), ("to_next_position", 5, 64), ("position", 0, 64)]
 RB_PROLOGUE = [("w2_slice_load", 1019, 1023), ("anchor_update", 1023, 1022), ("grid_barrier", 1022, 1021),
                ("anchor_dots", 1021, 1020), ("prologue", 1019, 1020)]
-# the state dots of up to four batch tiles (B <= 64) mark their first round at slots
-# 64 q + 40..43 of the state q they compute, i.e. 64 + 40.. after the position before it
-RB_SMALL_DOTS = [("dots_copies_issued", 4, 64 + 40), ("dots_copies_landed", 64 + 40, 64 + 41),
-                 ("dots_products", 64 + 41, 64 + 42), ("dots_reduce_store", 64 + 42, 64 + 43)]
+# the state dots mark the first round (B <= 64) or the first job (B > 64) of a block at
+# slots 64 q + 40..43 of the state q they compute, i.e. 64 + 40.. after the position
+# before it.  B <= 64: copies issued, landed, products, reduction and stores; B > 64:
+# the first three stages issued, the first stage landed and multiplied, the other
+# stages, reduction and stores (with the arrival count)
+RB_DOTS = [("dots_copies_issued", 4, 64 + 40), ("dots_copies_landed", 64 + 40, 64 + 41),
+           ("dots_products", 64 + 41, 64 + 42), ("dots_reduce_store", 64 + 42, 64 + 43)]
 
 
 def _span(t, a, b):
@@ -59,17 +65,40 @@ def _span(t, a, b):
     return float(np.median(d)), float(d.max())
 
 
-def summarize(t, K, batched, small_dots=False):
+def w2_groups(t, K, ngr):
+    """Batched kernel: the W2 phase per 16-row group (positions 1..K-2, median over
+    positions and blocks, in us): the wait for a group's copies (from the previous
+    group's end, or from the end of the wait for u) and its products and epilogue,
+    for the first group, the median of the middle ones and the last, and the time
+    from the last group's end to the phase's end."""
+    mids = range(1, K - 1)
+    if not len(mids) or ngr < 1:
+        return {}
+
+    def span(a, b):
+        return float(np.median(np.concatenate([(t[:, 64 * p + b] - t[:, 64 * p + a]) for p in mids]))) * TICK_US
+
+    wait = [span(7 if g == 0 else 9 + 2 * (g - 1), 8 + 2 * g) for g in range(ngr)]
+    work = [span(8 + 2 * g, 9 + 2 * g) for g in range(ngr)]
+    out = {"first_wait": wait[0], "first_group": work[0], "last_wait": wait[-1], "last_group": work[-1],
+           "after_last_group": span(9 + 2 * (ngr - 1), 1)}
+    if ngr > 2:
+        out["middle_wait"] = float(np.median(wait[1:-1]))
+        out["middle_group"] = float(np.median(work[1:-1]))
+    return {k: [round(v, 2), round(v, 2)] for k, v in out.items()}
+
+
+def summarize(t, K, batched, dots_detail=False):
     """t: [blocks, SLOTS] int64 timestamps of one call.  Returns a dict of phase -> [median, max] us."""
     if batched:
         col = lambda s: s  # noqa: E731
         per, pro, stride, end = RB_POSITION, RB_PROLOGUE, 64, 64 * (K - 1) + 2
-        if small_dots:
-            per = per + RB_SMALL_DOTS
+        if dots_detail:
+            per = per + RB_DOTS
         start = 1019
     else:
         col = lambda s: s + RES_BIAS  # noqa: E731
-        per, pro, stride, end = RES_POSITION, RES_PROLOGUE, 32, 32 * (K - 1) + 13
+        per, pro, stride, end = RES_POSITION + RES_DOTS, RES_PROLOGUE, 32, 32 * (K - 1) + 13
         start = 511
     out = {"kernel_us": round(float((t[:, col(end)].max() - t[:, col(start)].min()) * TICK_US), 1)}
     out["prologue"] = {n: [round(x, 2) for x in _span(t, col(a), col(b))] for n, a, b in pro}
@@ -127,11 +156,16 @@ def run(names, lib_path=None, persistent=False, lbase_bf16=False, fold=True, pla
         r = {"workload": name + (" bf16 L_base" if lbase_bf16 else "") + ("" if fold else " unfolded"), "B": wl.B,
              "kernel": "k_persistent_rb" if batched else "k_persistent_res", "grid": info["grid"],
              "call_us": round(e0.elapsed_time(e1) * 1e3, 1)}
-        # only blocks that compute state dots mark the small dots' rounds
-        nd = (sh.r + 3 * sh.h) // 16 if batched and wl.B <= 64 else 0
+        # only blocks that compute state dots mark their rounds
+        nd = 0
+        if batched:
+            nd = ((sh.r + 3 * sh.h) // 16 if wl.B <= 64 else
+                  min(info["grid"], (sh.r + 3 * sh.h) // 64 * (((wl.B + 15) // 16 + 3) // 4)))
         r.update(summarize(t, sh.K, batched))
+        if batched:
+            r["w2_groups"] = w2_groups(t, sh.K, (wl.B + 15) // 16)
         if nd:
-            r["state_dots_detail"] = summarize(t[:nd], sh.K, batched, small_dots=True)[
+            r["state_dots_detail"] = summarize(t[:nd], sh.K, batched, dots_detail=True)[
                 "positions_1_to_%d_median" % (sh.K - 2)]
             r["state_dots_detail"] = {k: v for k, v in r["state_dots_detail"].items()
                                       if k.startswith("dots_")}

@@ -233,7 +233,10 @@ __device__ __forceinline__ void phase_q_init(const Params &p, int blk, int nblk)
 }
 
 // ---- phase: g = W_ih E[x_q] + b_ih for the GRU step producing S_q (not folded) ------
-template <typename WT>
+// GRW: rows of a wave whose loads go out together (more rows take more registers: the
+// resident persistent kernel, one wave per SIMD, takes 3; the launches that rely on
+// several waves per SIMD take 1)
+template <typename WT, int GRW = 1>
 __device__ __forceinline__ void phase_g(const Params &p, int blk, int nblk, int q, float *smem, const int *atok = nullptr)
 {
     const int h3 = 3 * p.h;
@@ -245,15 +248,60 @@ __device__ __forceinline__ void phase_g(const Params &p, int blk, int nblk, int 
         if (threadIdx.x < nb)
             tok[threadIdx.x] = gru_input_token(p, q, b0 + threadIdx.x, atok);
         __syncthreads();
-        for (int m = blk * NWAVE + wave; m < h3; m += nblk * NWAVE) {
-            const float bias = p.b_ih ? WT16<WT>::one(p.b_ih, m) : 0.f;
+        // the wave's rows m = m0 + i mstep go GRW at a time, and for each batch row the
+        // loads of GCH chunks per lane of all of them (and of the embedding row) are
+        // issued before the first product: one memory round trip per GCH chunks
+        // instead of one per row and unrolled step.  Each row's sum is formed as in
+        // wave_dot (chunks lane, lane + 64, ... in order, then wave_sum), so the
+        // values equal the row-at-a-time ones bit for bit.
+        constexpr int EPC = WT16<WT>::EPC;
+        constexpr int GCH = 4;
+        const int nch = p.d / EPC, mstep = nblk * NWAVE;
+        for (int m0 = blk * NWAVE + wave; m0 < h3; m0 += GRW * mstep) {
+            float bias[GRW];
+#pragma unroll
+            for (int i = 0; i < GRW; ++i) {
+                const int m = m0 + i * mstep;
+                bias[i] = (m < h3 && p.b_ih) ? WT16<WT>::one(p.b_ih, m) : 0.f;
+            }
             for (int bb = 0; bb < nb; ++bb) {
                 const size_t eo = static_cast<size_t>(tok[bb]) * p.d;
-                const float v = bias + wave_dot<WT>(p.W_ih, static_cast<size_t>(m) * p.d, p.d, [&](int e, float *x) {
-                    WT16<WT>::unpack(ld16<WT>(p.E, eo + e), x);
-                });
-                if (lane == 0)
-                    xst(&p.g_buf[static_cast<size_t>(b0 + bb) * h3 + m], v);
+                float acc[GRW];
+#pragma unroll
+                for (int i = 0; i < GRW; ++i)
+                    acc[i] = 0.f;
+                for (int c0 = 0; c0 < nch; c0 += 64 * GCH) {
+                    uint4 ev[GCH], wv[GRW][GCH];
+#pragma unroll
+                    for (int k = 0; k < GCH; ++k) {
+                        const int c = c0 + k * 64 + lane;
+                        const int cc = c < nch ? c : 0;  // past the row: chunk 0, not multiplied
+                        ev[k] = ld16<WT>(p.E, eo + static_cast<size_t>(cc) * EPC);
+#pragma unroll
+                        for (int i = 0; i < GRW; ++i) {
+                            const int m = m0 + i * mstep;
+                            const int mc = m < h3 ? m : m0;
+                            wv[i][k] = ld16<WT>(p.W_ih, static_cast<size_t>(mc) * p.d + static_cast<size_t>(cc) * EPC);
+                        }
+                    }
+#pragma unroll
+                    for (int k = 0; k < GCH; ++k) {
+                        if (c0 + k * 64 + lane < nch) {
+                            float x[EPC];
+                            WT16<WT>::unpack(ev[k], x);
+#pragma unroll
+                            for (int i = 0; i < GRW; ++i)
+                                acc[i] = dot_chunk<WT>(wv[i][k], x, acc[i]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < GRW; ++i) {
+                    const int m = m0 + i * mstep;
+                    const float v = bias[i] + wave_sum(acc[i]);
+                    if (lane == 0 && m < h3)
+                        xst(&p.g_buf[static_cast<size_t>(b0 + bb) * h3 + m], v);
+                }
             }
         }
     }

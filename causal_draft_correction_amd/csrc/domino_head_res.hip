@@ -52,7 +52,7 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
         phase_q_init<bf16s>(p, blk, nblk);
         lbase_to_lds(p, blk, nblk, 0, smem);
         if (!p.P)
-            phase_g<bf16s>(p, blk, nblk, 0, smem);
+            phase_g<bf16s, 3>(p, blk, nblk, 0, smem);
         // the slice load overlaps the first barrier
         w2_resident_load<RT, KS>(p, blk, nblk, res, tl);
         DH_TRACE(508);
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
         DH_TRACE(pos * 32 + 13);
         if (pos + 1 < pl.K) {
             if (!pl.P) {
-                phase_g<bf16s>(pl, blk, nblk, pos + 1, smem, atok);
+                phase_g<bf16s, 3>(pl, blk, nblk, pos + 1, smem, atok);
                 if (!grid_sync(pl.bar, gen, pl.spin_limit, pl.flags))
                     return;
             }

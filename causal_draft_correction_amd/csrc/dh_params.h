@@ -29,6 +29,8 @@ struct Params {
                           // row stride (matrix-core state dots), or nullptr
     int ldw;              // row stride of s_hl and wst in elements
     float *g_buf;    // [maxB, 3h]    W_ih E[x] + b_ih (when not folded)
+    uint64_t *gtag;  // [min(maxB, BC), 3h] resident launch, not folded: g as words (tag << 32) |
+                     // float bits, which the state phase polls instead of a grid barrier; or nullptr
     uint64_t *keys;  // [K, NG, maxB] partial argmax keys
     uint64_t *bkeys; // batched resident launch: [maxB, grid] argmax key word of every block for every
                      // batch row, generation-tagged

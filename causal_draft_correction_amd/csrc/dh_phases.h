@@ -236,8 +236,10 @@ __device__ __forceinline__ void phase_q_init(const Params &p, int blk, int nblk)
 // GRW: rows of a wave whose loads go out together (more rows take more registers: the
 // resident persistent kernel, one wave per SIMD, takes 3; the launches that rely on
 // several waves per SIMD take 1)
+// With p.gtag each value goes out as a word carrying `tag` (see phase_state).
 template <typename WT, int GRW = 1>
-__device__ __forceinline__ void phase_g(const Params &p, int blk, int nblk, int q, float *smem, const int *atok = nullptr)
+__device__ __forceinline__ void phase_g(const Params &p, int blk, int nblk, int q, float *smem, const int *atok = nullptr,
+                                        unsigned tag = 0)
 {
     const int h3 = 3 * p.h;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -299,8 +301,15 @@ __device__ __forceinline__ void phase_g(const Params &p, int blk, int nblk, int 
                 for (int i = 0; i < GRW; ++i) {
                     const int m = m0 + i * mstep;
                     const float v = bias[i] + wave_sum(acc[i]);
-                    if (lane == 0 && m < h3)
-                        xst(&p.g_buf[static_cast<size_t>(b0 + bb) * h3 + m], v);
+                    if (lane == 0 && m < h3) {
+                        const size_t o = static_cast<size_t>(b0 + bb) * h3 + m;
+                        if (p.gtag)
+                            __hip_atomic_store(gmem(&p.gtag[o]),
+                                               (static_cast<uint64_t>(tag) << 32) | __float_as_uint(v),
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        else
+                            xst(&p.g_buf[o], v);
+                    }
                 }
             }
         }
@@ -664,6 +673,7 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
             auto batch = [&](auto qmode, int i0) {
                 constexpr int QM = decltype(qmode)::value;
                 float gv[SP_EL][3], qv[SP_EL][3], sp[SP_EL];
+                uint64_t gt[SP_EL][3];  // tagged g words (p.gtag)
 #pragma unroll
                 for (int e = 0; e < SP_EL; ++e) {
                     const int i = i0 + e * NT;
@@ -678,6 +688,11 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                         gv[e][0] = prow[j];
                         gv[e][1] = prow[h + j];
                         gv[e][2] = prow[2 * h + j];
+                    } else if (p.gtag) {
+                        const uint64_t *g = p.gtag + static_cast<size_t>(b) * h3;
+                        gt[e][0] = ld_agent_u64(&g[j]);
+                        gt[e][1] = ld_agent_u64(&g[h + j]);
+                        gt[e][2] = ld_agent_u64(&g[2 * h + j]);
                     } else {
                         const float *g = p.g_buf + static_cast<size_t>(b) * h3;
                         gv[e][0] = xld(&g[j]);
@@ -699,6 +714,39 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                         qv[e][1] = xld(&qq[h + j]);
                         qv[e][2] = xld(&qq[2 * h + j]);
                     }
+                }
+                if (!p.P && p.gtag) {
+                    // the g words of this step carry `tag` once their producers wrote them:
+                    // while any does not, re-read all of them (one round trip per round)
+                    unsigned spins = 0;
+                    for (;;) {
+                        uint32_t stale = 0;  // bit 3 e + c: word c of element e
+#pragma unroll
+                        for (int x = 0; x < 3 * SP_EL; ++x)
+                            stale |= static_cast<uint32_t>(i0 + (x / 3) * NT < ne &&
+                                                           static_cast<unsigned>(gt[x / 3][x % 3] >> 32) != tag)
+                                     << x;
+                        if (!stale)
+                            break;
+                        if (++spins > p.spin_limit) {
+                            __hip_atomic_fetch_or(gmem(p.flags), 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                        // (short loops with constant trips: the compiler unrolls them by itself)
+                        for (int e = 0; e < SP_EL; ++e) {
+                            const int i = i0 + e * NT;
+                            const int ic = i < ne ? i : 0;
+                            const uint64_t *g = p.gtag + static_cast<size_t>(b0 + ic / h) * h3 + ic % h;
+                            for (int c = 0; c < 3; ++c)
+                                gt[e][c] = ld_agent_u64(&g[c * h]);
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < SP_EL; ++e)
+#pragma unroll
+                        for (int c = 0; c < 3; ++c)
+                            gv[e][c] = __uint_as_float(static_cast<uint32_t>(gt[e][c]));
                 }
 #pragma unroll
                 for (int e = 0; e < SP_EL; ++e) {

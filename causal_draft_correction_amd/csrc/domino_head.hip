@@ -376,8 +376,8 @@ constexpr int W2_STEP_ROWS = 128;  // vocabulary rows per block in stepwise W2 l
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, u_all, utag, s_hl, q_buf, g_buf, P, M, mk_tmp, wst, bkeys, uop,
-        rbs, ucnt, total;
+    size_t bar, asy, flags, keys, A_H, S_buf, u_buf, u_all, utag, s_hl, q_buf, g_buf, gtag, P, M, mk_tmp, wst, bkeys,
+        uop, rbs, ucnt, total;
 };
 
 // Packed state-dot rows for the matrix-core state launches (bf16 heads): the rows of
@@ -399,6 +399,8 @@ int rb_ldp(const domino_head_config &c) { return c.h + 64; }
 // zero-state GRU rows of one chunk, plus W1_S as float32)
 constexpr int MARKOV_CHUNK = 8192;
 int markov_chunk(const domino_head_config &c) { return std::min(c.V, MARKOV_CHUNK); }
+
+size_t gtag_words(const domino_head_config &c) { return static_cast<size_t>(std::min(c.max_batch, BC)) * 3 * c.h; }
 
 Layout layout_of(const domino_head_config &c)
 {
@@ -429,6 +431,9 @@ Layout layout_of(const domino_head_config &c)
     off = align_up(off + sizeof(float) * 2 * static_cast<size_t>(c.max_batch) * 3 * c.h);
     L.g_buf = off;
     off = align_up(off + sizeof(float) * static_cast<size_t>(c.max_batch) * 3 * c.h);
+    L.gtag = off;  // tagged g words of the resident launch (not folded)
+    if (!(c.flags & DOMINO_FOLD_EMBED))
+        off = align_up(off + sizeof(uint64_t) * gtag_words(c));
     L.P = off;
     if (c.flags & DOMINO_FOLD_EMBED)
         off = align_up(off + sizeof(float) * static_cast<size_t>(c.V) * 3 * c.h);
@@ -875,6 +880,12 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
                            reinterpret_cast<uint32_t *>(hd->ws + hd->L.utag), 2 * c.max_batch * c.r,
                            reinterpret_cast<unsigned *>(hd->ws + hd->L.flags));
         HIP_TRY(hipGetLastError(), "launch k_clear_state");
+        if (hd->L.P > hd->L.gtag) {
+            // g words: no tag of the restarted generations may be found in them
+            hipLaunchKernelGGL(k_clear_words, dim3(64), dim3(256), 0, st,
+                               reinterpret_cast<uint64_t *>(hd->ws + hd->L.gtag), gtag_words(c));
+            HIP_TRY(hipGetLastError(), "launch k_clear_words");
+        }
         if (hd->L.uop > hd->L.bkeys) {
             // with the barrier generations restarting at 0, no old argmax word may keep its tag
             hipLaunchKernelGGL(k_clear_words, dim3(256), dim3(256), 0, st,
@@ -887,6 +898,8 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
     Params p = make_params(hd, B, H, L_base, last_tok, teacher, S_init, tokens, L_final, S_out, u_out, persistent);
     if (resident && !markov)
         p.utag = reinterpret_cast<uint32_t *>(hd->ws + hd->L.utag);
+    if (resident && !markov && !(c.flags & DOMINO_FOLD_EMBED))
+        p.gtag = reinterpret_cast<uint64_t *>(hd->ws + hd->L.gtag);
     hd->last_stream = st;
     if (batched) {
         // A_H of every position on the matrix cores, then the one persistent launch

@@ -51,8 +51,9 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
         phase_ah<bf16s>(p, blk, nblk, smem);
         phase_q_init<bf16s>(p, blk, nblk);
         lbase_to_lds(p, blk, nblk, 0, smem);
+        // (g words of the anchor step: tagged for the state phase after the barrier below)
         if (!p.P)
-            phase_g<bf16s, 3>(p, blk, nblk, 0, smem);
+            phase_g<bf16s, 3>(p, blk, nblk, 0, smem, nullptr, gen + 2);
         // the slice load overlaps the first barrier
         w2_resident_load<RT, KS>(p, blk, nblk, res, tl);
         DH_TRACE(508);
@@ -85,10 +86,14 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
         if (blk == 0 && threadIdx.x < pl.B)
             pl.tokens[static_cast<size_t>(threadIdx.x) * pl.K + pos] = bad[threadIdx.x] ? -1 : atok[threadIdx.x];
         DH_TRACE(pos * 32 + 13);
+        DH_TRACE(pos * 32 + 15);  // (back to back: the cost of one mark)
         if (pos + 1 < pl.K) {
             if (!pl.P) {
-                phase_g<bf16s, 3>(pl, blk, nblk, pos + 1, smem, atok);
-                if (!grid_sync(pl.bar, gen, pl.spin_limit, pl.flags))
+                // the input product goes out in tagged words, which the state phase
+                // polls: no grid barrier
+                phase_g<bf16s, 3>(pl, blk, nblk, pos + 1, smem, atok, gen + 1);
+                DH_TRACE(pos * 32 + 14);
+                if (!pl.gtag && !grid_sync(pl.bar, gen, pl.spin_limit, pl.flags))
                     return;
             }
             // q of this step is visible only after the argmax barrier: its loads go out

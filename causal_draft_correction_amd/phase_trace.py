@@ -43,7 +43,10 @@ RES_POSITION = [("w2_wait_u", 0, 1), ("w2_products", 2, 4), ("w2_block_key", 4, 
                 ("position", 0, 32)]
 # wave 0's first group of state rows (its u row) in the state dots: products and
 # sums, the stores, then the other rows
-RES_DOTS = [("dots_first_group", 19, 21), ("dots_first_stores", 21, 22), ("dots_other_rows", 22, 20)]
+RES_DOTS = [("dots_first_group", 19, 21), ("dots_first_stores", 21, 22), ("dots_other_rows", 22, 20),
+            ("mark_cost", 13, 15)]
+# unfolded head: the input product itself and its grid barrier
+RES_UNFOLDED = [("input_product_compute", 13, 14), ("input_product_barrier", 14, 16)]
 RES_PROLOGUE = [("slice_and_loads_issued", 511, 508), ("anchor_step", -16, -12), ("prologue", 511, 509)]
 
 # batched kernel (k_persistent_rb): hook slot is the column; marks relative to 64 * position
@@ -88,7 +91,7 @@ def w2_groups(t, K, ngr):
     return {k: [round(v, 2), round(v, 2)] for k, v in out.items()}
 
 
-def summarize(t, K, batched, dots_detail=False):
+def summarize(t, K, batched, dots_detail=False, unfolded=False):
     """t: [blocks, SLOTS] int64 timestamps of one call.  Returns a dict of phase -> [median, max] us."""
     if batched:
         col = lambda s: s  # noqa: E731
@@ -99,6 +102,8 @@ def summarize(t, K, batched, dots_detail=False):
     else:
         col = lambda s: s + RES_BIAS  # noqa: E731
         per, pro, stride, end = RES_POSITION + RES_DOTS, RES_PROLOGUE, 32, 32 * (K - 1) + 13
+        if unfolded:
+            per = per + RES_UNFOLDED
         start = 511
     out = {"kernel_us": round(float((t[:, col(end)].max() - t[:, col(start)].min()) * TICK_US), 1)}
     out["prologue"] = {n: [round(x, 2) for x in _span(t, col(a), col(b))] for n, a, b in pro}
@@ -161,7 +166,7 @@ def run(names, lib_path=None, persistent=False, lbase_bf16=False, fold=True, pla
         if batched:
             nd = ((sh.r + 3 * sh.h) // 16 if wl.B <= 64 else
                   min(info["grid"], (sh.r + 3 * sh.h) // 64 * (((wl.B + 15) // 16 + 3) // 4)))
-        r.update(summarize(t, sh.K, batched))
+        r.update(summarize(t, sh.K, batched, unfolded=not fold))
         if batched:
             r["w2_groups"] = w2_groups(t, sh.K, (wl.B + 15) // 16)
         if nd:

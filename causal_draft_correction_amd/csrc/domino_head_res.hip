@@ -35,14 +35,18 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
     // state phase runs), never 0, the value cleared words hold
     DH_TRACE(511);
     W2Resident<RT, KS> res;
-    if (NB == 1 && !p.S_init && p.P) {
-        // one batch row, no initial state, folded table: the prologue needs no grid
-        // barrier.  Each wave computes the A_H entries of its own u rows, q_0 is
-        // b_hh, and the W2 slice load is issued after the anchor gate update's
-        // loads, so it overlaps the dot products and the first u exchange
+    if (NB == 1 && !p.S_init && (p.P || p.gtag)) {
+        // one batch row, no initial state, folded table or tagged input-gate words:
+        // the prologue needs no grid barrier.  Each wave computes the A_H entries of
+        // its own u rows, q_0 is b_hh, the anchor step's input part (not folded) goes
+        // out in tagged words that its state phase polls, and the W2 slice load is
+        // issued after the anchor gate update's loads, so it overlaps the dot
+        // products and the first u exchange
         lbase_to_lds(p, blk, nblk, 0, smem);
         state_cache_load<bf16s>(p, blk, nblk, cache, false);
         ah_local_to_cache<bf16s>(p, blk, nblk, cache);
+        if (!p.P)
+            phase_g<bf16s, 3>(p, blk, nblk, 0, smem, nullptr, gen + 1);
         DH_TRACE(508);
         DH_TRACE(510);
         phase_state<bf16s>(p, blk, nblk, 0, smem, S_lds, nullptr, cache, true, nullptr, gen + 1,

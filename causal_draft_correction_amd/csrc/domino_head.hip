@@ -620,9 +620,9 @@ static bool choose_launch(const domino_head *hd, int B, bool *persistent, bool *
     const unsigned fl = hd->cfg.flags;
     *batched = false;
     // the batched persistent launch (8 < B <= 256) is ahead of the step launches at every batch
-    // measured (8B head, K = 16: 485 against 654 us at B = 32, 1044 against 1172 at B = 256)
-    if (!(fl & DOMINO_MARKOV) && B > BC && hd->rb_grid > 0 && B <= dhrb::max_batch() &&
-        !(fl & (DOMINO_EXEC_STEPWISE | DOMINO_EXEC_STREAM_W2))) {
+    // measured (8B head, K = 16: 454 against 668 us at B = 32, 1009 against 1167 at B = 256),
+    // for the recurrent and the Markov head
+    if (B > BC && hd->rb_grid > 0 && B <= dhrb::max_batch() && !(fl & (DOMINO_EXEC_STEPWISE | DOMINO_EXEC_STREAM_W2))) {
         *persistent = *resident = *batched = true;
         return true;
     }
@@ -759,17 +759,18 @@ int domino_head_create(const domino_head_config *cfg, void *workspace, size_t wo
         if (fits)
             hd->res_grid = cus;
     }
-    // batched resident-W2 variant (B > BC): bf16, r = 256, folded table, packed state
-    // rows, one 256-thread block per compute unit with static LDS only
+    // batched resident-W2 variant (B > BC): bf16, r = 256, folded table (or a Markov
+    // head), packed state rows, one 512-thread block per compute unit with static LDS only
     hd->rb_grid = 0;
-    if (cfg->wdtype == DOMINO_BF16 && (cfg->flags & DOMINO_FOLD_EMBED) && !(cfg->flags & DOMINO_MARKOV) &&
+    if (cfg->wdtype == DOMINO_BF16 && (cfg->flags & (DOMINO_FOLD_EMBED | DOMINO_MARKOV)) &&
         packed_state_rows(*cfg) && dhrb::supports(cfg->d, cfg->h, cfg->r, cfg->V, cus)) {
         bool fits = true;
         for (int lb16 = 0; lb16 < 2; ++lb16)
             for (int stl = 0; stl < 2; ++stl) {
                 int per_cu_b = 0;
                 hipError_t eb = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &per_cu_b, dhrb::kernel(lb16 != 0, stl != 0, cfg->V), dhrb::threads(), 0);
+                    &per_cu_b, dhrb::kernel(lb16 != 0, stl != 0, cfg->V, (cfg->flags & DOMINO_MARKOV) != 0),
+                    dhrb::threads(), 0);
                 fits = fits && eb == hipSuccess && per_cu_b >= 1;
             }
         if (fits)
@@ -918,7 +919,7 @@ int domino_head_draft(domino_head_t hd, int32_t B, const void *H, const void *L_
         HIP_TRY(hipLaunchKernel(dhbat::ah_kernel(B, c.K, c.r), dim3(dhbat::ah_grid(B, c.K, c.r)),
                                 dim3(dhbat::threads()), args, 0, st),
                 "launch A_H (matrix cores)");
-        const void *fn = dhrb::kernel(p.lbase_bf16 != 0, L_final != nullptr, c.V);
+        const void *fn = dhrb::kernel(p.lbase_bf16 != 0, L_final != nullptr, c.V, markov);
         if (c.flags & DOMINO_EXEC_PLAIN_LAUNCH)
             HIP_TRY(hipLaunchKernel(fn, dim3(hd->rb_grid), dim3(dhrb::threads()), args, 0, st),
                     "hipLaunchKernel(batched persistent)");

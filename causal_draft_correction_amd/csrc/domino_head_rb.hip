@@ -162,11 +162,20 @@ __device__ inline uint64_t pack4_bf16(uint32_t a, uint32_t b, uint32_t c, uint32
 // The block's share of the work, the same at every position.
 struct Ctx {
     int v0, n;       // vocabulary rows [v0, v0 + n) (v0 a multiple of 16; n may be 0)
-    int c0, c1;      // 4-entry state chunks [c0, c1) of the flat [B, h] index
+    int c0, c1;      // 4-entry chunks [c0, c1) of the flat [B, h] state index (of the flat
+                     // [B, r] u index for a Markov head)
     int rb0, nrows;  // batch rows of those chunks: rb0 .. rb0 + nrows - 1
+    int rc;          // chunks of one batch row (h / 4, or r / 4)
 };
 
-__device__ inline Ctx make_ctx(const Params &p, int blk, int nblk)
+// Blocks that hold chunks of the split into whole 16-chunk runs of nc chunks.
+__host__ __device__ inline int chunk_blocks(int nc, int nblk)
+{
+    const int per = ((nc + nblk - 1) / nblk + 15) & ~15;
+    return (nc + per - 1) / per;
+}
+
+__device__ inline Ctx make_ctx(const Params &p, int blk, int nblk, bool markov)
 {
     Ctx c;
     const long long T = (p.V + 15) / 16;
@@ -176,11 +185,13 @@ __device__ inline Ctx make_ctx(const Params &p, int blk, int nblk)
     if (c.n < 0)
         c.n = 0;
     // whole 16-chunk runs (64 entries: one 128-byte line of each plane) per block
-    const int nc = p.B * p.h / 4, per = ((nc + nblk - 1) / nblk + 15) & ~15;
+    const int e = markov ? p.r : p.h;
+    const int nc = p.B * e / 4, per = ((nc + nblk - 1) / nblk + 15) & ~15;
     c.c0 = blk * per < nc ? blk * per : nc;
     c.c1 = c.c0 + per < nc ? c.c0 + per : nc;
-    c.rb0 = c.c0 * 4 / p.h;
-    c.nrows = c.c1 > c.c0 ? (c.c1 * 4 - 1) / p.h - c.rb0 + 1 : 0;
+    c.rb0 = c.c0 * 4 / e;
+    c.nrows = c.c1 > c.c0 ? (c.c1 * 4 - 1) / e - c.rb0 + 1 : 0;
+    c.rc = e / 4;
     return c;
 }
 
@@ -544,7 +555,7 @@ __device__ __forceinline__ bool resolve(const Params &p, const Ctx &c, int pos, 
         const int tok = m ? static_cast<int>(KEY_IDX_MASK - (m & KEY_IDX_MASK)) : 0;
         rtok[threadIdx.x] = tok;
         const int b = c.rb0 + threadIdx.x;
-        if (b * p.h / 4 >= c.c0)  // this block owns the row's first entry
+        if (b * c.rc >= c.c0)  // this block owns the row's first entry
             p.tokens[static_cast<size_t>(b) * p.K + pos] = row_bad(p, b) ? -1 : tok;
     }
     __syncthreads();
@@ -956,13 +967,57 @@ __device__ __forceinline__ void dots(const Params &p, int blk, int nblk, int q, 
         dots_small(p, blk, q, lbA, lbB, lbC, uA, uB);
 }
 
+// Markov head: u_q = SiLU(A_H[q] + M[x_q]) (the table row of the token before position
+// q) for the block's chunks of the flat [B, r] index, as the W2 phase's bf16 operand
+// (and u_out), then the block counts itself in the position's arrival counter.  rtok:
+// the tokens of position q - 1 of the block's rows.
+__device__ __forceinline__ void markov_phase(const Params &p, const Ctx &c, int q, const int *rtok)
+{
+    const int r = p.r;
+    for (int cc = c.c0 + static_cast<int>(threadIdx.x); cc < c.c1; cc += NT) {
+        const int b = cc / c.rc, m = (cc % c.rc) * 4;
+        int x;
+        if (q == 0)
+            x = p.last_tok[b];
+        else if (p.teacher)
+            x = p.teacher[static_cast<size_t>(b) * p.K + (q - 1)];
+        else
+            x = rtok[b - c.rb0];
+        x = tok_ok(x, p.V) ? x : 0;
+        const float4 ah = ld_f4(p.A_H + (static_cast<size_t>(b) * p.K + q) * r + m);
+        const float4 mr = ld_f4(p.M + static_cast<size_t>(x) * r + m);
+        const float a4[4] = {ah.x + mr.x, ah.y + mr.y, ah.z + mr.z, ah.w + mr.w};
+        float u4[4];
+        uint32_t hi[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u4[i] = a4[i] * sigmoidf_(a4[i]);
+            hi[i] = bf16_rne_bits(u4[i]);
+        }
+        if (p.u_out)
+            *reinterpret_cast<float4 *>(p.u_out + (static_cast<size_t>(b) * p.K + q) * r + m) =
+                make_float4(u4[0], u4[1], u4[2], u4[3]);
+        const size_t ch = ((static_cast<size_t>(q) * p.rb_ngr + (b >> 4)) * KS + (m >> 5)) * 64 + (b & 15) +
+                          16 * ((m & 31) >> 3);
+        st_agent_u64(reinterpret_cast<char *>(p.uop + ch) + (m & 7) * 2, pack4_bf16(hi[0], hi[1], hi[2], hi[3]));
+    }
+    if (c.c1 > c.c0) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_add(gmem(&p.rb_ucnt[q]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // The W2 phase of position q waits until every block of the u rows has written its
 // share of u_q.  False on a timeout.
+template <bool MK>
 __device__ __forceinline__ bool wait_u(const Params &p, int q)
 {
     int ok = 1;
     if (threadIdx.x == 0) {
-        const unsigned want = static_cast<unsigned>(u_producers(p.B, p.r));
+        const unsigned want =
+            static_cast<unsigned>(MK ? chunk_blocks(p.B * p.r / 4, gridDim.x) : u_producers(p.B, p.r));
         unsigned spins = 0;
         while (__hip_atomic_load(gmem(&p.rb_ucnt[q]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
             if (++spins > p.spin_limit) {
@@ -980,7 +1035,7 @@ __device__ __forceinline__ bool wait_u(const Params &p, int q)
     return true;
 }
 
-template <bool LB16, bool FAST, bool ST>
+template <bool LB16, bool FAST, bool ST, bool MK>
 __global__ __launch_bounds__(NT) void k_persistent_rb(Params p)
 {
     __shared__ uint4 lbA[LBUF], lbB[LBUF], lbC[LBUF];
@@ -1003,7 +1058,7 @@ __global__ __launch_bounds__(NT) void k_persistent_rb(Params p)
         if (threadIdx.x < static_cast<unsigned>(p.K))
             __hip_atomic_store(gmem(&p.rb_ucnt[threadIdx.x]), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    const Ctx c = make_ctx(p, blk, nblk);
+    const Ctx c = make_ctx(p, blk, nblk, MK);
     // the block's W2 slice: tile t = wave + NWAVE j in registers (zero past the range),
     // and its tile of the state rows
     W2Resident<RT, KS> res;
@@ -1019,21 +1074,29 @@ __global__ __launch_bounds__(NT) void k_persistent_rb(Params p)
         }
     }
     RB_MARK(1023);
-    if (p.S_init) {
-        // q = W_hh S_init + b_hh for the anchor step
-        update(p, c, -1, rtok);
+    if constexpr (MK) {
+        // Markov head: no state.  One grid barrier (the u counters are zero before any
+        // block counts itself), then u_0 from the last tokens
         if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
             return;
-        dots(p, blk, nblk, -1, lbA, lbB, lbC, uA, uB);
+        markov_phase(p, c, 0, rtok);
+    } else {
+        if (p.S_init) {
+            // q = W_hh S_init + b_hh for the anchor step
+            update(p, c, -1, rtok);
+            if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+                return;
+            dots(p, blk, nblk, -1, lbA, lbB, lbC, uA, uB);
+            if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
+                return;
+        }
+        update(p, c, 0, rtok);
+        RB_MARK(1022);
         if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
             return;
+        RB_MARK(1021);
+        dots(p, blk, nblk, 0, lbA, lbB, lbC, uA, uB);
     }
-    update(p, c, 0, rtok);
-    RB_MARK(1022);
-    if (!grid_sync(p.bar, gen, p.spin_limit, p.flags))
-        return;
-    RB_MARK(1021);
-    dots(p, blk, nblk, 0, lbA, lbB, lbC, uA, uB);
     RB_MARK(1020);
     // per position: W2 phase (after the blocks of the u rows have written u), argmax
     // words, update of the block's state entries, one grid barrier, state products
@@ -1051,7 +1114,7 @@ __global__ __launch_bounds__(NT) void k_persistent_rb(Params p)
                           "+s"(pl.b_hh), "+s"(pl.flags), "+s"(pl.bar));
         w2_prefetch<LB16, FAST>(pl, c, pos, lbA, lbB);
         RB_MARK(64 * pos);
-        if (!wait_u(pl, pos))
+        if (!wait_u<MK>(pl, pos))
             return;
         RB_MARK(64 * pos + 7);
         w2_phase<LB16, FAST, ST>(pl, c, res, pos, tag14, lbA, lbB, lbC, uA, uB, kred, lkey);
@@ -1059,7 +1122,16 @@ __global__ __launch_bounds__(NT) void k_persistent_rb(Params p)
         if (!resolve(pl, c, pos, tag14, rtok, rred))
             return;
         RB_MARK(64 * pos + 2);
-        if (pos + 1 < pl.K) {
+        if constexpr (MK) {
+            // Markov head: u of the next position from the tokens just resolved.  No grid
+            // barrier: a block polls argmax words only for rows whose u it forms, and
+            // no block writes the next position's words before every such block has
+            // counted its u; generations still advance one per position
+            if (pos + 1 < pl.K) {
+                markov_phase(pl, c, pos + 1, rtok);
+                ++gen;
+            }
+        } else if (pos + 1 < pl.K) {
             update(pl, c, pos + 1, rtok);
             RB_MARK(64 * pos + 3);
             if (!grid_sync(pl.bar, gen, pl.spin_limit, pl.flags))
@@ -1099,22 +1171,31 @@ bool supports(int d, int h, int r, int V, int grid)
     // state chunks and rows per block at the largest batch, in whole 16-chunk runs as the
     // kernel splits them
     const long long nc = static_cast<long long>(rbk::MAXB) * h / 4, per = ((nc + grid - 1) / grid + 15) & ~15ll;
-    return per <= static_cast<long long>(rbk::CPT) * NT && per * 4 / h + 2 <= rbk::ROWS;
+    // (a Markov head splits the u entries the same way: r = 256 needs no more rows)
+    const long long ncu = static_cast<long long>(rbk::MAXB) * r / 4, peru = ((ncu + grid - 1) / grid + 15) & ~15ll;
+    return per <= static_cast<long long>(rbk::CPT) * NT && per * 4 / h + 2 <= rbk::ROWS &&
+           peru <= static_cast<long long>(rbk::CPT) * NT && peru * 4 / r + 2 <= rbk::ROWS;
+}
+
+template <bool LB16, bool FAST, bool ST>
+static const void *pick_mk(bool mk)
+{
+    return mk ? reinterpret_cast<const void *>(&rbk::k_persistent_rb<LB16, FAST, ST, true>)
+              : reinterpret_cast<const void *>(&rbk::k_persistent_rb<LB16, FAST, ST, false>);
 }
 
 template <bool LB16, bool FAST>
-static const void *pick_st(bool st)
+static const void *pick_st(bool st, bool mk)
 {
-    return st ? reinterpret_cast<const void *>(&rbk::k_persistent_rb<LB16, FAST, true>)
-              : reinterpret_cast<const void *>(&rbk::k_persistent_rb<LB16, FAST, false>);
+    return st ? pick_mk<LB16, FAST, true>(mk) : pick_mk<LB16, FAST, false>(mk);
 }
 
-const void *kernel(bool lbase_bf16, bool store_logits, int V)
+const void *kernel(bool lbase_bf16, bool store_logits, int V, bool markov)
 {
     const bool fast = V % (lbase_bf16 ? 8 : 4) == 0;
     if (lbase_bf16)
-        return fast ? pick_st<true, true>(store_logits) : pick_st<true, false>(store_logits);
-    return fast ? pick_st<false, true>(store_logits) : pick_st<false, false>(store_logits);
+        return fast ? pick_st<true, true>(store_logits, markov) : pick_st<true, false>(store_logits, markov);
+    return fast ? pick_st<false, true>(store_logits, markov) : pick_st<false, false>(store_logits, markov);
 }
 
 }  // namespace dhrb

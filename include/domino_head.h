@@ -62,8 +62,9 @@ extern "C" {
                                       8 < B <= 256 where the batched persistent launch is available (see
                                       below); the step launches otherwise */
 #define DOMINO_EXEC_PERSISTENT 1u  /* one cooperative launch covering all K positions: B <= 8, or (bf16
-                                      weights, r = 256, DOMINO_FOLD_EMBED, h a multiple of 64, d of 32)
-                                      B <= 256, where the GRU update and state products are spread over
+                                      weights, r = 256, DOMINO_FOLD_EMBED or DOMINO_MARKOV, h a multiple
+                                      of 64, d of 32) B <= 256, where the GRU update and state products
+                                      (for a Markov head, the table gather that forms u) are spread over
                                       the grid; either way each block keeps its W2 slice on chip */
 #define DOMINO_EXEC_STEPWISE 2u    /* one launch per phase and position */
 #define DOMINO_EXEC_STREAM_W2 8u   /* persistent launch: stream W2 from memory at every position instead of

@@ -124,16 +124,20 @@ def test_markov_resident_matches_oracle_and_step_launches(V, B):
         assert np.array_equal(g[k], gs[k]), k
 
 
-@pytest.mark.parametrize("V,B", [(20011, 40), (7001, 130)])
-def test_markov_batched_matrix_cores_match_oracle(V, B):
-    """B > 8: A_H and W2 on the matrix cores; teacher forcing takes the one W2 launch
-    over all B*K (row, position) pairs."""
+@pytest.mark.parametrize("mode", [dca.EXEC_AUTO, dca.EXEC_STEPWISE])
+@pytest.mark.parametrize("V,B", [(20011, 40), (7001, 130), (7001, 256)])
+def test_markov_batched_matrix_cores_match_oracle(V, B, mode):
+    """B > 8: A_H and W2 on the matrix cores, in the batched persistent launch (each
+    block forms its share of u from the table and counts itself in the position's
+    arrival counter) or in the step launches (where teacher forcing takes the one W2
+    launch over all B*K (row, position) pairs)."""
     sh = ds.HeadShape(d=512, h=256, r=256, V=V, K=16, wdtype="bf16")
     w = ds.make_weights(sh, (9, 64), gru_sensitive=True)
     inp = ds.make_inputs(sh, B, (9, 65), sigma=0.5, peak="none")
-    head = markov_head(w, B)
-    assert not head.exec_info(B)["persistent"]
-    both_protocols(w, inp, head, label="markov batched V=%d B=%d" % (V, B))
+    head = markov_head(w, B, mode)
+    info = head.exec_info(B)
+    assert info["persistent"] == (mode == dca.EXEC_AUTO) and info["w2_resident"] == info["persistent"]
+    both_protocols(w, inp, head, label="markov batched V=%d B=%d mode=%d" % (V, B, mode))
 
 
 def test_markov_position_batched_equals_per_position():
@@ -199,8 +203,8 @@ def test_markov_qwen3_8b_b1_full(w8b):
 
 @pytest.mark.slow
 def test_markov_qwen3_8b_b32_sampled_rows(w8b):
-    """The Markov head at the 8B shape, B = 32 (matrix-core step launches); the oracle
-    checks sampled rows."""
+    """The Markov head at the 8B shape, B = 32 (the batched persistent launch); the
+    oracle checks sampled rows."""
     wl = ds.WORKLOADS["qwen3_8b_b32"]
     rows = [0, 17, 31]
     inp = ds.make_inputs(wl.shape, wl.B, wl.row_key, wl.sigma, wl.peak, wl.peak_height, wl.temperature)
@@ -229,7 +233,8 @@ def test_markov_bf16_lbase_and_plain_launch_equal_float32(B, mode):
         assert np.array_equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("B,mode", [(3, dca.EXEC_PERSISTENT | dca.EXEC_PLAIN_LAUNCH), (40, dca.EXEC_AUTO)])
+@pytest.mark.parametrize("B,mode", [(3, dca.EXEC_PERSISTENT | dca.EXEC_PLAIN_LAUNCH),
+                                    (40, dca.EXEC_PERSISTENT | dca.EXEC_PLAIN_LAUNCH), (40, dca.EXEC_STEPWISE)])
 def test_markov_hip_graph_replay_matches_eager(B, mode):
     """A Markov draft captured in a HIP graph and replayed three times, with eager drafts
     of other inputs on the same handle in between, equals the eager result bitwise."""

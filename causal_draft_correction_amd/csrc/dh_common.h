@@ -24,6 +24,11 @@
 #ifndef DH_TRACE
 #define DH_TRACE(slot) ((void)(slot))
 #endif
+// DH_TRACE_LANDED(slot): the same mark taken once the thread's loads in flight
+// have landed (an instrumented build waits for them there; the default is a no-op)
+#ifndef DH_TRACE_LANDED
+#define DH_TRACE_LANDED(slot) ((void)(slot))
+#endif
 
 namespace DH_NS {
 
@@ -235,7 +240,21 @@ __device__ inline void block_sum(float (&v)[M], float *red)
     __syncthreads();
 }
 
-__device__ inline float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
+// The GRU and SiLU nonlinearities, on the hardware's base-2 exponential and
+// reciprocal (v_exp_f32, v_rcp_f32: about 1 ulp each) instead of the library's
+// correctly rounded exp and IEEE division: errors of a few 1e-7, far inside the
+// 1e-4 bound on S and u, in a fraction of the instructions.  Every kernel uses
+// these, so the launch paths stay bitwise equal.
+//   sigmoid x = 1 / (1 + 2^(-x log2 e))  (x -> +inf: 1; x -> -inf: 1 / inf = 0)
+//   tanh x    = 1 - 2 / (1 + 2^(2 x log2 e))  (+inf: 1; -inf: 1 - 2 = -1)
+__device__ inline float sigmoidf_(float x)
+{
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
+}
+__device__ inline float tanhf_(float x)
+{
+    return 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * 2.88539008177792681f));
+}
 
 // Argmax key: larger key = better candidate.  High word orders the float
 // (NaN above +inf, -0 folded into +0); low word prefers the lower index.

@@ -355,7 +355,7 @@ __device__ inline float gate_update(const Params &p, int q, int b, int j, int to
     }
     const float rg = sigmoidf_(gr + qr);
     const float zg = sigmoidf_(gz + qz);
-    const float ng = tanhf(gn + rg * qn);
+    const float ng = tanhf_(gn + rg * qn);
     return (1.f - zg) * ng + zg * sprev;
 }
 
@@ -715,6 +715,8 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                         qv[e][2] = xld(&qq[2 * h + j]);
                     }
                 }
+                if (i0 == static_cast<int>(threadIdx.x))
+                    DH_TRACE_LANDED(tslot + 9);
                 if (!p.P && p.gtag) {
                     // the g words of this step carry `tag` once their producers wrote them:
                     // while any does not, re-read all of them (one round trip per round)
@@ -756,7 +758,7 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                         // the cell of gate_update, on the values loaded above
                         const float rg = sigmoidf_(gv[e][0] + qv[e][0]);
                         const float zg = sigmoidf_(gv[e][1] + qv[e][1]);
-                        const float ng = tanhf(gv[e][2] + rg * qv[e][2]);
+                        const float ng = tanhf_(gv[e][2] + rg * qv[e][2]);
                         const float sn = (1.f - zg) * ng + zg * sp[e];
                         S_lds[bb * h + j] = sn;  // each thread reads only the entries it writes
                         if (blk == 0 && p.S_out)
@@ -805,6 +807,8 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
 #pragma unroll
                 for (int j = 0; j < RG; ++j)
                     acc[j] = 0.f;
+                if (k0 == 0 && bb == 0)
+                    DH_TRACE(tslot + 7);
 #pragma unroll 2
                 for (int ch = lane; ch < nch; ch += 64) {
                     float x[EPC];
@@ -822,6 +826,8 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                         }
                     }
                 }
+                if (k0 == 0 && bb == 0)
+                    DH_TRACE(tslot + 8);
                 float dot[RG];
 #pragma unroll
                 for (int j = 0; j < RG; ++j)

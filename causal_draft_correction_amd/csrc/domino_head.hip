@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void k_markov_state(const float *Pc, const voi
         const float bn = b_hh ? WT16<WT>::one(b_hh, 2 * h + j) : 0.f;
         const float rg = sigmoidf_(g[j] + br);
         const float zg = sigmoidf_(g[h + j] + bz);
-        const float ng = tanhf(g[2 * h + j] + rg * bn);
+        const float ng = tanhf_(g[2 * h + j] + rg * bn);
         Sc[i] = (1.f - zg) * ng;
     }
 }

@@ -620,7 +620,7 @@ __device__ __forceinline__ void update(const Params &p, const Ctx &c, int q, con
                 // the cell of gate_update
                 const float rg = sigmoidf_(g3[0][i] + q3[0][i]);
                 const float zg = sigmoidf_(g3[1][i] + q3[1][i]);
-                const float ng = tanhf(g3[2][i] + rg * q3[2][i]);
+                const float ng = tanhf_(g3[2][i] + rg * q3[2][i]);
                 sn[i] = (1.f - zg) * ng + zg * s4[i];
             }
             const float4 s = make_float4(sn[0], sn[1], sn[2], sn[3]);

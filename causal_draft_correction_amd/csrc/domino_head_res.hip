@@ -81,10 +81,12 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
         if (!phase_w2_resident<RT, KS, NB>(pl, blk, nblk, pos, smem, res, tl, local_keys, gen + 1))
             return;
         argmax_arrive(pl.asy, gen, local_keys, pl.B);
+        DH_TRACE(pos * 32 + 6);
         // L_base of the next position goes to LDS while the barrier is awaited (the
         // compiler makes the thread's next LDS access wait for these loads)
         if (pos + 1 < pl.K)
             lbase_to_lds(pl, blk, nblk, pos + 1, smem);
+        DH_TRACE(pos * 32 + 7);
         if (!argmax_wait(pl.asy, gen, pl.B, atok, pl.spin_limit, pl.flags))
             return;
         if (blk == 0 && threadIdx.x < pl.B)

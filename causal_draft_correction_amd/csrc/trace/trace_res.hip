@@ -4,6 +4,11 @@
 
 __device__ unsigned long long trace_res_buf[TRACE_BLOCKS * TRACE_SLOTS];
 #define DH_TRACE(slot) TRACE_MARK(trace_res_buf, 64, slot)
+#define DH_TRACE_LANDED(slot)                                                                            \
+    do {                                                                                                 \
+        __builtin_amdgcn_s_waitcnt(0);                                                                   \
+        TRACE_MARK(trace_res_buf, 64, slot);                                                             \
+    } while (0)
 
 #include "../domino_head_res.hip"
 

@@ -44,7 +44,13 @@ RES_POSITION = [("w2_wait_u", 0, 1), ("w2_products", 2, 4), ("w2_block_key", 4, 
 # wave 0's first group of state rows (its u row) in the state dots: products and
 # sums, the stores, then the other rows
 RES_DOTS = [("dots_first_group", 19, 21), ("dots_first_stores", 21, 22), ("dots_other_rows", 22, 20),
+            ("dots_first_setup", 19, 23), ("dots_first_products", 23, 24), ("dots_first_sums", 24, 21),
             ("mark_cost", 13, 15)]
+# the argmax exchange (arrival; next L_base slice issued; the wait for every block and
+# the reduction) and the gate update (the input token to LDS; the P row, q and state
+# loads landed; the cell and its stores)
+RES_SPLIT = [("exchange_arrive", 5, 6), ("exchange_lbase_issue", 6, 7), ("exchange_wait", 7, 13),
+             ("gates_token", 16, 17), ("gates_loads_landed", 17, 25), ("gates_cell", 25, 18)]
 # unfolded head: the input product itself and its grid barrier
 RES_UNFOLDED = [("input_product_compute", 13, 14), ("input_product_barrier", 14, 16)]
 RES_PROLOGUE = [("slice_and_loads_issued", 511, 508), ("anchor_step", -16, -12), ("prologue", 511, 509)]
@@ -101,7 +107,7 @@ def summarize(t, K, batched, dots_detail=False, unfolded=False):
         start = 1019
     else:
         col = lambda s: s + RES_BIAS  # noqa: E731
-        per, pro, stride, end = RES_POSITION + RES_DOTS, RES_PROLOGUE, 32, 32 * (K - 1) + 13
+        per, pro, stride, end = RES_POSITION + RES_DOTS + RES_SPLIT, RES_PROLOGUE, 32, 32 * (K - 1) + 13
         if unfolded:
             per = per + RES_UNFOLDED
         start = 511

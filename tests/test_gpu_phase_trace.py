@@ -57,9 +57,9 @@ def test_phase_trace_reports_every_phase(wl):
     r = json.loads(line[len("RESULT "):])
     mid = r["positions_1_to_14_median"]
     # every phase took a positive time and the phases add up to the position
-    # (the dots_ entries split state_dots)
+    # (the dots_, exchange_ and gates_ entries split state_dots, argmax_exchange and gru_gates)
     parts = {k: v[0] for k, v in mid.items()
-             if k != "position" and not k.startswith("dots_") and k != "mark_cost"}
+             if k != "position" and not k.startswith(("dots_", "exchange_", "gates_")) and k != "mark_cost"}
     assert all(v > 0 for v in parts.values()), parts
     assert 0.8 * mid["position"][0] <= sum(parts.values()) <= 1.2 * mid["position"][0], (parts, mid["position"])
     # the kernel spans the prologue and 16 positions

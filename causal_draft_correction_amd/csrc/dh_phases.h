@@ -670,10 +670,13 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
             __syncthreads();
             // qmode 0: q prefetched before the barrier (first batch), 1: q = b_hh (zero
             // initial state), 2: q loaded; one branch per batch, none per element
-            auto batch = [&](auto qmode, int i0) {
-                constexpr int QM = decltype(qmode)::value;
+            // gmode 0: g from the folded table's row (p.P), 1: g words (p.gtag), 2: g_buf.
+            // Both modes are template arguments, so each variant holds only its own
+            // loaded values in registers.
+            auto batch = [&](auto qmode, auto gmode, int i0) {
+                constexpr int QM = decltype(qmode)::value, GM = decltype(gmode)::value;
                 float gv[SP_EL][3], qv[SP_EL][3], sp[SP_EL];
-                uint64_t gt[SP_EL][3];  // tagged g words (p.gtag)
+                uint64_t gt[GM == 1 ? SP_EL : 1][3];  // tagged g words (p.gtag)
 #pragma unroll
                 for (int e = 0; e < SP_EL; ++e) {
                     const int i = i0 + e * NT;
@@ -682,13 +685,13 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                     // (an element past the end reads no S_lds entry: that entry belongs to
                     // another thread, which may be writing it)
                     sp[e] = (q == 0) ? state_prev(p, 0, b, j) : (i < ne ? S_lds[bb * h + j] : 0.f);
-                    if (p.P) {
+                    if constexpr (GM == 0) {
                         // (global loads: as flat loads they would also hold up the LDS reads)
                         const auto *prow = gmem(p.P + static_cast<size_t>(tokl[bb]) * h3);
                         gv[e][0] = prow[j];
                         gv[e][1] = prow[h + j];
                         gv[e][2] = prow[2 * h + j];
-                    } else if (p.gtag) {
+                    } else if constexpr (GM == 1) {
                         const uint64_t *g = p.gtag + static_cast<size_t>(b) * h3;
                         gt[e][0] = ld_agent_u64(&g[j]);
                         gt[e][1] = ld_agent_u64(&g[h + j]);
@@ -717,7 +720,7 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                 }
                 if (i0 == static_cast<int>(threadIdx.x))
                     DH_TRACE_LANDED(tslot + 9);
-                if (!p.P && p.gtag) {
+                if constexpr (GM == 1) {
                     // the g words of this step carry `tag` once their producers wrote them:
                     // while any does not, re-read all of them (one round trip per round)
                     unsigned spins = 0;
@@ -767,13 +770,21 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                 }
             };
             const bool use_pre = pre && b0 == 0, qbias = q == 0 && !p.S_init;
+            auto by_g = [&](auto qmode, int i0) {
+                if (p.P)
+                    batch(qmode, std::integral_constant<int, 0>(), i0);
+                else if (p.gtag)
+                    batch(qmode, std::integral_constant<int, 1>(), i0);
+                else
+                    batch(qmode, std::integral_constant<int, 2>(), i0);
+            };
             for (int i0 = threadIdx.x, it = 0; i0 < ne; i0 += SP_EL * NT, ++it) {
                 if (use_pre && it == 0)
-                    batch(std::integral_constant<int, 0>(), i0);
+                    by_g(std::integral_constant<int, 0>(), i0);
                 else if (qbias)
-                    batch(std::integral_constant<int, 1>(), i0);
+                    by_g(std::integral_constant<int, 1>(), i0);
                 else
-                    batch(std::integral_constant<int, 2>(), i0);
+                    by_g(std::integral_constant<int, 2>(), i0);
             }
         } else {
             __syncthreads();  // S_lds of the previous chunk is no longer read

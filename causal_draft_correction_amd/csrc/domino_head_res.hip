@@ -43,8 +43,11 @@ __global__ __launch_bounds__(NT) void k_persistent_res(Params p)
         // issued after the anchor gate update's loads, so it overlaps the dot
         // products and the first u exchange
         lbase_to_lds(p, blk, nblk, 0, smem);
+        DH_TRACE(507);
         state_cache_load<bf16s>(p, blk, nblk, cache, false);
+        DH_TRACE(506);
         ah_local_to_cache<bf16s>(p, blk, nblk, cache);
+        DH_TRACE(505);
         if (!p.P)
             phase_g<bf16s, 3>(p, blk, nblk, 0, smem, nullptr, gen + 1);
         DH_TRACE(508);

@@ -54,6 +54,12 @@ RES_SPLIT = [("exchange_arrive", 5, 6), ("exchange_lbase_issue", 6, 7), ("exchan
 # unfolded head: the input product itself and its grid barrier
 RES_UNFOLDED = [("input_product_compute", 13, 14), ("input_product_barrier", 14, 16)]
 RES_PROLOGUE = [("slice_and_loads_issued", 511, 508), ("anchor_step", -16, -12), ("prologue", 511, 509)]
+# the prologue of a B = 1 launch without initial state (no grid barrier): the first
+# L_base slice issued, the state rows to LDS, the A_H entries of the block's u rows;
+# then the anchor step's gate update, the W2 slice load issued after it, the dots
+RES_PROLOGUE_FAST = [("lbase_issue", 511, 507), ("state_rows_to_lds", 507, 506), ("ah_entries", 506, 505),
+                     ("anchor_gates", -16, -14), ("w2_slice_issue", -14, -13), ("anchor_dots", -13, -12),
+                     ("anchor_first_dot_group", -13, -11), ("to_first_w2", -12, 0)]
 
 # batched kernel (k_persistent_rb): hook slot is the column; marks relative to 64 * position
 RB_POSITION = [("wait_u", 0, 7), ("w2", 7, 1), ("resolve", 1, 2), ("gru_update", 2, 3), ("grid_barrier", 3, 4),
@@ -113,6 +119,8 @@ def summarize(t, K, batched, dots_detail=False, unfolded=False):
         start = 511
     out = {"kernel_us": round(float((t[:, col(end)].max() - t[:, col(start)].min()) * TICK_US), 1)}
     out["prologue"] = {n: [round(x, 2) for x in _span(t, col(a), col(b))] for n, a, b in pro}
+    if not batched and (t[:, col(505)] > 0).all():
+        out["prologue"].update({n: [round(x, 2) for x in _span(t, col(a), col(b))] for n, a, b in RES_PROLOGUE_FAST})
     for p in sorted({0, K - 1}):
         out["position_%d" % p] = {n: [round(x, 2) for x in _span(t, col(stride * p + a), col(stride * p + b))]
                                   for n, a, b in per if stride * p + max(a, b) <= end}

@@ -44,6 +44,13 @@ __host__ __device__ inline int smem_off_tok() { return 256 + 2 * NWAVE; }
 __host__ __device__ inline int smem_off_u() { return 256 + 2 * NWAVE + TOK_SLOTS; }
 __host__ __device__ inline int smem_off_lbuf(int r) { return smem_off_u() + BC * r; }
 __host__ __device__ inline int smem_off_S(int r, int rows_cap) { return smem_off_lbuf(r) + BC * rows_cap; }
+// First vocabulary row of block blk's slice, V * blk / nblk, in 32-bit arithmetic
+// (the resident launches take V <= 2^18 and at most MAX_GRID = 2^10 blocks, so the
+// product stays below 2^28; a 64-bit division costs about a hundred instructions).
+__host__ __device__ inline int vslice_lo(int V, int blk, int nblk)
+{
+    return static_cast<int>(static_cast<unsigned>(V) * static_cast<unsigned>(blk) / static_cast<unsigned>(nblk));
+}
 // Row stride of lbuf: the block's vocabulary rows, padded to whole 16-row tiles.
 __host__ __device__ inline int lbuf_stride(int V, int nblk) { return ((V + nblk - 1) / nblk + 15) & ~15; }
 __host__ __device__ inline int smem_floats_small() { return smem_off_u(); }
@@ -1108,8 +1115,8 @@ __device__ __forceinline__ void w2_resident_load(const Params &p, int blk, int n
                                                  uint4 *tl)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const long long v0 = static_cast<long long>(p.V) * blk / nblk;
-    const int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0);
+    const long long v0 = vslice_lo(p.V, blk, nblk);
+    const int n = vslice_lo(p.V, blk + 1, nblk) - static_cast<int>(v0);
     const int T = (n + 15) / 16;
 #pragma unroll
     for (int j = 0; j < RT; ++j) {
@@ -1131,8 +1138,8 @@ __device__ __forceinline__ void w2_resident_load(const Params &p, int blk, int n
 __device__ __forceinline__ void lbase_to_lds(const Params &p, int blk, int nblk, int pos, float *smem)
 {
     typedef __attribute__((address_space(3))) void lds_void;
-    const long long v0 = static_cast<long long>(p.V) * blk / nblk;
-    const int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0);
+    const long long v0 = vslice_lo(p.V, blk, nblk);
+    const int n = vslice_lo(p.V, blk + 1, nblk) - static_cast<int>(v0);
     const int rows_cap = lbuf_stride(p.V, nblk);
     float *dst = smem + smem_off_lbuf(p.r);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1220,8 +1227,8 @@ __device__ __forceinline__ bool phase_w2_resident(const Params &p, int blk, int 
 {
     static_assert(NB >= 1 && NB <= BC, "batch rows of one persistent launch");
     const int r = 32 * KS;
-    int v0i = static_cast<int>(static_cast<long long>(p.V) * blk / nblk);  // V < 2^31
-    int n = static_cast<int>(static_cast<long long>(p.V) * (blk + 1) / nblk - v0i);
+    int v0i = vslice_lo(p.V, blk, nblk);
+    int n = vslice_lo(p.V, blk + 1, nblk) - v0i;
     // opaque per call: keeps the compiler from hoisting the per-row index and
     // bound values of every tile out of the position loop into spilled registers
     asm volatile("" : "+s"(v0i), "+s"(n));

@@ -671,10 +671,18 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
             const int ne = nb * h;
             // the GRU input token of each row, once, into LDS: the batch loads below
             // then depend on an LDS read only
-            int *tokl = reinterpret_cast<int *>(smem + smem_off_tok());
-            if (p.P && static_cast<int>(threadIdx.x) < nb)
-                tokl[threadIdx.x] = gru_input_token(p, q, b0 + threadIdx.x, atok);
-            __syncthreads();
+            // (the argmax tokens of a persistent launch, atok, are visible to the whole
+            // block since the barrier that delivered them: no copy and no block sync)
+            const int *tokl = atok;
+            if (!(atok && q > 0 && !p.teacher)) {
+                int *tl = reinterpret_cast<int *>(smem + smem_off_tok());
+                if (p.P && static_cast<int>(threadIdx.x) < nb)
+                    tl[threadIdx.x] = gru_input_token(p, q, b0 + threadIdx.x, atok);
+                __syncthreads();
+                tokl = tl;
+            }
+            // (one batch row: element i is entry i of row b0, no division by h)
+            const bool one = nb == 1;
             // qmode 0: q prefetched before the barrier (first batch), 1: q = b_hh (zero
             // initial state), 2: q loaded; one branch per batch, none per element
             // gmode 0: g from the folded table's row (p.P), 1: g words (p.gtag), 2: g_buf.
@@ -688,7 +696,7 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                 for (int e = 0; e < SP_EL; ++e) {
                     const int i = i0 + e * NT;
                     const int ic = i < ne ? i : 0;
-                    const int bb = ic / h, j = ic % h, b = b0 + bb;
+                    const int bb = one ? 0 : ic / h, j = one ? ic : ic % h, b = b0 + bb;
                     // (an element past the end reads no S_lds entry: that entry belongs to
                     // another thread, which may be writing it)
                     sp[e] = (q == 0) ? state_prev(p, 0, b, j) : (i < ne ? S_lds[bb * h + j] : 0.f);
@@ -749,7 +757,8 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                         for (int e = 0; e < SP_EL; ++e) {
                             const int i = i0 + e * NT;
                             const int ic = i < ne ? i : 0;
-                            const uint64_t *g = p.gtag + static_cast<size_t>(b0 + ic / h) * h3 + ic % h;
+                            const uint64_t *g =
+                                p.gtag + static_cast<size_t>(b0 + (one ? 0 : ic / h)) * h3 + (one ? ic : ic % h);
                             for (int c = 0; c < 3; ++c)
                                 gt[e][c] = ld_agent_u64(&g[c * h]);
                         }
@@ -764,7 +773,7 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                 for (int e = 0; e < SP_EL; ++e) {
                     const int i = i0 + e * NT;
                     if (i < ne) {
-                        const int bb = i / h, j = i % h, b = b0 + bb;
+                        const int bb = one ? 0 : i / h, j = one ? i : i % h, b = b0 + bb;
                         // the cell of gate_update, on the values loaded above
                         const float rg = sigmoidf_(gv[e][0] + qv[e][0]);
                         const float zg = sigmoidf_(gv[e][1] + qv[e][1]);

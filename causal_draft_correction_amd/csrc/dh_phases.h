@@ -453,22 +453,97 @@ __device__ __forceinline__ void state_prefetch(const Params &p, int q, StatePre 
     }
 }
 
-// State rows of a wave: m0, m0 + NWAVE * nblk, ... with m0 = state_row0.  The
-// numbering is wave-major, so the r u rows (the first rows) are spread over all
-// blocks instead of filling the first r / NWAVE of them.
-__host__ __device__ inline int state_row0(int blk, int nblk, int wave) { return wave * nblk + blk; }
-
-// Rows of the state phase handled by each wave of a persistent launch, and the
-// LDS it takes to keep them: the rows (WT) plus their A_H entries for every
+// Rows of the state phase handled by each wave of a persistent launch (at most), and
+// the LDS it takes to keep them: the rows (WT) plus their A_H entries for every
 // position and batch row (u rows only).
 __host__ __device__ inline int state_rows_per_wave(int r, int h, int nblk)
 {
     return (r + 3 * h + nblk * NWAVE - 1) / (nblk * NWAVE);
 }
+
+// Dot rows of the state phase (the W1_S rows m < r, giving u, then the W_hh rows,
+// giving q).  Block blk owns the rows m = blk + t nblk, t = 0 .. T-1, its U u rows
+// first, so the u rows are spread over all blocks.  The u rows go to waves 0, 1, ...
+// in turn (slot k of wave w: t = w + k NWAVE).  The q rows go, DOT_RG at a time (one
+// dot group), to the waves that hold no u row, so a wave computing a u row -- the
+// value the next W2 phase waits for -- gets no q row when the others can take them
+// all; when every wave holds a u row, or this would give a wave more than
+// state_rows_per_wave rows, or the caller asks for it (`group` false), the q rows go
+// round-robin instead (q row t goes to wave t mod NWAVE).
+constexpr int DOT_RG = 4;
+struct DotRows {
+    int blk, nblk;
+    int U, Q;     // the block's u and q rows
+    int nq, qw0;  // q rows go to waves qw0, qw0 + 1, ... (mod NWAVE), nq of them
+    int rg;       // q rows per chunk: DOT_RG, or 1 (round-robin)
+};
+__host__ __device__ inline int dot_u_rows(const DotRows &d, int w)
+{
+    return w < d.U ? (d.U - w + NWAVE - 1) / NWAVE : 0;
+}
+// position of wave w among the q waves, or nq when it takes none
+__host__ __device__ inline int dot_q_index(const DotRows &d, int w)
+{
+    const int iw = (w - d.qw0 + NWAVE) % NWAVE;
+    return iw < d.nq ? iw : d.nq;
+}
+__host__ __device__ inline int dot_rows_of(const DotRows &d, int w)
+{
+    const int iw = dot_q_index(d, w), nc = (d.Q + d.rg - 1) / d.rg;
+    int nqr = 0;
+    if (iw < d.nq && iw < nc) {
+        nqr = (nc - iw + d.nq - 1) / d.nq * d.rg;
+        if ((nc - 1 - iw) % d.nq == 0)
+            nqr -= nc * d.rg - d.Q;  // this wave has the last, partial chunk
+    }
+    return dot_u_rows(d, w) + nqr;
+}
+__host__ __device__ inline DotRows dot_rows(int r, int R, int blk, int nblk, bool group = true)
+{
+    DotRows d;
+    d.blk = blk;
+    d.nblk = nblk;
+    const int T = blk < R ? (R - blk + nblk - 1) / nblk : 0;
+    d.U = blk < r ? (r - blk + nblk - 1) / nblk : 0;
+    d.Q = T - d.U;
+    bool grouped = group && d.U < NWAVE;
+    if (grouped) {
+        d.nq = NWAVE - d.U;
+        d.qw0 = d.U;
+        d.rg = DOT_RG;
+        const int cap = state_rows_per_wave(r, (R - r) / 3, nblk);
+        for (int w = 0; w < NWAVE; ++w)
+            grouped = grouped && dot_rows_of(d, w) <= cap;
+    }
+    if (!grouped) {
+        d.nq = NWAVE;
+        d.qw0 = d.U % NWAVE;
+        d.rg = 1;
+    }
+    return d;
+}
+// row m of slot k of wave w, or -1
+__host__ __device__ inline int dot_row(const DotRows &d, int w, int k)
+{
+    const int nu = dot_u_rows(d, w);
+    int t;
+    if (k < nu) {
+        t = w + k * NWAVE;
+    } else {
+        const int iw = dot_q_index(d, w), kq = k - nu;
+        const int tq = ((kq / d.rg) * d.nq + iw) * d.rg + kq % d.rg;
+        if (iw >= d.nq || tq >= d.Q)
+            return -1;
+        t = d.U + tq;
+    }
+    return d.blk + t * d.nblk;
+}
+// (then each wave's row table: its rows' ids, slots past its last -1, its u row count
+// and its row count, NWAVE x (rpw + 2) ints)
 __host__ __device__ inline int state_cache_floats(int r, int h, int K, int nblk, int wbytes)
 {
     const int rpw = state_rows_per_wave(r, h, nblk);
-    return NWAVE * rpw * (h * wbytes / 4 + K * BC);
+    return NWAVE * rpw * (h * wbytes / 4 + K * BC) + NWAVE * (rpw + 2);
 }
 
 // Once per persistent launch, after the prologue barrier: each wave copies its
@@ -485,15 +560,23 @@ __device__ __forceinline__ void state_cache_load(const Params &p, int blk, int n
     float *ac = cache + NWAVE * rpw * row_words;
     constexpr int CPL = (2048 / EPC + 63) / 64;  // 16-byte chunks per lane of a row at the largest h
     constexpr int RB = 16 / CPL;                 // rows whose loads go out together (16 registers of 16 bytes)
-    const int nchk = h / EPC, m0 = state_row0(blk, nblk, wave), mstep = nblk * NWAVE;
-    for (int k0 = 0; k0 < rpw && m0 + k0 * mstep < R; k0 += RB) {
+    const DotRows dr = dot_rows(p.r, R, blk, nblk);
+    const int nchk = h / EPC, nrw = dot_rows_of(dr, wave);
+    int *tab = reinterpret_cast<int *>(ac + NWAVE * rpw * p.K * BC) + wave * (rpw + 2);
+    if (lane < rpw)
+        tab[lane] = lane < nrw ? dot_row(dr, wave, lane) : -1;
+    if (lane == 0) {
+        tab[rpw] = dot_u_rows(dr, wave);
+        tab[rpw + 1] = nrw;
+    }
+    for (int k0 = 0; k0 < nrw; k0 += RB) {
         // the loads of RB rows first, every one issued (rows past the wave's last and
         // chunks past h read the group's first row / chunk 0), then the LDS stores
         uint4 v[RB][CPL];
 #pragma unroll
         for (int kk = 0; kk < RB; ++kk) {
-            const int k = k0 + kk, m = m0 + k * mstep;
-            const int mc = (k < rpw && m < R) ? m : m0 + k0 * mstep;
+            const int k = k0 + kk;
+            const int mc = dot_row(dr, wave, k < nrw ? k : k0);
             const void *W = mc < p.r ? p.W1 : p.W_hh;
             const size_t off = state_row_off<WT>(p, mc);
 #pragma unroll
@@ -504,8 +587,8 @@ __device__ __forceinline__ void state_cache_load(const Params &p, int blk, int n
         }
 #pragma unroll
         for (int kk = 0; kk < RB; ++kk) {
-            const int k = k0 + kk, m = m0 + k * mstep;
-            if (k < rpw && m < R) {
+            const int k = k0 + kk;
+            if (k < nrw) {
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
                     const int ch = lane + c * 64;
@@ -515,10 +598,8 @@ __device__ __forceinline__ void state_cache_load(const Params &p, int blk, int n
             }
         }
     }
-    for (int k = 0; k < rpw; ++k) {
-        const int m = m0 + k * mstep;
-        if (m >= R)
-            break;
+    for (int k = 0; k < nrw; ++k) {
+        const int m = dot_row(dr, wave, k);
         if (m < p.r) {
             for (int i = lane; with_ah && i < p.K * p.B; i += 64) {
                 const int qq = i / p.B, b = i % p.B;
@@ -547,14 +628,13 @@ __device__ __forceinline__ void ah_local_to_cache(const Params &p, int blk, int 
     constexpr int KK = 2;              // AH_LANES-chunk strides loaded together
     constexpr int VW = AH_LANES / 64;  // waves of the sum layout
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int h = p.h, d = p.d, rpw = state_rows_per_wave(p.r, h, nblk), mstep = nblk * NWAVE;
+    const int h = p.h, d = p.d, rpw = state_rows_per_wave(p.r, h, nblk);
     const int nch = d / EPC;
     float *ac = cache + NWAVE * rpw * (h * static_cast<int>(sizeof(WT)) / 4);
+    const DotRows dr = dot_rows(p.r, state_rows(p), blk, nblk);  // as state_cache_load
     for (int ow = 0; ow < NWAVE; ++ow) {
-        for (int k = 0; k < rpw; ++k) {
-            const int m = state_row0(blk, nblk, ow) + k * mstep;
-            if (m >= p.r)
-                break;
+        for (int k = 0; k < dot_u_rows(dr, ow); ++k) {
+            const int m = dot_row(dr, ow, k);
             float acc[PW][VW];
 #pragma unroll
             for (int t = 0; t < PW; ++t)
@@ -811,21 +891,31 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
         after_gate();
         __syncthreads();
         DH_TRACE(tslot + 3);
-        // dot rows of this wave: k-th row m = m0 + k * mstep; when `cached` (persistent
-        // launch) the row and its A_H entries come from LDS at `cache`.  Rows go in
+        // dot rows of this wave: slot k holds row dot_row(dr, wave, k); when `cached`
+        // (persistent launch) the row and its A_H entries come from LDS at `cache`.  Rows go in
         // groups of up to RG: the S chunks are read once per group and the sums are
         // reduced together (each row's sum is formed in the same order as alone).
         // The wave's u rows (m < r) form the first groups, so u is published before
         // the q rows are computed.
-        constexpr int RG = 4;
-        const int m0 = state_row0(blk, nblk, wave), mstep = nblk * NWAVE;
+        constexpr int RG = DOT_RG;
         const int rpw = state_rows_per_wave(r, h, nblk);
-        const int ku = m0 < r ? (r - m0 + mstep - 1) / mstep : 0;  // this wave's u rows
         const uint4 *wc = reinterpret_cast<const uint4 *>(cache);
         const float *ac = cache + NWAVE * rpw * (h * static_cast<int>(sizeof(WT)) / 4);
+        // this wave's u rows and all its rows: from its row table when cached
+        const int *tab = reinterpret_cast<const int *>(ac + NWAVE * rpw * p.K * BC) + wave * (rpw + 2);
+        DotRows dr{};
+        int ku, nrw;
+        if (cached) {
+            ku = tab[rpw];
+            nrw = tab[rpw + 1];
+        } else {
+            dr = dot_rows(r, R, blk, nblk);
+            ku = dot_u_rows(dr, wave);
+            nrw = dot_rows_of(dr, wave);
+        }
 #pragma unroll 1
-        for (int k0 = 0, kend = 0; m0 + k0 * mstep < R; k0 = kend) {
-            kend = k0 < ku ? (ku < k0 + RG ? ku : k0 + RG) : k0 + RG;
+        for (int k0 = 0, kend = 0; k0 < nrw; k0 = kend) {
+            kend = k0 < ku ? (ku < k0 + RG ? ku : k0 + RG) : (nrw < k0 + RG ? nrw : k0 + RG);
 #pragma unroll 1
             for (int bb = 0; bb < nb; ++bb) {
                 const int b = b0 + bb;
@@ -844,8 +934,9 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                         x[i2] = s[ch * EPC + i2];
 #pragma unroll
                     for (int j = 0; j < RG; ++j) {
-                        const int k = k0 + j, m = m0 + k * mstep;
-                        if (k < kend && m < R) {
+                        const int k = k0 + j;
+                        if (k < kend) {  // (slots below the wave's row count all hold rows)
+                            const int m = cached ? 0 : dot_row(dr, wave, k);
                             const uint4 wq = cached ? wc[(wave * rpw + k) * nch + ch]
                                                     : ld16<WT>(m < r ? p.W1 : p.W_hh,
                                                                state_row_off<WT>(p, m) + static_cast<size_t>(ch) * EPC);
@@ -863,9 +954,10 @@ __device__ __forceinline__ void phase_state(const Params &p, int blk, int nblk, 
                     DH_TRACE(tslot + 5);
 #pragma unroll
                 for (int j = 0; j < RG; ++j) {
-                    const int k = k0 + j, m = m0 + k * mstep;
-                    if (lane != 0 || k >= kend || m >= R)
+                    const int k = k0 + j;
+                    if (lane != 0 || k >= kend)
                         continue;
+                    const int m = cached ? tab[k] : dot_row(dr, wave, k);
                     if (m < r) {
                         const float ah = cached ? ac[((wave * rpw + k) * p.K + q) * BC + b]
                                                 : xld(&p.A_H[(static_cast<size_t>(b) * p.K + q) * r + m]);

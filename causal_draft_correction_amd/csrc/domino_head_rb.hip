@@ -56,6 +56,11 @@
 #ifndef RB_MARK
 #define RB_MARK(slot) ((void)(slot))
 #endif
+// RB_MARK_LANDED(slot): the same once the thread's memory operations in flight have
+// completed (an instrumented build waits for them there; the default is a no-op)
+#ifndef RB_MARK_LANDED
+#define RB_MARK_LANDED(slot) ((void)(slot))
+#endif
 // and RB_GMARK(i) to note the time of point i (< 32) of the W2 phase's groups (after
 // group g's wait: 2 g, after its products and epilogue: 2 g + 1), which RB_GFLUSH(pos,
 // n) records once the phase's copies are complete
@@ -543,6 +548,7 @@ __device__ __forceinline__ bool resolve(const Params &p, const Ctx &c, int pos, 
         }
     }
     const bool failed = block_failed(ok);
+    RB_MARK(64 * pos + 44);  // every argmax word of the block's rows read
     if (failed) {
         if (threadIdx.x == 0)
             __hip_atomic_fetch_or(gmem(p.flags), 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -612,6 +618,8 @@ __device__ __forceinline__ void update(const Params &p, const Ctx &c, int q, con
                               : make_float4(0.f, 0.f, 0.f, 0.f);
             else
                 sp = ld_f4(p.S_buf + static_cast<size_t>(b) * h + j);
+            if (u == 0 && q > 0)
+                RB_MARK_LANDED(64 * (q - 1) + 46);  // the gate inputs of the first entries landed
             const float g3[3][4] = {{gr.x, gr.y, gr.z, gr.w}, {gz.x, gz.y, gz.z, gz.w}, {gn.x, gn.y, gn.z, gn.w}};
             const float q3[3][4] = {{qr.x, qr.y, qr.z, qr.w}, {qz.x, qz.y, qz.z, qz.w}, {qn.x, qn.y, qn.z, qn.w}};
             const float s4[4] = {sp.x, sp.y, sp.z, sp.w};

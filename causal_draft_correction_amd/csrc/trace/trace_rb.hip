@@ -3,6 +3,11 @@
 
 __device__ unsigned long long trace_rb_buf[TRACE_BLOCKS * TRACE_SLOTS];
 #define RB_MARK(slot) TRACE_MARK(trace_rb_buf, 0, slot)
+#define RB_MARK_LANDED(slot)                                                                             \
+    do {                                                                                                 \
+        __builtin_amdgcn_s_waitcnt(0);                                                                   \
+        TRACE_MARK(trace_rb_buf, 0, slot);                                                               \
+    } while (0)
 // the W2 phase's group points: kept in LDS while the phase runs, written to slots
 // 64 pos + 8 + i afterwards
 __shared__ unsigned long long trace_rb_gt[32];

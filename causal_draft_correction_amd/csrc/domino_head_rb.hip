@@ -496,12 +496,14 @@ __device__ __forceinline__ void w2_phase(const Params &p, const Ctx &c, const W2
     // which the update of the next position waits for
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    RB_GFLUSH(pos, 2 * ngr);
     for (int b = threadIdx.x; b < p.B; b += NT) {
         const uint64_t m = lkey[b];
         st_agent_u64(&p.bkeys[static_cast<size_t>(b) * gridDim.x + blockIdx.x],
                      (m & (KEY_ORD_MASK | KEY_IDX_MASK)) | (static_cast<uint64_t>(tag14) << 18));
     }
+    // (an instrumented build writes the groups' times after the keys, so that they do not
+    // delay the key words that thread 0's wave stores)
+    RB_GFLUSH(pos, 2 * ngr);
 }
 
 // ---- update phase -----------------------------------------------------------------
